@@ -1,0 +1,337 @@
+"""CPU oracle of the Flint int4 routed-expert MoE layer — TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import or call this module.  The library and its Python
+binding never do: they share no code, constant table or helper with it.
+
+Everything here is plain NumPy in float64 and follows the pages step by step:
+
+* Flint model card for the int4-expert container (Aijuus/flint-w4exp),
+  introduction and table row "weights": 256 routed experts at top-6 plus an
+  ungated shared expert; routed experts are int4 codes with one bf16 scale
+  per 128 of K, stored in a 128-wide Hadamard (fwht128) rotated basis; the
+  shared expert and every other linear stay bf16.
+* NInfer README of Flint (WaveCut/Flint-UD-Q4_K_XL-NInfer-v3), section
+  "What is inside": sigmoid router scores renormalised over the 6 chosen
+  experts; each expert holds gate rows then up rows (2 x 512) and 2,048 down
+  rows; a shared expert of width 1024 with gate and up rows; router rows
+  kept in fp32, widened exactly from bf16.  Section "Quality": fp16 sums of
+  the routed experts overflow, so every sum here is at least fp32 (here fp64).
+* bloomery issue #632 ("model: Flint ..."), description and the design
+  thread: sigmoid router, 6 of 256 experts, no router correction bias, and
+  the normalisation policy max(sum of selected scores, 2**-14) with the six
+  (index, fp32 weight) slots handed to the expert stage.
+
+Readings where the pages are silent (each is listed in the design doc too):
+
+* Hadamard: Sylvester order, H[i][j] = (-1)**popcount(i & j) / sqrt(128),
+  no random signs; symmetric and its own inverse.
+* Rotation acts on the K side of all three expert planes: x before gate/up
+  (16 blocks), a = silu(g)*u before down (4 blocks).
+* Dequantisation is symmetric: w = code * scale; group g of a row covers
+  K in [128g, 128g+128); even K in the low nibble; two's complement codes.
+* Top-6 is chosen on fp32 logits (the precision the pages give the router),
+  higher logit first, equal logits to the lower expert index; the slot
+  order is that order.  A token whose 6th/7th fp64 logit gap is <= 1e-3 is
+  flagged as a near-tie.
+* The optional router bias is added to the logit before selection and
+  before the sigmoid (a synthetic skew; Flint itself has none).
+* silu(v) = v / (1 + exp(-v)); the shared expert is added with weight 1.
+* y is rounded once, fp64 -> bf16 round-to-nearest-even.
+
+Parity pins live in ``tests/test_oracle_*.py``.  Absolute output values on
+the synthetic workloads are "parity unpinned" against the pages (they print
+no worked example of the layer); the pins constrain every step instead.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+H = 2048
+E = 256
+K_TOP = 6
+I_R = 512
+I_S = 1024
+G = 128
+NEAR_TIE_GAP = 1e-3
+WEIGHT_FLOOR = 2.0 ** -14
+RMS_EPS = 1e-6
+
+
+# ---------------------------------------------------------------- numbers
+def bf16_to_f64(bits) -> np.ndarray:
+    """Widen bf16 bit patterns exactly (bf16 is the top half of an fp32)."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def f64_to_bf16_bits(v) -> np.ndarray:
+    """Round float64 to the nearest bf16 (ties to even), one rounding.
+
+    bf16 keeps 8 significant bits and fp32's exponent range; below 2**-126
+    the spacing is 2**-133.  Overflow goes to +-inf, NaN to a quiet NaN.
+    """
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    finite = np.isfinite(a) & (a > 0)
+    _, e = np.frexp(np.where(finite, a, 1.0))            # a = m * 2**e, m in [0.5, 1)
+    step_exp = np.where(e - 1 >= -126, e - 8, -133)       # 8 significant bits / subnormal spacing
+    q = np.ldexp(np.where(finite, a, 0.0), -step_exp)     # exact scaling by a power of two
+    r = np.rint(q)                                        # round half to even
+    val = np.ldexp(r, step_exp)
+    over = val >= 2.0 ** 128
+    with np.errstate(over="ignore"):
+        bits = (val.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint32)
+    bits = np.where(over | np.isinf(a), 0x7F80, bits)
+    bits = np.where(a == 0, 0, bits)
+    bits = bits | np.where(np.signbit(v), 0x8000, 0)
+    bits = np.where(np.isnan(v), 0x7FC0, bits)
+    return bits.astype(np.uint16)
+
+
+def f32_round(v) -> np.ndarray:
+    """Round to fp32 (IEEE round-to-nearest-even), returned as float64."""
+    return np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
+
+
+def sigmoid(v):
+    return 1.0 / (1.0 + np.exp(-np.asarray(v, dtype=np.float64)))
+
+
+def silu(v):
+    v = np.asarray(v, dtype=np.float64)
+    return v / (1.0 + np.exp(-v))
+
+
+# -------------------------------------------------------------- Hadamard
+def hadamard(n: int = G) -> np.ndarray:
+    """Normalised Sylvester Hadamard matrix of order n (a power of two).
+
+    Built by the doubling recursion H_2m = [[H_m, H_m], [H_m, -H_m]] and
+    divided by sqrt(n), so it is symmetric and orthogonal (its own inverse).
+    """
+    h = np.array([[1.0]])
+    while h.shape[0] < n:
+        h = np.block([[h, h], [h, -h]])
+    assert h.shape[0] == n
+    return h / math.sqrt(n)
+
+
+def rotate_blocks(v: np.ndarray, block: int = G) -> np.ndarray:
+    """Apply the normalised 128-point Hadamard to every 128-block of the last axis."""
+    v = np.asarray(v, dtype=np.float64)
+    hn = hadamard(block)
+    shp = v.shape
+    nb = shp[-1] // block
+    return (v.reshape(shp[:-1] + (nb, block)) @ hn).reshape(shp)
+
+
+# --------------------------------------------------------------- weights
+def unpack_int4(packed: np.ndarray, k: int) -> np.ndarray:
+    """Packed bytes [..., k/2] -> signed int4 values [..., k] (even k low nibble)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    lo = (p & 0x0F).astype(np.int16)
+    hi = (p >> 4).astype(np.int16)
+    vals = np.empty(p.shape[:-1] + (k,), dtype=np.int16)
+    vals[..., 0::2] = lo
+    vals[..., 1::2] = hi
+    vals[vals >= 8] -= 16                # two's complement
+    return vals
+
+
+def dequantize(packed_rows: np.ndarray, scale_bits: np.ndarray, k: int) -> np.ndarray:
+    """W[n, k] = code[n, k] * scale[n, k // 128] in float64."""
+    codes = unpack_int4(packed_rows, k).astype(np.float64)
+    s = bf16_to_f64(scale_bits)                      # [n, k/128]
+    return codes * np.repeat(s, G, axis=1)
+
+
+def expert_planes(code_bytes: np.ndarray, scale_bits: np.ndarray):
+    """Split one expert's blobs (library layout) into dequantised gate, up, down."""
+    cb = np.asarray(code_bytes, dtype=np.uint8)
+    sb = np.asarray(scale_bits, dtype=np.uint16)
+    nb_gu = I_R * H // 2
+    g_rows = cb[:nb_gu].reshape(I_R, H // 2)
+    u_rows = cb[nb_gu:2 * nb_gu].reshape(I_R, H // 2)
+    d_rows = cb[2 * nb_gu:].reshape(H, I_R // 2)
+    ns = I_R * (H // G)
+    sg = sb[:ns].reshape(I_R, H // G)
+    su = sb[ns:2 * ns].reshape(I_R, H // G)
+    sd = sb[2 * ns:].reshape(H, I_R // G)
+    return dequantize(g_rows, sg, H), dequantize(u_rows, su, H), dequantize(d_rows, sd, I_R)
+
+
+def shared_planes(shared_bits: np.ndarray):
+    sb = bf16_to_f64(shared_bits)
+    n = I_S * H
+    return sb[:n].reshape(I_S, H), sb[n:2 * n].reshape(I_S, H), sb[2 * n:].reshape(H, I_S)
+
+
+# ---------------------------------------------------------------- router
+def route(x: np.ndarray, router_bits: np.ndarray, bias=None):
+    """Sigmoid top-6 router with the 2**-14 floor on the renormaliser.
+
+    x: float64 [T, K] (already widened); router_bits: bf16 bits [n_experts, K]
+    (256 x 2048 for Flint; any n_experts >= 7 works).  Returns a dict with the fp64
+    logits, the fp32 logits the choice is made on, topk_idx [T, 6],
+    topk_w [T, 6] (float64), the 6th-7th gap and the near-tie flags.
+    """
+    R = bf16_to_f64(router_bits)                      # [256, 2048]
+    logits = x @ R.T                                  # [T, 256]
+    if bias is not None:
+        logits = logits + np.asarray(bias, dtype=np.float64)[None, :]
+    l32 = f32_round(logits)
+    T, n_exp = logits.shape
+    idx = np.empty((T, K_TOP), dtype=np.int32)
+    gap = np.empty(T, dtype=np.float64)
+    experts = np.arange(n_exp)
+    for t in range(T):
+        # higher fp32 logit first; equal logits -> lower expert index
+        order = np.lexsort((experts, -l32[t]))
+        idx[t] = order[:K_TOP]
+        srt = np.sort(logits[t])[::-1]
+        gap[t] = srt[K_TOP - 1] - srt[K_TOP]
+    sel = np.take_along_axis(logits, idx.astype(np.int64), axis=1)
+    sig = sigmoid(sel)
+    denom = np.maximum(sig.sum(axis=1, keepdims=True), WEIGHT_FLOOR)
+    w = sig / denom
+    return dict(logits=logits, logits32=l32, topk_idx=idx, topk_w=w,
+                gap=gap, near_tie=gap <= NEAR_TIE_GAP)
+
+
+def sort_assignments(topk_idx: np.ndarray):
+    """Counting sort of the 6T assignments a = 6t + j by expert, stable in a."""
+    flat = np.asarray(topk_idx, dtype=np.int64).ravel()
+    counts = np.bincount(flat, minlength=E)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    perm = np.argsort(flat, kind="stable")
+    pos = np.empty_like(perm)
+    pos[perm] = np.arange(perm.size)
+    return dict(counts=counts.astype(np.int32), offsets=offsets.astype(np.int32),
+                perm=perm.astype(np.int32), pos=pos.astype(np.int32))
+
+
+# ---------------------------------------------------------------- experts
+def expert_swiglu(xt: np.ndarray, wg, wu, wd) -> np.ndarray:
+    """One rotated int4 expert on rotated inputs xt [n, 2048] -> [n, 2048]."""
+    g = xt @ wg.T
+    u = xt @ wu.T
+    a = silu(g) * u
+    at = rotate_blocks(a)
+    return at @ wd.T
+
+
+def shared_expert(x: np.ndarray, shared_bits: np.ndarray) -> np.ndarray:
+    """Ungated bf16 SwiGLU of width 1024 on the unrotated input."""
+    sg, su, sd = shared_planes(shared_bits)
+    return (silu(x @ sg.T) * (x @ su.T)) @ sd.T
+
+
+def moe_layer(x_bits, router_bits, expert_blobs, shared_bits, bias=None, tokens=None):
+    """The layer: y = bf16( sum_j w_j * E_{e_j}(x) + S(x) ).
+
+    x_bits: bf16 bits [T, 2048]; router_bits: bf16 bits [256, 2048];
+    expert_blobs(e) -> (code bytes [1572864], scale bits [24576]) in the
+    library layout; shared_bits: bf16 bits [6291456]; bias: fp32 [256] or None.
+    tokens: optional subset of token rows whose expert outputs and y are
+    computed (routing and the sort always cover all T tokens).
+    """
+    x = bf16_to_f64(x_bits)
+    T = x.shape[0]
+    rt = route(x, router_bits, bias)
+    srt = sort_assignments(rt["topk_idx"])
+    rows = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    xt = rotate_blocks(x[rows])
+    routed = np.zeros((rows.size, H), dtype=np.float64)
+    need = {}
+    for r_i, t in enumerate(rows):
+        for j in range(K_TOP):
+            need.setdefault(int(rt["topk_idx"][t, j]), []).append((r_i, j))
+    for e in sorted(need):
+        wg, wu, wd = expert_planes(*expert_blobs(e))
+        lst = need[e]
+        ri = np.array([p[0] for p in lst])
+        jj = np.array([p[1] for p in lst])
+        o = expert_swiglu(xt[ri], wg, wu, wd)
+        w = rt["topk_w"][rows[ri], jj]
+        for n in range(len(lst)):
+            routed[ri[n]] += w[n] * o[n]
+    z = shared_expert(x[rows], shared_bits)
+    y = routed + z
+    out = dict(rt)
+    out.update(srt)
+    out.update(rows=rows, routed=routed, shared=z, y=y, y_bits=f64_to_bf16_bits(y))
+    return out
+
+
+def moe_layer_dense(x_bits, router_bits, expert_blobs, shared_bits, bias=None):
+    """Every expert evaluated, with the gate of non-selected experts set to zero."""
+    x = bf16_to_f64(x_bits)
+    T = x.shape[0]
+    rt = route(x, router_bits, bias)
+    gates = np.zeros((T, E))
+    for t in range(T):
+        gates[t, rt["topk_idx"][t]] = rt["topk_w"][t]
+    xt = rotate_blocks(x)
+    y = shared_expert(x, shared_bits)
+    for e in range(E):
+        wg, wu, wd = expert_planes(*expert_blobs(e))
+        y = y + gates[:, e:e + 1] * expert_swiglu(xt, wg, wu, wd)
+    return dict(y=y, y_bits=f64_to_bf16_bits(y), gates=gates)
+
+
+# ------------------------------------------------------------------ stack
+def rmsnorm(x: np.ndarray) -> np.ndarray:
+    """x / sqrt(mean(x^2) + 1e-6), unit gain, per row."""
+    x = np.asarray(x, dtype=np.float64)
+    return x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + RMS_EPS)
+
+
+def stack_step(resid: np.ndarray, layer_inputs):
+    """x_{l+1} = x_l + moe_l(bf16(rmsnorm(x_l))) over the given layers.
+
+    layer_inputs: list of (router_bits, expert_blobs, shared_bits) per layer.
+    resid: fp32-valued residual [T, 2048] (float64 array holding fp32 values).
+    The layer boundary is bf16 (the library's x and y); the residual is fp32.
+    Returns the final residual and the bf16 inputs of every layer.
+    """
+    x = f32_round(resid)
+    inputs = []
+    for router_bits, blobs, shared_bits in layer_inputs:
+        xin = f64_to_bf16_bits(rmsnorm(x))
+        inputs.append(xin)
+        out = moe_layer(xin, router_bits, blobs, shared_bits)
+        x = f32_round(x + bf16_to_f64(out["y_bits"]))
+    return x, inputs
+
+
+# ------------------------------------------------------- test-only quantizer
+def quantize_rotated(w: np.ndarray):
+    """Rotate a float weight [n, k] on K, then int4-quantise per group of 128.
+
+    The pages state the format (int4 codes, group 128, bf16 scale, fwht128
+    rotation) and its error (11.7% relative Frobenius per expert plane, model
+    card, "Why the linears stay bf16"), not the quantiser.  Reading used here:
+    scale = bf16(absmax / 7) per group, code = clamp(rint(w_rot / scale), -8, 7).
+    Returns (int4 values [n, k], scale bf16 bits [n, k/128]).
+    """
+    w = np.asarray(w, dtype=np.float64)
+    n, k = w.shape
+    wr = rotate_blocks(w)                              # W (I x Hn): the stored basis
+    grp = wr.reshape(n, k // G, G)
+    amax = np.abs(grp).max(axis=2)
+    s_bits = f64_to_bf16_bits(amax / 7.0)
+    s = bf16_to_f64(s_bits)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s[..., None] > 0, grp / s[..., None], 0.0)
+    codes = np.clip(np.rint(q), -8, 7).astype(np.int16).reshape(n, k)
+    return codes, s_bits
+
+
+def unrotated_effective(codes: np.ndarray, s_bits: np.ndarray) -> np.ndarray:
+    """Effective weight in the original basis: (code * scale) (I x Hn)."""
+    w = codes.astype(np.float64) * np.repeat(bf16_to_f64(s_bits), G, axis=1)
+    return rotate_blocks(w)

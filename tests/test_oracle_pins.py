@@ -1,0 +1,430 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test checks one step of the layer against what the pages print, a closed
+form, a textbook identity, an independent library routine (torch), brute force
+on a tiny case, or an independent re-derivation written differently (the
+rotation applied to the weights instead of the activations, a different int4
+decode).  A dropped term, a wrong sign or index, or a transposed operand in
+the oracle fails at least one of them.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import moe_oracle as O
+from tests.conftest import golden_constants
+
+# ------------------------------------------------------------ helpers (tests only)
+def butterfly_fwht(v):
+    """In-place iterative fast Walsh-Hadamard transform on the last axis, normalised.
+
+    Independent of the oracle's matrix construction: log2(n) add/sub stages.
+    """
+    v = np.array(v, dtype=np.float64, copy=True)
+    n = v.shape[-1]
+    h = 1
+    while h < n:
+        shp = v.shape[:-1] + (n // (2 * h), 2, h)
+        w = v.reshape(shp)
+        a = w[..., 0, :].copy()
+        b = w[..., 1, :].copy()
+        w[..., 0, :] = a + b
+        w[..., 1, :] = a - b
+        v = w.reshape(v.shape)
+        h *= 2
+    return v / math.sqrt(n)
+
+
+def rotate_rows_blockwise(w, block=128):
+    shp = w.shape
+    return butterfly_fwht(w.reshape(shp[:-1] + (shp[-1] // block, block))).reshape(shp)
+
+
+def decode_xor(packed, k):
+    """Signed int4 decode via (nibble ^ 8) - 8, indexing bytes by k // 2."""
+    ks = np.arange(k)
+    b = packed[..., ks // 2].astype(np.int16)
+    nib = (b >> (4 * (ks & 1))) & 0xF
+    return (nib ^ 8) - 8
+
+
+def widen(bits):
+    return torch.from_numpy(np.asarray(bits, dtype=np.uint16).astype(np.int32) << 16).view(torch.float32).double()
+
+
+class RandomBlobs:
+    """Fast random expert blobs in the library layout (not the splitmix generator)."""
+
+    def __init__(self, seed, zero_scales=False):
+        self.seed = seed
+        self.zero = zero_scales
+        self.cache = {}
+
+    def __call__(self, e):
+        if e not in self.cache:
+            rng = np.random.default_rng((self.seed, e))
+            codes = rng.integers(0, 256, size=synth.CODE_BYTES_PER_EXPERT, dtype=np.uint8)
+            if self.zero:
+                scales = np.zeros(synth.SCALES_PER_EXPERT, dtype=np.uint16)
+            else:
+                s = np.abs(rng.standard_normal(synth.SCALES_PER_EXPERT)).astype(np.float32) * np.float32(0.01)
+                scales = synth.f32_to_bf16_bits(s)
+            self.cache[e] = (codes, scales)
+        return self.cache[e]
+
+
+def small_layer(seed, T):
+    rng = np.random.default_rng(seed)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((T, 2048)).astype(np.float32))
+    R = synth.f32_to_bf16_bits((rng.standard_normal((256, 2048)) * 0.02).astype(np.float32))
+    S = synth.f32_to_bf16_bits((rng.standard_normal(synth.SHARED_ELEMS) * 0.02).astype(np.float32))
+    return x, R, S
+
+
+# ------------------------------------------------------------------ constants
+def test_layout_constants_match_pages():
+    c = golden_constants()
+    assert c["n_experts"] == O.E == synth.N_EXPERTS
+    assert c["top_k"] == O.K_TOP
+    assert c["group"] == O.G
+    assert c["expert_inter"] == O.I_R
+    assert c["hidden"] == O.H
+    assert c["shared_inter"] == O.I_S
+    assert c["moe_layers"] == synth.N_MOE_LAYERS
+    assert O.WEIGHT_FLOOR == 2.0 ** c["weight_floor_log2"]
+
+
+def test_expert_bytes_closed_form_matches_pages():
+    """1,622,016 B per expert; x 256 x 47 = 18.18 GiB (~18.2 GiB); 37.85 B params (37.8 B)."""
+    c = golden_constants()
+    per_expert = synth.CODE_BYTES_PER_EXPERT + 2 * synth.SCALES_PER_EXPERT
+    assert per_expert == 1_622_016
+    total = per_expert * O.E * synth.N_MOE_LAYERS
+    assert round(total / 2 ** 30, 1) == c["routed_gib"]
+    params = 3 * O.I_R * O.H * O.E * synth.N_MOE_LAYERS
+    assert math.floor(params / 1e8) / 10 == c["routed_params_billion"]
+    # 4 bits per code plus 16 bits per 128 codes
+    assert per_expert * 8 / (3 * O.I_R * O.H) == pytest.approx(4.125)
+
+
+# ------------------------------------------------------------------- numbers
+def test_bf16_rounding_matches_torch_on_fp32_values():
+    rng = np.random.default_rng(1)
+    v = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * np.float32(7.0),
+        (rng.standard_normal(2000) * 1e-39).astype(np.float32),          # subnormals
+        np.array([0.0, -0.0, 1.00390625, 1.01171875, -2.0078125, 3.3e38, 3.4e38, np.inf, -np.inf], dtype=np.float32),
+    ])
+    ours = O.f64_to_bf16_bits(v.astype(np.float64))
+    ref = torch.from_numpy(v).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_bf16_rounding_brute_force_on_fp64_values():
+    """Nearest bf16 by search over all finite bf16 values, ties to the even pattern."""
+    allbits = np.arange(0, 0x7F80, dtype=np.uint16)
+    allvals = O.bf16_to_f64(allbits)
+    rng = np.random.default_rng(2)
+    vals = np.concatenate([rng.standard_normal(300) * 10.0, [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -8 + 2 ** -40]])
+    ours = O.f64_to_bf16_bits(vals)
+    for v, b in zip(vals, ours):
+        d = np.abs(allvals - abs(v))
+        best = np.nonzero(d == d.min())[0]
+        cand = allbits[best]
+        want = cand[0] if len(cand) == 1 else cand[(cand & 1) == 0][0]
+        want = int(want) | (0x8000 if v < 0 else 0)
+        assert int(b) == want, (v, hex(b), hex(want))
+
+
+def test_silu_closed_forms():
+    assert O.silu(0.0) == 0.0
+    assert O.silu(40.0) == pytest.approx(40.0, rel=1e-15)
+    assert abs(O.silu(-40.0)) < 1e-15
+    assert O.silu(1.0) == pytest.approx(1.0 / (1.0 + math.exp(-1.0)))
+    v = np.linspace(-6, 6, 101)
+    np.testing.assert_allclose(O.silu(v), torch.nn.functional.silu(torch.from_numpy(v)).numpy(), rtol=1e-14, atol=1e-15)
+
+
+# ------------------------------------------------------------------- Hadamard
+def test_hadamard_textbook_identities():
+    hn = O.hadamard(128)
+    np.testing.assert_allclose(hn @ hn, np.eye(128), atol=1e-14)
+    np.testing.assert_array_equal(hn, hn.T)
+    i = np.arange(128)
+    pc = np.vectorize(lambda v: bin(int(v)).count("1"))(i[:, None] & i[None, :])
+    np.testing.assert_array_equal(hn * math.sqrt(128), (-1.0) ** pc)
+    np.testing.assert_allclose(hn[0], np.full(128, 1 / math.sqrt(128)))
+
+
+def test_rotation_matches_butterfly():
+    rng = np.random.default_rng(3)
+    v = rng.standard_normal((5, 2048))
+    np.testing.assert_allclose(O.rotate_blocks(v), rotate_rows_blockwise(v), atol=1e-12)
+    a = rng.standard_normal((3, 512))
+    np.testing.assert_allclose(O.rotate_blocks(a), rotate_rows_blockwise(a), atol=1e-12)
+    # sqrt(128) * e_0 of a block maps to all-ones, and back
+    e0 = np.zeros(128)
+    e0[0] = math.sqrt(128)
+    np.testing.assert_allclose(O.rotate_blocks(e0[None])[0], np.ones(128), atol=1e-13)
+
+
+def test_rotation_transparency():
+    """W (x rotated) == (W (I x Hn)) x: the rotated basis is invisible to the product."""
+    rng = np.random.default_rng(4)
+    w = rng.standard_normal((64, 2048))
+    x = rng.standard_normal(2048)
+    lhs = w @ O.rotate_blocks(x[None])[0]
+    rhs = rotate_rows_blockwise(w) @ x
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-11, atol=1e-11)
+
+
+# --------------------------------------------------------------- quantisation
+def test_int4_decode_probe_against_bitwise_reading():
+    blobs = RandomBlobs(5)
+    cb, sb = blobs(3)
+    wg, wu, wd = O.expert_planes(cb, sb)
+    rng = np.random.default_rng(6)
+    nb_gu = 512 * 1024
+    for _ in range(300):
+        plane = int(rng.integers(0, 3))
+        if plane < 2:
+            n, k = int(rng.integers(0, 512)), int(rng.integers(0, 2048))
+            byte = int(cb[plane * nb_gu + n * 1024 + k // 2])
+            sbits = int(sb[plane * 512 * 16 + n * 16 + k // 128])
+            got = (wg, wu)[plane][n, k]
+        else:
+            n, k = int(rng.integers(0, 2048)), int(rng.integers(0, 512))
+            byte = int(cb[2 * nb_gu + n * 256 + k // 2])
+            sbits = int(sb[2 * 512 * 16 + n * 4 + k // 128])
+            got = wd[n, k]
+        nib = (byte >> 4) if (k % 2) else (byte & 0xF)
+        code = nib - 16 if nib & 0x8 else nib
+        scale = np.frombuffer(np.uint32(sbits << 16).tobytes(), dtype=np.float32)[0]
+        assert got == code * float(scale)
+
+
+def test_unpack_matches_xor_decode():
+    rng = np.random.default_rng(7)
+    p = rng.integers(0, 256, size=(7, 64), dtype=np.uint8)
+    np.testing.assert_array_equal(O.unpack_int4(p, 128), decode_xor(p, 128))
+    vals = rng.integers(-8, 8, size=(3, 256)).astype(np.int8)
+    np.testing.assert_array_equal(O.unpack_int4(synth.pack_int4(vals), 256), vals)
+
+
+def test_quantize_roundtrip_within_int4_bound():
+    """rotate -> quantise -> dequantise -> unrotate recovers W within int4 error."""
+    c = golden_constants()
+    rng = np.random.default_rng(8)
+    w = rng.standard_normal((512, 2048))
+    codes, s_bits = O.quantize_rotated(w)
+    assert codes.min() >= -8 and codes.max() <= 7
+    s = np.repeat(O.bf16_to_f64(s_bits), 128, axis=1)
+    w_rot = rotate_rows_blockwise(w)
+    err_rot = w_rot - codes * s
+    assert np.all(np.abs(err_rot) <= s / 2 * (1 + 1e-12))
+    w_back = O.unrotated_effective(codes, s_bits)
+    err = w_back - w
+    # orthogonal rotation: the error norm is the same in both bases
+    assert np.linalg.norm(err) == pytest.approx(np.linalg.norm(err_rot), rel=1e-10)
+    rel = np.linalg.norm(err) / np.linalg.norm(w)
+    # the model card quotes 11.7% per expert plane; Gaussian data lands on it
+    assert abs(rel - c["int4_rel_frobenius"]) < 0.01, rel
+
+
+# ----------------------------------------------------------------------- router
+def _brute_top6(l32):
+    n = l32.shape[0]
+    best = None
+    for sub in itertools.combinations(range(n), 6):
+        s = sum(float(l32[i]) for i in sub)
+        key = (-s, sub)                      # max sum, then lexicographically lowest indices
+        if best is None or key < best[0]:
+            best = (key, sub)
+    sub = best[1]
+    return sorted(sub, key=lambda i: (-l32[i], i))
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_top6_matches_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    n_exp, k = 10, 32
+    x = O.bf16_to_f64(synth.f32_to_bf16_bits(rng.standard_normal((4, k)).astype(np.float32)))
+    R = synth.f32_to_bf16_bits(rng.standard_normal((n_exp, k)).astype(np.float32))
+    rt = O.route(x, R)
+    for t in range(4):
+        assert list(rt["topk_idx"][t]) == _brute_top6(rt["logits32"][t])
+        w = rt["topk_w"][t]
+        assert w.sum() == pytest.approx(1.0, abs=1e-14)
+        sig = 1.0 / (1.0 + np.exp(-rt["logits"][t, rt["topk_idx"][t]]))
+        np.testing.assert_allclose(w, sig / sig.sum(), rtol=1e-14)
+        assert np.all(np.diff(w) <= 0)
+
+
+def test_top6_ties_go_to_lower_index():
+    # integer-valued inputs: exact logits with deliberate ties
+    x = np.array([[1.0, 0.0], [0.0, 0.0]])
+    Rv = np.array([[1, 0], [3, 0], [2, 0], [3, 0], [2, 0], [1, 0], [2, 0], [0, 0], [2, 0], [1, 0]], dtype=np.float32)
+    R = synth.f32_to_bf16_bits(Rv)
+    rt = O.route(x, R)
+    assert list(rt["topk_idx"][0]) == [1, 3, 2, 4, 6, 8]
+    assert list(rt["topk_idx"][0]) == _brute_top6(rt["logits32"][0])
+    # all logits equal: experts 0..5 with weight 1/6 each
+    assert list(rt["topk_idx"][1]) == [0, 1, 2, 3, 4, 5]
+    np.testing.assert_allclose(rt["topk_w"][1], np.full(6, 1 / 6), rtol=1e-15)
+    assert rt["near_tie"][1] and rt["gap"][1] == 0.0
+
+
+def test_router_zero_weights_pick_first_six():
+    x = O.bf16_to_f64(small_layer(9, 3)[0])
+    rt = O.route(x, np.zeros((256, 2048), dtype=np.uint16))
+    assert np.all(rt["topk_idx"] == np.arange(6))
+    np.testing.assert_allclose(rt["topk_w"], 1 / 6)
+
+
+def test_weight_floor():
+    """Scores summing below 2**-14 are divided by the floor, not by their sum."""
+    x, R, _ = small_layer(10, 2)
+    xf = O.bf16_to_f64(x)
+    bias = np.full(256, -30.0, dtype=np.float32)
+    rt = O.route(xf, R, bias)
+    sig = 1.0 / (1.0 + np.exp(-rt["logits"][np.arange(2)[:, None], rt["topk_idx"]]))
+    assert np.all(sig.sum(axis=1) < 2 ** -14)
+    np.testing.assert_allclose(rt["topk_w"], sig * 2 ** 14, rtol=1e-14)
+    # the bias is part of the logit: it shifts selection and weights alike
+    bias2 = np.zeros(256, dtype=np.float32)
+    bias2[[7, 100, 200]] = 50.0
+    rt2 = O.route(xf, R, bias2)
+    assert set(rt2["topk_idx"][0][:3]) == {7, 100, 200}
+
+
+def test_near_tie_flag_uses_the_6th_7th_gap():
+    x, R, _ = small_layer(11, 64)
+    rt = O.route(O.bf16_to_f64(x), R)
+    srt = -np.sort(-rt["logits"], axis=1)
+    np.testing.assert_allclose(rt["gap"], srt[:, 5] - srt[:, 6])
+    np.testing.assert_array_equal(rt["near_tie"], rt["gap"] <= 1e-3)
+
+
+# ------------------------------------------------------------------------- sort
+def test_sort_against_nested_loops():
+    rng = np.random.default_rng(12)
+    T = 37
+    idx = np.stack([rng.choice(256, 6, replace=False) for _ in range(T)]).astype(np.int32)
+    idx[5] = [0, 1, 2, 3, 4, 5]
+    s = O.sort_assignments(idx)
+    perm = []
+    for e in range(256):
+        for t in range(T):
+            for j in range(6):
+                if idx[t, j] == e:
+                    perm.append(6 * t + j)
+    np.testing.assert_array_equal(s["perm"], perm)
+    assert s["offsets"][0] == 0 and s["offsets"][256] == 6 * T
+    for e in range(256):
+        assert s["offsets"][e + 1] - s["offsets"][e] == np.sum(idx == e)
+    np.testing.assert_array_equal(s["perm"][s["pos"]], np.arange(6 * T))
+
+
+# ------------------------------------------------------------------- the layer
+def test_layer_matches_weight_side_recomputation():
+    """Independent route: unrotate the weights (butterfly), decode with XOR, SwiGLU in torch."""
+    x, R, S = small_layer(13, 3)
+    blobs = RandomBlobs(14)
+    out = O.moe_layer(x, R, blobs, S)
+    xt = widen(x)                                              # [T, 2048]
+    logits = xt @ widen(R).T
+    nb_gu = 512 * 1024
+    for t in range(3):
+        l32 = logits[t].float().double().numpy()
+        sel = sorted(range(256), key=lambda i: (-l32[i], i))[:6]
+        sig = torch.sigmoid(logits[t, sel])
+        w = sig / sig.sum()
+        acc = torch.zeros(2048, dtype=torch.float64)
+        for j, e in enumerate(sel):
+            cb, sb = blobs(e)
+            g = decode_xor(cb[:nb_gu].reshape(512, 1024), 2048) * np.repeat(O.bf16_to_f64(sb[:8192].reshape(512, 16)), 128, 1)
+            u = decode_xor(cb[nb_gu:2 * nb_gu].reshape(512, 1024), 2048) * np.repeat(O.bf16_to_f64(sb[8192:16384].reshape(512, 16)), 128, 1)
+            d = decode_xor(cb[2 * nb_gu:].reshape(2048, 256), 512) * np.repeat(O.bf16_to_f64(sb[16384:].reshape(2048, 4)), 128, 1)
+            ge, ue, de = (torch.from_numpy(rotate_rows_blockwise(m)) for m in (g, u, d))
+            h = torch.nn.functional.silu(ge @ xt[t]) * (ue @ xt[t])
+            acc += w[j] * (de @ h)
+        sg = widen(S[:2048 * 1024]).reshape(1024, 2048)
+        su = widen(S[2048 * 1024:4096 * 1024]).reshape(1024, 2048)
+        sd = widen(S[4096 * 1024:]).reshape(2048, 1024)
+        z = sd @ (torch.nn.functional.silu(sg @ xt[t]) * (su @ xt[t]))
+        want = (acc + z).numpy()
+        assert list(out["topk_idx"][t]) == sel
+        np.testing.assert_allclose(out["y"][t], want, rtol=1e-9, atol=1e-9 * np.abs(want).max())
+
+
+def test_zero_scales_reduce_to_shared_expert():
+    x, R, S = small_layer(15, 4)
+    out = O.moe_layer(x, R, RandomBlobs(16, zero_scales=True), S)
+    xt = widen(x)
+    sg = widen(S[:2048 * 1024]).reshape(1024, 2048)
+    su = widen(S[2048 * 1024:4096 * 1024]).reshape(1024, 2048)
+    sd = widen(S[4096 * 1024:]).reshape(2048, 1024)
+    z = (torch.nn.functional.silu(xt @ sg.T) * (xt @ su.T)) @ sd.T
+    np.testing.assert_allclose(out["y"], z.numpy(), rtol=1e-12, atol=1e-12)
+    ref_bits = z.float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    # one rounding from fp64 vs torch's fp64->fp32->bf16: equal except at exact double-rounding cases
+    assert np.mean(out["y_bits"] == ref_bits) > 0.999
+
+
+def test_floor_case_makes_routed_part_vanish():
+    x, R, S = small_layer(17, 2)
+    bias = np.full(256, -30.0, dtype=np.float32)
+    out = O.moe_layer(x, R, RandomBlobs(18), S, bias=bias)
+    assert np.max(np.abs(out["routed"])) < 1e-6 * np.max(np.abs(out["shared"]))
+
+
+def test_dense_all_expert_evaluation_equals_sparse():
+    x, R, S = small_layer(19, 2)
+    blobs = RandomBlobs(20)
+    sparse = O.moe_layer(x, R, blobs, S)
+    dense = O.moe_layer_dense(x, R, blobs, S)
+    np.testing.assert_allclose(sparse["y"], dense["y"], rtol=1e-10, atol=1e-12)
+    assert np.count_nonzero(dense["gates"]) == 2 * 6
+
+
+def test_token_subset_matches_full():
+    x, R, S = small_layer(21, 5)
+    blobs = RandomBlobs(22)
+    full = O.moe_layer(x, R, blobs, S)
+    part = O.moe_layer(x, R, blobs, S, tokens=[4, 1])
+    np.testing.assert_array_equal(part["y"], full["y"][[4, 1]])
+    np.testing.assert_array_equal(part["perm"], full["perm"])
+
+
+# ------------------------------------------------------------------------ stack
+def test_rmsnorm_closed_form():
+    x = np.array([[3.0] * 2048, [-0.5] * 2048])
+    np.testing.assert_allclose(O.rmsnorm(x)[0], 3.0 / math.sqrt(9.0 + 1e-6))
+    np.testing.assert_allclose(O.rmsnorm(x)[1], -0.5 / math.sqrt(0.25 + 1e-6))
+    rng = np.random.default_rng(23)
+    v = rng.standard_normal((3, 2048))
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(v), (2048,), eps=1e-6).numpy()
+    np.testing.assert_allclose(O.rmsnorm(v), ref, rtol=1e-12)
+
+
+def test_stack_with_shared_only_layers():
+    """Zero routed scales: each layer adds bf16(shared(bf16(rmsnorm(x)))) to an fp32 residual."""
+    x0, R, S = small_layer(24, 2)
+    layers = [(R, RandomBlobs(25, zero_scales=True), S), (R, RandomBlobs(26, zero_scales=True), S)]
+    resid0 = O.bf16_to_f64(x0) * 3.0
+    out, inputs = O.stack_step(resid0, layers)
+    r = torch.from_numpy(resid0).float()
+    sg = widen(S[:2048 * 1024]).reshape(1024, 2048)
+    su = widen(S[2048 * 1024:4096 * 1024]).reshape(1024, 2048)
+    sd = widen(S[4096 * 1024:]).reshape(2048, 1024)
+    for _ in range(2):
+        xin = torch.nn.functional.rms_norm(r.double(), (2048,), eps=1e-6).float().to(torch.bfloat16).double()
+        z = (torch.nn.functional.silu(xin @ sg.T) * (xin @ su.T)) @ sd.T
+        r = r + z.float().to(torch.bfloat16).float()
+    # equal up to the rare double-rounding difference of fp64->fp32->bf16
+    np.testing.assert_allclose(out, r.double().numpy(), rtol=1e-2, atol=1e-2)
+    assert np.mean(out == r.double().numpy()) > 0.99
