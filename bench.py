@@ -1,0 +1,210 @@
+"""Throughput of the int4 routed-expert MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu]
+
+A step is one pass of the whole layer (router, sort, rotation, routed experts,
+shared expert, combine) over one batch of seeded synthetic tokens, with
+weights and inputs already resident in HBM.  Consecutive steps use different
+layers' weights (generated on the device from the same seeded recipe), so a
+step cannot be served from the 256 MB Infinity Cache left by the previous one,
+as in a real layer stack.  Prints one JSON line.
+
+The default workload is decode_t32: T = 32 tokens (8 sequences x (1 decoded +
+3 speculative)), x seed 1, weights seed 0.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
+
+EXPERT_GU_BYTES = 1_048_576 + 32_768      # one expert's [gate; up] codes + scales
+EXPERT_D_BYTES = 524_288 + 16_384         # one expert's down codes + scales
+EXPERT_BYTES = EXPERT_GU_BYTES + EXPERT_D_BYTES
+ROUTER_BYTES = 256 * 2048 * 2
+SHARED_BYTES = 3 * 1024 * 2048 * 2
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="decode_t32",
+                    choices=["decode_t1", "decode_t32", "prefill_t2048", "prefill_t2048_skew", "stack_t1", "stack_t8"])
+    ap.add_argument("--layers", type=int, default=0, help="distinct layers rotated through (0 = auto)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, T, x_bits, bias, budget_s):
+    """The CPU oracle as it stands, on a bounded sample of the same workload."""
+    import synth
+    from oracle import moe_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    R = synth.gen_router(0, 0)
+    S = synth.gen_shared(0, 0)
+    # the oracle routes every token; its expert work is timed on a token sample
+    rt = O.route(O.bf16_to_f64(x_bits), R, bias)
+    n_tok = T if T <= 32 else 8
+    tokens = np.arange(n_tok)
+    need = sorted(set(rt["topk_idx"][tokens].ravel().tolist()))
+    blobs = {}
+    for e in need:                               # input preparation, not timed
+        c, s = synth.gen_codes_scales(0, 0, experts=[e])
+        blobs[e] = (c[0], s[0])
+    reps, elapsed = 0, 0.0
+    while elapsed < budget_s and reps < 50:
+        t0 = time.perf_counter()
+        O.moe_layer(x_bits, R, blobs.__getitem__, S, bias=bias, tokens=tokens)
+        elapsed += time.perf_counter() - t0
+        reps += 1
+    per_rep = elapsed / reps
+    return {"value": n_tok / per_rep, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{reps} oracle layer calls on {n_tok} of the {T} tokens (fp64 NumPy, routing of all "
+                      f"{T} tokens included), {per_rep:.2f} s each"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported (the layer needs no "
+              "collective: a multi-GPU deployment replicates it per GPU).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import synth
+    from int4_routed_expert_amd import moe_w4 as m
+
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+    stack = a.config.startswith("stack")
+    if stack:
+        T = 1 if a.config == "stack_t1" else 8
+        n_layers = 47
+        cfg = dict(T=T, x_seed=synth.STACK_SEED, w_seed=synth.STACK_SEED, bias_seed=None)
+    else:
+        cfg = synth.CONFIGS[a.config]
+        T = cfg["T"]
+        n_layers = a.layers or 4
+    log(f"config {a.config}: T={T}, {n_layers} layers on the device")
+    layers = [m.generated_layer(cfg["w_seed"], l) for l in range(n_layers)]
+    x_bits = synth.gen_x(cfg["x_seed"], T)
+    x = torch.from_numpy(x_bits.view(np.int16)).to(dev)
+    bias_np = None if cfg["bias_seed"] is None else synth.skew_bias(cfg["bias_seed"])
+    bias = None if bias_np is None else torch.from_numpy(bias_np).to(dev)
+    y = torch.empty((T, 2048), dtype=torch.int16, device=dev)
+    ws = m.workspace(T)
+    stream = torch.cuda.current_stream()
+    n_pts = m.moe_w4_profile_points()
+    names = [m.moe_w4_profile_point_name(i) for i in range(n_pts)]
+
+    if stack:
+        resid0 = x.view(torch.bfloat16).float()
+        resid = resid0.clone()
+        xb = torch.empty_like(y)
+
+        def step(i, ev=None):
+            for w in layers:
+                m.moe_w4_stack_layer(resid, w["router_w"], w["codes"], w["scales"], w["shared_w"], xb, y, ws)
+    else:
+        def step(i, ev=None):
+            w = layers[i % n_layers]
+            if ev is None:
+                m.moe_w4_forward(x, w["router_w"], w["codes"], w["scales"], w["shared_w"], y, ws, router_bias=bias)
+            else:
+                m.moe_w4_forward_profiled(x, w["router_w"], w["codes"], w["scales"], w["shared_w"], y, ws,
+                                          ev, router_bias=bias)
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    log(f"warmup {a.warmup} done")
+
+    # timed region: exactly K steps; stage events are recorded on the call's stream
+    events = None if stack else m.HipEvents(a.steps * n_pts)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(i, None if events is None else events.handles[i * n_pts:(i + 1) * n_pts])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / a.steps
+    log(f"timed {a.steps} steps: {ms * 1e3:.1f} us/step")
+
+    result = {
+        "metric": "routed-MoE layer tokens/s + % HBM BW (T=1,32) / % bf16 MFMA (T=2048)",
+        "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4 x fp16/bf16 -> fp32", "data": "synthetic (seeded SplitMix64; random-init weights)",
+    }
+    if stack:
+        result["value"] = T / (ms / 1e3)
+        result["config"] = {"workload": f"{a.config}: 47-layer MoE stack, T={T}, seed 4, fp32 residual",
+                            "T": T, "layers": 47, "per_layer_us": ms * 1e3 / 47}
+        print(json.dumps(result), flush=True)
+        return
+
+    # stage times from the events of the timed steps
+    stage_ms = np.zeros(n_pts - 1)
+    for i in range(a.steps):
+        for s in range(n_pts - 1):
+            stage_ms[s] += events.elapsed_ms(i * n_pts + s, i * n_pts + s + 1)
+    stage_ms /= a.steps
+    events.close()
+
+    # routing of the benchmarked layers decides the algorithmic bytes
+    touched = []
+    for l in range(min(n_layers, a.steps)):
+        w = layers[l]
+        m.moe_w4_forward(x, w["router_w"], w["codes"], w["scales"], w["shared_w"], y, ws, router_bias=bias)
+        torch.cuda.synchronize()
+        touched.append(int(m.ws_view(ws, T, "n_active", torch.int32, 1).item()))
+    n_touched = float(np.mean(touched))
+    layer_bytes = n_touched * EXPERT_BYTES + ROUTER_BYTES + SHARED_BYTES + 2 * T * 2048 * 2
+    flops = T * (6 * 3 * 512 * 2048 * 2 + 3 * 1024 * 2048 * 2 + 256 * 2048 * 2)
+    stage = dict(zip(names[1:], stage_ms))
+    dom = max(stage, key=stage.get)
+    dom_bytes = {
+        "routed_gateup": n_touched * EXPERT_GU_BYTES,
+        "routed_down": n_touched * EXPERT_D_BYTES,
+        "shared_gateup": 2 * 1024 * 2048 * 2,
+        "shared_down": 1024 * 2048 * 2,
+        "route": ROUTER_BYTES,
+    }.get(dom, 0.0)
+    achieved = dom_bytes / (stage[dom] * 1e-3) / 1e9
+    result["value"] = T / (ms / 1e3)
+    result["config"] = {"workload": f"{a.config}: one MoE layer, T={T}, x seed {cfg['x_seed']}, weights seed "
+                                    f"{cfg['w_seed']}" + (", +3.0 bias on 26 experts (seed 3)" if bias is not None else ""),
+                        "T": T, "layers_rotated": n_layers, "touched_experts": n_touched}
+    result["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                          "algorithmic_bytes": dom_bytes, "kernel_us": stage[dom] * 1e3}
+    result["layer"] = {"algorithmic_bytes": layer_bytes, "hbm_gbs": layer_bytes / (ms * 1e-3) / 1e9,
+                       "hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                       "tflops": flops / (ms * 1e-3) / 1e12,
+                       "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                       "stage_us": {k: v * 1e3 for k, v in stage.items()}}
+    if not a.no_cpu:
+        log("timing the CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline(cfg, T, x_bits, bias_np, a.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

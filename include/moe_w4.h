@@ -1,0 +1,163 @@
+/*
+ * moe_w4 — the routed mixture-of-experts layer of Flint with four-bit experts,
+ * for one AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * What the layer computes (the pages this follows):
+ *   - Flint model card of the int4-expert container (Aijuus/flint-w4exp),
+ *     introduction and table row "weights": 256 routed experts, top-6, plus an
+ *     ungated shared expert; routed weights are signed int4 codes with one
+ *     bf16 scale per 128 of K, stored in a basis rotated by a 128-wide
+ *     Hadamard transform (fwht128); the shared expert stays bf16.
+ *   - NInfer README of Flint (WaveCut/Flint-UD-Q4_K_XL-NInfer-v3), section
+ *     "What is inside": sigmoid router scores renormalised over the chosen
+ *     experts; per expert, gate rows then up rows (2 x 512) and 2,048 down rows;
+ *     shared expert of width 1024; router rows in fp32 widened from bf16.
+ *   - bloomery issue #632 ("model: Flint ..."), design thread: no router
+ *     correction bias; weights w = score / max(sum of the 6 scores, 2^-14);
+ *     the router hands six (index, fp32 weight) slots to the expert stage.
+ *
+ *   logits = R x (+ bias)         fp32 sums of exact bf16 products
+ *   S      = 6 largest logits, larger first, equal logits -> lower index
+ *   w_j    = sigmoid(l_j) / max(sum_j sigmoid(l_j), 2^-14)
+ *   xr     = H128 applied to every 128-block of x      (H128 = normalised Sylvester Hadamard)
+ *   o_j    = Wd_e H128( silu(Wg_e xr) * (Wu_e xr) ),    W = code * scale[row][k/128]
+ *   z      = Wsd( silu(Wsg x) * (Wsu x) )              (bf16 weights, unrotated)
+ *   y      = bf16_rne( sum_j w_j o_j + z )
+ *
+ * Layouts (row-major, K contiguous; all pointers are device pointers):
+ *   x        bf16 [T][2048]
+ *   router_w bf16 [256][2048]
+ *   codes    u8   [256][1,572,864]: expert e at e*1,572,864 B holds
+ *            gate [512][1024 B], up [512][1024 B], down [2048][256 B];
+ *            element k of a row is the low nibble of byte k/2 when k is even,
+ *            the high nibble when k is odd; two's complement, [-8, 7].
+ *   scales   bf16 [256][24,576]: expert e at element e*24,576 holds
+ *            gate [512][16], up [512][16], down [2048][4]; scale g of a row
+ *            multiplies the codes of K in [128g, 128g+128).
+ *   shared_w bf16, 6,291,456 elements: gate [1024][2048], up [1024][2048],
+ *            down [2048][1024].
+ *   bias     fp32 [256] added to the logits, or NULL (Flint has none).
+ *   y        bf16 [T][2048].
+ *
+ * Ownership and threading: the caller owns every buffer, including the
+ * workspace.  The library allocates no device memory in these calls, keeps no
+ * pointer after the enqueued work completes and holds no mutable global state,
+ * so calls on different streams are independent if they use different
+ * workspaces.  Work is enqueued on `stream` (a hipStream_t passed as void*;
+ * NULL = the default stream) and the call returns without synchronising.
+ *
+ * Errors: arguments are validated before any HIP call.  Asynchronous device
+ * faults surface at the caller's next synchronisation.  No C++ exception
+ * crosses this interface.  Non-finite inputs are not checked.
+ */
+#ifndef MOE_W4_H
+#define MOE_W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_W4_HIDDEN 2048
+#define MOE_W4_EXPERTS 256
+#define MOE_W4_TOPK 6
+#define MOE_W4_INTER 512
+#define MOE_W4_SHARED_INTER 1024
+#define MOE_W4_GROUP 128
+#define MOE_W4_CODE_BYTES_PER_EXPERT 1572864
+#define MOE_W4_SCALES_PER_EXPERT 24576
+#define MOE_W4_SHARED_ELEMS 6291456
+#define MOE_W4_MAX_TOKENS 1048576
+#define MOE_W4_ALIGN 16
+
+/* status codes */
+#define MOE_W4_OK 0
+#define MOE_W4_EINVAL (-1)     /* bad pointer, size, alignment or aliasing      */
+#define MOE_W4_EWORKSPACE (-2) /* workspace_bytes below moe_w4_workspace_bytes */
+#define MOE_W4_EDEVICE (-3)    /* a HIP call or launch failed; see last_device_error */
+
+/* Byte offsets of the routing results and intermediates inside the workspace.
+ * Tests read the routing results through these after a forward call:
+ *   topk_idx  i32 [T][6]  chosen experts, slot order = descending logit
+ *   topk_w    f32 [T][6]  renormalised weights of those slots
+ *   offsets   i32 [257]   offsets[e]..offsets[e+1] = sorted positions of expert e; offsets[256] = 6T
+ *   perm      i32 [6T]    sorted position p -> assignment a = 6t + j, ordered by (expert, a)
+ *   pos       i32 [6T]    inverse of perm
+ *   n_active  i32 [1]     number of experts with at least one token
+ *   active    i32 [256]   those experts, ascending */
+typedef struct moe_w4_ws_layout {
+    size_t logits, topk_idx, topk_w, offsets, perm, pos, n_active, active;
+    size_t xt, xt_scale, act, at, at_scale, hs, o, z, sync;
+    size_t total;
+} moe_w4_ws_layout;
+
+/* Bytes of workspace a forward call over T tokens needs (0 <= T <= MOE_W4_MAX_TOKENS;
+ * returns 0 for an out-of-range T). */
+size_t moe_w4_workspace_bytes(int64_t T);
+
+/* Fills *out with the workspace layout for T tokens.  EINVAL for a NULL out or
+ * an out-of-range T. */
+int moe_w4_workspace_layout(int64_t T, moe_w4_ws_layout *out);
+
+/* One MoE layer over T tokens: y = layer(x).  All pointers 16-byte aligned;
+ * y must not overlap x or the workspace.  T == 0 returns MOE_W4_OK and
+ * enqueues nothing.  Returns MOE_W4_EINVAL / MOE_W4_EWORKSPACE with nothing
+ * enqueued, or MOE_W4_EDEVICE if a launch failed. */
+int moe_w4_forward(const void *x, const void *router_w, const void *codes, const void *scales,
+                   const void *shared_w, int64_t T, void *y, const float *router_bias,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/* Number of timing points moe_w4_forward_profiled records. */
+int moe_w4_profile_points(void);
+/* Name of timing point i (the stage that ends there), or NULL. */
+const char *moe_w4_profile_point_name(int i);
+
+/* moe_w4_forward that also records hipEvent_t events[i] (caller-created, passed
+ * as void*) on `stream` at the stage boundaries: events[0] before the first
+ * stage and events[i] after stage i, for i < moe_w4_profile_points().  The
+ * kernels and results are those of moe_w4_forward. */
+int moe_w4_forward_profiled(const void *x, const void *router_w, const void *codes,
+                            const void *scales, const void *shared_w, int64_t T, void *y,
+                            const float *router_bias, void *workspace, size_t workspace_bytes,
+                            void *stream, void *const *events, int n_events);
+
+/* Seeded synthetic weights of one layer, written on the device with the
+ * counter-based SplitMix64 generator (Steele, Lea and Flood, OOPSLA 2014):
+ *   r(seed, tid, i) = mix64(mix64(seed*G + tid) + (i+1)*G), G = 0x9E3779B97F4A7C15,
+ *   tid = 64*layer + kind (1 router, 2..4 gate/up/down codes, 5..7 their scales,
+ *   8..10 shared gate/up/down); codes = (r >> 60) - 8; "normal" bf16 values are
+ *   bf16_rne(f32(sum of the four 16-bit lanes of r - 131070) * f32(sigma*sqrt(3)/65536))
+ *   with sigma 0.02 for router and shared weights; scales use the absolute
+ *   value with sigma 0.01.  Any output pointer may be NULL to skip it. */
+int moe_w4_generate_layer(uint64_t seed, int layer, void *router_w, void *codes, void *scales,
+                          void *shared_w, void *stream);
+
+/* Seeded x: bf16 [T][2048], sigma 1, tid = 64*layer + 0. */
+int moe_w4_generate_x(uint64_t seed, int layer, int64_t T, void *x, void *stream);
+
+/* One layer of a stack: the caller's residual stream stays fp32.
+ *   x_in = bf16_rne( resid / sqrt(mean(resid^2) + 1e-6) )    (unit-gain RMS norm)
+ *   resid += f32( moe_w4_forward(x_in) )
+ * resid: f32 [T][2048] in/out.  x_buf: bf16 [T][2048] scratch that receives
+ * x_in (the layer input, kept for inspection); y_buf: bf16 [T][2048] scratch
+ * that receives the layer output.  Same validation as moe_w4_forward. */
+int moe_w4_stack_layer(float *resid, const void *router_w, const void *codes, const void *scales,
+                       const void *shared_w, int64_t T, void *x_buf, void *y_buf,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *moe_w4_status_string(int status);
+
+/* The hipError_t behind the last MOE_W4_EDEVICE returned on this thread (0 if none). */
+int moe_w4_last_device_error(void);
+
+/* Library version, major*10000 + minor*100 + patch. */
+int moe_w4_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4_H */

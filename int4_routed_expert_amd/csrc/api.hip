@@ -1,0 +1,292 @@
+// C ABI of the moe_w4 library: validation, workspace layout, launch order.
+// The declarations and their contracts are in include/moe_w4.h.
+#include <math.h>
+#include <string.h>
+
+#include "common.h"
+#include "launch.h"
+#include "moe_w4.h"
+
+using namespace moe_w4;
+
+namespace {
+
+thread_local int g_last_device_error = 0;
+
+constexpr size_t kAlignWs = 256;
+size_t align_up(size_t v) { return (v + kAlignWs - 1) & ~(kAlignWs - 1); }
+
+bool t_in_range(int64_t T) { return T >= 0 && T <= MOE_W4_MAX_TOKENS; }
+
+moe_w4_ws_layout make_layout(int64_t T) {
+    moe_w4_ws_layout L;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off = align_up(off + bytes);
+        return at;
+    };
+    const size_t t = (size_t)T, a = (size_t)kTopK * T;
+    L.logits = take(4 * kE * t);
+    L.topk_idx = take(4 * a);
+    L.topk_w = take(4 * a);
+    L.offsets = take(4 * (kE + 1));
+    L.perm = take(4 * a);
+    L.pos = take(4 * a);
+    L.n_active = take(4);
+    L.active = take(4 * kE);
+    L.xt = take(2 * kH * t);
+    L.xt_scale = take(4 * t);
+    L.act = take(4 * kI * a);
+    L.at = take(2 * kI * a);
+    L.at_scale = take(4 * (kI / kG) * a);
+    L.hs = take(2 * kIS * t);
+    L.o = take(4 * kH * a);
+    L.z = take(4 * kH * t);
+    L.sync = take(4096);
+    L.total = off;
+    return L;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+}
+
+int device_status(hipError_t err) {
+    if (err == hipSuccess) return MOE_W4_OK;
+    g_last_device_error = (int)err;
+    return MOE_W4_EDEVICE;
+}
+
+int validate_forward(const void *x, const void *router_w, const void *codes, const void *scales,
+                     const void *shared_w, int64_t T, const void *y, const float *bias,
+                     const void *ws, size_t ws_bytes) {
+    if (!t_in_range(T)) return MOE_W4_EINVAL;
+    if (T == 0) return MOE_W4_OK;
+    if (!x || !router_w || !codes || !scales || !shared_w || !y || !ws) return MOE_W4_EINVAL;
+    const void *ptrs[] = {x, router_w, codes, scales, shared_w, y, ws};
+    for (const void *p : ptrs)
+        if (!aligned(p, MOE_W4_ALIGN)) return MOE_W4_EINVAL;
+    if (bias && !aligned(bias, 4)) return MOE_W4_EINVAL;
+    if (ws_bytes < make_layout(T).total) return MOE_W4_EWORKSPACE;
+    const size_t act_bytes = (size_t)T * kH * 2;
+    if (overlap(y, act_bytes, x, act_bytes) || overlap(y, act_bytes, ws, ws_bytes)) return MOE_W4_EINVAL;
+    return MOE_W4_OK;
+}
+
+const char *kStageNames[] = {"route", "shared_gateup", "routed_gateup", "rotate_act",
+                             "routed_down", "shared_down", "combine"};
+constexpr int kStages = sizeof(kStageNames) / sizeof(kStageNames[0]);
+
+template <class T_>
+T_ *ws_at(void *ws, size_t off) { return reinterpret_cast<T_ *>(static_cast<char *>(ws) + off); }
+
+int run_forward(const void *x_, const void *router_w_, const void *codes_, const void *scales_,
+                const void *shared_w_, int64_t T64, void *y_, const float *bias, void *ws,
+                hipStream_t s, void *const *events, int n_events) {
+    const int T = (int)T64;
+    const moe_w4_ws_layout L = make_layout(T64);
+    const uint16_t *x = static_cast<const uint16_t *>(x_);
+    const uint16_t *router_w = static_cast<const uint16_t *>(router_w_);
+    const uint8_t *codes = static_cast<const uint8_t *>(codes_);
+    const uint16_t *scales = static_cast<const uint16_t *>(scales_);
+    const uint16_t *shared_w = static_cast<const uint16_t *>(shared_w_);
+    uint16_t *y = static_cast<uint16_t *>(y_);
+
+    float *logits = ws_at<float>(ws, L.logits);
+    int *topk_idx = ws_at<int>(ws, L.topk_idx);
+    float *topk_w = ws_at<float>(ws, L.topk_w);
+    int *offsets = ws_at<int>(ws, L.offsets);
+    int *perm = ws_at<int>(ws, L.perm);
+    int *pos = ws_at<int>(ws, L.pos);
+    int *n_active = ws_at<int>(ws, L.n_active);
+    int *active = ws_at<int>(ws, L.active);
+    uint32_t *xt = ws_at<uint32_t>(ws, L.xt);
+    float *xt_scale = ws_at<float>(ws, L.xt_scale);
+    float *act = ws_at<float>(ws, L.act);
+    uint32_t *at = ws_at<uint32_t>(ws, L.at);
+    float *at_scale = ws_at<float>(ws, L.at_scale);
+    uint16_t *hs = ws_at<uint16_t>(ws, L.hs);
+    float *o = ws_at<float>(ws, L.o);
+    float *z = ws_at<float>(ws, L.z);
+
+    int stage = 0;
+    auto mark = [&](void) -> int {
+        if (events && stage < n_events) {
+            hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[stage]), s);
+            if (e != hipSuccess) return device_status(e);
+        }
+        ++stage;
+        return MOE_W4_OK;
+    };
+    auto check = [&](void) -> int { return device_status(hipGetLastError()); };
+    int rc;
+#define MOE_STEP(call)                        \
+    do {                                      \
+        call;                                 \
+        if ((rc = check()) != MOE_W4_OK) return rc; \
+    } while (0)
+#define MOE_MARK()                            \
+    do {                                      \
+        if ((rc = mark()) != MOE_W4_OK) return rc; \
+    } while (0)
+
+    (void)hipGetLastError();   // clear a stale error so it is not blamed on this call
+    MOE_MARK();
+    MOE_STEP(launch_router_logits(x, router_w, bias, T, logits, s));
+    MOE_STEP(launch_topk_rotate(logits, x, T, topk_idx, topk_w, xt, xt_scale, s));
+    MOE_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, s));
+    MOE_MARK();
+    MOE_STEP(launch_shared_gateup(shared_w, x, T, hs, s));
+    MOE_MARK();
+    MOE_STEP(launch_gateup_gemv(codes, scales, xt, xt_scale, offsets, perm, n_active, active, T, act, s));
+    MOE_MARK();
+    MOE_STEP(launch_rotate_act(act, T, at, at_scale, s));
+    MOE_MARK();
+    MOE_STEP(launch_down_gemv(codes, scales, at, at_scale, offsets, n_active, active, T, o, s));
+    MOE_MARK();
+    MOE_STEP(launch_shared_down(shared_w, hs, T, z, s));
+    MOE_MARK();
+    MOE_STEP(launch_combine(z, o, topk_w, pos, T, y, s));
+    MOE_MARK();
+#undef MOE_STEP
+#undef MOE_MARK
+    return MOE_W4_OK;
+}
+
+uint64_t host_mix64(uint64_t z) {
+    z ^= z >> 30;
+    z *= 0xBF58476D1CE4E5B9ull;
+    z ^= z >> 27;
+    z *= 0x94D049BB133111EBull;
+    z ^= z >> 31;
+    return z;
+}
+uint64_t stream_key(uint64_t seed, int layer, int kind) {
+    return host_mix64(seed * 0x9E3779B97F4A7C15ull + (uint64_t)(64 * (int64_t)layer + kind));
+}
+float normal_mult(double sigma) { return (float)(sigma * sqrt(3.0) / 65536.0); }
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_w4_workspace_bytes(int64_t T) { return t_in_range(T) ? make_layout(T).total : 0; }
+
+int moe_w4_workspace_layout(int64_t T, moe_w4_ws_layout *out) {
+    if (!out || !t_in_range(T)) return MOE_W4_EINVAL;
+    *out = make_layout(T);
+    return MOE_W4_OK;
+}
+
+int moe_w4_forward(const void *x, const void *router_w, const void *codes, const void *scales,
+                   const void *shared_w, int64_t T, void *y, const float *router_bias,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = validate_forward(x, router_w, codes, scales, shared_w, T, y, router_bias, workspace, workspace_bytes);
+    if (rc != MOE_W4_OK || T == 0) return rc;
+    return run_forward(x, router_w, codes, scales, shared_w, T, y, router_bias, workspace,
+                       static_cast<hipStream_t>(stream), nullptr, 0);
+}
+
+int moe_w4_profile_points(void) { return kStages + 1; }
+
+const char *moe_w4_profile_point_name(int i) {
+    if (i == 0) return "start";
+    if (i < 1 || i > kStages) return nullptr;
+    return kStageNames[i - 1];
+}
+
+int moe_w4_forward_profiled(const void *x, const void *router_w, const void *codes,
+                            const void *scales, const void *shared_w, int64_t T, void *y,
+                            const float *router_bias, void *workspace, size_t workspace_bytes,
+                            void *stream, void *const *events, int n_events) {
+    if (n_events < 0 || (n_events > 0 && !events)) return MOE_W4_EINVAL;
+    int rc = validate_forward(x, router_w, codes, scales, shared_w, T, y, router_bias, workspace, workspace_bytes);
+    if (rc != MOE_W4_OK || T == 0) return rc;
+    return run_forward(x, router_w, codes, scales, shared_w, T, y, router_bias, workspace,
+                       static_cast<hipStream_t>(stream), events, n_events);
+}
+
+int moe_w4_generate_layer(uint64_t seed, int layer, void *router_w, void *codes, void *scales,
+                          void *shared_w, void *stream) {
+    if (layer < 0 || layer > (1 << 20)) return MOE_W4_EINVAL;
+    const void *ptrs[] = {router_w, codes, scales, shared_w};
+    for (const void *p : ptrs)
+        if (p && !aligned(p, MOE_W4_ALIGN)) return MOE_W4_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    const float m_w = normal_mult(0.02), m_s = normal_mult(0.01);
+    if (router_w)
+        launch_gen_normal_bf16(stream_key(seed, layer, 1), (int64_t)kE * kH, m_w, 0,
+                               static_cast<uint16_t *>(router_w), s);
+    if (codes) {
+        uint8_t *c = static_cast<uint8_t *>(codes);
+        const int64_t ee = (int64_t)kI * kH;
+        launch_gen_codes(stream_key(seed, layer, 2), kI, kH, kE, ee, kCodeBytesPerExpert, c, s);
+        launch_gen_codes(stream_key(seed, layer, 3), kI, kH, kE, ee, kCodeBytesPerExpert, c + kPlaneGateBytes, s);
+        launch_gen_codes(stream_key(seed, layer, 4), kH, kI, kE, ee, kCodeBytesPerExpert, c + kCodeBytesGu, s);
+    }
+    if (scales) {
+        uint16_t *sc = static_cast<uint16_t *>(scales);
+        launch_gen_scales(stream_key(seed, layer, 5), kH / kG, kI, kE, kScalesPerExpert, m_s, sc, s);
+        launch_gen_scales(stream_key(seed, layer, 6), kH / kG, kI, kE, kScalesPerExpert, m_s, sc + kScalesGate, s);
+        launch_gen_scales(stream_key(seed, layer, 7), kI / kG, kH, kE, kScalesPerExpert, m_s, sc + kScalesGu, s);
+    }
+    if (shared_w) {
+        uint16_t *w = static_cast<uint16_t *>(shared_w);
+        launch_gen_normal_bf16(stream_key(seed, layer, 8), (int64_t)kSharedGateElems, m_w, 0, w, s);
+        launch_gen_normal_bf16(stream_key(seed, layer, 9), (int64_t)kSharedGateElems, m_w, 0, w + kSharedGateElems, s);
+        launch_gen_normal_bf16(stream_key(seed, layer, 10), (int64_t)kSharedGateElems, m_w, 0, w + 2 * kSharedGateElems, s);
+    }
+    return device_status(hipGetLastError());
+}
+
+int moe_w4_generate_x(uint64_t seed, int layer, int64_t T, void *x, void *stream) {
+    if (!t_in_range(T) || layer < 0 || layer > (1 << 20)) return MOE_W4_EINVAL;
+    if (T == 0) return MOE_W4_OK;
+    if (!x || !aligned(x, MOE_W4_ALIGN)) return MOE_W4_EINVAL;
+    (void)hipGetLastError();
+    launch_gen_normal_bf16(stream_key(seed, layer, 0), T * kH, normal_mult(1.0), 0,
+                           static_cast<uint16_t *>(x), static_cast<hipStream_t>(stream));
+    return device_status(hipGetLastError());
+}
+
+int moe_w4_stack_layer(float *resid, const void *router_w, const void *codes, const void *scales,
+                       const void *shared_w, int64_t T, void *x_buf, void *y_buf, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    if (!t_in_range(T)) return MOE_W4_EINVAL;
+    if (T == 0) return MOE_W4_OK;
+    if (!resid || !aligned(resid, MOE_W4_ALIGN)) return MOE_W4_EINVAL;
+    int rc = validate_forward(x_buf, router_w, codes, scales, shared_w, T, y_buf, nullptr, workspace, workspace_bytes);
+    if (rc != MOE_W4_OK) return rc;
+    const size_t rb = (size_t)T * kH * 4, ab = (size_t)T * kH * 2;
+    if (overlap(resid, rb, x_buf, ab) || overlap(resid, rb, y_buf, ab) || overlap(resid, rb, workspace, workspace_bytes))
+        return MOE_W4_EINVAL;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    launch_rmsnorm_bf16(resid, (int)T, static_cast<uint16_t *>(x_buf), s);
+    if ((rc = device_status(hipGetLastError())) != MOE_W4_OK) return rc;
+    rc = run_forward(x_buf, router_w, codes, scales, shared_w, T, y_buf, nullptr, workspace, s, nullptr, 0);
+    if (rc != MOE_W4_OK) return rc;
+    launch_residual_add(resid, static_cast<const uint16_t *>(y_buf), (int)T, s);
+    return device_status(hipGetLastError());
+}
+
+const char *moe_w4_status_string(int status) {
+    switch (status) {
+        case MOE_W4_OK: return "ok";
+        case MOE_W4_EINVAL: return "invalid argument (pointer, size, alignment or aliasing)";
+        case MOE_W4_EWORKSPACE: return "workspace too small";
+        case MOE_W4_EDEVICE: return "HIP launch or runtime call failed";
+        default: return "unknown status";
+    }
+}
+
+int moe_w4_last_device_error(void) { return g_last_device_error; }
+
+int moe_w4_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,137 @@
+// Shared constants and device helpers of the moe_w4 kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe_w4 {
+
+constexpr int kH = 2048;            // model width
+constexpr int kE = 256;             // routed experts
+constexpr int kTopK = 6;            // experts per token
+constexpr int kI = 512;             // routed expert width
+constexpr int kIS = 1024;           // shared expert width
+constexpr int kG = 128;             // K per scale == Hadamard block
+constexpr int kWave = 64;
+
+constexpr size_t kPlaneGateBytes = (size_t)kI * kH / 2;                // 524,288
+constexpr size_t kCodeBytesGu = 2 * kPlaneGateBytes;                   // 1,048,576
+constexpr size_t kCodeBytesPerExpert = kCodeBytesGu + (size_t)kH * kI / 2;  // 1,572,864
+constexpr size_t kScalesGate = (size_t)kI * (kH / kG);                 // 8,192
+constexpr size_t kScalesGu = 2 * kScalesGate;                          // 16,384
+constexpr size_t kScalesPerExpert = kScalesGu + (size_t)kH * (kI / kG);  // 24,576
+constexpr size_t kSharedGateElems = (size_t)kIS * kH;                  // 2,097,152
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf162_t __attribute__((ext_vector_type(2)));
+
+// bf16 halves of a packed 32-bit word, widened exactly to fp32.
+__device__ __forceinline__ float bf16lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ uint32_t pack_half2(float lo, float hi) {
+    _Float16 a = (_Float16)lo, b = (_Float16)hi;   // v_cvt_f16_f32, round to nearest even
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+__device__ __forceinline__ float half_lo(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v & 0xffffu)); }
+__device__ __forceinline__ float half_hi(uint32_t v) { return (float)__builtin_bit_cast(_Float16, (uint16_t)(v >> 16)); }
+
+// v_dot2_f32_f16: acc + a.lo*b.lo + a.hi*b.hi with fp32 accumulation.
+__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(half2_t, a), __builtin_bit_cast(half2_t, b), acc, false);
+}
+// v_dot2_f32_bf16: acc + a.lo*b.lo + a.hi*b.hi (bf16 products are exact in fp32).
+__device__ __forceinline__ float dot2b(uint32_t a, uint32_t b, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf162_t, a), __builtin_bit_cast(bf162_t, b), acc, false);
+}
+
+// ---------------------------------------------------------------------------
+// int4 -> fp16 operands without a per-nibble conversion.
+//
+// Eight signed int4 codes c0..c7 sit in one dword (c_i in bits 4i..4i+3).
+// XOR with 0x88888888 turns each into u_i = c_i + 8 in [0, 15].  OR-ing a
+// nibble into the mantissa of the fp16 1024.0 (0x6400) gives 1024 + u exactly;
+// a nibble in bits 4..7 of a half gives 1024 + 16u.  So four masks give four
+// half2 words, each exact:
+//   q0 = (1024+u0, 1024+u4)   q1 = (1024+16u1, 1024+16u5)
+//   q2 = (1024+u2, 1024+u6)   q3 = (1024+16u3, 1024+16u7)
+// They pair with activations stored as (x0, x4), (x1/16, x5/16), (x2, x6),
+// (x3/16, x7/16).  Then sum(q . xs) = sum_k c_k x_k + 1032*sum_even(xs) + 1152*sum_odd(xs),
+// where xs are the stored fp16 activations; the second part (the "offset") is
+// known per activation slice and is subtracted once, by starting the fp32
+// accumulator at its negative.
+// ---------------------------------------------------------------------------
+struct Q4 { uint32_t q0, q1, q2, q3; };
+
+__device__ __forceinline__ Q4 int4x8_to_q(uint32_t w) {
+    const uint32_t v = w ^ 0x88888888u;
+    const uint32_t t = v >> 8;
+    Q4 r;
+    r.q0 = (v & 0x000f000fu) | 0x64006400u;
+    r.q1 = (v & 0x00f000f0u) | 0x64006400u;
+    r.q2 = (t & 0x000f000fu) | 0x64006400u;
+    r.q3 = (t & 0x00f000f0u) | 0x64006400u;
+    return r;
+}
+
+// Offset of one stored 8-group (four half2 words in the order above).
+__device__ __forceinline__ float q_offset(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
+    const float even = half_lo(x0) + half_hi(x0) + half_lo(x2) + half_hi(x2);
+    const float odd = half_lo(x1) + half_hi(x1) + half_lo(x3) + half_hi(x3);
+    return 1032.0f * even + 1152.0f * odd;
+}
+
+// ---------------------------------------------------------------------------
+// Wave-level helpers (wave64).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_f(v, m);
+    return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, shfl_xor_f(v, m));
+    return v;
+}
+
+// Sum V values over the `span` lanes that differ in the low log2(span) bits of
+// the lane id, leaving value i = (lane & (span-1)) >> (log2(span) - log2(V)) on
+// each lane (V <= span, both powers of two).  Each halving step exchanges half
+// of the remaining values with the partner lane, so the cost is about V
+// shuffles instead of V*log2(span).
+template <int V, int SPAN>
+__device__ __forceinline__ float transpose_reduce(float (&v)[V]) {
+    const int lane = threadIdx.x & (kWave - 1);
+    constexpr int kSteps = __builtin_ctz(V);
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+        const int m = SPAN >> (s + 1);          // partner distance
+        const int half = V >> (s + 1);          // values kept after this step
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int i = 0; i < half; ++i) {
+            const float send = upper ? v[i] : v[i + half];
+            const float keep = upper ? v[i + half] : v[i];
+            v[i] = keep + shfl_xor_f(send, m);
+        }
+    }
+    float r = v[0];
+#pragma unroll
+    for (int m = (SPAN >> kSteps) >> 1; m >= 1; m >>= 1) r += shfl_xor_f(r, m);
+    return r;
+}
+
+}  // namespace moe_w4

@@ -1,0 +1,49 @@
+// Host-side launchers of the moe_w4 kernels (one per kernel family).
+// Every launcher only enqueues on `stream`; the caller checks hipGetLastError.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe_w4 {
+
+// Router: logits[T][256] = x R^T (+ bias).
+void launch_router_logits(const uint16_t *x, const uint16_t *router_w, const float *bias, int T,
+                          float *logits, hipStream_t s);
+// Per token: top-6 of the logits, renormalised sigmoid weights, and the
+// Hadamard-rotated fp16 copy of x (with its power-of-two scale).
+void launch_topk_rotate(const float *logits, const uint16_t *x, int T, int *topk_idx, float *topk_w,
+                        uint32_t *xt, float *xt_scale, hipStream_t s);
+// Stable counting sort of the 6T assignments by expert (one workgroup).
+void launch_sort(const int *topk_idx, int T, int *offsets, int *perm, int *pos, int *n_active,
+                 int *active, hipStream_t s);
+
+// Routed experts, GEMV form (few tokens per expert).
+void launch_gateup_gemv(const uint8_t *codes, const uint16_t *scales, const uint32_t *xt,
+                        const float *xt_scale, const int *offsets, const int *perm,
+                        const int *n_active, const int *active, int T, float *act, hipStream_t s);
+void launch_rotate_act(const float *act, int T, uint32_t *at, float *at_scale, hipStream_t s);
+void launch_down_gemv(const uint8_t *codes, const uint16_t *scales, const uint32_t *at,
+                      const float *at_scale, const int *offsets, const int *n_active,
+                      const int *active, int T, float *o, hipStream_t s);
+
+// Shared expert (bf16 weights).
+void launch_shared_gateup(const uint16_t *shared_w, const uint16_t *x, int T, uint16_t *hs, hipStream_t s);
+void launch_shared_down(const uint16_t *shared_w, const uint16_t *hs, int T, float *z, hipStream_t s);
+
+// y = bf16(z + sum_j w_j o[pos[6t+j]]).
+void launch_combine(const float *z, const float *o, const float *topk_w, const int *pos, int T,
+                    uint16_t *y, hipStream_t s);
+
+// Stack glue: x_bf16 = bf16(rmsnorm(resid)); resid += f32(y).
+void launch_rmsnorm_bf16(const float *resid, int T, uint16_t *x, hipStream_t s);
+void launch_residual_add(float *resid, const uint16_t *y, int T, hipStream_t s);
+
+// Seeded generator.
+void launch_gen_normal_bf16(uint64_t key, int64_t n, float mult, int absval, uint16_t *out, hipStream_t s);
+void launch_gen_codes(uint64_t key, int rows, int k, int experts, int64_t expert_elems,
+                      int64_t expert_stride_bytes, uint8_t *out, hipStream_t s);
+void launch_gen_scales(uint64_t key, int groups_per_row, int rows, int experts, int64_t expert_stride,
+                       float mult, uint16_t *out, hipStream_t s);
+
+}  // namespace moe_w4

@@ -1,0 +1,316 @@
+// Router (sigmoid, top-6, renormalised with a 2^-14 floor), rotation of x,
+// and the stable token->expert counting sort.
+//
+// Follows: bloomery issue #632 ("model: Flint ..."), design thread — unbiased
+// sigmoid router over 256 experts, top-6, weights = score / max(sum, 2^-14),
+// six (index, fp32 weight) slots per token; NInfer README of Flint, section
+// "What is inside" — router rows are bf16 widened exactly to fp32; Flint
+// model card (Aijuus/flint-w4exp), table row "weights" — experts are stored in
+// a fwht128-rotated basis, so x is rotated per 128-block before the experts.
+#include "common.h"
+#include "launch.h"
+
+namespace moe_w4 {
+
+// ---------------------------------------------------------------------------
+// logits[t][e] = sum_k x[t][k] R[e][k] (+ bias[e]), fp32 sums of exact bf16
+// products.  One wave per expert row; lane l owns K [32l, 32l+32).  Four
+// tokens are reduced together with a transposing lane reduction.
+// ---------------------------------------------------------------------------
+constexpr int kRouterExpertsPerBlock = 4;   // one per wave
+constexpr int kRouterTokensPerBlock = 32;
+
+__global__ __launch_bounds__(256) void k_router_logits(const uint16_t *__restrict__ x,
+                                                       const uint16_t *__restrict__ router_w,
+                                                       const float *__restrict__ bias, int T,
+                                                       float *__restrict__ logits) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int e = blockIdx.x * kRouterExpertsPerBlock + wave;
+    const int t0 = blockIdx.y * kRouterTokensPerBlock;
+    const int t1 = min(t0 + kRouterTokensPerBlock, T);
+    const uint4 *rp = reinterpret_cast<const uint4 *>(router_w + (size_t)e * kH + lane * 32);
+    uint32_t r[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint4 v = rp[i];
+        r[4 * i] = v.x; r[4 * i + 1] = v.y; r[4 * i + 2] = v.z; r[4 * i + 3] = v.w;
+    }
+    const float b = bias ? bias[e] : 0.0f;
+    for (int t = t0; t < t1; t += 4) {
+        float acc[4];
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            acc[n] = 0.0f;
+            const int tt = min(t + n, t1 - 1);
+            const uint4 *xp = reinterpret_cast<const uint4 *>(x + (size_t)tt * kH + lane * 32);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint4 v = xp[i];
+                acc[n] = dot2b(r[4 * i], v.x, acc[n]);
+                acc[n] = dot2b(r[4 * i + 1], v.y, acc[n]);
+                acc[n] = dot2b(r[4 * i + 2], v.z, acc[n]);
+                acc[n] = dot2b(r[4 * i + 3], v.w, acc[n]);
+            }
+        }
+        const float sum = transpose_reduce<4, 64>(acc);   // lane holds token index lane >> 4
+        const int n = lane >> 4;
+        if ((lane & 15) == 0 && t + n < t1) logits[(size_t)(t + n) * kE + e] = sum + b;
+    }
+}
+
+void launch_router_logits(const uint16_t *x, const uint16_t *router_w, const float *bias, int T,
+                          float *logits, hipStream_t s) {
+    dim3 grid(kE / kRouterExpertsPerBlock, (T + kRouterTokensPerBlock - 1) / kRouterTokensPerBlock);
+    hipLaunchKernelGGL(k_router_logits, grid, dim3(256), 0, s, x, router_w, bias, T, logits);
+}
+
+// ---------------------------------------------------------------------------
+// Top-6 of one token's 256 logits, one wave per token.  Keys order floats
+// monotonically as unsigned integers; ties go to the lower expert index.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t order_key(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+// (key, e) beats (key2, e2) when the key is larger, or equal with a lower index.
+__device__ __forceinline__ bool beats(uint32_t k, int e, uint32_t k2, int e2) {
+    return k > k2 || (k == k2 && e < e2);
+}
+
+// Normalised 128-point Sylvester Hadamard on a 128-block spread over 4 lanes
+// (lane & 3 selects the 32-element quarter).  Five butterfly stages run inside
+// the lane, the strides 32 and 64 go across lanes.
+__device__ __forceinline__ void fwht128_4lanes(float (&v)[32], int lane) {
+#pragma unroll
+    for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            if ((i & h) == 0) {
+                const float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 1; m <= 2; m <<= 1) {
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const float p = shfl_xor_f(v[i], m);
+            v[i] = upper ? (p - v[i]) : (v[i] + p);
+        }
+    }
+    const float inv = 0.08838834764831845f;   // 1/sqrt(128)
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] *= inv;
+}
+
+// Store 32 consecutive rotated values as fp16 in the operand order of
+// int4x8_to_q: per 8-group (x0,x4) (x1/16,x5/16) (x2,x6) (x3/16,x7/16), after
+// multiplying by 2^-sh (a power-of-two prescale chosen per token or block).
+__device__ __forceinline__ void store_operand32(const float (&v)[32], int sh, uint32_t *dst) {
+    uint32_t w[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const float *q = v + 8 * g;
+        w[4 * g + 0] = pack_half2(ldexpf(q[0], -sh), ldexpf(q[4], -sh));
+        w[4 * g + 1] = pack_half2(ldexpf(q[1], -sh - 4), ldexpf(q[5], -sh - 4));
+        w[4 * g + 2] = pack_half2(ldexpf(q[2], -sh), ldexpf(q[6], -sh));
+        w[4 * g + 3] = pack_half2(ldexpf(q[3], -sh - 4), ldexpf(q[7], -sh - 4));
+    }
+    uint4 *d = reinterpret_cast<uint4 *>(dst);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+}
+
+// Power-of-two prescale: the largest magnitude lands in [2^13, 2^14), well
+// inside fp16, whatever the input scale (the NInfer README of Flint, section
+// "Quality", scales rows by exact powers of two against fp16 overflow).
+__device__ __forceinline__ int prescale_shift(float amax) {
+    if (!(amax > 0.0f) || !isfinite(amax)) return 0;
+    int ex;
+    frexpf(amax, &ex);   // amax = f * 2^ex, f in [0.5, 1)
+    return ex - 14;
+}
+
+__global__ __launch_bounds__(256) void k_topk_rotate(const float *__restrict__ logits,
+                                                     const uint16_t *__restrict__ x, int T,
+                                                     int *__restrict__ topk_idx,
+                                                     float *__restrict__ topk_w,
+                                                     uint32_t *__restrict__ xt,
+                                                     float *__restrict__ xt_scale) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = blockIdx.x * 4 + wave;
+    if (t >= T) return;
+
+    // ---- top-6 ----
+    const float4 lv = reinterpret_cast<const float4 *>(logits + (size_t)t * kE)[lane];
+    uint32_t key[4] = {order_key(lv.x), order_key(lv.y), order_key(lv.z), order_key(lv.w)};
+    unsigned taken = 0;
+    int sel_e[kTopK];
+    float sel_l[kTopK];
+#pragma unroll
+    for (int j = 0; j < kTopK; ++j) {
+        uint32_t bk = 0;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * lane + i;
+            if (!(taken & (1u << i)) && beats(key[i], e, bk, be)) { bk = key[i]; be = e; }
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+            const uint32_t ok = (uint32_t)__shfl_xor((int)bk, m, kWave);
+            const int oe = __shfl_xor(be, m, kWave);
+            if (beats(ok, oe, bk, be)) { bk = ok; be = oe; }
+        }
+        if ((be >> 2) == lane) taken |= 1u << (be & 3);
+        sel_e[j] = be;
+        sel_l[j] = key_value(bk);
+    }
+    float sig[kTopK], ssum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kTopK; ++j) {
+        sig[j] = 1.0f / (1.0f + expf(-sel_l[j]));
+        ssum += sig[j];
+    }
+    const float denom = fmaxf(ssum, 6.103515625e-05f);   // 2^-14
+#pragma unroll
+    for (int j = 0; j < kTopK; ++j) {
+        if (lane == j) {
+            topk_idx[(size_t)t * kTopK + j] = sel_e[j];
+            topk_w[(size_t)t * kTopK + j] = sig[j] / denom;
+        }
+    }
+
+    // ---- rotated x: 16 Hadamard blocks, lane l holds K [32l, 32l+32) ----
+    float v[32];
+    const uint4 *xp = reinterpret_cast<const uint4 *>(x + (size_t)t * kH + lane * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 q = xp[i];
+        v[8 * i + 0] = bf16lo(q.x); v[8 * i + 1] = bf16hi(q.x);
+        v[8 * i + 2] = bf16lo(q.y); v[8 * i + 3] = bf16hi(q.y);
+        v[8 * i + 4] = bf16lo(q.z); v[8 * i + 5] = bf16hi(q.z);
+        v[8 * i + 6] = bf16lo(q.w); v[8 * i + 7] = bf16hi(q.w);
+    }
+    fwht128_4lanes(v, lane);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = wave_max(amax);
+    const int sh = prescale_shift(amax);
+    store_operand32(v, sh, xt + (size_t)t * (kH / 2) + lane * 16);
+    if (lane == 0) xt_scale[t] = ldexpf(1.0f, sh);
+}
+
+void launch_topk_rotate(const float *logits, const uint16_t *x, int T, int *topk_idx, float *topk_w,
+                        uint32_t *xt, float *xt_scale, hipStream_t s) {
+    hipLaunchKernelGGL(k_topk_rotate, dim3((T + 3) / 4), dim3(256), 0, s, logits, x, T, topk_idx,
+                       topk_w, xt, xt_scale);
+}
+
+// ---------------------------------------------------------------------------
+// Stable counting sort of the assignments a = 6t + j by expert, in one
+// workgroup of 16 waves.  Wave w owns a contiguous range of assignments.
+//   1. per-wave histograms;  2. per-(wave, expert) bases = expert offset +
+//   counts of earlier waves;  3. each wave walks its range in order, 64 at a
+//   time, ranking equal experts inside the chunk with ballots.
+// The result depends only on topk_idx: offsets, perm and pos are exact.
+// ---------------------------------------------------------------------------
+constexpr int kSortWaves = 16;
+
+__global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx, int T,
+                                               int *__restrict__ offsets, int *__restrict__ perm,
+                                               int *__restrict__ pos, int *__restrict__ n_active,
+                                               int *__restrict__ active) {
+    __shared__ int cnt[kSortWaves][kE];
+    __shared__ int tot[kE];
+    __shared__ int offs[kE + 1];
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int N = kTopK * T;
+    const int per = ((N + kSortWaves * 64 - 1) / (kSortWaves * 64)) * 64;
+    const int a0 = wave * per, a1 = min(a0 + per, N);
+
+    for (int i = tid; i < kSortWaves * kE; i += blockDim.x) (&cnt[0][0])[i] = 0;
+    __syncthreads();
+    for (int a = a0 + lane; a < a1; a += 64) atomicAdd(&cnt[wave][topk_idx[a]], 1);
+    __syncthreads();
+    if (tid < kE) {
+        int run = 0;
+        for (int w = 0; w < kSortWaves; ++w) {
+            const int c = cnt[w][tid];
+            cnt[w][tid] = run;   // becomes the wave's base inside the expert
+            run += c;
+        }
+        tot[tid] = run;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        // exclusive scan of the 256 totals, 4 per lane, and of the non-empty flags
+        int c[4], f[4], sc = 0, sf = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            c[i] = tot[4 * lane + i];
+            f[i] = c[i] > 0;
+            sc += c[i];
+            sf += f[i];
+        }
+        int ic = sc, jf = sf;   // inclusive scans over lanes
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int pc = __shfl_up(ic, d, kWave);
+            const int pf = __shfl_up(jf, d, kWave);
+            if (lane >= d) { ic += pc; jf += pf; }
+        }
+        int ec = ic - sc, ef = jf - sf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * lane + i;
+            offs[e] = ec;
+            offsets[e] = ec;
+            if (f[i]) active[ef] = e;
+            ec += c[i];
+            ef += f[i];
+        }
+        if (lane == 63) {
+            offs[kE] = ec;
+            offsets[kE] = ec;
+            *n_active = ef;
+        }
+    }
+    __syncthreads();
+    for (int i = tid; i < kSortWaves * kE; i += blockDim.x) (&cnt[0][0])[i] += offs[i % kE];
+    __syncthreads();
+    const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    for (int c0 = a0; c0 < a1; c0 += 64) {
+        const int a = c0 + lane;
+        const bool valid = a < a1;
+        const int e = valid ? topk_idx[a] : 0;
+        uint64_t same = __ballot(valid);
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const uint64_t bal = __ballot((e >> b) & 1);
+            same &= ((e >> b) & 1) ? bal : ~bal;
+        }
+        if (valid) {
+            const int base = cnt[wave][e];
+            const int dest = base + __popcll(same & below);
+            perm[dest] = a;
+            pos[a] = dest;
+            if ((same >> lane) == 1ull) cnt[wave][e] = base + __popcll(same);
+        }
+    }
+}
+
+void launch_sort(const int *topk_idx, int T, int *offsets, int *perm, int *pos, int *n_active,
+                 int *active, hipStream_t s) {
+    hipLaunchKernelGGL(k_sort, dim3(1), dim3(1024), 0, s, topk_idx, T, offsets, perm, pos, n_active,
+                       active);
+}
+
+}  // namespace moe_w4

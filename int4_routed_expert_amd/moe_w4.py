@@ -1,0 +1,221 @@
+"""Python binding of libmoe_w4 (the int4 routed-expert MoE layer for MI355X).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels of
+libmoe_w4.so.  PyTorch supplies device memory and the stream.  The functions
+carry the C names; the contracts are in include/moe_w4.h.  If the library is
+not built, importing this package raises ImportError — there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # loads the HIP runtime that the library then shares
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_w4.so")
+
+HIDDEN = 2048
+EXPERTS = 256
+TOPK = 6
+INTER = 512
+SHARED_INTER = 1024
+GROUP = 128
+CODE_BYTES_PER_EXPERT = 1572864
+SCALES_PER_EXPERT = 24576
+SHARED_ELEMS = 6291456
+MAX_TOKENS = 1048576
+
+OK, EINVAL, EWORKSPACE, EDEVICE = 0, -1, -2, -3
+
+
+class MoeW4Error(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+
+
+class WsLayout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_size_t) for n in (
+        "logits", "topk_idx", "topk_w", "offsets", "perm", "pos", "n_active", "active",
+        "xt", "xt_scale", "act", "at", "at_scale", "hs", "o", "z", "sync", "total")]
+
+    def as_dict(self):
+        return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is not built; run `python -m int4_routed_expert_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _sz, _i64, _int, _u64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_int, ctypes.c_uint64
+_sig = {
+    "moe_w4_workspace_bytes": (_sz, [_i64]),
+    "moe_w4_workspace_layout": (_int, [_i64, ctypes.POINTER(WsLayout)]),
+    "moe_w4_forward": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "moe_w4_profile_points": (_int, []),
+    "moe_w4_profile_point_name": (ctypes.c_char_p, [_int]),
+    "moe_w4_forward_profiled": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp,
+                                       ctypes.POINTER(_vp), _int]),
+    "moe_w4_generate_layer": (_int, [_u64, _int, _vp, _vp, _vp, _vp, _vp]),
+    "moe_w4_generate_x": (_int, [_u64, _int, _i64, _vp, _vp]),
+    "moe_w4_stack_layer": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "moe_w4_status_string": (ctypes.c_char_p, [_int]),
+    "moe_w4_last_device_error": (_int, []),
+    "moe_w4_version": (_int, []),
+}
+for _name, (_res, _args) in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.restype = _res
+    _f.argtypes = _args
+
+EXPORTED = tuple(_sig)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status, what):
+    if status != OK:
+        raise MoeW4Error(status, what)
+
+
+def status_string(status: int) -> str:
+    return _lib.moe_w4_status_string(status).decode()
+
+
+moe_w4_status_string = status_string
+
+
+def moe_w4_version() -> int:
+    return _lib.moe_w4_version()
+
+
+def moe_w4_last_device_error() -> int:
+    return _lib.moe_w4_last_device_error()
+
+
+def moe_w4_workspace_bytes(T: int) -> int:
+    return _lib.moe_w4_workspace_bytes(T)
+
+
+def moe_w4_workspace_layout(T: int) -> dict:
+    lay = WsLayout()
+    _check(_lib.moe_w4_workspace_layout(T, ctypes.byref(lay)), "moe_w4_workspace_layout")
+    return lay.as_dict()
+
+
+def moe_w4_forward(x, router_w, codes, scales, shared_w, y, workspace, router_bias=None, stream=None,
+                   T=None) -> int:
+    """y <- layer(x).  Tensors on the GPU; returns the status (raises on error)."""
+    T = x.shape[0] if T is None else T
+    st = _lib.moe_w4_forward(_ptr(x), _ptr(router_w), _ptr(codes), _ptr(scales), _ptr(shared_w), T,
+                             _ptr(y), _ptr(router_bias), _ptr(workspace),
+                             workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "moe_w4_forward")
+    return st
+
+
+def moe_w4_profile_points() -> int:
+    return _lib.moe_w4_profile_points()
+
+
+def moe_w4_profile_point_name(i: int):
+    r = _lib.moe_w4_profile_point_name(i)
+    return None if r is None else r.decode()
+
+
+def moe_w4_forward_profiled(x, router_w, codes, scales, shared_w, y, workspace, events,
+                            router_bias=None, stream=None) -> int:
+    """moe_w4_forward recording raw hipEvent_t handles (ints) at the stage boundaries."""
+    arr = (_vp * len(events))(*events)
+    st = _lib.moe_w4_forward_profiled(_ptr(x), _ptr(router_w), _ptr(codes), _ptr(scales), _ptr(shared_w),
+                                      x.shape[0], _ptr(y), _ptr(router_bias), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream),
+                                      arr, len(events))
+    _check(st, "moe_w4_forward_profiled")
+    return st
+
+
+def moe_w4_generate_layer(seed, layer, router_w=None, codes=None, scales=None, shared_w=None, stream=None):
+    _check(_lib.moe_w4_generate_layer(seed, layer, _ptr(router_w), _ptr(codes), _ptr(scales), _ptr(shared_w),
+                                      _stream(stream)), "moe_w4_generate_layer")
+
+
+def moe_w4_generate_x(seed, layer, x, stream=None):
+    _check(_lib.moe_w4_generate_x(seed, layer, x.shape[0], _ptr(x), _stream(stream)), "moe_w4_generate_x")
+
+
+def moe_w4_stack_layer(resid, router_w, codes, scales, shared_w, x_buf, y_buf, workspace, stream=None):
+    _check(_lib.moe_w4_stack_layer(_ptr(resid), _ptr(router_w), _ptr(codes), _ptr(scales), _ptr(shared_w),
+                                   resid.shape[0], _ptr(x_buf), _ptr(y_buf), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream)),
+           "moe_w4_stack_layer")
+
+
+# ---------------------------------------------------------------- allocation helpers
+def empty_layer(device="cuda"):
+    """Uninitialised device tensors of one layer in the library layout (as raw integer dtypes)."""
+    return dict(
+        router_w=torch.empty((EXPERTS, HIDDEN), dtype=torch.int16, device=device),
+        codes=torch.empty((EXPERTS, CODE_BYTES_PER_EXPERT), dtype=torch.uint8, device=device),
+        scales=torch.empty((EXPERTS, SCALES_PER_EXPERT), dtype=torch.int16, device=device),
+        shared_w=torch.empty((SHARED_ELEMS,), dtype=torch.int16, device=device),
+    )
+
+
+def generated_layer(seed, layer=0, device="cuda"):
+    w = empty_layer(device)
+    moe_w4_generate_layer(seed, layer, w["router_w"], w["codes"], w["scales"], w["shared_w"])
+    return w
+
+
+def workspace(T, device="cuda"):
+    return torch.empty((max(moe_w4_workspace_bytes(T), 1),), dtype=torch.uint8, device=device)
+
+
+def ws_view(ws, T, name, dtype, count):
+    """A typed view of one workspace region (for reading routing results)."""
+    off = moe_w4_workspace_layout(T)[name]
+    nbytes = count * torch.empty((), dtype=dtype).element_size()
+    return ws[off:off + nbytes].view(dtype)
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime torch loaded (for forward_profiled)."""
+
+    def __init__(self, n):
+        self._hip = ctypes.CDLL("libamdhip64.so.7")
+        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(_vp)]
+        self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _vp, _vp]
+        self._hip.hipEventDestroy.argtypes = [_vp]
+        self.handles = []
+        for _ in range(n):
+            h = _vp()
+            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles.append(h.value)
+
+    def elapsed_ms(self, i, j):
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.handles[i], self.handles[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self):
+        for h in self.handles:
+            self._hip.hipEventDestroy(h)
+        self.handles = []

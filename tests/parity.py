@@ -1,0 +1,119 @@
+"""Parity helpers: run the HIP layer and the CPU oracle on the same seeded
+inputs and compare them to the stated bar.
+
+Bar (the layer's stated contract):
+  * expert indices (topk_idx) equal, for every token whose oracle 6th/7th
+    logit gap exceeds 1e-3 (near-ties are flagged and counted, not failed);
+  * offsets and perm bit-exact when no flagged token is routed differently;
+    otherwise offsets must equal the histogram of the GPU's own indices and
+    perm must be the stable sort of those indices;
+  * topk_w within 1e-5 relative of the oracle's (fp32 sigmoid vs fp64);
+  * y (bf16): max |y_gpu - y_oracle| <= 2e-2 * rms(y_oracle), over the tokens
+    routed identically.
+"""
+from __future__ import annotations
+
+import functools
+
+import numpy as np
+import torch
+
+import synth
+from oracle import moe_oracle as O
+
+Y_TOL = 2e-2
+W_RTOL = 1e-5
+
+
+@functools.lru_cache(maxsize=None)
+def _host_expert(seed, layer, e):
+    codes, scales = synth.gen_codes_scales(seed, layer, experts=[e])
+    return codes[0], scales[0]
+
+
+def host_blobs(seed, layer=0, scale_mult_log2=0):
+    def blobs(e):
+        c, s = _host_expert(seed, layer, e)
+        if scale_mult_log2:
+            f = O.bf16_to_f64(s) * 2.0 ** scale_mult_log2
+            s = O.f64_to_bf16_bits(f)
+        return c, s
+    return blobs
+
+
+@functools.lru_cache(maxsize=None)
+def host_router(seed, layer=0):
+    return synth.gen_router(seed, layer)
+
+
+@functools.lru_cache(maxsize=None)
+def host_shared(seed, layer=0):
+    return synth.gen_shared(seed, layer)
+
+
+def to_dev_u16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+
+def from_dev_u16(t):
+    return t.cpu().numpy().view(np.uint16)
+
+
+def run_gpu(m, x_bits, w, bias=None, ws=None, poison=False):
+    """Run one forward; returns y bits and the routing results read from the workspace."""
+    T = x_bits.shape[0]
+    x = to_dev_u16(x_bits)
+    y = torch.empty((T, 2048), dtype=torch.int16, device="cuda")
+    if ws is None:
+        ws = m.workspace(T)
+    if poison:
+        ws.fill_(0xFF)
+    b = None if bias is None else torch.from_numpy(np.asarray(bias, dtype=np.float32)).cuda()
+    m.moe_w4_forward(x, w["router_w"], w["codes"], w["scales"], w["shared_w"], y, ws, router_bias=b)
+    torch.cuda.synchronize()
+    out = dict(y_bits=from_dev_u16(y))
+    out["topk_idx"] = m.ws_view(ws, T, "topk_idx", torch.int32, 6 * T).cpu().numpy().reshape(T, 6)
+    out["topk_w"] = m.ws_view(ws, T, "topk_w", torch.float32, 6 * T).cpu().numpy().reshape(T, 6)
+    out["offsets"] = m.ws_view(ws, T, "offsets", torch.int32, 257).cpu().numpy()
+    out["perm"] = m.ws_view(ws, T, "perm", torch.int32, 6 * T).cpu().numpy()
+    out["pos"] = m.ws_view(ws, T, "pos", torch.int32, 6 * T).cpu().numpy()
+    out["n_active"] = int(m.ws_view(ws, T, "n_active", torch.int32, 1).cpu().numpy()[0])
+    out["active"] = m.ws_view(ws, T, "active", torch.int32, 256).cpu().numpy()
+    return out
+
+
+def compare(gpu, ref, tokens=None, label=""):
+    """Check the bar; returns a summary dict.  `tokens`: rows of ref['y'] (None = all)."""
+    T = gpu["topk_idx"].shape[0]
+    flagged = ref["near_tie"]
+    same_route = np.all(gpu["topk_idx"] == ref["topk_idx"], axis=1)
+    bad = ~same_route & ~flagged
+    assert not bad.any(), f"{label}: routing differs on unflagged tokens {np.nonzero(bad)[0][:10]}"
+    ok = same_route
+    np.testing.assert_allclose(gpu["topk_w"][ok], ref["topk_w"][ok], rtol=W_RTOL, atol=1e-7,
+                               err_msg=f"{label}: topk_w")
+    # sort results
+    if same_route.all():
+        np.testing.assert_array_equal(gpu["offsets"], ref["offsets"], err_msg=f"{label}: offsets")
+        np.testing.assert_array_equal(gpu["perm"], ref["perm"], err_msg=f"{label}: perm")
+        np.testing.assert_array_equal(gpu["pos"], ref["pos"], err_msg=f"{label}: pos")
+    else:
+        own = O.sort_assignments(gpu["topk_idx"])
+        for k in ("offsets", "perm", "pos"):
+            np.testing.assert_array_equal(gpu[k], own[k], err_msg=f"{label}: {k} vs the GPU's own indices")
+    counts = np.diff(gpu["offsets"])
+    act = np.nonzero(counts)[0]
+    assert gpu["n_active"] == len(act)
+    np.testing.assert_array_equal(gpu["active"][:len(act)], act)
+    # output
+    rows = np.arange(T) if tokens is None else np.asarray(tokens)
+    yr = ref["y"]                                      # fp64, rows = `rows`
+    yg = O.bf16_to_f64(gpu["y_bits"][rows])
+    keep = ok[rows]
+    rms = float(np.sqrt(np.mean(yr ** 2)))
+    err = np.abs(yg[keep] - yr[keep])
+    max_err = float(err.max()) if err.size else 0.0
+    assert np.all(np.isfinite(yg[keep])), f"{label}: non-finite output"
+    assert max_err <= Y_TOL * rms, f"{label}: max|err| {max_err:.3e} > {Y_TOL} * rms {rms:.3e}"
+    return dict(T=T, flagged=int(flagged.sum()), rerouted=int((~same_route).sum()),
+                max_err=max_err, rms=rms, ratio=max_err / rms if rms else 0.0)

@@ -1,0 +1,123 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and
+rejects bad arguments with the documented status before any HIP call."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from tests.conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "moe_w4.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_w4_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def m():
+    from int4_routed_expert_amd import moe_w4
+    return moe_w4
+
+
+def test_every_declared_symbol_is_exported(m):
+    names = declared_functions()
+    assert len(names) >= 10
+    out = subprocess.run(["nm", "-D", "--defined-only", m.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (moe_w4_\w+)", out))
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    lib = ctypes.CDLL(m.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n)
+    assert set(m.EXPORTED) == set(names)
+
+
+def test_workspace_layout(m):
+    assert m.moe_w4_workspace_bytes(-1) == 0
+    assert m.moe_w4_workspace_bytes(m.MAX_TOKENS + 1) == 0
+    for T in (0, 1, 7, 32, 2048):
+        lay = m.moe_w4_workspace_layout(T)
+        assert lay["total"] == m.moe_w4_workspace_bytes(T)
+        offs = sorted((v, k) for k, v in lay.items() if k != "total")
+        for (a, _), (b, _) in zip(offs, offs[1:]):
+            assert a <= b
+        assert all(v % 256 == 0 for v in lay.values())
+        # regions are large enough for what the header says they hold
+        assert lay["topk_w"] - lay["topk_idx"] >= 4 * 6 * T
+        assert lay["perm"] - lay["offsets"] >= 4 * 257
+    with pytest.raises(m.MoeW4Error):
+        m.moe_w4_workspace_layout(-5)
+
+
+class FakeBuf:
+    """Stands in for a device tensor: only an address and a size are used."""
+
+    def __init__(self, addr, nbytes=1 << 40):
+        self.addr, self.nbytes = addr, nbytes
+
+    def data_ptr(self):
+        return self.addr
+
+    def numel(self):
+        return self.nbytes
+
+    def element_size(self):
+        return 1
+
+
+class FakeX(FakeBuf):
+    def __init__(self, addr, T):
+        super().__init__(addr)
+        self.shape = (T, 2048)
+
+
+def call(m, T, x=0x10000000, r=0x20000000, c=0x30000000, s=0x40000000, sh=0x50000000, y=0x60000000,
+         bias=None, ws=0x70000000, ws_bytes=None):
+    lib = m._lib
+    if ws_bytes is None:
+        ws_bytes = m.moe_w4_workspace_bytes(max(T, 0)) if 0 <= T <= m.MAX_TOKENS else 1 << 30
+    return lib.moe_w4_forward(x, r, c, s, sh, T, y, bias, ws, ws_bytes, None)
+
+
+def test_validation_codes_without_device(m):
+    assert call(m, 0) == m.OK                         # T == 0: nothing enqueued
+    assert call(m, -1) == m.EINVAL
+    assert call(m, m.MAX_TOKENS + 1) == m.EINVAL
+    for k in ("x", "r", "c", "s", "sh", "y", "ws"):
+        assert call(m, 4, **{k: None}) == m.EINVAL, k
+        assert call(m, 4, **{k: 0x10000008 + 0x1000000}) == m.EINVAL, k    # misaligned
+    assert call(m, 4, bias=0x80000002) == m.EINVAL
+    assert call(m, 4, ws_bytes=m.moe_w4_workspace_bytes(4) - 1) == m.EWORKSPACE
+    assert call(m, 4, y=0x10000000 + 4096) == m.EINVAL                       # y overlaps x
+    assert call(m, 4, y=0x70000000 + 256) == m.EINVAL                        # y overlaps the workspace
+    assert m.moe_w4_last_device_error() == 0
+
+
+def test_profiled_and_stack_validation(m):
+    lib = m._lib
+    ev = (ctypes.c_void_p * 1)()
+    assert lib.moe_w4_forward_profiled(0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 4, 0x6000, None, 0x7000, 1 << 30, None, ev, -1) == m.EINVAL
+    assert lib.moe_w4_forward_profiled(0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 4, 0x6000, None, 0x7000, 1 << 30, None, None, 2) == m.EINVAL
+    assert lib.moe_w4_forward_profiled(None, 0x2000, 0x3000, 0x4000, 0x5000, 4, 0x6000, None, 0x7000, 1 << 30, None, ev, 1) == m.EINVAL
+    assert lib.moe_w4_stack_layer(None, 0x2000, 0x3000, 0x4000, 0x5000, 4, 0x6000, 0x7000, 0x8000, 1 << 30, None) == m.EINVAL
+    assert lib.moe_w4_stack_layer(0x100000, 0x2000, 0x3000, 0x4000, 0x5000, 0, 0x6000, 0x7000, 0x8000, 0, None) == m.OK
+    # residual overlapping the x buffer
+    assert lib.moe_w4_stack_layer(0x6000, 0x2000, 0x3000, 0x4000, 0x5000, 4, 0x6000, 0x7000000, 0x8000000, 1 << 30, None) == m.EINVAL
+    assert lib.moe_w4_generate_x(0, 0, -1, 0x1000, None) == m.EINVAL
+    assert lib.moe_w4_generate_x(0, 0, 4, 0x1001, None) == m.EINVAL
+    assert lib.moe_w4_generate_layer(0, -1, None, None, None, None, None) == m.EINVAL
+    assert lib.moe_w4_generate_layer(0, 0, 0x1002, None, None, None, None) == m.EINVAL
+
+
+def test_status_strings(m):
+    for st in (m.OK, m.EINVAL, m.EWORKSPACE, m.EDEVICE):
+        assert m.status_string(st)
+    assert m.status_string(42) == "unknown status"
+    assert m.moe_w4_profile_points() == len([m.moe_w4_profile_point_name(i) for i in range(m.moe_w4_profile_points())])
+    assert m.moe_w4_profile_point_name(0) == "start"
+    assert m.moe_w4_profile_point_name(99) is None

@@ -1,0 +1,227 @@
+"""HIP layer vs the CPU oracle, through the C ABI, on seeded synthetic inputs.
+
+Sizes: small and ragged T that the oracle finishes in seconds (tiles and tails
+of every kernel), the four single-layer workloads at full size (T = 1, 32,
+2048 uniform, 2048 skewed) with the oracle on sampled tokens for T = 2048,
+edge cases (one expert taking every token, all-tie router, the 2^-14 floor,
+large and tiny magnitudes, T = 0), and invariants (determinism, batch
+invariance, a poisoned workspace, the device generator against the host one).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import moe_oracle as O
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def m():
+    from int4_routed_expert_amd import moe_w4
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return moe_w4
+
+
+@pytest.fixture(scope="module")
+def layer0(m):
+    w = m.generated_layer(0, 0)
+    torch.cuda.synchronize()
+    return w
+
+
+def oracle_layer(x_bits, bias=None, tokens=None, seed=0, layer=0, scale_log2=0, router=None):
+    R = P.host_router(seed, layer) if router is None else router
+    return O.moe_layer(x_bits, R, P.host_blobs(seed, layer, scale_log2), P.host_shared(seed, layer),
+                       bias=bias, tokens=tokens)
+
+
+def report(label, s):
+    print(f"[parity] {label}: T={s['T']} flagged={s['flagged']} rerouted={s['rerouted']} "
+          f"max_err/rms={s['ratio']:.2e}", flush=True)
+
+
+# ------------------------------------------------------------------ generator
+def test_device_generator_matches_host(m, layer0):
+    rng = np.random.default_rng(0)
+    R = P.from_dev_u16(layer0["router_w"]).reshape(256, 2048)
+    np.testing.assert_array_equal(R, P.host_router(0, 0))
+    S = P.from_dev_u16(layer0["shared_w"])
+    np.testing.assert_array_equal(S, P.host_shared(0, 0))
+    codes = layer0["codes"]
+    scales = layer0["scales"]
+    for e in [0, 1, 77, 200, 255]:
+        hc, hs = P._host_expert(0, 0, e)
+        np.testing.assert_array_equal(codes[e].cpu().numpy(), hc, err_msg=f"codes of expert {e}")
+        np.testing.assert_array_equal(scales[e].cpu().numpy().view(np.uint16), hs, err_msg=f"scales of expert {e}")
+    # x of another seed/layer, and a second layer's tensors at sampled indices
+    for seed, layer, T in [(1, 0, 32), (4, 3, 5)]:
+        x = torch.empty((T, 2048), dtype=torch.int16, device="cuda")
+        m.moe_w4_generate_x(seed, layer, x)
+        np.testing.assert_array_equal(P.from_dev_u16(x), synth.gen_x(seed, T, layer))
+    w = m.empty_layer()
+    m.moe_w4_generate_layer(4, 46, w["router_w"], w["codes"], w["scales"], w["shared_w"])
+    e = int(rng.integers(0, 256))
+    hc, hs = synth.gen_codes_scales(4, 46, experts=[e])
+    np.testing.assert_array_equal(w["codes"][e].cpu().numpy(), hc[0])
+    np.testing.assert_array_equal(w["scales"][e].cpu().numpy().view(np.uint16), hs[0])
+    np.testing.assert_array_equal(P.from_dev_u16(w["router_w"]).reshape(256, 2048), synth.gen_router(4, 46))
+
+
+# ---------------------------------------------------------------- small / ragged
+@pytest.mark.parametrize("T", [1, 2, 3, 5, 7, 16, 31, 33, 63, 65])
+def test_layer_small_T(m, layer0, T):
+    x = synth.gen_x(100 + T, T)
+    g = P.run_gpu(m, x, layer0)
+    ref = oracle_layer(x)
+    report(f"small T={T}", P.compare(g, ref, label=f"T={T}"))
+
+
+# ------------------------------------------------------------- the workloads
+@pytest.mark.parametrize("name", ["decode_t1", "decode_t32"])
+def test_decode_workloads(m, layer0, name):
+    cfg = synth.CONFIGS[name]
+    x = synth.gen_x(cfg["x_seed"], cfg["T"])
+    g = P.run_gpu(m, x, layer0)
+    ref = oracle_layer(x)
+    report(name, P.compare(g, ref, label=name))
+
+
+@pytest.mark.parametrize("name", ["prefill_t2048", "prefill_t2048_skew"])
+def test_prefill_workloads_sampled(m, layer0, name):
+    cfg = synth.CONFIGS[name]
+    T = cfg["T"]
+    x = synth.gen_x(cfg["x_seed"], T)
+    bias = None if cfg["bias_seed"] is None else synth.skew_bias(cfg["bias_seed"])
+    g = P.run_gpu(m, x, layer0, bias=bias)
+    rng = np.random.default_rng(7)
+    tokens = np.unique(np.concatenate([[0, 1, T - 1], rng.choice(T, 13, replace=False)]))
+    ref = oracle_layer(x, bias=bias, tokens=tokens)
+    s = P.compare(g, ref, tokens=tokens, label=name)
+    report(name, s)
+    if bias is not None:
+        hot = synth.skew_experts(cfg["bias_seed"])
+        share = np.isin(g["topk_idx"], hot).mean()
+        print(f"[parity] {name}: share of assignments on the 26 biased experts = {share:.4f}", flush=True)
+        assert share > 0.5
+
+
+# ----------------------------------------------------------------- edge cases
+def test_one_expert_takes_every_token(m, layer0):
+    T = 40
+    x = synth.gen_x(200, T)
+    bias = np.zeros(256, dtype=np.float32)
+    bias[17] = 100.0
+    g = P.run_gpu(m, x, layer0, bias=bias)
+    assert np.all(g["topk_idx"][:, 0] == 17)
+    assert g["offsets"][18] - g["offsets"][17] == T
+    report("one hot expert", P.compare(g, oracle_layer(x, bias=bias), label="one hot expert"))
+
+
+def test_all_tie_router(m, layer0):
+    T = 9
+    x = synth.gen_x(201, T)
+    w = dict(layer0)
+    w["router_w"] = torch.zeros_like(layer0["router_w"])
+    g = P.run_gpu(m, x, w)
+    assert np.all(g["topk_idx"] == np.arange(6))
+    np.testing.assert_allclose(g["topk_w"], 1 / 6, rtol=1e-6)
+    ref = oracle_layer(x, router=np.zeros((256, 2048), dtype=np.uint16))
+    report("all-tie router", P.compare(g, ref, label="all-tie router"))
+
+
+def test_weight_floor(m, layer0):
+    T = 5
+    x = synth.gen_x(202, T)
+    bias = np.full(256, -30.0, dtype=np.float32)
+    g = P.run_gpu(m, x, layer0, bias=bias)
+    ref = oracle_layer(x, bias=bias)
+    assert np.all(ref["topk_w"].sum(axis=1) < 1e-6)
+    report("weight floor", P.compare(g, ref, label="weight floor"))
+
+
+@pytest.mark.parametrize("x_log2,s_log2", [(12, 10), (-20, 0), (0, -12)])
+def test_magnitudes(m, layer0, x_log2, s_log2):
+    """Power-of-two scalings (exact in bf16) of x and of the routed scales."""
+    T = 6
+    xf = O.bf16_to_f64(synth.gen_x(203, T)) * 2.0 ** x_log2
+    x = O.f64_to_bf16_bits(xf)
+    w = dict(layer0)
+    if s_log2:
+        sc = layer0["scales"].view(torch.bfloat16).float() * 2.0 ** s_log2
+        w["scales"] = sc.to(torch.bfloat16).view(torch.int16)
+    g = P.run_gpu(m, x, w)
+    ref = oracle_layer(x, scale_log2=s_log2)
+    report(f"magnitude x*2^{x_log2} s*2^{s_log2}", P.compare(g, ref, label="magnitudes"))
+
+
+def test_zero_tokens_is_a_noop(m, layer0):
+    ws = m.workspace(1)
+    x = torch.empty((0, 2048), dtype=torch.int16, device="cuda")
+    y = torch.full((1, 2048), 7, dtype=torch.int16, device="cuda")
+    m.moe_w4_forward(x, layer0["router_w"], layer0["codes"], layer0["scales"], layer0["shared_w"], y, ws, T=0)
+    torch.cuda.synchronize()
+    assert torch.all(y == 7)
+
+
+# ----------------------------------------------------------------- invariants
+def test_determinism_and_poisoned_workspace(m, layer0):
+    x = synth.gen_x(300, 48)
+    a = P.run_gpu(m, x, layer0)
+    b = P.run_gpu(m, x, layer0, poison=True)
+    np.testing.assert_array_equal(a["y_bits"], b["y_bits"])
+    np.testing.assert_array_equal(a["perm"], b["perm"])
+
+
+def test_batch_invariance(m, layer0):
+    x = synth.gen_x(301, 16)
+    full = P.run_gpu(m, x, layer0)
+    for t in (0, 5, 15):
+        one = P.run_gpu(m, x[t:t + 1], layer0)
+        np.testing.assert_array_equal(one["y_bits"][0], full["y_bits"][t])
+
+
+def test_token_permutation_equivariance(m, layer0):
+    x = synth.gen_x(302, 24)
+    perm = np.random.default_rng(3).permutation(24)
+    a = P.run_gpu(m, x, layer0)
+    b = P.run_gpu(m, x[perm], layer0)
+    np.testing.assert_array_equal(a["y_bits"][perm], b["y_bits"])
+    np.testing.assert_array_equal(a["topk_idx"][perm], b["topk_idx"])
+
+
+# ---------------------------------------------------------------------- stack
+def test_stack_teacher_forced(m):
+    """Two layers of the seed-4 stack; each layer checked on the GPU's own input."""
+    T = 8
+    layers = [m.generated_layer(synth.STACK_SEED, l) for l in range(2)]
+    x0 = torch.empty((T, 2048), dtype=torch.int16, device="cuda")
+    m.moe_w4_generate_x(synth.STACK_SEED, 0, x0)
+    resid = x0.view(torch.bfloat16).float().contiguous()
+    xb = torch.empty((T, 2048), dtype=torch.int16, device="cuda")
+    yb = torch.empty((T, 2048), dtype=torch.int16, device="cuda")
+    ws = m.workspace(T)
+    for l, w in enumerate(layers):
+        r_before = resid.double().cpu().numpy()
+        m.moe_w4_stack_layer(resid, w["router_w"], w["codes"], w["scales"], w["shared_w"], xb, yb, ws)
+        torch.cuda.synchronize()
+        x_in = P.from_dev_u16(xb)
+        # the layer input: bf16 of the unit-gain RMS norm, within one bf16 step
+        want = O.rmsnorm(r_before)
+        got = O.bf16_to_f64(x_in)
+        assert np.all(np.abs(got - want) <= np.abs(want) * 2.0 ** -7 + 1e-30)
+        ref = O.moe_layer(x_in, synth.gen_router(synth.STACK_SEED, l), P.host_blobs(synth.STACK_SEED, l),
+                          synth.gen_shared(synth.STACK_SEED, l))
+        g = dict(y_bits=P.from_dev_u16(yb),
+                 topk_idx=m.ws_view(ws, T, "topk_idx", torch.int32, 6 * T).cpu().numpy().reshape(T, 6),
+                 topk_w=m.ws_view(ws, T, "topk_w", torch.float32, 6 * T).cpu().numpy().reshape(T, 6),
+                 offsets=m.ws_view(ws, T, "offsets", torch.int32, 257).cpu().numpy(),
+                 perm=m.ws_view(ws, T, "perm", torch.int32, 6 * T).cpu().numpy(),
+                 pos=m.ws_view(ws, T, "pos", torch.int32, 6 * T).cpu().numpy(),
+                 n_active=int(m.ws_view(ws, T, "n_active", torch.int32, 1).cpu().numpy()[0]),
+                 active=m.ws_view(ws, T, "active", torch.int32, 256).cpu().numpy())
+        report(f"stack layer {l}", P.compare(g, ref, label=f"stack layer {l}"))
+        np.testing.assert_array_equal(resid.cpu().numpy(),
+                                      (r_before + O.bf16_to_f64(g["y_bits"])).astype(np.float32))
