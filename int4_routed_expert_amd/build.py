@@ -26,7 +26,7 @@ SOURCES = ["api.hip", "router.hip", "experts_gemv.hip", "shared_gemv.hip", "comb
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [
-    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wshadow", "-Wno-unused-function",
     "-I", INCLUDE, "-I", CSRC,
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-munsafe-fp-atomics", "-mcode-object-version=5",

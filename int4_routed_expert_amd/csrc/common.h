@@ -84,16 +84,40 @@ __device__ __forceinline__ Q4 int4x8_to_q(uint32_t w) {
     return r;
 }
 
-// Offset of one stored 8-group (four half2 words in the order above).
-__device__ __forceinline__ float q_offset(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3) {
-    const float even = half_lo(x0) + half_hi(x0) + half_lo(x2) + half_hi(x2);
-    const float odd = half_lo(x1) + half_hi(x1) + half_lo(x3) + half_hi(x3);
-    return 1032.0f * even + 1152.0f * odd;
+// Offset of one stored 8-group (four half2 words in the order above), added to
+// acc: 1032 * (even-position values) + 1152 * (odd-position values), on the
+// same dot2 unit as the products (fp16 1032.0 = 0x6408, 1152.0 = 0x6480).
+__device__ __forceinline__ float q_offset(uint32_t x0, uint32_t x1, uint32_t x2, uint32_t x3, float acc) {
+    acc = dot2h(x0, 0x64086408u, acc);
+    acc = dot2h(x1, 0x64806480u, acc);
+    acc = dot2h(x2, 0x64086408u, acc);
+    acc = dot2h(x3, 0x64806480u, acc);
+    return acc;
 }
 
 // ---------------------------------------------------------------------------
 // Wave-level helpers (wave64).
 // ---------------------------------------------------------------------------
+// Raw buffer loads: a wave-uniform descriptor (base, size) in SGPRs, one VGPR
+// byte offset per lane and a wave-uniform SGPR offset, so runs of row loads
+// need no per-row VGPR addresses; reads past `bytes` return zero.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buf(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint16_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
+// Mark a value the compiler cannot prove wave-uniform as uniform (SGPR), so
+// addresses built from it use scalar bases and loads through it are scalar.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ int wave_id() { return uniform(threadIdx.x >> 6); }
+
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
 
 __device__ __forceinline__ float wave_sum(float v) {

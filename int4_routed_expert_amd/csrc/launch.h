@@ -22,10 +22,9 @@ void launch_sort(const int *topk_idx, int T, int *offsets, int *perm, int *pos, 
 void launch_gateup_gemv(const uint8_t *codes, const uint16_t *scales, const uint32_t *xt,
                         const float *xt_scale, const int *offsets, const int *perm,
                         const int *n_active, const int *active, int T, float *act, hipStream_t s);
-void launch_rotate_act(const float *act, int T, uint32_t *at, float *at_scale, hipStream_t s);
-void launch_down_gemv(const uint8_t *codes, const uint16_t *scales, const uint32_t *at,
-                      const float *at_scale, const int *offsets, const int *n_active,
-                      const int *active, int T, float *o, hipStream_t s);
+// down: rotates a = silu(g)*u per wave item, then streams the down rows.
+void launch_down_gemv(const uint8_t *codes, const uint16_t *scales, const float *act, const int *offsets,
+                      const int *n_active, const int *active, int T, float *o, hipStream_t s);
 
 // Shared expert (bf16 weights).
 void launch_shared_gateup(const uint16_t *shared_w, const uint16_t *x, int T, uint16_t *hs, hipStream_t s);
