@@ -86,7 +86,10 @@ extern "C" {
  *   perm      i32 [6T]    sorted position p -> assignment a = 6t + j, ordered by (expert, a)
  *   pos       i32 [6T]    inverse of perm
  *   n_active  i32 [1]     number of experts with at least one token
- *   active    i32 [256]   those experts, ascending */
+ *   active    i32 [256][8] one record per expert with tokens, ascending by expert:
+ *                         {expert, offsets[expert], token count, first token,
+ *                         second token (= first if one), 0, 0, 0}; records past
+ *                         n_active hold expert -1 */
 typedef struct moe_w4_ws_layout {
     size_t logits, topk_idx, topk_w, offsets, perm, pos, n_active, active;
     size_t xt, xt_scale, act, at, at_scale, hs, o, z, sync;

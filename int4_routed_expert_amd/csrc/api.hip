@@ -34,7 +34,7 @@ moe_w4_ws_layout make_layout(int64_t T) {
     L.perm = take(4 * a);
     L.pos = take(4 * a);
     L.n_active = take(4);
-    L.active = take(4 * kE);
+    L.active = take(4 * 8 * kE);
     L.xt = take(2 * kH * t);
     L.xt_scale = take(4 * t);
     L.act = take(4 * kI * a);
@@ -77,8 +77,8 @@ int validate_forward(const void *x, const void *router_w, const void *codes, con
     return MOE_W4_OK;
 }
 
-const char *kStageNames[] = {"route", "shared_gateup", "routed_gateup", "routed_down", "shared_down",
-                             "combine"};
+const char *kStageNames[] = {"route", "shared_gateup", "routed_gateup", "rotate_act", "routed_down",
+                             "shared_down", "combine"};
 constexpr int kStages = sizeof(kStageNames) / sizeof(kStageNames[0]);
 
 template <class T_>
@@ -107,6 +107,8 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     uint32_t *xt = ws_at<uint32_t>(ws, L.xt);
     float *xt_scale = ws_at<float>(ws, L.xt_scale);
     float *act = ws_at<float>(ws, L.act);
+    uint32_t *at = ws_at<uint32_t>(ws, L.at);
+    float *at_scale = ws_at<float>(ws, L.at_scale);
     uint16_t *hs = ws_at<uint16_t>(ws, L.hs);
     float *o = ws_at<float>(ws, L.o);
     float *z = ws_at<float>(ws, L.z);
@@ -140,9 +142,11 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     MOE_MARK();
     MOE_STEP(launch_shared_gateup(shared_w, x, T, hs, s));
     MOE_MARK();
-    MOE_STEP(launch_gateup_gemv(codes, scales, xt, xt_scale, offsets, perm, n_active, active, T, act, s));
+    MOE_STEP(launch_gateup_gemv(codes, scales, xt, xt_scale, perm, active, T, act, s));
     MOE_MARK();
-    MOE_STEP(launch_down_gemv(codes, scales, act, offsets, n_active, active, T, o, s));
+    MOE_STEP(launch_rotate_act(act, T, at, at_scale, s));
+    MOE_MARK();
+    MOE_STEP(launch_down_gemv(codes, scales, at, at_scale, active, T, o, s));
     MOE_MARK();
     MOE_STEP(launch_shared_down(shared_w, hs, T, z, s));
     MOE_MARK();

@@ -73,14 +73,18 @@ __device__ __forceinline__ float dot2b(uint32_t a, uint32_t b, float acc) {
 // ---------------------------------------------------------------------------
 struct Q4 { uint32_t q0, q1, q2, q3; };
 
+// (w ^ B) on the mask bits A, B elsewhere: with B = 0x6400 | the nibble's sign
+// bit, this is the XOR-by-8, AND and OR above in one three-input bit op
+// (v_bitop3_b32), so eight codes cost one shift and four bit ops.
+__device__ __forceinline__ uint32_t nib_to_half(uint32_t w, uint32_t A, uint32_t B) { return (A & (w ^ B)) | (~A & B); }
+
 __device__ __forceinline__ Q4 int4x8_to_q(uint32_t w) {
-    const uint32_t v = w ^ 0x88888888u;
-    const uint32_t t = v >> 8;
+    const uint32_t t = w >> 8;
     Q4 r;
-    r.q0 = (v & 0x000f000fu) | 0x64006400u;
-    r.q1 = (v & 0x00f000f0u) | 0x64006400u;
-    r.q2 = (t & 0x000f000fu) | 0x64006400u;
-    r.q3 = (t & 0x00f000f0u) | 0x64006400u;
+    r.q0 = nib_to_half(w, 0x000f000fu, 0x64086408u);
+    r.q1 = nib_to_half(w, 0x00f000f0u, 0x64806480u);
+    r.q2 = nib_to_half(t, 0x000f000fu, 0x64086408u);
+    r.q3 = nib_to_half(t, 0x00f000f0u, 0x64806480u);
     return r;
 }
 
@@ -112,6 +116,37 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 __device__ __forceinline__ uint16_t bload2(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }
+// Non-temporal variants (cache policy "nt") for data read once, such as the
+// weight streams: on MI355X a plain streaming read reaches ~7.1 TB/s with nt
+// loads against ~5.5 TB/s without.
+constexpr int kCachePolicyNT = 2;
+__device__ __forceinline__ uint4 bload16_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCachePolicyNT);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint16_t bload2_nt(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kCachePolicyNT);
+}
+// Same loads marked volatile (bit 31 of the cache-policy operand): a reload
+// of data already in registers that the compiler must not merge with the
+// first load (which would make everything derived from it loop-invariant).
+constexpr int kVolatileLoad = (int)(1u << 31);
+__device__ __forceinline__ uint4 bload16_nt_reload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kCachePolicyNT | kVolatileLoad);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint16_t bload2_nt_reload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kCachePolicyNT | kVolatileLoad);
+}
+
+// Order point for register pressure: an empty asm that "reads" `after` and
+// "rewrites" `next`, so the compiler cannot start work on `next` (e.g. the
+// int4 -> fp16 conversion of the next row) before `after` is computed.  The
+// instruction scheduler barrier alone does not stop the earlier
+// instruction-selection scheduling from converting every row up front.
+__device__ __forceinline__ void order_after(uint4 &next, float after) {
+    asm volatile("" : "+v"(next.x), "+v"(next.y), "+v"(next.z), "+v"(next.w) : "v"(after));
+}
 
 // Mark a value the compiler cannot prove wave-uniform as uniform (SGPR), so
 // addresses built from it use scalar bases and loads through it are scalar.
@@ -136,6 +171,14 @@ __device__ __forceinline__ float wave_max(float v) {
 // each lane (V <= span, both powers of two).  Each halving step exchanges half
 // of the remaining values with the partner lane, so the cost is about V
 // shuffles instead of V*log2(span).
+// Lane-dependent choice between two register values as bit operations: a
+// plain `cond ? v[i] : v[i + half]` is turned by the compiler into a select
+// of addresses, i.e. dynamic indexing of v, which costs a compare and a
+// select per element of v.
+__device__ __forceinline__ float pick_bits(uint32_t mask, float if_set, float if_clear) {
+    return __uint_as_float((__float_as_uint(if_set) & mask) | (__float_as_uint(if_clear) & ~mask));
+}
+
 template <int V, int SPAN>
 __device__ __forceinline__ float transpose_reduce(float (&v)[V]) {
     const int lane = threadIdx.x & (kWave - 1);
@@ -144,11 +187,12 @@ __device__ __forceinline__ float transpose_reduce(float (&v)[V]) {
     for (int s = 0; s < kSteps; ++s) {
         const int m = SPAN >> (s + 1);          // partner distance
         const int half = V >> (s + 1);          // values kept after this step
-        const bool upper = (lane & m) != 0;
+        const uint32_t upper = (lane & m) ? 0xffffffffu : 0u;
 #pragma unroll
         for (int i = 0; i < half; ++i) {
-            const float send = upper ? v[i] : v[i + half];
-            const float keep = upper ? v[i + half] : v[i];
+            const float a = v[i], b = v[i + half];
+            const float send = pick_bits(upper, a, b);
+            const float keep = pick_bits(upper, b, a);
             v[i] = keep + shfl_xor_f(send, m);
         }
     }

@@ -54,141 +54,149 @@ __device__ __forceinline__ void convert16(const uint4 w, Q4 (&q)[4]) {
 
 __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + expf(-v)); }
 
-template <int N>
-__device__ __forceinline__ float pick(const float (&a)[N], int i) {
-    float r = a[0];
-#pragma unroll
-    for (int k = 1; k < N; ++k) r = (i == k) ? a[k] : r;
-    return r;
-}
+
 
 // =========================================================================
-// gate/up.  A wave item is (active expert slot, gate rows [r0, r0+RPI) and
-// the same up rows).  Lane l owns K [32l, 32l+32) of every row.  Rows are
-// consumed in pairs (gate r, up r); the loads of the pair four ahead are
-// issued into the registers a pair frees, so 8 KB per wave stay in flight
-// without a second buffer.  At most two tokens are held in registers; an
-// expert with more tokens is streamed again per pair of tokens (the rows are
-// then L2 hits).
+// gate/up.  A wave item is (active expert slot, gate rows [r0, r0 + 4*NB)
+// and the same up rows), streamed as NB batches of 4 row pairs (8 KB): the
+// loads of batch b+1 go into the registers batch b frees, so 8 KB per wave
+// stay in flight.  The first batch is requested as soon as the expert is
+// known, before the tokens are read.  Lane l owns K [32l, 32l+32) of every
+// row.  One or two tokens per pass; more tokens re-read the rows (L2 hits).
 // =========================================================================
-template <int NT>
-__device__ __forceinline__ void gu_tokens(const uint32_t *__restrict__ xt, const float *__restrict__ xt_scale,
-                                          const int *__restrict__ perm, int p0, int n_valid, int lane,
-                                          uint32_t (&xs)[NT][16], float (&off)[NT], float (&sc)[NT]) {
+constexpr int kGuPairs = 4;   // row pairs per batch
+
+struct GuRows {
+    uint4 g[kGuPairs], u[kGuPairs];
+    uint16_t sg[kGuPairs], su[kGuPairs];   // bf16 bits of the gate and up scales
+};
+
+template <bool RELOAD>
+__device__ __forceinline__ void gu_load_pair(GuRows &R, int i, rsrc_t cg, rsrc_t sp, uint32_t cv, uint32_t sv, int r) {
+    if (RELOAD) {
+        R.g[i] = bload16_nt_reload(cg, cv, r * (kH / 2));
+        R.u[i] = bload16_nt_reload(cg, cv, kPlaneGateBytes + r * (kH / 2));
+        R.sg[i] = bload2_nt_reload(sp, sv, 2 * r * (kH / kG));
+        R.su[i] = bload2_nt_reload(sp, sv, 2 * (kScalesGate + r * (kH / kG)));
+    } else {
+        R.g[i] = bload16_nt(cg, cv, r * (kH / 2));
+        R.u[i] = bload16_nt(cg, cv, kPlaneGateBytes + r * (kH / 2));
+        R.sg[i] = bload2_nt(sp, sv, 2 * r * (kH / kG));
+        R.su[i] = bload2_nt(sp, sv, 2 * (kScalesGate + r * (kH / kG)));
+    }
+}
+
+// NB batches of 4 row pairs for NT tokens (1 or 2; n_valid <= NT).  On entry
+// R holds the first batch; the next batch is loaded into the registers each
+// row frees.
+template <int NB, int NT>
+__device__ __forceinline__ void gu_compute(GuRows &R, rsrc_t cg, rsrc_t sp, uint32_t cv, uint32_t sv, int r0,
+                                           const uint32_t *__restrict__ xt, const float *__restrict__ xt_scale,
+                                           int t_a, int t_b, int p0, int n_valid, int lane,
+                                           float *__restrict__ act) {
+    constexpr int V = 2 * kGuPairs * NT;
+    constexpr int kLogV = __builtin_ctz(V);
+    uint32_t xs[NT][16];
+    float off[NT], sc[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-        const int p = p0 + min(n, n_valid - 1);
-        const int t = uniform(perm[p]) / kTopK;
+        const int t = n ? t_b : t_a;
         off[n] = load_operand32(xt + (size_t)t * (kH / 2) + lane * 16, xs[n]);
         sc[n] = __builtin_bit_cast(float, uniform(__builtin_bit_cast(int, xt_scale[t])));
     }
-}
-
-template <int NT, int RPI>
-__device__ __forceinline__ void gu_stream(rsrc_t cg, rsrc_t sp, uint32_t cv, uint32_t sv, int r0,
-                                          const uint32_t *__restrict__ xt, const float *__restrict__ xt_scale,
-                                          const int *__restrict__ perm, int p0, int n_valid, int lane,
-                                          float *__restrict__ act) {
-    constexpr int kDepth = 4;   // row pairs in flight
-    constexpr int V = 2 * kDepth * NT;
-    constexpr int kLogV = __builtin_ctz(V);
-    uint4 rg[kDepth], ru[kDepth];
-    uint16_t sg[kDepth], su[kDepth];   // bf16 bits of the gate and up scales
 #pragma unroll
-    for (int i = 0; i < kDepth; ++i) {
-        rg[i] = bload16(cg, cv, (r0 + i) * (kH / 2));
-        ru[i] = bload16(cg, cv, kPlaneGateBytes + (r0 + i) * (kH / 2));
-        sg[i] = bload2(sp, sv, 2 * (r0 + i) * (kH / kG));
-        su[i] = bload2(sp, sv, 2 * (kScalesGate + (r0 + i) * (kH / kG)));
-    }
-    uint32_t xs[NT][16];
-    float off[NT], sc[NT];
-    gu_tokens<NT>(xt, xt_scale, perm, p0, n_valid, lane, xs, off, sc);
-#pragma unroll
-    for (int b = 0; b < RPI / kDepth; ++b) {
+    for (int b = 0; b < NB; ++b) {
+        const int rb = r0 + kGuPairs * b;
         float v[V];
 #pragma unroll
-        for (int i = 0; i < kDepth; ++i) {
-            const int r = r0 + kDepth * b + i;
-            const bool more = kDepth * (b + 1) < RPI;
-            {
+        for (int i = 0; i < kGuPairs; ++i) {
+            const int rn = rb + kGuPairs + i;   // same pair of the next batch
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {      // gate row, then up row
                 Q4 q[4];
-                convert16(rg[i], q);
-                const float sc_row = bf16_to_f32(sg[i]);
-                if (more) {
-                    rg[i] = bload16(cg, cv, (r + kDepth) * (kH / 2));
-                    sg[i] = bload2(sp, sv, 2 * (r + kDepth) * (kH / kG));
+                convert16(h ? R.u[i] : R.g[i], q);
+                const float sr = bf16_to_f32(h ? R.su[i] : R.sg[i]);
+                if (b + 1 < NB) {   // refill the freed registers with the next batch
+                    if (h) {
+                        R.u[i] = bload16_nt(cg, cv, kPlaneGateBytes + rn * (kH / 2));
+                        R.su[i] = bload2_nt(sp, sv, 2 * (kScalesGate + rn * (kH / kG)));
+                    } else {
+                        R.g[i] = bload16_nt(cg, cv, rn * (kH / 2));
+                        R.sg[i] = bload2_nt(sp, sv, 2 * rn * (kH / kG));
+                    }
                 }
 #pragma unroll
-                for (int n = 0; n < NT; ++n) v[(i * NT + n) * 2 + 0] = dot_slice(q, xs[n], -off[n]) * sc_row;
+                for (int n = 0; n < NT; ++n) v[(i * NT + n) * 2 + h] = dot_slice(q, xs[n], -off[n]) * sr;
+                __builtin_amdgcn_sched_barrier(0);   // one row at a time (register pressure)
             }
-            {
-                Q4 q[4];
-                convert16(ru[i], q);
-                const float sc_row = bf16_to_f32(su[i]);
-                if (more) {
-                    ru[i] = bload16(cg, cv, kPlaneGateBytes + (r + kDepth) * (kH / 2));
-                    su[i] = bload2(sp, sv, 2 * (kScalesGate + (r + kDepth) * (kH / kG)));
-                }
-#pragma unroll
-                for (int n = 0; n < NT; ++n) v[(i * NT + n) * 2 + 1] = dot_slice(q, xs[n], -off[n]) * sc_row;
-            }
-            __builtin_amdgcn_sched_barrier(0);   // keep the ring: no hoisting of later loads
         }
         const float red = transpose_reduce<V, 64>(v);
         const float other = shfl_xor_f(red, 1 << (6 - kLogV));
         const int vi = lane >> (6 - kLogV);
         const int i = vi / (2 * NT), n = (vi >> 1) % NT;
         if ((vi & 1) == 0 && (lane & ((1 << (6 - kLogV)) - 1)) == 0 && n < n_valid) {
-            const float s = pick(sc, n);
+            const float s = n ? sc[NT - 1] : sc[0];
             const float g = red * s, u = other * s;
-            act[(size_t)(p0 + n) * kI + r0 + kDepth * b + i] = silu_f(g) * u;
+            act[(size_t)(p0 + n) * kI + rb + i] = silu_f(g) * u;
         }
     }
 }
 
-template <int RPI>
-__global__ __launch_bounds__(256) void k_gateup_dec(const uint8_t *__restrict__ codes,
-                                                    const uint16_t *__restrict__ scales,
-                                                    const uint32_t *__restrict__ xt,
-                                                    const float *__restrict__ xt_scale,
-                                                    const int *__restrict__ offsets,
-                                                    const int *__restrict__ perm,
-                                                    const int *__restrict__ n_active,
-                                                    const int *__restrict__ active,
-                                                    float *__restrict__ act) {
-    constexpr int kItems = kI / RPI;   // items per expert
+template <int NB>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_gateup_dec(
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, const uint32_t *__restrict__ xt,
+    const float *__restrict__ xt_scale, const int *__restrict__ perm, const int *__restrict__ slots,
+    float *__restrict__ act) {
+    constexpr int kRows = kGuPairs * NB;
+    constexpr int kItems = kI / kRows;   // items per expert
     const int lane = threadIdx.x & 63;
     const int item = blockIdx.x * 4 + wave_id();
-    const int slot = item / kItems;
-    if (slot >= uniform(*n_active)) return;
-    const int e = uniform(active[slot]);
-    const int r0 = (item % kItems) * RPI;
+    const int *rec = slots + 8 * (item / kItems);   // {expert, p_begin, n, t0, t1}
+    const int e = rec[0];
+    if (e < 0) return;   // slot without an expert
+    const int p_begin = rec[1], n = rec[2], t0 = rec[3], t1 = rec[4];
+    const int r0 = (item % kItems) * kRows;
     const rsrc_t cg = make_buf(codes + (size_t)e * kCodeBytesPerExpert, kCodeBytesGu);
     const rsrc_t sp = make_buf(scales + (size_t)e * kScalesPerExpert, 2 * kScalesGu);
     const uint32_t cv = lane * 16, sv = (lane >> 2) * 2;
-    const int p_begin = uniform(offsets[e]), p_end = uniform(offsets[e + 1]);
-    for (int p0 = p_begin; p0 < p_end; p0 += 2) {
-        if (p_end - p0 == 1) gu_stream<1, RPI>(cg, sp, cv, sv, r0, xt, xt_scale, perm, p0, 1, lane, act);
-        else gu_stream<2, RPI>(cg, sp, cv, sv, r0, xt, xt_scale, perm, p0, 2, lane, act);
+    GuRows R;
+    if (n == 1) {
+        // the common decode case: one token, no second operand set
+#pragma unroll
+        for (int i = 0; i < kGuPairs; ++i) gu_load_pair<false>(R, i, cg, sp, cv, sv, r0 + i);
+        gu_compute<NB, 1>(R, cg, sp, cv, sv, r0, xt, xt_scale, t0, t0, p_begin, 1, lane, act);
+        return;
+    }
+    // Two or more tokens, two at a time through one call site.  Later pairs
+    // re-read the rows (L2 hits) with volatile loads, which the compiler cannot
+    // merge with the first ones (that would make every row's conversion
+    // loop-invariant and hold all of them in registers).
+#pragma unroll
+    for (int i = kGuPairs - 1; i >= 0; --i) gu_load_pair<true>(R, i, cg, sp, cv, sv, r0 + i);
+    const int p_end = p_begin + n;
+    int ta = t0, tb = t1;
+    for (int p0 = p_begin;;) {
+        gu_compute<NB, 2>(R, cg, sp, cv, sv, r0, xt, xt_scale, ta, tb, p0, min(2, p_end - p0), lane, act);
+        p0 += 2;
+        if (p0 >= p_end) break;
+#pragma unroll
+        for (int i = kGuPairs - 1; i >= 0; --i) gu_load_pair<true>(R, i, cg, sp, cv, sv, r0 + i);
+        ta = perm[p0] / kTopK;
+        tb = perm[min(p0 + 1, p_end - 1)] / kTopK;
     }
 }
 
 // =========================================================================
-// down.  A wave item is (active expert slot, rows [n0, n0+RPI)).  The wave
-// first rotates a = silu(g)*u of the expert's tokens (Hadamard per 128-block,
-// power-of-two prescale per block, fp16 operands) through its own LDS slot,
-// then streams its rows: 16 lanes per row (lane j = lane & 15 owns K
-// [32j, 32j+32), inside block j/4), one 1 KiB wave load = 4 rows.
+// a -> fp16 operands of the down projection, once per assignment: Hadamard on
+// each of the four 128-blocks of a = silu(g)*u (one wave per assignment, lane
+// l owns 8 values), a power-of-two prescale per block, stored in the
+// int4x8_to_q operand order.
 // =========================================================================
-constexpr int kDownNT = 4;
-struct DownLds {
-    uint32_t at[kDownNT][kI / 2];   // fp16 operands, 1 KiB per token
-    float mult[kDownNT][kI / kG];   // 2^shift per block
-};
-
-// Rotate token p's a (fp32 [512]) into the wave's LDS slot n.
-__device__ __forceinline__ void rotate_into_lds(const float *__restrict__ act, int p, int n, int lane, DownLds &L) {
+__global__ __launch_bounds__(256) void k_rotate_act(const float *__restrict__ act, int n_rows,
+                                                    uint32_t *__restrict__ at, float *__restrict__ at_scale) {
+    const int lane = threadIdx.x & 63;
+    const int p = blockIdx.x * 4 + wave_id();
+    if (p >= n_rows) return;
     const float4 *src = reinterpret_cast<const float4 *>(act + (size_t)p * kI + lane * 8);
     const float4 a0 = src[0], a1 = src[1];
     float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
@@ -204,7 +212,7 @@ __device__ __forceinline__ void rotate_into_lds(const float *__restrict__ act, i
         }
     }
 #pragma unroll
-    for (int m = 1; m <= 8; m <<= 1) {
+    for (int m = 1; m <= 8; m <<= 1) {   // strides 8..64: lanes of the same block
         const bool upper = (lane & m) != 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -224,140 +232,132 @@ __device__ __forceinline__ void rotate_into_lds(const float *__restrict__ act, i
     if (amax > 0.0f && isfinite(amax)) {
         int ex;
         frexpf(amax, &ex);
-        sh = ex - 14;   // largest magnitude in [2^13, 2^14): exact, far from fp16 overflow
+        sh = ex - 14;   // largest magnitude in [2^13, 2^14): exact scaling, far from fp16 overflow
     }
     uint4 w;
     w.x = pack_half2(ldexpf(v[0], -sh), ldexpf(v[4], -sh));
     w.y = pack_half2(ldexpf(v[1], -sh - 4), ldexpf(v[5], -sh - 4));
     w.z = pack_half2(ldexpf(v[2], -sh), ldexpf(v[6], -sh));
     w.w = pack_half2(ldexpf(v[3], -sh - 4), ldexpf(v[7], -sh - 4));
-    reinterpret_cast<uint4 *>(L.at[n])[lane] = w;
-    if ((lane & 15) == 0) L.mult[n][lane >> 4] = ldexpf(1.0f, sh);
+    reinterpret_cast<uint4 *>(at + (size_t)p * (kI / 2))[lane] = w;
+    if ((lane & 15) == 0) at_scale[(size_t)p * (kI / kG) + (lane >> 4)] = ldexpf(1.0f, sh);
 }
 
-template <int NT, int RPI>
-__device__ __forceinline__ void dn_stream(rsrc_t cd, rsrc_t sp, uint32_t cv, uint32_t sv, int n0,
-                                          const DownLds &L, int slot0, int p0, int n_valid, int lane,
-                                          float *__restrict__ o) {
-    constexpr int kDepth = 4;          // wave loads (4 rows each) in flight
-    constexpr int V = kDepth * NT;
+// =========================================================================
+// down.  A wave item is (active expert slot, rows [n0, n0 + 4*kDnLoads)):
+// 8 KB of codes in kDnLoads wave loads (4 rows each; 16 lanes per row, lane
+// j = lane & 15 owns K [32j, 32j+32), inside block j/4), all requested as
+// soon as the expert is known.
+// =========================================================================
+constexpr int kDnLoads = 8;
+
+struct DnRows {
+    uint4 w[kDnLoads];
+    uint16_t s[kDnLoads];
+};
+
+template <bool RELOAD>
+__device__ __forceinline__ void dn_load(DnRows &R, rsrc_t cd, rsrc_t sp, uint32_t cv, uint32_t sv, int n0) {
+#pragma unroll
+    for (int q = 0; q < kDnLoads; ++q) {
+        if (RELOAD) {
+            R.w[q] = bload16_nt_reload(cd, cv, (n0 + 4 * q) * (kI / 2));
+            R.s[q] = bload2_nt_reload(sp, sv, 2 * (n0 + 4 * q) * (kI / kG));
+        } else {
+            R.w[q] = bload16_nt(cd, cv, (n0 + 4 * q) * (kI / 2));
+            R.s[q] = bload2_nt(sp, sv, 2 * (n0 + 4 * q) * (kI / kG));
+        }
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void dn_compute(DnRows &R, int n0, const uint32_t *__restrict__ at,
+                                           const float *__restrict__ at_scale, int p0, int n_valid, int lane,
+                                           float *__restrict__ o) {
+    constexpr int kPerRed = 2;                 // wave loads per reduction
+    constexpr int V = kPerRed * NT;
     constexpr int kLogV = __builtin_ctz(V);
     const int j = lane & 15, rsub = lane >> 4;
-    uint4 w[kDepth];
-    uint16_t s[kDepth];
-#pragma unroll
-    for (int q = 0; q < kDepth; ++q) {
-        w[q] = bload16(cd, cv, (n0 + 4 * q) * (kI / 2));
-        s[q] = bload2(sp, sv, 2 * (n0 + 4 * q) * (kI / kG));
-    }
     uint32_t xs[NT][16];
     float off[NT], mult[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-        const int nn = slot0 + min(n, n_valid - 1);   // LDS slot of this token
-        float acc = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint4 q = reinterpret_cast<const uint4 *>(L.at[nn] + 16 * j)[i];
-            xs[n][4 * i] = q.x; xs[n][4 * i + 1] = q.y; xs[n][4 * i + 2] = q.z; xs[n][4 * i + 3] = q.w;
-            acc = q_offset(q.x, q.y, q.z, q.w, acc);
-        }
-        off[n] = acc;
-        mult[n] = L.mult[nn][j >> 2];
+        const int p = p0 + min(n, n_valid - 1);
+        off[n] = load_operand32(at + (size_t)p * (kI / 2) + j * 16, xs[n]);
+        mult[n] = at_scale[(size_t)p * (kI / kG) + (j >> 2)];
     }
 #pragma unroll
-    for (int b = 0; b < RPI / (4 * kDepth); ++b) {
+    for (int q0 = 0; q0 < kDnLoads; q0 += kPerRed) {
         float v[V];
 #pragma unroll
-        for (int q = 0; q < kDepth; ++q) {
-            const int r = n0 + 4 * (kDepth * b + q);
+        for (int k = 0; k < kPerRed; ++k) {
             Q4 qq[4];
-            convert16(w[q], qq);
-            const float scale_row = bf16_to_f32(s[q]);
-            if (4 * kDepth * (b + 1) < RPI) {
-                w[q] = bload16(cd, cv, (r + 4 * kDepth) * (kI / 2));
-                s[q] = bload2(sp, sv, 2 * (r + 4 * kDepth) * (kI / kG));
-            }
+            convert16(R.w[q0 + k], qq);
+            const float scale_row = bf16_to_f32(R.s[q0 + k]);
 #pragma unroll
-            for (int n = 0; n < NT; ++n) v[q * NT + n] = dot_slice(qq, xs[n], -off[n]) * (scale_row * mult[n]);
-            __builtin_amdgcn_sched_barrier(0);
+            for (int n = 0; n < NT; ++n) v[k * NT + n] = dot_slice(qq, xs[n], -off[n]) * (scale_row * mult[n]);
+            if (q0 + k + 1 < kDnLoads) order_after(R.w[q0 + k + 1], v[k * NT]);
         }
         const float red = transpose_reduce<V, 16>(v);
         const int vi = j >> (4 - kLogV);
-        const int q = vi / NT, n = vi % NT;
+        const int k = vi / NT, n = vi % NT;
         if ((j & ((1 << (4 - kLogV)) - 1)) == 0 && n < n_valid)
-            o[(size_t)(p0 + n) * kH + n0 + 4 * (kDepth * b + q) + rsub] = red;
+            o[(size_t)(p0 + n) * kH + n0 + 4 * (q0 + k) + rsub] = red;
     }
 }
 
-template <int RPI>
-__global__ __launch_bounds__(256) void k_down_dec(const uint8_t *__restrict__ codes,
-                                                  const uint16_t *__restrict__ scales,
-                                                  const float *__restrict__ act,
-                                                  const int *__restrict__ offsets,
-                                                  const int *__restrict__ n_active,
-                                                  const int *__restrict__ active,
-                                                  float *__restrict__ o) {
-    __shared__ DownLds lds[4];
-    constexpr int kItems = kH / RPI;
-    const int lane = threadIdx.x & 63, wave = wave_id();
-    const int item = blockIdx.x * 4 + wave;
-    const int slot = item / kItems;
-    if (slot >= uniform(*n_active)) return;
-    const int e = uniform(active[slot]);
-    const int n0 = (item % kItems) * RPI;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_down_dec(
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, const uint32_t *__restrict__ at,
+    const float *__restrict__ at_scale, const int *__restrict__ slots, float *__restrict__ o) {
+    constexpr int kRows = 4 * kDnLoads;
+    constexpr int kItems = kH / kRows;
+    const int lane = threadIdx.x & 63;
+    const int item = blockIdx.x * 4 + wave_id();
+    const int *rec = slots + 8 * (item / kItems);   // {expert, p_begin, n, ...}
+    const int e = rec[0];
+    if (e < 0) return;
+    const int p_begin = rec[1], n = rec[2];
+    const int n0 = (item % kItems) * kRows;
     const int j = lane & 15, rsub = lane >> 4;
     const rsrc_t cd = make_buf(codes + (size_t)e * kCodeBytesPerExpert + kCodeBytesGu, kCodeBytesPerExpert - kCodeBytesGu);
     const rsrc_t sp = make_buf(scales + (size_t)e * kScalesPerExpert + kScalesGu, 2 * (kScalesPerExpert - kScalesGu));
     const uint32_t cv = rsub * (kI / 2) + j * 16, sv = 2 * (rsub * (kI / kG) + (j >> 2));
-    const int p_begin = uniform(offsets[e]), p_end = uniform(offsets[e + 1]);
-    DownLds &L = lds[wave];
-    for (int p0 = p_begin; p0 < p_end; p0 += kDownNT) {
-        const int nv = min(kDownNT, p_end - p0);
-        for (int n = 0; n < nv; ++n) rotate_into_lds(act, p0 + n, n, lane, L);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        for (int c = 0; c < nv; c += 2) {
-            if (nv - c == 1) dn_stream<1, RPI>(cd, sp, cv, sv, n0, L, c, p0 + c, 1, lane, o);
-            else dn_stream<2, RPI>(cd, sp, cv, sv, n0, L, c, p0 + c, 2, lane, o);
-        }
-        __builtin_amdgcn_wave_barrier();
+    DnRows R;
+    if (n == 1) {   // the common decode case
+        dn_load<false>(R, cd, sp, cv, sv, n0);
+        dn_compute<1>(R, n0, at, at_scale, p_begin, 1, lane, o);
+        return;
+    }
+    // two or more tokens, two at a time through one call site; volatile
+    // reloads (L2 hits) keep the rows loop-variant
+    const int p_end = p_begin + n;
+    for (int p0 = p_begin; p0 < p_end; p0 += 2) {
+        dn_load<true>(R, cd, sp, cv, sv, n0);
+        dn_compute<2>(R, n0, at, at_scale, p0, min(2, p_end - p0), lane, o);
     }
 }
 
 // ------------------------------------------------------------------ launchers
 void launch_gateup_gemv(const uint8_t *codes, const uint16_t *scales, const uint32_t *xt,
-                        const float *xt_scale, const int *offsets, const int *perm,
-                        const int *n_active, const int *active, int T, float *act, hipStream_t s) {
+                        const float *xt_scale, const int *perm, const int *slots, int T, float *act,
+                        hipStream_t s) {
     const int max_active = min(kE, kTopK * T);
-    if (T <= 8) {
-        constexpr int RPI = 4;
-        const int waves = max_active * (kI / RPI);
-        hipLaunchKernelGGL((k_gateup_dec<RPI>), dim3((waves + 3) / 4), dim3(256), 0, s, codes, scales, xt,
-                           xt_scale, offsets, perm, n_active, active, act);
-    } else {
-        constexpr int RPI = 16;
-        const int waves = max_active * (kI / RPI);
-        hipLaunchKernelGGL((k_gateup_dec<RPI>), dim3((waves + 3) / 4), dim3(256), 0, s, codes, scales, xt,
-                           xt_scale, offsets, perm, n_active, active, act);
-    }
+    const int waves = max_active * (kI / kGuPairs);
+    hipLaunchKernelGGL((k_gateup_dec<1>), dim3((waves + 3) / 4), dim3(256), 0, s, codes, scales, xt, xt_scale,
+                       perm, slots, act);
 }
 
-void launch_down_gemv(const uint8_t *codes, const uint16_t *scales, const float *act, const int *offsets,
-                      const int *n_active, const int *active, int T, float *o, hipStream_t s) {
+void launch_rotate_act(const float *act, int T, uint32_t *at, float *at_scale, hipStream_t s) {
+    const int n = kTopK * T;
+    hipLaunchKernelGGL(k_rotate_act, dim3((n + 3) / 4), dim3(256), 0, s, act, n, at, at_scale);
+}
+
+void launch_down_gemv(const uint8_t *codes, const uint16_t *scales, const uint32_t *at, const float *at_scale,
+                      const int *slots, int T, float *o, hipStream_t s) {
     const int max_active = min(kE, kTopK * T);
-    if (T <= 8) {
-        constexpr int RPI = 16;
-        const int waves = max_active * (kH / RPI);
-        hipLaunchKernelGGL((k_down_dec<RPI>), dim3((waves + 3) / 4), dim3(256), 0, s, codes, scales, act,
-                           offsets, n_active, active, o);
-    } else {
-        constexpr int RPI = 64;
-        const int waves = max_active * (kH / RPI);
-        hipLaunchKernelGGL((k_down_dec<RPI>), dim3((waves + 3) / 4), dim3(256), 0, s, codes, scales, act,
-                           offsets, n_active, active, o);
-    }
+    const int waves = max_active * (kH / (4 * kDnLoads));   // 64 items per expert
+    hipLaunchKernelGGL(k_down_dec, dim3((waves + 3) / 4), dim3(256), 0, s, codes, scales, at, at_scale, slots,
+                       o);
 }
 
 }  // namespace moe_w4

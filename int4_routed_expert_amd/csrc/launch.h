@@ -15,16 +15,19 @@ void launch_router_logits(const uint16_t *x, const uint16_t *router_w, const flo
 void launch_topk_rotate(const float *logits, const uint16_t *x, int T, int *topk_idx, float *topk_w,
                         uint32_t *xt, float *xt_scale, hipStream_t s);
 // Stable counting sort of the 6T assignments by expert (one workgroup).
+// slots: int[256][8] records {expert, first sorted position, count, first
+// token, second token, 0, 0, 0}, one per expert with tokens, then expert -1.
 void launch_sort(const int *topk_idx, int T, int *offsets, int *perm, int *pos, int *n_active,
-                 int *active, hipStream_t s);
+                 int *slots, hipStream_t s);
 
-// Routed experts, GEMV form (few tokens per expert).
+// Routed experts, GEMV form (few tokens per expert), driven by the slot records.
 void launch_gateup_gemv(const uint8_t *codes, const uint16_t *scales, const uint32_t *xt,
-                        const float *xt_scale, const int *offsets, const int *perm,
-                        const int *n_active, const int *active, int T, float *act, hipStream_t s);
-// down: rotates a = silu(g)*u per wave item, then streams the down rows.
-void launch_down_gemv(const uint8_t *codes, const uint16_t *scales, const float *act, const int *offsets,
-                      const int *n_active, const int *active, int T, float *o, hipStream_t s);
+                        const float *xt_scale, const int *perm, const int *slots, int T, float *act,
+                        hipStream_t s);
+// a = silu(g)*u -> rotated fp16 operands (+ per-block power-of-two scales).
+void launch_rotate_act(const float *act, int T, uint32_t *at, float *at_scale, hipStream_t s);
+void launch_down_gemv(const uint8_t *codes, const uint16_t *scales, const uint32_t *at, const float *at_scale,
+                      const int *slots, int T, float *o, hipStream_t s);
 
 // Shared expert (bf16 weights).
 void launch_shared_gateup(const uint16_t *shared_w, const uint16_t *x, int T, uint16_t *hs, hipStream_t s);

@@ -13,58 +13,6 @@
 namespace moe_w4 {
 
 // ---------------------------------------------------------------------------
-// logits[t][e] = sum_k x[t][k] R[e][k] (+ bias[e]), fp32 sums of exact bf16
-// products.  One wave per expert row; lane l owns K [32l, 32l+32).  Four
-// tokens are reduced together with a transposing lane reduction.
-// ---------------------------------------------------------------------------
-constexpr int kRouterExpertsPerBlock = 4;   // one per wave
-constexpr int kRouterTokensPerBlock = 32;
-
-__global__ __launch_bounds__(256) void k_router_logits(const uint16_t *__restrict__ x,
-                                                       const uint16_t *__restrict__ router_w,
-                                                       const float *__restrict__ bias, int T,
-                                                       float *__restrict__ logits) {
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int e = blockIdx.x * kRouterExpertsPerBlock + wave;
-    const int t0 = blockIdx.y * kRouterTokensPerBlock;
-    const int t1 = min(t0 + kRouterTokensPerBlock, T);
-    const uint4 *rp = reinterpret_cast<const uint4 *>(router_w + (size_t)e * kH + lane * 32);
-    uint32_t r[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        uint4 v = rp[i];
-        r[4 * i] = v.x; r[4 * i + 1] = v.y; r[4 * i + 2] = v.z; r[4 * i + 3] = v.w;
-    }
-    const float b = bias ? bias[e] : 0.0f;
-    for (int t = t0; t < t1; t += 4) {
-        float acc[4];
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            acc[n] = 0.0f;
-            const int tt = min(t + n, t1 - 1);
-            const uint4 *xp = reinterpret_cast<const uint4 *>(x + (size_t)tt * kH + lane * 32);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint4 v = xp[i];
-                acc[n] = dot2b(r[4 * i], v.x, acc[n]);
-                acc[n] = dot2b(r[4 * i + 1], v.y, acc[n]);
-                acc[n] = dot2b(r[4 * i + 2], v.z, acc[n]);
-                acc[n] = dot2b(r[4 * i + 3], v.w, acc[n]);
-            }
-        }
-        const float sum = transpose_reduce<4, 64>(acc);   // lane holds token index lane >> 4
-        const int n = lane >> 4;
-        if ((lane & 15) == 0 && t + n < t1) logits[(size_t)(t + n) * kE + e] = sum + b;
-    }
-}
-
-void launch_router_logits(const uint16_t *x, const uint16_t *router_w, const float *bias, int T,
-                          float *logits, hipStream_t s) {
-    dim3 grid(kE / kRouterExpertsPerBlock, (T + kRouterTokensPerBlock - 1) / kRouterTokensPerBlock);
-    hipLaunchKernelGGL(k_router_logits, grid, dim3(256), 0, s, x, router_w, bias, T, logits);
-}
-
-// ---------------------------------------------------------------------------
 // Top-6 of one token's 256 logits, one wave per token.  Keys order floats
 // monotonically as unsigned integers; ties go to the lower expert index.
 // ---------------------------------------------------------------------------
@@ -227,10 +175,12 @@ constexpr int kSortWaves = 16;
 __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx, int T,
                                                int *__restrict__ offsets, int *__restrict__ perm,
                                                int *__restrict__ pos, int *__restrict__ n_active,
-                                               int *__restrict__ active) {
+                                               int *__restrict__ slots) {
     __shared__ int cnt[kSortWaves][kE];
     __shared__ int tot[kE];
     __shared__ int offs[kE + 1];
+    __shared__ int first2[kE][2];   // tokens at the first two sorted positions of each expert
+    __shared__ int slot_e[kE + 1];  // expert of each active slot; [kE] = number of slots
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int N = kTopK * T;
     const int per = ((N + kSortWaves * 64 - 1) / (kSortWaves * 64)) * 64;
@@ -273,7 +223,7 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
             const int e = 4 * lane + i;
             offs[e] = ec;
             offsets[e] = ec;
-            if (f[i]) active[ef] = e;
+            if (f[i]) slot_e[ef] = e;
             ec += c[i];
             ef += f[i];
         }
@@ -281,6 +231,7 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
             offs[kE] = ec;
             offsets[kE] = ec;
             *n_active = ef;
+            slot_e[kE] = ef;
         }
     }
     __syncthreads();
@@ -302,15 +253,32 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
             const int dest = base + __popcll(same & below);
             perm[dest] = a;
             pos[a] = dest;
+            if (dest - offs[e] < 2) first2[e][dest - offs[e]] = a / kTopK;
             if ((same >> lane) == 1ull) cnt[wave][e] = base + __popcll(same);
+        }
+    }
+    __syncthreads();
+    // One 32-byte record per active slot, so a grouped kernel gets its expert,
+    // token range and first two tokens with a single scalar load; slots past
+    // n_active hold expert -1.
+    if (tid < kE) {
+        int4 *rec = reinterpret_cast<int4 *>(slots + 8 * tid);
+        if (tid < slot_e[kE]) {
+            const int e = slot_e[tid];
+            const int n = offs[e + 1] - offs[e];
+            rec[0] = make_int4(e, offs[e], n, first2[e][0]);
+            rec[1] = make_int4(n > 1 ? first2[e][1] : first2[e][0], 0, 0, 0);
+        } else {
+            rec[0] = make_int4(-1, 0, 0, 0);
+            rec[1] = make_int4(0, 0, 0, 0);
         }
     }
 }
 
 void launch_sort(const int *topk_idx, int T, int *offsets, int *perm, int *pos, int *n_active,
-                 int *active, hipStream_t s) {
+                 int *slots, hipStream_t s) {
     hipLaunchKernelGGL(k_sort, dim3(1), dim3(1024), 0, s, topk_idx, T, offsets, perm, pos, n_active,
-                       active);
+                       slots);
 }
 
 }  // namespace moe_w4

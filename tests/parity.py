@@ -78,7 +78,7 @@ def run_gpu(m, x_bits, w, bias=None, ws=None, poison=False):
     out["perm"] = m.ws_view(ws, T, "perm", torch.int32, 6 * T).cpu().numpy()
     out["pos"] = m.ws_view(ws, T, "pos", torch.int32, 6 * T).cpu().numpy()
     out["n_active"] = int(m.ws_view(ws, T, "n_active", torch.int32, 1).cpu().numpy()[0])
-    out["active"] = m.ws_view(ws, T, "active", torch.int32, 256).cpu().numpy()
+    out["active"] = m.ws_view(ws, T, "active", torch.int32, 8 * 256).cpu().numpy().reshape(256, 8)
     return out
 
 
@@ -104,7 +104,15 @@ def compare(gpu, ref, tokens=None, label=""):
     counts = np.diff(gpu["offsets"])
     act = np.nonzero(counts)[0]
     assert gpu["n_active"] == len(act)
-    np.testing.assert_array_equal(gpu["active"][:len(act)], act)
+    rec = gpu["active"]
+    np.testing.assert_array_equal(rec[:len(act), 0], act)
+    np.testing.assert_array_equal(rec[len(act):, 0], -1)
+    np.testing.assert_array_equal(rec[:len(act), 1], gpu["offsets"][act])
+    np.testing.assert_array_equal(rec[:len(act), 2], counts[act])
+    perm = gpu["perm"]
+    np.testing.assert_array_equal(rec[:len(act), 3], perm[gpu["offsets"][act]] // 6)
+    second = np.where(counts[act] > 1, gpu["offsets"][act] + 1, gpu["offsets"][act])
+    np.testing.assert_array_equal(rec[:len(act), 4], perm[second] // 6)
     # output
     rows = np.arange(T) if tokens is None else np.asarray(tokens)
     yr = ref["y"]                                      # fp64, rows = `rows`

@@ -221,7 +221,7 @@ def test_stack_teacher_forced(m):
                  perm=m.ws_view(ws, T, "perm", torch.int32, 6 * T).cpu().numpy(),
                  pos=m.ws_view(ws, T, "pos", torch.int32, 6 * T).cpu().numpy(),
                  n_active=int(m.ws_view(ws, T, "n_active", torch.int32, 1).cpu().numpy()[0]),
-                 active=m.ws_view(ws, T, "active", torch.int32, 256).cpu().numpy())
+                 active=m.ws_view(ws, T, "active", torch.int32, 8 * 256).cpu().numpy().reshape(256, 8))
         report(f"stack layer {l}", P.compare(g, ref, label=f"stack layer {l}"))
         np.testing.assert_array_equal(resid.cpu().numpy(),
                                       (r_before + O.bf16_to_f64(g["y_bits"])).astype(np.float32))
