@@ -187,13 +187,18 @@ def main():
     flops = T * (6 * 3 * 512 * 2048 * 2 + 3 * 1024 * 2048 * 2 + 256 * 2048 * 2)
     stage = dict(zip(names[1:], stage_ms))
     dom = max(stage, key=stage.get)
-    dom_bytes = {
-        "routed_gateup": n_touched * EXPERT_GU_BYTES,
-        "routed_down": n_touched * EXPERT_D_BYTES,
-        "shared_gateup": 2 * 1024 * 2048 * 2,
-        "shared_down": 1024 * 2048 * 2,
-        "route": ROUTER_BYTES,
-    }.get(dom, 0.0)
+    # algorithmic bytes of each stage: weights and scales it must read once, plus the
+    # activations it reads and writes
+    act = T * 2048 * 2
+    stage_bytes = {
+        "router_shared_gateup": ROUTER_BYTES + 2 * 1024 * 2048 * 2 + act + T * 256 * 4 + T * 1024 * 2,
+        "topk_sort": T * 256 * 4 + act + T * 6 * 4 * 4 + 257 * 4 + 256 * 32,
+        "routed_gateup": n_touched * EXPERT_GU_BYTES + T * 6 * 512 * 2,
+        "rotate_act": 2 * T * 6 * 512 * 2,
+        "routed_down": n_touched * EXPERT_D_BYTES + T * 6 * 2048 * 4,
+        "shared_down_combine": 1024 * 2048 * 2 + T * 1024 * 2 + T * 6 * 2048 * 4 + act,
+    }
+    dom_bytes = stage_bytes.get(dom, 0.0)
     achieved = dom_bytes / (stage[dom] * 1e-3) / 1e9
     result["value"] = T / (ms / 1e3)
     result["config"] = {"workload": f"{a.config}: one MoE layer, T={T}, x seed {cfg['x_seed']}, weights seed "

@@ -77,8 +77,8 @@ int validate_forward(const void *x, const void *router_w, const void *codes, con
     return MOE_W4_OK;
 }
 
-const char *kStageNames[] = {"route", "shared_gateup", "routed_gateup", "rotate_act", "routed_down",
-                             "shared_down", "combine"};
+const char *kStageNames[] = {"router_shared_gateup", "topk_sort", "routed_gateup", "rotate_act", "routed_down",
+                             "shared_down_combine"};
 constexpr int kStages = sizeof(kStageNames) / sizeof(kStageNames[0]);
 
 template <class T_>
@@ -111,7 +111,6 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     float *at_scale = ws_at<float>(ws, L.at_scale);
     uint16_t *hs = ws_at<uint16_t>(ws, L.hs);
     float *o = ws_at<float>(ws, L.o);
-    float *z = ws_at<float>(ws, L.z);
 
     int stage = 0;
     auto mark = [&](void) -> int {
@@ -136,11 +135,10 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
 
     (void)hipGetLastError();   // clear a stale error so it is not blamed on this call
     MOE_MARK();
-    MOE_STEP(launch_router_logits(x, router_w, bias, T, logits, s));
+    MOE_STEP(launch_router_and_shared_gateup(x, T, router_w, bias, logits, shared_w, hs, s));
+    MOE_MARK();
     MOE_STEP(launch_topk_rotate(logits, x, T, topk_idx, topk_w, xt, xt_scale, s));
     MOE_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, s));
-    MOE_MARK();
-    MOE_STEP(launch_shared_gateup(shared_w, x, T, hs, s));
     MOE_MARK();
     MOE_STEP(launch_gateup_gemv(codes, scales, xt, xt_scale, perm, active, T, act, s));
     MOE_MARK();
@@ -148,9 +146,7 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     MOE_MARK();
     MOE_STEP(launch_down_gemv(codes, scales, at, at_scale, active, T, o, s));
     MOE_MARK();
-    MOE_STEP(launch_shared_down(shared_w, hs, T, z, s));
-    MOE_MARK();
-    MOE_STEP(launch_combine(z, o, topk_w, pos, T, y, s));
+    MOE_STEP(launch_shared_down_combine(shared_w, hs, T, topk_w, pos, o, y, s));
     MOE_MARK();
 #undef MOE_STEP
 #undef MOE_MARK

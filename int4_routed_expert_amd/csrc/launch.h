@@ -7,9 +7,10 @@
 
 namespace moe_w4 {
 
-// Router: logits[T][256] = x R^T (+ bias).
-void launch_router_logits(const uint16_t *x, const uint16_t *router_w, const float *bias, int T,
-                          float *logits, hipStream_t s);
+// One launch: router logits[T][256] = x R^T (+ bias), and the shared expert's
+// h[T][1024] = bf16(silu(x Wsg^T) * (x Wsu^T)).
+void launch_router_and_shared_gateup(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
+                                     float *logits, const uint16_t *shared_w, uint16_t *hs, hipStream_t s);
 // Per token: top-6 of the logits, renormalised sigmoid weights, and the
 // Hadamard-rotated fp16 copy of x (with its power-of-two scale).
 void launch_topk_rotate(const float *logits, const uint16_t *x, int T, int *topk_idx, float *topk_w,
@@ -29,13 +30,10 @@ void launch_rotate_act(const float *act, int T, uint32_t *at, float *at_scale, h
 void launch_down_gemv(const uint8_t *codes, const uint16_t *scales, const uint32_t *at, const float *at_scale,
                       const int *slots, int T, float *o, hipStream_t s);
 
-// Shared expert (bf16 weights).
-void launch_shared_gateup(const uint16_t *shared_w, const uint16_t *x, int T, uint16_t *hs, hipStream_t s);
-void launch_shared_down(const uint16_t *shared_w, const uint16_t *hs, int T, float *z, hipStream_t s);
-
-// y = bf16(z + sum_j w_j o[pos[6t+j]]).
-void launch_combine(const float *z, const float *o, const float *topk_w, const int *pos, int T,
-                    uint16_t *y, hipStream_t s);
+// Shared expert down projection fused with the combine:
+// y = bf16(h Wsd^T + sum_j w_j o[pos[6t+j]]), slots in order.
+void launch_shared_down_combine(const uint16_t *shared_w, const uint16_t *hs, int T, const float *topk_w,
+                                const int *pos, const float *o, uint16_t *y, hipStream_t s);
 
 // Stack glue: x_bf16 = bf16(rmsnorm(resid)); resid += f32(y).
 void launch_rmsnorm_bf16(const float *resid, int T, uint16_t *x, hipStream_t s);

@@ -17,10 +17,10 @@
 // speed, so the product is a real (skinny) contraction; at T = 1 the MFMA
 // simply runs mostly empty while the weights stream.
 //
-// Tiling: a workgroup owns 16 output columns (for SwiGLU: 8 gate rows and the
-// same 8 up rows) and all tokens; its KS waves split K, each accumulating
+// Tiling: a workgroup owns CW output columns (for SwiGLU: CW/2 gate rows and
+// the same CW/2 up rows) and all tokens; its KS waves split K, each accumulating
 // 16x16 tiles of v_mfma_f32_16x16x32_bf16, and reduce through LDS.  Lane
-// (r = l % 16, g = l / 16) loads 32 consecutive K of weight row r and of
+// (r = l % 16, g = l / 16) loads 32 consecutive K of weight row r % CW and of
 // token row r, so every lane load is 64 contiguous bytes and the K order
 // inside an MFMA is the same for both operands.
 #include "common.h"
@@ -31,7 +31,29 @@ namespace moe_w4 {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-enum { kEpiStoreF32 = 0, kEpiSwiglu = 1 };
+enum { kEpiStoreF32 = 0, kEpiSwiglu = 1, kEpiCombine = 2 };
+
+// One job of a launch: a weight matrix, its output and its epilogue.  A launch
+// runs up to two jobs side by side (workgroups [0, n_blocks0) do job 0, the
+// rest job 1), so independent products share one launch and overlap.
+struct SkinnyJob {
+    const uint16_t *B;      // weight rows, K contiguous
+    int b_rows;             // rows of B the job reads
+    int b_split;            // SwiGLU: first up row (gate rows start at 0)
+    int n_blocks;           // workgroups of the job (CW output columns each)
+    int epi;                // kEpi*
+    const float *bias;      // kEpiStoreF32: added per column, or null
+    void *out;              // f32 [M][ldo] (store, combine: bf16), bf16 [M][ldo] (SwiGLU)
+    int ldo;
+    // kEpiCombine: y = bf16(acc + sum_j w[t][j] * o[pos[6t+j]][col])
+    const float *topk_w;
+    const int *pos;
+    const float *o;
+};
+
+struct SkinnyJobs {
+    SkinnyJob job[2];
+};
 
 __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
@@ -39,76 +61,102 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 }
 
 // MT: 16-row token tiles held at once (tokens are walked in chunks of 16*MT).
-// KS: waves per workgroup, splitting K.
-template <int MT, int KS, int EPI>
-__global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__ A, int M, int K,
-                                                    const uint16_t *__restrict__ B, int b_rows, int b_split,
-                                                    const float *__restrict__ bias, void *__restrict__ out,
-                                                    int ldo) {
+// KS: waves per workgroup, splitting K; KB: 128-wide K blocks per wave
+// (K = 128 * KS * KB).  CW: output columns per workgroup, 16 or 8.  With 8,
+// lanes r and r + 8 read the same weight row, which doubles the workgroups of
+// a small matrix (the 1024-row shared down projection would otherwise leave
+// half the CUs idle); the MFMA units have ample room for the duplicate columns.
+template <int MT, int KS, int KB, int CW>
+__global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__ A, int M, SkinnyJobs jobs) {
+    constexpr int K = 128 * KS * KB;
     __shared__ f32x4_t red[KS][MT][64];
+    const bool second = (int)blockIdx.x >= jobs.job[0].n_blocks;
+    const SkinnyJob &J = second ? jobs.job[1] : jobs.job[0];
+    const int blk = second ? (int)blockIdx.x - jobs.job[0].n_blocks : (int)blockIdx.x;
+    const int epi = J.epi;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int r = lane & 15, g = lane >> 4;
-    const int c0 = blockIdx.x * 16;   // first output column of the workgroup
-    // weight row of this lane's column
-    int brow;
-    if (EPI == kEpiSwiglu) brow = (r < 8) ? (c0 / 2 + r) : (b_split + c0 / 2 + r - 8);
-    else brow = c0 + r;
-    const int kw = K / KS;
-    const int k_begin = wave * kw;
+    constexpr int HC = CW / 2;
+    const int c = r & (CW - 1);   // column of this lane inside the workgroup's CW
+    const int c0 = blk * CW;      // first output column of the workgroup
+    // weight row of this lane's column: SwiGLU tiles are (CW/2 gate rows, the same CW/2 up rows)
+    const int brow = (epi == kEpiSwiglu) ? ((c < HC) ? (c0 / 2 + c) : (J.b_split + c0 / 2 + c - HC)) : (c0 + c);
+    const int k_begin = wave * (K / KS);
     // one wave-uniform descriptor over the weight matrix; the row is in the lane offset
-    const __amdgpu_buffer_rsrc_t bres = make_buf(B, (uint32_t)(b_rows * K * 2));
+    const __amdgpu_buffer_rsrc_t bres = make_buf(J.B, (uint32_t)(J.b_rows * K * 2));
     const uint32_t brow_off = (uint32_t)brow * K * 2;
+    uint4 b[KB][4];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            b[kb][s] = bload16_nt(bres, brow_off + (uint32_t)(k_begin + 128 * kb + 32 * g + 8 * s) * 2, 0);
 
     for (int m0 = 0; m0 < M; m0 += 16 * MT) {
         f32x4_t acc[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-        for (int k0 = k_begin; k0 < k_begin + kw; k0 += 128) {
-            uint4 b[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) b[s] = bload16_nt(bres, brow_off + (uint32_t)(k0 + 32 * g + 8 * s) * 2, 0);
+        for (int t = 0; t < MT; ++t) {
+            const int m = min(m0 + 16 * t + r, M - 1);
+            const uint4 *ap = reinterpret_cast<const uint4 *>(A + (size_t)m * K + k_begin + 32 * g);
+            uint4 a[KB][4];
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                const int m = min(m0 + 16 * t + r, M - 1);
-                const uint4 *ap = reinterpret_cast<const uint4 *>(A + (size_t)m * K + k0 + 32 * g);
-                uint4 a[4];
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) a[s] = ap[s];
+                for (int s = 0; s < 4; ++s) a[kb][s] = ap[16 * kb + s];
 #pragma unroll
-                for (int s = 0; s < 4; ++s) acc[t] = mfma16(a[s], b[s], acc[t]);
-            }
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) acc[t] = mfma16(a[kb][s], b[kb][s], acc[t]);
         }
-        // The accumulators are read right after the last MFMA of the loop; give
-        // the MFMA pipeline its wait states explicitly (the hazard is not always
-        // covered at the loop exit).
+        // The accumulators are read right after the last MFMA; give the MFMA
+        // pipeline its wait states explicitly (the hazard is not always
+        // covered by the compiler at a loop exit).
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
 #pragma unroll
         for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
         __syncthreads();
-        // wave t (< MT) finishes token tile t
+        // wave t (< MT) finishes token tile t; lanes with r < CW own the columns
         for (int t = wave; t < MT; t += KS) {
-            f32x4_t s = red[0][t][lane];
+            f32x4_t sum = red[0][t][lane];
 #pragma unroll
-            for (int w = 1; w < KS; ++w) s += red[w][t][lane];
-            // lane holds rows m0 + 16t + 4g + i of column c0 + r
-            if (EPI == kEpiStoreF32) {
-                const float bcol = bias ? bias[c0 + r] : 0.0f;
-                float *o = static_cast<float *>(out);
+            for (int w = 1; w < KS; ++w) sum += red[w][t][lane];
+            // lane holds rows m0 + 16t + 4g + i of column c0 + c
+            if (epi == kEpiStoreF32) {
+                const float bcol = J.bias ? J.bias[c0 + c] : 0.0f;
+                float *o = static_cast<float *>(J.out);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int m = m0 + 16 * t + 4 * g + i;
-                    if (m < M) o[(size_t)m * ldo + c0 + r] = s[i] + bcol;
+                    if (r < CW && m < M) o[(size_t)m * J.ldo + c0 + c] = sum[i] + bcol;
                 }
-            } else {
-                uint16_t *o = static_cast<uint16_t *>(out);
+            } else if (epi == kEpiSwiglu) {
+                uint16_t *o = static_cast<uint16_t *>(J.out);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float up = __shfl_xor(s[i], 8, kWave);   // column r+8 holds the up row
+                    const float up = __shfl_xor(sum[i], HC, kWave);   // column c + CW/2 holds the up row
                     const int m = m0 + 16 * t + 4 * g + i;
-                    if (r < 8 && m < M) {
-                        const float gv = s[i];
-                        o[(size_t)m * ldo + c0 / 2 + r] = f32_to_bf16(gv / (1.0f + expf(-gv)) * up);
+                    if (r < HC && m < M) {
+                        const float gv = sum[i];
+                        o[(size_t)m * J.ldo + c0 / 2 + c] = f32_to_bf16(gv / (1.0f + expf(-gv)) * up);
+                    }
+                }
+            } else {   // combine with the routed experts, in slot order
+                uint16_t *y = static_cast<uint16_t *>(J.out);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m = m0 + 16 * t + 4 * g + i;
+                    if (r < CW && m < M) {
+                        float acc_y = sum[i];
+#pragma unroll
+                        for (int j = 0; j < kTopK; ++j) {
+                            const float w = J.topk_w[(size_t)m * kTopK + j];
+                            const int p = J.pos[(size_t)m * kTopK + j];
+                            acc_y = fmaf(w, J.o[(size_t)p * kH + c0 + c], acc_y);
+                        }
+                        y[(size_t)m * J.ldo + c0 + c] = f32_to_bf16(acc_y);
                     }
                 }
             }
@@ -117,31 +165,35 @@ __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__
     }
 }
 
-template <int KS, int EPI>
-static void launch_skinny(const uint16_t *A, int M, int K, const uint16_t *B, int n_cols, int b_split,
-                          const float *bias, void *out, int ldo, hipStream_t s) {
-    dim3 grid(n_cols / 16), block(64 * KS);
-    const int b_rows = n_cols;   // weight rows the columns read
+template <int KB, int CW>
+static void launch_skinny_k(const uint16_t *A, int M, const SkinnyJobs &jobs, hipStream_t s) {
+    constexpr int KS = 8;
+    dim3 grid(jobs.job[0].n_blocks + jobs.job[1].n_blocks), block(64 * KS);
     if (M <= 16)
-        hipLaunchKernelGGL((k_skinny<1, KS, EPI>), grid, block, 0, s, A, M, K, B, b_rows, b_split, bias, out, ldo);
+        hipLaunchKernelGGL((k_skinny<1, KS, KB, CW>), grid, block, 0, s, A, M, jobs);
     else if (M <= 32)
-        hipLaunchKernelGGL((k_skinny<2, KS, EPI>), grid, block, 0, s, A, M, K, B, b_rows, b_split, bias, out, ldo);
+        hipLaunchKernelGGL((k_skinny<2, KS, KB, CW>), grid, block, 0, s, A, M, jobs);
     else
-        hipLaunchKernelGGL((k_skinny<4, KS, EPI>), grid, block, 0, s, A, M, K, B, b_rows, b_split, bias, out, ldo);
+        hipLaunchKernelGGL((k_skinny<4, KS, KB, CW>), grid, block, 0, s, A, M, jobs);
 }
 
-void launch_router_logits(const uint16_t *x, const uint16_t *router_w, const float *bias, int T,
-                          float *logits, hipStream_t s) {
-    launch_skinny<8, kEpiStoreF32>(x, T, kH, router_w, kE, 0, bias, logits, kE, s);
-}
+static SkinnyJob no_job() { return SkinnyJob{nullptr, 0, 0, 0, kEpiStoreF32, nullptr, nullptr, 0, nullptr, nullptr, nullptr}; }
 
-void launch_shared_gateup(const uint16_t *w, const uint16_t *x, int T, uint16_t *hs, hipStream_t s) {
+void launch_router_and_shared_gateup(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
+                                     float *logits, const uint16_t *shared_w, uint16_t *hs, hipStream_t s) {
+    SkinnyJobs jobs;
+    jobs.job[0] = SkinnyJob{router_w, kE, 0, kE / 16, kEpiStoreF32, bias, logits, kE, nullptr, nullptr, nullptr};
     // columns: 16-wide tiles of (8 gate rows, the same 8 up rows); up rows start at row 1024
-    launch_skinny<8, kEpiSwiglu>(x, T, kH, w, 2 * kIS, kIS, nullptr, hs, kIS, s);
+    jobs.job[1] = SkinnyJob{shared_w, 2 * kIS, kIS, 2 * kIS / 16, kEpiSwiglu, nullptr, hs, kIS, nullptr, nullptr, nullptr};
+    launch_skinny_k<kH / (128 * 8), 16>(x, T, jobs, s);
 }
 
-void launch_shared_down(const uint16_t *w, const uint16_t *hs, int T, float *z, hipStream_t s) {
-    launch_skinny<8, kEpiStoreF32>(hs, T, kIS, w + 2 * kSharedGateElems, kH, 0, nullptr, z, kH, s);
+void launch_shared_down_combine(const uint16_t *shared_w, const uint16_t *hs, int T, const float *topk_w,
+                                const int *pos, const float *o, uint16_t *y, hipStream_t s) {
+    SkinnyJobs jobs;
+    jobs.job[0] = SkinnyJob{shared_w + 2 * kSharedGateElems, kH, 0, kH / 8, kEpiCombine, nullptr, y, kH, topk_w, pos, o};
+    jobs.job[1] = no_job();
+    launch_skinny_k<kIS / (128 * 8), 8>(hs, T, jobs, s);
 }
 
 }  // namespace moe_w4

@@ -1,44 +1,9 @@
-// Weighted combine of the six routed outputs with the shared expert, and the
-// two element-wise steps of a layer stack (unit-gain RMS norm; residual add).
-//
-// Flint model card (Aijuus/flint-w4exp), introduction: the block output is the
-// top-6 routed experts plus the ungated shared expert.  The six slots are read
-// in slot order through pos, so the sum has a fixed order and no atomics.
+// The two element-wise steps of a layer stack: x_l = bf16(rmsnorm(resid)) with
+// unit gain and eps 1e-6, and resid += f32(y_l).
 #include "common.h"
 #include "launch.h"
 
 namespace moe_w4 {
-
-// One workgroup per token; thread i owns outputs [8i, 8i+8).
-__global__ __launch_bounds__(256) void k_combine(const float *__restrict__ z, const float *__restrict__ o,
-                                                 const float *__restrict__ topk_w,
-                                                 const int *__restrict__ pos, int T,
-                                                 uint16_t *__restrict__ y) {
-    const int t = blockIdx.x;
-    const int c = threadIdx.x * 8;
-    const float4 *zp = reinterpret_cast<const float4 *>(z + (size_t)t * kH + c);
-    float4 a = zp[0], b = zp[1];
-#pragma unroll
-    for (int j = 0; j < kTopK; ++j) {
-        const float w = topk_w[(size_t)t * kTopK + j];
-        const int p = pos[(size_t)t * kTopK + j];
-        const float4 *op = reinterpret_cast<const float4 *>(o + (size_t)p * kH + c);
-        const float4 oa = op[0], ob = op[1];
-        a.x = fmaf(w, oa.x, a.x); a.y = fmaf(w, oa.y, a.y); a.z = fmaf(w, oa.z, a.z); a.w = fmaf(w, oa.w, a.w);
-        b.x = fmaf(w, ob.x, b.x); b.y = fmaf(w, ob.y, b.y); b.z = fmaf(w, ob.z, b.z); b.w = fmaf(w, ob.w, b.w);
-    }
-    uint4 out;
-    out.x = (uint32_t)f32_to_bf16(a.x) | ((uint32_t)f32_to_bf16(a.y) << 16);
-    out.y = (uint32_t)f32_to_bf16(a.z) | ((uint32_t)f32_to_bf16(a.w) << 16);
-    out.z = (uint32_t)f32_to_bf16(b.x) | ((uint32_t)f32_to_bf16(b.y) << 16);
-    out.w = (uint32_t)f32_to_bf16(b.z) | ((uint32_t)f32_to_bf16(b.w) << 16);
-    reinterpret_cast<uint4 *>(y + (size_t)t * kH + c)[0] = out;
-}
-
-void launch_combine(const float *z, const float *o, const float *topk_w, const int *pos, int T,
-                    uint16_t *y, hipStream_t s) {
-    hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, s, z, o, topk_w, pos, T, y);
-}
 
 // x = bf16(resid / sqrt(mean(resid^2) + 1e-6)), one workgroup per token.
 __global__ __launch_bounds__(256) void k_rmsnorm_bf16(const float *__restrict__ resid, int T,
