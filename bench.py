@@ -1,6 +1,8 @@
 """Throughput of the int4 routed-expert MoE layer on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-cpu]
+    python bench.py --copy-calibration           # plain device copy, for HBM counter scaling
+    python bench.py --pmc-summary RUN.csv ...    # per-kernel means of rocprofv3 --pmc CSVs
 
 A step is one pass of the whole layer (router, sort, rotation, routed experts,
 shared expert, combine) over one batch of seeded synthetic tokens, with
@@ -46,7 +48,78 @@ def parse():
     ap.add_argument("--layers", type=int, default=0, help="distinct layers rotated through (0 = auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain device-to-device copy of known size (10 x 256 MiB)")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="CSV",
+                    help="print per-kernel mean counter values of rocprofv3 counter_collection CSVs")
     return ap.parse_args()
+
+
+# stage -> (kernel name prefix, sources that define it) for the HBM-traffic record
+STAGE_KERNELS = {
+    "router_shared_gateup": ("k_skinny", ["skinny_mfma.hip"]),
+    "topk_sort": ("k_topk_rotate", ["router.hip"]),
+    "routed_gateup": ("k_gateup_dec", ["experts_gemv.hip"]),
+    "rotate_act": ("k_rotate_act", ["experts_gemv.hip"]),
+    "routed_down": ("k_down_dec", ["experts_gemv.hip"]),
+    "shared_down_combine": ("k_skinny", ["skinny_mfma.hip"]),
+}
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "int4_routed_expert_amd", "csrc")
+
+
+def sources_digest(files):
+    """sha256 over common.h and the kernel's source files: a recorded traffic
+    figure is only valid for the kernel it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ["common.h"] + list(files):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload, stage):
+    """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    (profiles/hbm_traffic.txt), or None if absent or the kernel has changed."""
+    kern, files = STAGE_KERNELS.get(stage, (None, None))
+    path = os.path.join(HERE, "profiles", "hbm_traffic.txt")
+    if kern is None or not os.path.exists(path):
+        return None
+    digest = sources_digest(files)
+    for line in open(path):
+        f = line.split()
+        if len(f) == 6 and not line.startswith("#") and f[0] == workload and f[1] == kern and f[5] == digest:
+            return float(f[2]) + float(f[3])
+    return None
+
+
+def copy_calibration():
+    import torch
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 10}), flush=True)
+
+
+def pmc_summary(paths):
+    import csv
+    import collections
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in paths:
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+                agg[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    print(f"{'kernel':48s} {'dispatches':>10s}  counter means (per dispatch)")
+    for name, d in sorted(agg.items()):
+        n = max(len(v) for v in d.values())
+        vals = "  ".join(f"{c}={sum(v) / len(v):.1f}" for c, v in sorted(d.items()))
+        print(f"{name[:48]:48s} {n:10d}  {vals}")
 
 
 def cpu_baseline(cfg, T, x_bits, bias, budget_s):
@@ -83,10 +156,16 @@ def cpu_baseline(cfg, T, x_bits, bias, budget_s):
 
 def main():
     a = parse()
+    if a.pmc_summary:
+        pmc_summary(a.pmc_summary)
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported (the layer needs no "
               "collective: a multi-GPU deployment replicates it per GPU).", file=sys.stderr)
         sys.exit(2)
+    if a.copy_calibration:
+        copy_calibration()
+        return
     import torch
     import synth
     from int4_routed_expert_amd import moe_w4 as m
@@ -205,7 +284,7 @@ def main():
                                     f"{cfg['w_seed']}" + (", +3.0 bias on 26 experts (seed 3)" if bias is not None else ""),
                         "T": T, "layers_rotated": n_layers, "touched_experts": n_touched}
     result["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                          "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(a.config, dom),
                           "algorithmic_bytes": dom_bytes, "kernel_us": stage[dom] * 1e3}
     result["layer"] = {"algorithmic_bytes": layer_bytes, "hbm_gbs": layer_bytes / (ms * 1e-3) / 1e9,
                        "hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
