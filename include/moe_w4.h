@@ -89,10 +89,14 @@ extern "C" {
  *   active    i32 [256][8] one record per expert with tokens, ascending by expert:
  *                         {expert, offsets[expert], token count, first token,
  *                         second token (= first if one), 0, 0, 0}; records past
- *                         n_active hold expert -1 */
+ *                         n_active hold expert -1
+ *   chunks    i32 [n][4]  from T >= 128 on (MFMA grouped path): {expert, first sorted
+ *                         position, rows <= 64, 0} covering each expert's sorted
+ *                         positions in order, ascending by expert; n_chunks i32 [1]
+ *                         holds n.  (Written at every T; read only on that path.) */
 typedef struct moe_w4_ws_layout {
     size_t logits, topk_idx, topk_w, offsets, perm, pos, n_active, active;
-    size_t xt, xt_scale, act, at, at_scale, hs, o, z, sync;
+    size_t xt, xt_scale, act, at, at_scale, hs, o, chunks, n_chunks, sync;
     size_t total;
 } moe_w4_ws_layout;
 

@@ -42,7 +42,8 @@ moe_w4_ws_layout make_layout(int64_t T) {
     L.at_scale = take(4 * (kI / kG) * a);
     L.hs = take(2 * kIS * t);
     L.o = take(4 * kH * a);
-    L.z = take(4 * kH * t);
+    L.chunks = take(16 * (size_t)max_chunks((int)T));
+    L.n_chunks = take(4);
     L.sync = take(4096);
     L.total = off;
     return L;
@@ -81,6 +82,10 @@ const char *kStageNames[] = {"router_shared_gateup", "topk_sort", "routed_gateup
                              "shared_down_combine"};
 constexpr int kStages = sizeof(kStageNames) / sizeof(kStageNames[0]);
 
+// From this many tokens on, the routed experts run as MFMA grouped products
+// (chunks of up to 64 tokens per expert); below it, as streaming GEMVs.
+constexpr int kPrefillMinTokens = 128;
+
 template <class T_>
 T_ *ws_at(void *ws, size_t off) { return reinterpret_cast<T_ *>(static_cast<char *>(ws) + off); }
 
@@ -111,6 +116,9 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     float *at_scale = ws_at<float>(ws, L.at_scale);
     uint16_t *hs = ws_at<uint16_t>(ws, L.hs);
     float *o = ws_at<float>(ws, L.o);
+    int *chunks = ws_at<int>(ws, L.chunks);
+    int *n_chunks = ws_at<int>(ws, L.n_chunks);
+    const bool grouped = T >= kPrefillMinTokens;
 
     int stage = 0;
     auto mark = [&](void) -> int {
@@ -138,14 +146,23 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     MOE_STEP(launch_router_and_shared_gateup(x, T, router_w, bias, logits, shared_w, hs, s));
     MOE_MARK();
     MOE_STEP(launch_topk_rotate(logits, x, T, topk_idx, topk_w, xt, xt_scale, s));
-    MOE_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, s));
+    MOE_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, s));
     MOE_MARK();
-    MOE_STEP(launch_gateup_gemv(codes, scales, xt, xt_scale, perm, active, T, act, s));
-    MOE_MARK();
-    MOE_STEP(launch_rotate_act(act, T, at, at_scale, s));
-    MOE_MARK();
-    MOE_STEP(launch_down_gemv(codes, scales, at, at_scale, active, T, o, s));
-    MOE_MARK();
+    if (grouped) {
+        // gate/up also rotates a: the rotate_act stage is empty on this path
+        MOE_STEP(launch_gateup_mfma(codes, scales, xt, xt_scale, perm, chunks, n_chunks, T, at, at_scale, s));
+        MOE_MARK();
+        MOE_MARK();
+        MOE_STEP(launch_down_mfma(codes, scales, at, at_scale, chunks, n_chunks, T, o, s));
+        MOE_MARK();
+    } else {
+        MOE_STEP(launch_gateup_gemv(codes, scales, xt, xt_scale, perm, active, T, act, s));
+        MOE_MARK();
+        MOE_STEP(launch_rotate_act(act, T, at, at_scale, s));
+        MOE_MARK();
+        MOE_STEP(launch_down_gemv(codes, scales, at, at_scale, active, T, o, s));
+        MOE_MARK();
+    }
     MOE_STEP(launch_shared_down_combine(shared_w, hs, T, topk_w, pos, o, y, s));
     MOE_MARK();
 #undef MOE_STEP

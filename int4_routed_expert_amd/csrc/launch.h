@@ -18,8 +18,10 @@ void launch_topk_rotate(const float *logits, const uint16_t *x, int T, int *topk
 // Stable counting sort of the 6T assignments by expert (one workgroup).
 // slots: int[256][8] records {expert, first sorted position, count, first
 // token, second token, 0, 0, 0}, one per expert with tokens, then expert -1.
+// chunks: int[max_chunks(T)][4] records {expert, first sorted position, rows
+// (<= 64), 0} covering every expert's assignments; *n_chunks of them.
 void launch_sort(const int *topk_idx, int T, int *offsets, int *perm, int *pos, int *n_active,
-                 int *slots, hipStream_t s);
+                 int *slots, int *chunks, int *n_chunks, hipStream_t s);
 
 // Routed experts, GEMV form (few tokens per expert), driven by the slot records.
 void launch_gateup_gemv(const uint8_t *codes, const uint16_t *scales, const uint32_t *xt,
@@ -29,6 +31,16 @@ void launch_gateup_gemv(const uint8_t *codes, const uint16_t *scales, const uint
 void launch_rotate_act(const float *act, int T, uint32_t *at, float *at_scale, hipStream_t s);
 void launch_down_gemv(const uint8_t *codes, const uint16_t *scales, const uint32_t *at, const float *at_scale,
                       const int *slots, int T, float *o, hipStream_t s);
+
+// Routed experts, MFMA form (prefill): chunks of <= 64 assignments of one
+// expert against tiles of weight rows.  gate/up writes the rotated fp16
+// operands of the down projection directly (at, at_scale).
+int max_chunks(int T);
+void launch_gateup_mfma(const uint8_t *codes, const uint16_t *scales, const uint32_t *xt, const float *xt_scale,
+                        const int *perm, const int *chunks, const int *n_chunks, int T, uint32_t *at,
+                        float *at_scale, hipStream_t s);
+void launch_down_mfma(const uint8_t *codes, const uint16_t *scales, const uint32_t *at, const float *at_scale,
+                      const int *chunks, const int *n_chunks, int T, float *o, hipStream_t s);
 
 // Shared expert down projection fused with the combine:
 // y = bf16(h Wsd^T + sum_j w_j o[pos[6t+j]]), slots in order.

@@ -171,16 +171,19 @@ void launch_topk_rotate(const float *logits, const uint16_t *x, int T, int *topk
 // The result depends only on topk_idx: offsets, perm and pos are exact.
 // ---------------------------------------------------------------------------
 constexpr int kSortWaves = 16;
+constexpr int kSortChunkRows = 64;   // rows of one chunk of the MFMA grouped kernels
 
 __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx, int T,
                                                int *__restrict__ offsets, int *__restrict__ perm,
                                                int *__restrict__ pos, int *__restrict__ n_active,
-                                               int *__restrict__ slots) {
+                                               int *__restrict__ slots, int4 *__restrict__ chunks,
+                                               int *__restrict__ n_chunks) {
     __shared__ int cnt[kSortWaves][kE];
     __shared__ int tot[kE];
     __shared__ int offs[kE + 1];
     __shared__ int first2[kE][2];   // tokens at the first two sorted positions of each expert
     __shared__ int slot_e[kE + 1];  // expert of each active slot; [kE] = number of slots
+    __shared__ int chunk0[kE];      // first chunk of each expert
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int N = kTopK * T;
     const int per = ((N + kSortWaves * 64 - 1) / (kSortWaves * 64)) * 64;
@@ -201,41 +204,54 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
     }
     __syncthreads();
     if (wave == 0) {
-        // exclusive scan of the 256 totals, 4 per lane, and of the non-empty flags
-        int c[4], f[4], sc = 0, sf = 0;
+        // exclusive scans of the 256 totals (4 per lane), of the non-empty
+        // flags and of the chunk counts (kChunkRows assignments per chunk)
+        int c[4], f[4], k[4], sc = 0, sf = 0, sk = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             c[i] = tot[4 * lane + i];
             f[i] = c[i] > 0;
+            k[i] = (c[i] + kSortChunkRows - 1) / kSortChunkRows;
             sc += c[i];
             sf += f[i];
+            sk += k[i];
         }
-        int ic = sc, jf = sf;   // inclusive scans over lanes
+        int ic = sc, jf = sf, jk = sk;   // inclusive scans over lanes
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
             const int pc = __shfl_up(ic, d, kWave);
             const int pf = __shfl_up(jf, d, kWave);
-            if (lane >= d) { ic += pc; jf += pf; }
+            const int pk = __shfl_up(jk, d, kWave);
+            if (lane >= d) { ic += pc; jf += pf; jk += pk; }
         }
-        int ec = ic - sc, ef = jf - sf;
+        int ec = ic - sc, ef = jf - sf, ek = jk - sk;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = 4 * lane + i;
             offs[e] = ec;
             offsets[e] = ec;
+            chunk0[e] = ek;
             if (f[i]) slot_e[ef] = e;
             ec += c[i];
             ef += f[i];
+            ek += k[i];
         }
         if (lane == 63) {
             offs[kE] = ec;
             offsets[kE] = ec;
             *n_active = ef;
+            *n_chunks = ek;
             slot_e[kE] = ef;
         }
     }
     __syncthreads();
     for (int i = tid; i < kSortWaves * kE; i += blockDim.x) (&cnt[0][0])[i] += offs[i % kE];
+    // chunk list of the MFMA grouped path: {expert, first sorted position, rows, 0}
+    if (tid < kE) {
+        const int n = tot[tid];
+        for (int r = 0, q = chunk0[tid]; r < n; r += kSortChunkRows, ++q)
+            chunks[q] = make_int4(tid, offs[tid] + r, min(kSortChunkRows, n - r), 0);
+    }
     __syncthreads();
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int c0 = a0; c0 < a1; c0 += 64) {
@@ -276,9 +292,9 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
 }
 
 void launch_sort(const int *topk_idx, int T, int *offsets, int *perm, int *pos, int *n_active,
-                 int *slots, hipStream_t s) {
+                 int *slots, int *chunks, int *n_chunks, hipStream_t s) {
     hipLaunchKernelGGL(k_sort, dim3(1), dim3(1024), 0, s, topk_idx, T, offsets, perm, pos, n_active,
-                       slots);
+                       slots, reinterpret_cast<int4 *>(chunks), n_chunks);
 }
 
 }  // namespace moe_w4

@@ -79,6 +79,63 @@ def test_layer_small_T(m, layer0, T):
     report(f"small T={T}", P.compare(g, ref, label=f"T={T}"))
 
 
+# ------------------------------------------------- MFMA grouped path (T >= 128)
+def expected_chunks(offsets):
+    counts = np.diff(offsets)
+    return np.array([(e, offsets[e] + r, min(64, counts[e] - r), 0)
+                     for e in np.nonzero(counts)[0] for r in range(0, counts[e], 64)]).reshape(-1, 4)
+
+
+def read_chunks(m, ws, T):
+    n = int(m.ws_view(ws, T, "n_chunks", torch.int32, 1).item())
+    return m.ws_view(ws, T, "chunks", torch.int32, 4 * n).cpu().numpy().reshape(n, 4)
+
+
+def test_grouped_path_all_tokens(m, layer0):
+    """T = 128: every token against the oracle (chunks of 1..6 rows per expert)."""
+    T = 128
+    x = synth.gen_x(400, T)
+    ws = m.workspace(T)
+    g = P.run_gpu(m, x, layer0, ws=ws)
+    np.testing.assert_array_equal(read_chunks(m, ws, T), expected_chunks(g["offsets"]))
+    report("grouped T=128", P.compare(g, oracle_layer(x), label="grouped T=128"))
+
+
+@pytest.mark.parametrize("T", [129, 333])
+def test_grouped_path_sampled(m, layer0, T):
+    x = synth.gen_x(401 + T, T)
+    g = P.run_gpu(m, x, layer0)
+    rng = np.random.default_rng(T)
+    tokens = np.unique(np.concatenate([[0, T - 1], rng.choice(T, 22, replace=False)]))
+    report(f"grouped T={T}", P.compare(g, oracle_layer(x, tokens=tokens), tokens=tokens, label=f"grouped T={T}"))
+
+
+def test_grouped_chunks_of_a_hot_expert(m, layer0):
+    """One expert takes all 200 tokens: chunks of 64, 64, 64 and a ragged 8."""
+    T = 200
+    x = synth.gen_x(402, T)
+    bias = np.zeros(256, dtype=np.float32)
+    bias[17] = 100.0
+    ws = m.workspace(T)
+    g = P.run_gpu(m, x, layer0, bias=bias, ws=ws)
+    assert np.all(g["topk_idx"][:, 0] == 17)
+    ch = read_chunks(m, ws, T)
+    np.testing.assert_array_equal(ch, expected_chunks(g["offsets"]))
+    assert (ch[:, 0] == 17).sum() == 4 and ch[ch[:, 0] == 17][-1, 2] == 8
+    tokens = np.array([0, 1, 63, 64, 127, 128, 191, 192, 199])
+    report("grouped hot expert", P.compare(g, oracle_layer(x, bias=bias, tokens=tokens), tokens=tokens,
+                                           label="grouped hot expert"))
+
+
+def test_grouped_batch_invariance(m, layer0):
+    """Rows do not interact on the grouped path: the first 128 tokens of a
+    256-token batch give the bits of the 128-token batch."""
+    x = synth.gen_x(403, 256)
+    a = P.run_gpu(m, x[:128], layer0)
+    b = P.run_gpu(m, x, layer0)
+    np.testing.assert_array_equal(a["y_bits"], b["y_bits"][:128])
+
+
 # ------------------------------------------------------------- the workloads
 @pytest.mark.parametrize("name", ["decode_t1", "decode_t32"])
 def test_decode_workloads(m, layer0, name):
