@@ -22,7 +22,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_w4.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "router.hip", "skinny_mfma.hip", "experts_gemv.hip", "grouped_mfma.hip", "stack.hip",
+SOURCES = ["api.hip", "router.hip", "skinny_mfma.hip", "experts_gemv.hip", "grouped_mfma.hip", "dense_mfma.hip",
+           "stack.hip",
            "generate.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

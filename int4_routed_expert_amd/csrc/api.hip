@@ -83,7 +83,8 @@ const char *kStageNames[] = {"router_shared_gateup", "topk_sort", "routed_gateup
 constexpr int kStages = sizeof(kStageNames) / sizeof(kStageNames[0]);
 
 // From this many tokens on, the routed experts run as MFMA grouped products
-// (chunks of up to 64 tokens per expert); below it, as streaming GEMVs.
+// (chunks of up to 64 tokens per expert) and the router and shared expert as
+// LDS-tiled GEMMs; below it, as streaming GEMVs and few-row MFMA products.
 constexpr int kPrefillMinTokens = 128;
 
 template <class T_>
@@ -143,7 +144,10 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
 
     (void)hipGetLastError();   // clear a stale error so it is not blamed on this call
     MOE_MARK();
-    MOE_STEP(launch_router_and_shared_gateup(x, T, router_w, bias, logits, shared_w, hs, s));
+    if (grouped)
+        MOE_STEP(launch_router_and_shared_gateup_dense(x, T, router_w, bias, logits, shared_w, hs, s));
+    else
+        MOE_STEP(launch_router_and_shared_gateup(x, T, router_w, bias, logits, shared_w, hs, s));
     MOE_MARK();
     MOE_STEP(launch_topk_rotate(logits, x, T, topk_idx, topk_w, xt, xt_scale, s));
     MOE_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, s));
@@ -163,7 +167,10 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
         MOE_STEP(launch_down_gemv(codes, scales, at, at_scale, active, T, o, s));
         MOE_MARK();
     }
-    MOE_STEP(launch_shared_down_combine(shared_w, hs, T, topk_w, pos, o, y, s));
+    if (grouped)
+        MOE_STEP(launch_shared_down_combine_dense(shared_w, hs, T, topk_w, pos, o, y, s));
+    else
+        MOE_STEP(launch_shared_down_combine(shared_w, hs, T, topk_w, pos, o, y, s));
     MOE_MARK();
 #undef MOE_STEP
 #undef MOE_MARK

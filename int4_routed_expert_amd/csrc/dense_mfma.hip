@@ -1,0 +1,244 @@
+// bf16 x bf16 products with many rows (prefill sizes) on the MFMA units:
+// the router logits and the shared expert, the same contractions as the
+// few-row kernels of skinny_mfma.hip (router rows bf16 widened exactly with
+// fp32 sums, NInfer README of Flint, "What is inside"; ungated bf16 SwiGLU
+// shared expert of width 1024, Flint model card, Aijuus/flint-w4exp,
+// introduction and table row "weights").  bf16 products are exact and
+// v_mfma_f32_32x32x16_bf16 sums them in fp32.
+//
+// Tiling: a workgroup computes a 128 x 128 output tile with 4 waves (2 x 2,
+// 64 x 64 each: 2 x 2 MFMA tiles).  K advances 32 at a time: operands are
+// loaded into registers two steps ahead and written to a double-buffered LDS
+// tile one step ahead; rows of 32 bf16 (64 bytes) are stored with the
+// 16-byte group position swizzled by bits 2..3 of the row, so the MFMA reads
+// of 16 consecutive rows hit 16 distinct 4-bank slots.
+//
+// Epilogues: fp32 store (+ per-column bias) for the logits; SwiGLU for the
+// shared gate/up, whose 128-column tile is 64 gate rows and the same 64 up
+// rows (each wave's two 32-column MFMA tiles are a gate tile and its up tile,
+// so silu(g) * u pairs registers of one lane); and the combine of the layer
+// for the shared down projection: y = bf16(z + sum_j w_j o[pos[6t + j]]),
+// slots in order.
+#include "common.h"
+#include "launch.h"
+
+namespace moe_w4 {
+
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kTile = 128;
+constexpr int kStepK = 32;                       // bf16 per row per ring slot (64 bytes)
+constexpr int kSlotBytes = kTile * kStepK * 2;   // 8 KB per operand per slot
+constexpr int kXcds = 8;
+
+enum { kEpiStore = 0, kEpiSwiglu = 1, kEpiCombine = 2 };
+
+struct DenseJob {
+    const uint16_t *B;   // weight rows, K contiguous
+    int n_tiles;         // 128-column tiles of the job
+    int epi;
+    int up_row;          // SwiGLU: first up row (gate rows start at 0)
+    const float *bias;   // kEpiStore: per column, or null
+    void *out;           // f32 (store) or bf16 (SwiGLU, combine) [M][ldo]
+    int ldo;
+    const float *topk_w; // combine
+    const int *pos;
+    const float *o;
+};
+struct DenseJobs {
+    DenseJob job[2];
+};
+
+__device__ __forceinline__ f32x16_t mfma_bf16(uint4 a, uint4 b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                   0, 0, 0);
+}
+
+__device__ __forceinline__ void mfma_drain() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
+}
+
+}  // namespace
+
+// A: [M][K] bf16 rows.  Work item: (m tile, job n tile).
+template <int K>
+__global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__ A, int M, int m_tiles,
+                                                    DenseJobs jobs) {
+    constexpr int kSteps = K / kStepK;
+    static_assert(kSteps >= 3, "pipeline prologue");
+    __shared__ __attribute__((aligned(16))) uint8_t sa[2][kSlotBytes], sb[2][kSlotBytes];
+
+    // work item: XCD-aware when there are enough m tiles (each XCD keeps a
+    // few m tiles' A rows in its L2 and walks all n tiles), else linear
+    const int n_total = jobs.job[0].n_tiles + jobs.job[1].n_tiles;
+    int mt, nt;
+    if (m_tiles >= kXcds) {
+        const int b = blockIdx.x, xcd = b % kXcds, k = b / kXcds;
+        mt = xcd + kXcds * (k / n_total);
+        nt = k % n_total;
+    } else {
+        mt = blockIdx.x / n_total;
+        nt = blockIdx.x % n_total;
+    }
+    if (mt >= m_tiles) return;
+    const bool second = nt >= jobs.job[0].n_tiles;
+    const DenseJob &J = second ? jobs.job[1] : jobs.job[0];
+    if (second) nt -= jobs.job[0].n_tiles;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int n = lane & 31, g = lane >> 5;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int m0 = mt * kTile;
+
+    // B rows of this tile: tile column c (0..127) -> weight row.  SwiGLU:
+    // wave column half wn covers tile columns [64wn, 64wn+64): 32 gate rows
+    // then the same 32 up rows
+    auto b_row = [&](int c) -> int {
+        if (J.epi != kEpiSwiglu) return nt * kTile + c;
+        const int half = c >> 6, cc = c & 63;
+        const int r = nt * 64 + 32 * half + (cc & 31);
+        return (cc < 32) ? r : J.up_row + r;
+    };
+
+    // staging: per step each thread moves 16-byte chunks c = tid, tid + 256
+    // of A and of B (row c / 4, position c % 4 holding group (c % 4) ^ ((row >> 2) & 3));
+    // raw buffer loads keep their program order, two steps ahead
+    const __amdgpu_buffer_rsrc_t ares = make_buf(A, 0xffffffffu);
+    const __amdgpu_buffer_rsrc_t bres = make_buf(J.B, 0xffffffffu);
+    uint32_t aoff[2], boff[2];
+    int ldst[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int c = tid + 256 * i, r = c >> 2, pos = c & 3, grp = pos ^ ((r >> 2) & 3);
+        aoff[i] = (uint32_t)min(m0 + r, M - 1) * (K * 2) + grp * 16;
+        boff[i] = (uint32_t)b_row(r) * (K * 2) + grp * 16;
+        ldst[i] = r * 64 + pos * 16;
+    }
+    uint4 stg[2][4];
+    auto load = [&](int set, int step) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            stg[set][i] = bload16(ares, aoff[i] + step * 64, 0);
+            stg[set][2 + i] = bload16(bres, boff[i] + step * 64, 0);
+        }
+    };
+    auto store = [&](int set, int slot) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            *reinterpret_cast<uint4 *>(sa[slot] + ldst[i]) = stg[set][i];
+            *reinterpret_cast<uint4 *>(sb[slot] + ldst[i]) = stg[set][2 + i];
+        }
+    };
+
+    f32x16_t acc[2][2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int y = 0; y < 2; ++y)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[x][y][i] = 0.0f;
+
+    load(0, 0);
+    load(1, 1);
+    store(0, 0);
+    __syncthreads();
+
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+        const int slot = s & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 2 < kSteps) load(slot, s + 2);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int grp = 2 * g + j;
+            uint4 a[2], b[2];
+#pragma unroll
+            for (int x = 0; x < 2; ++x) {
+                const int r = 64 * wm + 32 * x + n;
+                a[x] = *reinterpret_cast<const uint4 *>(sa[slot] + r * 64 + ((grp ^ ((r >> 2) & 3)) * 16));
+            }
+#pragma unroll
+            for (int y = 0; y < 2; ++y) {
+                const int r = 64 * wn + 32 * y + n;
+                b[y] = *reinterpret_cast<const uint4 *>(sb[slot] + r * 64 + ((grp ^ ((r >> 2) & 3)) * 16));
+            }
+#pragma unroll
+            for (int x = 0; x < 2; ++x)
+#pragma unroll
+                for (int y = 0; y < 2; ++y) acc[x][y] = mfma_bf16(a[x], b[y], acc[x][y]);
+        }
+        // the next step's operands (loaded during the previous step) into the
+        // other LDS slot, which every wave finished reading before the last barrier
+        if (s + 1 < kSteps) store(slot ^ 1, slot ^ 1);
+        __syncthreads();
+    }
+    mfma_drain();
+
+    // epilogue: lane holds rows 64wm + 32x + 8(i/4) + 4g + (i%4), column 64wn + 32y + n
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int m = m0 + 64 * wm + 32 * x + 8 * (i >> 2) + 4 * g + (i & 3);
+            if (m >= M) continue;
+            if (J.epi == kEpiStore) {
+                float *o = static_cast<float *>(J.out);
+#pragma unroll
+                for (int y = 0; y < 2; ++y) {
+                    const int c = nt * kTile + 64 * wn + 32 * y + n;
+                    o[(size_t)m * J.ldo + c] = acc[x][y][i] + (J.bias ? J.bias[c] : 0.0f);
+                }
+            } else if (J.epi == kEpiSwiglu) {
+                const float gv = acc[x][0][i], uv = acc[x][1][i];
+                const int r = nt * 64 + 32 * wn + n;
+                static_cast<uint16_t *>(J.out)[(size_t)m * J.ldo + r] = f32_to_bf16(gv / (1.0f + expf(-gv)) * uv);
+            } else {
+#pragma unroll
+                for (int y = 0; y < 2; ++y) {
+                    const int c = nt * kTile + 64 * wn + 32 * y + n;
+                    float v = acc[x][y][i];
+#pragma unroll
+                    for (int j = 0; j < kTopK; ++j) {
+                        const float w = J.topk_w[(size_t)m * kTopK + j];
+                        const int p = J.pos[(size_t)m * kTopK + j];
+                        v = fmaf(w, J.o[(size_t)p * kH + c], v);
+                    }
+                    static_cast<uint16_t *>(J.out)[(size_t)m * J.ldo + c] = f32_to_bf16(v);
+                }
+            }
+        }
+    }
+}
+
+static DenseJob no_dense_job() { return DenseJob{nullptr, 0, kEpiStore, 0, nullptr, nullptr, 0, nullptr, nullptr, nullptr}; }
+
+template <int K>
+static void launch_dense(const uint16_t *A, int M, const DenseJobs &jobs, hipStream_t s) {
+    const int m_tiles = (M + kTile - 1) / kTile;
+    const int n_total = jobs.job[0].n_tiles + jobs.job[1].n_tiles;
+    const int grid = (m_tiles >= kXcds) ? kXcds * ((m_tiles + kXcds - 1) / kXcds) * n_total : m_tiles * n_total;
+    hipLaunchKernelGGL(k_dense_mfma<K>, dim3(grid), dim3(256), 0, s, A, M, m_tiles, jobs);
+}
+
+void launch_router_and_shared_gateup_dense(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
+                                           float *logits, const uint16_t *shared_w, uint16_t *hs, hipStream_t s) {
+    DenseJobs jobs;
+    jobs.job[0] = DenseJob{router_w, kE / kTile, kEpiStore, 0, bias, logits, kE, nullptr, nullptr, nullptr};
+    jobs.job[1] = DenseJob{shared_w, kIS / 64, kEpiSwiglu, kIS, nullptr, hs, kIS, nullptr, nullptr, nullptr};
+    launch_dense<kH>(x, T, jobs, s);
+}
+
+void launch_shared_down_combine_dense(const uint16_t *shared_w, const uint16_t *hs, int T, const float *topk_w,
+                                      const int *pos, const float *o, uint16_t *y, hipStream_t s) {
+    DenseJobs jobs;
+    jobs.job[0] = DenseJob{shared_w + 2 * kSharedGateElems, kH / kTile, kEpiCombine, 0, nullptr, y, kH, topk_w, pos, o};
+    jobs.job[1] = no_dense_job();
+    launch_dense<kIS>(hs, T, jobs, s);
+}
+
+}  // namespace moe_w4

@@ -47,6 +47,12 @@ void launch_down_mfma(const uint8_t *codes, const uint16_t *scales, const uint32
 void launch_shared_down_combine(const uint16_t *shared_w, const uint16_t *hs, int T, const float *topk_w,
                                 const int *pos, const float *o, uint16_t *y, hipStream_t s);
 
+// The same two launches for many tokens (prefill sizes): LDS-tiled MFMA GEMMs.
+void launch_router_and_shared_gateup_dense(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
+                                           float *logits, const uint16_t *shared_w, uint16_t *hs, hipStream_t s);
+void launch_shared_down_combine_dense(const uint16_t *shared_w, const uint16_t *hs, int T, const float *topk_w,
+                                      const int *pos, const float *o, uint16_t *y, hipStream_t s);
+
 // Stack glue: x_bf16 = bf16(rmsnorm(resid)); resid += f32(y).
 void launch_rmsnorm_bf16(const float *resid, int T, uint16_t *x, hipStream_t s);
 void launch_residual_add(float *resid, const uint16_t *y, int T, hipStream_t s);
