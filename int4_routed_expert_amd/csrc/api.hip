@@ -83,7 +83,7 @@ const char *kStageNames[] = {"router_shared_gateup", "topk_sort", "routed_gateup
 constexpr int kStages = sizeof(kStageNames) / sizeof(kStageNames[0]);
 
 // From this many tokens on, the routed experts run as MFMA grouped products
-// (chunks of up to 64 tokens per expert) and the router and shared expert as
+// (chunks of up to 96 tokens per expert) and the router and shared expert as
 // LDS-tiled GEMMs; below it, as streaming GEMVs and few-row MFMA products.
 constexpr int kPrefillMinTokens = 128;
 

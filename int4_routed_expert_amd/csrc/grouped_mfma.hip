@@ -6,7 +6,7 @@
 // layout (NInfer README of Flint, "What is inside"): per expert, gate rows then
 // up rows (2 x 512, K = 2048) and 2,048 down rows (K = 512).
 //
-// Work unit: a chunk of at most 64 sorted assignments of one expert (the chunk
+// Work unit: a chunk of at most 96 sorted assignments of one expert (the chunk
 // list comes from the sort) times a tile of weight rows.  Every code byte of
 // the tile is read from HBM once per chunk and turned into exact fp16 values
 // in registers: the mask trick of int4x8_to_q gives 1024+u and 1024+16u, and
@@ -14,8 +14,8 @@
 // activations are the fp16 operands the rotation wrote (odd positions of each
 // 8-group pre-divided by 16, exact), so each 8-group of codes is one MFMA B
 // operand and the matching 16 bytes of activations one A operand.  Products
-// are exact and the MFMA sums them in fp32; the partial sum of each 128-block
-// is scaled by its bf16 scale in fp32, as the format defines.
+// are exact and the MFMA sums them in fp32; each 128-block's bf16 scale
+// multiplies its codes exactly (see codes_to_f16_scaled) or its partial sum.
 //
 // The K order inside an MFMA is free as long as A and B agree, so lane group
 // g = lane / 32 of k-slice j in K-step q of a block takes 8-group 8g + 4q + j:
@@ -38,8 +38,9 @@ namespace moe_w4 {
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kChunkRows = 64;   // assignments per chunk (two 32-row MFMA tiles)
+constexpr int kChunkRows = 96;   // assignments per chunk: up to three 32-row MFMA tiles
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
@@ -57,6 +58,19 @@ __device__ __forceinline__ uint4 codes_to_f16(uint32_t w) {
     r.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, q.q1) + odd);
     r.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, q.q2) + even);
     r.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, q.q3) + odd);
+    return r;
+}
+
+// The same times a scale s' (fp16, both halves): c * s' and 16c * s' are
+// exact in fp16 when s' has at most 8 significant bits and the products stay
+// inside the fp16 range (|c| <= 8 adds at most 3 bits: 11 significant bits).
+__device__ __forceinline__ uint4 codes_to_f16_scaled(uint32_t w, half2_t s) {
+    const uint4 c = codes_to_f16(w);
+    uint4 r;
+    r.x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, c.x) * s);
+    r.y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, c.y) * s);
+    r.z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, c.z) * s);
+    r.w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, c.w) * s);
     return r;
 }
 
@@ -80,19 +94,6 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
     return v;
 }
 
-// chunk index and tile index of this workgroup (XCD-aware deal, see above)
-__device__ __forceinline__ void chunk_tile(int tiles, int &chunk, int &tile) {
-    const int b = blockIdx.x, xcd = b % kXcds, k = b / kXcds;
-    chunk = (k / tiles) * kXcds + xcd;
-    tile = k % tiles;
-}
-
-// =========================================================================
-// gate/up + SwiGLU + rotation of a
-// =========================================================================
-constexpr int kGuBuf = kChunkRows * 256;          // one A block: 64 rows x 128 fp16, swizzled
-constexpr int kGuRing = 3;                          // A blocks in LDS: current and two in flight
-
 // vmcnt-only wait (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and
 // lgkmcnt at their maxima, i.e. not waited for)
 template <int N>
@@ -107,8 +108,6 @@ __device__ __forceinline__ void wait_vmcnt_lds() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
 }
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-
 // Workgroup barrier without the release/acquire fences of __syncthreads:
 // those make every wave wait for all of its direct global->LDS loads
 // (vmcnt 0), which would drain the prefetch.  The callers wait for exactly
@@ -120,10 +119,65 @@ __device__ __forceinline__ void block_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// The A block of the chunk's 64 rows lives in LDS as [row][16 groups of 16 B]
-// with group position grp ^ (row & 15): unpadded rows (so one wave's direct
+// compile-time tile count for the main loops (one straight-line copy per
+// count instead of a branch around every MFMA)
+template <int N>
+struct Tiles {
+    static constexpr int value = N;
+};
+template <class F>
+__device__ __forceinline__ void with_tiles(int n_mt, F &&f) {
+    if (n_mt >= 3)
+        f(Tiles<3>{});
+    else if (n_mt == 2)
+        f(Tiles<2>{});
+    else
+        f(Tiles<1>{});
+}
+
+// chunk index and tile index of this workgroup (XCD-aware deal, see above)
+__device__ __forceinline__ void chunk_tile(int tiles, int &chunk, int &tile) {
+    const int b = blockIdx.x, xcd = b % kXcds, k = b / kXcds;
+    chunk = (k / tiles) * kXcds + xcd;
+    tile = k % tiles;
+}
+
+// Power-of-two exponent k making the largest of a row's bf16 scales land in
+// [2^7, 2^8) after multiplication by 2^k (0 if all scales are zero): the
+// largest B operand, 16c * s' with |16c| <= 128, then stays below 2^15.
+__device__ __forceinline__ int scale_shift(const uint4 &a, const uint4 &b) {
+    uint32_t e = 0;
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        e = max(e, (w[i] >> 7) & 0xffu);
+        e = max(e, (w[i] >> 23) & 0xffu);
+    }
+    return e ? 134 - (int)e : 0;
+}
+// bf16 scale s (low or high half of a word) -> fp16 s * 2^k in both halves
+__device__ __forceinline__ half2_t scaled_half2(uint32_t word2, int hi, int k) {
+    const float f = ldexpf(hi ? bf16hi(word2) : bf16lo(word2), k);
+    const _Float16 h = (_Float16)f;
+    return half2_t{h, h};
+}
+
+// =========================================================================
+// gate/up + SwiGLU + rotation of a
+//
+// The chunk's A block (up to 96 rows) lives in LDS as [row][16 groups of 16 B]
+// with group position grp ^ (row & 15): unpadded rows (one wave's direct
 // global->LDS load fills 4 whole rows) whose MFMA reads still hit 16
-// different 4-bank slots for 16 consecutive rows.
+// different 4-bank slots for 16 consecutive rows.  A three-slot ring keeps
+// two blocks in flight; the codes run three blocks ahead in registers.
+// Scales are folded into the B operand (codes_to_f16_scaled with the row's
+// scales normalised by one power of two), so the MFMA accumulates over the
+// whole of K and the normalisation is undone once at the end.
+// =========================================================================
+constexpr int kGuBuf = kChunkRows * 256;   // one A block: 96 rows x 128 fp16
+constexpr int kGuRing = 3;
+constexpr int kGuCodeRing = 4;
+
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gateup_mfma(
     const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, const uint32_t *__restrict__ xt,
     const float *__restrict__ xt_scale, const int *__restrict__ perm, const int4 *__restrict__ chunks,
@@ -139,34 +193,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     if (chunk >= *n_chunks) return;
     const int4 ch = chunks[chunk];
     const int e = uniform(ch.x), row0 = uniform(ch.y), rows = uniform(ch.z);
+    const int n_mt = uniform((rows + 31) >> 5);   // 32-row MFMA tiles in use
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int n = lane & 31, g = lane >> 5;
     constexpr int kBlocks = kH / kG;
 
     if (tid < kChunkRows) row_p[tid] = xt_scale[perm[row0 + min(tid, rows - 1)] / kTopK];
-    // A loads: wave w fills rows 16w..16w+15 of a block, 4 rows (1 KB) per
-    // instruction; lane l writes position l & 15 of row 16w + 4i + (l >> 4)
-    const uint8_t *asrc[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = 16 * wave + 4 * i + (lane >> 4);
-        const int tok = perm[row0 + min(r, rows - 1)] / kTopK;
-        asrc[i] = reinterpret_cast<const uint8_t *>(xt + (size_t)tok * (kH / 2)) + ((lane & 15) ^ (r & 15)) * 16;
-    }
-    auto issue_a = [&](int slot, int blk) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds(asrc[i] + blk * 256,
-                                             (lds_void_t *)(slot_ptr(slot) + (16 * wave + 4 * i) * 256), 16, 0, 0);
-    };
-
-    // this lane's gate and up rows; codes stream two blocks ahead
+    // this lane's gate and up rows
     const int gr = kG * nt + 32 * wave + n;
     const __amdgpu_buffer_rsrc_t cres = make_buf(codes + (size_t)e * kCodeBytesPerExpert, (uint32_t)kCodeBytesGu);
     const __amdgpu_buffer_rsrc_t sres = make_buf(scales + (size_t)e * kScalesPerExpert, (uint32_t)kScalesGu * 2);
     const uint32_t goff = (uint32_t)gr * (kH / 2) + 32 * g, uoff = goff + (uint32_t)kPlaneGateBytes;
     const uint32_t gsoff = (uint32_t)gr * 32, usoff = gsoff + (uint32_t)kScalesGate * 2;
-    uint4 cb[3][4];
+    uint4 cb[kGuCodeRing][4];
     auto fetch = [&](int slot, int blk) {
         const uint32_t o = (uint32_t)blk * 64;
         cb[slot][0] = bload16(cres, goff + o, 0);
@@ -181,95 +220,105 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     su[0] = bload16(sres, usoff, 0);
     su[1] = bload16(sres, usoff + 16, 0);
 
-    // issue order per block: codes(b+2) (4 loads) then A(b+2) (4 loads); the
-    // vmcnt waits below count on it: waiting for A(b+1) also covers codes(b+1)
+    const int kg = scale_shift(sg[0], sg[1]), ku = scale_shift(su[0], su[1]);
+
+    // a = silu(g) * u for this workgroup's 128 columns goes into LDS (fp32)
+    // after the main loop: rows 0..47 in ring0, rows 48..95 in ring1
+    auto act_row = [&](int m) -> float * {
+        return reinterpret_cast<float *>(m < 48 ? ring0 : ring1) + (m < 48 ? m : m - 48) * kG;
+    };
+    with_tiles(n_mt, [&](auto tiles) {
+    constexpr int MT = decltype(tiles)::value;
+    // A loads of the 32*MT rows in use: NI instructions per wave, 4 rows (1 KB)
+    // each; lane l writes position l & 15 of row 4*(NI*w + i) + (l >> 4)
+    constexpr int NI = 2 * MT;
+    const uint8_t *asrc[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int r = 4 * (NI * wave + i) + (lane >> 4);
+        const int tok = perm[row0 + min(r, rows - 1)] / kTopK;
+        asrc[i] = reinterpret_cast<const uint8_t *>(xt + (size_t)tok * (kH / 2)) + ((lane & 15) ^ (r & 15)) * 16;
+    }
+    auto issue_a = [&](int slot, int blk) {
+#pragma unroll
+        for (int i = 0; i < NI; ++i)
+            __builtin_amdgcn_global_load_lds(asrc[i] + blk * 256,
+                                             (lds_void_t *)(slot_ptr(slot) + 4 * (NI * wave + i) * 256), 16, 0, 0);
+    };
+    // issue order: codes(0..2), A(0), A(1); then per block b: codes(b+3) (4
+    // loads), A(b+2) (NI loads).  The vmcnt waits below count on this order:
+    // waiting for A(b+1) also covers every codes block up to b+2.
     __builtin_amdgcn_sched_barrier(0);
     fetch(0, 0);
-    issue_a(0, 0);
     fetch(1, 1);
+    fetch(2, 2);
+    issue_a(0, 0);
     issue_a(1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    wait_vmcnt_lds<8>();   // codes(0), A(0) and the row_p stores done (codes(1), A(1) may be in flight)
+    wait_vmcnt_lds<NI>();   // A(0) and the row_p stores done (A(1) may be in flight)
     block_barrier();
 
-    f32x16_t accg[2], accu[2];
+    f32x16_t accg[MT], accu[MT];
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < MT; ++h)
 #pragma unroll
         for (int i = 0; i < 16; ++i) accg[h][i] = accu[h][i] = 0.0f;
 
 #pragma unroll
     for (int b = 0; b < kBlocks; ++b) {
         const uint8_t *buf = slot_ptr(b % kGuRing);
-        const int cs = b % 3;
+        const int cs = b % kGuCodeRing;
         __builtin_amdgcn_sched_barrier(0);
-        if (b + 2 < kBlocks) {
-            fetch((b + 2) % 3, b + 2);
-            issue_a((b + 2) % kGuRing, b + 2);
-        }
+        if (b + 3 < kBlocks) fetch((b + 3) % kGuCodeRing, b + 3);
+        if (b + 2 < kBlocks) issue_a((b + 2) % kGuRing, b + 2);
         __builtin_amdgcn_sched_barrier(0);
-        f32x16_t dg[2], du[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) dg[h][i] = du[h][i] = 0.0f;
+        const half2_t s_g = scaled_half2(word(sg[b >> 3], (b >> 1) & 3), b & 1, kg);
+        const half2_t s_u = scaled_half2(word(su[b >> 3], (b >> 1) & 3), b & 1, ku);
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint4 bg = codes_to_f16(word(cb[cs][q], j));
-                const uint4 bu = codes_to_f16(word(cb[cs][2 + q], j));
+                const uint4 bg = codes_to_f16_scaled(word(cb[cs][q], j), s_g);
+                const uint4 bu = codes_to_f16_scaled(word(cb[cs][2 + q], j), s_u);
                 const int grp = 8 * g + 4 * q + j;
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
+                for (int h = 0; h < MT; ++h) {
                     const uint4 a =
                         *reinterpret_cast<const uint4 *>(buf + (32 * h + n) * 256 + ((grp ^ (n & 15)) * 16));
-                    dg[h] = mfma32(a, bg, dg[h]);
-                    du[h] = mfma32(a, bu, du[h]);
+                    accg[h] = mfma32(a, bg, accg[h]);
+                    accu[h] = mfma32(a, bu, accu[h]);
                 }
             }
         }
-        mfma_drain();
-        const uint32_t swg = word(sg[b >> 3], (b >> 1) & 3), swu = word(su[b >> 3], (b >> 1) & 3);
-        const float s_g = (b & 1) ? bf16hi(swg) : bf16lo(swg);
-        const float s_u = (b & 1) ? bf16hi(swu) : bf16lo(swu);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                accg[h][i] = fmaf(s_g, dg[h][i], accg[h][i]);
-                accu[h][i] = fmaf(s_u, du[h][i], accu[h][i]);
-            }
         // codes(b+1) and A(b+1) must have landed for every wave before the
-        // next block; after them only codes(b+2) and A(b+2) were issued
+        // next block; after A(b+1) only codes(b+3) and A(b+2) were issued
         __builtin_amdgcn_sched_barrier(0);
-        if (b + 2 < kBlocks)
-            wait_vmcnt<8>();
+        if (b + 3 < kBlocks)
+            wait_vmcnt<4 + NI>();
+        else if (b + 2 < kBlocks)
+            wait_vmcnt<NI>();
         else if (b + 1 < kBlocks)
             wait_vmcnt<0>();
         block_barrier();
     }
+    mfma_drain();
     __syncthreads();
-
-    // a = silu(g) * u for this workgroup's 128 columns, into LDS (fp32):
-    // rows 0..31 in ring0, rows 32..63 in ring1, 128 floats per row
-    auto act_row = [&](int m) -> float * {
-        return reinterpret_cast<float *>(m < 32 ? ring0 : ring1) + (m & 31) * kG;
-    };
+    const float gscale = ldexpf(1.0f, -kg), uscale = ldexpf(1.0f, -ku);
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
+    for (int h = 0; h < MT; ++h)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const int m = 32 * h + 8 * (i >> 2) + 4 * g + (i & 3);
             const float p = row_p[m];
-            const float gv = accg[h][i] * p, uv = accu[h][i] * p;
+            const float gv = accg[h][i] * gscale * p, uv = accu[h][i] * uscale * p;
             act_row(m)[32 * wave + n] = gv / (1.0f + expf(-gv)) * uv;
         }
+    });
     __syncthreads();
 
     // fwht128 of each row: 16 lanes per row, 8 values per lane, 4 rows per pass
     const int rl = lane & 15;
-    for (int r0 = 4 * wave; r0 < kChunkRows; r0 += 16) {
+    for (int r0 = 4 * wave; r0 < 32 * n_mt; r0 += 16) {
         const int m = r0 + (lane >> 4);
         const float4 *sp = reinterpret_cast<const float4 *>(act_row(m) + 8 * rl);
         const float4 a0 = sp[0], a1 = sp[1];
@@ -320,90 +369,124 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 }
 
 // =========================================================================
-// down: a workgroup owns a chunk and loops over output features in tiles of
-// 128 (32 per wave), so the chunk's A (64 rows x 512 fp16) is staged in LDS
-// once; the codes of the next two tiles are in flight during each tile.
+// down: a workgroup owns a chunk and loops over all 2048 output features in
+// tiles of 128 (32 per wave), so the chunk's A (96 rows x 512 fp16) is staged
+// in LDS once; the codes of the next three tiles are in flight during each
+// tile.  The MFMA runs transposed (codes as the row operand, tokens as the
+// column operand), so a lane ends with 4 consecutive features of one token
+// per group and writes o with 16-byte stores.  A carries a power-of-two
+// prescale per (token, 128-block), so each block's partial sum takes
+// scale(feature, block) * prescale(token, block).
 // =========================================================================
-constexpr int kDnPitch = 1040;    // bytes per LDS row (1024 + 16)
-constexpr int kDnSplit = 2;       // workgroups per chunk (each takes half of the 2048 features)
-constexpr int kDnTiles = kH / 128 / kDnSplit;
+constexpr int kDnPitch = 1040;   // bytes per LDS row (1024 + 16)
+constexpr int kDnTiles = kH / 128;
+constexpr int kDnCodeRing = 4;
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_down_mfma(
-    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, const uint32_t *__restrict__ at,
-    const float *__restrict__ at_scale, const int4 *__restrict__ chunks, const int *__restrict__ n_chunks,
-    float *__restrict__ o) {
+__global__ __launch_bounds__(256) void k_down_mfma(const uint8_t *__restrict__ codes,
+                                                   const uint16_t *__restrict__ scales,
+                                                   const uint32_t *__restrict__ at,
+                                                   const float *__restrict__ at_scale,
+                                                   const int4 *__restrict__ chunks,
+                                                   const int *__restrict__ n_chunks, float *__restrict__ o) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kChunkRows * kDnPitch];
-    __shared__ __attribute__((aligned(16))) float row_p[kI / kG][kChunkRows];   // [block][row]
-    int chunk, half;
-    chunk_tile(kDnSplit, chunk, half);
+    __shared__ __attribute__((aligned(16))) float row_p[kI / kG][kChunkRows];   // [block][token]
+    __shared__ __attribute__((aligned(16))) uint16_t sc[kI / kG][kH];           // [block][feature] bf16
+    int chunk, tile0;
+    chunk_tile(1, chunk, tile0);
     if (chunk >= *n_chunks) return;
     const int4 ch = chunks[chunk];
     const int e = uniform(ch.x), row0 = uniform(ch.y), rows = uniform(ch.z);
+    const int n_mt = uniform((rows + 31) >> 5);
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int n = lane & 31, g = lane >> 5;
 
     const __amdgpu_buffer_rsrc_t cres =
         make_buf(codes + (size_t)e * kCodeBytesPerExpert + kCodeBytesGu, (uint32_t)(kH * kI / 2));
-    const __amdgpu_buffer_rsrc_t sres =
-        make_buf(scales + (size_t)e * kScalesPerExpert + kScalesGu, (uint32_t)(kH * (kI / kG) * 2));
-    const int f0 = half * (kH / kDnSplit) + 32 * wave + n;   // this lane's feature in tile 0
-    uint4 cb[3][8];
-    uint2 sb[3];
+    const int f0 = 32 * wave + n;   // the feature whose codes this lane loads, in tile 0
+    uint4 cb[kDnCodeRing][8];
     auto fetch = [&](int slot, int tile) {
-        const uint32_t row = (uint32_t)(f0 + 128 * tile);
-        const uint32_t off = row * (kI / 2) + 32 * g;
+        const uint32_t off = (uint32_t)(f0 + 128 * tile) * (kI / 2) + 32 * g;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             cb[slot][2 * b] = bload16_nt(cres, off + 64 * b, 0);
             cb[slot][2 * b + 1] = bload16_nt(cres, off + 64 * b + 16, 0);
         }
-        const u32x2_t sv = __builtin_amdgcn_raw_buffer_load_b64(sres, row * 8, 0, 0);
-        sb[slot] = make_uint2(sv.x, sv.y);
     };
-    // stage the chunk's activations: thread -> (row, quarter of 1 KB)
-    {
-        const int srow = tid >> 2, part = tid & 3;
+
+    // stage the chunk's activations: thread -> (row, part); load i takes the
+    // row's 16-byte group 4i + part
+    for (int srow = tid >> 2; srow < kChunkRows; srow += 64) {
+        const int part = tid & 3;
         const int p = row0 + min(srow, rows - 1);
         const uint4 *src = reinterpret_cast<const uint4 *>(at + (size_t)p * (kI / 2)) + part;
         uint4 v[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = src[4 * i];
-        fetch(0, 0);   // after the activations: their wait below does not wait for the codes
-        fetch(1, 1);
 #pragma unroll
         for (int i = 0; i < 16; ++i) *reinterpret_cast<uint4 *>(lds + srow * kDnPitch + part * 16 + 64 * i) = v[i];
-        if (tid < kChunkRows) {
-            const float4 q = *reinterpret_cast<const float4 *>(at_scale + (size_t)(row0 + min(tid, rows - 1)) * (kI / kG));
-            row_p[0][tid] = q.x;
-            row_p[1][tid] = q.y;
-            row_p[2][tid] = q.z;
-            row_p[3][tid] = q.w;
+    }
+    if (tid < kChunkRows) {
+        const float4 q = *reinterpret_cast<const float4 *>(at_scale + (size_t)(row0 + min(tid, rows - 1)) * (kI / kG));
+        row_p[0][tid] = q.x;
+        row_p[1][tid] = q.y;
+        row_p[2][tid] = q.z;
+        row_p[3][tid] = q.w;
+    }
+    // the expert's down scales, transposed to [block][feature]: thread t takes features 8t..8t+7
+    {
+        const uint4 *src = reinterpret_cast<const uint4 *>(scales + (size_t)e * kScalesPerExpert + kScalesGu) + 4 * tid;
+        const uint4 s0 = src[0], s1 = src[1], s2 = src[2], s3 = src[3];
+        const uint32_t w[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
+                                s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
+        // feature f = 8t + k holds blocks 0,1 in w[2k] and 2,3 in w[2k+1]
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            uint32_t v[4];
+#pragma unroll
+            for (int k2 = 0; k2 < 4; ++k2) {
+                const uint32_t lo = w[2 * (2 * k2) + (bb >> 1)], hi = w[2 * (2 * k2 + 1) + (bb >> 1)];
+                const uint32_t a0 = (bb & 1) ? (lo >> 16) : (lo & 0xffffu);
+                const uint32_t a1 = (bb & 1) ? (hi >> 16) : (hi & 0xffffu);
+                v[k2] = a0 | (a1 << 16);
+            }
+            *reinterpret_cast<uint4 *>(&sc[bb][8 * tid]) = make_uint4(v[0], v[1], v[2], v[3]);
         }
     }
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(0, 0);
+    fetch(1, 1);
+    fetch(2, 2);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     // o rows of the chunk through a buffer descriptor: stores of rows past the
     // chunk's end fall outside it and are dropped by the hardware bounds check
     const __amdgpu_buffer_rsrc_t ores = make_buf(o + (size_t)row0 * kH, (uint32_t)rows * kH * 4);
 
-#pragma unroll
+    // unrolled by the ring size, so ring slots are compile-time; the fetch
+    // index is clamped (the last tiles re-read tile 15, in bounds) so that
+    // every iteration issues the same loads and the waits stay exact
+    with_tiles(n_mt, [&](auto tiles) {
+    constexpr int MT = decltype(tiles)::value;
+#pragma unroll kDnCodeRing
     for (int t = 0; t < kDnTiles; ++t) {
-        const int cs = t % 3;
+        const int cs = t % kDnCodeRing;
         __builtin_amdgcn_sched_barrier(0);
-        if (t + 2 < kDnTiles) fetch((t + 2) % 3, t + 2);
+        fetch((t + 3) % kDnCodeRing, min(t + 3, kDnTiles - 1));
         __builtin_amdgcn_sched_barrier(0);
         const uint32_t zero = opaque(0);
         const uint8_t *abase = lds + zero;
-        const float *pbase = &row_p[0][0] + zero + 4 * g;
-        f32x16_t acc[2];
+        // scales of features 128t + 32w + 8q + 4g + 0..3 (q = 0..3) of each block
+        const uint16_t *sbase = &sc[0][0] + zero + 128 * t + 32 * wave + 4 * g;
+        f32x16_t acc[MT];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < MT; ++h)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[h][i] = 0.0f;
 #pragma unroll
         for (int b = 0; b < kI / kG; ++b) {
-            f32x16_t d[2];
+            f32x16_t d[MT];
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int h = 0; h < MT; ++h)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) d[h][i] = 0.0f;
 #pragma unroll
@@ -413,38 +496,43 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                     const uint4 bw = codes_to_f16(word(cb[cs][2 * b + q], j));
                     const int grp = 16 * b + 8 * g + 4 * q + j;
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
+                    for (int h = 0; h < MT; ++h) {
                         const uint4 a = *reinterpret_cast<const uint4 *>(abase + (32 * h + n) * kDnPitch + grp * 16);
-                        d[h] = mfma32(a, bw, d[h]);
+                        d[h] = mfma32(bw, a, d[h]);
                     }
                     // one k-slice at a time: keeps the converted codes and A
                     // operands of a whole block from being live at once
                     __builtin_amdgcn_sched_barrier(0);
                 }
             mfma_drain();
-            const uint32_t sw = (b < 2) ? sb[cs].x : sb[cs].y;
-            const float s = (b & 1) ? bf16hi(sw) : bf16lo(sw);
+            float s[16];
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
+            for (int q = 0; q < 4; ++q) {
+                const uint2 sw = *reinterpret_cast<const uint2 *>(sbase + b * kH + 8 * q);
+                s[4 * q + 0] = bf16lo(sw.x);
+                s[4 * q + 1] = bf16hi(sw.x);
+                s[4 * q + 2] = bf16lo(sw.y);
+                s[4 * q + 3] = bf16hi(sw.y);
+            }
 #pragma unroll
-                for (int i4 = 0; i4 < 4; ++i4) {
-                    // rows 32h + 8*i4 + 4g + 0..3 of block b's prescales
-                    const float4 p4 = *reinterpret_cast<const float4 *>(pbase + b * kChunkRows + 32 * h + 8 * i4);
-                    acc[h][4 * i4 + 0] = fmaf(s * p4.x, d[h][4 * i4 + 0], acc[h][4 * i4 + 0]);
-                    acc[h][4 * i4 + 1] = fmaf(s * p4.y, d[h][4 * i4 + 1], acc[h][4 * i4 + 1]);
-                    acc[h][4 * i4 + 2] = fmaf(s * p4.z, d[h][4 * i4 + 2], acc[h][4 * i4 + 2]);
-                    acc[h][4 * i4 + 3] = fmaf(s * p4.w, d[h][4 * i4 + 3], acc[h][4 * i4 + 3]);
-                }
+            for (int h = 0; h < MT; ++h) {
+                const float p = row_p[b][32 * h + n + zero];
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[h][i] = fmaf(s[i] * p, d[h][i], acc[h][i]);
+            }
         }
-        const uint32_t ob = (uint32_t)(f0 + 128 * t + 4 * g * kH) * 4;
+        // lane: token 32h + n, features 128t + 32w + 8q + 4g + 0..3 in acc[h][4q..4q+3]
+        const uint32_t ob = (uint32_t)(n * kH + 128 * t + 32 * wave + 4 * g) * 4;
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int h = 0; h < MT; ++h)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const uint32_t r = 32 * h + 8 * (i >> 2) + (i & 3);
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[h][i]), ores, ob + r * kH * 4, 0, 0);
+            for (int q = 0; q < 4; ++q) {
+                const u32x4_t v = {__float_as_uint(acc[h][4 * q]), __float_as_uint(acc[h][4 * q + 1]),
+                                   __float_as_uint(acc[h][4 * q + 2]), __float_as_uint(acc[h][4 * q + 3])};
+                __builtin_amdgcn_raw_buffer_store_b128(v, ores, ob + (uint32_t)(32 * h * kH + 8 * q) * 4, 0, 0);
             }
     }
+    });
 }
 
 int max_chunks(int T) { return min(kE, kTopK * T) + (kTopK * T + kChunkRows - 1) / kChunkRows; }
@@ -463,7 +551,7 @@ void launch_gateup_mfma(const uint8_t *codes, const uint16_t *scales, const uint
 
 void launch_down_mfma(const uint8_t *codes, const uint16_t *scales, const uint32_t *at, const float *at_scale,
                       const int *chunks, const int *n_chunks, int T, float *o, hipStream_t s) {
-    hipLaunchKernelGGL(k_down_mfma, dim3(grid_for(T, kDnSplit)), dim3(256), 0, s, codes, scales, at, at_scale,
+    hipLaunchKernelGGL(k_down_mfma, dim3(grid_for(T, 1)), dim3(256), 0, s, codes, scales, at, at_scale,
                        reinterpret_cast<const int4 *>(chunks), n_chunks, o);
 }
 

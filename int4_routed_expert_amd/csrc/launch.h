@@ -19,7 +19,7 @@ void launch_topk_rotate(const float *logits, const uint16_t *x, int T, int *topk
 // slots: int[256][8] records {expert, first sorted position, count, first
 // token, second token, 0, 0, 0}, one per expert with tokens, then expert -1.
 // chunks: int[max_chunks(T)][4] records {expert, first sorted position, rows
-// (<= 64), 0} covering every expert's assignments; *n_chunks of them.
+// (<= 96), 0} covering every expert's assignments; *n_chunks of them.
 void launch_sort(const int *topk_idx, int T, int *offsets, int *perm, int *pos, int *n_active,
                  int *slots, int *chunks, int *n_chunks, hipStream_t s);
 
@@ -32,7 +32,7 @@ void launch_rotate_act(const float *act, int T, uint32_t *at, float *at_scale, h
 void launch_down_gemv(const uint8_t *codes, const uint16_t *scales, const uint32_t *at, const float *at_scale,
                       const int *slots, int T, float *o, hipStream_t s);
 
-// Routed experts, MFMA form (prefill): chunks of <= 64 assignments of one
+// Routed experts, MFMA form (prefill): chunks of <= 96 assignments of one
 // expert against tiles of weight rows.  gate/up writes the rotated fp16
 // operands of the down projection directly (at, at_scale).
 int max_chunks(int T);

@@ -171,7 +171,7 @@ void launch_topk_rotate(const float *logits, const uint16_t *x, int T, int *topk
 // The result depends only on topk_idx: offsets, perm and pos are exact.
 // ---------------------------------------------------------------------------
 constexpr int kSortWaves = 16;
-constexpr int kSortChunkRows = 64;   // rows of one chunk of the MFMA grouped kernels
+constexpr int kSortChunkRows = 96;   // rows of one chunk of the MFMA grouped kernels
 
 __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx, int T,
                                                int *__restrict__ offsets, int *__restrict__ perm,

@@ -80,10 +80,13 @@ def test_layer_small_T(m, layer0, T):
 
 
 # ------------------------------------------------- MFMA grouped path (T >= 128)
+CHUNK_ROWS = 96   # rows of one chunk of the grouped kernels (include/moe_w4.h)
+
+
 def expected_chunks(offsets):
     counts = np.diff(offsets)
-    return np.array([(e, offsets[e] + r, min(64, counts[e] - r), 0)
-                     for e in np.nonzero(counts)[0] for r in range(0, counts[e], 64)]).reshape(-1, 4)
+    return np.array([(e, offsets[e] + r, min(CHUNK_ROWS, counts[e] - r), 0)
+                     for e in np.nonzero(counts)[0] for r in range(0, counts[e], CHUNK_ROWS)]).reshape(-1, 4)
 
 
 def read_chunks(m, ws, T):
@@ -92,7 +95,7 @@ def read_chunks(m, ws, T):
 
 
 def test_grouped_path_all_tokens(m, layer0):
-    """T = 128: every token against the oracle (chunks of 1..6 rows per expert)."""
+    """T = 128: every token against the oracle (chunks of a few rows per expert)."""
     T = 128
     x = synth.gen_x(400, T)
     ws = m.workspace(T)
@@ -111,7 +114,7 @@ def test_grouped_path_sampled(m, layer0, T):
 
 
 def test_grouped_chunks_of_a_hot_expert(m, layer0):
-    """One expert takes all 200 tokens: chunks of 64, 64, 64 and a ragged 8."""
+    """One expert takes all 200 tokens: chunks of 96, 96 and a ragged 8."""
     T = 200
     x = synth.gen_x(402, T)
     bias = np.zeros(256, dtype=np.float32)
@@ -121,8 +124,8 @@ def test_grouped_chunks_of_a_hot_expert(m, layer0):
     assert np.all(g["topk_idx"][:, 0] == 17)
     ch = read_chunks(m, ws, T)
     np.testing.assert_array_equal(ch, expected_chunks(g["offsets"]))
-    assert (ch[:, 0] == 17).sum() == 4 and ch[ch[:, 0] == 17][-1, 2] == 8
-    tokens = np.array([0, 1, 63, 64, 127, 128, 191, 192, 199])
+    assert (ch[:, 0] == 17).sum() == 3 and ch[ch[:, 0] == 17][-1, 2] == 8
+    tokens = np.array([0, 1, 31, 32, 63, 64, 95, 96, 191, 192, 199])
     report("grouped hot expert", P.compare(g, oracle_layer(x, bias=bias, tokens=tokens), tokens=tokens,
                                            label="grouped hot expert"))
 
