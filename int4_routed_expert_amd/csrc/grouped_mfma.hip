@@ -155,6 +155,11 @@ __device__ __forceinline__ int scale_shift(const uint4 &a, const uint4 &b) {
     }
     return e ? 134 - (int)e : 0;
 }
+// The same over the 4 bf16 scales of one down row (two words).
+__device__ __forceinline__ int scale_shift4(uint32_t a, uint32_t b) {
+    const uint32_t e = max(max((a >> 7) & 0xffu, (a >> 23) & 0xffu), max((b >> 7) & 0xffu, (b >> 23) & 0xffu));
+    return e ? 134 - (int)e : 0;
+}
 // bf16 scale s (low or high half of a word) -> fp16 s * 2^k in both halves
 __device__ __forceinline__ half2_t scaled_half2(uint32_t word2, int hi, int k) {
     const float f = ldexpf(hi ? bf16hi(word2) : bf16lo(word2), k);
@@ -374,9 +379,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // in LDS once; the codes of the next three tiles are in flight during each
 // tile.  The MFMA runs transposed (codes as the row operand, tokens as the
 // column operand), so a lane ends with 4 consecutive features of one token
-// per group and writes o with 16-byte stores.  A carries a power-of-two
-// prescale per (token, 128-block), so each block's partial sum takes
-// scale(feature, block) * prescale(token, block).
+// per group and writes o with 16-byte stores.
+//
+// Scales: A arrives with a power-of-two prescale per (token, 128-block); at
+// staging each block is brought to the token's largest prescale (an exact
+// power-of-two multiply in fp16), and each feature's 4 bf16 scales are
+// normalised by one power of two and folded exactly into its fp16 codes
+// (codes_to_f16_scaled), so the MFMA accumulates over all of K and the two
+// normalisations are undone once per output.
 // =========================================================================
 constexpr int kDnPitch = 1040;   // bytes per LDS row (1024 + 16)
 constexpr int kDnTiles = kH / 128;
@@ -389,8 +399,9 @@ __global__ __launch_bounds__(256) void k_down_mfma(const uint8_t *__restrict__ c
                                                    const int4 *__restrict__ chunks,
                                                    const int *__restrict__ n_chunks, float *__restrict__ o) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kChunkRows * kDnPitch];
-    __shared__ __attribute__((aligned(16))) float row_p[kI / kG][kChunkRows];   // [block][token]
-    __shared__ __attribute__((aligned(16))) uint16_t sc[kI / kG][kH];           // [block][feature] bf16
+    __shared__ float row_p[kChunkRows];                                       // per token
+    __shared__ __attribute__((aligned(16))) uint16_t sc[kI / kG][kH];         // [block][feature] bf16
+    __shared__ __attribute__((aligned(16))) float fk[kH];                     // 2^-k per feature
     int chunk, tile0;
     chunk_tile(1, chunk, tile0);
     if (chunk >= *n_chunks) return;
@@ -412,27 +423,15 @@ __global__ __launch_bounds__(256) void k_down_mfma(const uint8_t *__restrict__ c
             cb[slot][2 * b + 1] = bload16_nt(cres, off + 64 * b + 16, 0);
         }
     };
+    // the codes do not depend on the chunk's tokens: in flight first
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(0, 0);
+    fetch(1, 1);
+    fetch(2, 2);
+    __builtin_amdgcn_sched_barrier(0);
 
-    // stage the chunk's activations: thread -> (row, part); load i takes the
-    // row's 16-byte group 4i + part
-    for (int srow = tid >> 2; srow < kChunkRows; srow += 64) {
-        const int part = tid & 3;
-        const int p = row0 + min(srow, rows - 1);
-        const uint4 *src = reinterpret_cast<const uint4 *>(at + (size_t)p * (kI / 2)) + part;
-        uint4 v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = src[4 * i];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) *reinterpret_cast<uint4 *>(lds + srow * kDnPitch + part * 16 + 64 * i) = v[i];
-    }
-    if (tid < kChunkRows) {
-        const float4 q = *reinterpret_cast<const float4 *>(at_scale + (size_t)(row0 + min(tid, rows - 1)) * (kI / kG));
-        row_p[0][tid] = q.x;
-        row_p[1][tid] = q.y;
-        row_p[2][tid] = q.z;
-        row_p[3][tid] = q.w;
-    }
-    // the expert's down scales, transposed to [block][feature]: thread t takes features 8t..8t+7
+    // the expert's down scales, transposed to [block][feature], and each
+    // feature's normalisation: thread t takes features 8t..8t+7
     {
         const uint4 *src = reinterpret_cast<const uint4 *>(scales + (size_t)e * kScalesPerExpert + kScalesGu) + 4 * tid;
         const uint4 s0 = src[0], s1 = src[1], s2 = src[2], s3 = src[3];
@@ -451,12 +450,38 @@ __global__ __launch_bounds__(256) void k_down_mfma(const uint8_t *__restrict__ c
             }
             *reinterpret_cast<uint4 *>(&sc[bb][8 * tid]) = make_uint4(v[0], v[1], v[2], v[3]);
         }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) fk[8 * tid + k] = ldexpf(1.0f, -scale_shift4(w[2 * k], w[2 * k + 1]));
     }
-    __builtin_amdgcn_sched_barrier(0);
-    fetch(0, 0);
-    fetch(1, 1);
-    fetch(2, 2);
-    __builtin_amdgcn_sched_barrier(0);
+    // stage the chunk's activations: thread -> (row, part); load i takes the
+    // row's 16-byte group 4i + part (block i / 4), brought to the row's
+    // largest block prescale
+    for (int srow = tid >> 2; srow < kChunkRows; srow += 64) {
+        const int part = tid & 3;
+        const int p = row0 + min(srow, rows - 1);
+        const uint4 *src = reinterpret_cast<const uint4 *>(at + (size_t)p * (kI / 2)) + part;
+        uint4 v[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = src[4 * i];
+        const float4 ps = *reinterpret_cast<const float4 *>(at_scale + (size_t)p * (kI / kG));
+        const float pm = fmaxf(fmaxf(ps.x, ps.y), fmaxf(ps.z, ps.w));
+        const float pb[4] = {ps.x / pm, ps.y / pm, ps.z / pm, ps.w / pm};   // exact powers of two <= 1
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            const _Float16 r = (_Float16)pb[bb];
+            const half2_t r2 = {r, r};
+#pragma unroll
+            for (int i = 4 * bb; i < 4 * bb + 4; ++i) {
+                v[i].x = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, v[i].x) * r2);
+                v[i].y = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, v[i].y) * r2);
+                v[i].z = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, v[i].z) * r2);
+                v[i].w = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, v[i].w) * r2);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) *reinterpret_cast<uint4 *>(lds + srow * kDnPitch + part * 16 + 64 * i) = v[i];
+        if (part == 0) row_p[srow] = pm;
+    }
     __syncthreads();
     // o rows of the chunk through a buffer descriptor: stores of rows past the
     // chunk's end fall outside it and are dropped by the hardware bounds check
@@ -475,62 +500,70 @@ __global__ __launch_bounds__(256) void k_down_mfma(const uint8_t *__restrict__ c
         __builtin_amdgcn_sched_barrier(0);
         const uint32_t zero = opaque(0);
         const uint8_t *abase = lds + zero;
-        // scales of features 128t + 32w + 8q + 4g + 0..3 (q = 0..3) of each block
-        const uint16_t *sbase = &sc[0][0] + zero + 128 * t + 32 * wave + 4 * g;
+        // this lane's codes feature and its normalised scales, as fp16 pairs
+        const int fl = f0 + 128 * t;
+        const int kf = -ilogbf(fk[fl + zero]);
+        half2_t s2[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const _Float16 h = (_Float16)ldexpf(bf16_to_f32(sc[b][fl + zero]), kf);
+            s2[b] = half2_t{h, h};
+        }
         f32x16_t acc[MT];
 #pragma unroll
         for (int h = 0; h < MT; ++h)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[h][i] = 0.0f;
-#pragma unroll
-        for (int b = 0; b < kI / kG; ++b) {
-            f32x16_t d[MT];
+        // 32 k-slices of 16; the A operands and converted codes of slice
+        // ks + 1 are read and built while the MFMAs of slice ks run (one wave
+        // per SIMD here, so nothing else hides the LDS latency)
+        auto slice_a = [&](int ks, uint4 (&dst)[MT]) {
+            const int b = ks >> 3, q = (ks >> 2) & 1, j = ks & 3;
+            const int grp = 16 * b + 8 * g + 4 * q + j;
 #pragma unroll
             for (int h = 0; h < MT; ++h)
+                dst[h] = *reinterpret_cast<const uint4 *>(abase + (32 * h + n) * kDnPitch + grp * 16);
+        };
+        auto slice_b = [&](int ks) -> uint4 {
+            const int b = ks >> 3, q = (ks >> 2) & 1, j = ks & 3;
+            return codes_to_f16_scaled(word(cb[cs][2 * b + q], j), s2[b]);
+        };
+        uint4 a_cur[MT], a_nxt[MT];
+        slice_a(0, a_cur);
+        uint4 b_cur = slice_b(0);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) d[h][i] = 0.0f;
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint4 bw = codes_to_f16(word(cb[cs][2 * b + q], j));
-                    const int grp = 16 * b + 8 * g + 4 * q + j;
-#pragma unroll
-                    for (int h = 0; h < MT; ++h) {
-                        const uint4 a = *reinterpret_cast<const uint4 *>(abase + (32 * h + n) * kDnPitch + grp * 16);
-                        d[h] = mfma32(bw, a, d[h]);
-                    }
-                    // one k-slice at a time: keeps the converted codes and A
-                    // operands of a whole block from being live at once
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            mfma_drain();
-            float s[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint2 sw = *reinterpret_cast<const uint2 *>(sbase + b * kH + 8 * q);
-                s[4 * q + 0] = bf16lo(sw.x);
-                s[4 * q + 1] = bf16hi(sw.x);
-                s[4 * q + 2] = bf16lo(sw.y);
-                s[4 * q + 3] = bf16hi(sw.y);
+        for (int ks = 0; ks < 32; ++ks) {
+            uint4 b_nxt = b_cur;
+            if (ks + 1 < 32) {
+                slice_a(ks + 1, a_nxt);
+                b_nxt = slice_b(ks + 1);
             }
 #pragma unroll
-            for (int h = 0; h < MT; ++h) {
-                const float p = row_p[b][32 * h + n + zero];
+            for (int h = 0; h < MT; ++h) acc[h] = mfma32(b_cur, a_cur[h], acc[h]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 0; i < 16; ++i) acc[h][i] = fmaf(s[i] * p, d[h][i], acc[h][i]);
-            }
+            for (int h = 0; h < MT; ++h) a_cur[h] = a_nxt[h];
+            b_cur = b_nxt;
         }
+        mfma_drain();
         // lane: token 32h + n, features 128t + 32w + 8q + 4g + 0..3 in acc[h][4q..4q+3]
-        const uint32_t ob = (uint32_t)(n * kH + 128 * t + 32 * wave + 4 * g) * 4;
+        const int fb = 128 * t + 32 * wave + 4 * g;
+        float4 kq[4];
 #pragma unroll
-        for (int h = 0; h < MT; ++h)
+        for (int q = 0; q < 4; ++q) kq[q] = *reinterpret_cast<const float4 *>(&fk[fb + 8 * q + zero]);
+        const uint32_t ob = (uint32_t)(n * kH + fb) * 4;
+#pragma unroll
+        for (int h = 0; h < MT; ++h) {
+            const float p = row_p[32 * h + n + zero];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const u32x4_t v = {__float_as_uint(acc[h][4 * q]), __float_as_uint(acc[h][4 * q + 1]),
-                                   __float_as_uint(acc[h][4 * q + 2]), __float_as_uint(acc[h][4 * q + 3])};
+                const u32x4_t v = {__float_as_uint(acc[h][4 * q] * (kq[q].x * p)),
+                                   __float_as_uint(acc[h][4 * q + 1] * (kq[q].y * p)),
+                                   __float_as_uint(acc[h][4 * q + 2] * (kq[q].z * p)),
+                                   __float_as_uint(acc[h][4 * q + 3] * (kq[q].w * p))};
                 __builtin_amdgcn_raw_buffer_store_b128(v, ores, ob + (uint32_t)(32 * h * kH + 8 * q) * 4, 0, 0);
             }
+        }
     }
     });
 }
