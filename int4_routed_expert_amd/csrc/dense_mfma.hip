@@ -7,10 +7,10 @@
 // v_mfma_f32_32x32x16_bf16 sums them in fp32.
 //
 // Tiling: a workgroup computes a 128 x 128 output tile with 4 waves (2 x 2,
-// 64 x 64 each: 2 x 2 MFMA tiles).  K advances 32 at a time: operands are
+// 64 x 64 each: 2 x 2 MFMA tiles).  K advances 64 at a time: operands are
 // loaded into registers two steps ahead and written to a double-buffered LDS
-// tile one step ahead; rows of 32 bf16 (64 bytes) are stored with the
-// 16-byte group position swizzled by bits 2..3 of the row, so the MFMA reads
+// tile one step ahead; rows of 64 bf16 (128 bytes) are stored with the
+// 16-byte group position swizzled by bits 1..3 of the row, so the MFMA reads
 // of 16 consecutive rows hit 16 distinct 4-bank slots.
 //
 // Epilogues: fp32 store (+ per-column bias) for the logits; SwiGLU for the
@@ -30,8 +30,11 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kTile = 128;
-constexpr int kStepK = 32;                       // bf16 per row per ring slot (64 bytes)
-constexpr int kSlotBytes = kTile * kStepK * 2;   // 8 KB per operand per slot
+constexpr int kStepK = 64;                       // bf16 per row per LDS slot (128 bytes, 8 groups)
+constexpr int kRowBytes = kStepK * 2;
+constexpr int kChunksPerRow = kRowBytes / 16;
+constexpr int kSlotBytes = kTile * kRowBytes;    // 16 KB per operand per slot
+constexpr int kStageLoads = kTile * kChunksPerRow / 256;   // 16-byte loads per thread per operand per step
 constexpr int kXcds = 8;
 
 enum { kEpiStore = 0, kEpiSwiglu = 1, kEpiCombine = 2 };
@@ -85,9 +88,22 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
         nt = blockIdx.x % n_total;
     }
     if (mt >= m_tiles) return;
-    const bool second = nt >= jobs.job[0].n_tiles;
-    const DenseJob &J = second ? jobs.job[1] : jobs.job[0];
-    if (second) nt -= jobs.job[0].n_tiles;
+    // both jobs' fields are read in parallel and then selected (indexing the
+    // kernel argument by the job number would chain dependent scalar loads)
+    const DenseJob j0 = jobs.job[0], j1 = jobs.job[1];
+    const bool second = nt >= j0.n_tiles;
+    DenseJob J;
+    J.B = second ? j1.B : j0.B;
+    J.n_tiles = second ? j1.n_tiles : j0.n_tiles;
+    J.epi = second ? j1.epi : j0.epi;
+    J.up_row = second ? j1.up_row : j0.up_row;
+    J.bias = second ? j1.bias : j0.bias;
+    J.out = second ? j1.out : j0.out;
+    J.ldo = second ? j1.ldo : j0.ldo;
+    J.topk_w = second ? j1.topk_w : j0.topk_w;
+    J.pos = second ? j1.pos : j0.pos;
+    J.o = second ? j1.o : j0.o;
+    if (second) nt -= j0.n_tiles;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int n = lane & 31, g = lane >> 5;
@@ -104,33 +120,34 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
         return (cc < 32) ? r : J.up_row + r;
     };
 
-    // staging: per step each thread moves 16-byte chunks c = tid, tid + 256
-    // of A and of B (row c / 4, position c % 4 holding group (c % 4) ^ ((row >> 2) & 3));
+    // staging: per step each thread moves 16-byte chunks c = tid + 256 i of A
+    // and of B (row c / 8, position c % 8 holding group (c % 8) ^ ((row >> 1) & 7));
     // raw buffer loads keep their program order, two steps ahead
     const __amdgpu_buffer_rsrc_t ares = make_buf(A, 0xffffffffu);
     const __amdgpu_buffer_rsrc_t bres = make_buf(J.B, 0xffffffffu);
-    uint32_t aoff[2], boff[2];
-    int ldst[2];
+    uint32_t aoff[kStageLoads], boff[kStageLoads];
+    int ldst[kStageLoads];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int c = tid + 256 * i, r = c >> 2, pos = c & 3, grp = pos ^ ((r >> 2) & 3);
+    for (int i = 0; i < kStageLoads; ++i) {
+        const int c = tid + 256 * i, r = c / kChunksPerRow, pos = c % kChunksPerRow;
+        const int grp = pos ^ ((r >> 1) & 7);
         aoff[i] = (uint32_t)min(m0 + r, M - 1) * (K * 2) + grp * 16;
         boff[i] = (uint32_t)b_row(r) * (K * 2) + grp * 16;
-        ldst[i] = r * 64 + pos * 16;
+        ldst[i] = r * kRowBytes + pos * 16;
     }
-    uint4 stg[2][4];
+    uint4 stg[2][2 * kStageLoads];
     auto load = [&](int set, int step) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            stg[set][i] = bload16(ares, aoff[i] + step * 64, 0);
-            stg[set][2 + i] = bload16(bres, boff[i] + step * 64, 0);
+        for (int i = 0; i < kStageLoads; ++i) {
+            stg[set][i] = bload16(ares, aoff[i] + step * kRowBytes, 0);
+            stg[set][kStageLoads + i] = bload16(bres, boff[i] + step * kRowBytes, 0);
         }
     };
     auto store = [&](int set, int slot) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = 0; i < kStageLoads; ++i) {
             *reinterpret_cast<uint4 *>(sa[slot] + ldst[i]) = stg[set][i];
-            *reinterpret_cast<uint4 *>(sb[slot] + ldst[i]) = stg[set][2 + i];
+            *reinterpret_cast<uint4 *>(sb[slot] + ldst[i]) = stg[set][kStageLoads + i];
         }
     };
 
@@ -154,18 +171,18 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
         if (s + 2 < kSteps) load(slot, s + 2);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int grp = 2 * g + j;
+        for (int j = 0; j < kChunksPerRow / 2; ++j) {
+            const int grp = (kChunksPerRow / 2) * g + j;
             uint4 a[2], b[2];
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
                 const int r = 64 * wm + 32 * x + n;
-                a[x] = *reinterpret_cast<const uint4 *>(sa[slot] + r * 64 + ((grp ^ ((r >> 2) & 3)) * 16));
+                a[x] = *reinterpret_cast<const uint4 *>(sa[slot] + r * kRowBytes + ((grp ^ ((r >> 1) & 7)) * 16));
             }
 #pragma unroll
             for (int y = 0; y < 2; ++y) {
                 const int r = 64 * wn + 32 * y + n;
-                b[y] = *reinterpret_cast<const uint4 *>(sb[slot] + r * 64 + ((grp ^ ((r >> 2) & 3)) * 16));
+                b[y] = *reinterpret_cast<const uint4 *>(sb[slot] + r * kRowBytes + ((grp ^ ((r >> 1) & 7)) * 16));
             }
 #pragma unroll
             for (int x = 0; x < 2; ++x)

@@ -171,6 +171,7 @@ void launch_topk_rotate(const float *logits, const uint16_t *x, int T, int *topk
 // The result depends only on topk_idx: offsets, perm and pos are exact.
 // ---------------------------------------------------------------------------
 constexpr int kSortWaves = 16;
+constexpr int kSortBatch = 8;        // chunks of 64 assignments whose loads are issued together
 constexpr int kSortChunkRows = 96;   // rows of one chunk of the MFMA grouped kernels
 
 __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx, int T,
@@ -191,7 +192,19 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
 
     for (int i = tid; i < kSortWaves * kE; i += blockDim.x) (&cnt[0][0])[i] = 0;
     __syncthreads();
-    for (int a = a0 + lane; a < a1; a += 64) atomicAdd(&cnt[wave][topk_idx[a]], 1);
+    // the wave's assignments are read kSortBatch chunks of 64 at a time, all
+    // loads of a batch in flight together
+    for (int c0 = a0; c0 < a1; c0 += 64 * kSortBatch) {
+        int ev[kSortBatch];
+#pragma unroll
+        for (int u = 0; u < kSortBatch; ++u) {
+            const int a = c0 + 64 * u + lane;
+            ev[u] = a < a1 ? topk_idx[a] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < kSortBatch; ++u)
+            if (ev[u] >= 0) atomicAdd(&cnt[wave][ev[u]], 1);
+    }
     __syncthreads();
     if (tid < kE) {
         int run = 0;
@@ -254,10 +267,20 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
     }
     __syncthreads();
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int c0 = a0; c0 < a1; c0 += 64) {
+    for (int cb = a0; cb < a1; cb += 64 * kSortBatch) {
+    int ev[kSortBatch];
+#pragma unroll
+    for (int u = 0; u < kSortBatch; ++u) {
+        const int a = cb + 64 * u + lane;
+        ev[u] = a < a1 ? topk_idx[a] : 0;
+    }
+#pragma unroll
+    for (int u = 0; u < kSortBatch; ++u) {
+        const int c0 = cb + 64 * u;
+        if (c0 >= a1) break;
         const int a = c0 + lane;
         const bool valid = a < a1;
-        const int e = valid ? topk_idx[a] : 0;
+        const int e = ev[u];
         uint64_t same = __ballot(valid);
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
@@ -272,6 +295,7 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
             if (dest - offs[e] < 2) first2[e][dest - offs[e]] = a / kTopK;
             if ((same >> lane) == 1ull) cnt[wave][e] = base + __popcll(same);
         }
+    }
     }
     __syncthreads();
     // One 32-byte record per active slot, so a grouped kernel gets its expert,

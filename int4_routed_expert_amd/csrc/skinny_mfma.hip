@@ -70,9 +70,24 @@ template <int MT, int KS, int KB, int CW>
 __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__ A, int M, SkinnyJobs jobs) {
     constexpr int K = 128 * KS * KB;
     __shared__ f32x4_t red[KS][MT][64];
-    const bool second = (int)blockIdx.x >= jobs.job[0].n_blocks;
-    const SkinnyJob &J = second ? jobs.job[1] : jobs.job[0];
-    const int blk = second ? (int)blockIdx.x - jobs.job[0].n_blocks : (int)blockIdx.x;
+    // both jobs' fields are read (in parallel, at fixed kernel-argument
+    // offsets) and then selected: indexing the argument by the job number
+    // would make every field a dependent scalar load
+    const SkinnyJob j0 = jobs.job[0], j1 = jobs.job[1];
+    const bool second = (int)blockIdx.x >= j0.n_blocks;
+    SkinnyJob J;
+    J.B = second ? j1.B : j0.B;
+    J.b_rows = second ? j1.b_rows : j0.b_rows;
+    J.b_split = second ? j1.b_split : j0.b_split;
+    J.n_blocks = second ? j1.n_blocks : j0.n_blocks;
+    J.epi = second ? j1.epi : j0.epi;
+    J.bias = second ? j1.bias : j0.bias;
+    J.out = second ? j1.out : j0.out;
+    J.ldo = second ? j1.ldo : j0.ldo;
+    J.topk_w = second ? j1.topk_w : j0.topk_w;
+    J.pos = second ? j1.pos : j0.pos;
+    J.o = second ? j1.o : j0.o;
+    const int blk = second ? (int)blockIdx.x - j0.n_blocks : (int)blockIdx.x;
     const int epi = J.epi;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int r = lane & 15, g = lane >> 4;
