@@ -96,7 +96,7 @@ extern "C" {
  *                         holds n.  (Written at every T; read only on that path.) */
 typedef struct moe_w4_ws_layout {
     size_t logits, topk_idx, topk_w, offsets, perm, pos, n_active, active;
-    size_t xt, xt_scale, act, at, at_scale, hs, o, chunks, n_chunks, sync;
+    size_t xt, xt_scale, act, at, at_scale, hs, o, z, chunks, n_chunks, sync;
     size_t total;
 } moe_w4_ws_layout;
 

@@ -42,6 +42,7 @@ moe_w4_ws_layout make_layout(int64_t T) {
     L.at_scale = take(4 * (kI / kG) * a);
     L.hs = take(2 * kIS * t);
     L.o = take(4 * kH * a);
+    L.z = take(4 * kH * t);
     L.chunks = take(16 * (size_t)max_chunks((int)T));
     L.n_chunks = take(4);
     L.sync = take(4096);
@@ -117,6 +118,7 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     float *at_scale = ws_at<float>(ws, L.at_scale);
     uint16_t *hs = ws_at<uint16_t>(ws, L.hs);
     float *o = ws_at<float>(ws, L.o);
+    float *z = ws_at<float>(ws, L.z);
     int *chunks = ws_at<int>(ws, L.chunks);
     int *n_chunks = ws_at<int>(ws, L.n_chunks);
     const bool grouped = T >= kPrefillMinTokens;
@@ -167,9 +169,10 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
         MOE_STEP(launch_down_gemv(codes, scales, at, at_scale, active, T, o, s));
         MOE_MARK();
     }
-    if (grouped)
-        MOE_STEP(launch_shared_down_combine_dense(shared_w, hs, T, topk_w, pos, o, y, s));
-    else
+    if (grouped) {
+        MOE_STEP(launch_shared_down_dense(shared_w, hs, T, z, s));
+        MOE_STEP(launch_combine(z, topk_w, pos, o, T, y, s));
+    } else
         MOE_STEP(launch_shared_down_combine(shared_w, hs, T, topk_w, pos, o, y, s));
     MOE_MARK();
 #undef MOE_STEP

@@ -8,17 +8,16 @@
 //
 // Tiling: a workgroup computes a 128 x 128 output tile with 4 waves (2 x 2,
 // 64 x 64 each: 2 x 2 MFMA tiles).  K advances 64 at a time: operands are
-// loaded into registers two steps ahead and written to a double-buffered LDS
-// tile one step ahead; rows of 64 bf16 (128 bytes) are stored with the
+// loaded into registers kPrefetch steps ahead and written to a double-buffered
+// LDS tile one step ahead; rows of 64 bf16 (128 bytes) are stored with the
 // 16-byte group position swizzled by bits 1..3 of the row, so the MFMA reads
 // of 16 consecutive rows hit 16 distinct 4-bank slots.
 //
-// Epilogues: fp32 store (+ per-column bias) for the logits; SwiGLU for the
-// shared gate/up, whose 128-column tile is 64 gate rows and the same 64 up
-// rows (each wave's two 32-column MFMA tiles are a gate tile and its up tile,
-// so silu(g) * u pairs registers of one lane); and the combine of the layer
-// for the shared down projection: y = bf16(z + sum_j w_j o[pos[6t + j]]),
-// slots in order.
+// Epilogues: fp32 store (+ per-column bias) for the logits and the shared
+// down projection z; SwiGLU for the shared gate/up, whose 128-column tile is
+// 64 gate rows and the same 64 up rows (each wave's two 32-column MFMA tiles
+// are a gate tile and its up tile, so silu(g) * u pairs registers of one
+// lane).  The layer's combine follows as its own pass (k_combine).
 #include "common.h"
 #include "launch.h"
 
@@ -35,9 +34,10 @@ constexpr int kRowBytes = kStepK * 2;
 constexpr int kChunksPerRow = kRowBytes / 16;
 constexpr int kSlotBytes = kTile * kRowBytes;    // 16 KB per operand per slot
 constexpr int kStageLoads = kTile * kChunksPerRow / 256;   // 16-byte loads per thread per operand per step
+constexpr int kPrefetch = 2;                     // steps whose operands are in flight in registers
 constexpr int kXcds = 8;
 
-enum { kEpiStore = 0, kEpiSwiglu = 1, kEpiCombine = 2 };
+enum { kEpiStore = 0, kEpiSwiglu = 1 };
 
 struct DenseJob {
     const uint16_t *B;   // weight rows, K contiguous
@@ -45,11 +45,8 @@ struct DenseJob {
     int epi;
     int up_row;          // SwiGLU: first up row (gate rows start at 0)
     const float *bias;   // kEpiStore: per column, or null
-    void *out;           // f32 (store) or bf16 (SwiGLU, combine) [M][ldo]
+    void *out;           // f32 (store) or bf16 (SwiGLU) [M][ldo]
     int ldo;
-    const float *topk_w; // combine
-    const int *pos;
-    const float *o;
 };
 struct DenseJobs {
     DenseJob job[2];
@@ -100,9 +97,6 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
     J.bias = second ? j1.bias : j0.bias;
     J.out = second ? j1.out : j0.out;
     J.ldo = second ? j1.ldo : j0.ldo;
-    J.topk_w = second ? j1.topk_w : j0.topk_w;
-    J.pos = second ? j1.pos : j0.pos;
-    J.o = second ? j1.o : j0.o;
     if (second) nt -= j0.n_tiles;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
@@ -135,7 +129,7 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
         boff[i] = (uint32_t)b_row(r) * (K * 2) + grp * 16;
         ldst[i] = r * kRowBytes + pos * 16;
     }
-    uint4 stg[2][2 * kStageLoads];
+    uint4 stg[kPrefetch][2 * kStageLoads];
     auto load = [&](int set, int step) {
 #pragma unroll
         for (int i = 0; i < kStageLoads; ++i) {
@@ -159,8 +153,8 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[x][y][i] = 0.0f;
 
-    load(0, 0);
-    load(1, 1);
+#pragma unroll
+    for (int d = 0; d < kPrefetch; ++d) load(d, d);
     store(0, 0);
     __syncthreads();
 
@@ -168,7 +162,8 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
     for (int s = 0; s < kSteps; ++s) {
         const int slot = s & 1;
         __builtin_amdgcn_sched_barrier(0);
-        if (s + 2 < kSteps) load(slot, s + 2);
+        // the register set of step s (already in LDS) takes step s + kPrefetch
+        if (s + kPrefetch < kSteps) load(s % kPrefetch, s + kPrefetch);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int j = 0; j < kChunksPerRow / 2; ++j) {
@@ -191,12 +186,17 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
         }
         // the next step's operands (loaded during the previous step) into the
         // other LDS slot, which every wave finished reading before the last barrier
-        if (s + 1 < kSteps) store(slot ^ 1, slot ^ 1);
+        if (s + 1 < kSteps) store((s + 1) % kPrefetch, slot ^ 1);
         __syncthreads();
     }
     mfma_drain();
 
     // epilogue: lane holds rows 64wm + 32x + 8(i/4) + 4g + (i%4), column 64wn + 32y + n
+    float bcol[2] = {0.0f, 0.0f};
+    if (J.epi == kEpiStore && J.bias) {
+        bcol[0] = J.bias[nt * kTile + 64 * wn + n];
+        bcol[1] = J.bias[nt * kTile + 64 * wn + 32 + n];
+    }
 #pragma unroll
     for (int x = 0; x < 2; ++x) {
 #pragma unroll
@@ -208,31 +208,18 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
 #pragma unroll
                 for (int y = 0; y < 2; ++y) {
                     const int c = nt * kTile + 64 * wn + 32 * y + n;
-                    o[(size_t)m * J.ldo + c] = acc[x][y][i] + (J.bias ? J.bias[c] : 0.0f);
+                    o[(size_t)m * J.ldo + c] = acc[x][y][i] + bcol[y];
                 }
-            } else if (J.epi == kEpiSwiglu) {
+            } else {   // kEpiSwiglu
                 const float gv = acc[x][0][i], uv = acc[x][1][i];
                 const int r = nt * 64 + 32 * wn + n;
                 static_cast<uint16_t *>(J.out)[(size_t)m * J.ldo + r] = f32_to_bf16(gv / (1.0f + expf(-gv)) * uv);
-            } else {
-#pragma unroll
-                for (int y = 0; y < 2; ++y) {
-                    const int c = nt * kTile + 64 * wn + 32 * y + n;
-                    float v = acc[x][y][i];
-#pragma unroll
-                    for (int j = 0; j < kTopK; ++j) {
-                        const float w = J.topk_w[(size_t)m * kTopK + j];
-                        const int p = J.pos[(size_t)m * kTopK + j];
-                        v = fmaf(w, J.o[(size_t)p * kH + c], v);
-                    }
-                    static_cast<uint16_t *>(J.out)[(size_t)m * J.ldo + c] = f32_to_bf16(v);
-                }
             }
         }
     }
 }
 
-static DenseJob no_dense_job() { return DenseJob{nullptr, 0, kEpiStore, 0, nullptr, nullptr, 0, nullptr, nullptr, nullptr}; }
+static DenseJob no_dense_job() { return DenseJob{nullptr, 0, kEpiStore, 0, nullptr, nullptr, 0}; }
 
 template <int K>
 static void launch_dense(const uint16_t *A, int M, const DenseJobs &jobs, hipStream_t s) {
@@ -245,17 +232,65 @@ static void launch_dense(const uint16_t *A, int M, const DenseJobs &jobs, hipStr
 void launch_router_and_shared_gateup_dense(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
                                            float *logits, const uint16_t *shared_w, uint16_t *hs, hipStream_t s) {
     DenseJobs jobs;
-    jobs.job[0] = DenseJob{router_w, kE / kTile, kEpiStore, 0, bias, logits, kE, nullptr, nullptr, nullptr};
-    jobs.job[1] = DenseJob{shared_w, kIS / 64, kEpiSwiglu, kIS, nullptr, hs, kIS, nullptr, nullptr, nullptr};
+    jobs.job[0] = DenseJob{router_w, kE / kTile, kEpiStore, 0, bias, logits, kE};
+    jobs.job[1] = DenseJob{shared_w, kIS / 64, kEpiSwiglu, kIS, nullptr, hs, kIS};
     launch_dense<kH>(x, T, jobs, s);
 }
 
-void launch_shared_down_combine_dense(const uint16_t *shared_w, const uint16_t *hs, int T, const float *topk_w,
-                                      const int *pos, const float *o, uint16_t *y, hipStream_t s) {
+void launch_shared_down_dense(const uint16_t *shared_w, const uint16_t *hs, int T, float *z, hipStream_t s) {
     DenseJobs jobs;
-    jobs.job[0] = DenseJob{shared_w + 2 * kSharedGateElems, kH / kTile, kEpiCombine, 0, nullptr, y, kH, topk_w, pos, o};
+    jobs.job[0] = DenseJob{shared_w + 2 * kSharedGateElems, kH / kTile, kEpiStore, 0, nullptr, z, kH};
     jobs.job[1] = no_dense_job();
     launch_dense<kIS>(hs, T, jobs, s);
+}
+
+// y[t] = bf16(z[t] + sum_j w[t][j] o[pos[6t + j]]), slots in order: a wave per
+// token, lane l owns columns [32l, 32l + 32); every load of the token is in
+// flight at once (the gathers of an epilogue inside the GEMM tile were
+// latency-bound).
+__global__ __launch_bounds__(256) void k_combine(const float *__restrict__ z, const float *__restrict__ topk_w,
+                                                 const int *__restrict__ pos, const float *__restrict__ o, int T,
+                                                 uint16_t *__restrict__ y) {
+    const int t = blockIdx.x * 4 + wave_id();
+    if (t >= T) return;
+    const int lane = threadIdx.x & 63;
+    float w[kTopK];
+    int p[kTopK];
+#pragma unroll
+    for (int j = 0; j < kTopK; ++j) {
+        w[j] = __builtin_bit_cast(float, uniform(__builtin_bit_cast(int, topk_w[(size_t)t * kTopK + j])));
+        p[j] = uniform(pos[(size_t)t * kTopK + j]);
+    }
+    const float4 *zr = reinterpret_cast<const float4 *>(z + (size_t)t * kH) + 8 * lane;
+    float4 acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = zr[i];
+#pragma unroll
+    for (int j = 0; j < kTopK; ++j) {
+        const float4 *orow = reinterpret_cast<const float4 *>(o + (size_t)p[j] * kH) + 8 * lane;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float4 v = orow[i];
+            acc[i].x = fmaf(w[j], v.x, acc[i].x);
+            acc[i].y = fmaf(w[j], v.y, acc[i].y);
+            acc[i].z = fmaf(w[j], v.z, acc[i].z);
+            acc[i].w = fmaf(w[j], v.w, acc[i].w);
+        }
+    }
+    uint32_t packed[16];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        packed[2 * i] = (uint32_t)f32_to_bf16(acc[i].x) | ((uint32_t)f32_to_bf16(acc[i].y) << 16);
+        packed[2 * i + 1] = (uint32_t)f32_to_bf16(acc[i].z) | ((uint32_t)f32_to_bf16(acc[i].w) << 16);
+    }
+    uint4 *yr = reinterpret_cast<uint4 *>(y + (size_t)t * kH) + 4 * lane;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) yr[i] = make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
+}
+
+void launch_combine(const float *z, const float *topk_w, const int *pos, const float *o, int T, uint16_t *y,
+                    hipStream_t s) {
+    hipLaunchKernelGGL(k_combine, dim3((T + 3) / 4), dim3(256), 0, s, z, topk_w, pos, o, T, y);
 }
 
 }  // namespace moe_w4

@@ -50,8 +50,10 @@ void launch_shared_down_combine(const uint16_t *shared_w, const uint16_t *hs, in
 // The same two launches for many tokens (prefill sizes): LDS-tiled MFMA GEMMs.
 void launch_router_and_shared_gateup_dense(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
                                            float *logits, const uint16_t *shared_w, uint16_t *hs, hipStream_t s);
-void launch_shared_down_combine_dense(const uint16_t *shared_w, const uint16_t *hs, int T, const float *topk_w,
-                                      const int *pos, const float *o, uint16_t *y, hipStream_t s);
+// shared down projection z = h Wsd^T (fp32), then the combine as its own pass
+void launch_shared_down_dense(const uint16_t *shared_w, const uint16_t *hs, int T, float *z, hipStream_t s);
+void launch_combine(const float *z, const float *topk_w, const int *pos, const float *o, int T, uint16_t *y,
+                    hipStream_t s);
 
 // Stack glue: x_bf16 = bf16(rmsnorm(resid)); resid += f32(y).
 void launch_rmsnorm_bf16(const float *resid, int T, uint16_t *x, hipStream_t s);
