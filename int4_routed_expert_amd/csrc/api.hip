@@ -118,6 +118,7 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     float *at_scale = ws_at<float>(ws, L.at_scale);
     uint16_t *hs = ws_at<uint16_t>(ws, L.hs);
     float *o = ws_at<float>(ws, L.o);
+    uint16_t *o_bf16 = ws_at<uint16_t>(ws, L.o);   // the grouped path keeps o in bf16
     float *z = ws_at<float>(ws, L.z);
     int *chunks = ws_at<int>(ws, L.chunks);
     int *n_chunks = ws_at<int>(ws, L.n_chunks);
@@ -159,7 +160,7 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
         MOE_STEP(launch_gateup_mfma(codes, scales, xt, xt_scale, perm, chunks, n_chunks, T, at, at_scale, s));
         MOE_MARK();
         MOE_MARK();
-        MOE_STEP(launch_down_mfma(codes, scales, at, at_scale, chunks, n_chunks, T, o, s));
+        MOE_STEP(launch_down_mfma(codes, scales, at, at_scale, chunks, n_chunks, T, o_bf16, s));
         MOE_MARK();
     } else {
         MOE_STEP(launch_gateup_gemv(codes, scales, xt, xt_scale, perm, active, T, act, s));
@@ -171,7 +172,7 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     }
     if (grouped) {
         MOE_STEP(launch_shared_down_dense(shared_w, hs, T, z, s));
-        MOE_STEP(launch_combine(z, topk_w, pos, o, T, y, s));
+        MOE_STEP(launch_combine(z, topk_w, pos, o_bf16, T, y, s));
     } else
         MOE_STEP(launch_shared_down_combine(shared_w, hs, T, topk_w, pos, o, y, s));
     MOE_MARK();

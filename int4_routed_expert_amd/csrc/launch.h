@@ -39,8 +39,9 @@ int max_chunks(int T);
 void launch_gateup_mfma(const uint8_t *codes, const uint16_t *scales, const uint32_t *xt, const float *xt_scale,
                         const int *perm, const int *chunks, const int *n_chunks, int T, uint32_t *at,
                         float *at_scale, hipStream_t s);
+// o in bf16 on this path
 void launch_down_mfma(const uint8_t *codes, const uint16_t *scales, const uint32_t *at, const float *at_scale,
-                      const int *chunks, const int *n_chunks, int T, float *o, hipStream_t s);
+                      const int *chunks, const int *n_chunks, int T, uint16_t *o, hipStream_t s);
 
 // Shared expert down projection fused with the combine:
 // y = bf16(h Wsd^T + sum_j w_j o[pos[6t+j]]), slots in order.
@@ -52,7 +53,7 @@ void launch_router_and_shared_gateup_dense(const uint16_t *x, int T, const uint1
                                            float *logits, const uint16_t *shared_w, uint16_t *hs, hipStream_t s);
 // shared down projection z = h Wsd^T (fp32), then the combine as its own pass
 void launch_shared_down_dense(const uint16_t *shared_w, const uint16_t *hs, int T, float *z, hipStream_t s);
-void launch_combine(const float *z, const float *topk_w, const int *pos, const float *o, int T, uint16_t *y,
+void launch_combine(const float *z, const float *topk_w, const int *pos, const uint16_t *o, int T, uint16_t *y,
                     hipStream_t s);
 
 // Stack glue: x_bf16 = bf16(rmsnorm(resid)); resid += f32(y).
