@@ -391,10 +391,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // normalisations are undone once per output.
 // =========================================================================
 constexpr int kDnPitch = 1040;   // bytes per LDS row (1024 + 16)
-constexpr int kDnTiles = kH / 128;
-constexpr int kDnCodeRing = 4;
+constexpr int kDnHalves = 2;     // wave groups of the workgroup, each over half of the features
+constexpr int kDnTiles = kH / 128 / kDnHalves;
+constexpr int kDnCodeRing = 2;
 
-__global__ __launch_bounds__(256) void k_down_mfma(const uint8_t *__restrict__ codes,
+__global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu(2))) void k_down_mfma(const uint8_t *__restrict__ codes,
                                                    const uint16_t *__restrict__ scales,
                                                    const uint32_t *__restrict__ at,
                                                    const float *__restrict__ at_scale,
@@ -410,12 +411,14 @@ __global__ __launch_bounds__(256) void k_down_mfma(const uint8_t *__restrict__ c
     const int4 ch = chunks[chunk];
     const int e = uniform(ch.x), row0 = uniform(ch.y), rows = uniform(ch.z);
     const int n_mt = uniform((rows + 31) >> 5);
-    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id() & 3, half = wave_id() >> 2;
     const int n = lane & 31, g = lane >> 5;
 
     const __amdgpu_buffer_rsrc_t cres =
         make_buf(codes + (size_t)e * kCodeBytesPerExpert + kCodeBytesGu, (uint32_t)(kH * kI / 2));
-    const int f0 = 32 * wave + n;   // the feature whose codes this lane loads, in tile 0
+    // the feature whose codes this lane loads, in tile 0 of its half
+    const int fh = half * (kH / kDnHalves);
+    const int f0 = fh + 32 * wave + n;
     uint4 cb[kDnCodeRing][8];
     auto fetch = [&](int slot, int tile) {
         const uint32_t off = (uint32_t)(f0 + 128 * tile) * (kI / 2) + 32 * g;
@@ -427,14 +430,13 @@ __global__ __launch_bounds__(256) void k_down_mfma(const uint8_t *__restrict__ c
     };
     // the codes do not depend on the chunk's tokens: in flight first
     __builtin_amdgcn_sched_barrier(0);
-    fetch(0, 0);
-    fetch(1, 1);
-    fetch(2, 2);
+#pragma unroll
+    for (int d = 0; d < kDnCodeRing - 1; ++d) fetch(d, d);
     __builtin_amdgcn_sched_barrier(0);
 
     // the expert's down scales, transposed to [block][feature], and each
-    // feature's normalisation: thread t takes features 8t..8t+7
-    {
+    // feature's normalisation: thread t < 256 takes features 8t..8t+7
+    if (tid < 256) {
         const uint4 *src = reinterpret_cast<const uint4 *>(scales + (size_t)e * kScalesPerExpert + kScalesGu) + 4 * tid;
         const uint4 s0 = src[0], s1 = src[1], s2 = src[2], s3 = src[3];
         const uint32_t w[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
@@ -458,7 +460,7 @@ __global__ __launch_bounds__(256) void k_down_mfma(const uint8_t *__restrict__ c
     // stage the chunk's activations: thread -> (row, part); load i takes the
     // row's 16-byte group 4i + part (block i / 4), brought to the row's
     // largest block prescale
-    for (int srow = tid >> 2; srow < kChunkRows; srow += 64) {
+    for (int srow = tid >> 2; srow < kChunkRows; srow += 64 * kDnHalves) {
         const int part = tid & 3;
         const int p = row0 + min(srow, rows - 1);
         const uint4 *src = reinterpret_cast<const uint4 *>(at + (size_t)p * (kI / 2)) + part;
@@ -491,15 +493,15 @@ __global__ __launch_bounds__(256) void k_down_mfma(const uint8_t *__restrict__ c
     const __amdgpu_buffer_rsrc_t ores = make_buf(o + (size_t)row0 * kH, (uint32_t)rows * kH * 2);
 
     // unrolled by the ring size, so ring slots are compile-time; the fetch
-    // index is clamped (the last tiles re-read tile 15, in bounds) so that
-    // every iteration issues the same loads and the waits stay exact
+    // index is clamped (the last tiles re-read the last tile, in bounds) so
+    // that every iteration issues the same loads and the waits stay exact
     with_tiles(n_mt, [&](auto tiles) {
     constexpr int MT = decltype(tiles)::value;
 #pragma unroll kDnCodeRing
     for (int t = 0; t < kDnTiles; ++t) {
         const int cs = t % kDnCodeRing;
         __builtin_amdgcn_sched_barrier(0);
-        fetch((t + 3) % kDnCodeRing, min(t + 3, kDnTiles - 1));
+        fetch((t + kDnCodeRing - 1) % kDnCodeRing, min(t + kDnCodeRing - 1, kDnTiles - 1));
         __builtin_amdgcn_sched_barrier(0);
         const uint32_t zero = opaque(0);
         const uint8_t *abase = lds + zero;
@@ -550,7 +552,7 @@ __global__ __launch_bounds__(256) void k_down_mfma(const uint8_t *__restrict__ c
         }
         mfma_drain();
         // lane: token 32h + n, features 128t + 32w + 8q + 4g + 0..3 in acc[h][4q..4q+3]
-        const int fb = 128 * t + 32 * wave + 4 * g;
+        const int fb = fh + 128 * t + 32 * wave + 4 * g;
         float4 kq[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) kq[q] = *reinterpret_cast<const float4 *>(&fk[fb + 8 * q + zero]);
@@ -588,7 +590,7 @@ void launch_gateup_mfma(const uint8_t *codes, const uint16_t *scales, const uint
 
 void launch_down_mfma(const uint8_t *codes, const uint16_t *scales, const uint32_t *at, const float *at_scale,
                       const int *chunks, const int *n_chunks, int T, uint16_t *o, hipStream_t s) {
-    hipLaunchKernelGGL(k_down_mfma, dim3(grid_for(T, 1)), dim3(256), 0, s, codes, scales, at, at_scale,
+    hipLaunchKernelGGL(k_down_mfma, dim3(grid_for(T, 1)), dim3(256 * kDnHalves), 0, s, codes, scales, at, at_scale,
                        reinterpret_cast<const int4 *>(chunks), n_chunks, o);
 }
 
