@@ -203,7 +203,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const int n = lane & 31, g = lane >> 5;
     constexpr int kBlocks = kH / kG;
 
-    if (tid < kChunkRows) row_p[tid] = xt_scale[perm[row0 + min(tid, rows - 1)] / kTopK];
     // this lane's gate and up rows
     const int gr = kG * nt + 32 * wave + n;
     const __amdgpu_buffer_rsrc_t cres = make_buf(codes + (size_t)e * kCodeBytesPerExpert, (uint32_t)kCodeBytesGu);
@@ -218,14 +217,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         cb[slot][2] = bload16(cres, uoff + o, 0);
         cb[slot][3] = bload16(cres, uoff + o + 16, 0);
     };
+    // the codes and scales depend only on the expert: requested before the
+    // chunk's tokens are looked up.  Issue order: codes(0..2), scales, then
+    // (below) A(0), A(1); per block b: codes(b+3) (4 loads), A(b+2) (NI
+    // loads).  The vmcnt waits count on this order: waiting for A(b+1) also
+    // covers every codes block up to b+2.
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(0, 0);
+    fetch(1, 1);
+    fetch(2, 2);
     // the 16 block scales of the gate row and of the up row (bf16)
     uint4 sg[2], su[2];
     sg[0] = bload16(sres, gsoff, 0);
     sg[1] = bload16(sres, gsoff + 16, 0);
     su[0] = bload16(sres, usoff, 0);
     su[1] = bload16(sres, usoff + 16, 0);
-
-    const int kg = scale_shift(sg[0], sg[1]), ku = scale_shift(su[0], su[1]);
+    __builtin_amdgcn_sched_barrier(0);
+    if (tid < kChunkRows) row_p[tid] = xt_scale[perm[row0 + min(tid, rows - 1)] / kTopK];
 
     // a = silu(g) * u for this workgroup's 128 columns goes into LDS (fp32)
     // after the main loop: rows 0..47 in ring0, rows 48..95 in ring1
@@ -250,16 +258,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             __builtin_amdgcn_global_load_lds(asrc[i] + blk * 256,
                                              (lds_void_t *)(slot_ptr(slot) + 4 * (NI * wave + i) * 256), 16, 0, 0);
     };
-    // issue order: codes(0..2), A(0), A(1); then per block b: codes(b+3) (4
-    // loads), A(b+2) (NI loads).  The vmcnt waits below count on this order:
-    // waiting for A(b+1) also covers every codes block up to b+2.
     __builtin_amdgcn_sched_barrier(0);
-    fetch(0, 0);
-    fetch(1, 1);
-    fetch(2, 2);
     issue_a(0, 0);
     issue_a(1, 1);
     __builtin_amdgcn_sched_barrier(0);
+    const int kg = scale_shift(sg[0], sg[1]), ku = scale_shift(su[0], su[1]);
     wait_vmcnt_lds<NI>();   // A(0) and the row_p stores done (A(1) may be in flight)
     block_barrier();
 
@@ -316,7 +319,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             const int m = 32 * h + 8 * (i >> 2) + 4 * g + (i & 3);
             const float p = row_p[m];
             const float gv = accg[h][i] * gscale * p, uv = accu[h][i] * uscale * p;
-            act_row(m)[32 * wave + n] = gv / (1.0f + expf(-gv)) * uv;
+            // silu with the hardware exp and reciprocal (relative error ~1e-7)
+            act_row(m)[32 * wave + n] = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv)) * uv;
         }
     });
     __syncthreads();
