@@ -95,6 +95,14 @@ __global__ __launch_bounds__(256) void k_topk_rotate(const float *__restrict__ l
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
 
+    // x is independent of the logits: its loads go out first, so the two
+    // memory round trips overlap
+    uint4 xq[4];
+    {
+        const uint4 *xp = reinterpret_cast<const uint4 *>(x + (size_t)t * kH + lane * 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xq[i] = xp[i];
+    }
     // ---- top-6 ----
     const float4 lv = reinterpret_cast<const float4 *>(logits + (size_t)t * kE)[lane];
     uint32_t key[4] = {order_key(lv.x), order_key(lv.y), order_key(lv.z), order_key(lv.w)};
@@ -137,10 +145,9 @@ __global__ __launch_bounds__(256) void k_topk_rotate(const float *__restrict__ l
 
     // ---- rotated x: 16 Hadamard blocks, lane l holds K [32l, 32l+32) ----
     float v[32];
-    const uint4 *xp = reinterpret_cast<const uint4 *>(x + (size_t)t * kH + lane * 32);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const uint4 q = xp[i];
+        const uint4 q = xq[i];
         v[8 * i + 0] = bf16lo(q.x); v[8 * i + 1] = bf16hi(q.x);
         v[8 * i + 2] = bf16lo(q.y); v[8 * i + 3] = bf16hi(q.y);
         v[8 * i + 4] = bf16lo(q.z); v[8 * i + 5] = bf16hi(q.z);
