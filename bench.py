@@ -315,6 +315,11 @@ def main():
         "routed_down": n_touched * EXPERT_D_BYTES + T * 6 * 2048 * 4,
         "shared_down_combine": 1024 * 2048 * 2 + T * 1024 * 2 + T * 6 * 2048 * 4 + act,
     }
+    if T <= m.FUSED_MAX_TOKENS:
+        # one launch after the router runs the rest of the layer (its time is
+        # recorded under routed_gateup; the later stages are empty)
+        stage_bytes["routed_gateup"] = (n_touched * EXPERT_BYTES + 1024 * 2048 * 2 + T * 256 * 4 + act
+                                        + T * 1024 * 2 + act)
     dom_bytes = stage_bytes.get(dom, 0.0)
     achieved = dom_bytes / (stage[dom] * 1e-3) / 1e9
     result["value"] = T / (ms / 1e3)

@@ -71,6 +71,12 @@ extern "C" {
 #define MOE_W4_SHARED_ELEMS 6291456
 #define MOE_W4_MAX_TOKENS 1048576
 #define MOE_W4_ALIGN 16
+/* From 1 to this many tokens a forward call is two launches (router + shared
+ * gate/up, then the rest of the layer in one launch whose workgroups hand the
+ * routed gate/up results to the down projection through device-scope counters
+ * in the workspace's `sync` region, cleared by the first launch); from
+ * MOE_W4_FUSED_MAX_TOKENS + 1 tokens on, one launch per step. */
+#define MOE_W4_FUSED_MAX_TOKENS 8
 
 /* status codes */
 #define MOE_W4_OK 0
@@ -93,7 +99,9 @@ extern "C" {
  *   chunks    i32 [n][4]  from T >= 128 on (MFMA grouped path): {expert, first sorted
  *                         position, rows <= 96, 0} covering each expert's sorted
  *                         positions in order, ascending by expert; n_chunks i32 [1]
- *                         holds n.  (Written at every T; read only on that path.) */
+ *                         holds n.  (Written at every T; read only on that path.)
+ *   sync      4096 bytes of counters for the fused decode launch; their
+ *             contents on entry do not matter (the call clears them itself). */
 typedef struct moe_w4_ws_layout {
     size_t logits, topk_idx, topk_w, offsets, perm, pos, n_active, active;
     size_t xt, xt_scale, act, at, at_scale, hs, o, z, chunks, n_chunks, sync;

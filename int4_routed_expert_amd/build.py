@@ -23,7 +23,7 @@ LIB = os.path.join(PKG, "libmoe_w4.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "router.hip", "skinny_mfma.hip", "experts_gemv.hip", "grouped_mfma.hip", "dense_mfma.hip",
-           "stack.hip",
+           "stack.hip", "decode_fused.hip",
            "generate.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -123,6 +123,8 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     int *chunks = ws_at<int>(ws, L.chunks);
     int *n_chunks = ws_at<int>(ws, L.n_chunks);
     const bool grouped = T >= kPrefillMinTokens;
+    const bool fused = T <= kFusedMaxTokens;
+    int *counters = ws_at<int>(ws, L.sync);
 
     int stage = 0;
     auto mark = [&](void) -> int {
@@ -147,10 +149,40 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
 
     (void)hipGetLastError();   // clear a stale error so it is not blamed on this call
     MOE_MARK();
+    if (fused) {
+        // two launches: router + shared gate/up (which also clears the
+        // counters), then the rest of the layer; the other stages are empty
+        MOE_STEP(launch_router_and_shared_gateup(x, T, router_w, bias, logits, shared_w, hs, counters, s));
+        MOE_MARK();
+        MOE_MARK();
+        FusedDecodeArgs fa;
+        fa.x = x;
+        fa.logits = logits;
+        fa.codes = codes;
+        fa.scales = scales;
+        fa.shared_down = shared_w + 2 * kSharedGateElems;
+        fa.hs = hs;
+        fa.T = T;
+        fa.topk_idx = topk_idx;
+        fa.topk_w = topk_w;
+        fa.offsets = offsets;
+        fa.perm = perm;
+        fa.pos = pos;
+        fa.n_active = n_active;
+        fa.slots = active;
+        fa.chunks = reinterpret_cast<int4 *>(chunks);
+        fa.n_chunks = n_chunks;
+        fa.act = act;
+        fa.y = y;
+        fa.counters = counters;
+        MOE_STEP(launch_decode_fused(fa, s));
+        for (int i = 0; i < 4; ++i) MOE_MARK();
+        return MOE_W4_OK;
+    }
     if (grouped)
         MOE_STEP(launch_router_and_shared_gateup_dense(x, T, router_w, bias, logits, shared_w, hs, s));
     else
-        MOE_STEP(launch_router_and_shared_gateup(x, T, router_w, bias, logits, shared_w, hs, s));
+        MOE_STEP(launch_router_and_shared_gateup(x, T, router_w, bias, logits, shared_w, hs, nullptr, s));
     MOE_MARK();
     MOE_STEP(launch_topk_rotate(logits, x, T, topk_idx, topk_w, xt, xt_scale, s));
     MOE_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, s));

@@ -153,7 +153,28 @@ __device__ __forceinline__ void order_after(uint4 &next, float after) {
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ int wave_id() { return uniform(threadIdx.x >> 6); }
 
-__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, kWave); }
+// v of lane (lane ^ m).  For the partners inside a row of 16 lanes (m = 1, 2,
+// 4, 8, known at compile time after unrolling) this is a DPP move (quad
+// permutes and row rotations) instead of an LDS crossbar round trip; other
+// distances use ds_bpermute.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float shfl_xor_f(float v, int m) {
+    if (__builtin_constant_p(m)) {
+        if (m == 1) return dpp_move<0xb1>(v);   // quad_perm [1, 0, 3, 2]
+        if (m == 2) return dpp_move<0x4e>(v);   // quad_perm [2, 3, 0, 1]
+        if (m == 4) {
+            // row_ror:r gives lane i the value of lane (i - r) mod 16 of its row
+            const float from_below = dpp_move<0x124>(v);   // lane i - 4
+            const float from_above = dpp_move<0x12c>(v);   // lane i + 4
+            return (threadIdx.x & 4) ? from_below : from_above;
+        }
+        if (m == 8) return dpp_move<0x128>(v);  // row_ror:8: lane i ^ 8
+    }
+    return __shfl_xor(v, m, kWave);
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

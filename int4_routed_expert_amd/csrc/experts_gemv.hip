@@ -15,46 +15,9 @@
 // HBM once for all tokens routed to that expert.
 #include "common.h"
 #include "launch.h"
+#include "gemv_ops.h"
 
 namespace moe_w4 {
-
-__device__ __forceinline__ uint4 ldg4(const void *p) { return *reinterpret_cast<const uint4 *>(p); }
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-// Load one lane's 32 stored activations (16 half2 words) and their offset.
-__device__ __forceinline__ float load_operand32(const uint32_t *src, uint32_t (&xs)[16]) {
-    float off = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint4 v = ldg4(src + 4 * i);
-        xs[4 * i] = v.x; xs[4 * i + 1] = v.y; xs[4 * i + 2] = v.z; xs[4 * i + 3] = v.w;
-        off = q_offset(v.x, v.y, v.z, v.w, off);
-    }
-    return off;
-}
-
-// sum_k c_k x_k over one lane's 32-element slice: 16 dot2 on mask-converted codes.
-__device__ __forceinline__ float dot_slice(const Q4 (&q)[4], const uint32_t (&xs)[16], float acc) {
-#pragma unroll
-    for (int d = 0; d < 4; ++d) {
-        acc = dot2h(q[d].q0, xs[4 * d + 0], acc);
-        acc = dot2h(q[d].q1, xs[4 * d + 1], acc);
-        acc = dot2h(q[d].q2, xs[4 * d + 2], acc);
-        acc = dot2h(q[d].q3, xs[4 * d + 3], acc);
-    }
-    return acc;
-}
-
-__device__ __forceinline__ void convert16(const uint4 w, Q4 (&q)[4]) {
-    q[0] = int4x8_to_q(w.x);
-    q[1] = int4x8_to_q(w.y);
-    q[2] = int4x8_to_q(w.z);
-    q[3] = int4x8_to_q(w.w);
-}
-
-__device__ __forceinline__ float silu_f(float v) { return v / (1.0f + expf(-v)); }
-
-
 
 // =========================================================================
 // gate/up.  A wave item is (active expert slot, gate rows [r0, r0 + 4*NB)
@@ -64,28 +27,6 @@ __device__ __forceinline__ float silu_f(float v) { return v / (1.0f + expf(-v));
 // known, before the tokens are read.  Lane l owns K [32l, 32l+32) of every
 // row.  One or two tokens per pass; more tokens re-read the rows (L2 hits).
 // =========================================================================
-constexpr int kGuPairs = 4;   // row pairs per batch
-
-struct GuRows {
-    uint4 g[kGuPairs], u[kGuPairs];
-    uint16_t sg[kGuPairs], su[kGuPairs];   // bf16 bits of the gate and up scales
-};
-
-template <bool RELOAD>
-__device__ __forceinline__ void gu_load_pair(GuRows &R, int i, rsrc_t cg, rsrc_t sp, uint32_t cv, uint32_t sv, int r) {
-    if (RELOAD) {
-        R.g[i] = bload16_nt_reload(cg, cv, r * (kH / 2));
-        R.u[i] = bload16_nt_reload(cg, cv, kPlaneGateBytes + r * (kH / 2));
-        R.sg[i] = bload2_nt_reload(sp, sv, 2 * r * (kH / kG));
-        R.su[i] = bload2_nt_reload(sp, sv, 2 * (kScalesGate + r * (kH / kG)));
-    } else {
-        R.g[i] = bload16_nt(cg, cv, r * (kH / 2));
-        R.u[i] = bload16_nt(cg, cv, kPlaneGateBytes + r * (kH / 2));
-        R.sg[i] = bload2_nt(sp, sv, 2 * r * (kH / kG));
-        R.su[i] = bload2_nt(sp, sv, 2 * (kScalesGate + r * (kH / kG)));
-    }
-}
-
 // NB batches of 4 row pairs for NT tokens (1 or 2; n_valid <= NT).  On entry
 // R holds the first batch; the next batch is loaded into the registers each
 // row frees.
@@ -198,49 +139,7 @@ __global__ __launch_bounds__(256) void k_rotate_act(const float *__restrict__ ac
     const int p = blockIdx.x * 4 + wave_id();
     if (p >= n_rows) return;
     const float4 *src = reinterpret_cast<const float4 *>(act + (size_t)p * kI + lane * 8);
-    const float4 a0 = src[0], a1 = src[1];
-    float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-    for (int h = 1; h < 8; h <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if ((i & h) == 0) {
-                const float a = v[i], b = v[i + h];
-                v[i] = a + b;
-                v[i + h] = a - b;
-            }
-        }
-    }
-#pragma unroll
-    for (int m = 1; m <= 8; m <<= 1) {   // strides 8..64: lanes of the same block
-        const bool upper = (lane & m) != 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float q = shfl_xor_f(v[i], m);
-            v[i] = upper ? (q - v[i]) : (v[i] + q);
-        }
-    }
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        v[i] *= 0.08838834764831845f;
-        amax = fmaxf(amax, fabsf(v[i]));
-    }
-#pragma unroll
-    for (int m = 1; m <= 8; m <<= 1) amax = fmaxf(amax, shfl_xor_f(amax, m));
-    int sh = 0;
-    if (amax > 0.0f && isfinite(amax)) {
-        int ex;
-        frexpf(amax, &ex);
-        sh = ex - 14;   // largest magnitude in [2^13, 2^14): exact scaling, far from fp16 overflow
-    }
-    uint4 w;
-    w.x = pack_half2(ldexpf(v[0], -sh), ldexpf(v[4], -sh));
-    w.y = pack_half2(ldexpf(v[1], -sh - 4), ldexpf(v[5], -sh - 4));
-    w.z = pack_half2(ldexpf(v[2], -sh), ldexpf(v[6], -sh));
-    w.w = pack_half2(ldexpf(v[3], -sh - 4), ldexpf(v[7], -sh - 4));
-    reinterpret_cast<uint4 *>(at + (size_t)p * (kI / 2))[lane] = w;
-    if ((lane & 15) == 0) at_scale[(size_t)p * (kI / kG) + (lane >> 4)] = ldexpf(1.0f, sh);
+    rotate_act_wave(src[0], src[1], lane, at + (size_t)p * (kI / 2), at_scale + (size_t)p * (kI / kG));
 }
 
 // =========================================================================

@@ -9,81 +9,9 @@
 // a fwht128-rotated basis, so x is rotated per 128-block before the experts.
 #include "common.h"
 #include "launch.h"
+#include "token_ops.h"
 
 namespace moe_w4 {
-
-// ---------------------------------------------------------------------------
-// Top-6 of one token's 256 logits, one wave per token.  Keys order floats
-// monotonically as unsigned integers; ties go to the lower expert index.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t order_key(float f) {
-    const uint32_t u = __float_as_uint(f);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_value(uint32_t k) {
-    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-// (key, e) beats (key2, e2) when the key is larger, or equal with a lower index.
-__device__ __forceinline__ bool beats(uint32_t k, int e, uint32_t k2, int e2) {
-    return k > k2 || (k == k2 && e < e2);
-}
-
-// Normalised 128-point Sylvester Hadamard on a 128-block spread over 4 lanes
-// (lane & 3 selects the 32-element quarter).  Five butterfly stages run inside
-// the lane, the strides 32 and 64 go across lanes.
-__device__ __forceinline__ void fwht128_4lanes(float (&v)[32], int lane) {
-#pragma unroll
-    for (int h = 1; h < 32; h <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            if ((i & h) == 0) {
-                const float a = v[i], b = v[i + h];
-                v[i] = a + b;
-                v[i + h] = a - b;
-            }
-        }
-    }
-#pragma unroll
-    for (int m = 1; m <= 2; m <<= 1) {
-        const bool upper = (lane & m) != 0;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const float p = shfl_xor_f(v[i], m);
-            v[i] = upper ? (p - v[i]) : (v[i] + p);
-        }
-    }
-    const float inv = 0.08838834764831845f;   // 1/sqrt(128)
-#pragma unroll
-    for (int i = 0; i < 32; ++i) v[i] *= inv;
-}
-
-// Store 32 consecutive rotated values as fp16 in the operand order of
-// int4x8_to_q: per 8-group (x0,x4) (x1/16,x5/16) (x2,x6) (x3/16,x7/16), after
-// multiplying by 2^-sh (a power-of-two prescale chosen per token or block).
-__device__ __forceinline__ void store_operand32(const float (&v)[32], int sh, uint32_t *dst) {
-    uint32_t w[16];
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-        const float *q = v + 8 * g;
-        w[4 * g + 0] = pack_half2(ldexpf(q[0], -sh), ldexpf(q[4], -sh));
-        w[4 * g + 1] = pack_half2(ldexpf(q[1], -sh - 4), ldexpf(q[5], -sh - 4));
-        w[4 * g + 2] = pack_half2(ldexpf(q[2], -sh), ldexpf(q[6], -sh));
-        w[4 * g + 3] = pack_half2(ldexpf(q[3], -sh - 4), ldexpf(q[7], -sh - 4));
-    }
-    uint4 *d = reinterpret_cast<uint4 *>(dst);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) d[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
-}
-
-// Power-of-two prescale: the largest magnitude lands in [2^13, 2^14), well
-// inside fp16, whatever the input scale (the NInfer README of Flint, section
-// "Quality", scales rows by exact powers of two against fp16 overflow).
-__device__ __forceinline__ int prescale_shift(float amax) {
-    if (!(amax > 0.0f) || !isfinite(amax)) return 0;
-    int ex;
-    frexpf(amax, &ex);   // amax = f * 2^ex, f in [0.5, 1)
-    return ex - 14;
-}
 
 __global__ __launch_bounds__(256) void k_topk_rotate(const float *__restrict__ logits,
                                                      const uint16_t *__restrict__ x, int T,
@@ -103,63 +31,16 @@ __global__ __launch_bounds__(256) void k_topk_rotate(const float *__restrict__ l
 #pragma unroll
         for (int i = 0; i < 4; ++i) xq[i] = xp[i];
     }
-    // ---- top-6 ----
     const float4 lv = reinterpret_cast<const float4 *>(logits + (size_t)t * kE)[lane];
-    uint32_t key[4] = {order_key(lv.x), order_key(lv.y), order_key(lv.z), order_key(lv.w)};
-    unsigned taken = 0;
-    int sel_e[kTopK];
-    float sel_l[kTopK];
-#pragma unroll
-    for (int j = 0; j < kTopK; ++j) {
-        uint32_t bk = 0;
-        int be = 0x7fffffff;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = 4 * lane + i;
-            if (!(taken & (1u << i)) && beats(key[i], e, bk, be)) { bk = key[i]; be = e; }
-        }
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
-            const uint32_t ok = (uint32_t)__shfl_xor((int)bk, m, kWave);
-            const int oe = __shfl_xor(be, m, kWave);
-            if (beats(ok, oe, bk, be)) { bk = ok; be = oe; }
-        }
-        if ((be >> 2) == lane) taken |= 1u << (be & 3);
-        sel_e[j] = be;
-        sel_l[j] = key_value(bk);
-    }
-    float sig[kTopK], ssum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kTopK; ++j) {
-        sig[j] = 1.0f / (1.0f + expf(-sel_l[j]));
-        ssum += sig[j];
-    }
-    const float denom = fmaxf(ssum, 6.103515625e-05f);   // 2^-14
+    const Top6 sel = top6_wave(lv, lane);
 #pragma unroll
     for (int j = 0; j < kTopK; ++j) {
         if (lane == j) {
-            topk_idx[(size_t)t * kTopK + j] = sel_e[j];
-            topk_w[(size_t)t * kTopK + j] = sig[j] / denom;
+            topk_idx[(size_t)t * kTopK + j] = sel.e[j];
+            topk_w[(size_t)t * kTopK + j] = sel.w[j];
         }
     }
-
-    // ---- rotated x: 16 Hadamard blocks, lane l holds K [32l, 32l+32) ----
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint4 q = xq[i];
-        v[8 * i + 0] = bf16lo(q.x); v[8 * i + 1] = bf16hi(q.x);
-        v[8 * i + 2] = bf16lo(q.y); v[8 * i + 3] = bf16hi(q.y);
-        v[8 * i + 4] = bf16lo(q.z); v[8 * i + 5] = bf16hi(q.z);
-        v[8 * i + 6] = bf16lo(q.w); v[8 * i + 7] = bf16hi(q.w);
-    }
-    fwht128_4lanes(v, lane);
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-    amax = wave_max(amax);
-    const int sh = prescale_shift(amax);
-    store_operand32(v, sh, xt + (size_t)t * (kH / 2) + lane * 16);
+    const int sh = rotate_x_wave(xq, lane, xt + (size_t)t * (kH / 2) + lane * 16);
     if (lane == 0) xt_scale[t] = ldexpf(1.0f, sh);
 }
 

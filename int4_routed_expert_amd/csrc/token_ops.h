@@ -1,0 +1,155 @@
+// Per-token device routines shared by the routing kernels and the fused
+// decode kernel: top-6 selection of one token's logits, the normalised
+// 128-point Hadamard of x, and the fp16 operand layout of the int4 GEMVs.
+#pragma once
+
+#include "common.h"
+
+namespace moe_w4 {
+
+// ---------------------------------------------------------------------------
+// Top-6 of one token's 256 logits, one wave per token.  Keys order floats
+// monotonically as unsigned integers; ties go to the lower expert index.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t order_key(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_value(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Normalised 128-point Sylvester Hadamard on a 128-block spread over 4 lanes
+// (lane & 3 selects the 32-element quarter).  Five butterfly stages run inside
+// the lane, the strides 32 and 64 go across lanes.
+__device__ __forceinline__ void fwht128_4lanes(float (&v)[32], int lane) {
+#pragma unroll
+    for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            if ((i & h) == 0) {
+                const float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 1; m <= 2; m <<= 1) {
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const float p = shfl_xor_f(v[i], m);
+            v[i] = upper ? (p - v[i]) : (v[i] + p);
+        }
+    }
+    const float inv = 0.08838834764831845f;   // 1/sqrt(128)
+#pragma unroll
+    for (int i = 0; i < 32; ++i) v[i] *= inv;
+}
+
+// Store 32 consecutive rotated values as fp16 in the operand order of
+// int4x8_to_q: per 8-group (x0,x4) (x1/16,x5/16) (x2,x6) (x3/16,x7/16), after
+// multiplying by 2^-sh (a power-of-two prescale chosen per token or block).
+__device__ __forceinline__ void store_operand32(const float (&v)[32], int sh, uint32_t *dst) {
+    uint32_t w[16];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const float *q = v + 8 * g;
+        w[4 * g + 0] = pack_half2(ldexpf(q[0], -sh), ldexpf(q[4], -sh));
+        w[4 * g + 1] = pack_half2(ldexpf(q[1], -sh - 4), ldexpf(q[5], -sh - 4));
+        w[4 * g + 2] = pack_half2(ldexpf(q[2], -sh), ldexpf(q[6], -sh));
+        w[4 * g + 3] = pack_half2(ldexpf(q[3], -sh - 4), ldexpf(q[7], -sh - 4));
+    }
+    uint4 *d = reinterpret_cast<uint4 *>(dst);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+}
+
+// Power-of-two prescale: the largest magnitude lands in [2^13, 2^14), well
+// inside fp16, whatever the input scale (the NInfer README of Flint, section
+// "Quality", scales rows by exact powers of two against fp16 overflow).
+__device__ __forceinline__ int prescale_shift(float amax) {
+    if (!(amax > 0.0f) || !isfinite(amax)) return 0;
+    int ex;
+    frexpf(amax, &ex);   // amax = f * 2^ex, f in [0.5, 1)
+    return ex - 14;
+}
+
+// Top-6 of one token's 256 logits by one wave (lane l holds logits 4l..4l+3).
+// Every lane ends with the six experts in slot order (descending logit, ties
+// to the lower index) and their weights sigmoid(l_j) / max(sum sigmoid, 2^-14).
+struct Top6 {
+    int e[kTopK];
+    float w[kTopK];
+};
+
+// Largest value over the wave, left in lane 63 by DPP steps (a running
+// maximum over row shifts 1, 2, 4, 8, then the two row broadcasts) and read
+// from there: no LDS round trips, unlike a butterfly of lane shuffles.  Lanes
+// that read outside their row take 0, which never wins.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));   // row_shr:1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));   // row_shr:2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));   // row_shr:4
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));   // row_shr:8
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));   // row_bcast:15
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));   // row_bcast:31
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+__device__ __forceinline__ Top6 top6_wave(float4 lv, int lane) {
+    // a taken key becomes 0, below the key of every non-NaN logit
+    uint32_t key[4] = {order_key(lv.x), order_key(lv.y), order_key(lv.z), order_key(lv.w)};
+    Top6 r;
+    float sel_l[kTopK];
+#pragma unroll
+    for (int j = 0; j < kTopK; ++j) {
+        const uint32_t K = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
+        // the lowest expert index holding K: lowest lane, then lowest slot in it
+        const int here = key[0] == K ? 0 : key[1] == K ? 1 : key[2] == K ? 2 : key[3] == K ? 3 : 4;
+        const int L = (int)__builtin_ctzll(__ballot(here < 4));
+        const int i = __builtin_amdgcn_readlane(here, L);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (lane == L && q == i) key[q] = 0;
+        r.e[j] = 4 * L + i;
+        sel_l[j] = key_value(K);
+    }
+    float ssum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kTopK; ++j) {
+        r.w[j] = 1.0f / (1.0f + expf(-sel_l[j]));
+        ssum += r.w[j];
+    }
+    const float denom = fmaxf(ssum, 6.103515625e-05f);   // 2^-14
+#pragma unroll
+    for (int j = 0; j < kTopK; ++j) r.w[j] /= denom;
+    return r;
+}
+
+// Rotated x of one token by one wave: lane l holds K [32l, 32l+32) of the bf16
+// row (four 16-byte words), so lanes 4b..4b+3 hold Hadamard block b.  Writes the
+// lane's 16 operand words to dst and returns the token's prescale shift sh
+// (operands are x_rot * 2^-sh).
+__device__ __forceinline__ int rotate_x_wave(const uint4 (&xq)[4], int lane, uint32_t *dst) {
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 q = xq[i];
+        v[8 * i + 0] = bf16lo(q.x); v[8 * i + 1] = bf16hi(q.x);
+        v[8 * i + 2] = bf16lo(q.y); v[8 * i + 3] = bf16hi(q.y);
+        v[8 * i + 4] = bf16lo(q.z); v[8 * i + 5] = bf16hi(q.z);
+        v[8 * i + 6] = bf16lo(q.w); v[8 * i + 7] = bf16hi(q.w);
+    }
+    fwht128_4lanes(v, lane);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = wave_max(amax);
+    const int sh = prescale_shift(amax);
+    store_operand32(v, sh, dst);
+    return sh;
+}
+
+}  // namespace moe_w4

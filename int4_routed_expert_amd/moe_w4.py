@@ -25,6 +25,7 @@ CODE_BYTES_PER_EXPERT = 1572864
 SCALES_PER_EXPERT = 24576
 SHARED_ELEMS = 6291456
 MAX_TOKENS = 1048576
+FUSED_MAX_TOKENS = 8
 
 OK, EINVAL, EWORKSPACE, EDEVICE = 0, -1, -2, -3
 

@@ -37,6 +37,14 @@ def test_every_declared_symbol_is_exported(m):
     assert set(m.EXPORTED) == set(names)
 
 
+def test_header_constants_match_the_binding(m):
+    defines = dict(re.findall(r"#define MOE_W4_(\w+) \(?(-?\d+)\)?", open(HEADER).read()))
+    names = ["HIDDEN", "EXPERTS", "TOPK", "INTER", "SHARED_INTER", "GROUP", "CODE_BYTES_PER_EXPERT",
+             "SCALES_PER_EXPERT", "SHARED_ELEMS", "MAX_TOKENS", "FUSED_MAX_TOKENS"]
+    for n in names:
+        assert int(defines[n]) == getattr(m, n), n
+
+
 def test_workspace_layout(m):
     assert m.moe_w4_workspace_bytes(-1) == 0
     assert m.moe_w4_workspace_bytes(m.MAX_TOKENS + 1) == 0

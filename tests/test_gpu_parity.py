@@ -169,8 +169,8 @@ def test_prefill_workloads_sampled(m, layer0, name):
 
 
 # ----------------------------------------------------------------- edge cases
-def test_one_expert_takes_every_token(m, layer0):
-    T = 40
+@pytest.mark.parametrize("T", [8, 40])
+def test_one_expert_takes_every_token(m, layer0, T):
     x = synth.gen_x(200, T)
     bias = np.zeros(256, dtype=np.float32)
     bias[17] = 100.0
@@ -180,8 +180,8 @@ def test_one_expert_takes_every_token(m, layer0):
     report("one hot expert", P.compare(g, oracle_layer(x, bias=bias), label="one hot expert"))
 
 
-def test_all_tie_router(m, layer0):
-    T = 9
+@pytest.mark.parametrize("T", [8, 9])
+def test_all_tie_router(m, layer0, T):
     x = synth.gen_x(201, T)
     w = dict(layer0)
     w["router_w"] = torch.zeros_like(layer0["router_w"])
@@ -227,20 +227,26 @@ def test_zero_tokens_is_a_noop(m, layer0):
 
 
 # ----------------------------------------------------------------- invariants
-def test_determinism_and_poisoned_workspace(m, layer0):
-    x = synth.gen_x(300, 48)
+@pytest.mark.parametrize("T", [8, 48])
+def test_determinism_and_poisoned_workspace(m, layer0, T):
+    x = synth.gen_x(300, T)
     a = P.run_gpu(m, x, layer0)
     b = P.run_gpu(m, x, layer0, poison=True)
     np.testing.assert_array_equal(a["y_bits"], b["y_bits"])
     np.testing.assert_array_equal(a["perm"], b["perm"])
 
 
-def test_batch_invariance(m, layer0):
-    x = synth.gen_x(301, 16)
+@pytest.mark.parametrize("T_full,parts", [(8, [(5, 6), (0, 3), (2, 8)]), (16, [(0, 9), (7, 16)])])
+def test_batch_invariance(m, layer0, T_full, parts):
+    """A token's output bits do not depend on the other tokens of the call, for
+    calls that take the same launch sequence (1-8 tokens: one launch after the
+    router; 9-127: the GEMV launches); across sequences the summation order
+    differs and only the oracle tolerance holds."""
+    x = synth.gen_x(301, T_full)
     full = P.run_gpu(m, x, layer0)
-    for t in (0, 5, 15):
-        one = P.run_gpu(m, x[t:t + 1], layer0)
-        np.testing.assert_array_equal(one["y_bits"][0], full["y_bits"][t])
+    for a, b in parts:
+        part = P.run_gpu(m, x[a:b], layer0)
+        np.testing.assert_array_equal(part["y_bits"], full["y_bits"][a:b])
 
 
 def test_token_permutation_equivariance(m, layer0):
