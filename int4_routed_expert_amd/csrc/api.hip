@@ -150,9 +150,9 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     (void)hipGetLastError();   // clear a stale error so it is not blamed on this call
     MOE_MARK();
     if (fused) {
-        // two launches: router + shared gate/up (which also clears the
+        // two launches: router logits and shared h (which also clear the
         // counters), then the rest of the layer; the other stages are empty
-        MOE_STEP(launch_router_and_shared_gateup(x, T, router_w, bias, logits, shared_w, hs, counters, s));
+        MOE_STEP(launch_router_shared_small(x, T, router_w, bias, shared_w, logits, hs, counters, s));
         MOE_MARK();
         MOE_MARK();
         FusedDecodeArgs fa;
@@ -182,7 +182,7 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     if (grouped)
         MOE_STEP(launch_router_and_shared_gateup_dense(x, T, router_w, bias, logits, shared_w, hs, s));
     else
-        MOE_STEP(launch_router_and_shared_gateup(x, T, router_w, bias, logits, shared_w, hs, nullptr, s));
+        MOE_STEP(launch_router_and_shared_gateup(x, T, router_w, bias, logits, shared_w, hs, s));
     MOE_MARK();
     MOE_STEP(launch_topk_rotate(logits, x, T, topk_idx, topk_w, xt, xt_scale, s));
     MOE_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, s));

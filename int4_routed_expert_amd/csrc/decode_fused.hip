@@ -1,43 +1,44 @@
-// Decode sizes (1..8 tokens): everything after the router in one launch.
+// Decode sizes (1..8 tokens): the layer in two launches.
 //
 // At these sizes every step of the layer moves little data, so the layer is
 // bound by the latency of its dependent steps rather than by bandwidth: a
-// launch per step (top-6, sort, gate/up, rotation of a, down, combine) costs
-// a few microseconds each.  Here one launch runs them all, with two roles of
-// workgroups and one dependency between them:
+// launch per step (router, top-6, sort, gate/up, rotation of a, down, combine)
+// costs a few microseconds each.  Here the first launch computes everything
+// that needs only x: the router logits (one wave per router row) and the
+// shared expert's h = bf16(silu(x Wsg^T) * (x Wsu^T)) (ungated bf16 SwiGLU of
+// width 1024, Flint model card, Aijuus/flint-w4exp, introduction; one
+// workgroup per column of h).  The second launch runs all the rest, with two
+// roles of workgroups:
 //
 //   every workgroup: the routing of all tokens from the logits (wave t: top-6
-//       of token t, Flint model card, Aijuus/flint-w4exp, introduction: 256
-//       experts, top-6; weights sigmoid / max(sum, 2^-14), bloomery issue #632,
-//       design thread), then a stable sort of the <= 48 assignments in LDS;
-//   gate/up workgroups (the first kFuGuWgs): rotated x in LDS (fwht128, model
-//       card, table row "weights"), then wave batches of 4 (gate, up) row pairs
-//       of an active expert for all of its tokens, a = silu(g) * u stored in
-//       fp32 (sorted-position order); then each workgroup counts itself done;
-//   down workgroups (the rest): each owns 8 output features.  Before waiting
-//       it computes the shared expert's down projection for its features (h is
-//       complete: the router launch wrote it) and requests the down codes of
-//       its features for every active expert.  Once every gate/up workgroup
-//       has counted itself done it rotates a of every assignment in LDS,
-//       finishes the routed down products and writes y = bf16(z + sum_j w_j o_j)
-//       in slot order.
+//       of token t, model card, introduction: 256 experts, top-6; weights
+//       sigmoid / max(sum, 2^-14), bloomery issue #632, design thread), then a
+//       stable sort of the <= 48 assignments in LDS;
+//   gate/up workgroups (the first 256): x is rotated in LDS (fwht128 per
+//       128-block, model card, table row "weights"; four waves per token, one
+//       power-of-two prescale per block, beside the top-6), then wave batches
+//       of 2 (gate, up) row pairs of an active expert for all of its tokens,
+//       a = silu(g) * u in fp32 (sorted-position order), the next batch's codes
+//       in flight while one is multiplied;
+//   down workgroups (the other 256): each owns 8 output features.  Before
+//       waiting it computes the shared down projection z of its features and
+//       requests the down codes of its features for every active expert; once
+//       a is complete it rotates a of every assignment in LDS, finishes the
+//       routed down products and writes y = bf16(z + sum_j w_j o_j) in slot
+//       order.
 //
-// The dependency is a device-scope completion counter that the router launch
-// sets to zero.  It is kept in 16 replicas on separate 256-byte lines (every
-// gate/up workgroup adds 1 to each, with one atomic per lane of a wave) and
-// each down workgroup polls one of them: 256 pollers of a single line crowd
-// that line's memory channel, and the gate/up code loads that land on the
-// same channel wait behind them (measured: 3 us loads became 8-13 us).  a crosses between the
-// workgroups with device-scope stores and loads (cache policy sc0 sc1: written
-// through to, and read from, the level shared by all XCDs), so neither side
-// needs a whole-L2 writeback or invalidate (a fence at device scope costs one
-// of those per workgroup, and with 512 workgroups they dominated the launch):
-// a gate/up workgroup waits until its stores are complete, then counts
-// itself done.  The down workgroups only ever wait for gate/up workgroups,
-// which have lower indices and never wait, so they were dispatched first and
-// finish whatever else is resident; the wait is also bounded in time, and a
-// down workgroup that gives up writes NaN to its outputs, so a failure cannot
-// hang the device and cannot go unnoticed.
+// a crosses between workgroups through device-scope stores and loads (cache
+// policy sc0 sc1: written through to, and read from, the level shared by all
+// XCDs), so neither side needs a whole-L2 writeback or invalidate, and through
+// a completion counter that the first launch sets to zero.  The counter is
+// kept in 16 replicas on separate lines (every gate/up workgroup adds 1 to
+// each, one atomic per lane) and each down workgroup polls one replica: 256
+// pollers of a single line crowd its memory channel, and code loads that land
+// on the same channel wait behind them.  Only the down workgroups wait, and
+// only for gate/up workgroups, which have lower indices and never wait, so
+// they were dispatched first and finish whatever else is resident; the wait
+// is also bounded in time, and a down workgroup that gives up writes NaN to
+// its outputs, so a failure cannot hang the device and cannot go unnoticed.
 #include "common.h"
 #include "gemv_ops.h"
 #include "launch.h"
@@ -47,52 +48,58 @@ namespace moe_w4 {
 
 namespace {
 
-constexpr int kFuMaxA = kTopK * kFusedMaxTokens;   // 48 assignments at most
 constexpr int kFuThreads = 512;
 constexpr int kFuWaves = kFuThreads / kWave;        // 8
 constexpr int kFuGuWgs = 256;                       // gate/up workgroups
 constexpr int kFuDnWgs = 256;                       // down workgroups
 constexpr int kFuCols = kH / kFuDnWgs;              // 8 output features per down workgroup
-constexpr int kFuBatchesPerExpert = kI / kGuPairs;  // 128 batches of 4 row pairs
+constexpr int kFuPairs = 2;                         // (gate, up) row pairs per wave batch
+constexpr int kFuBatchesPerExpert = kI / kFuPairs;  // 256
 constexpr uint64_t kFuWaitTicks = 500000;           // 5 ms of the 100 MHz s_memrealtime clock
 
 static_assert(kFuWaves == kFuCols, "a down wave owns one feature of the shared projection");
 static_assert(kFuWaves >= kFusedMaxTokens, "one wave per token for the routing");
 
+// Cache policy of the a hand-off: device scope (sc1) plus the volatile
+// bit, which keeps the accesses in program order around the counter and
+// barriers (the compiler adds sc0: system scope, also coherent across XCDs).
+constexpr int kHandOff = 16 | (int)(1u << 31);
+
+template <int T>
 struct FuRouting {
-    int e[kFuMaxA];       // expert of assignment a = 6t + j
-    float w[kFuMaxA];     // its weight
-    int pos[kFuMaxA];     // sorted position of assignment a
-    int perm[kFuMaxA];    // assignment at sorted position p
-    int se[kFuMaxA];      // expert at sorted position p
-    int act_e[kFuMaxA];   // active experts, ascending
-    int act_begin[kFuMaxA];
-    int act_n[kFuMaxA];
+    static constexpr int N = kTopK * T;
+    int e[N];       // expert of assignment a = 6t + j
+    float w[N];     // its weight
+    int pos[N];     // sorted position of assignment a
+    int perm[N];    // assignment at sorted position p
+    int se[N];      // expert at sorted position p
+    int act_e[N];   // active experts, ascending
+    int act_begin[N];
+    int act_n[N];
     int n_act;
 };
 
+template <int T>
 struct FuGateUp {
-    uint32_t xt[kFusedMaxTokens][kH / 2];   // rotated x, fp16 operand order
-    float xsc[kFusedMaxTokens];             // 2^sh of each token
+    uint32_t xt[T][kH / 2];         // rotated x, fp16 operand order
+    float xsc[T][kH / kG];          // 2^sh of each (token, block)
 };
 
+template <int T>
 struct FuDown {
-    uint32_t at[kFuMaxA][kI / 2];           // rotated a per sorted position
-    float atsc[kFuMaxA][kI / kG];
-    float o[kFuMaxA][kFuCols];              // routed outputs of this workgroup's features
-    float z[kFusedMaxTokens][kFuCols];      // shared expert outputs
+    static constexpr int N = kTopK * T;
+    uint32_t at[N][kI / 2];         // rotated a per sorted position
+    float atsc[N][kI / kG];
+    float o[N][kFuCols];            // routed outputs of this workgroup's features
+    float z[T][kFuCols];            // shared expert outputs
     int fail;
 };
 
+template <int T>
 union FuWork {
-    FuGateUp gu;
-    FuDown dn;
+    FuGateUp<T> gu;
+    FuDown<T> dn;
 };
-
-// Cache policy of the a hand-off: device scope (sc1) plus the volatile bit,
-// which keeps the accesses in program order around the counter and barrier
-// (the compiler adds sc0: system scope, also coherent across the XCDs).
-constexpr int kHandOff = 16 | (int)(1u << 31);
 
 // Empty asm that "rewrites" a register quad: the mask conversion of codes that
 // are reused for several tokens is then redone per token instead of being
@@ -101,52 +108,154 @@ __device__ __forceinline__ void refresh(uint4 &v) {
     asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
 }
 
-// One instance per token count: every loop over tokens, assignments and
-// down slots has a compile-time trip count, so the loads of a phase are all
-// issued before the first of them is waited for.
+__device__ __forceinline__ float4 bf16x4_lo(uint4 q) {
+    return make_float4(bf16lo(q.x), bf16hi(q.x), bf16lo(q.y), bf16hi(q.y));
+}
+__device__ __forceinline__ float4 bf16x4_hi(uint4 q) {
+    return make_float4(bf16lo(q.z), bf16hi(q.z), bf16lo(q.w), bf16hi(q.w));
+}
+
+// Poll one replica of a completion counter until it reaches `target` or the
+// time bound passes; returns whether it was reached.
+__device__ __forceinline__ bool wait_count(const int *counter, int target) {
+    const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+    for (;;) {
+        if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return true;
+        if (__builtin_amdgcn_s_memrealtime() - t_start > kFuWaitTicks) return false;
+        __builtin_amdgcn_s_sleep(8);
+    }
+}
+
+// Add 1 to every replica of a counter (lanes 0..15 of the calling wave).
+__device__ __forceinline__ void count_done(int *counters, int lane) {
+    if (lane < kFusedCounters)
+        __hip_atomic_fetch_add(counters + lane * kFusedCounterStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// One wave batch of gate/up codes: 2 row pairs, lane l owning K [32l, 32l+32).
+struct GuBatch {
+    uint4 g[kFuPairs], u[kFuPairs];
+    uint16_t sg[kFuPairs], su[kFuPairs];
+};
+
+// Row . x_t for every token, by one wave (lane l owns K [32l, 32l+32) of the
+// bf16 row); token t's sum ends on lanes 8t..8t+7 (all of them).
+template <int T>
+__device__ __forceinline__ float row_dot_tokens(const uint16_t *row, const uint16_t *x, int lane) {
+    const __amdgpu_buffer_rsrc_t rb = make_buf(row, kH * 2);
+    const __amdgpu_buffer_rsrc_t xb = make_buf(x, T * kH * 2);
+    uint4 w[4], xv[T][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = bload16_nt(rb, lane * 64 + 16 * i, 0);
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xv[t][i] = bload16(xb, lane * 64 + 16 * i, t * kH * 2);
+    float v[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        float acc = 0.0f;
+        if (t < T) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                acc = dot2b(xv[t][i].x, w[i].x, acc);
+                acc = dot2b(xv[t][i].y, w[i].y, acc);
+                acc = dot2b(xv[t][i].z, w[i].z, acc);
+                acc = dot2b(xv[t][i].w, w[i].w, acc);
+            }
+        }
+        v[t] = acc;
+    }
+    return transpose_reduce<8, kWave>(v);
+}
+
+// ---------------------------------------------------------------------------
+// Launch 1: what needs only x.  Workgroups of 2 waves: the first 128 compute
+// router logits (one row per wave; fp32 sums of exact bf16 products, NInfer
+// README of Flint, "What is inside": router rows widened exactly from bf16),
+// the other 1024 one column c of h each (wave 0 the gate row c, wave 1 the up
+// row c).  Workgroup 0 also clears the counters of the second launch.
+// ---------------------------------------------------------------------------
+constexpr int kRouterWgs = kE / 2;
+
+template <int T>
+__global__ __launch_bounds__(128) void k_router_shared_small(const uint16_t *__restrict__ x,
+                                                             const uint16_t *__restrict__ router_w,
+                                                             const float *__restrict__ bias,
+                                                             const uint16_t *__restrict__ shared_gu,
+                                                             float *__restrict__ logits, uint16_t *__restrict__ hs,
+                                                             int *__restrict__ counters) {
+    __shared__ float up[8];
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
+    if (blockIdx.x == 0 && threadIdx.x < kFusedCounters) counters[threadIdx.x * kFusedCounterStride] = 0;
+    const int t = lane >> 3;
+    if ((int)blockIdx.x < kRouterWgs) {
+        const int e = 2 * (int)blockIdx.x + wave;
+        const float sum = row_dot_tokens<T>(router_w + (size_t)e * kH, x, lane);
+        if ((lane & 7) == 0 && t < T) logits[(size_t)t * kE + e] = sum + (bias ? bias[e] : 0.0f);
+        return;
+    }
+    const int c = (int)blockIdx.x - kRouterWgs;
+    const float sum = row_dot_tokens<T>(shared_gu + (size_t)(wave * kIS + c) * kH, x, lane);
+    if (wave == 1 && (lane & 7) == 0) up[t] = sum;
+    __syncthreads();
+    if (wave == 0 && (lane & 7) == 0 && t < T) hs[(size_t)t * kIS + c] = f32_to_bf16(silu_f(sum) * up[t]);
+}
+
+// ---------------------------------------------------------------------------
+// Launch 2: everything else (one instance per token count, so that every loop
+// over tokens, assignments and down slots has a compile-time trip count and
+// the loads of a phase are all issued before the first of them is waited for).
+// ---------------------------------------------------------------------------
 template <int T>
 __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_fused(FusedDecodeArgs A) {
-    constexpr int N = kTopK * T;                       // assignments
-    constexpr int kSlots = (N + kFuWaves - 1) / kFuWaves;   // down experts per wave at most
-    __shared__ FuRouting R;
-    __shared__ FuWork U;
+    constexpr int N = kTopK * T;                              // assignments
+    constexpr int kSlots = (N + kFuWaves - 1) / kFuWaves;     // down experts (or positions) per wave at most
+    __shared__ FuRouting<T> R;
+    __shared__ FuWork<T> U;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
     const bool gu_role = blockIdx.x < kFuGuWgs;
-    const int c0 = ((int)blockIdx.x - kFuGuWgs) * kFuCols;   // down role: first output feature
 
-    // ---- work that depends on nothing: the loads of x (gate/up role), or
-    // the shared expert's down projection for this workgroup's features (down
-    // role): z[t][c0 + wave] = h_t . Wsd[c0 + wave], lane l owning K [16l, 16l+16)
+    // ---- work that depends on nothing: the loads of the logits and of x
+    // (gate/up role), or the shared down projection of this workgroup's
+    // features, z[t][c0 + wave] = h_t . Wsd[c0 + wave], lane l owning
+    // K [16l, 16l+16) (down role) ----
     float4 lv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (wave < T) lv = reinterpret_cast<const float4 *>(A.logits + (size_t)wave * kE)[lane];
-    uint4 xq[4];
+    constexpr int kRotTasks = (4 * T + kFuWaves - 1) / kFuWaves;   // x quarters per wave
+    uint4 xq[kRotTasks];
     if (gu_role) {
-        if (wave < T) {
-            const uint4 *xp = reinterpret_cast<const uint4 *>(A.x + (size_t)wave * kH + lane * 32);
+        // task k = (token k / 4, 512-wide quarter k % 4), dealt from the last wave down
 #pragma unroll
-            for (int i = 0; i < 4; ++i) xq[i] = xp[i];
+        for (int i = 0; i < kRotTasks; ++i) {
+            const int k = min(kFuWaves - 1 - wave + kFuWaves * i, 4 * T - 1);
+            xq[i] = reinterpret_cast<const uint4 *>(A.x + (size_t)(k >> 2) * kH + (k & 3) * 512)[lane];
         }
     } else {
+        const int c0 = ((int)blockIdx.x - kFuGuWgs) * kFuCols;
         const __amdgpu_buffer_rsrc_t wb = make_buf(A.shared_down + (size_t)(c0 + wave) * kIS, kIS * 2);
-        const uint4 w0 = bload16_nt(wb, lane * 32, 0), w1 = bload16_nt(wb, lane * 32 + 16, 0);
         const __amdgpu_buffer_rsrc_t hb = make_buf(A.hs, (uint32_t)(T * kIS * 2));
-        uint4 h[T][2];
+        const uint4 w0 = bload16_nt(wb, lane * 32, 0), w1 = bload16_nt(wb, lane * 32 + 16, 0);
+        uint4 hq[T][2];
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            h[t][0] = bload16(hb, lane * 32, t * kIS * 2);
-            h[t][1] = bload16(hb, lane * 32 + 16, t * kIS * 2);
+            hq[t][0] = bload16(hb, lane * 32, t * kIS * 2);
+            hq[t][1] = bload16(hb, lane * 32 + 16, t * kIS * 2);
         }
+        float v[8];
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const uint4 h0 = h[t][0], h1 = h[t][1];
+        for (int t = 0; t < 8; ++t) {
             float acc = 0.0f;
-            acc = dot2b(h0.x, w0.x, acc); acc = dot2b(h0.y, w0.y, acc);
-            acc = dot2b(h0.z, w0.z, acc); acc = dot2b(h0.w, w0.w, acc);
-            acc = dot2b(h1.x, w1.x, acc); acc = dot2b(h1.y, w1.y, acc);
-            acc = dot2b(h1.z, w1.z, acc); acc = dot2b(h1.w, w1.w, acc);
-            acc = wave_sum(acc);
-            if (lane == 0) U.dn.z[t][wave] = acc;
+            if (t < T) {
+                acc = dot2b(hq[t][0].x, w0.x, acc); acc = dot2b(hq[t][0].y, w0.y, acc);
+                acc = dot2b(hq[t][0].z, w0.z, acc); acc = dot2b(hq[t][0].w, w0.w, acc);
+                acc = dot2b(hq[t][1].x, w1.x, acc); acc = dot2b(hq[t][1].y, w1.y, acc);
+                acc = dot2b(hq[t][1].z, w1.z, acc); acc = dot2b(hq[t][1].w, w1.w, acc);
+            }
+            v[t] = acc;
         }
+        const float sum = transpose_reduce<8, kWave>(v);   // token lane / 8
+        if ((lane & 7) == 0 && (lane >> 3) < T) U.dn.z[lane >> 3][wave] = sum;
     }
 
     // ---- routing: wave t selects token t's six experts ----
@@ -160,9 +269,16 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
                 R.w[kTopK * t + j] = sel.w[j];
             }
         }
-        if (gu_role) {
-            const int sh = rotate_x_wave(xq, lane, &U.gu.xt[t][lane * 16]);
-            if (lane == 0) U.gu.xsc[t] = ldexpf(1.0f, sh);
+    }
+    if (gu_role) {
+        // rotated x, 4 blocks per task, beside the top-6 (waves from the first up)
+#pragma unroll
+        for (int i = 0; i < kRotTasks; ++i) {
+            const int k = kFuWaves - 1 - wave + kFuWaves * i;
+            if (k < 4 * T) {
+                const int t = k >> 2, qq = k & 3;
+                rotate_act_wave(bf16x4_lo(xq[i]), bf16x4_hi(xq[i]), lane, &U.gu.xt[t][qq * 256], &U.gu.xsc[t][qq * 4]);
+            }
         }
     }
     __syncthreads();
@@ -171,8 +287,9 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
     if (wave == 0) {
         const int ei = lane < N ? R.e[lane] : 0x7fffffff;
         int rank = 0;
+#pragma unroll
         for (int k = 0; k < N; ++k) {
-            const int ek = R.e[k];
+            const int ek = __builtin_amdgcn_readlane(ei, k);
             rank += (ek < ei) || (ek == ei && k < lane);
         }
         if (lane < N) {
@@ -233,59 +350,88 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
     }
 
     if (gu_role) {
-        // ---- gate/up: wave batches of 4 row pairs of one active expert ----
+        // ---- routed gate/up: wave batches of 2 row pairs of one active expert,
+        // dealt workgroup-major (consecutive batches on different CUs), the
+        // next batch's loads in flight while one is multiplied ----
         const int nb = n_act * kFuBatchesPerExpert;
         const rsrc_t act_buf = make_buf(A.act, (uint32_t)(N * kI * 4));
         const uint32_t cv = lane * 16, sv = (lane >> 2) * 2;
-        for (int b = (int)blockIdx.x * kFuWaves + wave; b < nb; b += kFuGuWgs * kFuWaves) {
-            const int ai = b / kFuBatchesPerExpert;
-            const int r0 = (b % kFuBatchesPerExpert) * kGuPairs;
-            const int e = uniform(R.act_e[ai]), p0 = uniform(R.act_begin[ai]), n = uniform(R.act_n[ai]);
+        constexpr int kStride = kFuGuWgs * kFuWaves;
+        auto load = [&](GuBatch &G, int bb) {
+            const int ai = bb / kFuBatchesPerExpert, r0 = (bb % kFuBatchesPerExpert) * kFuPairs;
+            const int e = uniform(R.act_e[ai]);
             const rsrc_t cg = make_buf(A.codes + (size_t)e * kCodeBytesPerExpert, kCodeBytesGu);
             const rsrc_t sp = make_buf(A.scales + (size_t)e * kScalesPerExpert, 2 * kScalesGu);
-            GuRows G;
 #pragma unroll
-            for (int i = 0; i < kGuPairs; ++i) gu_load_pair<false>(G, i, cg, sp, cv, sv, r0 + i);
+            for (int i = 0; i < kFuPairs; ++i) {
+                const int r = r0 + i;
+                G.g[i] = bload16_nt(cg, cv, r * (kH / 2));
+                G.u[i] = bload16_nt(cg, cv, kPlaneGateBytes + r * (kH / 2));
+                G.sg[i] = bload2_nt(sp, sv, 2 * r * (kH / kG));
+                G.su[i] = bload2_nt(sp, sv, 2 * (kScalesGate + r * (kH / kG)));
+            }
+        };
+        // a batch's products for every token of its expert (codes in G)
+        auto compute = [&](GuBatch &G, int bb) {
+            const int ai = bb / kFuBatchesPerExpert, r0 = (bb % kFuBatchesPerExpert) * kFuPairs;
+            const int p0 = uniform(R.act_begin[ai]), n = uniform(R.act_n[ai]);
             for (int k = 0; k < n; ++k) {
                 const int p = p0 + k;
                 const int t = R.perm[p] / kTopK;
 #pragma unroll
-                for (int i = 0; i < kGuPairs; ++i) {
+                for (int i = 0; i < kFuPairs; ++i) {
                     refresh(G.g[i]);
                     refresh(G.u[i]);
                 }
                 uint32_t xs[16];
                 const float off = load_operand32(&U.gu.xt[t][lane * 16], xs);
-                const float sc = U.gu.xsc[t];
-                float v[2 * kGuPairs];
+                const float xsc = U.gu.xsc[t][lane >> 2];
+                float v[2 * kFuPairs];
 #pragma unroll
-                for (int i = 0; i < kGuPairs; ++i) {
+                for (int i = 0; i < kFuPairs; ++i) {
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         Q4 q[4];
                         convert16(h ? G.u[i] : G.g[i], q);
-                        v[2 * i + h] = dot_slice(q, xs, -off) * bf16_to_f32(h ? G.su[i] : G.sg[i]);
+                        v[2 * i + h] = dot_slice(q, xs, -off) * (bf16_to_f32(h ? G.su[i] : G.sg[i]) * xsc);
                     }
                 }
-                // value 2i (gate row r0+i) and 2i+1 (its up row) end on lanes 8*(2i)..
-                const float red = transpose_reduce<2 * kGuPairs, kWave>(v);
-                const float other = shfl_xor_f(red, 8);
-                const int vi = lane >> 3;
-                if ((vi & 1) == 0 && (lane & 7) == 0)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(silu_f(red * sc) * (other * sc)), act_buf,
-                                                          4 * (p * kI + r0 + (vi >> 1)), 0, kHandOff);
+                // value 2i (gate row r0+i) ends on lanes 32i..32i+15, its up row on the next 16
+                const float red = transpose_reduce<2 * kFuPairs, kWave>(v);
+                const float other = shfl_xor_f(red, 16);
+                if ((lane & 31) == 0)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(silu_f(red) * other), act_buf,
+                                                          4 * (p * kI + r0 + (lane >> 5)), 0, kHandOff);
+            }
+        };
+        // two register sets in turn (no copies, so the loads of one stay in
+        // flight while the other is multiplied); past the end a set re-reads
+        // the wave's last batch (in bounds, unused)
+        int b = wave * kFuGuWgs + (int)blockIdx.x;
+        if (b < nb) {
+            GuBatch G0, G1;
+            load(G0, b);
+            for (;;) {
+                load(G1, min(b + kStride, nb - 1));
+                compute(G0, b);
+                b += kStride;
+                if (b >= nb) break;
+                load(G0, min(b + kStride, nb - 1));
+                compute(G1, b);
+                b += kStride;
+                if (b >= nb) break;
             }
         }
         // count this workgroup done once every wave's stores of a are complete
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (tid < kFusedCounters)
-            __hip_atomic_fetch_add(A.counters + tid * kFusedCounterStride, 1, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
+        if (wave == 0) count_done(A.counters, lane);
         return;
     }
 
     // ---- down role ----
+    const int c0 = ((int)blockIdx.x - kFuGuWgs) * kFuCols;
+    const int replica = ((int)blockIdx.x % kFusedCounters) * kFusedCounterStride;
     // down codes of this workgroup's 8 features for every active expert this
     // wave handles (experts wave, wave + 8, ...): lane l takes row l / 8 and
     // K [64 (l % 8), 64 (l % 8) + 64), inside block (l % 8) / 2
@@ -308,34 +454,30 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
     }
 
     // wait until every gate/up workgroup is done (bounded)
-    if (tid == 0) {
-        const int *counter = A.counters + (blockIdx.x % kFusedCounters) * kFusedCounterStride;
-        const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
-        int ok = 0;
-        for (;;) {
-            if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= kFuGuWgs) {
-                ok = 1;
-                break;
-            }
-            if (__builtin_amdgcn_s_memrealtime() - t_start > kFuWaitTicks) break;
-            __builtin_amdgcn_s_sleep(8);
-        }
-        U.dn.fail = !ok;
-    }
+    if (tid == 0) U.dn.fail = !wait_count(A.counters + replica, kFuGuWgs);
     __syncthreads();
     if (U.dn.fail) {
         if (tid < T * kFuCols) A.y[(size_t)(tid / kFuCols) * kH + c0 + tid % kFuCols] = 0x7fc0;   // NaN
         return;
     }
 
-    // rotated a of every assignment (wave per sorted position)
-    const rsrc_t act_buf = make_buf(A.act, (uint32_t)(N * kI * 4));
+    // rotated a of every assignment (wave per sorted position), all loads first
+    {
+        const rsrc_t act_buf = make_buf(A.act, (uint32_t)(N * kI * 4));
+        u32x4_t a[kSlots][2];
 #pragma unroll
-    for (int p = wave; p < N; p += kFuWaves) {
-        const u32x4_t a0 = __builtin_amdgcn_raw_buffer_load_b128(act_buf, 4 * (p * kI + lane * 8), 0, kHandOff);
-        const u32x4_t a1 = __builtin_amdgcn_raw_buffer_load_b128(act_buf, 4 * (p * kI + lane * 8 + 4), 0, kHandOff);
-        rotate_act_wave(__builtin_bit_cast(float4, a0), __builtin_bit_cast(float4, a1), lane, &U.dn.at[p][0],
-                        &U.dn.atsc[p][0]);
+        for (int i = 0; i < kSlots; ++i) {
+            const int p = min(wave + kFuWaves * i, N - 1);
+            a[i][0] = __builtin_amdgcn_raw_buffer_load_b128(act_buf, 4 * (p * kI + lane * 8), 0, kHandOff);
+            a[i][1] = __builtin_amdgcn_raw_buffer_load_b128(act_buf, 4 * (p * kI + lane * 8 + 4), 0, kHandOff);
+        }
+#pragma unroll
+        for (int i = 0; i < kSlots; ++i) {
+            const int p = wave + kFuWaves * i;
+            if (p < N)
+                rotate_act_wave(__builtin_bit_cast(float4, a[i][0]), __builtin_bit_cast(float4, a[i][1]), lane,
+                                &U.dn.at[p][0], &U.dn.atsc[p][0]);
+        }
     }
     __syncthreads();
 
@@ -382,18 +524,30 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
 
 }  // namespace
 
-void launch_decode_fused(const FusedDecodeArgs &args, hipStream_t s) {
-    const dim3 grid(kFuGuWgs + kFuDnWgs), block(kFuThreads);
-    switch (args.T) {
-    case 1: hipLaunchKernelGGL(k_decode_fused<1>, grid, block, 0, s, args); break;
-    case 2: hipLaunchKernelGGL(k_decode_fused<2>, grid, block, 0, s, args); break;
-    case 3: hipLaunchKernelGGL(k_decode_fused<3>, grid, block, 0, s, args); break;
-    case 4: hipLaunchKernelGGL(k_decode_fused<4>, grid, block, 0, s, args); break;
-    case 5: hipLaunchKernelGGL(k_decode_fused<5>, grid, block, 0, s, args); break;
-    case 6: hipLaunchKernelGGL(k_decode_fused<6>, grid, block, 0, s, args); break;
-    case 7: hipLaunchKernelGGL(k_decode_fused<7>, grid, block, 0, s, args); break;
-    default: hipLaunchKernelGGL(k_decode_fused<8>, grid, block, 0, s, args); break;
+#define MOE_FUSED_DISPATCH(KERNEL, ...)                                          \
+    switch (T) {                                                                 \
+    case 1: hipLaunchKernelGGL(KERNEL<1>, __VA_ARGS__); break;                   \
+    case 2: hipLaunchKernelGGL(KERNEL<2>, __VA_ARGS__); break;                   \
+    case 3: hipLaunchKernelGGL(KERNEL<3>, __VA_ARGS__); break;                   \
+    case 4: hipLaunchKernelGGL(KERNEL<4>, __VA_ARGS__); break;                   \
+    case 5: hipLaunchKernelGGL(KERNEL<5>, __VA_ARGS__); break;                   \
+    case 6: hipLaunchKernelGGL(KERNEL<6>, __VA_ARGS__); break;                   \
+    case 7: hipLaunchKernelGGL(KERNEL<7>, __VA_ARGS__); break;                   \
+    case 8: hipLaunchKernelGGL(KERNEL<8>, __VA_ARGS__); break;                   \
+    default: break;                                                              \
     }
+
+void launch_router_shared_small(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
+                                const uint16_t *shared_w, float *logits, uint16_t *hs, int *counters, hipStream_t s) {
+    MOE_FUSED_DISPATCH(k_router_shared_small, dim3(kRouterWgs + kIS), dim3(128), 0, s, x, router_w, bias, shared_w,
+                       logits, hs, counters)
 }
+
+void launch_decode_fused(const FusedDecodeArgs &args, hipStream_t s) {
+    const int T = args.T;
+    MOE_FUSED_DISPATCH(k_decode_fused, dim3(kFuGuWgs + kFuDnWgs), dim3(kFuThreads), 0, s, args)
+}
+
+#undef MOE_FUSED_DISPATCH
 
 }  // namespace moe_w4

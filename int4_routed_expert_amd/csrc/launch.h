@@ -8,26 +8,25 @@
 namespace moe_w4 {
 
 // One launch: router logits[T][256] = x R^T (+ bias), and the shared expert's
-// h[T][1024] = bf16(silu(x Wsg^T) * (x Wsu^T)).  If `clear` is not null, the
-// launch also sets clear[i * kFusedCounterStride] to zero for i < kFusedCounters
-// (the counters of the fused decode launch that follows it).
+// h[T][1024] = bf16(silu(x Wsg^T) * (x Wsu^T)).
 void launch_router_and_shared_gateup(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
-                                     float *logits, const uint16_t *shared_w, uint16_t *hs, int *clear,
-                                     hipStream_t s);
+                                     float *logits, const uint16_t *shared_w, uint16_t *hs, hipStream_t s);
 
-// Decode sizes: from the logits on, the whole layer in one launch (top-6, sort,
-// rotation of x, routed gate/up, rotation of a, routed and shared down,
-// combine).  `counters` must be zero at launch (the router launch clears them).
+// Decode sizes (1..kFusedMaxTokens tokens): one launch for what needs only x
+// (router logits and the shared expert's h; it also clears the counters of the
+// launch after it), then the whole rest of the layer in one launch (top-6,
+// sort, rotation of x, routed gate/up, rotation of a, routed and shared down,
+// combine).
 constexpr int kFusedMaxTokens = 8;
-constexpr int kFusedCounters = 16;        // replicas of the completion counter ...
-constexpr int kFusedCounterStride = 64;   // ... one per 256-byte line of `counters`
+constexpr int kFusedCounters = 16;        // replicas of the completion counter,
+constexpr int kFusedCounterStride = 64;   // one per 256 bytes of `counters`
 struct FusedDecodeArgs {
     const uint16_t *x;
     const float *logits;
     const uint8_t *codes;
     const uint16_t *scales;
     const uint16_t *shared_down;   // [2048][1024] bf16
-    const uint16_t *hs;            // [T][1024] bf16
+    const uint16_t *hs;            // [T][1024] bf16, from the first launch
     int T;
     int *topk_idx;
     float *topk_w;
@@ -40,8 +39,10 @@ struct FusedDecodeArgs {
     int *n_chunks;
     float *act;                    // [6T][512] fp32 scratch, sorted-position order
     uint16_t *y;
-    int *counters;
+    int *counters;                 // 4096 bytes; zero at launch (the first launch clears them)
 };
+void launch_router_shared_small(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
+                                const uint16_t *shared_w, float *logits, uint16_t *hs, int *counters, hipStream_t s);
 void launch_decode_fused(const FusedDecodeArgs &args, hipStream_t s);
 
 // Per token: top-6 of the logits, renormalised sigmoid weights, and the

@@ -53,7 +53,6 @@ struct SkinnyJob {
 
 struct SkinnyJobs {
     SkinnyJob job[2];
-    int *clear;   // if set, workgroup 0 zeroes the fused decode counters here
 };
 
 __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
@@ -89,8 +88,6 @@ __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__
     J.pos = second ? j1.pos : j0.pos;
     J.o = second ? j1.o : j0.o;
     const int blk = second ? (int)blockIdx.x - j0.n_blocks : (int)blockIdx.x;
-    if (jobs.clear && blockIdx.x == 0 && threadIdx.x < kFusedCounters)
-        jobs.clear[threadIdx.x * kFusedCounterStride] = 0;
     const int epi = J.epi;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int r = lane & 15, g = lane >> 4;
@@ -198,10 +195,8 @@ static void launch_skinny_k(const uint16_t *A, int M, const SkinnyJobs &jobs, hi
 static SkinnyJob no_job() { return SkinnyJob{nullptr, 0, 0, 0, kEpiStoreF32, nullptr, nullptr, 0, nullptr, nullptr, nullptr}; }
 
 void launch_router_and_shared_gateup(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
-                                     float *logits, const uint16_t *shared_w, uint16_t *hs, int *clear,
-                                     hipStream_t s) {
+                                     float *logits, const uint16_t *shared_w, uint16_t *hs, hipStream_t s) {
     SkinnyJobs jobs;
-    jobs.clear = clear;
     jobs.job[0] = SkinnyJob{router_w, kE, 0, kE / 16, kEpiStoreF32, bias, logits, kE, nullptr, nullptr, nullptr};
     // columns: 16-wide tiles of (8 gate rows, the same 8 up rows); up rows start at row 1024
     jobs.job[1] = SkinnyJob{shared_w, 2 * kIS, kIS, 2 * kIS / 16, kEpiSwiglu, nullptr, hs, kIS, nullptr, nullptr, nullptr};
@@ -211,7 +206,6 @@ void launch_router_and_shared_gateup(const uint16_t *x, int T, const uint16_t *r
 void launch_shared_down_combine(const uint16_t *shared_w, const uint16_t *hs, int T, const float *topk_w,
                                 const int *pos, const float *o, uint16_t *y, hipStream_t s) {
     SkinnyJobs jobs;
-    jobs.clear = nullptr;
     jobs.job[0] = SkinnyJob{shared_w + 2 * kSharedGateElems, kH, 0, kH / 8, kEpiCombine, nullptr, y, kH, topk_w, pos, o};
     jobs.job[1] = no_job();
     launch_skinny_k<kIS / (128 * 8), 8>(hs, T, jobs, s);

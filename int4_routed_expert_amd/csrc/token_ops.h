@@ -98,33 +98,52 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
+// (key, index) order of the selection: larger key first, equal keys by the
+// lower expert index.
+__device__ __forceinline__ bool ahead(uint32_t ka, int ia, uint32_t kb, int ib) {
+    return ka > kb || (ka == kb && ia < ib);
+}
+
 __device__ __forceinline__ Top6 top6_wave(float4 lv, int lane) {
-    // a taken key becomes 0, below the key of every non-NaN logit
-    uint32_t key[4] = {order_key(lv.x), order_key(lv.y), order_key(lv.z), order_key(lv.w)};
+    // each lane sorts its 4 (key, expert) pairs (a 5-comparator network on the
+    // total order above), then six rounds take the largest head over the wave
+    uint32_t k[4] = {order_key(lv.x), order_key(lv.y), order_key(lv.z), order_key(lv.w)};
+    int ix[4] = {4 * lane, 4 * lane + 1, 4 * lane + 2, 4 * lane + 3};
+    auto cswap = [&](int a, int b) {
+        if (ahead(k[b], ix[b], k[a], ix[a])) {
+            const uint32_t tk = k[a]; k[a] = k[b]; k[b] = tk;
+            const int ti = ix[a]; ix[a] = ix[b]; ix[b] = ti;
+        }
+    };
+    cswap(0, 1); cswap(2, 3); cswap(0, 2); cswap(1, 3); cswap(1, 2);
     Top6 r;
-    float sel_l[kTopK];
+    uint32_t sel_k[kTopK];
+    int head = 0;   // entries of this lane's list already taken
 #pragma unroll
     for (int j = 0; j < kTopK; ++j) {
-        const uint32_t K = wave_max_u32(max(max(key[0], key[1]), max(key[2], key[3])));
-        // the lowest expert index holding K: lowest lane, then lowest slot in it
-        const int here = key[0] == K ? 0 : key[1] == K ? 1 : key[2] == K ? 2 : key[3] == K ? 3 : 4;
-        const int L = (int)__builtin_ctzll(__ballot(here < 4));
-        const int i = __builtin_amdgcn_readlane(here, L);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (lane == L && q == i) key[q] = 0;
-        r.e[j] = 4 * L + i;
-        sel_l[j] = key_value(K);
+        // an exhausted list offers 0, below the key of every non-NaN logit
+        const uint32_t hk = head == 0 ? k[0] : head == 1 ? k[1] : head == 2 ? k[2] : head == 3 ? k[3] : 0u;
+        const int hi = head == 0 ? ix[0] : head == 1 ? ix[1] : head == 2 ? ix[2] : ix[3];
+        const uint32_t K = wave_max_u32(hk);
+        // among equal heads the lowest lane holds the lowest expert index
+        const int L = (int)__builtin_ctzll(__ballot(hk == K));
+        r.e[j] = __builtin_amdgcn_readlane(hi, L);
+        sel_k[j] = K;
+        if (lane == L) ++head;
     }
+    // sigmoids side by side (lane j < 6), summed in slot order
+    uint32_t mine = sel_k[0];
+#pragma unroll
+    for (int j = 1; j < kTopK; ++j)
+        if (lane == j) mine = sel_k[j];
+    const float sig = 1.0f / (1.0f + expf(-key_value(mine)));
     float ssum = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kTopK; ++j) {
-        r.w[j] = 1.0f / (1.0f + expf(-sel_l[j]));
-        ssum += r.w[j];
-    }
+    for (int j = 0; j < kTopK; ++j) ssum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sig), j));
     const float denom = fmaxf(ssum, 6.103515625e-05f);   // 2^-14
+    const float w = sig / denom;
 #pragma unroll
-    for (int j = 0; j < kTopK; ++j) r.w[j] /= denom;
+    for (int j = 0; j < kTopK; ++j) r.w[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));
     return r;
 }
 
