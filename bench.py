@@ -52,20 +52,47 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device-to-device copy of known size (10 x 256 MiB)")
+    ap.add_argument("--traffic-lines", nargs=5,
+                    metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV", "CAL_FETCH_CSV", "CAL_WRITE_CSV"),
+                    help="print profiles/hbm_traffic.txt lines for the workload's kernels from rocprofv3 "
+                         "FETCH_SIZE / WRITE_SIZE runs of it and of --copy-calibration")
     ap.add_argument("--pmc-summary", nargs="+", metavar="CSV",
                     help="print per-kernel mean counter values of rocprofv3 counter_collection CSVs")
     return ap.parse_args()
 
 
-# stage -> (kernel name prefix, sources that define it) for the HBM-traffic record
-STAGE_KERNELS = {
+# stage -> (kernel name prefix, sources that define it) for the HBM-traffic
+# record, per launch sequence (1-8 tokens: two launches; 9-127: GEMVs;
+# from 128: MFMA tiles)
+FUSED_MAX_TOKENS = 8
+GROUPED_MIN_TOKENS = 128
+STAGE_KERNELS_FUSED = {
+    "router_shared_gateup": ("k_router_shared_small", ["decode_fused.hip", "gemv_ops.h", "token_ops.h"]),
+    "routed_gateup": ("k_decode_fused", ["decode_fused.hip", "gemv_ops.h", "token_ops.h"]),
+}
+STAGE_KERNELS_GEMV = {
     "router_shared_gateup": ("k_skinny", ["skinny_mfma.hip"]),
-    "topk_sort": ("k_topk_rotate", ["router.hip"]),
-    "routed_gateup": ("k_gateup_dec", ["experts_gemv.hip"]),
-    "rotate_act": ("k_rotate_act", ["experts_gemv.hip"]),
-    "routed_down": ("k_down_dec", ["experts_gemv.hip"]),
+    "topk_sort": ("k_topk_rotate", ["router.hip", "token_ops.h"]),
+    "routed_gateup": ("k_gateup_dec", ["experts_gemv.hip", "gemv_ops.h"]),
+    "rotate_act": ("k_rotate_act", ["experts_gemv.hip", "gemv_ops.h"]),
+    "routed_down": ("k_down_dec", ["experts_gemv.hip", "gemv_ops.h"]),
     "shared_down_combine": ("k_skinny", ["skinny_mfma.hip"]),
 }
+STAGE_KERNELS_GROUPED = {
+    "router_shared_gateup": ("k_dense_mfma", ["dense_mfma.hip"]),
+    "topk_sort": ("k_topk_rotate", ["router.hip", "token_ops.h"]),
+    "routed_gateup": ("k_gateup_mfma", ["grouped_mfma.hip"]),
+    "routed_down": ("k_down_mfma", ["grouped_mfma.hip"]),
+    "shared_down_combine": ("k_dense_mfma", ["dense_mfma.hip"]),
+}
+
+
+def stage_kernels(T):
+    if T <= FUSED_MAX_TOKENS:
+        return STAGE_KERNELS_FUSED
+    return STAGE_KERNELS_GROUPED if T >= GROUPED_MIN_TOKENS else STAGE_KERNELS_GEMV
+
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "int4_routed_expert_amd", "csrc")
 
@@ -81,10 +108,10 @@ def sources_digest(files):
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(workload, stage):
+def recorded_traffic(workload, stage, T):
     """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
     (profiles/hbm_traffic.txt), or None if absent or the kernel has changed."""
-    kern, files = STAGE_KERNELS.get(stage, (None, None))
+    kern, files = stage_kernels(T).get(stage, (None, None))
     path = os.path.join(HERE, "profiles", "hbm_traffic.txt")
     if kern is None or not os.path.exists(path):
         return None
@@ -124,6 +151,36 @@ def pmc_summary(paths):
         print(f"{name[:48]:48s} {n:10d}  {vals}")
 
 
+def counter_means(path):
+    """kernel name (without namespaces and arguments) -> mean counter value (KiB per dispatch)."""
+    import csv
+    import collections
+    agg = collections.defaultdict(list)
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "").split("::")[-1]
+            agg[name].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in agg.items()}
+
+
+def traffic_lines(workload, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
+    """Record lines: counters scaled by what they read for a plain copy of known size."""
+    import synth
+    T = synth.CONFIGS[workload]["T"]
+    copy_kib = 256 * 1024   # one calibration copy: 256 MiB read and written
+    ffac = copy_kib / counter_means(cal_fetch_csv)["__amd_rocclr_copyBuffer"]
+    wfac = copy_kib / counter_means(cal_write_csv)["__amd_rocclr_copyBuffer"]
+    fetch, write = counter_means(fetch_csv), counter_means(write_csv)
+    print(f"# {workload}: FETCH_SIZE x {ffac:.5f}, WRITE_SIZE x {wfac:.5f}")
+    seen = set()
+    for stage, (kern, files) in stage_kernels(T).items():
+        for name in sorted(fetch):
+            if name.startswith(kern) and name not in seen and name in write:
+                seen.add(name)
+                fb, wb = fetch[name] * 1024 * ffac, write[name] * 1024 * wfac
+                print(f"{workload} {kern} {fb:.0f} {wb:.0f} {fb + wb:.0f} {sources_digest(files)}")
+
+
 def cpu_baseline(cfg, T, x_bits, bias, budget_s):
     """The CPU oracle as it stands, on a bounded sample of the same workload."""
     import synth
@@ -160,6 +217,9 @@ def main():
     a = parse()
     if a.pmc_summary:
         pmc_summary(a.pmc_summary)
+        return
+    if a.traffic_lines:
+        traffic_lines(*a.traffic_lines)
         return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported (the layer needs no "
@@ -315,20 +375,36 @@ def main():
         "routed_down": n_touched * EXPERT_D_BYTES + T * 6 * 2048 * 4,
         "shared_down_combine": 1024 * 2048 * 2 + T * 1024 * 2 + T * 6 * 2048 * 4 + act,
     }
-    if T <= m.FUSED_MAX_TOKENS:
+    if T <= FUSED_MAX_TOKENS:
         # one launch after the router runs the rest of the layer (its time is
         # recorded under routed_gateup; the later stages are empty)
         stage_bytes["routed_gateup"] = (n_touched * EXPERT_BYTES + 1024 * 2048 * 2 + T * 256 * 4 + act
                                         + T * 1024 * 2 + act)
     dom_bytes = stage_bytes.get(dom, 0.0)
     achieved = dom_bytes / (stage[dom] * 1e-3) / 1e9
+    # from 128 tokens on the routed experts and the shared expert run as MFMA
+    # contractions: their roofline is the fp16/bf16 MFMA peak
+    stage_flops = {
+        "router_shared_gateup": T * (256 + 2 * 1024) * 2048 * 2,
+        "routed_gateup": T * 6 * 2 * 512 * 2048 * 2,
+        "routed_down": T * 6 * 2048 * 512 * 2,
+        "shared_down_combine": T * 1024 * 2048 * 2,
+    }
     result["value"] = T / (ms / 1e3)
     result["config"] = {"workload": f"{a.config}: one MoE layer, T={T}, x seed {cfg['x_seed']}, weights seed "
                                     f"{cfg['w_seed']}" + (", +3.0 bias on 26 experts (seed 3)" if bias is not None else ""),
                         "T": T, "layers_rotated": n_layers, "touched_experts": n_touched}
-    result["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                          "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(a.config, dom),
-                          "algorithmic_bytes": dom_bytes, "kernel_us": stage[dom] * 1e3}
+    if T >= GROUPED_MIN_TOKENS:
+        dom_flops = stage_flops.get(dom, 0.0)
+        tf = dom_flops / (stage[dom] * 1e-3) / 1e12
+        result["roofline"] = {"bound": "mfma", "kernel": dom, "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
+                              "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
+                              "traffic": recorded_traffic(a.config, dom, T), "algorithmic_flops": dom_flops,
+                              "algorithmic_bytes": dom_bytes, "kernel_us": stage[dom] * 1e3}
+    else:
+        result["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                              "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(a.config, dom, T),
+                              "algorithmic_bytes": dom_bytes, "kernel_us": stage[dom] * 1e3}
     result["layer"] = {"algorithmic_bytes": layer_bytes, "hbm_gbs": layer_bytes / (ms * 1e-3) / 1e9,
                        "hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                        "tflops": flops / (ms * 1e-3) / 1e12,
