@@ -79,11 +79,11 @@ STAGE_KERNELS_GEMV = {
     "shared_down_combine": ("k_skinny", ["skinny_mfma.hip"]),
 }
 STAGE_KERNELS_GROUPED = {
-    "router_shared_gateup": ("k_dense_mfma", ["dense_mfma.hip"]),
+    "router_shared_gateup": ("k_dense_mfma<2048>", ["dense_mfma.hip"]),
     "topk_sort": ("k_topk_rotate", ["router.hip", "token_ops.h"]),
     "routed_gateup": ("k_gateup_mfma", ["grouped_mfma.hip"]),
     "routed_down": ("k_down_mfma", ["grouped_mfma.hip"]),
-    "shared_down_combine": ("k_dense_mfma", ["dense_mfma.hip"]),
+    "shared_down_combine": ("k_dense_mfma<1024>", ["dense_mfma.hip"]),
 }
 
 
@@ -142,7 +142,7 @@ def pmc_summary(paths):
     for path in paths:
         with open(path) as fh:
             for r in csv.DictReader(fh):
-                name = r["Kernel_Name"].split("(")[0].replace("void ", "")
+                name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
                 agg[name][r["Counter_Name"]].append(float(r["Counter_Value"]))
     print(f"{'kernel':48s} {'dispatches':>10s}  counter means (per dispatch)")
     for name, d in sorted(agg.items()):
@@ -158,7 +158,8 @@ def counter_means(path):
     agg = collections.defaultdict(list)
     with open(path) as fh:
         for r in csv.DictReader(fh):
-            name = r["Kernel_Name"].split("(")[0].replace("void ", "").split("::")[-1]
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "").split("(")[0]
+            name = name.replace("void ", "").split("::")[-1]
             agg[name].append(float(r["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in agg.items()}
 
