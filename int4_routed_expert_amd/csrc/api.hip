@@ -124,6 +124,7 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     int *n_chunks = ws_at<int>(ws, L.n_chunks);
     const bool grouped = T >= kPrefillMinTokens;
     const bool fused = T <= kFusedMaxTokens;
+    const bool small_route = !grouped && T <= kRouteSmallMaxTokens;
     int *counters = ws_at<int>(ws, L.sync);
 
     int stage = 0;
@@ -182,10 +183,18 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     if (grouped)
         MOE_STEP(launch_router_and_shared_gateup_dense(x, T, router_w, bias, logits, shared_w, hs, s));
     else
-        MOE_STEP(launch_router_and_shared_gateup(x, T, router_w, bias, logits, shared_w, hs, s));
+        // up to kRouteSmallMaxTokens tokens this launch also rotates x, and the
+        // routing is one workgroup
+        MOE_STEP(launch_router_and_shared_gateup(x, T, router_w, bias, logits, shared_w, hs,
+                                                 small_route ? xt : nullptr, xt_scale, s));
     MOE_MARK();
-    MOE_STEP(launch_topk_rotate(logits, x, T, topk_idx, topk_w, xt, xt_scale, s));
-    MOE_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, s));
+    if (small_route) {
+        MOE_STEP(launch_route_small(logits, T, topk_idx, topk_w, offsets, perm, pos, n_active, active, chunks,
+                                    n_chunks, s));
+    } else {
+        MOE_STEP(launch_topk_rotate(logits, x, T, topk_idx, topk_w, xt, xt_scale, s));
+        MOE_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, s));
+    }
     MOE_MARK();
     if (grouped) {
         // gate/up also rotates a: the rotate_act stage is empty on this path

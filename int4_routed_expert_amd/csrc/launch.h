@@ -8,9 +8,11 @@
 namespace moe_w4 {
 
 // One launch: router logits[T][256] = x R^T (+ bias), and the shared expert's
-// h[T][1024] = bf16(silu(x Wsg^T) * (x Wsu^T)).
+// h[T][1024] = bf16(silu(x Wsg^T) * (x Wsu^T)); if xt is not null, also the
+// rotated fp16 copy of x (xt, xt_scale, as launch_topk_rotate writes them).
 void launch_router_and_shared_gateup(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
-                                     float *logits, const uint16_t *shared_w, uint16_t *hs, hipStream_t s);
+                                     float *logits, const uint16_t *shared_w, uint16_t *hs, uint32_t *xt,
+                                     float *xt_scale, hipStream_t s);
 
 // Decode sizes (1..kFusedMaxTokens tokens): one launch for what needs only x
 // (router logits and the shared expert's h; it also clears the counters of the
@@ -56,6 +58,12 @@ void launch_topk_rotate(const float *logits, const uint16_t *x, int T, int *topk
 // (<= 96), 0} covering every expert's assignments; *n_chunks of them.
 void launch_sort(const int *topk_idx, int T, int *offsets, int *perm, int *pos, int *n_active,
                  int *slots, int *chunks, int *n_chunks, hipStream_t s);
+// Top-6 and the stable sort in one workgroup (16 waves, one token per wave at
+// a time; the sort ranks the <= 288 assignments in LDS), for up to
+// kRouteSmallMaxTokens tokens whose rotated x is written elsewhere.
+constexpr int kRouteSmallMaxTokens = 48;
+void launch_route_small(const float *logits, int T, int *topk_idx, float *topk_w, int *offsets, int *perm,
+                        int *pos, int *n_active, int *slots, int *chunks, int *n_chunks, hipStream_t s);
 
 // Routed experts, GEMV form (few tokens per expert), driven by the slot records.
 void launch_gateup_gemv(const uint8_t *codes, const uint16_t *scales, const uint32_t *xt,

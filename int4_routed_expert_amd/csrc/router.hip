@@ -203,6 +203,158 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Top-6 and sort of a few tokens (up to kRouteSmallMaxTokens) in one
+// workgroup of 16 waves: wave w selects tokens w, w + 16, ... (all their logit
+// loads issued first); then a stable counting sort of the <= 288 assignments
+// in LDS (the algorithm of k_sort, with the chosen experts never leaving the
+// workgroup).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_route_small(const float *__restrict__ logits, int T,
+                                                      int *__restrict__ topk_idx, float *__restrict__ topk_w,
+                                                      int *__restrict__ offsets, int *__restrict__ perm,
+                                                      int *__restrict__ pos, int *__restrict__ n_active,
+                                                      int *__restrict__ slots, int4 *__restrict__ chunks,
+                                                      int *__restrict__ n_chunks) {
+    constexpr int kPerWave = (kRouteSmallMaxTokens + kSortWaves - 1) / kSortWaves;
+    constexpr int kMaxChunks = (kTopK * kRouteSmallMaxTokens + 63) / 64;
+    __shared__ int sel[kTopK * kRouteSmallMaxTokens];     // expert of assignment a
+    __shared__ int sperm[kTopK * kRouteSmallMaxTokens];   // assignment at sorted position p
+    __shared__ int cnt[kMaxChunks][kE];                   // per chunk: count, then base of each expert
+    __shared__ int tot[kE];
+    __shared__ int offs[kE + 1];
+    __shared__ int act_rank[kE];                          // active experts below e (-1: e not active)
+    __shared__ int act_list[kE];                          // active expert of each slot
+    __shared__ int n_act_s;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int N = kTopK * T;
+    for (int i = tid; i < kMaxChunks * kE; i += blockDim.x) (&cnt[0][0])[i] = 0;
+
+    float4 lv[kPerWave];
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+        const int t = min(wave + kSortWaves * i, T - 1);   // past the end: token T-1 again (unused)
+        lv[i] = reinterpret_cast<const float4 *>(logits + (size_t)t * kE)[lane];
+    }
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+        const int t = wave + kSortWaves * i;
+        if (t < T) {
+            const Top6 r = top6_wave(lv[i], lane);
+#pragma unroll
+            for (int j = 0; j < kTopK; ++j) {
+                if (lane == j) {
+                    topk_idx[(size_t)t * kTopK + j] = r.e[j];
+                    topk_w[(size_t)t * kTopK + j] = r.w[j];
+                    sel[kTopK * t + j] = r.e[j];
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // stable counting sort: chunk c = assignments [64c, 64c + 64) belongs to
+    // wave c; equal experts inside a chunk are ranked with ballots, and the
+    // counts of earlier chunks and of smaller experts give the base
+    const int n_chunks_a = (N + 63) >> 6;
+    int e_mine = -1, within = 0;
+    if (wave < n_chunks_a) {
+        const int a = 64 * wave + lane;
+        const bool valid = a < N;
+        e_mine = valid ? sel[a] : 0;
+        uint64_t same = __ballot(valid);
+#pragma unroll
+        for (int bit = 0; bit < 8; ++bit) {
+            const uint64_t bal = __ballot((e_mine >> bit) & 1);
+            same &= ((e_mine >> bit) & 1) ? bal : ~bal;
+        }
+        const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+        within = __popcll(same & below);
+        // the lowest lane of each group of equal experts records the group size
+        if (valid && (same & below) == 0) cnt[wave][e_mine] = __popcll(same);
+        if (!valid) e_mine = -1;
+    }
+    __syncthreads();
+    // per expert: base of each chunk, total (thread e < 256)
+    if (tid < kE) {
+        int run = 0;
+        for (int c = 0; c < n_chunks_a; ++c) {
+            const int v = cnt[c][tid];
+            cnt[c][tid] = run;
+            run += v;
+        }
+        tot[tid] = run;
+    }
+    __syncthreads();
+    // exclusive scan of the totals (wave 0, 4 per lane) -> offsets; flags of
+    // the non-empty experts -> slot of each active expert
+    if (wave == 0) {
+        int c4[4], f[4], sc = 0, sf = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            c4[i] = tot[4 * lane + i];
+            f[i] = c4[i] > 0;
+            sc += c4[i];
+            sf += f[i];
+        }
+        int ic = sc, jf = sf;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int pc = __shfl_up(ic, d, kWave), pf = __shfl_up(jf, d, kWave);
+            if (lane >= d) { ic += pc; jf += pf; }
+        }
+        int ec = ic - sc, ef = jf - sf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = 4 * lane + i;
+            offs[e] = ec;
+            offsets[e] = ec;
+            act_rank[e] = f[i] ? ef : -1;
+            ec += c4[i];
+            ef += f[i];
+        }
+        if (lane == 63) {
+            offs[kE] = ec;
+            offsets[kE] = ec;
+            *n_active = ef;
+            *n_chunks = ef;
+            n_act_s = ef;
+        }
+    }
+    __syncthreads();
+    if (e_mine >= 0) {
+        const int a = 64 * wave + lane;
+        const int dest = offs[e_mine] + cnt[wave][e_mine] + within;
+        pos[a] = dest;
+        perm[dest] = a;
+        sperm[dest] = a;
+    }
+    if (tid < kE && act_rank[tid] >= 0) act_list[act_rank[tid]] = tid;
+    __syncthreads();
+    // slot records {expert, first sorted position, count, first token, second
+    // token}, records past n_active hold expert -1; chunks {expert, first
+    // position, rows, 0} (rows <= 48 < 96: one chunk per active expert)
+    if (tid < kE) {
+        int4 *rec = reinterpret_cast<int4 *>(slots + 8 * tid);
+        if (tid < n_act_s) {
+            const int e = act_list[tid], b = offs[e], n = offs[e + 1] - offs[e];
+            const int t0 = sperm[b] / kTopK, t1 = n > 1 ? sperm[b + 1] / kTopK : t0;
+            rec[0] = make_int4(e, b, n, t0);
+            rec[1] = make_int4(t1, 0, 0, 0);
+            chunks[tid] = make_int4(e, b, n, 0);
+        } else {
+            rec[0] = make_int4(-1, 0, 0, 0);
+            rec[1] = make_int4(0, 0, 0, 0);
+        }
+    }
+}
+
+void launch_route_small(const float *logits, int T, int *topk_idx, float *topk_w, int *offsets, int *perm,
+                        int *pos, int *n_active, int *slots, int *chunks, int *n_chunks, hipStream_t s) {
+    hipLaunchKernelGGL(k_route_small, dim3(1), dim3(1024), 0, s, logits, T, topk_idx, topk_w, offsets, perm, pos,
+                       n_active, slots, reinterpret_cast<int4 *>(chunks), n_chunks);
+}
+
 void launch_sort(const int *topk_idx, int T, int *offsets, int *perm, int *pos, int *n_active,
                  int *slots, int *chunks, int *n_chunks, hipStream_t s) {
     hipLaunchKernelGGL(k_sort, dim3(1), dim3(1024), 0, s, topk_idx, T, offsets, perm, pos, n_active,

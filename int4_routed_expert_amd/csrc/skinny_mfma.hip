@@ -25,6 +25,7 @@
 // inside an MFMA is the same for both operands.
 #include "common.h"
 #include "launch.h"
+#include "token_ops.h"
 
 namespace moe_w4 {
 
@@ -53,6 +54,12 @@ struct SkinnyJob {
 
 struct SkinnyJobs {
     SkinnyJob job[2];
+    // optional third role, workgroups past the two jobs: the Hadamard-rotated
+    // fp16 copy of x (rotate_x_wave), one wave per token
+    const uint16_t *rot_x;
+    int rot_tokens;
+    uint32_t *xt;
+    float *xt_scale;
 };
 
 __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
@@ -74,6 +81,18 @@ __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__
     // offsets) and then selected: indexing the argument by the job number
     // would make every field a dependent scalar load
     const SkinnyJob j0 = jobs.job[0], j1 = jobs.job[1];
+    if ((int)blockIdx.x >= j0.n_blocks + j1.n_blocks) {
+        const int lane = threadIdx.x & 63;
+        const int t = ((int)blockIdx.x - j0.n_blocks - j1.n_blocks) * KS + wave_id();
+        if (t >= jobs.rot_tokens) return;
+        uint4 xq[4];
+        const uint4 *xp = reinterpret_cast<const uint4 *>(jobs.rot_x + (size_t)t * kH + lane * 32);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xq[i] = xp[i];
+        const int sh = rotate_x_wave(xq, lane, jobs.xt + (size_t)t * (kH / 2) + lane * 16);
+        if (lane == 0) jobs.xt_scale[t] = ldexpf(1.0f, sh);
+        return;
+    }
     const bool second = (int)blockIdx.x >= j0.n_blocks;
     SkinnyJob J;
     J.B = second ? j1.B : j0.B;
@@ -183,7 +202,7 @@ __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__
 template <int KB, int CW>
 static void launch_skinny_k(const uint16_t *A, int M, const SkinnyJobs &jobs, hipStream_t s) {
     constexpr int KS = 8;
-    dim3 grid(jobs.job[0].n_blocks + jobs.job[1].n_blocks), block(64 * KS);
+    dim3 grid(jobs.job[0].n_blocks + jobs.job[1].n_blocks + (jobs.rot_tokens + KS - 1) / KS), block(64 * KS);
     if (M <= 16)
         hipLaunchKernelGGL((k_skinny<1, KS, KB, CW>), grid, block, 0, s, A, M, jobs);
     else if (M <= 32)
@@ -195,8 +214,13 @@ static void launch_skinny_k(const uint16_t *A, int M, const SkinnyJobs &jobs, hi
 static SkinnyJob no_job() { return SkinnyJob{nullptr, 0, 0, 0, kEpiStoreF32, nullptr, nullptr, 0, nullptr, nullptr, nullptr}; }
 
 void launch_router_and_shared_gateup(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
-                                     float *logits, const uint16_t *shared_w, uint16_t *hs, hipStream_t s) {
+                                     float *logits, const uint16_t *shared_w, uint16_t *hs, uint32_t *xt,
+                                     float *xt_scale, hipStream_t s) {
     SkinnyJobs jobs;
+    jobs.rot_x = x;
+    jobs.rot_tokens = xt ? T : 0;
+    jobs.xt = xt;
+    jobs.xt_scale = xt_scale;
     jobs.job[0] = SkinnyJob{router_w, kE, 0, kE / 16, kEpiStoreF32, bias, logits, kE, nullptr, nullptr, nullptr};
     // columns: 16-wide tiles of (8 gate rows, the same 8 up rows); up rows start at row 1024
     jobs.job[1] = SkinnyJob{shared_w, 2 * kIS, kIS, 2 * kIS / 16, kEpiSwiglu, nullptr, hs, kIS, nullptr, nullptr, nullptr};
@@ -206,6 +230,10 @@ void launch_router_and_shared_gateup(const uint16_t *x, int T, const uint16_t *r
 void launch_shared_down_combine(const uint16_t *shared_w, const uint16_t *hs, int T, const float *topk_w,
                                 const int *pos, const float *o, uint16_t *y, hipStream_t s) {
     SkinnyJobs jobs;
+    jobs.rot_x = nullptr;
+    jobs.rot_tokens = 0;
+    jobs.xt = nullptr;
+    jobs.xt_scale = nullptr;
     jobs.job[0] = SkinnyJob{shared_w + 2 * kSharedGateElems, kH, 0, kH / 8, kEpiCombine, nullptr, y, kH, topk_w, pos, o};
     jobs.job[1] = no_job();
     launch_skinny_k<kIS / (128 * 8), 8>(hs, T, jobs, s);
