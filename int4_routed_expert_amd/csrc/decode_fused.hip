@@ -138,19 +138,20 @@ struct GuBatch {
     uint16_t sg[kFuPairs], su[kFuPairs];
 };
 
-// Row . x_t for every token, by one wave (lane l owns K [32l, 32l+32) of the
-// bf16 row); token t's sum ends on lanes 8t..8t+7 (all of them).
+// Row . x_t for every token, by one wave (load i of lane l takes K
+// [512i + 8l, 512i + 8l + 8) of the bf16 row, so each load reads 1 KB
+// contiguous); token t's sum ends on lanes 8t..8t+7 (all of them).
 template <int T>
 __device__ __forceinline__ float row_dot_tokens(const uint16_t *row, const uint16_t *x, int lane) {
     const __amdgpu_buffer_rsrc_t rb = make_buf(row, kH * 2);
     const __amdgpu_buffer_rsrc_t xb = make_buf(x, T * kH * 2);
     uint4 w[4], xv[T][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) w[i] = bload16_nt(rb, lane * 64 + 16 * i, 0);
+    for (int i = 0; i < 4; ++i) w[i] = bload16_nt(rb, lane * 16 + 1024 * i, 0);
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xv[t][i] = bload16(xb, lane * 64 + 16 * i, t * kH * 2);
+        for (int i = 0; i < 4; ++i) xv[t][i] = bload16(xb, lane * 16 + 1024 * i, t * kH * 2);
     float v[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -218,8 +219,8 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
 
     // ---- work that depends on nothing: the loads of the logits and of x
     // (gate/up role), or the shared down projection of this workgroup's
-    // features, z[t][c0 + wave] = h_t . Wsd[c0 + wave], lane l owning
-    // K [16l, 16l+16) (down role) ----
+    // features, z[t][c0 + wave] = h_t . Wsd[c0 + wave], load i of lane l taking
+    // K [512i + 8l, 512i + 8l + 8) (down role) ----
     float4 lv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (wave < T) lv = reinterpret_cast<const float4 *>(A.logits + (size_t)wave * kE)[lane];
     constexpr int kRotTasks = (4 * T + kFuWaves - 1) / kFuWaves;   // x quarters per wave
@@ -235,12 +236,12 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
         const int c0 = ((int)blockIdx.x - kFuGuWgs) * kFuCols;
         const __amdgpu_buffer_rsrc_t wb = make_buf(A.shared_down + (size_t)(c0 + wave) * kIS, kIS * 2);
         const __amdgpu_buffer_rsrc_t hb = make_buf(A.hs, (uint32_t)(T * kIS * 2));
-        const uint4 w0 = bload16_nt(wb, lane * 32, 0), w1 = bload16_nt(wb, lane * 32 + 16, 0);
+        const uint4 w0 = bload16_nt(wb, lane * 16, 0), w1 = bload16_nt(wb, lane * 16 + 1024, 0);
         uint4 hq[T][2];
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-            hq[t][0] = bload16(hb, lane * 32, t * kIS * 2);
-            hq[t][1] = bload16(hb, lane * 32 + 16, t * kIS * 2);
+            hq[t][0] = bload16(hb, lane * 16, t * kIS * 2);
+            hq[t][1] = bload16(hb, lane * 16 + 1024, t * kIS * 2);
         }
         float v[8];
 #pragma unroll
@@ -433,11 +434,12 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
     const int c0 = ((int)blockIdx.x - kFuGuWgs) * kFuCols;
     const int replica = ((int)blockIdx.x % kFusedCounters) * kFusedCounterStride;
     // down codes of this workgroup's 8 features for every active expert this
-    // wave handles (experts wave, wave + 8, ...): lane l takes row l / 8 and
-    // K [64 (l % 8), 64 (l % 8) + 64), inside block (l % 8) / 2
+    // wave handles (experts wave, wave + 8, ...): lane l takes row l / 8 and,
+    // in half h, K [256h + 32 (l % 8), 256h + 32 (l % 8) + 32) (inside block
+    // 2h + (l % 8) / 4), so each load reads 128 contiguous bytes per row
     const int rr = lane >> 3, kq = lane & 7;
     uint4 dw[kSlots][2];
-    uint16_t ds[kSlots];
+    uint16_t ds[kSlots][2];
 #pragma unroll
     for (int s = 0; s < kSlots; ++s) {
         // slots past the last active expert re-read its rows (in bounds, unused),
@@ -448,9 +450,11 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
                                    kFuCols * (kI / 2));
         const rsrc_t sd = make_buf(A.scales + (size_t)e * kScalesPerExpert + kScalesGu + (size_t)c0 * (kI / kG),
                                    kFuCols * (kI / kG) * 2);
-        dw[s][0] = bload16_nt(cd, rr * (kI / 2) + kq * 32, 0);
-        dw[s][1] = bload16_nt(cd, rr * (kI / 2) + kq * 32 + 16, 0);
-        ds[s] = bload2_nt(sd, 2 * (rr * (kI / kG) + (kq >> 1)), 0);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+            dw[s][hf] = bload16_nt(cd, rr * (kI / 2) + 128 * hf + kq * 16, 0);
+            ds[s][hf] = bload2_nt(sd, 2 * (rr * (kI / kG) + 2 * hf + (kq >> 2)), 0);
+        }
     }
 
     // wait until every gate/up workgroup is done (bounded)
@@ -487,11 +491,9 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
         const int ai = wave + kFuWaves * s;
         if (ai < n_act) {
             const int p0 = uniform(R.act_begin[ai]), n = uniform(R.act_n[ai]);
-            const float srow = bf16_to_f32(ds[s]);
             for (int k = 0; k < n; ++k) {
                 const int p = p0 + k;
-                // operands of K [64 kq, 64 kq + 64): words 32 kq .. 32 kq + 31,
-                // one 32-code half at a time
+                // operands of K [256h + 32 kq, +32): words 128h + 16 kq .. +15
                 float acc = 0.0f;
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
@@ -499,10 +501,10 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
                     Q4 q[4];
                     convert16(dw[s][hf], q);
                     uint32_t xs[16];
-                    const float off = load_operand32(&U.dn.at[p][32 * kq + 16 * hf], xs);
-                    acc = dot_slice(q, xs, acc - off);
+                    const float off = load_operand32(&U.dn.at[p][128 * hf + 16 * kq], xs);
+                    acc += dot_slice(q, xs, -off) *
+                           (bf16_to_f32(ds[s][hf]) * U.dn.atsc[p][2 * hf + (kq >> 2)]);
                 }
-                acc *= srow * U.dn.atsc[p][kq >> 1];
                 acc += shfl_xor_f(acc, 1);
                 acc += shfl_xor_f(acc, 2);
                 acc += shfl_xor_f(acc, 4);

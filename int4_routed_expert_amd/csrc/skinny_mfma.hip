@@ -19,10 +19,12 @@
 //
 // Tiling: a workgroup owns CW output columns (for SwiGLU: CW/2 gate rows and
 // the same CW/2 up rows) and all tokens; its KS waves split K, each accumulating
-// 16x16 tiles of v_mfma_f32_16x16x32_bf16, and reduce through LDS.  Lane
-// (r = l % 16, g = l / 16) loads 32 consecutive K of weight row r % CW and of
-// token row r, so every lane load is 64 contiguous bytes and the K order
-// inside an MFMA is the same for both operands.
+// 16x16 tiles of v_mfma_f32_16x16x32_bf16, and reduce through LDS.  MFMA s of
+// a 128-wide K block takes K [32s, 32s + 32) of the block, lane (r = l % 16,
+// g = l / 16) holding K [32s + 8g, 32s + 8g + 8) of weight row r % CW and of
+// token row r: the four lanes of a row read 64 contiguous bytes in one load
+// (whole half lines, not 16-byte pieces spread over two lines), and the K
+// order inside an MFMA is the same for both operands.
 #include "common.h"
 #include "launch.h"
 #include "token_ops.h"
@@ -124,7 +126,7 @@ __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__
     for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int s = 0; s < 4; ++s)
-            b[kb][s] = bload16_nt(bres, brow_off + (uint32_t)(k_begin + 128 * kb + 32 * g + 8 * s) * 2, 0);
+            b[kb][s] = bload16_nt(bres, brow_off + (uint32_t)(k_begin + 128 * kb + 32 * s + 8 * g) * 2, 0);
 
     for (int m0 = 0; m0 < M; m0 += 16 * MT) {
         f32x4_t acc[MT];
@@ -133,12 +135,12 @@ __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__
 #pragma unroll
         for (int t = 0; t < MT; ++t) {
             const int m = min(m0 + 16 * t + r, M - 1);
-            const uint4 *ap = reinterpret_cast<const uint4 *>(A + (size_t)m * K + k_begin + 32 * g);
+            const uint4 *ap = reinterpret_cast<const uint4 *>(A + (size_t)m * K + k_begin + 8 * g);
             uint4 a[KB][4];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) a[kb][s] = ap[16 * kb + s];
+                for (int s = 0; s < 4; ++s) a[kb][s] = ap[16 * kb + 4 * s];
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
