@@ -91,9 +91,11 @@ constexpr int kPrefillMinTokens = 128;
 template <class T_>
 T_ *ws_at(void *ws, size_t off) { return reinterpret_cast<T_ *>(static_cast<char *>(ws) + off); }
 
+// resid (stack layers of 1-8 tokens only): x_ is then written, as
+// bf16(rmsnorm(resid)), by the first launch, and the last adds y to resid.
 int run_forward(const void *x_, const void *router_w_, const void *codes_, const void *scales_,
                 const void *shared_w_, int64_t T64, void *y_, const float *bias, void *ws,
-                hipStream_t s, void *const *events, int n_events) {
+                hipStream_t s, void *const *events, int n_events, float *resid = nullptr) {
     const int T = (int)T64;
     const moe_w4_ws_layout L = make_layout(T64);
     const uint16_t *x = static_cast<const uint16_t *>(x_);
@@ -153,7 +155,8 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     if (fused) {
         // two launches: router logits and shared h (which also clear the
         // counters), then the rest of the layer; the other stages are empty
-        MOE_STEP(launch_router_shared_small(x, T, router_w, bias, shared_w, logits, hs, counters, s));
+        MOE_STEP(launch_router_shared_small(x, resid, const_cast<uint16_t *>(x), T, router_w, bias, shared_w, logits,
+                                            hs, counters, s));
         MOE_MARK();
         MOE_MARK();
         FusedDecodeArgs fa;
@@ -175,6 +178,7 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
         fa.n_chunks = n_chunks;
         fa.act = act;
         fa.y = y;
+        fa.resid = resid;
         fa.counters = counters;
         MOE_STEP(launch_decode_fused(fa, s));
         for (int i = 0; i < 4; ++i) MOE_MARK();
@@ -332,6 +336,9 @@ int moe_w4_stack_layer(float *resid, const void *router_w, const void *codes, co
         return MOE_W4_EINVAL;
     hipStream_t s = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
+    if (T <= kFusedMaxTokens)   // rmsnorm and residual add inside the two launches
+        return run_forward(x_buf, router_w, codes, scales, shared_w, T, y_buf, nullptr, workspace, s, nullptr, 0,
+                           resid);
     launch_rmsnorm_bf16(resid, (int)T, static_cast<uint16_t *>(x_buf), s);
     if ((rc = device_status(hipGetLastError())) != MOE_W4_OK) return rc;
     rc = run_forward(x_buf, router_w, codes, scales, shared_w, T, y_buf, nullptr, workspace, s, nullptr, 0);

@@ -6,9 +6,11 @@
 // costs a few microseconds each.  Here the first launch computes everything
 // that needs only x: the router logits (one wave per router row) and the
 // shared expert's h = bf16(silu(x Wsg^T) * (x Wsu^T)) (ungated bf16 SwiGLU of
-// width 1024, Flint model card, Aijuus/flint-w4exp, introduction; one
-// workgroup per column of h).  The second launch runs all the rest, with two
-// roles of workgroups:
+// width 1024, Flint model card, Aijuus/flint-w4exp, introduction; four
+// columns of h per workgroup).  In a layer of a stack it also computes x
+// itself from the residual stream (rmsnorm), and the second launch adds y to
+// the residual stream, so a stack layer is two launches as well.  The second
+// launch runs all the rest, with two roles of workgroups:
 //
 //   every workgroup: the routing of all tokens from the logits (wave t: top-6
 //       of token t, model card, introduction: 256 experts, top-6; weights
@@ -140,18 +142,14 @@ struct GuBatch {
 
 // Row . x_t for every token, by one wave (load i of lane l takes K
 // [512i + 8l, 512i + 8l + 8) of the bf16 row, so each load reads 1 KB
-// contiguous); token t's sum ends on lanes 8t..8t+7 (all of them).
+// contiguous; x from LDS in the same layout); token t's sum ends on lanes
+// 8t..8t+7 (all of them).
 template <int T>
-__device__ __forceinline__ float row_dot_tokens(const uint16_t *row, const uint16_t *x, int lane) {
+__device__ __forceinline__ float row_dot_tokens(const uint16_t *row, const uint4 (*xl)[kH / 8], int lane) {
     const __amdgpu_buffer_rsrc_t rb = make_buf(row, kH * 2);
-    const __amdgpu_buffer_rsrc_t xb = make_buf(x, T * kH * 2);
-    uint4 w[4], xv[T][4];
+    uint4 w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = bload16_nt(rb, lane * 16 + 1024 * i, 0);
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xv[t][i] = bload16(xb, lane * 16 + 1024 * i, t * kH * 2);
     float v[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -159,10 +157,11 @@ __device__ __forceinline__ float row_dot_tokens(const uint16_t *row, const uint1
         if (t < T) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                acc = dot2b(xv[t][i].x, w[i].x, acc);
-                acc = dot2b(xv[t][i].y, w[i].y, acc);
-                acc = dot2b(xv[t][i].z, w[i].z, acc);
-                acc = dot2b(xv[t][i].w, w[i].w, acc);
+                const uint4 xv = xl[t][64 * i + lane];
+                acc = dot2b(xv.x, w[i].x, acc);
+                acc = dot2b(xv.y, w[i].y, acc);
+                acc = dot2b(xv.z, w[i].z, acc);
+                acc = dot2b(xv.w, w[i].w, acc);
             }
         }
         v[t] = acc;
@@ -171,36 +170,84 @@ __device__ __forceinline__ float row_dot_tokens(const uint16_t *row, const uint1
 }
 
 // ---------------------------------------------------------------------------
-// Launch 1: what needs only x.  Workgroups of 2 waves: the first 128 compute
-// router logits (one row per wave; fp32 sums of exact bf16 products, NInfer
-// README of Flint, "What is inside": router rows widened exactly from bf16),
-// the other 1024 one column c of h each (wave 0 the gate row c, wave 1 the up
-// row c).  Workgroup 0 also clears the counters of the second launch.
+// Launch 1: what needs only x.  Workgroups of 8 waves, one weight row per
+// wave: the first 32 compute router logits (fp32 sums of exact bf16
+// products, NInfer README of Flint, "What is inside": router rows widened
+// exactly from bf16), the other 256 four columns c of h each (waves 0-3 the
+// gate rows, 4-7 the up rows).  x is staged in LDS once per workgroup; in a
+// stack layer (RESID) it is computed there from the fp32 residual stream as
+// bf16(resid / sqrt(mean(resid^2) + 1e-6)) (wave t: token t; every
+// workgroup sums in the same order, so all agree bit for bit) and workgroup 0
+// writes it out.  Workgroup 0 also clears the counters of the second launch.
 // ---------------------------------------------------------------------------
-constexpr int kRouterWgs = kE / 2;
+constexpr int kRouterWgs = kE / 8;
+constexpr int kSharedWgs = kIS / 4;
 
-template <int T>
-__global__ __launch_bounds__(128) void k_router_shared_small(const uint16_t *__restrict__ x,
+template <int T, bool RESID>
+__global__ __launch_bounds__(512) void k_router_shared_small(const uint16_t *__restrict__ x,
+                                                             const float *__restrict__ resid,
+                                                             uint16_t *__restrict__ x_out,
                                                              const uint16_t *__restrict__ router_w,
                                                              const float *__restrict__ bias,
                                                              const uint16_t *__restrict__ shared_gu,
                                                              float *__restrict__ logits, uint16_t *__restrict__ hs,
                                                              int *__restrict__ counters) {
-    __shared__ float up[8];
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x >> 6;
-    if (blockIdx.x == 0 && threadIdx.x < kFusedCounters) counters[threadIdx.x * kFusedCounterStride] = 0;
+    __shared__ uint4 xl[T][kH / 8];
+    __shared__ float part[8][8];   // shared role: [wave][token]
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    if (blockIdx.x == 0 && tid < kFusedCounters) counters[tid * kFusedCounterStride] = 0;
+    if (!RESID) {
+#pragma unroll
+        for (int i = 0; i < (T * (kH / 8) + 511) / 512; ++i) {
+            const int q = tid + 512 * i;
+            if (q < T * (kH / 8)) (&xl[0][0])[q] = reinterpret_cast<const uint4 *>(x)[q];
+        }
+    } else if (wave < T) {
+        // lane l: values 8l .. 8l+7 of each 512-wide quarter (16-byte words 64i + l)
+        const int t = wave;
+        float4 r[4][2];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 *rp = reinterpret_cast<const float4 *>(resid + (size_t)t * kH + 512 * i + 8 * lane);
+            r[i][0] = rp[0];
+            r[i][1] = rp[1];
+        }
+        float ss = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                ss += r[i][h].x * r[i][h].x + r[i][h].y * r[i][h].y + r[i][h].z * r[i][h].z + r[i][h].w * r[i][h].w;
+        const float inv = 1.0f / sqrtf(wave_sum(ss) / (float)kH + 1e-6f);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 a = r[i][0], b = r[i][1];
+            uint4 q;
+            q.x = (uint32_t)f32_to_bf16(a.x * inv) | ((uint32_t)f32_to_bf16(a.y * inv) << 16);
+            q.y = (uint32_t)f32_to_bf16(a.z * inv) | ((uint32_t)f32_to_bf16(a.w * inv) << 16);
+            q.z = (uint32_t)f32_to_bf16(b.x * inv) | ((uint32_t)f32_to_bf16(b.y * inv) << 16);
+            q.w = (uint32_t)f32_to_bf16(b.z * inv) | ((uint32_t)f32_to_bf16(b.w * inv) << 16);
+            xl[t][64 * i + lane] = q;
+            if (blockIdx.x == 0) reinterpret_cast<uint4 *>(x_out + (size_t)t * kH + 512 * i + 8 * lane)[0] = q;
+        }
+    }
+    __syncthreads();
     const int t = lane >> 3;
     if ((int)blockIdx.x < kRouterWgs) {
-        const int e = 2 * (int)blockIdx.x + wave;
-        const float sum = row_dot_tokens<T>(router_w + (size_t)e * kH, x, lane);
+        const int e = 8 * (int)blockIdx.x + wave;
+        const float sum = row_dot_tokens<T>(router_w + (size_t)e * kH, xl, lane);
         if ((lane & 7) == 0 && t < T) logits[(size_t)t * kE + e] = sum + (bias ? bias[e] : 0.0f);
         return;
     }
-    const int c = (int)blockIdx.x - kRouterWgs;
-    const float sum = row_dot_tokens<T>(shared_gu + (size_t)(wave * kIS + c) * kH, x, lane);
-    if (wave == 1 && (lane & 7) == 0) up[t] = sum;
+    const int c0 = ((int)blockIdx.x - kRouterWgs) * 4;
+    const int row = (wave < 4 ? 0 : kIS) + c0 + (wave & 3);
+    const float sum = row_dot_tokens<T>(shared_gu + (size_t)row * kH, xl, lane);
+    if ((lane & 7) == 0) part[wave][t] = sum;
     __syncthreads();
-    if (wave == 0 && (lane & 7) == 0 && t < T) hs[(size_t)t * kIS + c] = f32_to_bf16(silu_f(sum) * up[t]);
+    if (tid < 4 * T) {
+        const int tt = tid >> 2, c = tid & 3;
+        hs[(size_t)tt * kIS + c0 + c] = f32_to_bf16(silu_f(part[c][tt]) * part[4 + c][tt]);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -520,7 +567,9 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
         float acc = U.dn.z[t][c];
 #pragma unroll
         for (int j = 0; j < kTopK; ++j) acc = fmaf(R.w[kTopK * t + j], U.dn.o[R.pos[kTopK * t + j]][c], acc);
-        A.y[(size_t)t * kH + c0 + c] = f32_to_bf16(acc);
+        const uint16_t yb = f32_to_bf16(acc);
+        A.y[(size_t)t * kH + c0 + c] = yb;
+        if (A.resid) A.resid[(size_t)t * kH + c0 + c] += bf16_to_f32(yb);   // stack layer: resid += y
     }
 }
 
@@ -539,11 +588,32 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
     default: break;                                                              \
     }
 
-void launch_router_shared_small(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
-                                const uint16_t *shared_w, float *logits, uint16_t *hs, int *counters, hipStream_t s) {
-    MOE_FUSED_DISPATCH(k_router_shared_small, dim3(kRouterWgs + kIS), dim3(128), 0, s, x, router_w, bias, shared_w,
-                       logits, hs, counters)
+#define MOE_FUSED_DISPATCH2(KERNEL, B, ...)                                      \
+    switch (T) {                                                                 \
+    case 1: hipLaunchKernelGGL((KERNEL<1, B>), __VA_ARGS__); break;              \
+    case 2: hipLaunchKernelGGL((KERNEL<2, B>), __VA_ARGS__); break;              \
+    case 3: hipLaunchKernelGGL((KERNEL<3, B>), __VA_ARGS__); break;              \
+    case 4: hipLaunchKernelGGL((KERNEL<4, B>), __VA_ARGS__); break;              \
+    case 5: hipLaunchKernelGGL((KERNEL<5, B>), __VA_ARGS__); break;              \
+    case 6: hipLaunchKernelGGL((KERNEL<6, B>), __VA_ARGS__); break;              \
+    case 7: hipLaunchKernelGGL((KERNEL<7, B>), __VA_ARGS__); break;              \
+    case 8: hipLaunchKernelGGL((KERNEL<8, B>), __VA_ARGS__); break;              \
+    default: break;                                                              \
+    }
+
+void launch_router_shared_small(const uint16_t *x, const float *resid, uint16_t *x_out, int T,
+                                const uint16_t *router_w, const float *bias, const uint16_t *shared_w, float *logits,
+                                uint16_t *hs, int *counters, hipStream_t s) {
+    if (resid) {
+        MOE_FUSED_DISPATCH2(k_router_shared_small, true, dim3(kRouterWgs + kSharedWgs), dim3(512), 0, s, x, resid, x_out,
+                            router_w, bias, shared_w, logits, hs, counters)
+    } else {
+        MOE_FUSED_DISPATCH2(k_router_shared_small, false, dim3(kRouterWgs + kSharedWgs), dim3(512), 0, s, x, resid, x_out,
+                            router_w, bias, shared_w, logits, hs, counters)
+    }
 }
+
+#undef MOE_FUSED_DISPATCH2
 
 void launch_decode_fused(const FusedDecodeArgs &args, hipStream_t s) {
     const int T = args.T;

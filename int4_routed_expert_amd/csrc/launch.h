@@ -41,10 +41,14 @@ struct FusedDecodeArgs {
     int *n_chunks;
     float *act;                    // [6T][512] fp32 scratch, sorted-position order
     uint16_t *y;
+    float *resid;                  // stack layer: resid += y (else null)
     int *counters;                 // 4096 bytes; zero at launch (the first launch clears them)
 };
-void launch_router_shared_small(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
-                                const uint16_t *shared_w, float *logits, uint16_t *hs, int *counters, hipStream_t s);
+// With resid (a stack layer), x is computed as bf16(rmsnorm(resid)) and also
+// written to x_out, and the second launch adds y to resid.
+void launch_router_shared_small(const uint16_t *x, const float *resid, uint16_t *x_out, int T,
+                                const uint16_t *router_w, const float *bias, const uint16_t *shared_w, float *logits,
+                                uint16_t *hs, int *counters, hipStream_t s);
 void launch_decode_fused(const FusedDecodeArgs &args, hipStream_t s);
 
 // Per token: top-6 of the logits, renormalised sigmoid weights, and the
