@@ -71,7 +71,7 @@ def test_device_generator_matches_host(m, layer0):
 
 
 # ---------------------------------------------------------------- small / ragged
-@pytest.mark.parametrize("T", [1, 2, 3, 5, 7, 16, 31, 33, 63, 65])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 6, 7, 8, 9, 16, 31, 33, 48, 49, 63, 65])
 def test_layer_small_T(m, layer0, T):
     x = synth.gen_x(100 + T, T)
     g = P.run_gpu(m, x, layer0)
@@ -259,9 +259,10 @@ def test_token_permutation_equivariance(m, layer0):
 
 
 # ---------------------------------------------------------------------- stack
-def test_stack_teacher_forced(m):
-    """Two layers of the seed-4 stack; each layer checked on the GPU's own input."""
-    T = 8
+@pytest.mark.parametrize("T", [1, 8, 9])
+def test_stack_teacher_forced(m, T):
+    """Two layers of the seed-4 stack; each layer checked on the GPU's own input
+    (1-8 tokens: rmsnorm and residual add inside the layer's two launches)."""
     layers = [m.generated_layer(synth.STACK_SEED, l) for l in range(2)]
     x0 = torch.empty((T, 2048), dtype=torch.int16, device="cuda")
     m.moe_w4_generate_x(synth.STACK_SEED, 0, x0)
