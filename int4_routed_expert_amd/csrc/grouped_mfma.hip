@@ -428,50 +428,60 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
         const uint32_t off = (uint32_t)(f0 + 128 * tile) * (kI / 2) + 32 * g;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            cb[slot][2 * b] = bload16_nt(cres, off + 64 * b, 0);
-            cb[slot][2 * b + 1] = bload16_nt(cres, off + 64 * b + 16, 0);
+            cb[slot][2 * b] = bload16(cres, off + 64 * b, 0);
+            cb[slot][2 * b + 1] = bload16(cres, off + 64 * b + 16, 0);
         }
     };
-    // the codes do not depend on the chunk's tokens: in flight first
+    // the chunk's activations are needed first: thread -> (row, part), load
+    // i takes the row's 16-byte group 4i + part (block i / 4); the codes of
+    // the first tiles are requested right behind them
+    const bool stager = tid < 4 * kChunkRows;
+    const int srow = tid >> 2, part = tid & 3;
+    uint4 v[16];
+    float4 ps;
+    __builtin_amdgcn_sched_barrier(0);
+    if (stager) {
+        const int p = row0 + min(srow, rows - 1);
+        const uint4 *src = reinterpret_cast<const uint4 *>(at + (size_t)p * (kI / 2)) + part;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = src[4 * i];
+        ps = *reinterpret_cast<const float4 *>(at_scale + (size_t)p * (kI / kG));
+    }
+    // the expert's down scales: thread t < 256 takes features 8t..8t+7
+    uint4 s4[4];
+    if (tid < 256) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(scales + (size_t)e * kScalesPerExpert + kScalesGu) + 4 * tid;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s4[i] = src[i];
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int d = 0; d < kDnCodeRing - 1; ++d) fetch(d, d);
     __builtin_amdgcn_sched_barrier(0);
 
-    // the expert's down scales, transposed to [block][feature], and each
-    // feature's normalisation: thread t < 256 takes features 8t..8t+7
+    // the down scales transposed to [block][feature], and each feature's
+    // normalisation
     if (tid < 256) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(scales + (size_t)e * kScalesPerExpert + kScalesGu) + 4 * tid;
-        const uint4 s0 = src[0], s1 = src[1], s2 = src[2], s3 = src[3];
-        const uint32_t w[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
-                                s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
+        const uint32_t w[16] = {s4[0].x, s4[0].y, s4[0].z, s4[0].w, s4[1].x, s4[1].y, s4[1].z, s4[1].w,
+                                s4[2].x, s4[2].y, s4[2].z, s4[2].w, s4[3].x, s4[3].y, s4[3].z, s4[3].w};
         // feature f = 8t + k holds blocks 0,1 in w[2k] and 2,3 in w[2k+1]
 #pragma unroll
         for (int bb = 0; bb < 4; ++bb) {
-            uint32_t v[4];
+            uint32_t t4[4];
 #pragma unroll
             for (int k2 = 0; k2 < 4; ++k2) {
                 const uint32_t lo = w[2 * (2 * k2) + (bb >> 1)], hi = w[2 * (2 * k2 + 1) + (bb >> 1)];
                 const uint32_t a0 = (bb & 1) ? (lo >> 16) : (lo & 0xffffu);
                 const uint32_t a1 = (bb & 1) ? (hi >> 16) : (hi & 0xffffu);
-                v[k2] = a0 | (a1 << 16);
+                t4[k2] = a0 | (a1 << 16);
             }
-            *reinterpret_cast<uint4 *>(&sc[bb][8 * tid]) = make_uint4(v[0], v[1], v[2], v[3]);
+            *reinterpret_cast<uint4 *>(&sc[bb][8 * tid]) = make_uint4(t4[0], t4[1], t4[2], t4[3]);
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) fk[8 * tid + k] = ldexpf(1.0f, -scale_shift4(w[2 * k], w[2 * k + 1]));
     }
-    // stage the chunk's activations: thread -> (row, part); load i takes the
-    // row's 16-byte group 4i + part (block i / 4), brought to the row's
-    // largest block prescale
-    for (int srow = tid >> 2; srow < kChunkRows; srow += 64 * kDnHalves) {
-        const int part = tid & 3;
-        const int p = row0 + min(srow, rows - 1);
-        const uint4 *src = reinterpret_cast<const uint4 *>(at + (size_t)p * (kI / 2)) + part;
-        uint4 v[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = src[4 * i];
-        const float4 ps = *reinterpret_cast<const float4 *>(at_scale + (size_t)p * (kI / kG));
+    // stage the activations, each block brought to the row's largest prescale
+    if (stager) {
         const float pm = fmaxf(fmaxf(ps.x, ps.y), fmaxf(ps.z, ps.w));
         const float pb[4] = {ps.x / pm, ps.y / pm, ps.z / pm, ps.w / pm};   // exact powers of two <= 1
 #pragma unroll
@@ -501,7 +511,7 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
     // that every iteration issues the same loads and the waits stay exact
     with_tiles(n_mt, [&](auto tiles) {
     constexpr int MT = decltype(tiles)::value;
-#pragma unroll kDnCodeRing
+#pragma unroll
     for (int t = 0; t < kDnTiles; ++t) {
         const int cs = t % kDnCodeRing;
         __builtin_amdgcn_sched_barrier(0);
