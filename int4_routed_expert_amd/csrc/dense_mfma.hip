@@ -153,40 +153,46 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[x][y][i] = 0.0f;
 
+    // step k's operands live in register set k % 2 until stored to LDS slot
+    // k % 2: step 0 is stored before the loop, step s + 1 during step s
 #pragma unroll
     for (int d = 0; d < kPrefetch; ++d) load(d, d);
     store(0, 0);
+    load(0, 2);
     __syncthreads();
 
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
         const int slot = s & 1;
-        __builtin_amdgcn_sched_barrier(0);
-        // the register set of step s (already in LDS) takes step s + kPrefetch
-        if (s + kPrefetch < kSteps) load(s % kPrefetch, s + kPrefetch);
-        __builtin_amdgcn_sched_barrier(0);
+        // every operand of the step is requested from LDS first, so the MFMAs
+        // below wait for the LDS latency once per step, not once per k-slice
+        uint4 a[kChunksPerRow / 2][2], b[kChunksPerRow / 2][2];
 #pragma unroll
         for (int j = 0; j < kChunksPerRow / 2; ++j) {
             const int grp = (kChunksPerRow / 2) * g + j;
-            uint4 a[2], b[2];
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
                 const int r = 64 * wm + 32 * x + n;
-                a[x] = *reinterpret_cast<const uint4 *>(sa[slot] + r * kRowBytes + ((grp ^ ((r >> 1) & 7)) * 16));
+                a[j][x] = *reinterpret_cast<const uint4 *>(sa[slot] + r * kRowBytes + ((grp ^ ((r >> 1) & 7)) * 16));
             }
 #pragma unroll
             for (int y = 0; y < 2; ++y) {
                 const int r = 64 * wn + 32 * y + n;
-                b[y] = *reinterpret_cast<const uint4 *>(sb[slot] + r * kRowBytes + ((grp ^ ((r >> 1) & 7)) * 16));
+                b[j][y] = *reinterpret_cast<const uint4 *>(sb[slot] + r * kRowBytes + ((grp ^ ((r >> 1) & 7)) * 16));
             }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // step s + 1 (loaded two steps ago) into the other slot, whose readers
+        // all passed the previous barrier; its registers then take step s + 3
+        if (s + 1 < kSteps) store((s + 1) % kPrefetch, slot ^ 1);
+        if (s + 3 < kSteps) load((s + 1) % kPrefetch, s + 3);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < kChunksPerRow / 2; ++j)
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
-                for (int y = 0; y < 2; ++y) acc[x][y] = mfma_bf16(a[x], b[y], acc[x][y]);
-        }
-        // the next step's operands (loaded during the previous step) into the
-        // other LDS slot, which every wave finished reading before the last barrier
-        if (s + 1 < kSteps) store((s + 1) % kPrefetch, slot ^ 1);
+                for (int y = 0; y < 2; ++y) acc[x][y] = mfma_bf16(a[j][x], b[j][y], acc[x][y]);
         __syncthreads();
     }
     mfma_drain();
