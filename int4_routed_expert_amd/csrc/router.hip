@@ -60,6 +60,7 @@ void launch_topk_rotate(const float *logits, const uint16_t *x, int T, int *topk
 // ---------------------------------------------------------------------------
 constexpr int kSortWaves = 16;
 constexpr int kSortBatch = 8;        // chunks of 64 assignments whose loads are issued together
+constexpr int kSortKeep = 16;        // chunks per wave kept in registers between the two passes
 constexpr int kSortChunkRows = 96;   // rows of one chunk of the MFMA grouped kernels
 
 __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx, int T,
@@ -79,10 +80,26 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
     const int a0 = wave * per, a1 = min(a0 + per, N);
 
     for (int i = tid; i < kSortWaves * kE; i += blockDim.x) (&cnt[0][0])[i] = 0;
+    // up to kSortKeep chunks of 64 per wave (6 * T <= 16384) are loaded once,
+    // all in flight together, and stay in registers for the ranking pass
+    const bool keep = per <= 64 * kSortKeep;
+    int kv[kSortKeep];
+    if (keep) {
+#pragma unroll
+        for (int u = 0; u < kSortKeep; ++u) {
+            const int a = a0 + 64 * u + lane;
+            kv[u] = a < a1 ? topk_idx[a] : -1;
+        }
+    }
     __syncthreads();
-    // the wave's assignments are read kSortBatch chunks of 64 at a time, all
-    // loads of a batch in flight together
-    for (int c0 = a0; c0 < a1; c0 += 64 * kSortBatch) {
+    if (keep) {
+#pragma unroll
+        for (int u = 0; u < kSortKeep; ++u)
+            if (kv[u] >= 0) atomicAdd(&cnt[wave][kv[u]], 1);
+    }
+    // otherwise the wave's assignments are read kSortBatch chunks of 64 at a
+    // time, all loads of a batch in flight together
+    for (int c0 = a0; !keep && c0 < a1; c0 += 64 * kSortBatch) {
         int ev[kSortBatch];
 #pragma unroll
         for (int u = 0; u < kSortBatch; ++u) {
@@ -155,20 +172,10 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
     }
     __syncthreads();
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int cb = a0; cb < a1; cb += 64 * kSortBatch) {
-    int ev[kSortBatch];
-#pragma unroll
-    for (int u = 0; u < kSortBatch; ++u) {
-        const int a = cb + 64 * u + lane;
-        ev[u] = a < a1 ? topk_idx[a] : 0;
-    }
-#pragma unroll
-    for (int u = 0; u < kSortBatch; ++u) {
-        const int c0 = cb + 64 * u;
-        if (c0 >= a1) break;
+    // stable rank of each assignment of chunk [c0, c0 + 64) (expert e) in its expert
+    auto rank_chunk = [&](int c0, int e) {
         const int a = c0 + lane;
         const bool valid = a < a1;
-        const int e = ev[u];
         uint64_t same = __ballot(valid);
 #pragma unroll
         for (int b = 0; b < 8; ++b) {
@@ -183,7 +190,26 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
             if (dest - offs[e] < 2) first2[e][dest - offs[e]] = a / kTopK;
             if ((same >> lane) == 1ull) cnt[wave][e] = base + __popcll(same);
         }
+    };
+    if (keep) {
+#pragma unroll
+        for (int u = 0; u < kSortKeep; ++u) {
+            if (a0 + 64 * u >= a1) break;
+            rank_chunk(a0 + 64 * u, kv[u] < 0 ? 0 : kv[u]);
+        }
     }
+    for (int cb = a0; !keep && cb < a1; cb += 64 * kSortBatch) {
+        int ev[kSortBatch];
+#pragma unroll
+        for (int u = 0; u < kSortBatch; ++u) {
+            const int a = cb + 64 * u + lane;
+            ev[u] = a < a1 ? topk_idx[a] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kSortBatch; ++u) {
+            if (cb + 64 * u >= a1) break;
+            rank_chunk(cb + 64 * u, ev[u]);
+        }
     }
     __syncthreads();
     // One 32-byte record per active slot, so a grouped kernel gets its expert,

@@ -127,6 +127,21 @@ __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__
 #pragma unroll
         for (int s = 0; s < 4; ++s)
             b[kb][s] = bload16_nt(bres, brow_off + (uint32_t)(k_begin + 128 * kb + 32 * s + 8 * g) * 2, 0);
+    // combine: the weights and expert rows of the first token tiles do not
+    // depend on the product and are requested now (wave t finishes tile t)
+    float pw[4][kTopK], po[4][kTopK];
+    const bool pre = epi == kEpiCombine && wave < MT && r < CW;
+    if (pre) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = min(16 * wave + 4 * g + i, M - 1);
+#pragma unroll
+            for (int j = 0; j < kTopK; ++j) {
+                pw[i][j] = J.topk_w[(size_t)m * kTopK + j];
+                po[i][j] = J.o[(size_t)J.pos[(size_t)m * kTopK + j] * kH + c0 + c];
+            }
+        }
+    }
 
     for (int m0 = 0; m0 < M; m0 += 16 * MT) {
         f32x4_t acc[MT];
@@ -186,11 +201,16 @@ __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__
                     const int m = m0 + 16 * t + 4 * g + i;
                     if (r < CW && m < M) {
                         float acc_y = sum[i];
+                        if (m0 == 0) {
 #pragma unroll
-                        for (int j = 0; j < kTopK; ++j) {
-                            const float w = J.topk_w[(size_t)m * kTopK + j];
-                            const int p = J.pos[(size_t)m * kTopK + j];
-                            acc_y = fmaf(w, J.o[(size_t)p * kH + c0 + c], acc_y);
+                            for (int j = 0; j < kTopK; ++j) acc_y = fmaf(pw[i][j], po[i][j], acc_y);
+                        } else {
+#pragma unroll
+                            for (int j = 0; j < kTopK; ++j) {
+                                const float w = J.topk_w[(size_t)m * kTopK + j];
+                                const int p = J.pos[(size_t)m * kTopK + j];
+                                acc_y = fmaf(w, J.o[(size_t)p * kH + c0 + c], acc_y);
+                            }
                         }
                         y[(size_t)m * J.ldo + c0 + c] = f32_to_bf16(acc_y);
                     }
