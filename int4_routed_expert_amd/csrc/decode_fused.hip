@@ -17,8 +17,10 @@
 //       sigmoid / max(sum, 2^-14), bloomery issue #632, design thread), then a
 //       stable sort of the <= 48 assignments in LDS;
 //   gate/up workgroups (the first 256): x is rotated in LDS (fwht128 per
-//       128-block, model card, table row "weights"; four waves per token, one
-//       power-of-two prescale per block, beside the top-6), then wave batches
+//       128-block, model card, table row "weights"; one task per 512-wide
+//       quarter of a token, dealt from the last wave down so that it runs
+//       beside the top-6 of the first waves; one power-of-two prescale per
+//       block), then wave batches
 //       of 2 (gate, up) row pairs of an active expert for all of its tokens,
 //       a = silu(g) * u in fp32 (sorted-position order), the next batch's codes
 //       in flight while one is multiplied;
