@@ -62,9 +62,10 @@ def parse():
 
 
 # stage -> (kernel name prefix, sources that define it) for the HBM-traffic
-# record, per launch sequence (1-8 tokens: two launches; 9-127: GEMVs;
-# from 128: MFMA tiles)
+# record, per launch sequence (1-8 tokens: two launches; 9-127: GEMVs, the
+# routing in one workgroup up to 48 tokens; from 128: MFMA tiles)
 FUSED_MAX_TOKENS = 8
+ROUTE_SMALL_MAX_TOKENS = 48
 GROUPED_MIN_TOKENS = 128
 STAGE_KERNELS_FUSED = {
     "router_shared_gateup": ("k_router_shared_small", ["decode_fused.hip", "gemv_ops.h", "token_ops.h"]),
@@ -90,7 +91,11 @@ STAGE_KERNELS_GROUPED = {
 def stage_kernels(T):
     if T <= FUSED_MAX_TOKENS:
         return STAGE_KERNELS_FUSED
-    return STAGE_KERNELS_GROUPED if T >= GROUPED_MIN_TOKENS else STAGE_KERNELS_GEMV
+    if T >= GROUPED_MIN_TOKENS:
+        return STAGE_KERNELS_GROUPED
+    if T <= ROUTE_SMALL_MAX_TOKENS:
+        return dict(STAGE_KERNELS_GEMV, topk_sort=("k_route_small", ["router.hip", "token_ops.h"]))
+    return STAGE_KERNELS_GEMV
 
 
 HERE = os.path.dirname(os.path.abspath(__file__))
