@@ -36,7 +36,8 @@
  *            multiplies the codes of K in [128g, 128g+128).
  *   shared_w bf16, 6,291,456 elements: gate [1024][2048], up [1024][2048],
  *            down [2048][1024].
- *   bias     fp32 [256] added to the logits, or NULL (Flint has none).
+ *   bias     fp32 [256] added to the logits (for the choice, and by default for
+ *            the sigmoid too), or NULL (Flint has none).
  *   y        bf16 [T][2048].
  *
  * Ownership and threading: the caller owns every buffer, including the
@@ -78,6 +79,18 @@ extern "C" {
  * MOE_W4_FUSED_MAX_TOKENS + 1 tokens on, one launch per step. */
 #define MOE_W4_FUSED_MAX_TOKENS 8
 
+/* Router policy of moe_w4_forward_policy (bloomery issue #632, design thread
+ * and its host-policy slice: the router rule distinguishes no normalisation,
+ * the legacy selected sum and the selected sum with the 2^-14 floor, and a
+ * router bias that is absent or used for the selection only).  One of the
+ * three normalisations, optionally OR-ed with MOE_W4_ROUTER_BIAS_SELECT_ONLY;
+ * 0 is Flint's own policy, the one moe_w4_forward uses. */
+#define MOE_W4_ROUTER_NORM_FLOOR 0       /* w_j = s_j / max(sum s, 2^-14)        */
+#define MOE_W4_ROUTER_NORM_SUM 1         /* w_j = s_j / sum s (legacy; no floor) */
+#define MOE_W4_ROUTER_NORM_NONE 2        /* w_j = s_j                            */
+#define MOE_W4_ROUTER_NORM_MASK 3
+#define MOE_W4_ROUTER_BIAS_SELECT_ONLY 4 /* s_j = sigmoid(R x) without the bias  */
+
 /* status codes */
 #define MOE_W4_OK 0
 #define MOE_W4_EINVAL (-1)     /* bad pointer, size, alignment or aliasing      */
@@ -100,6 +113,7 @@ extern "C" {
  *                         position, rows <= 96, 0} covering each expert's sorted
  *                         positions in order, ascending by expert; n_chunks i32 [1]
  *                         holds n.  (Written at every T; read only on that path.)
+ *   logits    f32 [T][256] router logits R x, without the bias
  *   sync      4096 bytes of counters for the fused decode launch; their
  *             contents on entry do not matter (the call clears them itself). */
 typedef struct moe_w4_ws_layout {
@@ -123,6 +137,16 @@ int moe_w4_workspace_layout(int64_t T, moe_w4_ws_layout *out);
 int moe_w4_forward(const void *x, const void *router_w, const void *codes, const void *scales,
                    const void *shared_w, int64_t T, void *y, const float *router_bias,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* moe_w4_forward with a router policy (MOE_W4_ROUTER_* above): the choice
+ * is always the 6 largest of (logit + bias); router_policy selects the
+ * normalisation of the sigmoid scores and whether the sigmoid sees the bias.
+ * With MOE_W4_ROUTER_NORM_SUM, six scores that all underflow to 0 in fp32
+ * give NaN weights (0/0).  EINVAL for an unknown policy; otherwise as
+ * moe_w4_forward. */
+int moe_w4_forward_policy(const void *x, const void *router_w, const void *codes, const void *scales,
+                          const void *shared_w, int64_t T, void *y, const float *router_bias, int router_policy,
+                          void *workspace, size_t workspace_bytes, void *stream);
 
 /* Number of timing points moe_w4_forward_profiled records. */
 int moe_w4_profile_points(void);

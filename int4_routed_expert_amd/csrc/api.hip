@@ -6,6 +6,12 @@
 #include "common.h"
 #include "launch.h"
 #include "moe_w4.h"
+#include "token_ops.h"
+
+static_assert(MOE_W4_ROUTER_NORM_FLOOR == moe_w4::kNormFloor && MOE_W4_ROUTER_NORM_SUM == moe_w4::kNormSum &&
+                  MOE_W4_ROUTER_NORM_NONE == moe_w4::kNormNone &&
+                  MOE_W4_ROUTER_BIAS_SELECT_ONLY == moe_w4::kBiasSelectOnly,
+              "router policy flags of the header and the kernels agree");
 
 using namespace moe_w4;
 
@@ -95,7 +101,7 @@ T_ *ws_at(void *ws, size_t off) { return reinterpret_cast<T_ *>(static_cast<char
 // bf16(rmsnorm(resid)), by the first launch, and the last adds y to resid.
 int run_forward(const void *x_, const void *router_w_, const void *codes_, const void *scales_,
                 const void *shared_w_, int64_t T64, void *y_, const float *bias, void *ws,
-                hipStream_t s, void *const *events, int n_events, float *resid = nullptr) {
+                hipStream_t s, void *const *events, int n_events, float *resid = nullptr, int policy = 0) {
     const int T = (int)T64;
     const moe_w4_ws_layout L = make_layout(T64);
     const uint16_t *x = static_cast<const uint16_t *>(x_);
@@ -120,7 +126,6 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     float *at_scale = ws_at<float>(ws, L.at_scale);
     uint16_t *hs = ws_at<uint16_t>(ws, L.hs);
     float *o = ws_at<float>(ws, L.o);
-    uint16_t *o_bf16 = ws_at<uint16_t>(ws, L.o);   // the grouped path keeps o in bf16
     float *z = ws_at<float>(ws, L.z);
     int *chunks = ws_at<int>(ws, L.chunks);
     int *n_chunks = ws_at<int>(ws, L.n_chunks);
@@ -155,13 +160,16 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     if (fused) {
         // two launches: router logits and shared h (which also clear the
         // counters), then the rest of the layer; the other stages are empty
-        MOE_STEP(launch_router_shared_small(x, resid, const_cast<uint16_t *>(x), T, router_w, bias, shared_w, logits,
-                                            hs, counters, s));
+        // the logits are written without the bias; the routing adds it
+        MOE_STEP(launch_router_shared_small(x, resid, const_cast<uint16_t *>(x), T, router_w, nullptr, shared_w,
+                                            logits, hs, counters, s));
         MOE_MARK();
         MOE_MARK();
         FusedDecodeArgs fa;
         fa.x = x;
         fa.logits = logits;
+        fa.router_bias = bias;
+        fa.router_policy = policy;
         fa.codes = codes;
         fa.scales = scales;
         fa.shared_down = shared_w + 2 * kSharedGateElems;
@@ -185,18 +193,18 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
         return MOE_W4_OK;
     }
     if (grouped)
-        MOE_STEP(launch_router_and_shared_gateup_dense(x, T, router_w, bias, logits, shared_w, hs, s));
+        MOE_STEP(launch_router_and_shared_gateup_dense(x, T, router_w, nullptr, logits, shared_w, hs, s));
     else
         // up to kRouteSmallMaxTokens tokens this launch also rotates x, and the
         // routing is one workgroup
-        MOE_STEP(launch_router_and_shared_gateup(x, T, router_w, bias, logits, shared_w, hs,
+        MOE_STEP(launch_router_and_shared_gateup(x, T, router_w, nullptr, logits, shared_w, hs,
                                                  small_route ? xt : nullptr, xt_scale, s));
     MOE_MARK();
     if (small_route) {
-        MOE_STEP(launch_route_small(logits, T, topk_idx, topk_w, offsets, perm, pos, n_active, active, chunks,
-                                    n_chunks, s));
+        MOE_STEP(launch_route_small(logits, T, bias, policy, topk_idx, topk_w, offsets, perm, pos, n_active, active,
+                                    chunks, n_chunks, s));
     } else {
-        MOE_STEP(launch_topk_rotate(logits, x, T, topk_idx, topk_w, xt, xt_scale, s));
+        MOE_STEP(launch_topk_rotate(logits, x, T, bias, policy, topk_idx, topk_w, xt, xt_scale, s));
         MOE_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, s));
     }
     MOE_MARK();
@@ -205,7 +213,7 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
         MOE_STEP(launch_gateup_mfma(codes, scales, xt, xt_scale, perm, chunks, n_chunks, T, at, at_scale, s));
         MOE_MARK();
         MOE_MARK();
-        MOE_STEP(launch_down_mfma(codes, scales, at, at_scale, chunks, n_chunks, T, o_bf16, s));
+        MOE_STEP(launch_down_mfma(codes, scales, at, at_scale, chunks, n_chunks, T, o, s));
         MOE_MARK();
     } else {
         MOE_STEP(launch_gateup_gemv(codes, scales, xt, xt_scale, perm, active, T, act, s));
@@ -217,7 +225,7 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     }
     if (grouped) {
         MOE_STEP(launch_shared_down_dense(shared_w, hs, T, z, s));
-        MOE_STEP(launch_combine(z, topk_w, pos, o_bf16, T, y, s));
+        MOE_STEP(launch_combine(z, topk_w, pos, o, T, y, s));
     } else
         MOE_STEP(launch_shared_down_combine(shared_w, hs, T, topk_w, pos, o, y, s));
     MOE_MARK();
@@ -258,6 +266,18 @@ int moe_w4_forward(const void *x, const void *router_w, const void *codes, const
     if (rc != MOE_W4_OK || T == 0) return rc;
     return run_forward(x, router_w, codes, scales, shared_w, T, y, router_bias, workspace,
                        static_cast<hipStream_t>(stream), nullptr, 0);
+}
+
+int moe_w4_forward_policy(const void *x, const void *router_w, const void *codes, const void *scales,
+                          const void *shared_w, int64_t T, void *y, const float *router_bias, int router_policy,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    if ((router_policy & ~(MOE_W4_ROUTER_NORM_MASK | MOE_W4_ROUTER_BIAS_SELECT_ONLY)) != 0 ||
+        (router_policy & MOE_W4_ROUTER_NORM_MASK) > MOE_W4_ROUTER_NORM_NONE)
+        return MOE_W4_EINVAL;
+    int rc = validate_forward(x, router_w, codes, scales, shared_w, T, y, router_bias, workspace, workspace_bytes);
+    if (rc != MOE_W4_OK || T == 0) return rc;
+    return run_forward(x, router_w, codes, scales, shared_w, T, y, router_bias, workspace,
+                       static_cast<hipStream_t>(stream), nullptr, 0, nullptr, router_policy);
 }
 
 int moe_w4_profile_points(void) { return kStages + 1; }

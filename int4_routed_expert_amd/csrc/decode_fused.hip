@@ -311,7 +311,7 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
     // ---- routing: wave t selects token t's six experts ----
     if (wave < T) {
         const int t = wave;
-        const Top6 sel = top6_wave(lv, lane);
+        const Top6 sel = top6_wave(lv, lane, RouterPolicy{A.router_bias, A.router_policy});
 #pragma unroll
         for (int j = 0; j < kTopK; ++j) {
             if (lane == j) {

@@ -257,7 +257,7 @@ void launch_shared_down_dense(const uint16_t *shared_w, const uint16_t *hs, int 
 // columns [32l, 32l + 32); every load of the token is in flight at once (the
 // gathers of an epilogue inside the GEMM tile were latency-bound).
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ z, const float *__restrict__ topk_w,
-                                                 const int *__restrict__ pos, const uint16_t *__restrict__ o, int T,
+                                                 const int *__restrict__ pos, const float *__restrict__ o, int T,
                                                  uint16_t *__restrict__ y) {
     const int t = blockIdx.x * 4 + wave_id();
     if (t >= T) return;
@@ -275,18 +275,14 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ z, co
     for (int i = 0; i < 8; ++i) acc[i] = zr[i];
 #pragma unroll
     for (int j = 0; j < kTopK; ++j) {
-        const uint4 *orow = reinterpret_cast<const uint4 *>(o + (size_t)p[j] * kH) + 4 * lane;
+        const float4 *orow = reinterpret_cast<const float4 *>(o + (size_t)p[j] * kH) + 8 * lane;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint4 v = orow[i];
-            acc[2 * i].x = fmaf(w[j], bf16lo(v.x), acc[2 * i].x);
-            acc[2 * i].y = fmaf(w[j], bf16hi(v.x), acc[2 * i].y);
-            acc[2 * i].z = fmaf(w[j], bf16lo(v.y), acc[2 * i].z);
-            acc[2 * i].w = fmaf(w[j], bf16hi(v.y), acc[2 * i].w);
-            acc[2 * i + 1].x = fmaf(w[j], bf16lo(v.z), acc[2 * i + 1].x);
-            acc[2 * i + 1].y = fmaf(w[j], bf16hi(v.z), acc[2 * i + 1].y);
-            acc[2 * i + 1].z = fmaf(w[j], bf16lo(v.w), acc[2 * i + 1].z);
-            acc[2 * i + 1].w = fmaf(w[j], bf16hi(v.w), acc[2 * i + 1].w);
+        for (int i = 0; i < 8; ++i) {
+            const float4 v = orow[i];
+            acc[i].x = fmaf(w[j], v.x, acc[i].x);
+            acc[i].y = fmaf(w[j], v.y, acc[i].y);
+            acc[i].z = fmaf(w[j], v.z, acc[i].z);
+            acc[i].w = fmaf(w[j], v.w, acc[i].w);
         }
     }
     uint32_t packed[16];
@@ -300,7 +296,7 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ z, co
     for (int i = 0; i < 4; ++i) yr[i] = make_uint4(packed[4 * i], packed[4 * i + 1], packed[4 * i + 2], packed[4 * i + 3]);
 }
 
-void launch_combine(const float *z, const float *topk_w, const int *pos, const uint16_t *o, int T, uint16_t *y,
+void launch_combine(const float *z, const float *topk_w, const int *pos, const float *o, int T, uint16_t *y,
                     hipStream_t s) {
     hipLaunchKernelGGL(k_combine, dim3((T + 3) / 4), dim3(256), 0, s, z, topk_w, pos, o, T, y);
 }

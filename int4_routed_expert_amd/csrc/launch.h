@@ -24,7 +24,9 @@ constexpr int kFusedCounters = 16;        // replicas of the completion counter,
 constexpr int kFusedCounterStride = 64;   // one per 256 bytes of `counters`
 struct FusedDecodeArgs {
     const uint16_t *x;
-    const float *logits;
+    const float *logits;           // without the router bias
+    const float *router_bias;      // fp32 [256] or null
+    int router_policy;             // MOE_W4_ROUTER_* flags
     const uint8_t *codes;
     const uint16_t *scales;
     const uint16_t *shared_down;   // [2048][1024] bf16
@@ -51,10 +53,12 @@ void launch_router_shared_small(const uint16_t *x, const float *resid, uint16_t 
                                 uint16_t *hs, int *counters, hipStream_t s);
 void launch_decode_fused(const FusedDecodeArgs &args, hipStream_t s);
 
-// Per token: top-6 of the logits, renormalised sigmoid weights, and the
-// Hadamard-rotated fp16 copy of x (with its power-of-two scale).
-void launch_topk_rotate(const float *logits, const uint16_t *x, int T, int *topk_idx, float *topk_w,
-                        uint32_t *xt, float *xt_scale, hipStream_t s);
+// Per token: top-6 of the logits (+ bias, if any), the sigmoid weights
+// normalised as the router policy says (bias, policy: MOE_W4_ROUTER_* flags),
+// and the Hadamard-rotated fp16 copy of x (with its power-of-two scale).  The
+// router launches write the logits without the bias.
+void launch_topk_rotate(const float *logits, const uint16_t *x, int T, const float *bias, int policy,
+                        int *topk_idx, float *topk_w, uint32_t *xt, float *xt_scale, hipStream_t s);
 // Stable counting sort of the 6T assignments by expert (one workgroup).
 // slots: int[256][8] records {expert, first sorted position, count, first
 // token, second token, 0, 0, 0}, one per expert with tokens, then expert -1.
@@ -66,8 +70,9 @@ void launch_sort(const int *topk_idx, int T, int *offsets, int *perm, int *pos, 
 // a time; the sort ranks the <= 288 assignments in LDS), for up to
 // kRouteSmallMaxTokens tokens whose rotated x is written elsewhere.
 constexpr int kRouteSmallMaxTokens = 48;
-void launch_route_small(const float *logits, int T, int *topk_idx, float *topk_w, int *offsets, int *perm,
-                        int *pos, int *n_active, int *slots, int *chunks, int *n_chunks, hipStream_t s);
+void launch_route_small(const float *logits, int T, const float *bias, int policy, int *topk_idx, float *topk_w,
+                        int *offsets, int *perm, int *pos, int *n_active, int *slots, int *chunks, int *n_chunks,
+                        hipStream_t s);
 
 // Routed experts, GEMV form (few tokens per expert), driven by the slot records.
 void launch_gateup_gemv(const uint8_t *codes, const uint16_t *scales, const uint32_t *xt,
@@ -85,9 +90,8 @@ int max_chunks(int T);
 void launch_gateup_mfma(const uint8_t *codes, const uint16_t *scales, const uint32_t *xt, const float *xt_scale,
                         const int *perm, const int *chunks, const int *n_chunks, int T, uint32_t *at,
                         float *at_scale, hipStream_t s);
-// o in bf16 on this path
 void launch_down_mfma(const uint8_t *codes, const uint16_t *scales, const uint32_t *at, const float *at_scale,
-                      const int *chunks, const int *n_chunks, int T, uint16_t *o, hipStream_t s);
+                      const int *chunks, const int *n_chunks, int T, float *o, hipStream_t s);
 
 // Shared expert down projection fused with the combine:
 // y = bf16(h Wsd^T + sum_j w_j o[pos[6t+j]]), slots in order.
@@ -99,7 +103,7 @@ void launch_router_and_shared_gateup_dense(const uint16_t *x, int T, const uint1
                                            float *logits, const uint16_t *shared_w, uint16_t *hs, hipStream_t s);
 // shared down projection z = h Wsd^T (fp32), then the combine as its own pass
 void launch_shared_down_dense(const uint16_t *shared_w, const uint16_t *hs, int T, float *z, hipStream_t s);
-void launch_combine(const float *z, const float *topk_w, const int *pos, const uint16_t *o, int T, uint16_t *y,
+void launch_combine(const float *z, const float *topk_w, const int *pos, const float *o, int T, uint16_t *y,
                     hipStream_t s);
 
 // Stack glue: x_bf16 = bf16(rmsnorm(resid)); resid += f32(y).

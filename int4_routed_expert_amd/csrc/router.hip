@@ -18,7 +18,7 @@ __global__ __launch_bounds__(256) void k_topk_rotate(const float *__restrict__ l
                                                      int *__restrict__ topk_idx,
                                                      float *__restrict__ topk_w,
                                                      uint32_t *__restrict__ xt,
-                                                     float *__restrict__ xt_scale) {
+                                                     float *__restrict__ xt_scale, RouterPolicy rp) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * 4 + wave;
     if (t >= T) return;
@@ -32,7 +32,7 @@ __global__ __launch_bounds__(256) void k_topk_rotate(const float *__restrict__ l
         for (int i = 0; i < 4; ++i) xq[i] = xp[i];
     }
     const float4 lv = reinterpret_cast<const float4 *>(logits + (size_t)t * kE)[lane];
-    const Top6 sel = top6_wave(lv, lane);
+    const Top6 sel = top6_wave(lv, lane, rp);
 #pragma unroll
     for (int j = 0; j < kTopK; ++j) {
         if (lane == j) {
@@ -44,10 +44,10 @@ __global__ __launch_bounds__(256) void k_topk_rotate(const float *__restrict__ l
     if (lane == 0) xt_scale[t] = ldexpf(1.0f, sh);
 }
 
-void launch_topk_rotate(const float *logits, const uint16_t *x, int T, int *topk_idx, float *topk_w,
-                        uint32_t *xt, float *xt_scale, hipStream_t s) {
+void launch_topk_rotate(const float *logits, const uint16_t *x, int T, const float *bias, int policy,
+                        int *topk_idx, float *topk_w, uint32_t *xt, float *xt_scale, hipStream_t s) {
     hipLaunchKernelGGL(k_topk_rotate, dim3((T + 3) / 4), dim3(256), 0, s, logits, x, T, topk_idx,
-                       topk_w, xt, xt_scale);
+                       topk_w, xt, xt_scale, RouterPolicy{bias, policy});
 }
 
 // ---------------------------------------------------------------------------
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(1024) void k_route_small(const float *__restrict__ 
                                                       int *__restrict__ offsets, int *__restrict__ perm,
                                                       int *__restrict__ pos, int *__restrict__ n_active,
                                                       int *__restrict__ slots, int4 *__restrict__ chunks,
-                                                      int *__restrict__ n_chunks) {
+                                                      int *__restrict__ n_chunks, RouterPolicy rp) {
     constexpr int kPerWave = (kRouteSmallMaxTokens + kSortWaves - 1) / kSortWaves;
     constexpr int kMaxChunks = (kTopK * kRouteSmallMaxTokens + 63) / 64;
     __shared__ int sel[kTopK * kRouteSmallMaxTokens];     // expert of assignment a
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(1024) void k_route_small(const float *__restrict__ 
     for (int i = 0; i < kPerWave; ++i) {
         const int t = wave + kSortWaves * i;
         if (t < T) {
-            const Top6 r = top6_wave(lv[i], lane);
+            const Top6 r = top6_wave(lv[i], lane, rp);
 #pragma unroll
             for (int j = 0; j < kTopK; ++j) {
                 if (lane == j) {
@@ -375,10 +375,11 @@ __global__ __launch_bounds__(1024) void k_route_small(const float *__restrict__ 
     }
 }
 
-void launch_route_small(const float *logits, int T, int *topk_idx, float *topk_w, int *offsets, int *perm,
-                        int *pos, int *n_active, int *slots, int *chunks, int *n_chunks, hipStream_t s) {
+void launch_route_small(const float *logits, int T, const float *bias, int policy, int *topk_idx, float *topk_w,
+                        int *offsets, int *perm, int *pos, int *n_active, int *slots, int *chunks, int *n_chunks,
+                        hipStream_t s) {
     hipLaunchKernelGGL(k_route_small, dim3(1), dim3(1024), 0, s, logits, T, topk_idx, topk_w, offsets, perm, pos,
-                       n_active, slots, reinterpret_cast<int4 *>(chunks), n_chunks);
+                       n_active, slots, reinterpret_cast<int4 *>(chunks), n_chunks, RouterPolicy{bias, policy});
 }
 
 void launch_sort(const int *topk_idx, int T, int *offsets, int *perm, int *pos, int *n_active,

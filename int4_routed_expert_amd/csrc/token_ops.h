@@ -104,10 +104,27 @@ __device__ __forceinline__ bool ahead(uint32_t ka, int ia, uint32_t kb, int ib) 
     return ka > kb || (ka == kb && ia < ib);
 }
 
-__device__ __forceinline__ Top6 top6_wave(float4 lv, int lane) {
+// Router policy (bloomery issue #632, design thread and its host-policy
+// slice: the router rule distinguishes no normalisation, the legacy selected
+// sum and the selected sum with the 2^-14 floor, and a bias that is absent or
+// used for selection only).  flags: bits 0-1 the normalisation (kNormFloor,
+// kNormSum, kNormNone), bit 2 kBiasSelectOnly.  bias: fp32 [256] or null.
+constexpr int kNormFloor = 0, kNormSum = 1, kNormNone = 2, kBiasSelectOnly = 4;
+struct RouterPolicy {
+    const float *bias;
+    int flags;
+};
+
+__device__ __forceinline__ Top6 top6_wave(float4 lv, int lane, RouterPolicy rp) {
+    // the choice is made on the fp32 logit plus the bias, if any
+    float4 kv = lv;
+    if (rp.bias) {
+        const float4 b = reinterpret_cast<const float4 *>(rp.bias)[lane];
+        kv.x += b.x; kv.y += b.y; kv.z += b.z; kv.w += b.w;
+    }
     // each lane sorts its 4 (key, expert) pairs (a 5-comparator network on the
     // total order above), then six rounds take the largest head over the wave
-    uint32_t k[4] = {order_key(lv.x), order_key(lv.y), order_key(lv.z), order_key(lv.w)};
+    uint32_t k[4] = {order_key(kv.x), order_key(kv.y), order_key(kv.z), order_key(kv.w)};
     int ix[4] = {4 * lane, 4 * lane + 1, 4 * lane + 2, 4 * lane + 3};
     auto cswap = [&](int a, int b) {
         if (ahead(k[b], ix[b], k[a], ix[a])) {
@@ -131,16 +148,30 @@ __device__ __forceinline__ Top6 top6_wave(float4 lv, int lane) {
         sel_k[j] = K;
         if (lane == L) ++head;
     }
-    // sigmoids side by side (lane j < 6), summed in slot order
+    // sigmoids side by side (lane j < 6), summed in slot order; the sigmoid
+    // takes the selection key, or with a selection-only bias the logit itself
     uint32_t mine = sel_k[0];
+    int mine_e = r.e[0];
 #pragma unroll
     for (int j = 1; j < kTopK; ++j)
-        if (lane == j) mine = sel_k[j];
-    const float sig = 1.0f / (1.0f + expf(-key_value(mine)));
+        if (lane == j) {
+            mine = sel_k[j];
+            mine_e = r.e[j];
+        }
+    float lw = key_value(mine);
+    if (rp.flags & kBiasSelectOnly) {
+        const int src = mine_e >> 2, q = mine_e & 3;   // lane src holds logits 4 src .. 4 src + 3
+        const float c0 = __shfl(lv.x, src, kWave), c1 = __shfl(lv.y, src, kWave);
+        const float c2 = __shfl(lv.z, src, kWave), c3 = __shfl(lv.w, src, kWave);
+        lw = q == 0 ? c0 : q == 1 ? c1 : q == 2 ? c2 : c3;
+    }
+    const float sig = 1.0f / (1.0f + expf(-lw));
     float ssum = 0.0f;
 #pragma unroll
     for (int j = 0; j < kTopK; ++j) ssum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(sig), j));
-    const float denom = fmaxf(ssum, 6.103515625e-05f);   // 2^-14
+    const int norm = rp.flags & 3;
+    const float denom = norm == kNormFloor ? fmaxf(ssum, 6.103515625e-05f)   // 2^-14
+                        : norm == kNormSum ? ssum : 1.0f;
     const float w = sig / denom;
 #pragma unroll
     for (int j = 0; j < kTopK; ++j) r.w[j] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), j));

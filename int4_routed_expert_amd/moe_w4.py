@@ -26,6 +26,9 @@ SCALES_PER_EXPERT = 24576
 SHARED_ELEMS = 6291456
 MAX_TOKENS = 1048576
 FUSED_MAX_TOKENS = 8
+# router policy flags of moe_w4_forward_policy (include/moe_w4.h)
+ROUTER_NORM_FLOOR, ROUTER_NORM_SUM, ROUTER_NORM_NONE, ROUTER_NORM_MASK = 0, 1, 2, 3
+ROUTER_BIAS_SELECT_ONLY = 4
 
 OK, EINVAL, EWORKSPACE, EDEVICE = 0, -1, -2, -3
 
@@ -54,6 +57,7 @@ _sig = {
     "moe_w4_workspace_bytes": (_sz, [_i64]),
     "moe_w4_workspace_layout": (_int, [_i64, ctypes.POINTER(WsLayout)]),
     "moe_w4_forward": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "moe_w4_forward_policy": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _int, _vp, _sz, _vp]),
     "moe_w4_profile_points": (_int, []),
     "moe_w4_profile_point_name": (ctypes.c_char_p, [_int]),
     "moe_w4_forward_profiled": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp,
@@ -127,6 +131,17 @@ def moe_w4_forward(x, router_w, codes, scales, shared_w, y, workspace, router_bi
                              _ptr(y), _ptr(router_bias), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "moe_w4_forward")
+    return st
+
+
+def moe_w4_forward_policy(x, router_w, codes, scales, shared_w, y, workspace, router_bias=None,
+                          router_policy=ROUTER_NORM_FLOOR, stream=None, T=None) -> int:
+    """moe_w4_forward with a router policy (ROUTER_* flags)."""
+    T = x.shape[0] if T is None else T
+    st = _lib.moe_w4_forward_policy(_ptr(x), _ptr(router_w), _ptr(codes), _ptr(scales), _ptr(shared_w), T,
+                                    _ptr(y), _ptr(router_bias), int(router_policy), _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "moe_w4_forward_policy")
     return st
 
 

@@ -36,6 +36,14 @@ Readings where the pages are silent (each is listed in the design doc too):
   flagged as a near-tie.
 * The optional router bias is added to the logit before selection and
   before the sigmoid (a synthetic skew; Flint itself has none).
+* Router policy variants (bloomery issue #632, design thread and the
+  follow-up host-policy slice: the router description distinguishes no
+  normalisation, the legacy selected-sum and the selected-sum with the
+  2**-14 floor, and a bias that is absent or used for selection only):
+  norm "floor" (Flint, the default) divides by max(sum, 2**-14), "sum"
+  divides by the plain sum, "none" keeps the sigmoid scores; bias_mode
+  "logit" (default) adds the bias to the logit for both the choice and the
+  sigmoid, "select" adds it for the choice only.
 * silu(v) = v / (1 + exp(-v)); the shared expert is added with weight 1.
 * y is rounded once, fp64 -> bf16 round-to-nearest-even.
 
@@ -170,18 +178,28 @@ def shared_planes(shared_bits: np.ndarray):
 
 
 # ---------------------------------------------------------------- router
-def route(x: np.ndarray, router_bits: np.ndarray, bias=None):
-    """Sigmoid top-6 router with the 2**-14 floor on the renormaliser.
+NORMS = ("floor", "sum", "none")
+BIAS_MODES = ("logit", "select")
+
+
+def route(x: np.ndarray, router_bits: np.ndarray, bias=None, norm="floor", bias_mode="logit"):
+    """Sigmoid top-6 router; by default the renormaliser has the 2**-14 floor.
 
     x: float64 [T, K] (already widened); router_bits: bf16 bits [n_experts, K]
-    (256 x 2048 for Flint; any n_experts >= 7 works).  Returns a dict with the fp64
-    logits, the fp32 logits the choice is made on, topk_idx [T, 6],
-    topk_w [T, 6] (float64), the 6th-7th gap and the near-tie flags.
+    (256 x 2048 for Flint; any n_experts >= 7 works).  norm / bias_mode: the
+    policy variants above.  Returns a dict with the fp64 logits the choice is
+    made on, their fp32 rounding, the logits the sigmoid takes (logits_w),
+    topk_idx [T, 6], topk_w [T, 6] (float64), the 6th-7th gap and the
+    near-tie flags.
     """
+    if norm not in NORMS or bias_mode not in BIAS_MODES:
+        raise ValueError("unknown router policy")
     R = bf16_to_f64(router_bits)                      # [256, 2048]
-    logits = x @ R.T                                  # [T, 256]
+    unbiased = x @ R.T                                # [T, 256]
+    logits = unbiased
     if bias is not None:
         logits = logits + np.asarray(bias, dtype=np.float64)[None, :]
+    logits_w = unbiased if bias_mode == "select" else logits
     l32 = f32_round(logits)
     T, n_exp = logits.shape
     idx = np.empty((T, K_TOP), dtype=np.int32)
@@ -193,11 +211,15 @@ def route(x: np.ndarray, router_bits: np.ndarray, bias=None):
         idx[t] = order[:K_TOP]
         srt = np.sort(logits[t])[::-1]
         gap[t] = srt[K_TOP - 1] - srt[K_TOP]
-    sel = np.take_along_axis(logits, idx.astype(np.int64), axis=1)
+    sel = np.take_along_axis(logits_w, idx.astype(np.int64), axis=1)
     sig = sigmoid(sel)
-    denom = np.maximum(sig.sum(axis=1, keepdims=True), WEIGHT_FLOOR)
-    w = sig / denom
-    return dict(logits=logits, logits32=l32, topk_idx=idx, topk_w=w,
+    if norm == "floor":
+        w = sig / np.maximum(sig.sum(axis=1, keepdims=True), WEIGHT_FLOOR)
+    elif norm == "sum":
+        w = sig / sig.sum(axis=1, keepdims=True)
+    else:
+        w = sig
+    return dict(logits=logits, logits32=l32, logits_w=logits_w, topk_idx=idx, topk_w=w,
                 gap=gap, near_tie=gap <= NEAR_TIE_GAP)
 
 
@@ -230,18 +252,20 @@ def shared_expert(x: np.ndarray, shared_bits: np.ndarray) -> np.ndarray:
     return (silu(x @ sg.T) * (x @ su.T)) @ sd.T
 
 
-def moe_layer(x_bits, router_bits, expert_blobs, shared_bits, bias=None, tokens=None):
+def moe_layer(x_bits, router_bits, expert_blobs, shared_bits, bias=None, tokens=None, norm="floor",
+              bias_mode="logit"):
     """The layer: y = bf16( sum_j w_j * E_{e_j}(x) + S(x) ).
 
     x_bits: bf16 bits [T, 2048]; router_bits: bf16 bits [256, 2048];
     expert_blobs(e) -> (code bytes [1572864], scale bits [24576]) in the
     library layout; shared_bits: bf16 bits [6291456]; bias: fp32 [256] or None.
     tokens: optional subset of token rows whose expert outputs and y are
-    computed (routing and the sort always cover all T tokens).
+    computed (routing and the sort always cover all T tokens).  norm,
+    bias_mode: the router policy (see route).
     """
     x = bf16_to_f64(x_bits)
     T = x.shape[0]
-    rt = route(x, router_bits, bias)
+    rt = route(x, router_bits, bias, norm, bias_mode)
     srt = sort_assignments(rt["topk_idx"])
     rows = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
     xt = rotate_blocks(x[rows])

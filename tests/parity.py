@@ -59,7 +59,7 @@ def from_dev_u16(t):
     return t.cpu().numpy().view(np.uint16)
 
 
-def run_gpu(m, x_bits, w, bias=None, ws=None, poison=False):
+def run_gpu(m, x_bits, w, bias=None, ws=None, poison=False, policy=None):
     """Run one forward; returns y bits and the routing results read from the workspace."""
     T = x_bits.shape[0]
     x = to_dev_u16(x_bits)
@@ -69,7 +69,11 @@ def run_gpu(m, x_bits, w, bias=None, ws=None, poison=False):
     if poison:
         ws.fill_(0xFF)
     b = None if bias is None else torch.from_numpy(np.asarray(bias, dtype=np.float32)).cuda()
-    m.moe_w4_forward(x, w["router_w"], w["codes"], w["scales"], w["shared_w"], y, ws, router_bias=b)
+    if policy is None:
+        m.moe_w4_forward(x, w["router_w"], w["codes"], w["scales"], w["shared_w"], y, ws, router_bias=b)
+    else:
+        m.moe_w4_forward_policy(x, w["router_w"], w["codes"], w["scales"], w["shared_w"], y, ws, router_bias=b,
+                                router_policy=policy)
     torch.cuda.synchronize()
     out = dict(y_bits=from_dev_u16(y))
     out["topk_idx"] = m.ws_view(ws, T, "topk_idx", torch.int32, 6 * T).cpu().numpy().reshape(T, 6)

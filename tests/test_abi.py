@@ -40,7 +40,8 @@ def test_every_declared_symbol_is_exported(m):
 def test_header_constants_match_the_binding(m):
     defines = dict(re.findall(r"#define MOE_W4_(\w+) \(?(-?\d+)\)?", open(HEADER).read()))
     names = ["HIDDEN", "EXPERTS", "TOPK", "INTER", "SHARED_INTER", "GROUP", "CODE_BYTES_PER_EXPERT",
-             "SCALES_PER_EXPERT", "SHARED_ELEMS", "MAX_TOKENS", "FUSED_MAX_TOKENS"]
+             "SCALES_PER_EXPERT", "SHARED_ELEMS", "MAX_TOKENS", "FUSED_MAX_TOKENS", "ROUTER_NORM_FLOOR",
+             "ROUTER_NORM_SUM", "ROUTER_NORM_NONE", "ROUTER_NORM_MASK", "ROUTER_BIAS_SELECT_ONLY"]
     for n in names:
         assert int(defines[n]) == getattr(m, n), n
 
@@ -120,6 +121,19 @@ def test_profiled_and_stack_validation(m):
     assert lib.moe_w4_generate_x(0, 0, 4, 0x1001, None) == m.EINVAL
     assert lib.moe_w4_generate_layer(0, -1, None, None, None, None, None) == m.EINVAL
     assert lib.moe_w4_generate_layer(0, 0, 0x1002, None, None, None, None) == m.EINVAL
+
+
+def test_router_policy_validation(m):
+    lib = m._lib
+    args = (0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000)
+    ws_bytes = m.moe_w4_workspace_bytes(4)
+    for bad in (3, 7, 8, -1, 1 << 20):
+        assert lib.moe_w4_forward_policy(*args, 4, 0x60000000, None, bad, 0x70000000, ws_bytes, None) == m.EINVAL
+    for ok in (0, 1, 2, 4, 5, 6):
+        # valid policies get as far as the usual checks: T == 0 returns OK
+        assert lib.moe_w4_forward_policy(*args, 0, 0x60000000, None, ok, 0x70000000, ws_bytes, None) == m.OK
+        assert lib.moe_w4_forward_policy(None, *args[1:], 4, 0x60000000, None, ok, 0x70000000, ws_bytes,
+                                         None) == m.EINVAL
 
 
 def test_status_strings(m):

@@ -32,10 +32,11 @@ def layer0(m):
     return w
 
 
-def oracle_layer(x_bits, bias=None, tokens=None, seed=0, layer=0, scale_log2=0, router=None):
+def oracle_layer(x_bits, bias=None, tokens=None, seed=0, layer=0, scale_log2=0, router=None, norm="floor",
+                 bias_mode="logit"):
     R = P.host_router(seed, layer) if router is None else router
     return O.moe_layer(x_bits, R, P.host_blobs(seed, layer, scale_log2), P.host_shared(seed, layer),
-                       bias=bias, tokens=tokens)
+                       bias=bias, tokens=tokens, norm=norm, bias_mode=bias_mode)
 
 
 def report(label, s):
@@ -190,6 +191,43 @@ def test_all_tie_router(m, layer0, T):
     np.testing.assert_allclose(g["topk_w"], 1 / 6, rtol=1e-6)
     ref = oracle_layer(x, router=np.zeros((256, 2048), dtype=np.uint16))
     report("all-tie router", P.compare(g, ref, label="all-tie router"))
+
+
+# ------------------------------------------------------------ router policies
+POLICIES = [("floor", "select"), ("sum", "logit"), ("sum", "select"), ("none", "logit"), ("none", "select")]
+
+
+def policy_flags(m, norm, bias_mode):
+    f = {"floor": m.ROUTER_NORM_FLOOR, "sum": m.ROUTER_NORM_SUM, "none": m.ROUTER_NORM_NONE}[norm]
+    return f | (m.ROUTER_BIAS_SELECT_ONLY if bias_mode == "select" else 0)
+
+
+@pytest.mark.parametrize("T", [3, 32, 128])
+@pytest.mark.parametrize("norm,bias_mode", POLICIES)
+def test_router_policies(m, layer0, T, norm, bias_mode):
+    """Every router policy on each launch sequence (two launches, GEMVs, MFMA
+    tiles), with a bias that favours some experts and disfavours others."""
+    x = synth.gen_x(300 + T, T)
+    rng = np.random.default_rng(T)
+    bias = rng.normal(0.0, 1.0, 256).astype(np.float32)
+    g = P.run_gpu(m, x, layer0, bias=bias, policy=policy_flags(m, norm, bias_mode))
+    ref = oracle_layer(x, bias=bias, norm=norm, bias_mode=bias_mode)
+    report(f"policy {norm}/{bias_mode} T={T}", P.compare(g, ref, label=f"policy {norm}/{bias_mode} T={T}"))
+    if norm == "none":
+        # no renormalisation: the weights are the sigmoid scores themselves
+        lw = ref["logits_w"][np.arange(T)[:, None], g["topk_idx"]]
+        np.testing.assert_allclose(g["topk_w"], 1.0 / (1.0 + np.exp(-lw)), rtol=1e-5)
+
+
+def test_router_policy_sum_without_floor(m, layer0):
+    """Below the floor the legacy selected-sum still renormalises to 1."""
+    T = 5
+    x = synth.gen_x(202, T)
+    bias = np.full(256, -30.0, dtype=np.float32)
+    g = P.run_gpu(m, x, layer0, bias=bias, policy=m.ROUTER_NORM_SUM)
+    ref = oracle_layer(x, bias=bias, norm="sum")
+    np.testing.assert_allclose(g["topk_w"].sum(axis=1), 1.0, rtol=1e-5)
+    report("legacy sum below the floor", P.compare(g, ref, label="legacy sum below the floor"))
 
 
 def test_weight_floor(m, layer0):

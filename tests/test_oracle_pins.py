@@ -301,6 +301,85 @@ def test_weight_floor():
     assert set(rt2["topk_idx"][0][:3]) == {7, 100, 200}
 
 
+def _policy_case(seed, n_exp=10, k=32, T=3):
+    rng = np.random.default_rng(seed)
+    x = O.bf16_to_f64(synth.f32_to_bf16_bits(rng.standard_normal((T, k)).astype(np.float32)))
+    R = synth.f32_to_bf16_bits(rng.standard_normal((n_exp, k)).astype(np.float32))
+    # the logits recomputed here by nested loops, independent of route()
+    Rw = widen(R)
+    lg = np.array([[sum(x[t, i] * Rw[e, i] for i in range(k)) for e in range(n_exp)] for t in range(T)])
+    return x, R, lg
+
+
+def _sig(v):
+    return 1.0 / (1.0 + np.exp(-np.asarray(v, dtype=np.float64)))
+
+
+def test_router_policy_plain_sum_and_no_normalisation():
+    """Legacy selected-sum and no normalisation (bloomery #632, host-policy
+    slice): above the floor the selected-sum equals the floored one; "none"
+    keeps the six sigmoid scores as they are."""
+    x, R, lg = _policy_case(20)
+    fl = O.route(x, R, norm="floor")
+    sm = O.route(x, R, norm="sum")
+    nn = O.route(x, R, norm="none")
+    for t in range(x.shape[0]):
+        sel = _brute_top6(O.f32_round(lg[t]))
+        assert list(sm["topk_idx"][t]) == sel and list(nn["topk_idx"][t]) == sel
+        s6 = _sig(lg[t, sel])
+        np.testing.assert_allclose(nn["topk_w"][t], s6, rtol=1e-13)
+        np.testing.assert_allclose(sm["topk_w"][t], s6 / s6.sum(), rtol=1e-13)
+        assert sm["topk_w"][t].sum() == pytest.approx(1.0, abs=1e-14)
+    np.testing.assert_array_equal(sm["topk_w"], fl["topk_w"])
+
+
+def test_router_policy_sum_without_floor_at_tiny_scores():
+    """With every logit near -30 the six scores sum below 2**-14: the floored
+    policy gives weights far below 1, the legacy sum still renormalises to 1."""
+    x, R, lg = _policy_case(21)
+    bias = np.full(10, -30.0, dtype=np.float32)
+    fl = O.route(x, R, bias, norm="floor")
+    sm = O.route(x, R, bias, norm="sum")
+    for t in range(x.shape[0]):
+        sel = _brute_top6(O.f32_round(lg[t] - 30.0))
+        s6 = _sig(lg[t, sel] - 30.0)
+        assert s6.sum() < 2 ** -14
+        np.testing.assert_allclose(fl["topk_w"][t], s6 * 2 ** 14, rtol=1e-12)
+        np.testing.assert_allclose(sm["topk_w"][t], s6 / s6.sum(), rtol=1e-12)
+        assert sm["topk_w"][t].sum() == pytest.approx(1.0, abs=1e-12)
+        assert fl["topk_w"][t].sum() < 1e-3
+
+
+def test_router_bias_for_selection_only():
+    """A selection-only bias changes which experts are chosen, never their
+    scores: a constant bias leaves the route exactly as without one, and a
+    large bias on three experts puts them first with unbiased sigmoid weights."""
+    x, R, lg = _policy_case(22)
+    plain = O.route(x, R)
+    c = np.full(10, 1.5, dtype=np.float32)
+    sel_c = O.route(x, R, c, bias_mode="select")
+    log_c = O.route(x, R, c, bias_mode="logit")
+    np.testing.assert_array_equal(sel_c["topk_idx"], plain["topk_idx"])
+    np.testing.assert_allclose(sel_c["topk_w"], plain["topk_w"], rtol=1e-14)
+    assert np.abs(log_c["topk_w"] - plain["topk_w"]).max() > 1e-4   # the logit-mode bias moves the weights
+    b = np.zeros(10, dtype=np.float32)
+    b[[2, 5, 9]] = 50.0
+    rt = O.route(x, R, b, bias_mode="select")
+    for t in range(x.shape[0]):
+        sel = _brute_top6(O.f32_round(lg[t] + b))
+        assert list(rt["topk_idx"][t]) == sel and set(sel[:3]) == {2, 5, 9}
+        s6 = _sig(lg[t, sel])
+        np.testing.assert_allclose(rt["topk_w"][t], s6 / s6.sum(), rtol=1e-12)
+
+
+def test_router_policy_rejects_unknown_names():
+    x, R, _ = _policy_case(23)
+    with pytest.raises(ValueError):
+        O.route(x, R, norm="softmax")
+    with pytest.raises(ValueError):
+        O.route(x, R, bias_mode="both")
+
+
 def test_near_tie_flag_uses_the_6th_7th_gap():
     x, R, _ = small_layer(11, 64)
     rt = O.route(O.bf16_to_f64(x), R)
