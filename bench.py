@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="decode_t32",
-                    choices=["decode_t1", "decode_t32", "prefill_t2048", "prefill_t2048_skew", "stack_t1", "stack_t8"])
+                    choices=["decode_t1", "decode_t32", "prefill_t2048", "prefill_t2048_skew", "stack_t1", "stack_t8",
+                             "pack_layer"])
     ap.add_argument("--layers", type=int, default=0, help="distinct layers rotated through (0 = auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--eager", action="store_true",
@@ -219,6 +220,62 @@ def cpu_baseline(cfg, T, x_bits, bias, budget_s):
                       f"{T} tokens included), {per_rep:.2f} s each"}
 
 
+def bench_pack(a):
+    """The packer on one layer's 256 experts: bf16 weights (seeded, N(0, 0.02)) ->
+    int4 codes and bf16 scales.  A step is one moe_w4_pack_experts call over the
+    whole bank; the roofline is HBM (bf16 in, codes and scales out)."""
+    import torch
+    from int4_routed_expert_amd import moe_w4 as m
+    from oracle import moe_oracle as O
+    n = 256
+    g = torch.Generator(device="cuda").manual_seed(5)
+    w = (torch.randn((n, m.EXPERT_WEIGHTS), generator=g, device="cuda") * 0.02).to(torch.bfloat16).view(torch.int16)
+    codes = torch.empty((n, m.CODE_BYTES_PER_EXPERT), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((n, m.SCALES_PER_EXPERT), dtype=torch.int16, device="cuda")
+    for _ in range(a.warmup):
+        m.moe_w4_pack_experts(w, codes, scales)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(a.steps):
+        m.moe_w4_pack_experts(w, codes, scales)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / a.steps
+    nbytes = n * (m.EXPERT_WEIGHTS * 2 + m.CODE_BYTES_PER_EXPERT + m.SCALES_PER_EXPERT * 2)
+    # the packer launches on torch's current stream, where these events are recorded
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    for e0, e1 in ev:
+        e0.record()
+        m.moe_w4_pack_experts(w, codes, scales)
+        e1.record()
+    torch.cuda.synchronize()
+    kern_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    achieved = nbytes / (kern_ms * 1e-3) / 1e9
+    result = {"metric": "packer: experts/s (bf16 experts -> fwht128 int4 codes + bf16 scales)",
+              "value": n / (ms * 1e-3), "unit": "experts/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+              "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+              "data": "synthetic", "config": {"workload": "pack_layer: 256 experts of one layer, bf16 N(0, 0.02), "
+                                                          "torch seed 5", "experts": n},
+              "roofline": {"bound": "hbm", "kernel": "k_pack_groups", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                           "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                           "algorithmic_bytes": nbytes, "kernel_us": kern_ms * 1e3}}
+    if not a.no_cpu:
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        except Exception:
+            cores = os.cpu_count()
+        sample = w[:2].cpu().numpy().view(np.uint16)
+        reps, elapsed = 0, 0.0
+        while elapsed < a.cpu_seconds and reps < 20:
+            t0 = time.perf_counter()
+            O.pack_expert_bank(sample)
+            elapsed += time.perf_counter() - t0
+            reps += 1
+        result["cpu_baseline"] = {"value": 2 * reps / elapsed, "unit": "experts/s", "cores": int(cores),
+                                  "kind": "oracle", "sample": f"{reps} oracle packs of 2 of the 256 experts"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     a = parse()
     if a.pmc_summary:
@@ -233,6 +290,9 @@ def main():
         sys.exit(2)
     if a.copy_calibration:
         copy_calibration()
+        return
+    if a.config == "pack_layer":
+        bench_pack(a)
         return
     import torch
     import synth

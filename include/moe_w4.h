@@ -186,6 +186,26 @@ int moe_w4_stack_layer(float *resid, const void *router_w, const void *codes, co
                        const void *shared_w, int64_t T, void *x_buf, void *y_buf,
                        void *workspace, size_t workspace_bytes, void *stream);
 
+/* The packer: bf16 expert weights -> this library's int4 expert format (the
+ * step before the layer).  Format from the Flint model card (Aijuus/flint-w4exp),
+ * table row "weights" (int4 codes, group 128, bf16 scale, fwht128 rotation);
+ * its error, 11.7% relative Frobenius per expert plane, from the card's "Why
+ * the linears stay bf16".  The quantiser is not printed there; it is read as:
+ *   rotated row  r = every 128-block of the row times H128 (fp32 butterfly,
+ *                    strides 1..64 in ascending order, then 1/sqrt(128))
+ *   scale        s = bf16_rne( fp32(absmax of the block's r) / 7 )
+ *   code         c = clamp( round_half_even( fp32(r / s) ), -8, 7 ), 0 if s == 0
+ * w: bf16, n_experts experts of MOE_W4_EXPERT_WEIGHTS elements each: gate
+ * [512][2048], up [512][2048], down [2048][512] (the row order of the codes).
+ * codes, scales: the layouts of moe_w4_forward (expert e at e*1,572,864 B and
+ * at element e*24,576).  All pointers 16-byte aligned device pointers; the
+ * outputs must not overlap w or each other.  n_experts == 0 enqueues nothing.
+ * EINVAL for a bad pointer, alignment, overlap or n_experts outside
+ * [0, MOE_W4_PACK_MAX_EXPERTS]; EDEVICE if the launch failed. */
+#define MOE_W4_EXPERT_WEIGHTS 3145728
+#define MOE_W4_PACK_MAX_EXPERTS 65536
+int moe_w4_pack_experts(const void *w, int64_t n_experts, void *codes, void *scales, void *stream);
+
 /* Static text for a status code. */
 const char *moe_w4_status_string(int status);
 

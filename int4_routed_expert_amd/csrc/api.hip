@@ -8,6 +8,7 @@
 #include "moe_w4.h"
 #include "token_ops.h"
 
+static_assert(MOE_W4_EXPERT_WEIGHTS == 2 * moe_w4::kCodeBytesPerExpert, "two int4 codes per byte");
 static_assert(MOE_W4_ROUTER_NORM_FLOOR == moe_w4::kNormFloor && MOE_W4_ROUTER_NORM_SUM == moe_w4::kNormSum &&
                   MOE_W4_ROUTER_NORM_NONE == moe_w4::kNormNone &&
                   MOE_W4_ROUTER_BIAS_SELECT_ONLY == moe_w4::kBiasSelectOnly,
@@ -297,6 +298,22 @@ int moe_w4_forward_profiled(const void *x, const void *router_w, const void *cod
     if (rc != MOE_W4_OK || T == 0) return rc;
     return run_forward(x, router_w, codes, scales, shared_w, T, y, router_bias, workspace,
                        static_cast<hipStream_t>(stream), events, n_events);
+}
+
+int moe_w4_pack_experts(const void *w, int64_t n_experts, void *codes, void *scales, void *stream) {
+    if (n_experts < 0 || n_experts > MOE_W4_PACK_MAX_EXPERTS) return MOE_W4_EINVAL;
+    if (n_experts == 0) return MOE_W4_OK;
+    if (!w || !codes || !scales) return MOE_W4_EINVAL;
+    if (!aligned(w, MOE_W4_ALIGN) || !aligned(codes, MOE_W4_ALIGN) || !aligned(scales, MOE_W4_ALIGN))
+        return MOE_W4_EINVAL;
+    const size_t nw = (size_t)n_experts * MOE_W4_EXPERT_WEIGHTS * 2;
+    const size_t nc = (size_t)n_experts * kCodeBytesPerExpert, ns = (size_t)n_experts * kScalesPerExpert * 2;
+    if (overlap(w, nw, codes, nc) || overlap(w, nw, scales, ns) || overlap(codes, nc, scales, ns))
+        return MOE_W4_EINVAL;
+    (void)hipGetLastError();
+    launch_pack_experts(static_cast<const uint16_t *>(w), n_experts, static_cast<uint8_t *>(codes),
+                        static_cast<uint16_t *>(scales), static_cast<hipStream_t>(stream));
+    return device_status(hipGetLastError());
 }
 
 int moe_w4_generate_layer(uint64_t seed, int layer, void *router_w, void *codes, void *scales,

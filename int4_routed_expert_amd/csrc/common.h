@@ -176,6 +176,35 @@ __device__ __forceinline__ float shfl_xor_f(float v, int m) {
     return __shfl_xor(v, m, kWave);
 }
 
+// fwht128 of the 128-blocks held by 16-lane groups (lane j of a group holds
+// elements [8j, 8j + 8) of its block), in fp32: the Sylvester butterfly, each
+// stage replacing (a, b) at distance h by (a + b, a - b), h = 1, 2, 4 inside
+// a lane and 8, 16, 32, 64 across lanes, then the 1/sqrt(128) factor.
+__device__ __forceinline__ void fwht128_lanes16(float (&v)[8], int lane) {
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if ((i & h) == 0) {
+                const float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 1; m <= 8; m <<= 1) {   // strides 8..64: lanes of the same block
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float q = shfl_xor_f(v[i], m);
+            v[i] = upper ? (q - v[i]) : (v[i] + q);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] *= 0.08838834764831845f;   // 1/sqrt(128)
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) v += shfl_xor_f(v, m);

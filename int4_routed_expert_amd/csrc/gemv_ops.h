@@ -73,32 +73,10 @@ __device__ __forceinline__ void gu_load_pair(GuRows &R, int i, rsrc_t cg, rsrc_t
 // (a0, a1: the lane's 8 values of a, K [8 lane, 8 lane + 8).)
 __device__ __forceinline__ void rotate_act_wave(float4 a0, float4 a1, int lane, uint32_t *at, float *at_scale) {
     float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-    for (int h = 1; h < 8; h <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            if ((i & h) == 0) {
-                const float a = v[i], b = v[i + h];
-                v[i] = a + b;
-                v[i + h] = a - b;
-            }
-        }
-    }
-#pragma unroll
-    for (int m = 1; m <= 8; m <<= 1) {   // strides 8..64: lanes of the same block
-        const bool upper = (lane & m) != 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float q = shfl_xor_f(v[i], m);
-            v[i] = upper ? (q - v[i]) : (v[i] + q);
-        }
-    }
+    fwht128_lanes16(v, lane);
     float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        v[i] *= 0.08838834764831845f;
-        amax = fmaxf(amax, fabsf(v[i]));
-    }
+    for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
 #pragma unroll
     for (int m = 1; m <= 8; m <<= 1) amax = fmaxf(amax, shfl_xor_f(amax, m));
     int sh = 0;

@@ -106,6 +106,11 @@ void launch_shared_down_dense(const uint16_t *shared_w, const uint16_t *hs, int 
 void launch_combine(const float *z, const float *topk_w, const int *pos, const float *o, int T, uint16_t *y,
                     hipStream_t s);
 
+// The packer: n_experts experts of bf16 weights (gate [512][2048], up
+// [512][2048], down [2048][512] each) -> int4 codes and bf16 scales in the
+// library layout (fwht128 on K, scale = bf16(absmax / 7) per 128-group).
+void launch_pack_experts(const uint16_t *w, int64_t n_experts, uint8_t *codes, uint16_t *scales, hipStream_t s);
+
 // Stack glue: x_bf16 = bf16(rmsnorm(resid)); resid += f32(y).
 void launch_rmsnorm_bf16(const float *resid, int T, uint16_t *x, hipStream_t s);
 void launch_residual_add(float *resid, const uint16_t *y, int T, hipStream_t s);

@@ -29,6 +29,8 @@ FUSED_MAX_TOKENS = 8
 # router policy flags of moe_w4_forward_policy (include/moe_w4.h)
 ROUTER_NORM_FLOOR, ROUTER_NORM_SUM, ROUTER_NORM_NONE, ROUTER_NORM_MASK = 0, 1, 2, 3
 ROUTER_BIAS_SELECT_ONLY = 4
+EXPERT_WEIGHTS = 3145728       # bf16 elements of one expert's gate, up and down rows
+PACK_MAX_EXPERTS = 65536
 
 OK, EINVAL, EWORKSPACE, EDEVICE = 0, -1, -2, -3
 
@@ -62,6 +64,7 @@ _sig = {
     "moe_w4_profile_point_name": (ctypes.c_char_p, [_int]),
     "moe_w4_forward_profiled": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp,
                                        ctypes.POINTER(_vp), _int]),
+    "moe_w4_pack_experts": (_int, [_vp, _i64, _vp, _vp, _vp]),
     "moe_w4_generate_layer": (_int, [_u64, _int, _vp, _vp, _vp, _vp, _vp]),
     "moe_w4_generate_x": (_int, [_u64, _int, _i64, _vp, _vp]),
     "moe_w4_stack_layer": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
@@ -169,6 +172,12 @@ def moe_w4_forward_profiled(x, router_w, codes, scales, shared_w, y, workspace, 
 def moe_w4_generate_layer(seed, layer, router_w=None, codes=None, scales=None, shared_w=None, stream=None):
     _check(_lib.moe_w4_generate_layer(seed, layer, _ptr(router_w), _ptr(codes), _ptr(scales), _ptr(shared_w),
                                       _stream(stream)), "moe_w4_generate_layer")
+
+
+def moe_w4_pack_experts(w, codes, scales, n_experts=None, stream=None):
+    """bf16 expert weights (n_experts x EXPERT_WEIGHTS) -> int4 codes and bf16 scales."""
+    n = w.numel() // EXPERT_WEIGHTS if n_experts is None else n_experts
+    _check(_lib.moe_w4_pack_experts(_ptr(w), n, _ptr(codes), _ptr(scales), _stream(stream)), "moe_w4_pack_experts")
 
 
 def moe_w4_generate_x(seed, layer, x, stream=None):

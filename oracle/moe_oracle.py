@@ -355,6 +355,81 @@ def quantize_rotated(w: np.ndarray):
     return codes, s_bits
 
 
+def fwht128_f32(v: np.ndarray) -> np.ndarray:
+    """The fwht128 butterfly in fp32 on every 128-block of the last axis.
+
+    The fast Walsh-Hadamard transform (Sylvester order): stages of stride
+    h = 1, 2, ..., 64, each replacing (a, b) at distance h by (a + b, a - b),
+    every add in fp32, then the fp32 factor 1/sqrt(128).  This is the
+    rotation as a packer computes it in fp32; rotate_blocks is the same
+    transform in fp64.
+    """
+    v = np.asarray(v, dtype=np.float32)
+    shp = v.shape
+    w = v.reshape(-1, G).copy()
+    h = 1
+    while h < G:
+        q = w.reshape(-1, G // (2 * h), 2, h)
+        a = q[:, :, 0, :].copy()
+        b = q[:, :, 1, :].copy()
+        q[:, :, 0, :] = a + b
+        q[:, :, 1, :] = a - b
+        w = q.reshape(-1, G)
+        h *= 2
+    return (w * np.float32(1.0 / math.sqrt(G))).reshape(shp)
+
+
+def quantize_rotated_f32(w_bits: np.ndarray):
+    """quantize_rotated with every decision taken in fp32, as the packer takes it.
+
+    w_bits: bf16 bits [n, k].  Rotation by fwht128_f32; scale = bf16(fp32(absmax) /
+    7) with the fp32 division rounded once to fp32 and then to bf16; code =
+    clamp(round-half-even(fp32(w_rot / scale)), -8, 7), 0 where the scale is 0.
+    Returns (int4 values [n, k], scale bf16 bits [n, k/128]).
+    """
+    w = bf16_to_f64(w_bits).astype(np.float32)         # exact: bf16 values are fp32 values
+    n, k = w.shape
+    grp = fwht128_f32(w).reshape(n, k // G, G)
+    amax = np.abs(grp).max(axis=2)
+    s_bits = f64_to_bf16_bits((amax / np.float32(7.0)).astype(np.float64))
+    s = bf16_to_f64(s_bits).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s[..., None] > 0, grp / s[..., None], np.float32(0.0))
+    codes = np.clip(np.rint(q), -8, 7).astype(np.int16).reshape(n, k)
+    return codes, s_bits
+
+
+def pack_int4(vals: np.ndarray) -> np.ndarray:
+    """Signed int4 values [..., k] -> bytes [..., k/2]: element k in the low
+    nibble of byte k/2 when k is even, two's complement (the inverse of
+    unpack_int4)."""
+    u = (np.asarray(vals, dtype=np.int16) & 0xF).astype(np.uint8)
+    return (u[..., 0::2] | (u[..., 1::2] << 4)).astype(np.uint8)
+
+
+EXPERT_WEIGHTS = 2 * I_R * H + H * I_R                 # 3,145,728 bf16 per expert
+
+
+def pack_expert_bank(w_bits: np.ndarray):
+    """bf16 weights of n experts [n, EXPERT_WEIGHTS] (gate [512][2048], up
+    [512][2048], down [2048][512] each) -> (code bytes [n, 1572864], scale
+    bits [n, 24576]) in the library layout, by quantize_rotated_f32 row by row."""
+    w_bits = np.asarray(w_bits, dtype=np.uint16)
+    n = w_bits.shape[0]
+    codes = np.empty((n, EXPERT_WEIGHTS // 2), dtype=np.uint8)
+    scales = np.empty((n, EXPERT_WEIGHTS // G), dtype=np.uint16)
+    for e in range(n):
+        parts = [(w_bits[e, :2 * I_R * H].reshape(2 * I_R, H)), (w_bits[e, 2 * I_R * H:].reshape(H, I_R))]
+        cb, sb = [], []
+        for m in parts:
+            c, sbits = quantize_rotated_f32(m)
+            cb.append(pack_int4(c).ravel())
+            sb.append(sbits.ravel())
+        codes[e] = np.concatenate(cb)
+        scales[e] = np.concatenate(sb)
+    return codes, scales
+
+
 def unrotated_effective(codes: np.ndarray, s_bits: np.ndarray) -> np.ndarray:
     """Effective weight in the original basis: (code * scale) (I x Hn)."""
     w = codes.astype(np.float64) * np.repeat(bf16_to_f64(s_bits), G, axis=1)

@@ -136,6 +136,22 @@ def test_router_policy_validation(m):
                                          None) == m.EINVAL
 
 
+def test_pack_validation(m):
+    lib = m._lib
+    n = 2
+    wb = n * m.EXPERT_WEIGHTS * 2
+    w, c, s = 0x10000000, 0x10000000 + wb, 0x10000000 + wb + n * m.CODE_BYTES_PER_EXPERT
+    assert lib.moe_w4_pack_experts(w, 0, None, None, None) == m.OK               # nothing to do
+    assert lib.moe_w4_pack_experts(w, -1, c, s, None) == m.EINVAL
+    assert lib.moe_w4_pack_experts(w, m.PACK_MAX_EXPERTS + 1, c, s, None) == m.EINVAL
+    assert lib.moe_w4_pack_experts(None, n, c, s, None) == m.EINVAL
+    assert lib.moe_w4_pack_experts(w, n, None, s, None) == m.EINVAL
+    assert lib.moe_w4_pack_experts(w + 8, n, c, s, None) == m.EINVAL            # misaligned
+    assert lib.moe_w4_pack_experts(w, n, w + 4096, s, None) == m.EINVAL         # codes overlap the weights
+    assert lib.moe_w4_pack_experts(w, n, c, c + 16, None) == m.EINVAL           # scales overlap the codes
+    assert m.moe_w4_last_device_error() == 0
+
+
 def test_status_strings(m):
     for st in (m.OK, m.EINVAL, m.EWORKSPACE, m.EDEVICE):
         assert m.status_string(st)

@@ -235,6 +235,91 @@ def test_quantize_roundtrip_within_int4_bound():
     assert abs(rel - c["int4_rel_frobenius"]) < 0.01, rel
 
 
+# ----------------------------------------------------------------------- packer
+def test_fwht128_f32_is_the_butterfly_within_fp32_rounding():
+    rng = np.random.default_rng(30)
+    v = rng.standard_normal((64, 2048)).astype(np.float32)
+    got = O.fwht128_f32(v).astype(np.float64)
+    ref = rotate_rows_blockwise(v.astype(np.float64))
+    # seven fp32 add stages and one multiply: each value within a few ulps of the block's 1-norm
+    l1 = np.abs(v.astype(np.float64)).reshape(64, 16, 128).sum(axis=2)
+    bound = np.repeat(l1, 128, axis=1) * 2.0 ** -21
+    assert np.all(np.abs(got - ref) <= bound)
+    # its own inverse up to fp32 rounding
+    back = O.fwht128_f32(O.fwht128_f32(v))
+    assert np.abs(back - v).max() < 1e-5 * np.abs(v).max()
+
+
+def test_quantizer_f32_agrees_with_the_fp64_reading():
+    """Deciding in fp32 (the packer's precision) moves a code only where the
+    rotated value sits on a rounding boundary: rare, and by one step."""
+    rng = np.random.default_rng(31)
+    bits = synth.f32_to_bf16_bits((rng.standard_normal((512, 2048)) * 0.02).astype(np.float32))
+    c32, s32 = O.quantize_rotated_f32(bits)
+    c64, s64 = O.quantize_rotated(O.bf16_to_f64(bits))
+    same_s = s32 == s64
+    assert same_s.mean() > 0.999
+    # a scale differs by at most one bf16 step
+    assert np.all(np.abs(s32.astype(np.int32) - s64.astype(np.int32)) <= 1)
+    rows_groups = np.repeat(same_s, 128, axis=1)
+    diff = c32 != c64
+    assert diff[rows_groups].mean() < 1e-4
+    assert np.all(np.abs(c32.astype(np.int32) - c64)[rows_groups] <= 1)
+
+
+def test_quantizer_f32_error_is_the_cards_figure():
+    c = golden_constants()
+    rng = np.random.default_rng(32)
+    w = (rng.standard_normal((512, 2048)) * 0.02).astype(np.float32)
+    bits = synth.f32_to_bf16_bits(w)
+    codes, s_bits = O.quantize_rotated_f32(bits)
+    assert codes.min() >= -8 and codes.max() <= 7
+    w_back = O.unrotated_effective(codes, s_bits)
+    wb = O.bf16_to_f64(bits)
+    rel = np.linalg.norm(w_back - wb) / np.linalg.norm(wb)
+    assert abs(rel - c["int4_rel_frobenius"]) < 0.01, rel
+    # every rotated value within half a step of its code (no group needs the clamp)
+    s = np.repeat(O.bf16_to_f64(s_bits), 128, axis=1)
+    r = rotate_rows_blockwise(wb)
+    assert np.all(np.abs(r - codes * s) <= s / 2 * (1 + 1e-3) + 1e-9)
+
+
+def test_pack_int4_inverts_the_decoder():
+    vals = np.array([[-8, -7, -1, 0, 1, 6, 7, 3, -2, 5]], dtype=np.int16)
+    packed = O.pack_int4(vals)
+    np.testing.assert_array_equal(decode_xor(packed, 10), vals)
+    np.testing.assert_array_equal(O.unpack_int4(packed, 10), vals)
+    assert packed[0, 0] == (0x8 | (0x9 << 4))       # -8 low nibble, -7 high nibble
+
+
+def test_pack_bank_of_one_hot_rows():
+    """A row holding 1.0 at position j of a block rotates to +-1/sqrt(128) with
+    the signs of Hadamard row j, so its 16 codes of that block are
+    7 * (-1)^popcount(i & j): the layout, the sign convention and the scale
+    all show in one closed form."""
+    w = np.zeros((2, O.EXPERT_WEIGHTS), dtype=np.uint16)
+    one = synth.f32_to_bf16_bits(np.float32([1.0]))[0]
+    # expert 1: gate row 3, block 5, position 77; down row 2000, block 2, position 9
+    gate_off = 3 * 2048 + 5 * 128 + 77
+    down_off = 2 * 512 * 2048 + 2000 * 512 + 2 * 128 + 9
+    w[1, gate_off] = one
+    w[1, down_off] = one
+    codes, scales = O.pack_expert_bank(w)
+    assert not codes[0].any() and not scales[0].any()
+    vals = O.unpack_int4(codes[1], O.EXPERT_WEIGHTS)
+    i = np.arange(128)
+    sign77 = np.array([(-1) ** bin(k & 77).count("1") for k in i])
+    sign9 = np.array([(-1) ** bin(k & 9).count("1") for k in i])
+    np.testing.assert_array_equal(vals[3 * 2048 + 5 * 128: 3 * 2048 + 6 * 128], 7 * sign77)
+    base = 2 * 512 * 2048 + 2000 * 512 + 2 * 128
+    np.testing.assert_array_equal(vals[base: base + 128], 7 * sign9)
+    assert np.count_nonzero(vals) == 256
+    s = O.bf16_to_f64(scales[1])
+    nz = np.nonzero(s)[0]
+    assert list(nz) == [(3 * 2048 + 5 * 128) // 128, base // 128]
+    np.testing.assert_allclose(s[nz], 1 / (7 * math.sqrt(128)), rtol=2 ** -8)
+
+
 # ----------------------------------------------------------------------- router
 def _brute_top6(l32):
     n = l32.shape[0]
