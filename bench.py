@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="decode_t32",
                     choices=["decode_t1", "decode_t32", "prefill_t2048", "prefill_t2048_skew", "stack_t1", "stack_t8",
-                             "pack_layer"])
+                             "pack_layer", "mlp_t1", "mlp_t2048"])
     ap.add_argument("--layers", type=int, default=0, help="distinct layers rotated through (0 = auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--eager", action="store_true",
@@ -282,6 +282,74 @@ def bench_pack(a):
     print(json.dumps(result), flush=True)
 
 
+def bench_mlp(a, T):
+    """The dense SwiGLU MLP block (width 6144) over T tokens: seeded bf16 weights
+    N(0, 0.02) (4 sets rotated, 302 MB, beyond the Infinity Cache) and x N(0, 1).
+    A step is one moe_w4_dense_mlp call (two launches); its roofline is HBM at
+    T = 1 and bf16 MFMA at T = 2048, over the whole call."""
+    import torch
+    import synth
+    from int4_routed_expert_amd import moe_w4 as m
+    from oracle import moe_oracle as O
+    g = torch.Generator(device="cuda").manual_seed(6)
+    ws_ = [(torch.randn(m.DENSE_WEIGHTS, generator=g, device="cuda") * 0.02).to(torch.bfloat16).view(torch.int16)
+           for _ in range(4)]
+    x_bits = synth.gen_x(6, T)
+    x = torch.from_numpy(x_bits.view(np.int16)).cuda()
+    y = torch.empty((T, 2048), dtype=torch.int16, device="cuda")
+    work = torch.empty(m.moe_w4_dense_mlp_workspace_bytes(T), dtype=torch.uint8, device="cuda")
+    for i in range(a.warmup):
+        m.moe_w4_dense_mlp(x, ws_[i % 4], y, work)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        m.moe_w4_dense_mlp(x, ws_[i % 4], y, work)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / a.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
+    for i, (e0, e1) in enumerate(ev):
+        e0.record()
+        m.moe_w4_dense_mlp(x, ws_[i % 4], y, work)
+        e1.record()
+    torch.cuda.synchronize()
+    call_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    nbytes = m.DENSE_WEIGHTS * 2 + 2 * T * 2048 * 2
+    flops = 2 * T * 3 * m.DENSE_INTER * 2048
+    if T >= 128:
+        tf = flops / (call_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "dense MLP call (gate/up + down launches)", "achieved": tf,
+                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
+                "algorithmic_flops": flops, "algorithmic_bytes": nbytes, "kernel_us": call_ms * 1e3}
+    else:
+        gbs = nbytes / (call_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "kernel": "dense MLP call (gate/up + down launches)", "achieved": gbs,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                "algorithmic_bytes": nbytes, "kernel_us": call_ms * 1e3}
+    result = {"metric": "dense SwiGLU MLP block (width 6144) tokens/s", "value": T / (ms * 1e-3), "unit": "tokens/s",
+              "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True,
+              "scaling": "weak", "vs_baseline": None, "dtype": "bf16 x bf16 -> fp32", "data": "synthetic",
+              "config": {"workload": f"mlp_t{T}: dense SwiGLU MLP block, T={T}, x seed 6, weights torch seed 6 "
+                                     f"(4 sets rotated)", "T": T},
+              "roofline": roof}
+    if not a.no_cpu:
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        except Exception:
+            cores = os.cpu_count()
+        wb = ws_[0].cpu().numpy().view(np.uint16)
+        n_tok = min(T, 64)
+        reps, elapsed = 0, 0.0
+        while elapsed < a.cpu_seconds and reps < 20:
+            t0 = time.perf_counter()
+            O.dense_mlp(x_bits[:n_tok], wb)
+            elapsed += time.perf_counter() - t0
+            reps += 1
+        result["cpu_baseline"] = {"value": n_tok * reps / elapsed, "unit": "tokens/s", "cores": int(cores),
+                                  "kind": "oracle", "sample": f"{reps} oracle calls on {n_tok} of the {T} tokens"}
+    print(json.dumps(result), flush=True)
+
+
 def cpu_baseline_stack(T, x_bits, budget_s):
     """The CPU oracle's stack step on a bounded sample: the first two layers
     (router, shared expert and the selected experts generated on demand by the
@@ -335,6 +403,9 @@ def main():
         return
     if a.config == "pack_layer":
         bench_pack(a)
+        return
+    if a.config.startswith("mlp_t"):
+        bench_mlp(a, int(a.config[5:]))
         return
     import torch
     import synth

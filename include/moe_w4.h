@@ -206,6 +206,21 @@ int moe_w4_stack_layer(float *resid, const void *router_w, const void *codes, co
 #define MOE_W4_PACK_MAX_EXPERTS 65536
 int moe_w4_pack_experts(const void *w, int64_t n_experts, void *codes, void *scales, void *stream);
 
+/* Dense SwiGLU MLP block, the neighbour of the MoE blocks in the same model
+ * (NInfer README of Flint, "What is inside": blocks 0 and 1 are dense SwiGLU
+ * MLPs of width 6144; the model card keeps every linear bf16):
+ *   y = bf16_rne( Wd( silu(Wg x) * (Wu x) ) )     fp32 sums of exact bf16 products,
+ *                                                  the SwiGLU product rounded to bf16 once
+ * w: bf16, MOE_W4_DENSE_WEIGHTS elements: gate [6144][2048], up [6144][2048],
+ * down [2048][6144].  x, y: bf16 [T][2048].  workspace: at least
+ * moe_w4_dense_mlp_workspace_bytes(T) bytes, contents on entry irrelevant.
+ * Validation, T == 0 and errors as for moe_w4_forward. */
+#define MOE_W4_DENSE_INTER 6144
+#define MOE_W4_DENSE_WEIGHTS 37748736
+size_t moe_w4_dense_mlp_workspace_bytes(int64_t T);
+int moe_w4_dense_mlp(const void *x, const void *w, int64_t T, void *y, void *workspace, size_t workspace_bytes,
+                     void *stream);
+
 /* Static text for a status code. */
 const char *moe_w4_status_string(int status);
 

@@ -9,6 +9,8 @@
 #include "token_ops.h"
 
 static_assert(MOE_W4_EXPERT_WEIGHTS == 2 * moe_w4::kCodeBytesPerExpert, "two int4 codes per byte");
+static_assert(MOE_W4_DENSE_INTER == moe_w4::kDenseInter && MOE_W4_DENSE_WEIGHTS == 3 * moe_w4::kDenseInter * moe_w4::kH,
+              "dense MLP shape");
 static_assert(MOE_W4_ROUTER_NORM_FLOOR == moe_w4::kNormFloor && MOE_W4_ROUTER_NORM_SUM == moe_w4::kNormSum &&
                   MOE_W4_ROUTER_NORM_NONE == moe_w4::kNormNone &&
                   MOE_W4_ROUTER_BIAS_SELECT_ONLY == moe_w4::kBiasSelectOnly,
@@ -298,6 +300,38 @@ int moe_w4_forward_profiled(const void *x, const void *router_w, const void *cod
     if (rc != MOE_W4_OK || T == 0) return rc;
     return run_forward(x, router_w, codes, scales, shared_w, T, y, router_bias, workspace,
                        static_cast<hipStream_t>(stream), events, n_events);
+}
+
+size_t moe_w4_dense_mlp_workspace_bytes(int64_t T) {
+    return t_in_range(T) ? align_up((size_t)T * kDenseInter * 2) + 256 : 0;
+}
+
+int moe_w4_dense_mlp(const void *x, const void *w, int64_t T, void *y, void *workspace, size_t workspace_bytes,
+                     void *stream) {
+    if (!t_in_range(T)) return MOE_W4_EINVAL;
+    if (T == 0) return MOE_W4_OK;
+    if (!x || !w || !y || !workspace) return MOE_W4_EINVAL;
+    const void *ptrs[] = {x, w, y, workspace};
+    for (const void *p : ptrs)
+        if (!aligned(p, MOE_W4_ALIGN)) return MOE_W4_EINVAL;
+    if (workspace_bytes < moe_w4_dense_mlp_workspace_bytes(T)) return MOE_W4_EWORKSPACE;
+    const size_t act_bytes = (size_t)T * kH * 2;
+    if (overlap(y, act_bytes, x, act_bytes) || overlap(y, act_bytes, workspace, workspace_bytes) ||
+        overlap(y, act_bytes, w, (size_t)MOE_W4_DENSE_WEIGHTS * 2))
+        return MOE_W4_EINVAL;
+    const int t = (int)T;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t *xb = static_cast<const uint16_t *>(x), *wb = static_cast<const uint16_t *>(w);
+    uint16_t *h = static_cast<uint16_t *>(workspace), *yb = static_cast<uint16_t *>(y);
+    (void)hipGetLastError();
+    if (t >= kPrefillMinTokens) {
+        launch_dense_mlp_gateup_dense(xb, t, wb, h, s);
+        if (hipPeekAtLastError() == hipSuccess) launch_dense_mlp_down_dense(wb, h, t, yb, s);
+    } else {
+        launch_dense_mlp_gateup_skinny(xb, t, wb, h, s);
+        if (hipPeekAtLastError() == hipSuccess) launch_dense_mlp_down_skinny(wb, h, t, yb, s);
+    }
+    return device_status(hipGetLastError());
 }
 
 int moe_w4_pack_experts(const void *w, int64_t n_experts, void *codes, void *scales, void *stream) {

@@ -12,6 +12,7 @@ constexpr int kE = 256;             // routed experts
 constexpr int kTopK = 6;            // experts per token
 constexpr int kI = 512;             // routed expert width
 constexpr int kIS = 1024;           // shared expert width
+constexpr int kDenseInter = 6144;   // width of the dense SwiGLU MLP blocks
 constexpr int kG = 128;             // K per scale == Hadamard block
 constexpr int kWave = 64;
 

@@ -37,7 +37,7 @@ constexpr int kStageLoads = kTile * kChunksPerRow / 256;   // 16-byte loads per 
 constexpr int kPrefetch = 2;                     // steps whose operands are in flight in registers
 constexpr int kXcds = 8;
 
-enum { kEpiStore = 0, kEpiSwiglu = 1 };
+enum { kEpiStore = 0, kEpiSwiglu = 1, kEpiStoreBf16 = 2 };
 
 struct DenseJob {
     const uint16_t *B;   // weight rows, K contiguous
@@ -45,7 +45,7 @@ struct DenseJob {
     int epi;
     int up_row;          // SwiGLU: first up row (gate rows start at 0)
     const float *bias;   // kEpiStore: per column, or null
-    void *out;           // f32 (store) or bf16 (SwiGLU) [M][ldo]
+    void *out;           // f32 (store) or bf16 (SwiGLU, bf16 store) [M][ldo]
     int ldo;
 };
 struct DenseJobs {
@@ -161,7 +161,10 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
     load(0, 2);
     __syncthreads();
 
-#pragma unroll
+    // fully unrolled up to K = 2048; longer K in pairs of steps (a full unroll
+    // of 96 steps holds enough addresses live to fall to one wave per SIMD)
+    constexpr int kUnroll = kSteps <= 32 ? kSteps : 2;
+#pragma unroll kUnroll
     for (int s = 0; s < kSteps; ++s) {
         const int slot = s & 1;
         // every operand of the step is requested from LDS first, so the MFMAs
@@ -216,6 +219,13 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
                     const int c = nt * kTile + 64 * wn + 32 * y + n;
                     o[(size_t)m * J.ldo + c] = acc[x][y][i] + bcol[y];
                 }
+            } else if (J.epi == kEpiStoreBf16) {
+                uint16_t *o = static_cast<uint16_t *>(J.out);
+#pragma unroll
+                for (int y = 0; y < 2; ++y) {
+                    const int c = nt * kTile + 64 * wn + 32 * y + n;
+                    o[(size_t)m * J.ldo + c] = f32_to_bf16(acc[x][y][i]);
+                }
             } else {   // kEpiSwiglu
                 const float gv = acc[x][0][i], uv = acc[x][1][i];
                 const int r = nt * 64 + 32 * wn + n;
@@ -252,8 +262,25 @@ void launch_shared_down_dense(const uint16_t *shared_w, const uint16_t *hs, int 
     launch_dense<kIS>(hs, T, jobs, s);
 }
 
-// y[t] = bf16(z[t] + sum_j w[t][j] o[pos[6t + j]]), slots in order, with o in
-// bf16 (the grouped down kernel's output): a wave per token, lane l owns
+// Dense SwiGLU MLP block (NInfer README of Flint, "What is inside": blocks 0
+// and 1 are dense SwiGLU MLPs of width 6144; the model card keeps every
+// linear bf16): h = bf16(silu(x Wg^T) * (x Wu^T)), then y = bf16(h Wd^T).
+void launch_dense_mlp_gateup_dense(const uint16_t *x, int T, const uint16_t *w, uint16_t *h, hipStream_t s) {
+    DenseJobs jobs;
+    jobs.job[0] = DenseJob{w, kDenseInter / 64, kEpiSwiglu, kDenseInter, nullptr, h, kDenseInter};
+    jobs.job[1] = no_dense_job();
+    launch_dense<kH>(x, T, jobs, s);
+}
+
+void launch_dense_mlp_down_dense(const uint16_t *w, const uint16_t *h, int T, uint16_t *y, hipStream_t s) {
+    DenseJobs jobs;
+    jobs.job[0] = DenseJob{w + 2 * (size_t)kDenseInter * kH, kH / kTile, kEpiStoreBf16, 0, nullptr, y, kH};
+    jobs.job[1] = no_dense_job();
+    launch_dense<kDenseInter>(h, T, jobs, s);
+}
+
+// y[t] = bf16(z[t] + sum_j w[t][j] o[pos[6t + j]]), slots in order, with o the
+// grouped down kernel's fp32 rows: a wave per token, lane l owns
 // columns [32l, 32l + 32); every load of the token is in flight at once (the
 // gathers of an epilogue inside the GEMM tile were latency-bound).
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ z, const float *__restrict__ topk_w,

@@ -111,6 +111,14 @@ void launch_combine(const float *z, const float *topk_w, const int *pos, const f
 // library layout (fwht128 on K, scale = bf16(absmax / 7) per 128-group).
 void launch_pack_experts(const uint16_t *w, int64_t n_experts, uint8_t *codes, uint16_t *scales, hipStream_t s);
 
+// Dense SwiGLU MLP block (width kDenseInter): w = bf16 gate [6144][2048], up
+// [6144][2048], down [2048][6144]; h bf16 [T][6144]; y bf16 [T][2048].  Skinny
+// kernels below kPrefillMinTokens tokens, LDS-tiled MFMA GEMMs from there on.
+void launch_dense_mlp_gateup_skinny(const uint16_t *x, int T, const uint16_t *w, uint16_t *h, hipStream_t s);
+void launch_dense_mlp_down_skinny(const uint16_t *w, const uint16_t *h, int T, uint16_t *y, hipStream_t s);
+void launch_dense_mlp_gateup_dense(const uint16_t *x, int T, const uint16_t *w, uint16_t *h, hipStream_t s);
+void launch_dense_mlp_down_dense(const uint16_t *w, const uint16_t *h, int T, uint16_t *y, hipStream_t s);
+
 // Stack glue: x_bf16 = bf16(rmsnorm(resid)); resid += f32(y).
 void launch_rmsnorm_bf16(const float *resid, int T, uint16_t *x, hipStream_t s);
 void launch_residual_add(float *resid, const uint16_t *y, int T, hipStream_t s);

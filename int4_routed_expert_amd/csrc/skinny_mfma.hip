@@ -34,7 +34,7 @@ namespace moe_w4 {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-enum { kEpiStoreF32 = 0, kEpiSwiglu = 1, kEpiCombine = 2 };
+enum { kEpiStoreF32 = 0, kEpiSwiglu = 1, kEpiCombine = 2, kEpiStoreBf16 = 3 };
 
 // One job of a launch: a weight matrix, its output and its epilogue.  A launch
 // runs up to two jobs side by side (workgroups [0, n_blocks0) do job 0, the
@@ -175,7 +175,14 @@ __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__
 #pragma unroll
             for (int w = 1; w < KS; ++w) sum += red[w][t][lane];
             // lane holds rows m0 + 16t + 4g + i of column c0 + c
-            if (epi == kEpiStoreF32) {
+            if (epi == kEpiStoreBf16) {
+                uint16_t *o = static_cast<uint16_t *>(J.out);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int m = m0 + 16 * t + 4 * g + i;
+                    if (r < CW && m < M) o[(size_t)m * J.ldo + c0 + c] = f32_to_bf16(sum[i]);
+                }
+            } else if (epi == kEpiStoreF32) {
                 const float bcol = J.bias ? J.bias[c0 + c] : 0.0f;
                 float *o = static_cast<float *>(J.out);
 #pragma unroll
@@ -259,6 +266,35 @@ void launch_shared_down_combine(const uint16_t *shared_w, const uint16_t *hs, in
     jobs.job[0] = SkinnyJob{shared_w + 2 * kSharedGateElems, kH, 0, kH / 8, kEpiCombine, nullptr, y, kH, topk_w, pos, o};
     jobs.job[1] = no_job();
     launch_skinny_k<kIS / (128 * 8), 8>(hs, T, jobs, s);
+}
+
+
+// Dense SwiGLU MLP block of width 6144 (NInfer README of Flint, "What is
+// inside": blocks 0 and 1; bf16 like every linear of the model card): the
+// gate/up job as for the shared expert, 16-column tiles of (8 gate rows, the
+// same 8 up rows); the down projection over K = 6144, 8 waves splitting K.
+void launch_dense_mlp_gateup_skinny(const uint16_t *x, int T, const uint16_t *w, uint16_t *h, hipStream_t s) {
+    SkinnyJobs jobs;
+    jobs.rot_x = nullptr;
+    jobs.rot_tokens = 0;
+    jobs.xt = nullptr;
+    jobs.xt_scale = nullptr;
+    jobs.job[0] = SkinnyJob{w, 2 * kDenseInter, kDenseInter, 2 * kDenseInter / 16, kEpiSwiglu, nullptr, h, kDenseInter,
+                            nullptr, nullptr, nullptr};
+    jobs.job[1] = no_job();
+    launch_skinny_k<kH / (128 * 8), 16>(x, T, jobs, s);
+}
+
+void launch_dense_mlp_down_skinny(const uint16_t *w, const uint16_t *h, int T, uint16_t *y, hipStream_t s) {
+    SkinnyJobs jobs;
+    jobs.rot_x = nullptr;
+    jobs.rot_tokens = 0;
+    jobs.xt = nullptr;
+    jobs.xt_scale = nullptr;
+    jobs.job[0] = SkinnyJob{w + 2 * (size_t)kDenseInter * kH, kH, 0, kH / 8, kEpiStoreBf16, nullptr, y, kH, nullptr,
+                            nullptr, nullptr};
+    jobs.job[1] = no_job();
+    launch_skinny_k<kDenseInter / (128 * 8), 8>(h, T, jobs, s);
 }
 
 }  // namespace moe_w4

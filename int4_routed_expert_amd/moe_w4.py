@@ -31,6 +31,8 @@ ROUTER_NORM_FLOOR, ROUTER_NORM_SUM, ROUTER_NORM_NONE, ROUTER_NORM_MASK = 0, 1, 2
 ROUTER_BIAS_SELECT_ONLY = 4
 EXPERT_WEIGHTS = 3145728       # bf16 elements of one expert's gate, up and down rows
 PACK_MAX_EXPERTS = 65536
+DENSE_INTER = 6144
+DENSE_WEIGHTS = 37748736       # bf16 elements of a dense MLP block: gate, up [6144][2048], down [2048][6144]
 
 OK, EINVAL, EWORKSPACE, EDEVICE = 0, -1, -2, -3
 
@@ -65,6 +67,8 @@ _sig = {
     "moe_w4_forward_profiled": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp,
                                        ctypes.POINTER(_vp), _int]),
     "moe_w4_pack_experts": (_int, [_vp, _i64, _vp, _vp, _vp]),
+    "moe_w4_dense_mlp_workspace_bytes": (_sz, [_i64]),
+    "moe_w4_dense_mlp": (_int, [_vp, _vp, _i64, _vp, _vp, _sz, _vp]),
     "moe_w4_generate_layer": (_int, [_u64, _int, _vp, _vp, _vp, _vp, _vp]),
     "moe_w4_generate_x": (_int, [_u64, _int, _i64, _vp, _vp]),
     "moe_w4_stack_layer": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
@@ -178,6 +182,17 @@ def moe_w4_pack_experts(w, codes, scales, n_experts=None, stream=None):
     """bf16 expert weights (n_experts x EXPERT_WEIGHTS) -> int4 codes and bf16 scales."""
     n = w.numel() // EXPERT_WEIGHTS if n_experts is None else n_experts
     _check(_lib.moe_w4_pack_experts(_ptr(w), n, _ptr(codes), _ptr(scales), _stream(stream)), "moe_w4_pack_experts")
+
+
+def moe_w4_dense_mlp_workspace_bytes(T: int) -> int:
+    return _lib.moe_w4_dense_mlp_workspace_bytes(T)
+
+
+def moe_w4_dense_mlp(x, w, y, workspace, stream=None, T=None):
+    """y <- dense SwiGLU MLP block (width 6144) of x.  Tensors on the GPU."""
+    T = x.shape[0] if T is None else T
+    _check(_lib.moe_w4_dense_mlp(_ptr(x), _ptr(w), T, _ptr(y), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream)), "moe_w4_dense_mlp")
 
 
 def moe_w4_generate_x(seed, layer, x, stream=None):

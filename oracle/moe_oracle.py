@@ -307,6 +307,27 @@ def moe_layer_dense(x_bits, router_bits, expert_blobs, shared_bits, bias=None):
     return dict(y=y, y_bits=f64_to_bf16_bits(y), gates=gates)
 
 
+# --------------------------------------------------------- dense MLP block
+I_D = 6144
+DENSE_WEIGHTS = 3 * I_D * H
+
+
+def dense_mlp(x_bits: np.ndarray, w_bits: np.ndarray) -> dict:
+    """Dense SwiGLU MLP block (NInfer README of Flint, "What is inside": blocks 0
+    and 1 are dense SwiGLU MLPs of width 6144; bf16 like every linear of the
+    model card): y = bf16( Wd (silu(Wg x) * (Wu x)) ), fp64 throughout.
+
+    x_bits: bf16 bits [T, 2048]; w_bits: bf16 bits [DENSE_WEIGHTS], gate
+    [6144][2048], up [6144][2048], down [2048][6144].
+    """
+    x = bf16_to_f64(x_bits)
+    w = bf16_to_f64(np.asarray(w_bits, dtype=np.uint16).ravel())
+    n = I_D * H
+    wg, wu, wd = w[:n].reshape(I_D, H), w[n:2 * n].reshape(I_D, H), w[2 * n:].reshape(H, I_D)
+    y = (silu(x @ wg.T) * (x @ wu.T)) @ wd.T
+    return dict(y=y, y_bits=f64_to_bf16_bits(y))
+
+
 # ------------------------------------------------------------------ stack
 def rmsnorm(x: np.ndarray) -> np.ndarray:
     """x / sqrt(mean(x^2) + 1e-6), unit gain, per row."""

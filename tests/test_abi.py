@@ -41,7 +41,8 @@ def test_header_constants_match_the_binding(m):
     defines = dict(re.findall(r"#define MOE_W4_(\w+) \(?(-?\d+)\)?", open(HEADER).read()))
     names = ["HIDDEN", "EXPERTS", "TOPK", "INTER", "SHARED_INTER", "GROUP", "CODE_BYTES_PER_EXPERT",
              "SCALES_PER_EXPERT", "SHARED_ELEMS", "MAX_TOKENS", "FUSED_MAX_TOKENS", "ROUTER_NORM_FLOOR",
-             "ROUTER_NORM_SUM", "ROUTER_NORM_NONE", "ROUTER_NORM_MASK", "ROUTER_BIAS_SELECT_ONLY"]
+             "ROUTER_NORM_SUM", "ROUTER_NORM_NONE", "ROUTER_NORM_MASK", "ROUTER_BIAS_SELECT_ONLY", "EXPERT_WEIGHTS",
+             "PACK_MAX_EXPERTS", "DENSE_INTER", "DENSE_WEIGHTS"]
     for n in names:
         assert int(defines[n]) == getattr(m, n), n
 
@@ -149,6 +150,22 @@ def test_pack_validation(m):
     assert lib.moe_w4_pack_experts(w + 8, n, c, s, None) == m.EINVAL            # misaligned
     assert lib.moe_w4_pack_experts(w, n, w + 4096, s, None) == m.EINVAL         # codes overlap the weights
     assert lib.moe_w4_pack_experts(w, n, c, c + 16, None) == m.EINVAL           # scales overlap the codes
+    assert m.moe_w4_last_device_error() == 0
+
+
+def test_dense_mlp_validation(m):
+    lib = m._lib
+    x, w, y, ws = 0x10000000, 0x20000000, 0x60000000, 0x70000000
+    nb = m.moe_w4_dense_mlp_workspace_bytes(4)
+    assert nb >= 4 * m.DENSE_INTER * 2
+    assert m.moe_w4_dense_mlp_workspace_bytes(-1) == 0
+    assert lib.moe_w4_dense_mlp(x, w, 0, y, ws, 0, None) == m.OK
+    assert lib.moe_w4_dense_mlp(x, w, -1, y, ws, nb, None) == m.EINVAL
+    assert lib.moe_w4_dense_mlp(None, w, 4, y, ws, nb, None) == m.EINVAL
+    assert lib.moe_w4_dense_mlp(x, w + 2, 4, y, ws, nb, None) == m.EINVAL
+    assert lib.moe_w4_dense_mlp(x, w, 4, y, ws, nb - 1, None) == m.EWORKSPACE
+    assert lib.moe_w4_dense_mlp(x, w, 4, x + 4096, ws, nb, None) == m.EINVAL       # y overlaps x
+    assert lib.moe_w4_dense_mlp(x, w, 4, w + 4096, ws, nb, None) == m.EINVAL       # y overlaps the weights
     assert m.moe_w4_last_device_error() == 0
 
 

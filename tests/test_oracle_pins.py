@@ -320,6 +320,49 @@ def test_pack_bank_of_one_hot_rows():
     np.testing.assert_allclose(s[nz], 1 / (7 * math.sqrt(128)), rtol=2 ** -8)
 
 
+# ------------------------------------------------------------- dense MLP block
+def test_dense_mlp_closed_form_on_one_hot_rows():
+    """Gate row j = a e_k, up row j = b e_k, down column j = c e_m: the only
+    nonzero output is y_m = c silu(a x_k) (b x_k)."""
+    rng = np.random.default_rng(40)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((3, 2048)).astype(np.float32))
+    w = np.zeros(O.DENSE_WEIGHTS, dtype=np.uint16)
+    n = O.I_D * 2048
+    j, k, m_out = 4000, 77, 1500
+    a, b, c = 0.75, -1.25, 0.5
+    bits = synth.f32_to_bf16_bits(np.float32([a, b, c]))
+    w[j * 2048 + k] = bits[0]
+    w[n + j * 2048 + k] = bits[1]
+    w[2 * n + m_out * O.I_D + j] = bits[2]
+    out = O.dense_mlp(x, w)
+    xk = O.bf16_to_f64(x)[:, k]
+    expect = c * (a * xk / (1 + np.exp(-a * xk))) * (b * xk)
+    np.testing.assert_allclose(out["y"][:, m_out], expect, rtol=1e-13)
+    assert np.count_nonzero(out["y"]) == np.count_nonzero(expect)
+
+
+def test_dense_mlp_with_zero_up_rows_is_zero():
+    rng = np.random.default_rng(41)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((2, 2048)).astype(np.float32))
+    w = synth.f32_to_bf16_bits((rng.standard_normal(O.DENSE_WEIGHTS) * 0.02).astype(np.float32))
+    n = O.I_D * 2048
+    w[n:2 * n] = 0
+    assert not O.dense_mlp(x, w)["y"].any()
+
+
+def test_dense_mlp_embeds_the_shared_expert():
+    """Width-1024 weights padded with zero rows and columns to width 6144 give
+    the shared expert's output (silu(0) * 0 adds nothing)."""
+    x, _, S = small_layer(42, 2)
+    sg, su, sd = [O.f64_to_bf16_bits(p) for p in O.shared_planes(S)]
+    n = O.I_D * 2048
+    w = np.zeros(O.DENSE_WEIGHTS, dtype=np.uint16)
+    w[:n].reshape(O.I_D, 2048)[:1024] = sg
+    w[n:2 * n].reshape(O.I_D, 2048)[:1024] = su
+    w[2 * n:].reshape(2048, O.I_D)[:, :1024] = sd
+    np.testing.assert_allclose(O.dense_mlp(x, w)["y"], O.shared_expert(O.bf16_to_f64(x), S), rtol=1e-12, atol=1e-15)
+
+
 # ----------------------------------------------------------------------- router
 def _brute_top6(l32):
     n = l32.shape[0]
