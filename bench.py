@@ -246,14 +246,15 @@ def bench_pack(a):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / a.steps
     nbytes = n * (m.EXPERT_WEIGHTS * 2 + m.CODE_BYTES_PER_EXPERT + m.SCALES_PER_EXPERT * 2)
-    # the packer launches on torch's current stream, where these events are recorded
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
-    for e0, e1 in ev:
-        e0.record()
+    # events on the launch stream (torch's current one) around each launch
+    ev = m.HipEvents(2 * a.steps)
+    for i in range(a.steps):
+        ev.record(2 * i)
         m.moe_w4_pack_experts(w, codes, scales)
-        e1.record()
+        ev.record(2 * i + 1)
     torch.cuda.synchronize()
-    kern_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    kern_ms = float(np.mean([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(a.steps)]))
+    ev.close()
     achieved = nbytes / (kern_ms * 1e-3) / 1e9
     result = {"metric": "packer: experts/s (bf16 experts -> fwht128 int4 codes + bf16 scales)",
               "value": n / (ms * 1e-3), "unit": "experts/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
@@ -306,13 +307,14 @@ def bench_mlp(a, T):
         m.moe_w4_dense_mlp(x, ws_[i % 4], y, work)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / a.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(a.steps)]
-    for i, (e0, e1) in enumerate(ev):
-        e0.record()
+    ev = m.HipEvents(2 * a.steps)
+    for i in range(a.steps):
+        ev.record(2 * i)
         m.moe_w4_dense_mlp(x, ws_[i % 4], y, work)
-        e1.record()
+        ev.record(2 * i + 1)
     torch.cuda.synchronize()
-    call_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev]))
+    call_ms = float(np.mean([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(a.steps)]))
+    ev.close()
     nbytes = m.DENSE_WEIGHTS * 2 + 2 * T * 2048 * 2
     flops = 2 * T * 3 * m.DENSE_INTER * 2048
     if T >= 128:

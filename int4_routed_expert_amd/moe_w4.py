@@ -235,19 +235,30 @@ def ws_view(ws, T, name, dtype, count):
 
 
 class HipEvents:
-    """Raw hipEvent_t handles from the HIP runtime torch loaded (for forward_profiled)."""
+    """Raw hipEvent_t handles from the HIP runtime torch loaded, for timing only.
+
+    Created with hipEventDisableSystemFence: a timing event then needs no
+    system-scope cache writeback and invalidation when it is recorded, which
+    otherwise adds microseconds between the kernels it brackets."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
 
     def __init__(self, n):
         self._hip = ctypes.CDLL("libamdhip64.so.7")
-        self._hip.hipEventCreate.argtypes = [ctypes.POINTER(_vp)]
+        self._hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(_vp), ctypes.c_uint]
+        self._hip.hipEventRecord.argtypes = [_vp, _vp]
         self._hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _vp, _vp]
         self._hip.hipEventDestroy.argtypes = [_vp]
         self.handles = []
         for _ in range(n):
             h = _vp()
-            if self._hip.hipEventCreate(ctypes.byref(h)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if self._hip.hipEventCreateWithFlags(ctypes.byref(h), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             self.handles.append(h.value)
+
+    def record(self, i, stream=None):
+        if self._hip.hipEventRecord(self.handles[i], _stream(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, i, j):
         ms = ctypes.c_float()
