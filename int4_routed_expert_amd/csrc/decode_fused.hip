@@ -145,13 +145,15 @@ struct GuBatch {
 // Row . x_t for every token, by one wave (load i of lane l takes K
 // [512i + 8l, 512i + 8l + 8) of the bf16 row, so each load reads 1 KB
 // contiguous; x from LDS in the same layout); token t's sum ends on lanes
-// 8t..8t+7 (all of them).
-template <int T>
-__device__ __forceinline__ float row_dot_tokens(const uint16_t *row, const uint4 (*xl)[kH / 8], int lane) {
+// 8t..8t+7 (all of them).  The row is requested first (row_load), so that
+// its loads are in flight while x is staged.
+__device__ __forceinline__ void row_load(const uint16_t *row, int lane, uint4 (&w)[4]) {
     const __amdgpu_buffer_rsrc_t rb = make_buf(row, kH * 2);
-    uint4 w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) w[i] = bload16_nt(rb, lane * 16 + 1024 * i, 0);
+}
+template <int T>
+__device__ __forceinline__ float row_dot_tokens(const uint4 (&w)[4], const uint4 (*xl)[kH / 8], int lane) {
     float v[8];
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -198,6 +200,14 @@ __global__ __launch_bounds__(512) void k_router_shared_small(const uint16_t *__r
     __shared__ float part[8][8];   // shared role: [wave][token]
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     if (blockIdx.x == 0 && tid < kFusedCounters) counters[tid * kFusedCounterStride] = 0;
+    // this wave's weight row (router row e, or gate (waves 0-3) / up (4-7) row
+    // c0 + (wave & 3) of the shared expert), requested before x is staged
+    const bool router = (int)blockIdx.x < kRouterWgs;
+    const int e = 8 * (int)blockIdx.x + wave;
+    const int c0 = ((int)blockIdx.x - kRouterWgs) * 4;
+    uint4 w[4];
+    row_load(router ? router_w + (size_t)e * kH : shared_gu + (size_t)((wave < 4 ? 0 : kIS) + c0 + (wave & 3)) * kH,
+             lane, w);
     if (!RESID) {
 #pragma unroll
         for (int i = 0; i < (T * (kH / 8) + 511) / 512; ++i) {
@@ -235,15 +245,11 @@ __global__ __launch_bounds__(512) void k_router_shared_small(const uint16_t *__r
     }
     __syncthreads();
     const int t = lane >> 3;
-    if ((int)blockIdx.x < kRouterWgs) {
-        const int e = 8 * (int)blockIdx.x + wave;
-        const float sum = row_dot_tokens<T>(router_w + (size_t)e * kH, xl, lane);
+    const float sum = row_dot_tokens<T>(w, xl, lane);
+    if (router) {
         if ((lane & 7) == 0 && t < T) logits[(size_t)t * kE + e] = sum + (bias ? bias[e] : 0.0f);
         return;
     }
-    const int c0 = ((int)blockIdx.x - kRouterWgs) * 4;
-    const int row = (wave < 4 ? 0 : kIS) + c0 + (wave & 3);
-    const float sum = row_dot_tokens<T>(shared_gu + (size_t)row * kH, xl, lane);
     if ((lane & 7) == 0) part[wave][t] = sum;
     __syncthreads();
     if (tid < 4 * T) {
