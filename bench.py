@@ -76,7 +76,6 @@ STAGE_KERNELS_GEMV = {
     "router_shared_gateup": ("k_skinny", ["skinny_mfma.hip"]),
     "topk_sort": ("k_topk_rotate", ["router.hip", "token_ops.h"]),
     "routed_gateup": ("k_gateup_dec", ["experts_gemv.hip", "gemv_ops.h"]),
-    "rotate_act": ("k_rotate_act", ["experts_gemv.hip", "gemv_ops.h"]),
     "routed_down": ("k_down_dec", ["experts_gemv.hip", "gemv_ops.h"]),
     "shared_down_combine": ("k_skinny", ["skinny_mfma.hip"]),
 }
@@ -559,8 +558,8 @@ def main():
         "router_shared_gateup": ROUTER_BYTES + 2 * 1024 * 2048 * 2 + act + T * 256 * 4 + T * 1024 * 2,
         "topk_sort": T * 256 * 4 + act + T * 6 * 4 * 4 + 257 * 4 + 256 * 32,
         "routed_gateup": n_touched * EXPERT_GU_BYTES + T * 6 * 512 * 2,
-        "rotate_act": 2 * T * 6 * 512 * 2,
-        "routed_down": n_touched * EXPERT_D_BYTES + T * 6 * 2048 * 4,
+        # the GEMV down launch reads a (fp32) and rotates it itself
+        "routed_down": n_touched * EXPERT_D_BYTES + T * 6 * 512 * 4 + T * 6 * 2048 * 4,
         "shared_down_combine": 1024 * 2048 * 2 + T * 1024 * 2 + T * 6 * 2048 * 4 + act,
     }
     if T <= FUSED_MAX_TOKENS:

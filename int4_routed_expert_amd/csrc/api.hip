@@ -221,9 +221,9 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     } else {
         MOE_STEP(launch_gateup_gemv(codes, scales, xt, xt_scale, perm, active, T, act, s));
         MOE_MARK();
-        MOE_STEP(launch_rotate_act(act, T, at, at_scale, s));
+        // the down launch rotates a itself: the rotate_act stage is empty
         MOE_MARK();
-        MOE_STEP(launch_down_gemv(codes, scales, at, at_scale, active, T, o, s));
+        MOE_STEP(launch_down_gemv(codes, scales, act, active, T, o, s));
         MOE_MARK();
     }
     if (grouped) {

@@ -128,25 +128,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
 }
 
 // =========================================================================
-// a -> fp16 operands of the down projection, once per assignment: Hadamard on
-// each of the four 128-blocks of a = silu(g)*u (one wave per assignment, lane
-// l owns 8 values), a power-of-two prescale per block, stored in the
-// int4x8_to_q operand order.
-// =========================================================================
-__global__ __launch_bounds__(256) void k_rotate_act(const float *__restrict__ act, int n_rows,
-                                                    uint32_t *__restrict__ at, float *__restrict__ at_scale) {
-    const int lane = threadIdx.x & 63;
-    const int p = blockIdx.x * 4 + wave_id();
-    if (p >= n_rows) return;
-    const float4 *src = reinterpret_cast<const float4 *>(act + (size_t)p * kI + lane * 8);
-    rotate_act_wave(src[0], src[1], lane, at + (size_t)p * (kI / 2), at_scale + (size_t)p * (kI / kG));
-}
-
-// =========================================================================
 // down.  A wave item is (active expert slot, rows [n0, n0 + 4*kDnLoads)):
 // 8 KB of codes in kDnLoads wave loads (4 rows each; 16 lanes per row, lane
 // j = lane & 15 owns K [32j, 32j+32), inside block j/4), all requested as
-// soon as the expert is known.
+// soon as the expert is known.  The four waves of a workgroup share one
+// expert; while their codes are in flight they turn up to four of its
+// assignments' a = silu(g)*u into fp16 operands in LDS (wave w: assignment
+// w; Hadamard per 128-block and a power-of-two prescale per block, as the
+// down projection's rotated basis needs).
 // =========================================================================
 constexpr int kDnLoads = 8;
 
@@ -169,10 +158,11 @@ __device__ __forceinline__ void dn_load(DnRows &R, rsrc_t cd, rsrc_t sp, uint32_
     }
 }
 
+// at, at_scale: the NT assignments' operands in LDS (rows of kI/2 words and
+// kI/kG block multipliers); p0: the sorted position of the first.
 template <int NT>
-__device__ __forceinline__ void dn_compute(DnRows &R, int n0, const uint32_t *__restrict__ at,
-                                           const float *__restrict__ at_scale, int p0, int n_valid, int lane,
-                                           float *__restrict__ o) {
+__device__ __forceinline__ void dn_compute(DnRows &R, int n0, const uint32_t *at, const float *at_scale, int p0,
+                                           int n_valid, int lane, float *__restrict__ o) {
     constexpr int kPerRed = 2;                 // wave loads per reduction
     constexpr int V = kPerRed * NT;
     constexpr int kLogV = __builtin_ctz(V);
@@ -181,9 +171,9 @@ __device__ __forceinline__ void dn_compute(DnRows &R, int n0, const uint32_t *__
     float off[NT], mult[NT];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-        const int p = p0 + min(n, n_valid - 1);
-        off[n] = load_operand32(at + (size_t)p * (kI / 2) + j * 16, xs[n]);
-        mult[n] = at_scale[(size_t)p * (kI / kG) + (j >> 2)];
+        const int q = min(n, n_valid - 1);
+        off[n] = load_operand32(at + q * (kI / 2) + j * 16, xs[n]);
+        mult[n] = at_scale[q * (kI / kG) + (j >> 2)];
     }
 #pragma unroll
     for (int q0 = 0; q0 < kDnLoads; q0 += kPerRed) {
@@ -206,12 +196,16 @@ __device__ __forceinline__ void dn_compute(DnRows &R, int n0, const uint32_t *__
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_down_dec(
-    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, const uint32_t *__restrict__ at,
-    const float *__restrict__ at_scale, const int *__restrict__ slots, float *__restrict__ o) {
+    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, const float *__restrict__ act,
+    const int *__restrict__ slots, float *__restrict__ o) {
     constexpr int kRows = 4 * kDnLoads;
     constexpr int kItems = kH / kRows;
+    static_assert(kItems % 4 == 0, "the four waves of a workgroup must share one expert");
+    __shared__ uint32_t at[4][kI / 2];
+    __shared__ float at_scale[4][kI / kG];
+    const int wave = wave_id();
     const int lane = threadIdx.x & 63;
-    const int item = blockIdx.x * 4 + wave_id();
+    const int item = blockIdx.x * 4 + wave;
     const int *rec = slots + 8 * (item / kItems);   // {expert, p_begin, n, ...}
     const int e = rec[0];
     if (e < 0) return;
@@ -221,18 +215,40 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
     const rsrc_t cd = make_buf(codes + (size_t)e * kCodeBytesPerExpert + kCodeBytesGu, kCodeBytesPerExpert - kCodeBytesGu);
     const rsrc_t sp = make_buf(scales + (size_t)e * kScalesPerExpert + kScalesGu, 2 * (kScalesPerExpert - kScalesGu));
     const uint32_t cv = rsub * (kI / 2) + j * 16, sv = 2 * (rsub * (kI / kG) + (j >> 2));
+    // a of the assignment p (wave w: p = c + w), requested before the codes so
+    // that the rotation waits only for it; its operands go to LDS slot w
+    float4 a0, a1;
+    auto load_a = [&](int p) {
+        const rsrc_t ab = make_buf(act + (size_t)p * kI, kI * 4);
+        a0 = __builtin_bit_cast(float4, bload16(ab, lane * 32, 0));
+        a1 = __builtin_bit_cast(float4, bload16(ab, lane * 32 + 16, 0));
+    };
+    auto rotate = [&]() { rotate_act_wave(a0, a1, lane, at[wave], at_scale[wave]); };
     DnRows R;
     if (n == 1) {   // the common decode case
+        if (wave == 0) load_a(p_begin);
         dn_load<false>(R, cd, sp, cv, sv, n0);
-        dn_compute<1>(R, n0, at, at_scale, p_begin, 1, lane, o);
+        if (wave == 0) rotate();
+        __syncthreads();
+        dn_compute<1>(R, n0, at[0], at_scale[0], p_begin, 1, lane, o);
         return;
     }
-    // two or more tokens, two at a time through one call site; volatile
-    // reloads (L2 hits) keep the rows loop-variant
+    // two or more tokens: four assignments per round of operands, two at a
+    // time through one call site; volatile reloads (L2 hits) keep the rows
+    // loop-variant
     const int p_end = p_begin + n;
-    for (int p0 = p_begin; p0 < p_end; p0 += 2) {
+    for (int c = p_begin; c < p_end; c += 4) {
+        const bool mine = c + wave < p_end;
+        if (mine) load_a(c + wave);
         dn_load<true>(R, cd, sp, cv, sv, n0);
-        dn_compute<2>(R, n0, at, at_scale, p0, min(2, p_end - p0), lane, o);
+        if (c != p_begin) __syncthreads();   // every wave is done with the last round's operands
+        if (mine) rotate();
+        __syncthreads();
+        const int m = min(4, p_end - c);
+        for (int q = 0; q < m; q += 2) {
+            if (q) dn_load<true>(R, cd, sp, cv, sv, n0);
+            dn_compute<2>(R, n0, at[q], at_scale[q], c + q, min(2, m - q), lane, o);
+        }
     }
 }
 
@@ -246,17 +262,11 @@ void launch_gateup_gemv(const uint8_t *codes, const uint16_t *scales, const uint
                        perm, slots, act);
 }
 
-void launch_rotate_act(const float *act, int T, uint32_t *at, float *at_scale, hipStream_t s) {
-    const int n = kTopK * T;
-    hipLaunchKernelGGL(k_rotate_act, dim3((n + 3) / 4), dim3(256), 0, s, act, n, at, at_scale);
-}
-
-void launch_down_gemv(const uint8_t *codes, const uint16_t *scales, const uint32_t *at, const float *at_scale,
-                      const int *slots, int T, float *o, hipStream_t s) {
+void launch_down_gemv(const uint8_t *codes, const uint16_t *scales, const float *act, const int *slots, int T,
+                      float *o, hipStream_t s) {
     const int max_active = min(kE, kTopK * T);
     const int waves = max_active * (kH / (4 * kDnLoads));   // 64 items per expert
-    hipLaunchKernelGGL(k_down_dec, dim3((waves + 3) / 4), dim3(256), 0, s, codes, scales, at, at_scale, slots,
-                       o);
+    hipLaunchKernelGGL(k_down_dec, dim3((waves + 3) / 4), dim3(256), 0, s, codes, scales, act, slots, o);
 }
 
 }  // namespace moe_w4

@@ -91,7 +91,7 @@ __device__ __forceinline__ void rotate_act_wave(float4 a0, float4 a1, int lane, 
     w.z = pack_half2(ldexpf(v[2], -sh), ldexpf(v[6], -sh));
     w.w = pack_half2(ldexpf(v[3], -sh - 4), ldexpf(v[7], -sh - 4));
     reinterpret_cast<uint4 *>(at)[lane] = w;
-    if ((lane & 15) == 0) at_scale[lane >> 4] = ldexpf(1.0f, sh);
+    at_scale[lane >> 4] = ldexpf(1.0f, sh);   // the 16 lanes of a block store the same value
 }
 
 }  // namespace moe_w4

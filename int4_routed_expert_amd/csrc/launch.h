@@ -78,10 +78,10 @@ void launch_route_small(const float *logits, int T, const float *bias, int polic
 void launch_gateup_gemv(const uint8_t *codes, const uint16_t *scales, const uint32_t *xt,
                         const float *xt_scale, const int *perm, const int *slots, int T, float *act,
                         hipStream_t s);
-// a = silu(g)*u -> rotated fp16 operands (+ per-block power-of-two scales).
-void launch_rotate_act(const float *act, int T, uint32_t *at, float *at_scale, hipStream_t s);
-void launch_down_gemv(const uint8_t *codes, const uint16_t *scales, const uint32_t *at, const float *at_scale,
-                      const int *slots, int T, float *o, hipStream_t s);
+// Down projection of a = silu(g)*u (act, fp32, sorted positions); the launch
+// itself turns a into rotated fp16 operands (+ per-block power-of-two scales).
+void launch_down_gemv(const uint8_t *codes, const uint16_t *scales, const float *act, const int *slots, int T,
+                      float *o, hipStream_t s);
 
 // Routed experts, MFMA form (prefill): chunks of <= 96 assignments of one
 // expert against tiles of weight rows.  gate/up writes the rotated fp16
