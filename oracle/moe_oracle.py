@@ -21,6 +21,10 @@ Everything here is plain NumPy in float64 and follows the pages step by step:
   thread: sigmoid router, 6 of 256 experts, no router correction bias, and
   the normalisation policy max(sum of selected scores, 2**-14) with the six
   (index, fp32 weight) slots handed to the expert stage.
+* Flint NVFP4 repack (kekzle/Flint-NVFP4), rows "Layout per Linear" and
+  "Declaration": the second expert container, E2M1 codes with E4M3 block
+  scales per 16 columns and an F32 tensor scale, W4A16 (the section at the
+  end of this module, with its readings).
 
 Readings where the pages are silent (each is listed in the design doc too):
 
@@ -455,3 +459,112 @@ def unrotated_effective(codes: np.ndarray, s_bits: np.ndarray) -> np.ndarray:
     """Effective weight in the original basis: (code * scale) (I x Hn)."""
     w = codes.astype(np.float64) * np.repeat(bf16_to_f64(s_bits), G, axis=1)
     return rotate_blocks(w)
+
+
+# ------------------------------------------------------ NVFP4 expert format
+# The second 4-bit expert container of the pages (Flint NVFP4 repack,
+# kekzle/Flint-NVFP4, table rows "Repack", "Layout per Linear" and
+# "Declaration"): per Linear, E2M1 codes two per byte, one E4M3 block scale
+# per 16 columns and one F32 tensor scale, declared W4A16 (weights 4-bit,
+# activations 16-bit).  Readings (listed in DESIGN.md):
+#
+# * E2M1 and E4M3 are the OCP microscaling element and FP8 "FN" formats the
+#   names denote: E2M1 = sign, 2 exponent bits (bias 1), 1 mantissa bit,
+#   exponent 0 subnormal (0.5 * mantissa); E4M3 = sign, 4 exponent bits
+#   (bias 7), 3 mantissa bits, exponent 0 subnormal (mantissa * 2**-9), no
+#   infinities, S.1111.111 NaN.
+# * w[n, k] = e2m1(code[n, k]) * e4m3(scale[n, k // 16]) * tensor_scale, with
+#   "columns" the K (input) index of the row-major [out][in] weight; the code
+#   of even k sits in the low nibble of its byte.
+# * The weights stay in the original basis: no Hadamard on x or on a.
+# * W4A16 is read as "the activations are not quantised": the layer is the
+#   plain product with these weights, evaluated here exactly in float64
+#   (no bf16 rounding of the dequantised weights).
+NV_BLOCK = 16
+NV_CODE_BYTES_PER_EXPERT = (2 * I_R * H + H * I_R) // 2     # 1,572,864
+NV_SCALE_BYTES_PER_EXPERT = (2 * I_R * H + H * I_R) // 16   # 196,608
+
+
+def e2m1_value(code) -> np.ndarray:
+    """E2M1 code (0..15) -> float64."""
+    c = np.asarray(code, dtype=np.int64)
+    e = (c >> 1) & 3
+    m = (c & 1).astype(np.float64)
+    mag = np.where(e == 0, 0.5 * m, np.ldexp(1.0 + 0.5 * m, (e - 1).astype(np.int32)))
+    return np.where(c & 8, -mag, mag)
+
+
+def e4m3_value(byte) -> np.ndarray:
+    """E4M3 byte (0..255) -> float64 (NaN for S.1111.111)."""
+    b = np.asarray(byte, dtype=np.int64)
+    e = (b >> 3) & 15
+    m = (b & 7).astype(np.float64)
+    mag = np.where(e == 0, np.ldexp(m, -9), np.ldexp(1.0 + m / 8.0, (e - 7).astype(np.int32)))
+    mag = np.where((e == 15) & ((b & 7) == 7), np.nan, mag)
+    return np.where(b & 0x80, -mag, mag)
+
+
+def unpack_e2m1(packed: np.ndarray, k: int) -> np.ndarray:
+    """Packed bytes [..., k/2] -> E2M1 codes [..., k] (even k in the low nibble)."""
+    p = np.asarray(packed, dtype=np.uint8)
+    codes = np.empty(p.shape[:-1] + (k,), dtype=np.int64)
+    codes[..., 0::2] = p & 0x0F
+    codes[..., 1::2] = p >> 4
+    return codes
+
+
+def dequantize_nvfp4(packed_rows, scale_bytes, tensor_scale, k: int) -> np.ndarray:
+    """W[n, k] = e2m1(code[n, k]) * e4m3(scale[n, k // 16]) * tensor_scale, float64."""
+    s = e4m3_value(scale_bytes)
+    return (e2m1_value(unpack_e2m1(packed_rows, k)) * np.repeat(s, NV_BLOCK, axis=-1)
+            * float(np.float32(tensor_scale)))
+
+
+def nvfp4_expert_planes(code_bytes, scale_bytes, tensor_scales):
+    """One NVFP4 expert (library layout: codes gate [512][1024 B], up, down
+    [2048][256 B]; E4M3 scales gate [512][128], up, down [2048][32]; f32
+    tensor scales [gate, up, down]) -> dequantised gate, up, down."""
+    cb = np.asarray(code_bytes, dtype=np.uint8)
+    sb = np.asarray(scale_bytes, dtype=np.uint8)
+    ts = np.asarray(tensor_scales, dtype=np.float32)
+    nb = I_R * H // 2
+    ns = I_R * H // NV_BLOCK
+    wg = dequantize_nvfp4(cb[:nb].reshape(I_R, H // 2), sb[:ns].reshape(I_R, H // NV_BLOCK), ts[0], H)
+    wu = dequantize_nvfp4(cb[nb:2 * nb].reshape(I_R, H // 2), sb[ns:2 * ns].reshape(I_R, H // NV_BLOCK), ts[1], H)
+    wd = dequantize_nvfp4(cb[2 * nb:].reshape(H, I_R // 2), sb[2 * ns:].reshape(H, I_R // NV_BLOCK), ts[2], I_R)
+    return wg, wu, wd
+
+
+def moe_layer_nvfp4(x_bits, router_bits, expert_blobs, shared_bits, bias=None, tokens=None):
+    """The layer with NVFP4 experts: y = bf16( sum_j w_j * E_{e_j}(x) + S(x) ),
+    E(x) = Wd (silu(Wg x) * (Wu x)) on the unrotated x.
+
+    expert_blobs(e) -> (code bytes [1572864], E4M3 scale bytes [196608], f32
+    tensor scales [3]); the rest as in moe_layer (Flint router policy).
+    """
+    x = bf16_to_f64(x_bits)
+    T = x.shape[0]
+    rt = route(x, router_bits, bias)
+    srt = sort_assignments(rt["topk_idx"])
+    rows = np.arange(T) if tokens is None else np.asarray(tokens, dtype=np.int64)
+    routed = np.zeros((rows.size, H), dtype=np.float64)
+    need = {}
+    for r_i, t in enumerate(rows):
+        for j in range(K_TOP):
+            need.setdefault(int(rt["topk_idx"][t, j]), []).append((r_i, j))
+    for e in sorted(need):
+        wg, wu, wd = nvfp4_expert_planes(*expert_blobs(e))
+        lst = need[e]
+        ri = np.array([p[0] for p in lst])
+        jj = np.array([p[1] for p in lst])
+        xe = x[rows[ri]]
+        o = (silu(xe @ wg.T) * (xe @ wu.T)) @ wd.T
+        w = rt["topk_w"][rows[ri], jj]
+        for n in range(len(lst)):
+            routed[ri[n]] += w[n] * o[n]
+    z = shared_expert(x[rows], shared_bits)
+    y = routed + z
+    out = dict(rt)
+    out.update(srt)
+    out.update(rows=rows, routed=routed, shared=z, y=y, y_bits=f64_to_bf16_bits(y))
+    return out

@@ -75,6 +75,7 @@ KIND_CODE_G, KIND_CODE_U, KIND_CODE_D = 2, 3, 4
 KIND_SCALE_G, KIND_SCALE_U, KIND_SCALE_D = 5, 6, 7
 KIND_SH_G, KIND_SH_U, KIND_SH_D = 8, 9, 10
 KIND_BIAS = 11
+KIND_NV_SCALE, KIND_NV_TSCALE = 12, 13
 
 SIGMA_X = 1.0
 SIGMA_W = 0.02
@@ -232,6 +233,42 @@ def gen_codes_scales(seed: int, layer: int = 0, experts=None):
         codes[i] = expert_code_bytes(*gen_expert_codes_values(seed, layer, e))
         scales[i] = expert_scale_bits(*gen_expert_scales_bits(seed, layer, e))
     return codes, scales
+
+
+# ---- NVFP4 experts --------------------------------------------------------
+# Codes: the same random bytes as the int4 codes of the seed (every nibble
+# pattern is a valid E2M1 code, uniform over the 16).  Block scales: E4M3
+# bytes with sign 0, exponent field uniform in 0..4 and any mantissa (values
+# m * 2**-9 up to 1.875 * 2**-3, subnormals included).  Tensor scales: fp32
+# in [0.125, 0.25).  With uniform codes (rms 2.93) the weights have rms
+# about 0.03, like the int4 experts.
+NV_SCALE_BYTES_PER_EXPERT = 3 * INTER * HIDDEN // 16   # 196,608
+
+
+def nvfp4_scale_bytes(seed, tid, idx) -> np.ndarray:
+    r = draw(seed, tid, idx)
+    e = r % np.uint64(5)
+    m = (r >> np.uint64(8)) & np.uint64(7)
+    return ((e << np.uint64(3)) | m).astype(np.uint8)
+
+
+def gen_nvfp4_scales(seed: int, layer: int = 0, experts=None) -> np.ndarray:
+    """E4M3 block-scale bytes u8 [E][196608] (gate [512][128], up, down [2048][32])."""
+    experts = range(N_EXPERTS) if experts is None else list(experts)
+    experts = list(experts)
+    out = np.empty((len(experts), NV_SCALE_BYTES_PER_EXPERT), dtype=np.uint8)
+    base = np.arange(NV_SCALE_BYTES_PER_EXPERT, dtype=np.uint64)
+    for i, e in enumerate(experts):
+        out[i] = nvfp4_scale_bytes(seed, tensor_id(layer, KIND_NV_SCALE),
+                                   base + np.uint64(e * NV_SCALE_BYTES_PER_EXPERT))
+    return out
+
+
+def gen_nvfp4_tensor_scales(seed: int, layer: int = 0) -> np.ndarray:
+    """fp32 [256][3] tensor scales (gate, up, down) in [0.125, 0.25)."""
+    r = draw(seed, tensor_id(layer, KIND_NV_TSCALE), np.arange(3 * N_EXPERTS, dtype=np.uint64))
+    u = (r >> np.uint64(40)).astype(np.float64) / float(1 << 24)
+    return (0.125 * (1.0 + u)).astype(np.float32).reshape(N_EXPERTS, 3)
 
 
 def gen_shared(seed: int, layer: int = 0) -> np.ndarray:

@@ -635,3 +635,124 @@ def test_stack_with_shared_only_layers():
     # equal up to the rare double-rounding difference of fp64->fp32->bf16
     np.testing.assert_allclose(out, r.double().numpy(), rtol=1e-2, atol=1e-2)
     assert np.mean(out == r.double().numpy()) > 0.99
+
+
+# ------------------------------------------------------------ NVFP4 experts
+# E2M1 element values of the OCP microscaling format (the format the name
+# E2M1 denotes): codes 0..7 and the same magnitudes with the sign bit.
+E2M1_TABLE = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e2m1_table():
+    v = O.e2m1_value(np.arange(16))
+    np.testing.assert_array_equal(v[:8], E2M1_TABLE)
+    np.testing.assert_array_equal(v[8:], [-t for t in E2M1_TABLE])
+    assert math.copysign(1.0, v[8]) == -1.0          # code 8 is -0
+
+
+def test_e4m3_matches_torch_for_every_byte():
+    b = np.arange(256)
+    ours = O.e4m3_value(b)
+    ref = torch.tensor(b, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    assert np.isnan(ours).sum() == 2                  # S.1111.111 only
+    fin = ~np.isnan(ref)
+    np.testing.assert_array_equal(ours[fin], ref[fin])
+
+
+def test_e4m3_points():
+    assert O.e4m3_value(0x38) == 1.0
+    assert O.e4m3_value(0x7E) == 448.0                # largest finite
+    assert O.e4m3_value(0x01) == 2.0 ** -9            # smallest subnormal
+    assert O.e4m3_value(0x08) == 2.0 ** -6            # smallest normal
+    assert O.e4m3_value(0xB8) == -1.0
+
+
+def test_nvfp4_dequant_nibble_order_and_blocks():
+    # one row of K = 32: code of column k is k % 16 (even k in the low nibble),
+    # block scales 1.0 (0x38) and 2.0 (0x40), tensor scale 0.5
+    k = np.arange(32)
+    c = k % 16
+    packed = (c[0::2] | (c[1::2] << 4)).astype(np.uint8)[None, :]
+    w = O.dequantize_nvfp4(packed, np.array([[0x38, 0x40]], dtype=np.uint8), np.float32(0.5), 32)[0]
+    table = E2M1_TABLE + [-t for t in E2M1_TABLE]
+    expect = [table[ki % 16] * (1.0 if ki < 16 else 2.0) * 0.5 for ki in k]
+    np.testing.assert_array_equal(w, expect)
+
+
+def _nv_onehot_blob(k0, r1, cg, cu, cd, sbytes, ts):
+    """Every gate/up row r has one code, cg[r] / cu[r], at column k0; every down
+    row n one code cd[n] at column r1; each plane's block holding it has scale
+    byte sbytes[plane]; tensor scales ts."""
+    cb = np.zeros(O.NV_CODE_BYTES_PER_EXPERT, dtype=np.uint8)
+    sb = np.zeros(O.NV_SCALE_BYTES_PER_EXPERT, dtype=np.uint8)
+    H, I = O.H, O.I_R
+    shift = 4 * (k0 & 1)
+    for r in range(I):
+        cb[r * (H // 2) + k0 // 2] |= np.uint8(cg[r] << shift)
+        cb[I * H // 2 + r * (H // 2) + k0 // 2] |= np.uint8(cu[r] << shift)
+        sb[r * (H // 16) + k0 // 16] = sbytes[0]
+        sb[I * H // 16 + r * (H // 16) + k0 // 16] = sbytes[1]
+    dshift = 4 * (r1 & 1)
+    for n in range(H):
+        cb[I * H + n * (I // 2) + r1 // 2] |= np.uint8(cd[n] << dshift)
+        sb[2 * I * H // 16 + n * (I // 16) + r1 // 16] = sbytes[2]
+    return cb, sb, np.asarray(ts, dtype=np.float32)
+
+
+def test_nvfp4_layer_one_hot_closed_form():
+    T, k0, r1 = 3, 1001, 77
+    rng = np.random.default_rng(5)
+    cg = rng.integers(0, 16, O.I_R)
+    cu = rng.integers(0, 16, O.I_R)
+    cd = rng.integers(0, 16, O.H)
+    sbytes = (0x30, 0x3C, 0x28)                       # 0.5, 1.5, 0.25
+    svals = (0.5, 1.5, 0.25)
+    ts = (0.5, 0.25, 2.0)
+    blob = _nv_onehot_blob(k0, r1, cg, cu, cd, sbytes, ts)
+    x_bits = synth.gen_x(3, T)
+    router, shared = synth.gen_router(3), synth.gen_shared(3)
+    out = O.moe_layer_nvfp4(x_bits, router, lambda e: blob, shared)
+    table = E2M1_TABLE + [-t for t in E2M1_TABLE]
+    x = O.bf16_to_f64(x_bits)
+    for t in range(T):
+        xk = x[t, k0]
+        g = table[cg[r1]] * svals[0] * ts[0] * xk
+        u = table[cu[r1]] * svals[1] * ts[1] * xk
+        a = g / (1.0 + math.exp(-g)) * u
+        # every expert is the same; the six weights sum to 1 (sum of sigmoids > 2**-14)
+        o = np.array([table[c] for c in cd]) * svals[2] * ts[2] * a
+        np.testing.assert_allclose(out["routed"][t], o * out["topk_w"][t].sum(), rtol=1e-12, atol=1e-300)
+        assert abs(out["topk_w"][t].sum() - 1.0) < 1e-12
+    np.testing.assert_allclose(out["y"], out["routed"] + out["shared"], rtol=0, atol=0)
+
+
+def test_nvfp4_layer_zero_codes_leave_the_shared_expert():
+    T = 2
+    blob = (np.zeros(O.NV_CODE_BYTES_PER_EXPERT, np.uint8), synth.gen_nvfp4_scales(1, 0, [0])[0],
+            np.ones(3, np.float32))
+    x_bits = synth.gen_x(1, T)
+    out = O.moe_layer_nvfp4(x_bits, synth.gen_router(1), lambda e: blob, synth.gen_shared(1))
+    assert np.all(out["routed"] == 0.0)
+    z = O.shared_expert(O.bf16_to_f64(x_bits), synth.gen_shared(1))
+    np.testing.assert_array_equal(out["y_bits"], O.f64_to_bf16_bits(z))
+
+
+def test_nvfp4_layer_scales_with_the_down_tensor_scale():
+    # the routed part is linear in the down plane's tensor scale (exact in fp64
+    # for a power of two)
+    T = 2
+    cache = {}
+
+    def blob(e):
+        if e not in cache:
+            cache[e] = (synth.gen_codes_scales(2, 0, experts=[e])[0][0], synth.gen_nvfp4_scales(2, 0, [e])[0])
+        return cache[e]
+    ts = synth.gen_nvfp4_tensor_scales(2)
+    ts2 = ts.copy()
+    ts2[:, 2] *= 4
+    x_bits = synth.gen_x(2, T)
+    r, sh = synth.gen_router(2), synth.gen_shared(2)
+    a = O.moe_layer_nvfp4(x_bits, r, lambda e: blob(e) + (ts[e],), sh)
+    b = O.moe_layer_nvfp4(x_bits, r, lambda e: blob(e) + (ts2[e],), sh)
+    np.testing.assert_array_equal(b["routed"], 4 * a["routed"])
