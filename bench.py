@@ -30,6 +30,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA, published
 EXPERT_GU_BYTES = 1_048_576 + 32_768      # one expert's [gate; up] codes + scales
 EXPERT_D_BYTES = 524_288 + 16_384         # one expert's down codes + scales
 EXPERT_BYTES = EXPERT_GU_BYTES + EXPERT_D_BYTES
+NV_GU_BYTES = 1_048_576 + 131_072 + 8     # one NVFP4 expert's [gate; up] codes, E4M3 scales, tensor scales
+NV_D_BYTES = 524_288 + 65_536 + 4          # its down codes, scales, tensor scale
 ROUTER_BYTES = 256 * 2048 * 2
 SHARED_BYTES = 3 * 1024 * 2048 * 2
 
@@ -45,7 +47,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="decode_t32",
                     choices=["decode_t1", "decode_t32", "prefill_t2048", "prefill_t2048_skew", "stack_t1", "stack_t8",
-                             "pack_layer", "mlp_t1", "mlp_t2048"])
+                             "pack_layer", "mlp_t1", "mlp_t2048", "nvfp4_t1", "nvfp4_t32"])
     ap.add_argument("--layers", type=int, default=0, help="distinct layers rotated through (0 = auto)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--eager", action="store_true",
@@ -91,9 +93,17 @@ STAGE_KERNELS_GROUPED = {
 STAGE_KERNELS_PACK = {"pack": ("k_pack_groups", ["pack.hip"])}
 
 
-def stage_kernels(T):
+STAGE_KERNELS_NVFP4 = {
+    "routed_gateup": ("k_gateup_nv", ["nvfp4.hip", "gemv_ops.h", "token_ops.h"]),
+    "routed_down": ("k_down_nv", ["nvfp4.hip", "gemv_ops.h", "token_ops.h"]),
+}
+
+
+def stage_kernels(T, workload=""):
     if T is None:   # the packer workload
         return STAGE_KERNELS_PACK
+    if workload.startswith("nvfp4"):
+        return STAGE_KERNELS_NVFP4
     if T <= FUSED_MAX_TOKENS:
         return STAGE_KERNELS_FUSED
     if T >= GROUPED_MIN_TOKENS:
@@ -121,7 +131,7 @@ def sources_digest(files):
 def recorded_traffic(workload, stage, T):
     """HBM bytes per launch recorded from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
     (profiles/hbm_traffic.txt), or None if absent or the kernel has changed."""
-    kern, files = stage_kernels(T).get(stage, (None, None))
+    kern, files = stage_kernels(T, workload).get(stage, (None, None))
     path = os.path.join(HERE, "profiles", "hbm_traffic.txt")
     if kern is None or not os.path.exists(path):
         return None
@@ -177,14 +187,19 @@ def counter_means(path):
 def traffic_lines(workload, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
     """Record lines: counters scaled by what they read for a plain copy of known size."""
     import synth
-    T = None if workload == "pack_layer" else synth.CONFIGS[workload]["T"]
+    if workload == "pack_layer":
+        T = None
+    elif workload.startswith("nvfp4_t"):
+        T = int(workload[7:])
+    else:
+        T = synth.CONFIGS[workload]["T"]
     copy_kib = 256 * 1024   # one calibration copy: 256 MiB read and written
     ffac = copy_kib / counter_means(cal_fetch_csv)["__amd_rocclr_copyBuffer"]
     wfac = copy_kib / counter_means(cal_write_csv)["__amd_rocclr_copyBuffer"]
     fetch, write = counter_means(fetch_csv), counter_means(write_csv)
     print(f"# {workload}: FETCH_SIZE x {ffac:.5f}, WRITE_SIZE x {wfac:.5f}")
     seen = set()
-    for stage, (kern, files) in stage_kernels(T).items():
+    for stage, (kern, files) in stage_kernels(T, workload).items():
         for name in sorted(fetch):
             if name.startswith(kern) and name not in seen and name in write:
                 seen.add(name)
@@ -222,6 +237,118 @@ def cpu_baseline(cfg, T, x_bits, bias, budget_s):
     return {"value": n_tok / per_rep, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{reps} oracle layer calls on {n_tok} of the {T} tokens (fp64 NumPy, routing of all "
                       f"{T} tokens included), {per_rep:.2f} s each"}
+
+
+def bench_nvfp4(a, T):
+    """The layer with NVFP4 experts (moe_w4_forward_nvfp4) at T tokens: the
+    seeded layers of the int4 decode configs (their code bytes read as E2M1
+    codes) with seeded E4M3 block scales and fp32 tensor scales.  Roofline of
+    the dominant stage: HBM (the expert GEMVs stream codes and scales)."""
+    import torch
+    import synth
+    from int4_routed_expert_amd import moe_w4 as m
+    from oracle import moe_oracle as O
+    cfg = synth.CONFIGS["decode_t1" if T == 1 else "decode_t32"]
+    assert cfg["T"] == T
+    n_layers = a.layers or 4
+    log(f"config {a.config}: T={T}, {n_layers} layers with NVFP4 experts on the device")
+    layers = []
+    for l in range(n_layers):
+        w = m.generated_layer(cfg["w_seed"], l)
+        w["nv_scales"] = torch.from_numpy(synth.gen_nvfp4_scales(cfg["w_seed"], l).ravel().copy()).cuda()
+        w["nv_tscales"] = torch.from_numpy(synth.gen_nvfp4_tensor_scales(cfg["w_seed"], l).ravel().copy()).cuda()
+        layers.append(w)
+    x_bits = synth.gen_x(cfg["x_seed"], T)
+    x = torch.from_numpy(x_bits.view(np.int16)).cuda()
+    y = torch.empty((T, 2048), dtype=torch.int16, device="cuda")
+    ws = m.workspace(T)
+    n_pts = m.moe_w4_profile_points()
+    names = [m.moe_w4_profile_point_name(i) for i in range(n_pts)]
+
+    def step(i, ev=None):
+        w = layers[i % n_layers]
+        if ev is None:
+            m.moe_w4_forward_nvfp4(x, w["router_w"], w["codes"], w["nv_scales"], w["nv_tscales"], w["shared_w"], y, ws)
+        else:
+            m.moe_w4_forward_nvfp4_profiled(x, w["router_w"], w["codes"], w["nv_scales"], w["nv_tscales"],
+                                            w["shared_w"], y, ws, ev)
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / a.steps
+    log(f"timed {a.steps} steps: {ms * 1e3:.1f} us/step")
+    events = m.HipEvents(a.steps * n_pts)
+    for i in range(a.steps):
+        step(i, events.handles[i * n_pts:(i + 1) * n_pts])
+    torch.cuda.synchronize()
+    stage_ms = np.zeros(n_pts - 1)
+    for i in range(a.steps):
+        for k in range(n_pts - 1):
+            stage_ms[k] += events.elapsed_ms(i * n_pts + k, i * n_pts + k + 1)
+    stage_ms /= a.steps
+    events.close()
+    touched = []
+    for l in range(min(n_layers, a.steps)):
+        step(l)
+        torch.cuda.synchronize()
+        touched.append(int(m.ws_view(ws, T, "n_active", torch.int32, 1).item()))
+    n_touched = float(np.mean(touched))
+    act = T * 2048 * 2
+    layer_bytes = n_touched * (NV_GU_BYTES + NV_D_BYTES) + ROUTER_BYTES + SHARED_BYTES + 2 * act
+    stage = dict(zip(names[1:], stage_ms))
+    dom = max(stage, key=stage.get)
+    stage_bytes = {
+        "router_shared_gateup": ROUTER_BYTES + 2 * 1024 * 2048 * 2 + act + T * 256 * 4 + T * 1024 * 2,
+        "topk_sort": T * 256 * 4 + T * 6 * 4 * 4 + 257 * 4 + 256 * 32,
+        "routed_gateup": n_touched * NV_GU_BYTES + act + T * 6 * 512 * 4,
+        "routed_down": n_touched * NV_D_BYTES + T * 6 * 512 * 4 + T * 6 * 2048 * 4,
+        "shared_down_combine": 1024 * 2048 * 2 + T * 1024 * 2 + T * 6 * 2048 * 4 + act,
+    }
+    dom_bytes = stage_bytes.get(dom, 0.0)
+    achieved = dom_bytes / (stage[dom] * 1e-3) / 1e9
+    result = {
+        "metric": "routed-MoE layer tokens/s, NVFP4 experts (W4A16)", "value": T / (ms / 1e3), "unit": "tokens/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "e2m1 x fp16 -> fp32",
+        "data": "synthetic (seeded SplitMix64; random-init weights)",
+        "config": {"workload": f"{a.config}: one MoE layer with NVFP4 experts, T={T}, x seed {cfg['x_seed']}, "
+                               f"weights seed {cfg['w_seed']}", "T": T, "layers_rotated": n_layers,
+                   "touched_experts": n_touched},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(a.config, dom, T),
+                     "algorithmic_bytes": dom_bytes, "kernel_us": stage[dom] * 1e3},
+        "layer": {"algorithmic_bytes": layer_bytes, "hbm_gbs": layer_bytes / (ms * 1e-3) / 1e9,
+                  "hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                  "stage_us": {k: v * 1e3 for k, v in stage.items()}},
+    }
+    if not a.no_cpu:
+        log("timing the CPU oracle baseline")
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+        except Exception:
+            cores = os.cpu_count()
+        R, S = synth.gen_router(cfg["w_seed"], 0), synth.gen_shared(cfg["w_seed"], 0)
+        rt = O.route(O.bf16_to_f64(x_bits), R)
+        sc, ts = synth.gen_nvfp4_scales(cfg["w_seed"], 0), synth.gen_nvfp4_tensor_scales(cfg["w_seed"], 0)
+        blobs = {}
+        for e in sorted(set(rt["topk_idx"].ravel().tolist())):   # input preparation, not timed
+            blobs[e] = (synth.gen_codes_scales(cfg["w_seed"], 0, experts=[e])[0][0], sc[e], ts[e])
+        reps, elapsed = 0, 0.0
+        while elapsed < a.cpu_seconds and reps < 50:
+            t0 = time.perf_counter()
+            O.moe_layer_nvfp4(x_bits, R, blobs.__getitem__, S)
+            elapsed += time.perf_counter() - t0
+            reps += 1
+        per_rep = elapsed / reps
+        result["cpu_baseline"] = {"value": T / per_rep, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
+                                  "sample": f"{reps} oracle layer calls on all {T} tokens (fp64 NumPy), "
+                                            f"{per_rep:.2f} s each"}
+    print(json.dumps(result), flush=True)
 
 
 def bench_pack(a):
@@ -407,6 +534,9 @@ def main():
         return
     if a.config.startswith("mlp_t"):
         bench_mlp(a, int(a.config[5:]))
+        return
+    if a.config.startswith("nvfp4_t"):
+        bench_nvfp4(a, int(a.config[7:]))
         return
     import torch
     import synth

@@ -162,6 +162,36 @@ int moe_w4_forward_profiled(const void *x, const void *router_w, const void *cod
                             const float *router_bias, void *workspace, size_t workspace_bytes,
                             void *stream, void *const *events, int n_events);
 
+/* The layer with routed experts in the NVFP4 container instead of int4 (Flint
+ * NVFP4 repack, kekzle/Flint-NVFP4, rows "Layout per Linear" and
+ * "Declaration": per Linear E2M1 codes two per byte, one E4M3 block scale per
+ * 16 columns, one F32 tensor scale; W4A16).  Read as
+ *   w[n][k] = e2m1(code[n][k]) * e4m3(scale[n][k / 16]) * tensor_scale
+ * (OCP E2M1: sign, 2 exponent bits bias 1, 1 mantissa bit; OCP E4M3 "FN":
+ * sign, 4 exponent bits bias 7, 3 mantissa bits, S.1111.111 NaN), weights in
+ * the original basis (x and a are not rotated), activations not quantised.
+ * Router, shared expert, routing and combine are those of moe_w4_forward
+ * (Flint's router policy); expert outputs are fp32 sums of exact products.
+ * codes: u8, expert e at e * MOE_W4_NVFP4_CODE_BYTES: gate [512][1024], up
+ *        [512][1024], down [2048][256]; code of even k in the low nibble.
+ * scales: u8 E4M3, expert e at e * MOE_W4_NVFP4_SCALE_BYTES: gate [512][128],
+ *        up [512][128], down [2048][32] (block k / 16 of row n).
+ * tensor_scales: f32 [256][3] (gate, up, down), 4-byte aligned device pointer.
+ * Other arguments, the workspace and the errors as moe_w4_forward (EINVAL
+ * also for a NULL or misaligned tensor_scales).  A NaN scale byte gives NaN
+ * outputs for the tokens routed to that expert. */
+#define MOE_W4_NVFP4_CODE_BYTES 1572864
+#define MOE_W4_NVFP4_SCALE_BYTES 196608
+int moe_w4_forward_nvfp4(const void *x, const void *router_w, const void *codes, const void *scales,
+                         const float *tensor_scales, const void *shared_w, int64_t T, void *y,
+                         const float *router_bias, void *workspace, size_t workspace_bytes, void *stream);
+/* The same with the timing events of moe_w4_forward_profiled (the rotate_act
+ * point follows routed_gateup with nothing between them). */
+int moe_w4_forward_nvfp4_profiled(const void *x, const void *router_w, const void *codes, const void *scales,
+                                  const float *tensor_scales, const void *shared_w, int64_t T, void *y,
+                                  const float *router_bias, void *workspace, size_t workspace_bytes,
+                                  void *stream, void *const *events, int n_events);
+
 /* Seeded synthetic weights of one layer, written on the device with the
  * counter-based SplitMix64 generator (Steele, Lea and Flood, OOPSLA 2014):
  *   r(seed, tid, i) = mix64(mix64(seed*G + tid) + (i+1)*G), G = 0x9E3779B97F4A7C15,

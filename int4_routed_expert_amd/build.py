@@ -24,7 +24,7 @@ ARCH = "gfx950"
 
 SOURCES = ["api.hip", "router.hip", "skinny_mfma.hip", "experts_gemv.hip", "grouped_mfma.hip", "dense_mfma.hip",
            "stack.hip", "decode_fused.hip",
-           "generate.hip", "pack.hip"]
+           "generate.hip", "pack.hip", "nvfp4.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CFLAGS = [

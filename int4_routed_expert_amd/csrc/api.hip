@@ -9,6 +9,9 @@
 #include "token_ops.h"
 
 static_assert(MOE_W4_EXPERT_WEIGHTS == 2 * moe_w4::kCodeBytesPerExpert, "two int4 codes per byte");
+static_assert(MOE_W4_NVFP4_CODE_BYTES == moe_w4::kCodeBytesPerExpert &&
+                  MOE_W4_NVFP4_SCALE_BYTES == 3 * moe_w4::kI * moe_w4::kH / 16,
+              "NVFP4 expert layout");
 static_assert(MOE_W4_DENSE_INTER == moe_w4::kDenseInter && MOE_W4_DENSE_WEIGHTS == 3 * moe_w4::kDenseInter * moe_w4::kH,
               "dense MLP shape");
 static_assert(MOE_W4_ROUTER_NORM_FLOOR == moe_w4::kNormFloor && MOE_W4_ROUTER_NORM_SUM == moe_w4::kNormSum &&
@@ -237,6 +240,91 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     return MOE_W4_OK;
 }
 
+// The layer with NVFP4 experts: the router, the shared expert, the routing
+// and the combine of the int4 path (no rotated x is needed), the experts as
+// NVFP4 GEMVs at every token count.  Stage marks as in run_forward (the
+// rotate_act stage is empty).
+int run_forward_nvfp4(const void *x_, const void *router_w_, const void *codes_, const void *scales_,
+                      const float *tscales, const void *shared_w_, int64_t T64, void *y_, const float *bias,
+                      void *ws, hipStream_t s, void *const *events, int n_events) {
+    const int T = (int)T64;
+    const moe_w4_ws_layout L = make_layout(T64);
+    const uint16_t *x = static_cast<const uint16_t *>(x_);
+    const uint16_t *router_w = static_cast<const uint16_t *>(router_w_);
+    const uint8_t *codes = static_cast<const uint8_t *>(codes_);
+    const uint8_t *scales = static_cast<const uint8_t *>(scales_);
+    const uint16_t *shared_w = static_cast<const uint16_t *>(shared_w_);
+    uint16_t *y = static_cast<uint16_t *>(y_);
+    float *logits = ws_at<float>(ws, L.logits);
+    int *topk_idx = ws_at<int>(ws, L.topk_idx);
+    float *topk_w = ws_at<float>(ws, L.topk_w);
+    int *offsets = ws_at<int>(ws, L.offsets);
+    int *perm = ws_at<int>(ws, L.perm);
+    int *pos = ws_at<int>(ws, L.pos);
+    int *n_active = ws_at<int>(ws, L.n_active);
+    int *active = ws_at<int>(ws, L.active);
+    uint32_t *xt = ws_at<uint32_t>(ws, L.xt);
+    float *xt_scale = ws_at<float>(ws, L.xt_scale);
+    float *act = ws_at<float>(ws, L.act);
+    uint16_t *hs = ws_at<uint16_t>(ws, L.hs);
+    float *o = ws_at<float>(ws, L.o);
+    float *z = ws_at<float>(ws, L.z);
+    int *chunks = ws_at<int>(ws, L.chunks);
+    int *n_chunks = ws_at<int>(ws, L.n_chunks);
+    const bool dense = T >= kPrefillMinTokens;
+    const bool small_route = T <= kRouteSmallMaxTokens;
+
+    int stage = 0;
+    int rc;
+    auto mark = [&](void) -> int {
+        if (events && stage < n_events) {
+            hipError_t e = hipEventRecord(static_cast<hipEvent_t>(events[stage]), s);
+            if (e != hipSuccess) return device_status(e);
+        }
+        ++stage;
+        return MOE_W4_OK;
+    };
+#define NV_STEP(call)                                                          \
+    do {                                                                       \
+        call;                                                                  \
+        if ((rc = device_status(hipGetLastError())) != MOE_W4_OK) return rc;   \
+    } while (0)
+#define NV_MARK()                                  \
+    do {                                           \
+        if ((rc = mark()) != MOE_W4_OK) return rc; \
+    } while (0)
+    (void)hipGetLastError();
+    NV_MARK();
+    if (dense)
+        NV_STEP(launch_router_and_shared_gateup_dense(x, T, router_w, nullptr, logits, shared_w, hs, s));
+    else
+        NV_STEP(launch_router_and_shared_gateup(x, T, router_w, nullptr, logits, shared_w, hs, nullptr, xt_scale, s));
+    NV_MARK();
+    if (small_route) {
+        NV_STEP(launch_route_small(logits, T, bias, 0, topk_idx, topk_w, offsets, perm, pos, n_active, active, chunks,
+                                   n_chunks, s));
+    } else {
+        // (the rotated x it also writes is not used by NVFP4 experts)
+        NV_STEP(launch_topk_rotate(logits, x, T, bias, 0, topk_idx, topk_w, xt, xt_scale, s));
+        NV_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, s));
+    }
+    NV_MARK();
+    NV_STEP(launch_gateup_nvfp4(codes, scales, tscales, x, perm, active, T, act, s));
+    NV_MARK();
+    NV_MARK();
+    NV_STEP(launch_down_nvfp4(codes, scales, tscales, act, active, T, o, s));
+    NV_MARK();
+    if (dense) {
+        NV_STEP(launch_shared_down_dense(shared_w, hs, T, z, s));
+        NV_STEP(launch_combine(z, topk_w, pos, o, T, y, s));
+    } else
+        NV_STEP(launch_shared_down_combine(shared_w, hs, T, topk_w, pos, o, y, s));
+    NV_MARK();
+#undef NV_STEP
+#undef NV_MARK
+    return MOE_W4_OK;
+}
+
 uint64_t host_mix64(uint64_t z) {
     z ^= z >> 30;
     z *= 0xBF58476D1CE4E5B9ull;
@@ -300,6 +388,25 @@ int moe_w4_forward_profiled(const void *x, const void *router_w, const void *cod
     if (rc != MOE_W4_OK || T == 0) return rc;
     return run_forward(x, router_w, codes, scales, shared_w, T, y, router_bias, workspace,
                        static_cast<hipStream_t>(stream), events, n_events);
+}
+
+int moe_w4_forward_nvfp4_profiled(const void *x, const void *router_w, const void *codes, const void *scales,
+                                  const float *tensor_scales, const void *shared_w, int64_t T, void *y,
+                                  const float *router_bias, void *workspace, size_t workspace_bytes, void *stream,
+                                  void *const *events, int n_events) {
+    if (n_events < 0 || (n_events > 0 && !events)) return MOE_W4_EINVAL;
+    int rc = validate_forward(x, router_w, codes, scales, shared_w, T, y, router_bias, workspace, workspace_bytes);
+    if (rc != MOE_W4_OK || T == 0) return rc;
+    if (!tensor_scales || !aligned(tensor_scales, 4)) return MOE_W4_EINVAL;
+    return run_forward_nvfp4(x, router_w, codes, scales, tensor_scales, shared_w, T, y, router_bias, workspace,
+                             static_cast<hipStream_t>(stream), events, n_events);
+}
+
+int moe_w4_forward_nvfp4(const void *x, const void *router_w, const void *codes, const void *scales,
+                         const float *tensor_scales, const void *shared_w, int64_t T, void *y,
+                         const float *router_bias, void *workspace, size_t workspace_bytes, void *stream) {
+    return moe_w4_forward_nvfp4_profiled(x, router_w, codes, scales, tensor_scales, shared_w, T, y, router_bias,
+                                         workspace, workspace_bytes, stream, nullptr, 0);
 }
 
 size_t moe_w4_dense_mlp_workspace_bytes(int64_t T) {

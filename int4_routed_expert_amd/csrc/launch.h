@@ -119,6 +119,15 @@ void launch_dense_mlp_down_skinny(const uint16_t *w, const uint16_t *h, int T, u
 void launch_dense_mlp_gateup_dense(const uint16_t *x, int T, const uint16_t *w, uint16_t *h, hipStream_t s);
 void launch_dense_mlp_down_dense(const uint16_t *w, const uint16_t *h, int T, uint16_t *y, hipStream_t s);
 
+// Routed experts in the NVFP4 container (E2M1 codes, E4M3 scales per 16 of
+// K, fp32 tensor scales [256][3]; original basis), GEMV form at every token
+// count, driven by the slot records: gate/up writes a = silu(g) * u (fp32,
+// sorted positions); down reads it and writes the expert rows o.
+void launch_gateup_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscales, const uint16_t *x,
+                         const int *perm, const int *slots, int T, float *act, hipStream_t s);
+void launch_down_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscales, const float *act,
+                       const int *slots, int T, float *o, hipStream_t s);
+
 // Stack glue: x_bf16 = bf16(rmsnorm(resid)); resid += f32(y).
 void launch_rmsnorm_bf16(const float *resid, int T, uint16_t *x, hipStream_t s);
 void launch_residual_add(float *resid, const uint16_t *y, int T, hipStream_t s);

@@ -1,0 +1,322 @@
+// Routed experts in the NVFP4 container (Flint NVFP4 repack, kekzle/Flint-NVFP4,
+// rows "Layout per Linear" and "Declaration"): per Linear, E2M1 codes two per
+// byte, one E4M3 block scale per 16 columns of K and one fp32 tensor scale;
+// the weights are in the original basis (no Hadamard) and the activations are
+// not quantised (W4A16).  The experts run as streaming GEMVs at every token
+// count, driven by the slot records of the sort like the int4 GEMVs.
+//
+// Arithmetic: an E2M1 value (0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives)
+// is an fp16 whose low byte is zero; its high byte comes from an 8-entry byte
+// table through v_perm_b32 and the sign bit is copied in.  The activations
+// become fp16 with a power-of-two prescale (largest magnitude in [2^13,
+// 2^14)), products are exact in v_dot2_f32_f16 and summed in fp32 per
+// 16-element block, the block's E4M3 scale (exact in fp32) multiplies that
+// block sum, and the tensor scale and the prescale multiply the row sum.
+//
+// Library layout per expert e (rows in the int4 layout's order):
+//   codes   e * 1,572,864 B: gate [512][1024 B], up [512][1024 B], down [2048][256 B]
+//           (two codes per byte, even K in the low nibble)
+//   scales  e * 196,608 B:   gate [512][128], up [512][128], down [2048][32] (E4M3)
+//   tensor  e * 3 floats:    gate, up, down
+#include "common.h"
+#include "gemv_ops.h"
+#include "launch.h"
+#include "token_ops.h"
+
+namespace moe_w4 {
+
+namespace {
+
+constexpr int kNvBlock = 16;
+constexpr uint32_t kNvScaleGate = (uint32_t)kI * kH / kNvBlock;                    // 65,536 bytes
+constexpr uint32_t kNvScaleGu = 2 * kNvScaleGate;                                  // 131,072
+constexpr uint32_t kNvScalePerExpert = kNvScaleGu + (uint32_t)kH * kI / kNvBlock;  // 196,608
+
+// fp16 high bytes of the E2M1 magnitudes 0..7 (low bytes are zero):
+// 0x00 0x38 0x3C 0x3E | 0x40 0x42 0x44 0x46  =  0, 0.5, 1, 1.5 | 2, 3, 4, 6.
+// v_perm_b32 byte selectors 0-3 pick bytes of its second source, 4-7 of the
+// first, 12 gives 0x00.
+constexpr uint32_t kE2m1Lo = 0x3E3C3800u;
+constexpr uint32_t kE2m1Hi = 0x46444240u;
+
+// Eight codes (nibble k = element k of an 8-group) -> four fp16 pairs
+// h[k] = (value k, value k + 4).
+__device__ __forceinline__ void e2m1x8_to_half(uint32_t w, uint32_t (&h)[4]) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t t = w << (12 - 4 * k);   // nibble k at bits 12-15, nibble k + 4 at 28-31
+        const uint32_t sel = ((t >> 4) & 0x07000700u) | 0x000c000cu;
+        const uint32_t mag = __builtin_amdgcn_perm(kE2m1Hi, kE2m1Lo, sel);
+        h[k] = mag | (t & 0x80008000u);
+    }
+}
+
+// E4M3 byte -> fp32 (exact): sign, 4 exponent bits (bias 7), 3 mantissa bits,
+// exponent 0 subnormal (m * 2^-9), S.1111.111 NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+    if (e == 15u && m == 7u) mag = __uint_as_float(0x7fc00000u);
+    return (b & 0x80u) ? -mag : mag;
+}
+
+// One lane's 32 codes (word i: elements 8i .. 8i + 7) against the operand words
+// xs[4i + k] = (x[8i + k], x[8i + k + 4]): s0 * (sum over elements 0..15) +
+// s1 * (sum over elements 16..31).
+__device__ __forceinline__ float dot32_nv(const uint4 c, const uint32_t (&xs)[16], float s0, float s1) {
+    uint32_t h[4];
+    float a0 = 0.0f, a1 = 0.0f;
+    e2m1x8_to_half(c.x, h);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a0 = dot2h(h[k], xs[k], a0);
+    e2m1x8_to_half(c.y, h);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a0 = dot2h(h[k], xs[4 + k], a0);
+    e2m1x8_to_half(c.z, h);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a1 = dot2h(h[k], xs[8 + k], a1);
+    e2m1x8_to_half(c.w, h);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) a1 = dot2h(h[k], xs[12 + k], a1);
+    return a0 * s0 + a1 * s1;
+}
+
+// Empty asm that "rewrites" a register quad, so that the conversion of codes
+// reused for several tokens is redone per token instead of being hoisted out
+// of the token loop (all converted rows would not fit in registers).
+__device__ __forceinline__ void refresh(uint4 &v) {
+    asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+}
+
+// =========================================================================
+// gate/up.  A wave item is (active expert slot, gate rows [r0, r0 + 4) and
+// the same up rows): 8 rows of 1 KiB, lane l owning K [32l, 32l + 32) of each
+// (16 bytes of codes, the 2 scale bytes of blocks 2l and 2l + 1), all
+// requested as soon as the expert is known.  Per token of the expert the
+// wave turns the token's x into fp16 operands (the whole row is in the
+// wave, so the prescale needs no other wave) and writes a = silu(g) * u.
+// =========================================================================
+constexpr int kNvGuPairs = 4;
+
+__global__ __launch_bounds__(256) void k_gateup_nv(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+                                                   const float *__restrict__ tscales, const uint16_t *__restrict__ x,
+                                                   const int *__restrict__ perm, const int *__restrict__ slots,
+                                                   float *__restrict__ act) {
+    constexpr int kItems = kI / kNvGuPairs;   // 128 per expert
+    const int lane = threadIdx.x & 63;
+    const int item = blockIdx.x * 4 + wave_id();
+    const int *rec = slots + 8 * (item / kItems);   // {expert, p_begin, n, ...}
+    const int e = rec[0];
+    if (e < 0) return;
+    const int p_begin = rec[1], n = rec[2];
+    const int r0 = (item % kItems) * kNvGuPairs;
+    const rsrc_t cres = make_buf(codes + (size_t)e * kCodeBytesPerExpert, (uint32_t)kCodeBytesGu);
+    const rsrc_t sres = make_buf(scales + (size_t)e * kNvScalePerExpert, kNvScaleGu);
+    uint4 c[2 * kNvGuPairs];
+    uint16_t sb[2 * kNvGuPairs];
+#pragma unroll
+    for (int i = 0; i < 2 * kNvGuPairs; ++i) {   // rows 0-3: gate r0 + i; 4-7: up r0 + i - 4
+        const int r = r0 + (i % kNvGuPairs);
+        const uint32_t coff = (i < kNvGuPairs ? 0u : (uint32_t)kPlaneGateBytes) + (uint32_t)r * (kH / 2);
+        const uint32_t soff = (i < kNvGuPairs ? 0u : kNvScaleGate) + (uint32_t)r * (kH / kNvBlock);
+        c[i] = bload16_nt(cres, lane * 16, coff);
+        sb[i] = bload2_nt(sres, lane * 2, soff);
+    }
+    const float tg = tscales[3 * e], tu = tscales[3 * e + 1];
+    for (int p = p_begin; p < p_begin + n; ++p) {
+        const int t = uniform(perm[p] / kTopK);
+        const uint4 *xp = reinterpret_cast<const uint4 *>(x + (size_t)t * kH + 32 * lane);
+        float v[32];
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 q = xp[i];
+            v[8 * i + 0] = bf16lo(q.x); v[8 * i + 1] = bf16hi(q.x);
+            v[8 * i + 2] = bf16lo(q.y); v[8 * i + 3] = bf16hi(q.y);
+            v[8 * i + 4] = bf16lo(q.z); v[8 * i + 5] = bf16hi(q.z);
+            v[8 * i + 6] = bf16lo(q.w); v[8 * i + 7] = bf16hi(q.w);
+        }
+#pragma unroll
+        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        const int sh = prescale_shift(wave_max(amax));
+        uint32_t xs[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) xs[4 * i + k] = pack_half2(ldexpf(v[8 * i + k], -sh), ldexpf(v[8 * i + k + 4], -sh));
+        float r[2 * kNvGuPairs];
+#pragma unroll
+        for (int i = 0; i < 2 * kNvGuPairs; ++i) {
+            uint4 ci = c[i];
+            refresh(ci);
+            r[i] = dot32_nv(ci, xs, e4m3_to_f32(sb[i] & 0xffu), e4m3_to_f32(sb[i] >> 8));
+        }
+        const float red = transpose_reduce<2 * kNvGuPairs, 64>(r);   // row i on lanes 8i .. 8i + 7
+        const float up = shfl_xor_f(red, 32);                        // row i + 4 (lanes 32 apart)
+        if (lane < 32 && (lane & 7) == 0) {
+            const float mult = ldexpf(1.0f, sh);
+            const float g = red * tg * mult, u = up * tu * mult;
+            act[(size_t)p * kI + r0 + (lane >> 3)] = silu_f(g) * u;
+        }
+    }
+}
+
+// =========================================================================
+// down.  A wave item is (active expert slot, rows [n0, n0 + 32)) in 8 wave
+// loads of 4 rows (16 lanes per row, lane j = lane & 15 owning K [32j,
+// 32j + 32): 16 bytes of codes, the scale bytes of blocks 2j and 2j + 1).
+// The four waves of a workgroup share the expert; while their codes are in
+// flight they turn up to four of its assignments' a into fp16 operands in
+// LDS (one prescale per assignment).
+// =========================================================================
+constexpr int kNvDnLoads = 8;
+
+struct NvDnRows {
+    uint4 c[kNvDnLoads];
+    uint16_t s[kNvDnLoads];
+};
+
+template <bool RELOAD>
+__device__ __forceinline__ void nv_dn_load(NvDnRows &R, rsrc_t cd, rsrc_t sd, uint32_t cv, uint32_t sv, int n0) {
+#pragma unroll
+    for (int q = 0; q < kNvDnLoads; ++q) {
+        if (RELOAD) {
+            R.c[q] = bload16_nt_reload(cd, cv, (n0 + 4 * q) * (kI / 2));
+            R.s[q] = bload2_nt_reload(sd, sv, (n0 + 4 * q) * (kI / kNvBlock));
+        } else {
+            R.c[q] = bload16_nt(cd, cv, (n0 + 4 * q) * (kI / 2));
+            R.s[q] = bload2_nt(sd, sv, (n0 + 4 * q) * (kI / kNvBlock));
+        }
+    }
+}
+
+// at, at_mult: the NT assignments' operands in LDS (rows of kI/2 words) and
+// their 2^sh; p0: the sorted position of the first.
+template <int NT>
+__device__ __forceinline__ void nv_dn_compute(const NvDnRows &R, int n0, const uint32_t *at, const float *at_mult,
+                                              float tdown, int p0, int n_valid, int lane, float *__restrict__ o) {
+    constexpr int kPerRed = 2;   // wave loads per reduction
+    constexpr int V = kPerRed * NT;
+    constexpr int kLogV = __builtin_ctz(V);
+    const int j = lane & 15, rsub = lane >> 4;
+    uint32_t xs[NT][16];
+    float mult[NT];
+#pragma unroll
+    for (int nn = 0; nn < NT; ++nn) {
+        const int q = min(nn, n_valid - 1);
+        const uint4 *src = reinterpret_cast<const uint4 *>(at + q * (kI / 2) + j * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 w = src[i];
+            xs[nn][4 * i] = w.x; xs[nn][4 * i + 1] = w.y; xs[nn][4 * i + 2] = w.z; xs[nn][4 * i + 3] = w.w;
+        }
+        mult[nn] = at_mult[q] * tdown;
+    }
+#pragma unroll
+    for (int q0 = 0; q0 < kNvDnLoads; q0 += kPerRed) {
+        float v[V];
+#pragma unroll
+        for (int k = 0; k < kPerRed; ++k) {
+            const uint16_t s = R.s[q0 + k];
+            const float s0 = e4m3_to_f32(s & 0xffu), s1 = e4m3_to_f32(s >> 8);
+#pragma unroll
+            for (int nn = 0; nn < NT; ++nn) v[k * NT + nn] = dot32_nv(R.c[q0 + k], xs[nn], s0, s1) * mult[nn];
+        }
+        const float red = transpose_reduce<V, 16>(v);
+        const int vi = j >> (4 - kLogV);
+        const int k = vi / NT, nn = vi % NT;
+        if ((j & ((1 << (4 - kLogV)) - 1)) == 0 && nn < n_valid)
+            o[(size_t)(p0 + nn) * kH + n0 + 4 * (q0 + k) + rsub] = red;
+    }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_down_nv(
+    const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales, const float *__restrict__ tscales,
+    const float *__restrict__ act, const int *__restrict__ slots, float *__restrict__ o) {
+    constexpr int kRows = 4 * kNvDnLoads;
+    constexpr int kItems = kH / kRows;
+    static_assert(kItems % 4 == 0, "the four waves of a workgroup must share one expert");
+    __shared__ uint32_t at[4][kI / 2];
+    __shared__ float at_mult[4];
+    const int wave = wave_id();
+    const int lane = threadIdx.x & 63;
+    const int item = blockIdx.x * 4 + wave;
+    const int *rec = slots + 8 * (item / kItems);   // {expert, p_begin, n, ...}
+    const int e = rec[0];
+    if (e < 0) return;
+    const int p_begin = rec[1], n = rec[2];
+    const int n0 = (item % kItems) * kRows;
+    const int j = lane & 15, rsub = lane >> 4;
+    const rsrc_t cd = make_buf(codes + (size_t)e * kCodeBytesPerExpert + kCodeBytesGu,
+                               (uint32_t)(kCodeBytesPerExpert - kCodeBytesGu));
+    const rsrc_t sd = make_buf(scales + (size_t)e * kNvScalePerExpert + kNvScaleGu, kNvScalePerExpert - kNvScaleGu);
+    const uint32_t cv = rsub * (kI / 2) + j * 16, sv = rsub * (kI / kNvBlock) + j * 2;
+    const float tdown = tscales[3 * e + 2];
+    // a of the assignment p (wave w: p = c + w), requested before the codes so
+    // that staging waits only for it; lane l holds a[8l .. 8l + 8)
+    float4 a0, a1;
+    auto load_a = [&](int p) {
+        const rsrc_t ab = make_buf(act + (size_t)p * kI, kI * 4);
+        a0 = __builtin_bit_cast(float4, bload16(ab, lane * 32, 0));
+        a1 = __builtin_bit_cast(float4, bload16(ab, lane * 32 + 16, 0));
+    };
+    auto stage = [&]() {
+        const float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        float amax = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        const int sh = prescale_shift(wave_max(amax));
+        uint4 w;
+        w.x = pack_half2(ldexpf(v[0], -sh), ldexpf(v[4], -sh));
+        w.y = pack_half2(ldexpf(v[1], -sh), ldexpf(v[5], -sh));
+        w.z = pack_half2(ldexpf(v[2], -sh), ldexpf(v[6], -sh));
+        w.w = pack_half2(ldexpf(v[3], -sh), ldexpf(v[7], -sh));
+        reinterpret_cast<uint4 *>(at[wave])[lane] = w;
+        at_mult[wave] = ldexpf(1.0f, sh);   // every lane stores the same value
+    };
+    NvDnRows R;
+    if (n == 1) {   // the common decode case
+        if (wave == 0) load_a(p_begin);
+        nv_dn_load<false>(R, cd, sd, cv, sv, n0);
+        if (wave == 0) stage();
+        __syncthreads();
+        nv_dn_compute<1>(R, n0, at[0], at_mult, tdown, p_begin, 1, lane, o);
+        return;
+    }
+    // two or more tokens: four assignments per round of operands, two at a
+    // time through one call site; volatile reloads (L2 hits) keep the rows
+    // loop-variant
+    const int p_end = p_begin + n;
+    for (int c = p_begin; c < p_end; c += 4) {
+        const bool mine = c + wave < p_end;
+        if (mine) load_a(c + wave);
+        nv_dn_load<true>(R, cd, sd, cv, sv, n0);
+        if (c != p_begin) __syncthreads();   // every wave is done with the last round's operands
+        if (mine) stage();
+        __syncthreads();
+        const int m = min(4, p_end - c);
+        for (int q = 0; q < m; q += 2) {
+            if (q) nv_dn_load<true>(R, cd, sd, cv, sv, n0);
+            nv_dn_compute<2>(R, n0, at[q], at_mult + q, tdown, c + q, min(2, m - q), lane, o);
+        }
+    }
+}
+
+}  // namespace
+
+void launch_gateup_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscales, const uint16_t *x,
+                         const int *perm, const int *slots, int T, float *act, hipStream_t s) {
+    const int max_active = min(kE, kTopK * T);
+    const int waves = max_active * (kI / kNvGuPairs);
+    hipLaunchKernelGGL(k_gateup_nv, dim3((waves + 3) / 4), dim3(256), 0, s, codes, scales, tscales, x, perm, slots,
+                       act);
+}
+
+void launch_down_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscales, const float *act,
+                       const int *slots, int T, float *o, hipStream_t s) {
+    const int max_active = min(kE, kTopK * T);
+    const int waves = max_active * (kH / (4 * kNvDnLoads));
+    hipLaunchKernelGGL(k_down_nv, dim3((waves + 3) / 4), dim3(256), 0, s, codes, scales, tscales, act, slots, o);
+}
+
+}  // namespace moe_w4

@@ -33,6 +33,8 @@ EXPERT_WEIGHTS = 3145728       # bf16 elements of one expert's gate, up and down
 PACK_MAX_EXPERTS = 65536
 DENSE_INTER = 6144
 DENSE_WEIGHTS = 37748736       # bf16 elements of a dense MLP block: gate, up [6144][2048], down [2048][6144]
+NVFP4_CODE_BYTES = 1572864     # bytes of one NVFP4 expert's E2M1 codes
+NVFP4_SCALE_BYTES = 196608     # E4M3 block-scale bytes of one NVFP4 expert
 
 OK, EINVAL, EWORKSPACE, EDEVICE = 0, -1, -2, -3
 
@@ -66,6 +68,9 @@ _sig = {
     "moe_w4_profile_point_name": (ctypes.c_char_p, [_int]),
     "moe_w4_forward_profiled": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp,
                                        ctypes.POINTER(_vp), _int]),
+    "moe_w4_forward_nvfp4": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "moe_w4_forward_nvfp4_profiled": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp,
+                                             ctypes.POINTER(_vp), _int]),
     "moe_w4_pack_experts": (_int, [_vp, _i64, _vp, _vp, _vp]),
     "moe_w4_dense_mlp_workspace_bytes": (_sz, [_i64]),
     "moe_w4_dense_mlp": (_int, [_vp, _vp, _i64, _vp, _vp, _sz, _vp]),
@@ -170,6 +175,30 @@ def moe_w4_forward_profiled(x, router_w, codes, scales, shared_w, y, workspace, 
                                       workspace.numel() * workspace.element_size(), _stream(stream),
                                       arr, len(events))
     _check(st, "moe_w4_forward_profiled")
+    return st
+
+
+def moe_w4_forward_nvfp4(x, router_w, codes, scales, tensor_scales, shared_w, y, workspace, router_bias=None,
+                         stream=None, T=None) -> int:
+    """y <- layer(x) with NVFP4 experts (codes u8, E4M3 scales u8, f32 tensor scales [256][3])."""
+    T = x.shape[0] if T is None else T
+    st = _lib.moe_w4_forward_nvfp4(_ptr(x), _ptr(router_w), _ptr(codes), _ptr(scales), _ptr(tensor_scales),
+                                   _ptr(shared_w), T, _ptr(y), _ptr(router_bias), _ptr(workspace),
+                                   workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(st, "moe_w4_forward_nvfp4")
+    return st
+
+
+def moe_w4_forward_nvfp4_profiled(x, router_w, codes, scales, tensor_scales, shared_w, y, workspace, events,
+                                  router_bias=None, stream=None) -> int:
+    """moe_w4_forward_nvfp4 recording raw hipEvent_t handles at the stage boundaries."""
+    arr = (_vp * len(events))(*events)
+    st = _lib.moe_w4_forward_nvfp4_profiled(_ptr(x), _ptr(router_w), _ptr(codes), _ptr(scales),
+                                            _ptr(tensor_scales), _ptr(shared_w), x.shape[0], _ptr(y),
+                                            _ptr(router_bias), _ptr(workspace),
+                                            workspace.numel() * workspace.element_size(), _stream(stream),
+                                            arr, len(events))
+    _check(st, "moe_w4_forward_nvfp4_profiled")
     return st
 
 

@@ -59,7 +59,9 @@ def from_dev_u16(t):
     return t.cpu().numpy().view(np.uint16)
 
 
-def run_gpu(m, x_bits, w, bias=None, ws=None, poison=False, policy=None):
+def run_gpu(m, x_bits, w, bias=None, ws=None, poison=False, policy=None, nvfp4=None):
+    """nvfp4: dict(codes, scales, tscales) of NVFP4 experts (device tensors) to
+    run moe_w4_forward_nvfp4 instead of the int4 layer."""
     """Run one forward; returns y bits and the routing results read from the workspace."""
     T = x_bits.shape[0]
     x = to_dev_u16(x_bits)
@@ -69,7 +71,10 @@ def run_gpu(m, x_bits, w, bias=None, ws=None, poison=False, policy=None):
     if poison:
         ws.fill_(0xFF)
     b = None if bias is None else torch.from_numpy(np.asarray(bias, dtype=np.float32)).cuda()
-    if policy is None:
+    if nvfp4 is not None:
+        m.moe_w4_forward_nvfp4(x, w["router_w"], nvfp4["codes"], nvfp4["scales"], nvfp4["tscales"], w["shared_w"],
+                               y, ws, router_bias=b)
+    elif policy is None:
         m.moe_w4_forward(x, w["router_w"], w["codes"], w["scales"], w["shared_w"], y, ws, router_bias=b)
     else:
         m.moe_w4_forward_policy(x, w["router_w"], w["codes"], w["scales"], w["shared_w"], y, ws, router_bias=b,

@@ -42,7 +42,7 @@ def test_header_constants_match_the_binding(m):
     names = ["HIDDEN", "EXPERTS", "TOPK", "INTER", "SHARED_INTER", "GROUP", "CODE_BYTES_PER_EXPERT",
              "SCALES_PER_EXPERT", "SHARED_ELEMS", "MAX_TOKENS", "FUSED_MAX_TOKENS", "ROUTER_NORM_FLOOR",
              "ROUTER_NORM_SUM", "ROUTER_NORM_NONE", "ROUTER_NORM_MASK", "ROUTER_BIAS_SELECT_ONLY", "EXPERT_WEIGHTS",
-             "PACK_MAX_EXPERTS", "DENSE_INTER", "DENSE_WEIGHTS"]
+             "PACK_MAX_EXPERTS", "DENSE_INTER", "DENSE_WEIGHTS", "NVFP4_CODE_BYTES", "NVFP4_SCALE_BYTES"]
     for n in names:
         assert int(defines[n]) == getattr(m, n), n
 
@@ -166,6 +166,25 @@ def test_dense_mlp_validation(m):
     assert lib.moe_w4_dense_mlp(x, w, 4, y, ws, nb - 1, None) == m.EWORKSPACE
     assert lib.moe_w4_dense_mlp(x, w, 4, x + 4096, ws, nb, None) == m.EINVAL       # y overlaps x
     assert lib.moe_w4_dense_mlp(x, w, 4, w + 4096, ws, nb, None) == m.EINVAL       # y overlaps the weights
+    assert m.moe_w4_last_device_error() == 0
+
+
+def test_nvfp4_validation(m):
+    lib = m._lib
+    x, r, c, sc, ts, sh, y, ws = (0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x48000000, 0x50000000,
+                                  0x60000000, 0x70000000)
+    nb = m.moe_w4_workspace_bytes(4)
+    assert lib.moe_w4_forward_nvfp4(x, r, c, sc, ts, sh, 0, y, None, ws, nb, None) == m.OK    # T == 0
+    assert lib.moe_w4_forward_nvfp4(x, r, c, sc, ts, sh, -1, y, None, ws, nb, None) == m.EINVAL
+    assert lib.moe_w4_forward_nvfp4(x, r, c, sc, None, sh, 4, y, None, ws, nb, None) == m.EINVAL
+    assert lib.moe_w4_forward_nvfp4(x, r, c, sc, ts + 2, sh, 4, y, None, ws, nb, None) == m.EINVAL
+    assert lib.moe_w4_forward_nvfp4(x, r, None, sc, ts, sh, 4, y, None, ws, nb, None) == m.EINVAL
+    assert lib.moe_w4_forward_nvfp4(x, r, c, sc + 8, ts, sh, 4, y, None, ws, nb, None) == m.EINVAL
+    assert lib.moe_w4_forward_nvfp4(x, r, c, sc, ts, sh, 4, y, None, ws, nb - 1, None) == m.EWORKSPACE
+    assert lib.moe_w4_forward_nvfp4(x, r, c, sc, ts, sh, 4, x + 4096, None, ws, nb, None) == m.EINVAL
+    ev = (ctypes.c_void_p * 1)()
+    assert lib.moe_w4_forward_nvfp4_profiled(x, r, c, sc, ts, sh, 4, y, None, ws, nb, None, ev, -1) == m.EINVAL
+    assert lib.moe_w4_forward_nvfp4_profiled(x, r, c, sc, ts, sh, 4, y, None, ws, nb, None, None, 1) == m.EINVAL
     assert m.moe_w4_last_device_error() == 0
 
 
