@@ -5,9 +5,8 @@
 // not quantised (W4A16).  The experts run as streaming GEMVs at every token
 // count, driven by the slot records of the sort like the int4 GEMVs.
 //
-// Arithmetic: an E2M1 value (0, 0.5, 1, 1.5, 2, 3, 4, 6 and their negatives)
-// is an fp16 whose low byte is zero; its high byte comes from an 8-entry byte
-// table through v_perm_b32 and the sign bit is copied in.  The activations
+// Arithmetic: gfx950 converts two E2M1 codes (one byte) to an exact fp16 pair
+// in one instruction (v_cvt_scalef32_pk_f16_fp4, scale 1).  The activations
 // become fp16 with a power-of-two prescale (largest magnitude in [2^13,
 // 2^14)), products are exact in v_dot2_f32_f16 and summed in fp32 per
 // 16-element block, the block's E4M3 scale (exact in fp32) multiplies that
@@ -32,23 +31,13 @@ constexpr uint32_t kNvScaleGate = (uint32_t)kI * kH / kNvBlock;                 
 constexpr uint32_t kNvScaleGu = 2 * kNvScaleGate;                                  // 131,072
 constexpr uint32_t kNvScalePerExpert = kNvScaleGu + (uint32_t)kH * kI / kNvBlock;  // 196,608
 
-// fp16 high bytes of the E2M1 magnitudes 0..7 (low bytes are zero):
-// 0x00 0x38 0x3C 0x3E | 0x40 0x42 0x44 0x46  =  0, 0.5, 1, 1.5 | 2, 3, 4, 6.
-// v_perm_b32 byte selectors 0-3 pick bytes of its second source, 4-7 of the
-// first, 12 gives 0x00.
-constexpr uint32_t kE2m1Lo = 0x3E3C3800u;
-constexpr uint32_t kE2m1Hi = 0x46444240u;
-
-// Eight codes (nibble k = element k of an 8-group) -> four fp16 pairs
-// h[k] = (value k, value k + 4).
+// Eight codes (byte b: element 2b in the low nibble, 2b + 1 in the high one)
+// -> four fp16 pairs h[b] = (value 2b, value 2b + 1).
 __device__ __forceinline__ void e2m1x8_to_half(uint32_t w, uint32_t (&h)[4]) {
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const uint32_t t = w << (12 - 4 * k);   // nibble k at bits 12-15, nibble k + 4 at 28-31
-        const uint32_t sel = ((t >> 4) & 0x07000700u) | 0x000c000cu;
-        const uint32_t mag = __builtin_amdgcn_perm(kE2m1Hi, kE2m1Lo, sel);
-        h[k] = mag | (t & 0x80008000u);
-    }
+    h[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0));
+    h[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1));
+    h[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2));
+    h[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3));
 }
 
 // E4M3 byte -> fp32 (exact): sign, 4 exponent bits (bias 7), 3 mantissa bits,
@@ -60,9 +49,29 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
     return (b & 0x80u) ? -mag : mag;
 }
 
-// One lane's 32 codes (word i: elements 8i .. 8i + 7) against the operand words
-// xs[4i + k] = (x[8i + k], x[8i + k + 4]): s0 * (sum over elements 0..15) +
-// s1 * (sum over elements 16..31).
+// One lane's 32 codes (word i: elements 8i .. 8i + 7) as fp16 pairs
+// h[4i + b] = (value 8i + 2b, value 8i + 2b + 1).
+__device__ __forceinline__ void conv32_nv(const uint4 c, uint32_t (&h)[16]) {
+    uint32_t q[4];
+    e2m1x8_to_half(c.x, q);
+    h[0] = q[0]; h[1] = q[1]; h[2] = q[2]; h[3] = q[3];
+    e2m1x8_to_half(c.y, q);
+    h[4] = q[0]; h[5] = q[1]; h[6] = q[2]; h[7] = q[3];
+    e2m1x8_to_half(c.z, q);
+    h[8] = q[0]; h[9] = q[1]; h[10] = q[2]; h[11] = q[3];
+    e2m1x8_to_half(c.w, q);
+    h[12] = q[0]; h[13] = q[1]; h[14] = q[2]; h[15] = q[3];
+}
+// Those against the operand words xs[4i + b] = (x[8i + 2b], x[8i + 2b + 1]):
+// s0 * (sum over elements 0..15) + s1 * (sum over elements 16..31).
+__device__ __forceinline__ float dot32h_nv(const uint32_t (&h)[16], const uint32_t (&xs)[16], float s0, float s1) {
+    float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) a0 = dot2h(h[k], xs[k], a0);
+#pragma unroll
+    for (int k = 8; k < 16; ++k) a1 = dot2h(h[k], xs[k], a1);
+    return a0 * s0 + a1 * s1;
+}
 __device__ __forceinline__ float dot32_nv(const uint4 c, const uint32_t (&xs)[16], float s0, float s1) {
     uint32_t h[4];
     float a0 = 0.0f, a1 = 0.0f;
@@ -92,19 +101,66 @@ __device__ __forceinline__ void refresh(uint4 &v) {
 // gate/up.  A wave item is (active expert slot, gate rows [r0, r0 + 4) and
 // the same up rows): 8 rows of 1 KiB, lane l owning K [32l, 32l + 32) of each
 // (16 bytes of codes, the 2 scale bytes of blocks 2l and 2l + 1), all
-// requested as soon as the expert is known.  Per token of the expert the
-// wave turns the token's x into fp16 operands (the whole row is in the
-// wave, so the prescale needs no other wave) and writes a = silu(g) * u.
+// requested as soon as the expert is known.  The four waves of a workgroup
+// share the expert: while their codes are in flight they turn up to four of
+// its tokens' x into fp16 operands in LDS (wave w: token w of the round; the
+// whole row is in one wave, so the prescale needs no other wave).  Codes are
+// converted once per pair of tokens; a = silu(g) * u goes to act.
 // =========================================================================
 constexpr int kNvGuPairs = 4;
+constexpr int kNvRows = 2 * kNvGuPairs;   // rows 0-3: gate r0 + i; 4-7: up r0 + i - 4
 
-__global__ __launch_bounds__(256) void k_gateup_nv(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+// NT tokens (operands xo rows, multipliers xm) against the item's 8 rows.
+template <int NT>
+__device__ __forceinline__ void nv_gu_compute(const uint4 (&c)[kNvRows], const float (&s0)[kNvRows],
+                                              const float (&s1)[kNvRows], const uint32_t *xo, const float *xm,
+                                              float tg, float tu, int r0, int p0, int n_valid, int lane,
+                                              float *__restrict__ act) {
+    constexpr int V = kNvRows * NT;
+    constexpr int kSpan = kWave / V;   // lanes that end with one value
+    uint32_t xs[NT][16];
+    float mult[NT];
+#pragma unroll
+    for (int nn = 0; nn < NT; ++nn) {
+        const int q = min(nn, n_valid - 1);
+        const uint4 *src = reinterpret_cast<const uint4 *>(xo + q * (kH / 2) + lane * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint4 w = src[i];
+            xs[nn][4 * i] = w.x; xs[nn][4 * i + 1] = w.y; xs[nn][4 * i + 2] = w.z; xs[nn][4 * i + 3] = w.w;
+        }
+        mult[nn] = xm[q];
+    }
+    float r[V];
+#pragma unroll
+    for (int i = 0; i < kNvRows; ++i) {
+        uint4 ci = c[i];
+        refresh(ci);
+        uint32_t h[16];
+        conv32_nv(ci, h);
+#pragma unroll
+        for (int nn = 0; nn < NT; ++nn) r[i * NT + nn] = dot32h_nv(h, xs[nn], s0[i], s1[i]);
+    }
+    const float red = transpose_reduce<V, kWave>(r);   // value v = i * NT + nn on lanes kSpan*v ..
+    const float up = shfl_xor_f(red, 32);               // row i + 4: lanes 32 apart
+    const int v = lane / kSpan, i = v / NT, nn = v % NT;
+    if (lane < 32 && lane % kSpan == 0 && nn < n_valid) {
+        const float g = red * tg * mult[nn], u = up * tu * mult[nn];
+        act[(size_t)(p0 + nn) * kI + r0 + i] = silu_f(g) * u;
+    }
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_gateup_nv(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
                                                    const float *__restrict__ tscales, const uint16_t *__restrict__ x,
                                                    const int *__restrict__ perm, const int *__restrict__ slots,
                                                    float *__restrict__ act) {
     constexpr int kItems = kI / kNvGuPairs;   // 128 per expert
+    static_assert(kItems % 4 == 0, "the four waves of a workgroup must share one expert");
+    __shared__ uint32_t xo[4][kH / 2];
+    __shared__ float xm[4];
     const int lane = threadIdx.x & 63;
-    const int item = blockIdx.x * 4 + wave_id();
+    const int wave = wave_id();
+    const int item = blockIdx.x * 4 + wave;
     const int *rec = slots + 8 * (item / kItems);   // {expert, p_begin, n, ...}
     const int e = rec[0];
     if (e < 0) return;
@@ -112,25 +168,20 @@ __global__ __launch_bounds__(256) void k_gateup_nv(const uint8_t *__restrict__ c
     const int r0 = (item % kItems) * kNvGuPairs;
     const rsrc_t cres = make_buf(codes + (size_t)e * kCodeBytesPerExpert, (uint32_t)kCodeBytesGu);
     const rsrc_t sres = make_buf(scales + (size_t)e * kNvScalePerExpert, kNvScaleGu);
-    uint4 c[2 * kNvGuPairs];
-    uint16_t sb[2 * kNvGuPairs];
-#pragma unroll
-    for (int i = 0; i < 2 * kNvGuPairs; ++i) {   // rows 0-3: gate r0 + i; 4-7: up r0 + i - 4
-        const int r = r0 + (i % kNvGuPairs);
-        const uint32_t coff = (i < kNvGuPairs ? 0u : (uint32_t)kPlaneGateBytes) + (uint32_t)r * (kH / 2);
-        const uint32_t soff = (i < kNvGuPairs ? 0u : kNvScaleGate) + (uint32_t)r * (kH / kNvBlock);
-        c[i] = bload16_nt(cres, lane * 16, coff);
-        sb[i] = bload2_nt(sres, lane * 2, soff);
-    }
-    const float tg = tscales[3 * e], tu = tscales[3 * e + 1];
-    for (int p = p_begin; p < p_begin + n; ++p) {
+    // x of the round's token for this wave, requested before the codes
+    uint4 xq[4];
+    auto load_x = [&](int p) {
         const int t = uniform(perm[p] / kTopK);
         const uint4 *xp = reinterpret_cast<const uint4 *>(x + (size_t)t * kH + 32 * lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xq[i] = xp[i];
+    };
+    auto stage_x = [&]() {
         float v[32];
         float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const uint4 q = xp[i];
+            const uint4 q = xq[i];
             v[8 * i + 0] = bf16lo(q.x); v[8 * i + 1] = bf16hi(q.x);
             v[8 * i + 2] = bf16lo(q.y); v[8 * i + 3] = bf16hi(q.y);
             v[8 * i + 4] = bf16lo(q.z); v[8 * i + 5] = bf16hi(q.z);
@@ -139,25 +190,54 @@ __global__ __launch_bounds__(256) void k_gateup_nv(const uint8_t *__restrict__ c
 #pragma unroll
         for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
         const int sh = prescale_shift(wave_max(amax));
-        uint32_t xs[16];
+        uint4 *dst = reinterpret_cast<uint4 *>(xo[wave] + lane * 16);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int k = 0; k < 4; ++k) xs[4 * i + k] = pack_half2(ldexpf(v[8 * i + k], -sh), ldexpf(v[8 * i + k + 4], -sh));
-        float r[2 * kNvGuPairs];
-#pragma unroll
-        for (int i = 0; i < 2 * kNvGuPairs; ++i) {
-            uint4 ci = c[i];
-            refresh(ci);
-            r[i] = dot32_nv(ci, xs, e4m3_to_f32(sb[i] & 0xffu), e4m3_to_f32(sb[i] >> 8));
+        for (int i = 0; i < 4; ++i) {
+            const float *q = v + 8 * i;
+            dst[i] = make_uint4(pack_half2(ldexpf(q[0], -sh), ldexpf(q[1], -sh)),
+                                pack_half2(ldexpf(q[2], -sh), ldexpf(q[3], -sh)),
+                                pack_half2(ldexpf(q[4], -sh), ldexpf(q[5], -sh)),
+                                pack_half2(ldexpf(q[6], -sh), ldexpf(q[7], -sh)));
         }
-        const float red = transpose_reduce<2 * kNvGuPairs, 64>(r);   // row i on lanes 8i .. 8i + 7
-        const float up = shfl_xor_f(red, 32);                        // row i + 4 (lanes 32 apart)
-        if (lane < 32 && (lane & 7) == 0) {
-            const float mult = ldexpf(1.0f, sh);
-            const float g = red * tg * mult, u = up * tu * mult;
-            act[(size_t)p * kI + r0 + (lane >> 3)] = silu_f(g) * u;
+        xm[wave] = ldexpf(1.0f, sh);   // every lane stores the same value
+    };
+    const int p_end = p_begin + n;
+    if (wave < n) load_x(p_begin + wave);
+    uint4 c[kNvRows];
+    uint16_t sb[kNvRows];
+#pragma unroll
+    for (int i = 0; i < kNvRows; ++i) {
+        const int r = r0 + (i % kNvGuPairs);
+        const uint32_t coff = (i < kNvGuPairs ? 0u : (uint32_t)kPlaneGateBytes) + (uint32_t)r * (kH / 2);
+        const uint32_t soff = (i < kNvGuPairs ? 0u : kNvScaleGate) + (uint32_t)r * (kH / kNvBlock);
+        c[i] = bload16_nt(cres, lane * 16, coff);
+        sb[i] = bload2_nt(sres, lane * 2, soff);
+    }
+    const float tg = tscales[3 * e], tu = tscales[3 * e + 1];
+    if (wave < n) stage_x();
+    __syncthreads();
+    float s0[kNvRows], s1[kNvRows];
+#pragma unroll
+    for (int i = 0; i < kNvRows; ++i) {
+        s0[i] = e4m3_to_f32(sb[i] & 0xffu);
+        s1[i] = e4m3_to_f32(sb[i] >> 8);
+    }
+    if (n == 1) {   // the common decode case
+        nv_gu_compute<1>(c, s0, s1, xo[0], xm, tg, tu, r0, p_begin, 1, lane, act);
+        return;
+    }
+    for (int cb = p_begin;;) {
+        const int m = min(4, p_end - cb);
+        for (int q = 0; q < m; q += 2)
+            nv_gu_compute<2>(c, s0, s1, xo[q], xm + q, tg, tu, r0, cb + q, min(2, m - q), lane, act);
+        cb += 4;
+        if (cb >= p_end) break;
+        __syncthreads();   // every wave is done with this round's operands
+        if (cb + wave < p_end) {
+            load_x(cb + wave);
+            stage_x();
         }
+        __syncthreads();
     }
 }
 
@@ -267,10 +347,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
         for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
         const int sh = prescale_shift(wave_max(amax));
         uint4 w;
-        w.x = pack_half2(ldexpf(v[0], -sh), ldexpf(v[4], -sh));
-        w.y = pack_half2(ldexpf(v[1], -sh), ldexpf(v[5], -sh));
-        w.z = pack_half2(ldexpf(v[2], -sh), ldexpf(v[6], -sh));
-        w.w = pack_half2(ldexpf(v[3], -sh), ldexpf(v[7], -sh));
+        w.x = pack_half2(ldexpf(v[0], -sh), ldexpf(v[1], -sh));
+        w.y = pack_half2(ldexpf(v[2], -sh), ldexpf(v[3], -sh));
+        w.z = pack_half2(ldexpf(v[4], -sh), ldexpf(v[5], -sh));
+        w.w = pack_half2(ldexpf(v[6], -sh), ldexpf(v[7], -sh));
         reinterpret_cast<uint4 *>(at[wave])[lane] = w;
         at_mult[wave] = ldexpf(1.0f, sh);   // every lane stores the same value
     };
