@@ -219,7 +219,9 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
         MOE_STEP(launch_gateup_mfma(codes, scales, xt, xt_scale, perm, chunks, n_chunks, T, at, at_scale, s));
         MOE_MARK();
         MOE_MARK();
-        MOE_STEP(launch_down_mfma(codes, scales, at, at_scale, chunks, n_chunks, T, o, s));
+        // fp16 rows in the first half of the o region, their multipliers behind them
+        MOE_STEP(launch_down_mfma(codes, scales, at, at_scale, chunks, n_chunks, T, reinterpret_cast<uint16_t *>(o),
+                                  o + (size_t)kTopK * T * kH / 2, s));
         MOE_MARK();
     } else {
         MOE_STEP(launch_gateup_gemv(codes, scales, xt, xt_scale, perm, active, T, act, s));
@@ -231,7 +233,8 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     }
     if (grouped) {
         MOE_STEP(launch_shared_down_dense(shared_w, hs, T, z, s));
-        MOE_STEP(launch_combine(z, topk_w, pos, o, T, y, s));
+        MOE_STEP(launch_combine_half(z, topk_w, pos, reinterpret_cast<const uint16_t *>(o),
+                                     o + (size_t)kTopK * T * kH / 2, T, y, s));
     } else
         MOE_STEP(launch_shared_down_combine(shared_w, hs, T, topk_w, pos, o, y, s));
     MOE_MARK();

@@ -280,12 +280,14 @@ void launch_dense_mlp_down_dense(const uint16_t *w, const uint16_t *h, int T, ui
 }
 
 // y[t] = bf16(z[t] + sum_j w[t][j] o[pos[6t + j]]), slots in order, with o the
-// grouped down kernel's fp32 rows: a wave per token, lane l owns
-// columns [32l, 32l + 32); every load of the token is in flight at once (the
-// gathers of an epilogue inside the GEMM tile were latency-bound).
+// grouped down kernel's rows: fp16 times a per-row multiplier (HALF) or fp32
+// (the NVFP4 experts' rows): a wave per token, lane l owns columns [32l,
+// 32l + 32); every load of the token is in flight at once (the gathers of an
+// epilogue inside the GEMM tile were latency-bound).
+template <bool HALF>
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ z, const float *__restrict__ topk_w,
-                                                 const int *__restrict__ pos, const float *__restrict__ o, int T,
-                                                 uint16_t *__restrict__ y) {
+                                                 const int *__restrict__ pos, const void *__restrict__ o,
+                                                 const float *__restrict__ o_scale, int T, uint16_t *__restrict__ y) {
     const int t = blockIdx.x * 4 + wave_id();
     if (t >= T) return;
     const int lane = threadIdx.x & 63;
@@ -300,16 +302,45 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ z, co
     float4 acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = zr[i];
+    if (HALF) {
+        float ws[kTopK];
+        uint4 h[kTopK][4];
 #pragma unroll
-    for (int j = 0; j < kTopK; ++j) {
-        const float4 *orow = reinterpret_cast<const float4 *>(o + (size_t)p[j] * kH) + 8 * lane;
+        for (int j = 0; j < kTopK; ++j) {
+            ws[j] = w[j] * __builtin_bit_cast(float, uniform(__builtin_bit_cast(int, o_scale[p[j]])));
+            const uint4 *orow = reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(o) + (size_t)p[j] * kH) +
+                                4 * lane;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float4 v = orow[i];
-            acc[i].x = fmaf(w[j], v.x, acc[i].x);
-            acc[i].y = fmaf(w[j], v.y, acc[i].y);
-            acc[i].z = fmaf(w[j], v.z, acc[i].z);
-            acc[i].w = fmaf(w[j], v.w, acc[i].w);
+            for (int i = 0; i < 4; ++i) h[j][i] = orow[i];
+        }
+#pragma unroll
+        for (int j = 0; j < kTopK; ++j) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t q[4] = {h[j][i].x, h[j][i].y, h[j][i].z, h[j][i].w};
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    float4 &a = acc[2 * i + k];
+                    a.x = fmaf(ws[j], half_lo(q[2 * k]), a.x);
+                    a.y = fmaf(ws[j], half_hi(q[2 * k]), a.y);
+                    a.z = fmaf(ws[j], half_lo(q[2 * k + 1]), a.z);
+                    a.w = fmaf(ws[j], half_hi(q[2 * k + 1]), a.w);
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kTopK; ++j) {
+            const float4 *orow = reinterpret_cast<const float4 *>(static_cast<const float *>(o) + (size_t)p[j] * kH) +
+                                 8 * lane;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float4 v = orow[i];
+                acc[i].x = fmaf(w[j], v.x, acc[i].x);
+                acc[i].y = fmaf(w[j], v.y, acc[i].y);
+                acc[i].z = fmaf(w[j], v.z, acc[i].z);
+                acc[i].w = fmaf(w[j], v.w, acc[i].w);
+            }
         }
     }
     uint32_t packed[16];
@@ -325,7 +356,14 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ z, co
 
 void launch_combine(const float *z, const float *topk_w, const int *pos, const float *o, int T, uint16_t *y,
                     hipStream_t s) {
-    hipLaunchKernelGGL(k_combine, dim3((T + 3) / 4), dim3(256), 0, s, z, topk_w, pos, o, T, y);
+    hipLaunchKernelGGL(k_combine<false>, dim3((T + 3) / 4), dim3(256), 0, s, z, topk_w, pos,
+                       static_cast<const void *>(o), nullptr, T, y);
+}
+
+void launch_combine_half(const float *z, const float *topk_w, const int *pos, const uint16_t *o,
+                         const float *o_scale, int T, uint16_t *y, hipStream_t s) {
+    hipLaunchKernelGGL(k_combine<true>, dim3((T + 3) / 4), dim3(256), 0, s, z, topk_w, pos,
+                       static_cast<const void *>(o), o_scale, T, y);
 }
 
 }  // namespace moe_w4

@@ -39,6 +39,8 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
 constexpr int kChunkRows = 96;   // assignments per chunk: up to three 32-row MFMA tiles
 constexpr int kXcds = 8;
 
@@ -382,10 +384,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // in LDS once; the codes of the next three tiles are in flight during each
 // tile.  The MFMA runs transposed (codes as the row operand, tokens as the
 // column operand), so a lane ends with 4 consecutive features of one token
-// per group.  o is stored in fp32: a bf16 o (one more rounding of every
-// expert output before the weighted combine, 2^-9 relative) halves that
-// traffic, but on outputs six standard deviations out it adds enough error
-// to the final bf16 rounding of y to cross the 2e-2 x rms bar.
+// per group.  o is stored in fp16 with one power-of-two multiplier per row
+// (o_scale), which halves the traffic of the fp32 rows at a relative rounding
+// of 2^-11 (a bf16 o, 2^-9, added enough error on outputs six standard
+// deviations out to cross the 2e-2 x rms bar).  The MFMA sums are bounded
+// independently of the data (fp16 operands below 2^14 and codes times
+// normalised scales below 2^11, 512 terms: |acc| < 2^34), so acc * 2^-20
+// times each feature's normalisation relative to the expert's largest
+// never overflows fp16; the row's prescale and that largest normalisation
+// go to o_scale.
 //
 // Scales: A arrives with a power-of-two prescale per (token, 128-block); at
 // staging each block is brought to the token's largest prescale (an exact
@@ -404,8 +411,10 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
                                                    const uint32_t *__restrict__ at,
                                                    const float *__restrict__ at_scale,
                                                    const int4 *__restrict__ chunks,
-                                                   const int *__restrict__ n_chunks, float *__restrict__ o) {
+                                                   const int *__restrict__ n_chunks, uint16_t *__restrict__ o,
+                                                   float *__restrict__ o_scale) {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kChunkRows * kDnPitch];
+    __shared__ float fk_wave[4];                                              // largest 2^-k per wave
     __shared__ float row_p[kChunkRows];                                       // per token
     __shared__ __attribute__((aligned(16))) uint16_t sc[kI / kG][kH];         // [block][feature] bf16
     __shared__ __attribute__((aligned(16))) float fk[kH];                     // 2^-k per feature
@@ -477,8 +486,17 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
             }
             *reinterpret_cast<uint4 *>(&sc[bb][8 * tid]) = make_uint4(t4[0], t4[1], t4[2], t4[3]);
         }
+        // the expert's largest normalisation, over the features with a
+        // nonzero scale (an all-zero feature's outputs are 0 whatever it is)
+        float fmax = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) fk[8 * tid + k] = ldexpf(1.0f, -scale_shift4(w[2 * k], w[2 * k + 1]));
+        for (int k = 0; k < 8; ++k) {
+            const float f = ldexpf(1.0f, -scale_shift4(w[2 * k], w[2 * k + 1]));
+            fk[8 * tid + k] = f;
+            if ((w[2 * k] | w[2 * k + 1]) & 0x7f807f80u) fmax = fmaxf(fmax, f);
+        }
+        fmax = wave_max(fmax);
+        if (lane == 0) fk_wave[wave] = fmax;
     }
     // stage the activations, each block brought to the row's largest prescale
     if (stager) {
@@ -501,10 +519,14 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
         if (part == 0) row_p[srow] = pm;
     }
     __syncthreads();
-    // o rows of the chunk (bf16) through a buffer descriptor: stores of rows
+    // o rows of the chunk (fp16) through a buffer descriptor: stores of rows
     // past the chunk's end fall outside it and are dropped by the hardware
     // bounds check
-    const __amdgpu_buffer_rsrc_t ores = make_buf(o + (size_t)row0 * kH, (uint32_t)rows * kH * 4);
+    const __amdgpu_buffer_rsrc_t ores = make_buf(o + (size_t)row0 * kH, (uint32_t)rows * kH * 2);
+    float fkmax = fmaxf(fmaxf(fk_wave[0], fk_wave[1]), fmaxf(fk_wave[2], fk_wave[3]));
+    if (fkmax == 0.0f) fkmax = 1.0f;   // every scale of the expert is zero: o is 0
+    const float to_half = 0x1p-20f / fkmax;   // a power of two
+    if (tid < rows) o_scale[row0 + tid] = row_p[tid] * fkmax * 0x1p20f;
 
     // unrolled by the ring size, so ring slots are compile-time; the fetch
     // index is clamped (the last tiles re-read the last tile, in bounds) so
@@ -570,17 +592,18 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
         float4 kq[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) kq[q] = *reinterpret_cast<const float4 *>(&fk[fb + 8 * q + zero]);
-        const uint32_t ob = (uint32_t)(n * kH + fb) * 4;
+        const uint32_t ob = (uint32_t)(n * kH + fb) * 2;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            kq[q].x *= to_half; kq[q].y *= to_half; kq[q].z *= to_half; kq[q].w *= to_half;
+        }
 #pragma unroll
         for (int h = 0; h < MT; ++h) {
-            const float p = row_p[32 * h + n + zero];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const u32x4_t v = {__float_as_uint(acc[h][4 * q] * (kq[q].x * p)),
-                                   __float_as_uint(acc[h][4 * q + 1] * (kq[q].y * p)),
-                                   __float_as_uint(acc[h][4 * q + 2] * (kq[q].z * p)),
-                                   __float_as_uint(acc[h][4 * q + 3] * (kq[q].w * p))};
-                __builtin_amdgcn_raw_buffer_store_b128(v, ores, ob + (uint32_t)(32 * h * kH + 8 * q) * 4, 0, 0);
+                const u32x2_t v = {pack_half2(acc[h][4 * q] * kq[q].x, acc[h][4 * q + 1] * kq[q].y),
+                                   pack_half2(acc[h][4 * q + 2] * kq[q].z, acc[h][4 * q + 3] * kq[q].w)};
+                __builtin_amdgcn_raw_buffer_store_b64(v, ores, ob + (uint32_t)(32 * h * kH + 8 * q) * 2, 0, 0);
             }
         }
     }
@@ -602,9 +625,9 @@ void launch_gateup_mfma(const uint8_t *codes, const uint16_t *scales, const uint
 }
 
 void launch_down_mfma(const uint8_t *codes, const uint16_t *scales, const uint32_t *at, const float *at_scale,
-                      const int *chunks, const int *n_chunks, int T, float *o, hipStream_t s) {
+                      const int *chunks, const int *n_chunks, int T, uint16_t *o, float *o_scale, hipStream_t s) {
     hipLaunchKernelGGL(k_down_mfma, dim3(grid_for(T, 1)), dim3(256 * kDnHalves), 0, s, codes, scales, at, at_scale,
-                       reinterpret_cast<const int4 *>(chunks), n_chunks, o);
+                       reinterpret_cast<const int4 *>(chunks), n_chunks, o, o_scale);
 }
 
 }  // namespace moe_w4

@@ -90,8 +90,9 @@ int max_chunks(int T);
 void launch_gateup_mfma(const uint8_t *codes, const uint16_t *scales, const uint32_t *xt, const float *xt_scale,
                         const int *perm, const int *chunks, const int *n_chunks, int T, uint32_t *at,
                         float *at_scale, hipStream_t s);
+// o: fp16 rows [6T][2048]; o_scale: fp32 [6T], the multiplier of each row.
 void launch_down_mfma(const uint8_t *codes, const uint16_t *scales, const uint32_t *at, const float *at_scale,
-                      const int *chunks, const int *n_chunks, int T, float *o, hipStream_t s);
+                      const int *chunks, const int *n_chunks, int T, uint16_t *o, float *o_scale, hipStream_t s);
 
 // Shared expert down projection fused with the combine:
 // y = bf16(h Wsd^T + sum_j w_j o[pos[6t+j]]), slots in order.
@@ -105,6 +106,9 @@ void launch_router_and_shared_gateup_dense(const uint16_t *x, int T, const uint1
 void launch_shared_down_dense(const uint16_t *shared_w, const uint16_t *hs, int T, float *z, hipStream_t s);
 void launch_combine(const float *z, const float *topk_w, const int *pos, const float *o, int T, uint16_t *y,
                     hipStream_t s);
+// the same with fp16 rows o times o_scale[row] (the grouped down kernel's output)
+void launch_combine_half(const float *z, const float *topk_w, const int *pos, const uint16_t *o,
+                         const float *o_scale, int T, uint16_t *y, hipStream_t s);
 
 // The packer: n_experts experts of bf16 weights (gate [512][2048], up
 // [512][2048], down [2048][512] each) -> int4 codes and bf16 scales in the
