@@ -255,6 +255,53 @@ def test_magnitudes(m, layer0, x_log2, s_log2):
     report(f"magnitude x*2^{x_log2} s*2^{s_log2}", P.compare(g, ref, label="magnitudes"))
 
 
+@pytest.mark.parametrize("x_log2,s_log2", [(12, 10), (-20, 0), (0, -12)])
+def test_magnitudes_grouped_path(m, layer0, x_log2, s_log2):
+    """The same scalings through the MFMA path (its expert rows cross HBM as
+    fp16 with a per-row multiplier), on sampled tokens."""
+    T = 160
+    print(f"[parity] case grouped magnitudes x*2^{x_log2} s*2^{s_log2}", flush=True)
+    xf = O.bf16_to_f64(synth.gen_x(204, T)) * 2.0 ** x_log2
+    x = O.f64_to_bf16_bits(xf)
+    w = dict(layer0)
+    if s_log2:
+        sc = layer0["scales"].view(torch.bfloat16).float() * 2.0 ** s_log2
+        w["scales"] = sc.to(torch.bfloat16).view(torch.int16)
+    g = P.run_gpu(m, x, w)
+    tokens = np.array([0, 1, 57, 100, T - 1])
+    ref = oracle_layer(x, scale_log2=s_log2, tokens=tokens)
+    report(f"grouped magnitude x*2^{x_log2} s*2^{s_log2}",
+           P.compare(g, ref, tokens=tokens, label="grouped magnitudes"))
+
+
+def test_grouped_path_uneven_down_scales(m, layer0):
+    """Down rows of one expert whose scales differ by 2^24 (every odd feature's
+    scales times 2^-24): the fp16 expert rows are normalised to the expert's
+    largest scales, so the small features lose relative precision but not the
+    bar (their outputs are 2^24 smaller)."""
+    T = 160
+    print("[parity] case uneven down scales", flush=True)
+    sc = layer0["scales"].view(torch.bfloat16).float().reshape(256, -1).clone()
+    down = sc[:, 16384:].reshape(256, 2048, 4)
+    down[:, 1::2, :] *= 2.0 ** -24
+    sc[:, 16384:] = down.reshape(256, -1)
+    w = dict(layer0, scales=sc.to(torch.bfloat16).view(torch.int16).reshape(-1))
+    base = P.host_blobs(0, 0)
+
+    def blobs(e):
+        c, s = base(e)
+        f = O.bf16_to_f64(s)
+        d = f[16384:].reshape(2048, 4)
+        d[1::2] *= 2.0 ** -24
+        f[16384:] = d.ravel()
+        return c, O.f64_to_bf16_bits(f)
+    x = synth.gen_x(205, T)
+    g = P.run_gpu(m, x, w)
+    tokens = np.array([0, 3, 80, T - 1])
+    ref = O.moe_layer(x, P.host_router(0, 0), blobs, P.host_shared(0, 0), tokens=tokens)
+    report("uneven down scales", P.compare(g, ref, tokens=tokens, label="uneven down scales"))
+
+
 def test_zero_tokens_is_a_noop(m, layer0):
     ws = m.workspace(1)
     x = torch.empty((0, 2048), dtype=torch.int16, device="cuda")
