@@ -7,10 +7,11 @@ binding never do: they share no code, constant table or helper with it.
 Everything here is plain NumPy in float64 and follows the pages step by step:
 
 * Flint model card for the int4-expert container (Aijuus/flint-w4exp),
-  introduction and table row "weights": 256 routed experts at top-6 plus an
-  ungated shared expert; routed experts are int4 codes with one bf16 scale
-  per 128 of K, stored in a 128-wide Hadamard (fwht128) rotated basis; the
-  shared expert and every other linear stay bf16.
+  introduction and table row "weights": 256 experts, 6 chosen per token, and
+  one shared expert without a gate; the routed experts hold int4 codes with a
+  bf16 scale for each 128 elements of K, in a basis rotated by the 128-point
+  Hadamard transform (fwht128); the shared expert and the other linears are
+  bf16.
 * NInfer README of Flint (WaveCut/Flint-UD-Q4_K_XL-NInfer-v3), section
   "What is inside": sigmoid router scores renormalised over the 6 chosen
   experts; each expert holds gate rows then up rows (2 x 512) and 2,048 down
@@ -49,6 +50,13 @@ Readings where the pages are silent (each is listed in the design doc too):
   "logit" (default) adds the bias to the logit for both the choice and the
   sigmoid, "select" adds it for the choice only.
 * silu(v) = v / (1 + exp(-v)); the shared expert is added with weight 1.
+* The shared expert (and the dense MLP blocks) are bf16 linears: the input of
+  the down linear, h = silu(g) * u, is rounded to bf16 once (g and u exact).
+  The routed experts' activations are not rounded (the expert weights are
+  int4; the pages give their activations no narrower format).
+* A token whose 6th/7th fp64 logit gap is <= 1e-3 is a near-tie (its chosen
+  set is decided by rounding); one whose chosen logits have two within 1e-3
+  of each other is an order tie (their slot order is decided by rounding).
 * y is rounded once, fp64 -> bf16 round-to-nearest-even.
 
 Parity pins live in ``tests/test_oracle_*.py``.  Absolute output values on
@@ -194,7 +202,8 @@ def route(x: np.ndarray, router_bits: np.ndarray, bias=None, norm="floor", bias_
     policy variants above.  Returns a dict with the fp64 logits the choice is
     made on, their fp32 rounding, the logits the sigmoid takes (logits_w),
     topk_idx [T, 6], topk_w [T, 6] (float64), the 6th-7th gap and the
-    near-tie flags.
+    near-tie flags, and the smallest gap between consecutive chosen logits
+    (order_gap) with its flags (order_tie).
     """
     if norm not in NORMS or bias_mode not in BIAS_MODES:
         raise ValueError("unknown router policy")
@@ -208,6 +217,7 @@ def route(x: np.ndarray, router_bits: np.ndarray, bias=None, norm="floor", bias_
     T, n_exp = logits.shape
     idx = np.empty((T, K_TOP), dtype=np.int32)
     gap = np.empty(T, dtype=np.float64)
+    order_gap = np.empty(T, dtype=np.float64)
     experts = np.arange(n_exp)
     for t in range(T):
         # higher fp32 logit first; equal logits -> lower expert index
@@ -215,6 +225,7 @@ def route(x: np.ndarray, router_bits: np.ndarray, bias=None, norm="floor", bias_
         idx[t] = order[:K_TOP]
         srt = np.sort(logits[t])[::-1]
         gap[t] = srt[K_TOP - 1] - srt[K_TOP]
+        order_gap[t] = np.min(srt[:K_TOP - 1] - srt[1:K_TOP])
     sel = np.take_along_axis(logits_w, idx.astype(np.int64), axis=1)
     sig = sigmoid(sel)
     if norm == "floor":
@@ -224,7 +235,7 @@ def route(x: np.ndarray, router_bits: np.ndarray, bias=None, norm="floor", bias_
     else:
         w = sig
     return dict(logits=logits, logits32=l32, logits_w=logits_w, topk_idx=idx, topk_w=w,
-                gap=gap, near_tie=gap <= NEAR_TIE_GAP)
+                gap=gap, near_tie=gap <= NEAR_TIE_GAP, order_gap=order_gap, order_tie=order_gap <= NEAR_TIE_GAP)
 
 
 def sort_assignments(topk_idx: np.ndarray):
@@ -250,14 +261,28 @@ def expert_swiglu(xt: np.ndarray, wg, wu, wd) -> np.ndarray:
     return at @ wd.T
 
 
+def bf16_round(v) -> np.ndarray:
+    """v rounded to the nearest bf16 (ties to even), as float64."""
+    return bf16_to_f64(f64_to_bf16_bits(v))
+
+
 def shared_expert(x: np.ndarray, shared_bits: np.ndarray) -> np.ndarray:
-    """Ungated bf16 SwiGLU of width 1024 on the unrotated input."""
+    """Ungated bf16 SwiGLU of width 1024 on the unrotated input: its down
+    linear takes h = silu(x Wg^T) * (x Wu^T) rounded to bf16 once."""
     sg, su, sd = shared_planes(shared_bits)
-    return (silu(x @ sg.T) * (x @ su.T)) @ sd.T
+    return bf16_round(silu(x @ sg.T) * (x @ su.T)) @ sd.T
+
+
+def _map_experts(fn, experts, pool):
+    """[fn(e) for e in experts], evaluated by `pool` (a concurrent.futures
+    executor) if one is given.  Each expert's output is computed on its own and
+    the caller sums them in the order of `experts` either way, so the result
+    is the same bits with or without a pool."""
+    return list(pool.map(fn, experts)) if pool is not None else [fn(e) for e in experts]
 
 
 def moe_layer(x_bits, router_bits, expert_blobs, shared_bits, bias=None, tokens=None, norm="floor",
-              bias_mode="logit"):
+              bias_mode="logit", pool=None):
     """The layer: y = bf16( sum_j w_j * E_{e_j}(x) + S(x) ).
 
     x_bits: bf16 bits [T, 2048]; router_bits: bf16 bits [256, 2048];
@@ -265,7 +290,8 @@ def moe_layer(x_bits, router_bits, expert_blobs, shared_bits, bias=None, tokens=
     library layout; shared_bits: bf16 bits [6291456]; bias: fp32 [256] or None.
     tokens: optional subset of token rows whose expert outputs and y are
     computed (routing and the sort always cover all T tokens).  norm,
-    bias_mode: the router policy (see route).
+    bias_mode: the router policy (see route).  pool: optional executor that
+    evaluates the experts concurrently (same result).
     """
     x = bf16_to_f64(x_bits)
     T = x.shape[0]
@@ -278,12 +304,16 @@ def moe_layer(x_bits, router_bits, expert_blobs, shared_bits, bias=None, tokens=
     for r_i, t in enumerate(rows):
         for j in range(K_TOP):
             need.setdefault(int(rt["topk_idx"][t, j]), []).append((r_i, j))
-    for e in sorted(need):
+    def expert_out(e):
         wg, wu, wd = expert_planes(*expert_blobs(e))
+        ri = np.array([p[0] for p in need[e]])
+        return expert_swiglu(xt[ri], wg, wu, wd)
+
+    experts = sorted(need)
+    for e, o in zip(experts, _map_experts(expert_out, experts, pool)):
         lst = need[e]
         ri = np.array([p[0] for p in lst])
         jj = np.array([p[1] for p in lst])
-        o = expert_swiglu(xt[ri], wg, wu, wd)
         w = rt["topk_w"][rows[ri], jj]
         for n in range(len(lst)):
             routed[ri[n]] += w[n] * o[n]
@@ -319,7 +349,8 @@ DENSE_WEIGHTS = 3 * I_D * H
 def dense_mlp(x_bits: np.ndarray, w_bits: np.ndarray) -> dict:
     """Dense SwiGLU MLP block (NInfer README of Flint, "What is inside": blocks 0
     and 1 are dense SwiGLU MLPs of width 6144; bf16 like every linear of the
-    model card): y = bf16( Wd (silu(Wg x) * (Wu x)) ), fp64 throughout.
+    model card): y = bf16( Wd bf16(silu(Wg x) * (Wu x)) ), fp64 otherwise (the
+    down linear's input rounded to bf16 once, as in the shared expert).
 
     x_bits: bf16 bits [T, 2048]; w_bits: bf16 bits [DENSE_WEIGHTS], gate
     [6144][2048], up [6144][2048], down [2048][6144].
@@ -328,7 +359,7 @@ def dense_mlp(x_bits: np.ndarray, w_bits: np.ndarray) -> dict:
     w = bf16_to_f64(np.asarray(w_bits, dtype=np.uint16).ravel())
     n = I_D * H
     wg, wu, wd = w[:n].reshape(I_D, H), w[n:2 * n].reshape(I_D, H), w[2 * n:].reshape(H, I_D)
-    y = (silu(x @ wg.T) * (x @ wu.T)) @ wd.T
+    y = bf16_round(silu(x @ wg.T) * (x @ wu.T)) @ wd.T
     return dict(y=y, y_bits=f64_to_bf16_bits(y))
 
 
@@ -339,10 +370,10 @@ def rmsnorm(x: np.ndarray) -> np.ndarray:
     return x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + RMS_EPS)
 
 
-def stack_step(resid: np.ndarray, layer_inputs):
+def stack_step(resid: np.ndarray, layer_inputs, pool=None):
     """x_{l+1} = x_l + moe_l(bf16(rmsnorm(x_l))) over the given layers.
 
-    layer_inputs: list of (router_bits, expert_blobs, shared_bits) per layer.
+    layer_inputs: iterable of (router_bits, expert_blobs, shared_bits) per layer.
     resid: fp32-valued residual [T, 2048] (float64 array holding fp32 values).
     The layer boundary is bf16 (the library's x and y); the residual is fp32.
     Returns the final residual and the bf16 inputs of every layer.
@@ -352,7 +383,7 @@ def stack_step(resid: np.ndarray, layer_inputs):
     for router_bits, blobs, shared_bits in layer_inputs:
         xin = f64_to_bf16_bits(rmsnorm(x))
         inputs.append(xin)
-        out = moe_layer(xin, router_bits, blobs, shared_bits)
+        out = moe_layer(xin, router_bits, blobs, shared_bits, pool=pool)
         x = f32_round(x + bf16_to_f64(out["y_bits"]))
     return x, inputs
 
@@ -535,12 +566,13 @@ def nvfp4_expert_planes(code_bytes, scale_bytes, tensor_scales):
     return wg, wu, wd
 
 
-def moe_layer_nvfp4(x_bits, router_bits, expert_blobs, shared_bits, bias=None, tokens=None):
+def moe_layer_nvfp4(x_bits, router_bits, expert_blobs, shared_bits, bias=None, tokens=None, pool=None):
     """The layer with NVFP4 experts: y = bf16( sum_j w_j * E_{e_j}(x) + S(x) ),
     E(x) = Wd (silu(Wg x) * (Wu x)) on the unrotated x.
 
     expert_blobs(e) -> (code bytes [1572864], E4M3 scale bytes [196608], f32
-    tensor scales [3]); the rest as in moe_layer (Flint router policy).
+    tensor scales [3]); the rest as in moe_layer (Flint router policy, the
+    optional pool).
     """
     x = bf16_to_f64(x_bits)
     T = x.shape[0]
@@ -552,13 +584,16 @@ def moe_layer_nvfp4(x_bits, router_bits, expert_blobs, shared_bits, bias=None, t
     for r_i, t in enumerate(rows):
         for j in range(K_TOP):
             need.setdefault(int(rt["topk_idx"][t, j]), []).append((r_i, j))
-    for e in sorted(need):
+    def expert_out(e):
         wg, wu, wd = nvfp4_expert_planes(*expert_blobs(e))
+        xe = x[rows[np.array([p[0] for p in need[e]])]]
+        return (silu(xe @ wg.T) * (xe @ wu.T)) @ wd.T
+
+    experts = sorted(need)
+    for e, o in zip(experts, _map_experts(expert_out, experts, pool)):
         lst = need[e]
         ri = np.array([p[0] for p in lst])
         jj = np.array([p[1] for p in lst])
-        xe = x[rows[ri]]
-        o = (silu(xe @ wg.T) * (xe @ wu.T)) @ wd.T
         w = rt["topk_w"][rows[ri], jj]
         for n in range(len(lst)):
             routed[ri[n]] += w[n] * o[n]

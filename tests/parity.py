@@ -2,18 +2,32 @@
 inputs and compare them to the stated bar.
 
 Bar (the layer's stated contract):
-  * expert indices (topk_idx) equal, for every token whose oracle 6th/7th
+  * the set of chosen experts equal, for every token whose oracle 6th/7th
     logit gap exceeds 1e-3 (near-ties are flagged and counted, not failed);
-  * offsets and perm bit-exact when no flagged token is routed differently;
+    their slot order (descending logit) equal too, unless two of the chosen
+    logits are within 1e-3 (an order tie, flagged the same way);
+  * offsets and perm bit-exact when every token is routed identically;
     otherwise offsets must equal the histogram of the GPU's own indices and
     perm must be the stable sort of those indices;
   * topk_w within 1e-5 relative of the oracle's (fp32 sigmoid vs fp64);
-  * y (bf16): max |y_gpu - y_oracle| <= 2e-2 * rms(y_oracle), over the tokens
-    routed identically.
+  * y (bf16), over the tokens with the oracle's chosen set: the error beyond
+    the rounding of the exact output to bf16, |y_gpu - y_oracle| - ulp(y_oracle)/2,
+    at most 2e-2 * rms(y_oracle).  Taken literally, max |y_gpu - y_oracle| <=
+    2e-2 * rms is not attainable by any bf16 output where that half ulp alone
+    exceeds 2e-2 rms: outputs of |y| >= 8 with rms ~1.3, which the skewed
+    prefill workload has (its correctly rounded output at 6.7 rms is 0.0267
+    from the exact value, against a bar of 0.0259);
+  * and element by element the same error beyond the output's rounding at most
+    Y_ELEM_TOL * rms(y_oracle): the roundings of the kernels' intermediates
+    (the fp16 operands of the routed experts, their fp16 expert rows on the
+    MFMA path, fp32 sums in another order), which the 2e-2 bar alone would
+    let hide in any output smaller than 0.02 rms.
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import functools
+import os
 
 import numpy as np
 import torch
@@ -22,7 +36,16 @@ import synth
 from oracle import moe_oracle as O
 
 Y_TOL = 2e-2
+Y_ELEM_TOL = 5e-3
 W_RTOL = 1e-5
+
+
+def half_ulp_bf16(v):
+    """Half the spacing of bf16 numbers at |v| (8 significant bits; the
+    subnormal spacing 2^-133 below 2^-126)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    _, e = np.frexp(np.where(a > 0, a, 1.0))           # a in [2^(e-1), 2^e)
+    return np.ldexp(1.0, np.maximum(e - 9, -134))
 
 
 @functools.lru_cache(maxsize=None)
@@ -59,10 +82,22 @@ def from_dev_u16(t):
     return t.cpu().numpy().view(np.uint16)
 
 
+_POOL = None
+
+
+def pool():
+    """A thread pool for the oracle's expert evaluations (NumPy releases the
+    interpreter lock in its array work), sized to this process's cores."""
+    global _POOL
+    if _POOL is None:
+        _POOL = cf.ThreadPoolExecutor(max_workers=max(1, min(16, len(os.sched_getaffinity(0)))))
+    return _POOL
+
+
 def run_gpu(m, x_bits, w, bias=None, ws=None, poison=False, policy=None, nvfp4=None):
-    """nvfp4: dict(codes, scales, tscales) of NVFP4 experts (device tensors) to
-    run moe_w4_forward_nvfp4 instead of the int4 layer."""
-    """Run one forward; returns y bits and the routing results read from the workspace."""
+    """Run one forward; returns y bits and the routing results read from the
+    workspace.  nvfp4: dict(codes, scales, tscales) of NVFP4 experts (device
+    tensors) to run moe_w4_forward_nvfp4 instead of the int4 layer."""
     T = x_bits.shape[0]
     x = to_dev_u16(x_bits)
     y = torch.empty((T, 2048), dtype=torch.int16, device="cuda")
@@ -95,11 +130,19 @@ def compare(gpu, ref, tokens=None, label=""):
     """Check the bar; returns a summary dict.  `tokens`: rows of ref['y'] (None = all)."""
     T = gpu["topk_idx"].shape[0]
     flagged = ref["near_tie"]
+    order_flag = ref["order_tie"]
     same_route = np.all(gpu["topk_idx"] == ref["topk_idx"], axis=1)
-    bad = ~same_route & ~flagged
-    assert not bad.any(), f"{label}: routing differs on unflagged tokens {np.nonzero(bad)[0][:10]}"
-    ok = same_route
-    np.testing.assert_allclose(gpu["topk_w"][ok], ref["topk_w"][ok], rtol=W_RTOL, atol=1e-7,
+    same_set = np.all(np.sort(gpu["topk_idx"], axis=1) == np.sort(ref["topk_idx"], axis=1), axis=1)
+    bad = ~same_set & ~flagged
+    assert not bad.any(), f"{label}: chosen experts differ on unflagged tokens {np.nonzero(bad)[0][:10]}"
+    bad = same_set & ~same_route & ~order_flag
+    assert not bad.any(), f"{label}: slot order differs without an order tie on tokens {np.nonzero(bad)[0][:10]}"
+    ok = same_set
+    # weights compared expert by expert (the slot order may differ on order ties)
+    go = np.argsort(gpu["topk_idx"], axis=1, kind="stable")
+    ro = np.argsort(ref["topk_idx"], axis=1, kind="stable")
+    np.testing.assert_allclose(np.take_along_axis(gpu["topk_w"], go, 1)[ok],
+                               np.take_along_axis(ref["topk_w"], ro, 1)[ok], rtol=W_RTOL, atol=1e-7,
                                err_msg=f"{label}: topk_w")
     # sort results
     if same_route.all():
@@ -131,6 +174,13 @@ def compare(gpu, ref, tokens=None, label=""):
     err = np.abs(yg[keep] - yr[keep])
     max_err = float(err.max()) if err.size else 0.0
     assert np.all(np.isfinite(yg[keep])), f"{label}: non-finite output"
-    assert max_err <= Y_TOL * rms, f"{label}: max|err| {max_err:.3e} > {Y_TOL} * rms {rms:.3e}"
-    return dict(T=T, flagged=int(flagged.sum()), rerouted=int((~same_route).sum()),
-                max_err=max_err, rms=rms, ratio=max_err / rms if rms else 0.0)
+    excess = (err - half_ulp_bf16(yr[keep])) / rms if rms else np.zeros_like(err)
+    elem = float(excess.max()) if excess.size else 0.0
+    assert elem <= Y_TOL, f"{label}: error beyond the bf16 rounding of y {elem:.3e} * rms > {Y_TOL} * rms"
+    if elem > Y_ELEM_TOL:
+        i = np.unravel_index(int(np.argmax(excess)), excess.shape)
+        raise AssertionError(f"{label}: element {i} of the compared rows: |err| {err[i]:.3e} exceeds half an ulp "
+                             f"of {yr[keep][i]:.4e} + {Y_ELEM_TOL} * rms ({elem:.3e} * rms beyond the ulp)")
+    return dict(T=T, flagged=int(flagged.sum()), rerouted=int((~same_set).sum()),
+                reordered=int((same_set & ~same_route).sum()), max_err=max_err, rms=rms,
+                ratio=max_err / rms if rms else 0.0, elem=elem)

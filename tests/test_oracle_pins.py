@@ -52,6 +52,21 @@ def decode_xor(packed, k):
     return (nib ^ 8) - 8
 
 
+def bf16_exact(t):
+    """A float64 tensor rounded to bf16 (nearest, ties to even) in one step,
+    element by element with Python's frexp and round-half-even (torch's own
+    fp64 -> bf16 conversion rounds twice, through fp32)."""
+    flat = t.reshape(-1).tolist()
+    out = []
+    for v in flat:
+        if v == 0.0 or not math.isfinite(v):
+            out.append(v)
+            continue
+        m, e = math.frexp(v)                 # v = m 2^e, 0.5 <= |m| < 1
+        out.append(math.ldexp(round(m * 256.0), e - 8))
+    return torch.tensor(out, dtype=torch.float64).reshape(t.shape)
+
+
 def widen(bits):
     return torch.from_numpy(np.asarray(bits, dtype=np.uint16).astype(np.int32) << 16).view(torch.float32).double()
 
@@ -336,7 +351,8 @@ def test_dense_mlp_closed_form_on_one_hot_rows():
     w[2 * n + m_out * O.I_D + j] = bits[2]
     out = O.dense_mlp(x, w)
     xk = O.bf16_to_f64(x)[:, k]
-    expect = c * (a * xk / (1 + np.exp(-a * xk))) * (b * xk)
+    h = (a * xk / (1 + np.exp(-a * xk))) * (b * xk)
+    expect = c * bf16_exact(torch.from_numpy(h)).numpy()   # the down linear's input is bf16
     np.testing.assert_allclose(out["y"][:, m_out], expect, rtol=1e-13)
     assert np.count_nonzero(out["y"]) == np.count_nonzero(expect)
 
@@ -516,6 +532,32 @@ def test_near_tie_flag_uses_the_6th_7th_gap():
     np.testing.assert_array_equal(rt["near_tie"], rt["gap"] <= 1e-3)
 
 
+def test_order_tie_flag_uses_the_gaps_inside_the_six():
+    """order_gap is the smallest difference between consecutive chosen logits
+    (brute force over the six), flagged at 1e-3; a router built with two
+    chosen logits 5e-4 apart flags exactly that token."""
+    x, R, _ = small_layer(12, 32)
+    xf = O.bf16_to_f64(x)
+    rt = O.route(xf, R)
+    for t in range(32):
+        six = sorted(rt["logits"][t][rt["topk_idx"][t]], reverse=True)
+        assert rt["order_gap"][t] == pytest.approx(min(a - b for a, b in zip(six, six[1:])), abs=1e-15)
+    np.testing.assert_array_equal(rt["order_tie"], rt["order_gap"] <= 1e-3)
+    # one-hot tokens: x_t = e_t picks router column t; rows 0..5 get logits
+    # 6, 5, 4, 3, 2.0005, 2 on token 0 (a 5e-4 gap between its 5th and 6th)
+    Rz = np.zeros((256, 2048), dtype=np.uint16)
+    vals = [6.0, 5.0, 4.0, 3.0, 2.0 + 2 ** -11, 2.0]
+    for e, v in enumerate(vals):
+        Rz[e, 0] = synth.f32_to_bf16_bits(np.float32([v]))[0] if v != 2.0 + 2 ** -11 else 0
+    xo = np.zeros((2, 2048))
+    xo[0, 0] = 1.0
+    bias = np.zeros(256)
+    bias[4] = 2.0 + 2 ** -11     # a logit that bf16 router rows cannot hold exactly, through the bias
+    r1 = O.route(xo, Rz, bias=bias)
+    assert r1["order_gap"][0] == pytest.approx(2 ** -11) and r1["order_tie"][0]
+    assert not r1["near_tie"][0]
+
+
 # ------------------------------------------------------------------------- sort
 def test_sort_against_nested_loops():
     rng = np.random.default_rng(12)
@@ -562,7 +604,7 @@ def test_layer_matches_weight_side_recomputation():
         sg = widen(S[:2048 * 1024]).reshape(1024, 2048)
         su = widen(S[2048 * 1024:4096 * 1024]).reshape(1024, 2048)
         sd = widen(S[4096 * 1024:]).reshape(2048, 1024)
-        z = sd @ (torch.nn.functional.silu(sg @ xt[t]) * (su @ xt[t]))
+        z = sd @ bf16_exact(torch.nn.functional.silu(sg @ xt[t]) * (su @ xt[t]))
         want = (acc + z).numpy()
         assert list(out["topk_idx"][t]) == sel
         np.testing.assert_allclose(out["y"][t], want, rtol=1e-9, atol=1e-9 * np.abs(want).max())
@@ -575,7 +617,7 @@ def test_zero_scales_reduce_to_shared_expert():
     sg = widen(S[:2048 * 1024]).reshape(1024, 2048)
     su = widen(S[2048 * 1024:4096 * 1024]).reshape(1024, 2048)
     sd = widen(S[4096 * 1024:]).reshape(2048, 1024)
-    z = (torch.nn.functional.silu(xt @ sg.T) * (xt @ su.T)) @ sd.T
+    z = bf16_exact(torch.nn.functional.silu(xt @ sg.T) * (xt @ su.T)) @ sd.T
     np.testing.assert_allclose(out["y"], z.numpy(), rtol=1e-12, atol=1e-12)
     ref_bits = z.float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     # one rounding from fp64 vs torch's fp64->fp32->bf16: equal except at exact double-rounding cases
@@ -630,7 +672,7 @@ def test_stack_with_shared_only_layers():
     sd = widen(S[4096 * 1024:]).reshape(2048, 1024)
     for _ in range(2):
         xin = torch.nn.functional.rms_norm(r.double(), (2048,), eps=1e-6).float().to(torch.bfloat16).double()
-        z = (torch.nn.functional.silu(xin @ sg.T) * (xin @ su.T)) @ sd.T
+        z = bf16_exact(torch.nn.functional.silu(xin @ sg.T) * (xin @ su.T)) @ sd.T
         r = r + z.float().to(torch.bfloat16).float()
     # equal up to the rare double-rounding difference of fp64->fp32->bf16
     np.testing.assert_allclose(out, r.double().numpy(), rtol=1e-2, atol=1e-2)
