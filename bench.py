@@ -7,12 +7,19 @@
 A step is one pass of the whole layer (router, sort, rotation, routed experts,
 shared expert, combine) over one batch of seeded synthetic tokens, with
 weights and inputs already resident in HBM.  Consecutive steps use different
-layers' weights (generated on the device from the same seeded recipe), so a
-step cannot be served from the 256 MB Infinity Cache left by the previous one,
-as in a real layer stack.  Prints one JSON line.
+layers' weights (generated on the device from the same seeded recipe; 24
+layers at T = 1, whose 23.4 MB per layer would otherwise fit the 256 MB
+Infinity Cache, 4 at larger T), so a step cannot be served from the cache
+contents of the steps before it, as in a real layer stack.  Prints one JSON
+line: `value` is tokens/s over exactly K back-to-back steps; `step_us` gives
+the median, p10 and p90 of at least 200 steps timed one by one with HIP
+events; `roofline` is that of the dominant stage.
 
 The default workload is decode_t32: T = 32 tokens (8 sequences x (1 decoded +
-3 speculative)), x seed 1, weights seed 0.
+3 speculative)), x seed 1, weights seed 0.  Its line also carries the
+metric's other points under "points": decode_t1 (T = 1) and prefill_t2048
+(T = 2048, uniform and skewed routing), each timed the same way with its own
+roofline.  The stack configs run moe_w4_stack_forward over 47 layers.
 """
 from __future__ import annotations
 
@@ -52,7 +59,10 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--eager", action="store_true",
                     help="stack configs: launch every layer from the host instead of replaying a captured graph")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="oracle baseline: seconds per thread setting (all cores, then one thread)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="decode_t32: skip the T = 1 and T = 2048 points of the default line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain device-to-device copy of known size (10 x 256 MiB)")
     ap.add_argument("--traffic-lines", nargs=5,
@@ -207,15 +217,42 @@ def traffic_lines(workload, fetch_csv, write_csv, cal_fetch_csv, cal_write_csv):
                 print(f"{workload} {kern} {fb:.0f} {wb:.0f} {fb + wb:.0f} {sources_digest(files)}")
 
 
+def cpu_cores():
+    """Cores this process may run on (its affinity mask)."""
+    return len(os.sched_getaffinity(0))
+
+
+def timed_oracle(fn, budget_s, max_reps, threads):
+    """Call fn() for about budget_s seconds (at least once) with NumPy's BLAS
+    pool limited to `threads`; returns (reps, seconds per rep, BLAS threads
+    used).  NumPy's element-wise work is single-threaded either way."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    with threadpool_limits(limits=threads):
+        used = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] + [1])
+        reps, elapsed = 0, 0.0
+        while reps == 0 or (elapsed < budget_s and reps < max_reps):
+            t0 = time.perf_counter()
+            fn()
+            elapsed += time.perf_counter() - t0
+            reps += 1
+    return reps, elapsed / reps, used
+
+
+def oracle_baseline(fn, units, unit, budget_s, max_reps, sample):
+    """The oracle timed on all of this process's cores and on one thread:
+    the cpu_baseline object (`units` of work per call of fn)."""
+    reps, per, used = timed_oracle(fn, budget_s, max_reps, cpu_cores())
+    reps1, per1, _ = timed_oracle(fn, budget_s, max_reps, 1)
+    return {"value": units / per, "unit": unit, "cores": int(used), "kind": "oracle",
+            "sample": f"{sample}; {reps} calls of {per:.2f} s on {used} BLAS threads ({cpu_cores()} cores in "
+                      f"the affinity mask), {reps1} of {per1:.2f} s on one thread",
+            "single_thread": {"value": units / per1, "unit": unit, "cores": 1}}
+
+
 def cpu_baseline(cfg, T, x_bits, bias, budget_s):
     """The CPU oracle as it stands, on a bounded sample of the same workload."""
     import synth
     from oracle import moe_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count()
     R = synth.gen_router(0, 0)
     S = synth.gen_shared(0, 0)
     # the oracle routes every token; its expert work is timed on a token sample
@@ -227,16 +264,10 @@ def cpu_baseline(cfg, T, x_bits, bias, budget_s):
     for e in need:                               # input preparation, not timed
         c, s = synth.gen_codes_scales(0, 0, experts=[e])
         blobs[e] = (c[0], s[0])
-    reps, elapsed = 0, 0.0
-    while elapsed < budget_s and reps < 50:
-        t0 = time.perf_counter()
-        O.moe_layer(x_bits, R, blobs.__getitem__, S, bias=bias, tokens=tokens)
-        elapsed += time.perf_counter() - t0
-        reps += 1
-    per_rep = elapsed / reps
-    return {"value": n_tok / per_rep, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{reps} oracle layer calls on {n_tok} of the {T} tokens (fp64 NumPy, routing of all "
-                      f"{T} tokens included), {per_rep:.2f} s each"}
+    return oracle_baseline(lambda: O.moe_layer(x_bits, R, blobs.__getitem__, S, bias=bias, tokens=tokens),
+                           n_tok, "tokens/s", budget_s, 50,
+                           f"oracle layer calls (fp64 NumPy) on {n_tok} of the {T} tokens, the routing of all "
+                           f"{T} included")
 
 
 def bench_nvfp4(a, T):
@@ -327,11 +358,6 @@ def bench_nvfp4(a, T):
     }
     if not a.no_cpu:
         log("timing the CPU oracle baseline")
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-        except Exception:
-            cores = os.cpu_count()
         R, S = synth.gen_router(cfg["w_seed"], 0), synth.gen_shared(cfg["w_seed"], 0)
         rt = O.route(O.bf16_to_f64(x_bits), R)
         sc, ts = synth.gen_nvfp4_scales(cfg["w_seed"], 0), synth.gen_nvfp4_tensor_scales(cfg["w_seed"], 0)
@@ -341,16 +367,10 @@ def bench_nvfp4(a, T):
         # past 32 tokens the expert work is timed on the first 8 tokens
         n_tok = T if T <= 32 else 8
         tokens = None if T <= 32 else np.arange(n_tok)
-        reps, elapsed = 0, 0.0
-        while elapsed < a.cpu_seconds and reps < 50:
-            t0 = time.perf_counter()
-            O.moe_layer_nvfp4(x_bits, R, blobs.__getitem__, S, tokens=tokens)
-            elapsed += time.perf_counter() - t0
-            reps += 1
-        per_rep = elapsed / reps
-        result["cpu_baseline"] = {"value": n_tok / per_rep, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-                                  "sample": f"{reps} oracle layer calls on {n_tok} of the {T} tokens (fp64 NumPy, "
-                                            f"routing of all {T} included), {per_rep:.2f} s each"}
+        result["cpu_baseline"] = oracle_baseline(
+            lambda: O.moe_layer_nvfp4(x_bits, R, blobs.__getitem__, S, tokens=tokens), n_tok, "tokens/s",
+            a.cpu_seconds, 50, f"oracle layer calls (fp64 NumPy) on {n_tok} of the {T} tokens, the routing of all "
+                               f"{T} included")
     print(json.dumps(result), flush=True)
 
 
@@ -395,20 +415,9 @@ def bench_pack(a):
                            "traffic": recorded_traffic("pack_layer", "pack", None),
                            "algorithmic_bytes": nbytes, "kernel_us": kern_ms * 1e3}}
     if not a.no_cpu:
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-        except Exception:
-            cores = os.cpu_count()
         sample = w[:2].cpu().numpy().view(np.uint16)
-        reps, elapsed = 0, 0.0
-        while elapsed < a.cpu_seconds and reps < 20:
-            t0 = time.perf_counter()
-            O.pack_expert_bank(sample)
-            elapsed += time.perf_counter() - t0
-            reps += 1
-        result["cpu_baseline"] = {"value": 2 * reps / elapsed, "unit": "experts/s", "cores": int(cores),
-                                  "kind": "oracle", "sample": f"{reps} oracle packs of 2 of the 256 experts"}
+        result["cpu_baseline"] = oracle_baseline(lambda: O.pack_expert_bank(sample), 2, "experts/s", a.cpu_seconds,
+                                                 20, "oracle packs of 2 of the 256 experts")
     print(json.dumps(result), flush=True)
 
 
@@ -463,21 +472,10 @@ def bench_mlp(a, T):
                                      f"(4 sets rotated)", "T": T},
               "roofline": roof}
     if not a.no_cpu:
-        try:
-            from threadpoolctl import threadpool_info
-            cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-        except Exception:
-            cores = os.cpu_count()
         wb = ws_[0].cpu().numpy().view(np.uint16)
         n_tok = min(T, 64)
-        reps, elapsed = 0, 0.0
-        while elapsed < a.cpu_seconds and reps < 20:
-            t0 = time.perf_counter()
-            O.dense_mlp(x_bits[:n_tok], wb)
-            elapsed += time.perf_counter() - t0
-            reps += 1
-        result["cpu_baseline"] = {"value": n_tok * reps / elapsed, "unit": "tokens/s", "cores": int(cores),
-                                  "kind": "oracle", "sample": f"{reps} oracle calls on {n_tok} of the {T} tokens"}
+        result["cpu_baseline"] = oracle_baseline(lambda: O.dense_mlp(x_bits[:n_tok], wb), n_tok, "tokens/s",
+                                                 a.cpu_seconds, 20, f"oracle calls on {n_tok} of the {T} tokens")
     print(json.dumps(result), flush=True)
 
 
@@ -487,16 +485,10 @@ def cpu_baseline_stack(T, x_bits, budget_s):
     host generator, generation included in the time), scaled to 47 layers."""
     import synth
     from oracle import moe_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        cores = os.cpu_count()
     n_l = 2
     resid0 = O.bf16_to_f64(x_bits)
-    reps, elapsed = 0, 0.0
-    while elapsed < budget_s and reps < 5:
-        t0 = time.perf_counter()
+
+    def run():
         layers = []
         for l in range(n_l):
             cache = {}
@@ -508,175 +500,93 @@ def cpu_baseline_stack(T, x_bits, budget_s):
                 return cache[e]
             layers.append((synth.gen_router(synth.STACK_SEED, l), blobs, synth.gen_shared(synth.STACK_SEED, l)))
         O.stack_step(resid0, layers)
-        elapsed += time.perf_counter() - t0
-        reps += 1
-    per_step = elapsed / reps * 47 / n_l
-    return {"value": T / per_step, "unit": "tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{reps} oracle runs of the first {n_l} of the 47 layers at T={T} (weights of each layer "
-                      f"and its selected experts generated on the host inside the timing), scaled to 47 layers: "
-                      f"{per_step:.1f} s per stack step"}
+    # T tokens per stack step = 47 / n_l sampled runs
+    return oracle_baseline(run, T * n_l / 47, "tokens/s", budget_s, 5,
+                           f"oracle runs of the first {n_l} of the 47 layers at T={T} (weights of each layer and "
+                           f"its selected experts generated on the host inside the timing), scaled to 47 layers")
 
 
-def main():
-    a = parse()
-    if a.pmc_summary:
-        pmc_summary(a.pmc_summary)
-        return
-    if a.traffic_lines:
-        traffic_lines(*a.traffic_lines)
-        return
-    if a.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported (the layer needs no "
-              "collective: a multi-GPU deployment replicates it per GPU).", file=sys.stderr)
-        sys.exit(2)
-    if a.copy_calibration:
-        copy_calibration()
-        return
-    if a.config == "pack_layer":
-        bench_pack(a)
-        return
-    if a.config.startswith("mlp_t"):
-        bench_mlp(a, int(a.config[5:]))
-        return
-    if a.config.startswith("nvfp4_t"):
-        bench_nvfp4(a, int(a.config[7:]))
-        return
+def step_distribution(m, step, reps):
+    """Per-step times from a HIP event pair around each of `reps` steps on the
+    launch stream: median, p10 and p90 in microseconds."""
+    import torch
+    ev = m.HipEvents(2 * reps)
+    for i in range(reps):
+        ev.record(2 * i)
+        step(i)
+        ev.record(2 * i + 1)
+    torch.cuda.synchronize()
+    t = np.array([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(reps)]) * 1e3
+    ev.close()
+    return {"reps": reps, "median_us": float(np.median(t)), "p10_us": float(np.percentile(t, 10)),
+            "p90_us": float(np.percentile(t, 90))}
+
+
+METRIC = "routed-MoE layer tokens/s + % HBM BW (T=1,32) / % bf16 MFMA (T=2048)"
+# layers rotated through by default: enough that the weights a run touches
+# exceed the 256 MB Infinity Cache (T = 1 touches 23.4 MB per layer)
+DEFAULT_LAYERS = {1: 24}
+
+
+def bench_layer(a, name, steps, warmup, with_cpu):
+    """One MoE layer (moe_w4_forward) over the workload `name`: returns the
+    result object (throughput of exactly `steps` back-to-back steps, per-step
+    distribution, per-stage times and the dominant stage's roofline)."""
     import torch
     import synth
     from int4_routed_expert_amd import moe_w4 as m
-
-    dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    stack = a.config.startswith("stack")
-    if stack:
-        T = 1 if a.config == "stack_t1" else 8
-        n_layers = 47
-        cfg = dict(T=T, x_seed=synth.STACK_SEED, w_seed=synth.STACK_SEED, bias_seed=None)
-    else:
-        cfg = synth.CONFIGS[a.config]
-        T = cfg["T"]
-        n_layers = a.layers or 4
-    log(f"config {a.config}: T={T}, {n_layers} layers on the device")
+    cfg = synth.CONFIGS[name]
+    T = cfg["T"]
+    n_layers = a.layers or DEFAULT_LAYERS.get(T, 4)
+    log(f"config {name}: T={T}, {n_layers} layers on the device")
     layers = [m.generated_layer(cfg["w_seed"], l) for l in range(n_layers)]
     x_bits = synth.gen_x(cfg["x_seed"], T)
-    x = torch.from_numpy(x_bits.view(np.int16)).to(dev)
+    x = torch.from_numpy(x_bits.view(np.int16)).cuda()
     bias_np = None if cfg["bias_seed"] is None else synth.skew_bias(cfg["bias_seed"])
-    bias = None if bias_np is None else torch.from_numpy(bias_np).to(dev)
-    y = torch.empty((T, 2048), dtype=torch.int16, device=dev)
+    bias = None if bias_np is None else torch.from_numpy(bias_np).cuda()
+    y = torch.empty((T, 2048), dtype=torch.int16, device="cuda")
     ws = m.workspace(T)
-    stream = torch.cuda.current_stream()
     n_pts = m.moe_w4_profile_points()
     names = [m.moe_w4_profile_point_name(i) for i in range(n_pts)]
 
-    stack_bytes = None
-    if stack:
-        resid0 = x.view(torch.bfloat16).float()
-        resid = resid0.clone()
-        xb = torch.empty_like(y)
-
-        def eager_step(i=0, ev=None):
-            for w in layers:
-                m.moe_w4_stack_layer(resid, w["router_w"], w["codes"], w["scales"], w["shared_w"], xb, y, ws)
-
-        # algorithmic bytes of one step: each layer's touched experts, router,
-        # shared expert, and the layer's x and y
-        resid.copy_(resid0)
-        touched = 0
-        for w in layers:
-            m.moe_w4_stack_layer(resid, w["router_w"], w["codes"], w["scales"], w["shared_w"], xb, y, ws)
-            touched += int(m.ws_view(ws, T, "n_active", torch.int32, 1).item())
-        stack_bytes = touched * EXPERT_BYTES + 47 * (ROUTER_BYTES + SHARED_BYTES + 2 * T * 2048 * 2)
-        ref = resid.clone()
-        if a.eager:
-            step = eager_step
+    def step(i, ev=None):
+        w = layers[i % n_layers]
+        if ev is None:
+            m.moe_w4_forward(x, w["router_w"], w["codes"], w["scales"], w["shared_w"], y, ws, router_bias=bias)
         else:
-            # one step (47 layers, all launches) captured as a HIP graph; each
-            # replay is checked against the eager result before timing
-            graph = torch.cuda.CUDAGraph()
-            resid.copy_(resid0)
-            torch.cuda.synchronize()
-            with torch.cuda.graph(graph):
-                eager_step()
-            torch.cuda.synchronize()
-            for rep in range(3):
-                resid.copy_(resid0)
-                graph.replay()
-                torch.cuda.synchronize()
-                if not torch.equal(resid, ref):
-                    print("graph replay differs from the eager stack step", file=sys.stderr)
-                    sys.exit(1)
-            log("graph replays match the eager step")
+            m.moe_w4_forward_profiled(x, w["router_w"], w["codes"], w["scales"], w["shared_w"], y, ws,
+                                      ev, router_bias=bias)
 
-            def step(i=0, ev=None):
-                graph.replay()
-    else:
-        def step(i, ev=None):
-            w = layers[i % n_layers]
-            if ev is None:
-                m.moe_w4_forward(x, w["router_w"], w["codes"], w["scales"], w["shared_w"], y, ws, router_bias=bias)
-            else:
-                m.moe_w4_forward_profiled(x, w["router_w"], w["codes"], w["scales"], w["shared_w"], y, ws,
-                                          ev, router_bias=bias)
-
-    for i in range(a.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    log(f"warmup {a.warmup} done")
-
-    # timed region: exactly K steps, no events inside
-    torch.cuda.synchronize()
+    # timed region: exactly `steps` steps, no events inside
     t0 = time.perf_counter()
-    for i in range(a.steps):
+    for i in range(steps):
         step(i)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / a.steps
-    log(f"timed {a.steps} steps: {ms * 1e3:.1f} us/step")
-    if not stack:
-        # per-kernel region: the same K steps again, with HIP events recorded on the
-        # launch stream at every stage boundary (each record adds a gap between
-        # kernels, which is why the throughput above is timed without them)
-        events = m.HipEvents(a.steps * n_pts)
-        for i in range(a.steps):
-            step(i, events.handles[i * n_pts:(i + 1) * n_pts])
-        torch.cuda.synchronize()
-
-    result = {
-        "metric": "routed-MoE layer tokens/s + % HBM BW (T=1,32) / % bf16 MFMA (T=2048)",
-        "value": None, "unit": "tokens/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
-        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "int4 x fp16/bf16 -> fp32", "data": "synthetic (seeded SplitMix64; random-init weights)",
-    }
-    if stack:
-        result["value"] = T / (ms / 1e3)
-        result["config"] = {"workload": f"{a.config}: 47-layer MoE stack, T={T}, seed 4, fp32 residual"
-                                        + (", host launches" if a.eager else ", one captured graph per step"),
-                            "T": T, "layers": 47, "per_layer_us": ms * 1e3 / 47}
-        gbs = stack_bytes / (ms * 1e-3) / 1e9
-        result["stack"] = {"algorithmic_bytes": stack_bytes, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS}
-        # the whole step is the unit here: 47 layers replayed as one graph
-        result["roofline"] = {"bound": "hbm", "kernel": "stack step (47 layers, one graph)", "achieved": gbs,
-                              "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                              "algorithmic_bytes": stack_bytes, "kernel_us": ms * 1e3}
-        if not a.no_cpu:
-            log("timing the CPU oracle baseline")
-            result["cpu_baseline"] = cpu_baseline_stack(T, x_bits, a.cpu_seconds)
-        print(json.dumps(result), flush=True)
-        return
-
-    # stage times from the events of the timed steps
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    log(f"{name}: timed {steps} steps: {ms * 1e3:.1f} us/step")
+    dist = step_distribution(m, step, max(steps, 200))
+    # per-stage times: the same steps again with HIP events on the launch stream
+    # at every stage boundary (each record adds a gap between kernels, which is
+    # why the throughput above is timed without them)
+    reps = max(steps, 200)
+    events = m.HipEvents(reps * n_pts)
+    for i in range(reps):
+        step(i, events.handles[i * n_pts:(i + 1) * n_pts])
+    torch.cuda.synchronize()
     stage_ms = np.zeros(n_pts - 1)
-    for i in range(a.steps):
-        for s in range(n_pts - 1):
-            stage_ms[s] += events.elapsed_ms(i * n_pts + s, i * n_pts + s + 1)
-    stage_ms /= a.steps
+    for i in range(reps):
+        for k in range(n_pts - 1):
+            stage_ms[k] += events.elapsed_ms(i * n_pts + k, i * n_pts + k + 1)
+    stage_ms /= reps
     events.close()
 
     # routing of the benchmarked layers decides the algorithmic bytes
     touched = []
-    for l in range(min(n_layers, a.steps)):
-        w = layers[l]
-        m.moe_w4_forward(x, w["router_w"], w["codes"], w["scales"], w["shared_w"], y, ws, router_bias=bias)
+    for l in range(n_layers):
+        step(l)
         torch.cuda.synchronize()
         touched.append(int(m.ws_view(ws, T, "n_active", torch.int32, 1).item()))
     n_touched = float(np.mean(touched))
@@ -710,29 +620,165 @@ def main():
         "routed_down": T * 6 * 2048 * 512 * 2,
         "shared_down_combine": T * 1024 * 2048 * 2,
     }
-    result["value"] = T / (ms / 1e3)
-    result["config"] = {"workload": f"{a.config}: one MoE layer, T={T}, x seed {cfg['x_seed']}, weights seed "
-                                    f"{cfg['w_seed']}" + (", +3.0 bias on 26 experts (seed 3)" if bias is not None else ""),
-                        "T": T, "layers_rotated": n_layers, "touched_experts": n_touched}
+    result = {
+        "metric": METRIC, "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4 x fp16/bf16 -> fp32", "data": "synthetic (seeded SplitMix64; random-init weights)",
+        "config": {"workload": f"{name}: one MoE layer, T={T}, x seed {cfg['x_seed']}, weights seed "
+                               f"{cfg['w_seed']}" + (", +3.0 bias on 26 experts (seed 3)" if bias is not None else ""),
+                   "T": T, "layers_rotated": n_layers, "touched_experts": n_touched},
+        "step_us": dist,
+    }
     if T >= GROUPED_MIN_TOKENS:
         dom_flops = stage_flops.get(dom, 0.0)
         tf = dom_flops / (stage[dom] * 1e-3) / 1e12
         result["roofline"] = {"bound": "mfma", "kernel": dom, "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
                               "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
-                              "traffic": recorded_traffic(a.config, dom, T), "algorithmic_flops": dom_flops,
+                              "traffic": recorded_traffic(name, dom, T), "algorithmic_flops": dom_flops,
                               "algorithmic_bytes": dom_bytes, "kernel_us": stage[dom] * 1e3}
     else:
         result["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                              "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(a.config, dom, T),
+                              "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(name, dom, T),
                               "algorithmic_bytes": dom_bytes, "kernel_us": stage[dom] * 1e3}
     result["layer"] = {"algorithmic_bytes": layer_bytes, "hbm_gbs": layer_bytes / (ms * 1e-3) / 1e9,
                        "hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                        "tflops": flops / (ms * 1e-3) / 1e12,
                        "mfma_frac": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
                        "stage_us": {k: v * 1e3 for k, v in stage.items()}}
-    if not a.no_cpu:
-        log("timing the CPU oracle baseline")
+    del layers
+    torch.cuda.empty_cache()
+    if with_cpu:
+        log(f"{name}: timing the CPU oracle baseline")
         result["cpu_baseline"] = cpu_baseline(cfg, T, x_bits, bias_np, a.cpu_seconds)
+    return result
+
+
+def bench_stack(a, T, with_cpu):
+    """The 47-layer stack at T tokens: one moe_w4_stack_forward call per step,
+    captured once as a HIP graph (checked against the eager call) and replayed."""
+    import torch
+    import synth
+    from int4_routed_expert_amd import moe_w4 as m
+    log(f"stack: T={T}, 47 layers on the device")
+    layers = [m.generated_layer(synth.STACK_SEED, l) for l in range(47)]
+    arr = m.stack_layers(layers)
+    x_bits = synth.gen_x(synth.STACK_SEED, T)
+    x = torch.from_numpy(x_bits.view(np.int16)).cuda()
+    resid0 = x.view(torch.bfloat16).float()
+    resid = resid0.clone()
+    ws = m.stack_workspace(T)
+    # algorithmic bytes of one step: each layer's touched experts, router,
+    # shared expert, and the layer's x and y (routing read from a traced run)
+    trace = torch.empty((47, 2, T, 2048), dtype=torch.int16, device="cuda")
+    m.moe_w4_stack_forward(resid, arr, ws, trace=trace)
+    torch.cuda.synchronize()
+    ref = resid.clone()
+    del trace
+    wsl = m.workspace(T)
+    yb = torch.empty((T, 2048), dtype=torch.int16, device="cuda")
+    touched = 0
+    resid.copy_(resid0)
+    xb = torch.empty_like(yb)
+    for w in layers:
+        m.moe_w4_stack_layer(resid, w["router_w"], w["codes"], w["scales"], w["shared_w"], xb, yb, wsl)
+        touched += int(m.ws_view(wsl, T, "n_active", torch.int32, 1).item())
+    torch.cuda.synchronize()
+    if not torch.equal(resid, ref):
+        print("per-layer calls differ from moe_w4_stack_forward", file=sys.stderr)
+        sys.exit(1)
+    stack_bytes = touched * EXPERT_BYTES + 47 * (ROUTER_BYTES + SHARED_BYTES + 2 * T * 2048 * 2)
+    if a.eager:
+        def step(i=0):
+            m.moe_w4_stack_forward(resid, arr, ws)
+    else:
+        graph = torch.cuda.CUDAGraph()
+        resid.copy_(resid0)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            m.moe_w4_stack_forward(resid, arr, ws)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            resid.copy_(resid0)
+            graph.replay()
+            torch.cuda.synchronize()
+            if not torch.equal(resid, ref):
+                print("graph replay differs from the eager stack step", file=sys.stderr)
+                sys.exit(1)
+        log("graph replays match the eager step")
+
+        def step(i=0):
+            graph.replay()
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / a.steps
+    log(f"stack T={T}: timed {a.steps} steps: {ms * 1e3:.1f} us/step")
+    dist = step_distribution(m, step, max(a.steps, 200))
+    gbs = stack_bytes / (ms * 1e-3) / 1e9
+    result = {
+        "metric": METRIC, "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4 x fp16/bf16 -> fp32", "data": "synthetic (seeded SplitMix64; random-init weights)",
+        "config": {"workload": f"stack_t{T}: 47-layer MoE stack (moe_w4_stack_forward), T={T}, seed 4, fp32 "
+                               "residual" + (", host launches" if a.eager else ", one captured graph per step"),
+                   "T": T, "layers": 47, "per_layer_us": ms * 1e3 / 47},
+        "step_us": dist,
+        "stack": {"algorithmic_bytes": stack_bytes, "hbm_gbs": gbs, "hbm_frac": gbs / HBM_PEAK_GBS},
+        # the whole step is the unit here: 47 layers replayed as one graph
+        "roofline": {"bound": "hbm", "kernel": "stack step (47 layers, one graph)", "achieved": gbs,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes": stack_bytes, "kernel_us": ms * 1e3},
+    }
+    if with_cpu:
+        log("timing the CPU oracle baseline")
+        result["cpu_baseline"] = cpu_baseline_stack(T, x_bits, a.cpu_seconds)
+    return result
+
+
+POINT_KEYS = ("value", "unit", "ms_per_step", "step_us", "config", "roofline", "layer")
+
+
+def main():
+    a = parse()
+    if a.pmc_summary:
+        pmc_summary(a.pmc_summary)
+        return
+    if a.traffic_lines:
+        traffic_lines(*a.traffic_lines)
+        return
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {a.gpus} is not supported (the layer needs no "
+              "collective: a multi-GPU deployment replicates it per GPU).", file=sys.stderr)
+        sys.exit(2)
+    if a.copy_calibration:
+        copy_calibration()
+        return
+    if a.config == "pack_layer":
+        bench_pack(a)
+        return
+    if a.config.startswith("mlp_t"):
+        bench_mlp(a, int(a.config[5:]))
+        return
+    if a.config.startswith("nvfp4_t"):
+        bench_nvfp4(a, int(a.config[7:]))
+        return
+    import torch
+    torch.cuda.set_device(0)
+    if a.config.startswith("stack"):
+        print(json.dumps(bench_stack(a, 1 if a.config == "stack_t1" else 8, not a.no_cpu)), flush=True)
+        return
+    result = bench_layer(a, a.config, a.steps, a.warmup, not a.no_cpu)
+    if a.config == "decode_t32" and not a.headline_only:
+        # the metric's other points (T = 1 and T = 2048, uniform and skewed
+        # routing), each timed the same way, under "points"
+        result["points"] = {}
+        for name in ("decode_t1", "prefill_t2048", "prefill_t2048_skew"):
+            r = bench_layer(a, name, a.steps, a.warmup, False)
+            result["points"][name] = {k: r[k] for k in POINT_KEYS}
     print(json.dumps(result), flush=True)
 
 

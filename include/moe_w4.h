@@ -42,9 +42,9 @@
  *
  * Ownership and threading: the caller owns every buffer, including the
  * workspace.  The library allocates no device memory in these calls, keeps no
- * pointer after the enqueued work completes and holds no mutable global state,
- * so calls on different streams are independent if they use different
- * workspaces.  Work is enqueued on `stream` (a hipStream_t passed as void*;
+ * pointer after the enqueued work completes and holds no mutable global state
+ * apart from the diagnostic setting of moe_w4_set_fused_wait, so calls on
+ * different streams are independent if they use different workspaces.  Work is enqueued on `stream` (a hipStream_t passed as void*;
  * NULL = the default stream) and the call returns without synchronising.
  *
  * Errors: arguments are validated before any HIP call.  Asynchronous device
@@ -70,7 +70,10 @@ extern "C" {
 #define MOE_W4_CODE_BYTES_PER_EXPERT 1572864
 #define MOE_W4_SCALES_PER_EXPERT 24576
 #define MOE_W4_SHARED_ELEMS 6291456
-#define MOE_W4_MAX_TOKENS 1048576
+/* Largest T of a call.  Every 32-bit buffer offset of the kernels stays in
+ * range up to here (the largest workspace region, the expert rows o of 6T
+ * assignments, is 3.2 GB at this T), and the GPU tests run this size. */
+#define MOE_W4_MAX_TOKENS 65536
 #define MOE_W4_ALIGN 16
 /* From 1 to this many tokens a forward call is two launches (router + shared
  * gate/up, then the rest of the layer in one launch whose workgroups hand the
@@ -78,6 +81,10 @@ extern "C" {
  * in the workspace's `sync` region, cleared by the first launch); from
  * MOE_W4_FUSED_MAX_TOKENS + 1 tokens on, one launch per step. */
 #define MOE_W4_FUSED_MAX_TOKENS 8
+/* Most layers in one moe_w4_stack_forward call. */
+#define MOE_W4_STACK_MAX_LAYERS 1024
+/* Most elements of one moe_w4_generate_normal_bf16 call. */
+#define MOE_W4_GENERATE_MAX_ELEMS (1LL << 40)
 
 /* Router policy of moe_w4_forward_policy (bloomery issue #632, design thread
  * and its host-policy slice: the router rule distinguishes no normalisation,
@@ -115,10 +122,15 @@ extern "C" {
  *                         holds n.  (Written at every T; read only on that path.)
  *   logits    f32 [T][256] router logits R x, without the bias
  *   sync      4096 bytes of counters for the fused decode launch; their
- *             contents on entry do not matter (the call clears them itself). */
+ *             contents on entry do not matter (the call clears them itself).
+ *   error     i32 [1]: 0 after a call that completed normally; 1 if a down
+ *             workgroup of the two-launch form (1-8 tokens) gave up its
+ *             bounded wait for the gate/up results (its outputs are then NaN;
+ *             see moe_w4_set_fused_wait).  A stack call keeps a failure of any
+ *             of its layers. */
 typedef struct moe_w4_ws_layout {
     size_t logits, topk_idx, topk_w, offsets, perm, pos, n_active, active;
-    size_t xt, xt_scale, act, at, at_scale, hs, o, z, chunks, n_chunks, sync;
+    size_t xt, xt_scale, act, at, at_scale, hs, o, z, chunks, n_chunks, sync, error;
     size_t total;
 } moe_w4_ws_layout;
 
@@ -206,6 +218,15 @@ int moe_w4_generate_layer(uint64_t seed, int layer, void *router_w, void *codes,
 /* Seeded x: bf16 [T][2048], sigma 1, tid = 64*layer + 0. */
 int moe_w4_generate_x(uint64_t seed, int layer, int64_t T, void *x, void *stream);
 
+/* Any seeded "normal" bf16 tensor of the same scheme: out[i] =
+ * bf16_rne(f32(S(r(seed, tensor_id, i))) * f32(sigma*sqrt(3)/65536)) for
+ * i < n, S the centred sum of the four 16-bit lanes of r (an Irwin-Hall
+ * variate with the standard deviation sigma, bounded at about 3.46 sigma).
+ * out: device pointer, 2-byte aligned, n bf16.  n == 0 enqueues nothing.
+ * EINVAL for n outside [0, MOE_W4_GENERATE_MAX_ELEMS], a negative or
+ * non-finite sigma, or a NULL / misaligned out. */
+int moe_w4_generate_normal_bf16(uint64_t seed, uint32_t tensor_id, int64_t n, double sigma, void *out, void *stream);
+
 /* One layer of a stack: the caller's residual stream stays fp32.
  *   x_in = bf16_rne( resid / sqrt(mean(resid^2) + 1e-6) )    (unit-gain RMS norm)
  *   resid += f32( moe_w4_forward(x_in) )
@@ -215,6 +236,53 @@ int moe_w4_generate_x(uint64_t seed, int layer, int64_t T, void *x, void *stream
 int moe_w4_stack_layer(float *resid, const void *router_w, const void *codes, const void *scales,
                        const void *shared_w, int64_t T, void *x_buf, void *y_buf,
                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* The weights of one layer of a stack (device pointers, layouts of
+ * moe_w4_forward). */
+typedef struct moe_w4_layer {
+    const void *router_w;
+    const void *codes;
+    const void *scales;
+    const void *shared_w;
+} moe_w4_layer;
+
+/* Workspace bytes of moe_w4_stack_forward over T tokens (0 for an
+ * out-of-range T): a forward workspace plus one layer's bf16 x and y. */
+size_t moe_w4_stack_workspace_bytes(int64_t T);
+
+/* A stack of MoE layers (bloomery issue #632, readiness comment: Flint has 2
+ * dense and 47 routed blocks; this call runs the routed ones) over one batch:
+ * for l = 0 .. n_layers-1,
+ *   x_l   = bf16_rne( resid / sqrt(mean(resid^2) + 1e-6) )   (unit-gain RMS norm)
+ *   y_l   = moe_w4_forward(x_l) with layers[l]
+ *   resid = resid + f32(y_l)                                  (fp32 residual stream)
+ * resid: f32 [T][2048] device, in/out.  layers: host array of n_layers
+ * descriptors (read during the call only).  trace: NULL, or bf16
+ * [n_layers][2][T][2048] device memory that receives x_l and y_l of every
+ * layer (so each layer can be checked on its own input).  workspace: at least
+ * moe_w4_stack_workspace_bytes(T) bytes, contents on entry irrelevant; after
+ * the call its routing results (moe_w4_workspace_layout) are the last layer's
+ * and its error word covers every layer.  Enqueues only kernels (no
+ * allocation, no synchronisation, no memset), so it may be captured into a
+ * HIP graph.  T == 0 or n_layers == 0 enqueues nothing.  EINVAL for a bad
+ * T, n_layers outside [0, MOE_W4_STACK_MAX_LAYERS], a NULL or misaligned
+ * pointer (16 bytes; every layer's four), or resid / trace / workspace
+ * overlapping; EWORKSPACE for a short workspace; EDEVICE if a launch failed. */
+int moe_w4_stack_forward(float *resid, const moe_w4_layer *layers, int n_layers, int64_t T, void *trace,
+                         void *workspace, size_t workspace_bytes, void *stream);
+
+/* Diagnostic of the two-launch form (1-8 tokens), for tests of its failure
+ * path.  Its down workgroups wait, bounded in time, for the gate/up results:
+ * max_ticks sets the bound in ticks of the GPU's 100 MHz real-time clock (0
+ * restores the default, 500,000 = 5 ms) and extra_count a count the wait
+ * needs beyond the gate/up workgroups (default 0).  With extra_count > 0 the
+ * wait can never complete, so every down workgroup gives up after max_ticks:
+ * it writes NaN to its outputs (and to the residual stream in a stack layer)
+ * and sets the workspace's error word, and every kernel still exits normally.
+ * Process-wide; read when a call enqueues its launches (a captured graph keeps
+ * the values of its capture), so set it only while no other thread calls the
+ * library.  EINVAL for max_ticks outside [0, 2^32) or extra_count < 0. */
+int moe_w4_set_fused_wait(int64_t max_ticks, int extra_count);
 
 /* The packer: bf16 expert weights -> this library's int4 expert format (the
  * step before the layer).  Format from the Flint model card (Aijuus/flint-w4exp),

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "common.h"
 #include "launch.h"
 #include "moe_w4.h"
@@ -24,6 +26,11 @@ using namespace moe_w4;
 namespace {
 
 thread_local int g_last_device_error = 0;
+
+// Diagnostics of the two-launch form's bounded wait (moe_w4_set_fused_wait).
+constexpr uint32_t kDefaultWaitTicks = 500000;   // 5 ms of the 100 MHz real-time clock
+std::atomic<uint32_t> g_wait_ticks{kDefaultWaitTicks};
+std::atomic<int> g_wait_extra{0};
 
 constexpr size_t kAlignWs = 256;
 size_t align_up(size_t v) { return (v + kAlignWs - 1) & ~(kAlignWs - 1); }
@@ -58,6 +65,7 @@ moe_w4_ws_layout make_layout(int64_t T) {
     L.chunks = take(16 * (size_t)max_chunks((int)T));
     L.n_chunks = take(4);
     L.sync = take(4096);
+    L.error = take(4);
     L.total = off;
     return L;
 }
@@ -105,9 +113,12 @@ T_ *ws_at(void *ws, size_t off) { return reinterpret_cast<T_ *>(static_cast<char
 
 // resid (stack layers of 1-8 tokens only): x_ is then written, as
 // bf16(rmsnorm(resid)), by the first launch, and the last adds y to resid.
+// keep_error: leave the workspace's error word as it is (the later layers of a
+// stack call, so that a failure of any layer stays visible).
 int run_forward(const void *x_, const void *router_w_, const void *codes_, const void *scales_,
                 const void *shared_w_, int64_t T64, void *y_, const float *bias, void *ws,
-                hipStream_t s, void *const *events, int n_events, float *resid = nullptr, int policy = 0) {
+                hipStream_t s, void *const *events, int n_events, float *resid = nullptr, int policy = 0,
+                bool keep_error = false) {
     const int T = (int)T64;
     const moe_w4_ws_layout L = make_layout(T64);
     const uint16_t *x = static_cast<const uint16_t *>(x_);
@@ -139,6 +150,8 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     const bool fused = T <= kFusedMaxTokens;
     const bool small_route = !grouped && T <= kRouteSmallMaxTokens;
     int *counters = ws_at<int>(ws, L.sync);
+    int *error = ws_at<int>(ws, L.error);
+    int *error_clear = keep_error ? nullptr : error;
 
     int stage = 0;
     auto mark = [&](void) -> int {
@@ -168,7 +181,7 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
         // counters), then the rest of the layer; the other stages are empty
         // the logits are written without the bias; the routing adds it
         MOE_STEP(launch_router_shared_small(x, resid, const_cast<uint16_t *>(x), T, router_w, nullptr, shared_w,
-                                            logits, hs, counters, s));
+                                            logits, hs, counters, error_clear, s));
         MOE_MARK();
         MOE_MARK();
         FusedDecodeArgs fa;
@@ -194,6 +207,9 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
         fa.y = y;
         fa.resid = resid;
         fa.counters = counters;
+        fa.error = error;
+        fa.wait_target_extra = g_wait_extra.load(std::memory_order_relaxed);
+        fa.wait_ticks = g_wait_ticks.load(std::memory_order_relaxed);
         MOE_STEP(launch_decode_fused(fa, s));
         for (int i = 0; i < 4; ++i) MOE_MARK();
         return MOE_W4_OK;
@@ -208,10 +224,10 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     MOE_MARK();
     if (small_route) {
         MOE_STEP(launch_route_small(logits, T, bias, policy, topk_idx, topk_w, offsets, perm, pos, n_active, active,
-                                    chunks, n_chunks, s));
+                                    chunks, n_chunks, error_clear, s));
     } else {
         MOE_STEP(launch_topk_rotate(logits, x, T, bias, policy, topk_idx, topk_w, xt, xt_scale, s));
-        MOE_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, s));
+        MOE_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, error_clear, s));
     }
     MOE_MARK();
     if (grouped) {
@@ -274,6 +290,7 @@ int run_forward_nvfp4(const void *x_, const void *router_w_, const void *codes_,
     float *z = ws_at<float>(ws, L.z);
     int *chunks = ws_at<int>(ws, L.chunks);
     int *n_chunks = ws_at<int>(ws, L.n_chunks);
+    int *error = ws_at<int>(ws, L.error);
     const bool dense = T >= kPrefillMinTokens;
     const bool small_route = T <= kRouteSmallMaxTokens;
 
@@ -305,11 +322,11 @@ int run_forward_nvfp4(const void *x_, const void *router_w_, const void *codes_,
     NV_MARK();
     if (small_route) {
         NV_STEP(launch_route_small(logits, T, bias, 0, topk_idx, topk_w, offsets, perm, pos, n_active, active, chunks,
-                                   n_chunks, s));
+                                   n_chunks, error, s));
     } else {
         // (the rotated x it also writes is not used by NVFP4 experts)
         NV_STEP(launch_topk_rotate(logits, x, T, bias, 0, topk_idx, topk_w, xt, xt_scale, s));
-        NV_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, s));
+        NV_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, error, s));
     }
     NV_MARK();
     NV_STEP(launch_gateup_nvfp4(codes, scales, tscales, x, perm, active, T, act, s));
@@ -340,6 +357,38 @@ uint64_t stream_key(uint64_t seed, int layer, int kind) {
     return host_mix64(seed * 0x9E3779B97F4A7C15ull + (uint64_t)(64 * (int64_t)layer + kind));
 }
 float normal_mult(double sigma) { return (float)(sigma * sqrt(3.0) / 65536.0); }
+
+// One layer of a stack on validated arguments: x_buf = bf16(rmsnorm(resid)),
+// y_buf = layer(x_buf), resid += f32(y_buf).  keep_error: see run_forward.
+int run_stack_layer(float *resid, const void *router_w, const void *codes, const void *scales,
+                    const void *shared_w, int64_t T, void *x_buf, void *y_buf, void *ws, hipStream_t s,
+                    bool keep_error) {
+    (void)hipGetLastError();
+    if (T <= kFusedMaxTokens)   // rmsnorm and residual add inside the two launches
+        return run_forward(x_buf, router_w, codes, scales, shared_w, T, y_buf, nullptr, ws, s, nullptr, 0, resid, 0,
+                           keep_error);
+    launch_rmsnorm_bf16(resid, (int)T, static_cast<uint16_t *>(x_buf), s);
+    int rc = device_status(hipGetLastError());
+    if (rc != MOE_W4_OK) return rc;
+    rc = run_forward(x_buf, router_w, codes, scales, shared_w, T, y_buf, nullptr, ws, s, nullptr, 0, nullptr, 0,
+                     keep_error);
+    if (rc != MOE_W4_OK) return rc;
+    launch_residual_add(resid, static_cast<const uint16_t *>(y_buf), (int)T, s);
+    return device_status(hipGetLastError());
+}
+
+// The stack's workspace: a forward workspace, then one layer's x and y (used
+// when no trace is given).
+struct StackWs {
+    size_t x, y, total;
+};
+StackWs stack_ws_parts(int64_t T) {
+    StackWs P;
+    P.x = make_layout(T).total;
+    P.y = align_up(P.x + (size_t)T * kH * 2);
+    P.total = align_up(P.y + (size_t)T * kH * 2);
+    return P;
+}
 
 }  // namespace
 
@@ -515,17 +564,61 @@ int moe_w4_stack_layer(float *resid, const void *router_w, const void *codes, co
     const size_t rb = (size_t)T * kH * 4, ab = (size_t)T * kH * 2;
     if (overlap(resid, rb, x_buf, ab) || overlap(resid, rb, y_buf, ab) || overlap(resid, rb, workspace, workspace_bytes))
         return MOE_W4_EINVAL;
+    return run_stack_layer(resid, router_w, codes, scales, shared_w, T, x_buf, y_buf, workspace,
+                           static_cast<hipStream_t>(stream), false);
+}
+
+size_t moe_w4_stack_workspace_bytes(int64_t T) {
+    if (!t_in_range(T)) return 0;
+    return stack_ws_parts(T).total;
+}
+
+int moe_w4_stack_forward(float *resid, const moe_w4_layer *layers, int n_layers, int64_t T, void *trace,
+                         void *workspace, size_t workspace_bytes, void *stream) {
+    if (!t_in_range(T) || n_layers < 0 || n_layers > MOE_W4_STACK_MAX_LAYERS) return MOE_W4_EINVAL;
+    if (T == 0 || n_layers == 0) return MOE_W4_OK;
+    if (!layers || !resid || !workspace) return MOE_W4_EINVAL;
+    if (!aligned(resid, MOE_W4_ALIGN) || !aligned(workspace, MOE_W4_ALIGN)) return MOE_W4_EINVAL;
+    if (trace && !aligned(trace, MOE_W4_ALIGN)) return MOE_W4_EINVAL;
+    for (int l = 0; l < n_layers; ++l) {
+        const moe_w4_layer &w = layers[l];
+        const void *ptrs[] = {w.router_w, w.codes, w.scales, w.shared_w};
+        for (const void *p : ptrs)
+            if (!p || !aligned(p, MOE_W4_ALIGN)) return MOE_W4_EINVAL;
+    }
+    const StackWs P = stack_ws_parts(T);
+    if (workspace_bytes < P.total) return MOE_W4_EWORKSPACE;
+    const size_t rb = (size_t)T * kH * 4, ab = (size_t)T * kH * 2, tb = (size_t)n_layers * 2 * ab;
+    if (overlap(resid, rb, workspace, workspace_bytes)) return MOE_W4_EINVAL;
+    if (trace && (overlap(trace, tb, resid, rb) || overlap(trace, tb, workspace, workspace_bytes)))
+        return MOE_W4_EINVAL;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    char *ws = static_cast<char *>(workspace);
+    for (int l = 0; l < n_layers; ++l) {
+        const moe_w4_layer &w = layers[l];
+        void *xb = trace ? static_cast<char *>(trace) + (size_t)(2 * l) * ab : ws + P.x;
+        void *yb = trace ? static_cast<char *>(trace) + (size_t)(2 * l + 1) * ab : ws + P.y;
+        const int rc = run_stack_layer(resid, w.router_w, w.codes, w.scales, w.shared_w, T, xb, yb, ws, s, l > 0);
+        if (rc != MOE_W4_OK) return rc;
+    }
+    return MOE_W4_OK;
+}
+
+int moe_w4_generate_normal_bf16(uint64_t seed, uint32_t tensor_id, int64_t n, double sigma, void *out, void *stream) {
+    if (n < 0 || n > MOE_W4_GENERATE_MAX_ELEMS || !(sigma >= 0.0) || !isfinite(sigma)) return MOE_W4_EINVAL;
+    if (n == 0) return MOE_W4_OK;
+    if (!out || !aligned(out, 2)) return MOE_W4_EINVAL;
     (void)hipGetLastError();
-    if (T <= kFusedMaxTokens)   // rmsnorm and residual add inside the two launches
-        return run_forward(x_buf, router_w, codes, scales, shared_w, T, y_buf, nullptr, workspace, s, nullptr, 0,
-                           resid);
-    launch_rmsnorm_bf16(resid, (int)T, static_cast<uint16_t *>(x_buf), s);
-    if ((rc = device_status(hipGetLastError())) != MOE_W4_OK) return rc;
-    rc = run_forward(x_buf, router_w, codes, scales, shared_w, T, y_buf, nullptr, workspace, s, nullptr, 0);
-    if (rc != MOE_W4_OK) return rc;
-    launch_residual_add(resid, static_cast<const uint16_t *>(y_buf), (int)T, s);
+    const uint64_t key = host_mix64(seed * 0x9E3779B97F4A7C15ull + (uint64_t)tensor_id);
+    launch_gen_normal_bf16(key, n, normal_mult(sigma), 0, static_cast<uint16_t *>(out), static_cast<hipStream_t>(stream));
     return device_status(hipGetLastError());
+}
+
+int moe_w4_set_fused_wait(int64_t max_ticks, int extra_count) {
+    if (max_ticks < 0 || max_ticks > 0xffffffffLL || extra_count < 0) return MOE_W4_EINVAL;
+    g_wait_ticks.store(max_ticks == 0 ? kDefaultWaitTicks : (uint32_t)max_ticks, std::memory_order_relaxed);
+    g_wait_extra.store(extra_count, std::memory_order_relaxed);
+    return MOE_W4_OK;
 }
 
 const char *moe_w4_status_string(int status) {

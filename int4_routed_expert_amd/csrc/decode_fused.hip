@@ -41,8 +41,10 @@
 // on the same channel wait behind them.  Only the down workgroups wait, and
 // only for gate/up workgroups, which have lower indices and never wait, so
 // they were dispatched first and finish whatever else is resident; the wait
-// is also bounded in time, and a down workgroup that gives up writes NaN to
-// its outputs, so a failure cannot hang the device and cannot go unnoticed.
+// is also bounded in time (5 ms by default), and a down workgroup that gives
+// up writes NaN to its outputs (y, and in a stack layer the residual stream,
+// so that every later layer's output is NaN too) and sets the workspace's
+// error word, so a failure cannot hang the device and cannot go unnoticed.
 #include "common.h"
 #include "gemv_ops.h"
 #include "launch.h"
@@ -59,7 +61,6 @@ constexpr int kFuDnWgs = 256;                       // down workgroups
 constexpr int kFuCols = kH / kFuDnWgs;              // 8 output features per down workgroup
 constexpr int kFuPairs = 2;                         // (gate, up) row pairs per wave batch
 constexpr int kFuBatchesPerExpert = kI / kFuPairs;  // 256
-constexpr uint64_t kFuWaitTicks = 500000;           // 5 ms of the 100 MHz s_memrealtime clock
 
 static_assert(kFuWaves == kFuCols, "a down wave owns one feature of the shared projection");
 static_assert(kFuWaves >= kFusedMaxTokens, "one wave per token for the routing");
@@ -119,13 +120,13 @@ __device__ __forceinline__ float4 bf16x4_hi(uint4 q) {
     return make_float4(bf16lo(q.z), bf16hi(q.z), bf16lo(q.w), bf16hi(q.w));
 }
 
-// Poll one replica of a completion counter until it reaches `target` or the
-// time bound passes; returns whether it was reached.
-__device__ __forceinline__ bool wait_count(const int *counter, int target) {
+// Poll one replica of a completion counter until it reaches `target` or
+// `ticks` of the 100 MHz real-time clock pass; returns whether it was reached.
+__device__ __forceinline__ bool wait_count(const int *counter, int target, uint32_t ticks) {
     const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
     for (;;) {
         if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return true;
-        if (__builtin_amdgcn_s_memrealtime() - t_start > kFuWaitTicks) return false;
+        if (__builtin_amdgcn_s_memrealtime() - t_start > ticks) return false;
         __builtin_amdgcn_s_sleep(8);
     }
 }
@@ -182,7 +183,8 @@ __device__ __forceinline__ float row_dot_tokens(const uint4 (&w)[4], const uint4
 // stack layer (RESID) it is computed there from the fp32 residual stream as
 // bf16(resid / sqrt(mean(resid^2) + 1e-6)) (wave t: token t; every
 // workgroup sums in the same order, so all agree bit for bit) and workgroup 0
-// writes it out.  Workgroup 0 also clears the counters of the second launch.
+// writes it out.  Workgroup 0 also clears the counters of the second launch
+// and, if `error` is not null, the error word.
 // ---------------------------------------------------------------------------
 constexpr int kRouterWgs = kE / 8;
 constexpr int kSharedWgs = kIS / 4;
@@ -195,11 +197,12 @@ __global__ __launch_bounds__(512) void k_router_shared_small(const uint16_t *__r
                                                              const float *__restrict__ bias,
                                                              const uint16_t *__restrict__ shared_gu,
                                                              float *__restrict__ logits, uint16_t *__restrict__ hs,
-                                                             int *__restrict__ counters) {
+                                                             int *__restrict__ counters, int *__restrict__ error) {
     __shared__ uint4 xl[T][kH / 8];
     __shared__ float part[8][8];   // shared role: [wave][token]
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
     if (blockIdx.x == 0 && tid < kFusedCounters) counters[tid * kFusedCounterStride] = 0;
+    if (blockIdx.x == 0 && tid == kFusedCounters && error) *error = 0;
     // this wave's weight row (router row e, or gate (waves 0-3) / up (4-7) row
     // c0 + (wave & 3) of the shared expert), requested before x is staged
     const bool router = (int)blockIdx.x < kRouterWgs;
@@ -513,10 +516,17 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
     }
 
     // wait until every gate/up workgroup is done (bounded)
-    if (tid == 0) U.dn.fail = !wait_count(A.counters + replica, kFuGuWgs);
+    if (tid == 0) U.dn.fail = !wait_count(A.counters + replica, kFuGuWgs + A.wait_target_extra, A.wait_ticks);
     __syncthreads();
     if (U.dn.fail) {
-        if (tid < T * kFuCols) A.y[(size_t)(tid / kFuCols) * kH + c0 + tid % kFuCols] = 0x7fc0;   // NaN
+        // NaN outputs for this workgroup's features (and in the residual
+        // stream of a stack layer), and the error word
+        if (tid < T * kFuCols) {
+            const size_t i = (size_t)(tid / kFuCols) * kH + c0 + tid % kFuCols;
+            A.y[i] = 0x7fc0;
+            if (A.resid) A.resid[i] = __builtin_nanf("");
+        }
+        if (tid == 0) __hip_atomic_store(A.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
 
@@ -611,13 +621,13 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
 
 void launch_router_shared_small(const uint16_t *x, const float *resid, uint16_t *x_out, int T,
                                 const uint16_t *router_w, const float *bias, const uint16_t *shared_w, float *logits,
-                                uint16_t *hs, int *counters, hipStream_t s) {
+                                uint16_t *hs, int *counters, int *error, hipStream_t s) {
     if (resid) {
         MOE_FUSED_DISPATCH2(k_router_shared_small, true, dim3(kRouterWgs + kSharedWgs), dim3(512), 0, s, x, resid, x_out,
-                            router_w, bias, shared_w, logits, hs, counters)
+                            router_w, bias, shared_w, logits, hs, counters, error)
     } else {
         MOE_FUSED_DISPATCH2(k_router_shared_small, false, dim3(kRouterWgs + kSharedWgs), dim3(512), 0, s, x, resid, x_out,
-                            router_w, bias, shared_w, logits, hs, counters)
+                            router_w, bias, shared_w, logits, hs, counters, error)
     }
 }
 

@@ -116,8 +116,11 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
 
     // staging: per step each thread moves 16-byte chunks c = tid + 256 i of A
     // and of B (row c / 8, position c % 8 holding group (c % 8) ^ ((row >> 1) & 7));
-    // raw buffer loads keep their program order, two steps ahead
-    const __amdgpu_buffer_rsrc_t ares = make_buf(A, 0xffffffffu);
+    // raw buffer loads keep their program order, two steps ahead.  The A
+    // descriptor starts at the tile's first row, so its 32-bit offsets stay
+    // below 128 rows (1.5 MiB at K = 6144) whatever M is; B offsets are below
+    // the weight matrix's size (at most 6144 rows of K = 6144)
+    const __amdgpu_buffer_rsrc_t ares = make_buf(A + (size_t)m0 * K, 0xffffffffu);
     const __amdgpu_buffer_rsrc_t bres = make_buf(J.B, 0xffffffffu);
     uint32_t aoff[kStageLoads], boff[kStageLoads];
     int ldst[kStageLoads];
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
     for (int i = 0; i < kStageLoads; ++i) {
         const int c = tid + 256 * i, r = c / kChunksPerRow, pos = c % kChunksPerRow;
         const int grp = pos ^ ((r >> 1) & 7);
-        aoff[i] = (uint32_t)min(m0 + r, M - 1) * (K * 2) + grp * 16;
+        aoff[i] = (uint32_t)(min(m0 + r, M - 1) - m0) * (K * 2) + grp * 16;
         boff[i] = (uint32_t)b_row(r) * (K * 2) + grp * 16;
         ldst[i] = r * kRowBytes + pos * 16;
     }

@@ -45,12 +45,19 @@ struct FusedDecodeArgs {
     uint16_t *y;
     float *resid;                  // stack layer: resid += y (else null)
     int *counters;                 // 4096 bytes; zero at launch (the first launch clears them)
+    int *error;                    // set to 1 by a down workgroup whose wait gave up
+    int wait_target_extra;         // added to the count the wait needs (0; > 0 only to test the failure path)
+    uint32_t wait_ticks;           // bound of the wait, in ticks of the 100 MHz real-time clock
 };
+// The wait bound and the extra count of the fused launch (process-wide;
+// moe_w4_set_fused_wait in the ABI).
+void fused_wait_params(uint32_t &ticks, int &extra);
 // With resid (a stack layer), x is computed as bf16(rmsnorm(resid)) and also
 // written to x_out, and the second launch adds y to resid.
+// error: the workspace's error word, cleared by this launch when non-null.
 void launch_router_shared_small(const uint16_t *x, const float *resid, uint16_t *x_out, int T,
                                 const uint16_t *router_w, const float *bias, const uint16_t *shared_w, float *logits,
-                                uint16_t *hs, int *counters, hipStream_t s);
+                                uint16_t *hs, int *counters, int *error, hipStream_t s);
 void launch_decode_fused(const FusedDecodeArgs &args, hipStream_t s);
 
 // Per token: top-6 of the logits (+ bias, if any), the sigmoid weights
@@ -64,15 +71,16 @@ void launch_topk_rotate(const float *logits, const uint16_t *x, int T, const flo
 // token, second token, 0, 0, 0}, one per expert with tokens, then expert -1.
 // chunks: int[max_chunks(T)][4] records {expert, first sorted position, rows
 // (<= 96), 0} covering every expert's assignments; *n_chunks of them.
+// error (or null): the workspace's error word, cleared (this sequence cannot fail).
 void launch_sort(const int *topk_idx, int T, int *offsets, int *perm, int *pos, int *n_active,
-                 int *slots, int *chunks, int *n_chunks, hipStream_t s);
+                 int *slots, int *chunks, int *n_chunks, int *error, hipStream_t s);
 // Top-6 and the stable sort in one workgroup (16 waves, one token per wave at
 // a time; the sort ranks the <= 288 assignments in LDS), for up to
 // kRouteSmallMaxTokens tokens whose rotated x is written elsewhere.
 constexpr int kRouteSmallMaxTokens = 48;
 void launch_route_small(const float *logits, int T, const float *bias, int policy, int *topk_idx, float *topk_w,
                         int *offsets, int *perm, int *pos, int *n_active, int *slots, int *chunks, int *n_chunks,
-                        hipStream_t s);
+                        int *error, hipStream_t s);
 
 // Routed experts, GEMV form (few tokens per expert), driven by the slot records.
 void launch_gateup_gemv(const uint8_t *codes, const uint16_t *scales, const uint32_t *xt,

@@ -67,7 +67,7 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
                                                int *__restrict__ offsets, int *__restrict__ perm,
                                                int *__restrict__ pos, int *__restrict__ n_active,
                                                int *__restrict__ slots, int4 *__restrict__ chunks,
-                                               int *__restrict__ n_chunks) {
+                                               int *__restrict__ n_chunks, int *__restrict__ error) {
     __shared__ int cnt[kSortWaves][kE];
     __shared__ int tot[kE];
     __shared__ int offs[kE + 1];
@@ -80,6 +80,7 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
     const int a0 = wave * per, a1 = min(a0 + per, N);
 
     for (int i = tid; i < kSortWaves * kE; i += blockDim.x) (&cnt[0][0])[i] = 0;
+    if (tid == 0 && error) *error = 0;   // this launch sequence cannot fail on the device
     // up to kSortKeep chunks of 64 per wave (6 * T <= 16384) are loaded once,
     // all in flight together, and stay in registers for the ranking pass
     const bool keep = per <= 64 * kSortKeep;
@@ -241,7 +242,8 @@ __global__ __launch_bounds__(1024) void k_route_small(const float *__restrict__ 
                                                       int *__restrict__ offsets, int *__restrict__ perm,
                                                       int *__restrict__ pos, int *__restrict__ n_active,
                                                       int *__restrict__ slots, int4 *__restrict__ chunks,
-                                                      int *__restrict__ n_chunks, RouterPolicy rp) {
+                                                      int *__restrict__ n_chunks, int *__restrict__ error,
+                                                      RouterPolicy rp) {
     constexpr int kPerWave = (kRouteSmallMaxTokens + kSortWaves - 1) / kSortWaves;
     constexpr int kMaxChunks = (kTopK * kRouteSmallMaxTokens + 63) / 64;
     __shared__ int sel[kTopK * kRouteSmallMaxTokens];     // expert of assignment a
@@ -255,6 +257,7 @@ __global__ __launch_bounds__(1024) void k_route_small(const float *__restrict__ 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int N = kTopK * T;
     for (int i = tid; i < kMaxChunks * kE; i += blockDim.x) (&cnt[0][0])[i] = 0;
+    if (tid == 0 && error) *error = 0;   // this launch sequence cannot fail on the device
 
     float4 lv[kPerWave];
 #pragma unroll
@@ -377,15 +380,15 @@ __global__ __launch_bounds__(1024) void k_route_small(const float *__restrict__ 
 
 void launch_route_small(const float *logits, int T, const float *bias, int policy, int *topk_idx, float *topk_w,
                         int *offsets, int *perm, int *pos, int *n_active, int *slots, int *chunks, int *n_chunks,
-                        hipStream_t s) {
+                        int *error, hipStream_t s) {
     hipLaunchKernelGGL(k_route_small, dim3(1), dim3(1024), 0, s, logits, T, topk_idx, topk_w, offsets, perm, pos,
-                       n_active, slots, reinterpret_cast<int4 *>(chunks), n_chunks, RouterPolicy{bias, policy});
+                       n_active, slots, reinterpret_cast<int4 *>(chunks), n_chunks, error, RouterPolicy{bias, policy});
 }
 
 void launch_sort(const int *topk_idx, int T, int *offsets, int *perm, int *pos, int *n_active,
-                 int *slots, int *chunks, int *n_chunks, hipStream_t s) {
+                 int *slots, int *chunks, int *n_chunks, int *error, hipStream_t s) {
     hipLaunchKernelGGL(k_sort, dim3(1), dim3(1024), 0, s, topk_idx, T, offsets, perm, pos, n_active,
-                       slots, reinterpret_cast<int4 *>(chunks), n_chunks);
+                       slots, reinterpret_cast<int4 *>(chunks), n_chunks, error);
 }
 
 }  // namespace moe_w4

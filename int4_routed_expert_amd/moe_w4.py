@@ -24,8 +24,10 @@ GROUP = 128
 CODE_BYTES_PER_EXPERT = 1572864
 SCALES_PER_EXPERT = 24576
 SHARED_ELEMS = 6291456
-MAX_TOKENS = 1048576
+MAX_TOKENS = 65536
 FUSED_MAX_TOKENS = 8
+STACK_MAX_LAYERS = 1024
+GENERATE_MAX_ELEMS = 1 << 40
 # router policy flags of moe_w4_forward_policy (include/moe_w4.h)
 ROUTER_NORM_FLOOR, ROUTER_NORM_SUM, ROUTER_NORM_NONE, ROUTER_NORM_MASK = 0, 1, 2, 3
 ROUTER_BIAS_SELECT_ONLY = 4
@@ -48,10 +50,15 @@ class MoeW4Error(RuntimeError):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "logits", "topk_idx", "topk_w", "offsets", "perm", "pos", "n_active", "active",
-        "xt", "xt_scale", "act", "at", "at_scale", "hs", "o", "z", "chunks", "n_chunks", "sync", "total")]
+        "xt", "xt_scale", "act", "at", "at_scale", "hs", "o", "z", "chunks", "n_chunks", "sync", "error", "total")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
+
+
+class Layer(ctypes.Structure):
+    """moe_w4_layer: the device pointers of one layer's weights."""
+    _fields_ = [(n, ctypes.c_void_p) for n in ("router_w", "codes", "scales", "shared_w")]
 
 
 if not os.path.exists(LIB_PATH):
@@ -77,6 +84,10 @@ _sig = {
     "moe_w4_generate_layer": (_int, [_u64, _int, _vp, _vp, _vp, _vp, _vp]),
     "moe_w4_generate_x": (_int, [_u64, _int, _i64, _vp, _vp]),
     "moe_w4_stack_layer": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
+    "moe_w4_stack_workspace_bytes": (_sz, [_i64]),
+    "moe_w4_stack_forward": (_int, [_vp, ctypes.POINTER(Layer), _int, _i64, _vp, _vp, _sz, _vp]),
+    "moe_w4_generate_normal_bf16": (_int, [_u64, ctypes.c_uint32, _i64, ctypes.c_double, _vp, _vp]),
+    "moe_w4_set_fused_wait": (_int, [_i64, _int]),
     "moe_w4_status_string": (ctypes.c_char_p, [_int]),
     "moe_w4_last_device_error": (_int, []),
     "moe_w4_version": (_int, []),
@@ -235,6 +246,41 @@ def moe_w4_stack_layer(resid, router_w, codes, scales, shared_w, x_buf, y_buf, w
            "moe_w4_stack_layer")
 
 
+def moe_w4_stack_workspace_bytes(T: int) -> int:
+    return _lib.moe_w4_stack_workspace_bytes(T)
+
+
+def stack_layers(layers):
+    """A ctypes array of moe_w4_layer from dicts of device tensors (router_w, codes, scales, shared_w)."""
+    arr = (Layer * len(layers))()
+    for i, w in enumerate(layers):
+        arr[i] = Layer(_ptr(w["router_w"]), _ptr(w["codes"]), _ptr(w["scales"]), _ptr(w["shared_w"]))
+    return arr
+
+
+def moe_w4_stack_forward(resid, layers, workspace, trace=None, stream=None):
+    """resid <- the stack of `layers` applied to resid (fp32 [T][2048]).  layers: a
+    stack_layers() array (or a list of weight dicts); trace: None or bf16 device
+    memory [n_layers][2][T][2048] that receives every layer's input and output."""
+    arr = layers if isinstance(layers, ctypes.Array) else stack_layers(layers)
+    _check(_lib.moe_w4_stack_forward(_ptr(resid), arr, len(arr), resid.shape[0], _ptr(trace), _ptr(workspace),
+                                     workspace.numel() * workspace.element_size(), _stream(stream)),
+           "moe_w4_stack_forward")
+
+
+def moe_w4_generate_normal_bf16(seed, tensor_id, out, sigma, n=None, stream=None):
+    """out[:n] <- seeded bf16 "normals" of standard deviation sigma (the scheme of the layer's inputs)."""
+    n = out.numel() if n is None else n
+    _check(_lib.moe_w4_generate_normal_bf16(seed, tensor_id, n, float(sigma), _ptr(out), _stream(stream)),
+           "moe_w4_generate_normal_bf16")
+
+
+def moe_w4_set_fused_wait(max_ticks: int = 0, extra_count: int = 0):
+    """Diagnostic: bound (ticks of the 100 MHz clock; 0 = default 5 ms) and extra count of the
+    two-launch form's wait; extra_count > 0 makes every such wait give up (tests of the failure path)."""
+    _check(_lib.moe_w4_set_fused_wait(max_ticks, extra_count), "moe_w4_set_fused_wait")
+
+
 # ---------------------------------------------------------------- allocation helpers
 def empty_layer(device="cuda"):
     """Uninitialised device tensors of one layer in the library layout (as raw integer dtypes)."""
@@ -254,6 +300,10 @@ def generated_layer(seed, layer=0, device="cuda"):
 
 def workspace(T, device="cuda"):
     return torch.empty((max(moe_w4_workspace_bytes(T), 1),), dtype=torch.uint8, device=device)
+
+
+def stack_workspace(T, device="cuda"):
+    return torch.empty((max(moe_w4_stack_workspace_bytes(T), 1),), dtype=torch.uint8, device=device)
 
 
 def ws_view(ws, T, name, dtype, count):

@@ -195,3 +195,75 @@ def test_status_strings(m):
     assert m.moe_w4_profile_points() == len([m.moe_w4_profile_point_name(i) for i in range(m.moe_w4_profile_points())])
     assert m.moe_w4_profile_point_name(0) == "start"
     assert m.moe_w4_profile_point_name(99) is None
+
+
+def layer_array(m, n, base=0x10000000, bad=None):
+    arr = (m.Layer * n)()
+    for i in range(n):
+        arr[i] = m.Layer(base + 0x100000 * i, base + 0x100000 * i + 0x10000, base + 0x100000 * i + 0x20000,
+                         base + 0x100000 * i + 0x30000)
+    if bad is not None:
+        i, field, value = bad
+        setattr(arr[i], field, value)
+    return arr
+
+
+def test_stack_forward_validation(m):
+    lib = m._lib
+    T = 8
+    resid, trace, ws = 0x40000000, 0x50000000, 0x60000000
+    nb = m.moe_w4_stack_workspace_bytes(T)
+    # a forward workspace plus one layer's bf16 x and y
+    assert nb >= m.moe_w4_workspace_bytes(T) + 2 * T * 2048 * 2
+    assert m.moe_w4_stack_workspace_bytes(-1) == 0
+    assert m.moe_w4_stack_workspace_bytes(m.MAX_TOKENS + 1) == 0
+    arr = layer_array(m, 3)
+    f = lib.moe_w4_stack_forward
+    assert f(resid, arr, 0, T, None, ws, nb, None) == m.OK                # no layers: nothing enqueued
+    assert f(resid, arr, 3, 0, None, ws, nb, None) == m.OK                # no tokens
+    assert f(resid, arr, -1, T, None, ws, nb, None) == m.EINVAL
+    assert f(resid, arr, m.STACK_MAX_LAYERS + 1, T, None, ws, nb, None) == m.EINVAL
+    assert f(resid, arr, 3, -1, None, ws, nb, None) == m.EINVAL
+    assert f(resid, arr, 3, m.MAX_TOKENS + 1, None, ws, nb, None) == m.EINVAL
+    assert f(None, arr, 3, T, None, ws, nb, None) == m.EINVAL
+    assert f(resid, None, 3, T, None, ws, nb, None) == m.EINVAL
+    assert f(resid, arr, 3, T, None, None, nb, None) == m.EINVAL
+    assert f(resid + 4, arr, 3, T, None, ws, nb, None) == m.EINVAL        # misaligned
+    assert f(resid, arr, 3, T, trace + 8, ws, nb, None) == m.EINVAL
+    for field in ("router_w", "codes", "scales", "shared_w"):
+        assert f(resid, layer_array(m, 3, bad=(2, field, None)), 3, T, None, ws, nb, None) == m.EINVAL, field
+        assert f(resid, layer_array(m, 3, bad=(1, field, 0x7000008)), 3, T, None, ws, nb, None) == m.EINVAL, field
+    assert f(resid, arr, 3, T, None, ws, nb - 1, None) == m.EWORKSPACE
+    assert f(ws + 256, arr, 3, T, None, ws, nb, None) == m.EINVAL         # resid inside the workspace
+    assert f(resid, arr, 3, T, resid + 4096, ws, nb, None) == m.EINVAL     # trace overlaps resid
+    assert f(resid, arr, 3, T, ws - 4096, ws, nb, None) == m.EINVAL        # trace runs into the workspace
+    assert m.moe_w4_last_device_error() == 0
+
+
+def test_generate_normal_validation(m):
+    lib = m._lib
+    g = lib.moe_w4_generate_normal_bf16
+    assert g(0, 1, 0, 1.0, None, None) == m.OK                            # n == 0: nothing enqueued
+    assert g(0, 1, -1, 1.0, 0x1000, None) == m.EINVAL
+    assert g(0, 1, m.GENERATE_MAX_ELEMS + 1, 1.0, 0x1000, None) == m.EINVAL
+    assert g(0, 1, 16, -0.5, 0x1000, None) == m.EINVAL
+    assert g(0, 1, 16, float("nan"), 0x1000, None) == m.EINVAL
+    assert g(0, 1, 16, float("inf"), 0x1000, None) == m.EINVAL
+    assert g(0, 1, 16, 1.0, None, None) == m.EINVAL
+    assert g(0, 1, 16, 1.0, 0x1001, None) == m.EINVAL                     # bf16 needs 2-byte alignment
+    assert m.moe_w4_last_device_error() == 0
+
+
+def test_fused_wait_setting(m):
+    lib = m._lib
+    assert lib.moe_w4_set_fused_wait(-1, 0) == m.EINVAL
+    assert lib.moe_w4_set_fused_wait(1 << 32, 0) == m.EINVAL
+    assert lib.moe_w4_set_fused_wait(1000, -1) == m.EINVAL
+    assert lib.moe_w4_set_fused_wait(1000, 1) == m.OK
+    assert lib.moe_w4_set_fused_wait(0, 0) == m.OK                        # back to the defaults
+
+
+def test_workspace_error_word(m):
+    for T in (1, 8, 9, 128):
+        lay = m.moe_w4_workspace_layout(T)
+        assert lay["sync"] + 4096 <= lay["error"] and lay["error"] + 4 <= lay["total"]

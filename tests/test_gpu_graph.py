@@ -40,3 +40,29 @@ def test_graph_replay_matches_eager(m, T):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(y, y_eager), f"replay {rep} differs"
+
+
+@pytest.mark.parametrize("T", [1, 9])
+def test_stack_graph_replay_matches_eager(m, T):
+    """moe_w4_stack_forward (3 layers) captured once and replayed: every replay
+    reproduces the eager residual bit for bit."""
+    layers = [m.generated_layer(4, l) for l in range(3)]
+    x0 = torch.empty((T, 2048), dtype=torch.int16, device="cuda")
+    m.moe_w4_generate_x(4, 0, x0)
+    resid0 = x0.view(torch.bfloat16).float().contiguous()
+    ws = m.stack_workspace(T)
+    arr = m.stack_layers(layers)
+    resid = resid0.clone()
+    m.moe_w4_stack_forward(resid, arr, ws)
+    torch.cuda.synchronize()
+    eager = resid.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        m.moe_w4_stack_forward(resid, arr, ws)
+    for rep in range(4):
+        resid.copy_(resid0)
+        ws.fill_(0x5A)                      # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(resid, eager), f"replay {rep} differs"
