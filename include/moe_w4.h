@@ -150,6 +150,21 @@ int moe_w4_forward(const void *x, const void *router_w, const void *codes, const
                    const void *shared_w, int64_t T, void *y, const float *router_bias,
                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* moe_w4_forward for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * no workspace argument; the workspace is a file-scope device array of the
+ * library (11 MiB, one copy per GPU the library runs on, kept until the
+ * process ends), located on the first call on each device.  The call itself
+ * allocates nothing and calls no allocating routine.  Every call on a GPU
+ * shares that GPU's array: calls that overlap on one GPU (on different
+ * streams, or from different threads) race and must not be made; routing
+ * results are not exposed.  T up to MOE_W4_STATIC_MAX_TOKENS; a larger T
+ * returns MOE_W4_EWORKSPACE with nothing enqueued.  Otherwise arguments,
+ * results and errors as moe_w4_forward. */
+#define MOE_W4_STATIC_MAX_TOKENS 128
+int moe_w4_forward_static(const void *x, const void *router_w, const void *codes, const void *scales,
+                          const void *shared_w, int64_t T, void *y, const float *router_bias, void *stream);
+
 /* moe_w4_forward with a router policy (MOE_W4_ROUTER_* above): the choice
  * is always the 6 largest of (logit + bias); router_policy selects the
  * normalisation of the sigmoid scores and whether the sigmoid sees the bias.

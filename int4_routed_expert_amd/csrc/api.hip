@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "common.h"
 #include "launch.h"
@@ -390,6 +391,45 @@ StackWs stack_ws_parts(int64_t T) {
     return P;
 }
 
+// ---------------------------------------------------------------------------
+// The forward without allocation (moe_w4_forward_static): its workspace is
+// this file-scope device array, one copy per GPU, held until the process
+// ends.  The array's name in host code is only a handle for the runtime; the
+// device address of each GPU's copy comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address reaches
+// the kernels.  Every call on a GPU shares its copy: nothing in it needs to
+// be initialised (each call writes what it reads, and clears its own
+// counters), but calls that overlap on one GPU race on it.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = 11u << 20;   // the workspace of MOE_W4_STATIC_MAX_TOKENS tokens fits
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The device address of the current GPU's copy of `scratch`.
+int static_scratch(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_status(e);
+    if (dev < 0 || dev >= kMaxDevices) return device_status(hipErrorInvalidDevice);
+    void *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!p) {
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess) return device_status(e);
+            if (!p || make_layout(MOE_W4_STATIC_MAX_TOKENS).total > kStaticScratchBytes)
+                return device_status(hipErrorInvalidSymbol);
+            g_scratch_ptr[dev].store(p, std::memory_order_release);
+        }
+    }
+    *out = p;
+    return MOE_W4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -421,6 +461,20 @@ int moe_w4_forward_policy(const void *x, const void *router_w, const void *codes
     if (rc != MOE_W4_OK || T == 0) return rc;
     return run_forward(x, router_w, codes, scales, shared_w, T, y, router_bias, workspace,
                        static_cast<hipStream_t>(stream), nullptr, 0, nullptr, router_policy);
+}
+
+int moe_w4_forward_static(const void *x, const void *router_w, const void *codes, const void *scales,
+                          const void *shared_w, int64_t T, void *y, const float *router_bias, void *stream) {
+    if (!t_in_range(T)) return MOE_W4_EINVAL;
+    if (T > MOE_W4_STATIC_MAX_TOKENS) return MOE_W4_EWORKSPACE;
+    if (T == 0) return MOE_W4_OK;
+    void *ws = nullptr;
+    int rc = static_scratch(&ws);
+    if (rc != MOE_W4_OK) return rc;
+    rc = validate_forward(x, router_w, codes, scales, shared_w, T, y, router_bias, ws, kStaticScratchBytes);
+    if (rc != MOE_W4_OK) return rc;
+    return run_forward(x, router_w, codes, scales, shared_w, T, y, router_bias, ws, static_cast<hipStream_t>(stream),
+                       nullptr, 0);
 }
 
 int moe_w4_profile_points(void) { return kStages + 1; }

@@ -27,6 +27,7 @@ SHARED_ELEMS = 6291456
 MAX_TOKENS = 65536
 FUSED_MAX_TOKENS = 8
 STACK_MAX_LAYERS = 1024
+STATIC_MAX_TOKENS = 128
 GENERATE_MAX_ELEMS = 1 << 40
 # router policy flags of moe_w4_forward_policy (include/moe_w4.h)
 ROUTER_NORM_FLOOR, ROUTER_NORM_SUM, ROUTER_NORM_NONE, ROUTER_NORM_MASK = 0, 1, 2, 3
@@ -71,6 +72,7 @@ _sig = {
     "moe_w4_workspace_layout": (_int, [_i64, ctypes.POINTER(WsLayout)]),
     "moe_w4_forward": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp]),
     "moe_w4_forward_policy": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _int, _vp, _sz, _vp]),
+    "moe_w4_forward_static": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp]),
     "moe_w4_profile_points": (_int, []),
     "moe_w4_profile_point_name": (ctypes.c_char_p, [_int]),
     "moe_w4_forward_profiled": (_int, [_vp, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp,
@@ -154,6 +156,15 @@ def moe_w4_forward(x, router_w, codes, scales, shared_w, y, workspace, router_bi
                              _ptr(y), _ptr(router_bias), _ptr(workspace),
                              workspace.numel() * workspace.element_size(), _stream(stream))
     _check(st, "moe_w4_forward")
+    return st
+
+
+def moe_w4_forward_static(x, router_w, codes, scales, shared_w, y, router_bias=None, stream=None, T=None) -> int:
+    """moe_w4_forward on the library's own per-GPU device array (no workspace, no allocation)."""
+    T = x.shape[0] if T is None else T
+    st = _lib.moe_w4_forward_static(_ptr(x), _ptr(router_w), _ptr(codes), _ptr(scales), _ptr(shared_w), T,
+                                    _ptr(y), _ptr(router_bias), _stream(stream))
+    _check(st, "moe_w4_forward_static")
     return st
 
 
