@@ -81,7 +81,7 @@ FUSED_MAX_TOKENS = 8
 ROUTE_SMALL_MAX_TOKENS = 48
 GROUPED_MIN_TOKENS = 128
 STAGE_KERNELS_FUSED = {
-    "router_shared_gateup": ("k_router_shared_small", ["decode_fused.hip", "gemv_ops.h", "token_ops.h"]),
+    "router_shared_gateup": ("k_router_small", ["decode_fused.hip", "gemv_ops.h", "token_ops.h"]),
     "routed_gateup": ("k_decode_fused", ["decode_fused.hip", "gemv_ops.h", "token_ops.h"]),
 }
 STAGE_KERNELS_GEMV = {
@@ -119,7 +119,8 @@ def stage_kernels(T, workload=""):
     if T >= GROUPED_MIN_TOKENS:
         return STAGE_KERNELS_GROUPED
     if T <= ROUTE_SMALL_MAX_TOKENS:
-        return dict(STAGE_KERNELS_GEMV, topk_sort=("k_route_small", ["router.hip", "token_ops.h"]))
+        # the router (+ rotation of x), then the shared gate/up beside the routing
+        return dict(STAGE_KERNELS_GEMV, topk_sort=("k_skinny", ["skinny_mfma.hip", "route_small.h", "token_ops.h"]))
     return STAGE_KERNELS_GEMV
 
 
@@ -605,11 +606,17 @@ def bench_layer(a, name, steps, warmup, with_cpu):
         "routed_down": n_touched * EXPERT_D_BYTES + T * 6 * 512 * 4 + T * 6 * 2048 * 4,
         "shared_down_combine": 1024 * 2048 * 2 + T * 1024 * 2 + T * 6 * 2048 * 4 + act,
     }
+    if FUSED_MAX_TOKENS < T <= ROUTE_SMALL_MAX_TOKENS:
+        # the router and the rotated x, then the shared gate/up beside the routing
+        stage_bytes["router_shared_gateup"] = ROUTER_BYTES + act + T * 256 * 4 + act
+        stage_bytes["topk_sort"] = 2 * 1024 * 2048 * 2 + act + T * 1024 * 2 + T * 256 * 4 + T * 6 * 4 * 4
     if T <= FUSED_MAX_TOKENS:
-        # one launch after the router runs the rest of the layer (its time is
-        # recorded under routed_gateup; the later stages are empty)
-        stage_bytes["routed_gateup"] = (n_touched * EXPERT_BYTES + 1024 * 2048 * 2 + T * 256 * 4 + act
-                                        + T * 1024 * 2 + act)
+        # the first launch is the router alone; the second runs the rest of the
+        # layer, the shared expert included (its time is recorded under
+        # routed_gateup; the later stages are empty)
+        stage_bytes["router_shared_gateup"] = ROUTER_BYTES + act + T * 256 * 4
+        stage_bytes["routed_gateup"] = (n_touched * EXPERT_BYTES + SHARED_BYTES + T * 256 * 4 + act
+                                        + 2 * T * 1024 * 2 + act)
     dom_bytes = stage_bytes.get(dom, 0.0)
     achieved = dom_bytes / (stage[dom] * 1e-3) / 1e9
     # from 128 tokens on the routed experts and the shared expert run as MFMA

@@ -75,11 +75,11 @@ extern "C" {
  * assignments, is 3.2 GB at this T), and the GPU tests run this size. */
 #define MOE_W4_MAX_TOKENS 65536
 #define MOE_W4_ALIGN 16
-/* From 1 to this many tokens a forward call is two launches (router + shared
- * gate/up, then the rest of the layer in one launch whose workgroups hand the
- * routed gate/up results to the down projection through device-scope counters
- * in the workspace's `sync` region, cleared by the first launch); from
- * MOE_W4_FUSED_MAX_TOKENS + 1 tokens on, one launch per step. */
+/* From 1 to this many tokens a forward call is two launches (the router, then
+ * the rest of the layer in one launch whose workgroups hand the routed gate/up
+ * results and the shared expert's activations to the down projection through
+ * device-scope counters in the workspace's `sync` region, cleared by the first
+ * launch); from MOE_W4_FUSED_MAX_TOKENS + 1 tokens on, one launch per step. */
 #define MOE_W4_FUSED_MAX_TOKENS 8
 /* Most layers in one moe_w4_stack_forward call. */
 #define MOE_W4_STACK_MAX_LAYERS 1024
@@ -121,16 +121,17 @@ extern "C" {
  *                         positions in order, ascending by expert; n_chunks i32 [1]
  *                         holds n.  (Written at every T; read only on that path.)
  *   logits    f32 [T][256] router logits R x, without the bias
- *   sync      4096 bytes of counters for the fused decode launch; their
+ *   sync      8192 bytes of counters for the fused decode launch; their
  *             contents on entry do not matter (the call clears them itself).
  *   error     i32 [1]: 0 after a call that completed normally; 1 if a down
  *             workgroup of the two-launch form (1-8 tokens) gave up its
  *             bounded wait for the gate/up results (its outputs are then NaN;
  *             see moe_w4_set_fused_wait).  A stack call keeps a failure of any
- *             of its layers. */
+ *             of its layers.
+ *   hist      scratch of the sort at prefill sizes (per-workgroup histograms). */
 typedef struct moe_w4_ws_layout {
     size_t logits, topk_idx, topk_w, offsets, perm, pos, n_active, active;
-    size_t xt, xt_scale, act, at, at_scale, hs, o, z, chunks, n_chunks, sync, error;
+    size_t xt, xt_scale, act, at, at_scale, hs, o, z, chunks, n_chunks, sync, error, hist;
     size_t total;
 } moe_w4_ws_layout;
 

@@ -65,8 +65,9 @@ moe_w4_ws_layout make_layout(int64_t T) {
     L.z = take(4 * kH * t);
     L.chunks = take(16 * (size_t)max_chunks((int)T));
     L.n_chunks = take(4);
-    L.sync = take(4096);
+    L.sync = take(kFusedSyncBytes);
     L.error = take(4);
+    L.hist = take(4 * (size_t)kE * sort_hist_blocks((int)T));
     L.total = off;
     return L;
 }
@@ -178,11 +179,11 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     (void)hipGetLastError();   // clear a stale error so it is not blamed on this call
     MOE_MARK();
     if (fused) {
-        // two launches: router logits and shared h (which also clear the
-        // counters), then the rest of the layer; the other stages are empty
-        // the logits are written without the bias; the routing adds it
-        MOE_STEP(launch_router_shared_small(x, resid, const_cast<uint16_t *>(x), T, router_w, nullptr, shared_w,
-                                            logits, hs, counters, error_clear, s));
+        // two launches: the router logits (which also clear the counters),
+        // then the rest of the layer; the other stages are empty.  The logits
+        // are written without the bias; the routing adds it
+        MOE_STEP(launch_router_small(x, resid, const_cast<uint16_t *>(x), T, router_w, nullptr, logits, counters,
+                                     error_clear, s));
         MOE_MARK();
         MOE_MARK();
         FusedDecodeArgs fa;
@@ -192,6 +193,7 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
         fa.router_policy = policy;
         fa.codes = codes;
         fa.scales = scales;
+        fa.shared_gu = shared_w;
         fa.shared_down = shared_w + 2 * kSharedGateElems;
         fa.hs = hs;
         fa.T = T;
@@ -208,6 +210,7 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
         fa.y = y;
         fa.resid = resid;
         fa.counters = counters;
+        fa.counters_h = counters + kFusedCounters * kFusedCounterStride;
         fa.error = error;
         fa.wait_target_extra = g_wait_extra.load(std::memory_order_relaxed);
         fa.wait_ticks = g_wait_ticks.load(std::memory_order_relaxed);
@@ -217,18 +220,26 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     }
     if (grouped)
         MOE_STEP(launch_router_and_shared_gateup_dense(x, T, router_w, nullptr, logits, shared_w, hs, s));
+    else if (small_route)
+        // up to kRouteSmallMaxTokens tokens: the router and the rotation of x
+        // first; the shared gate/up streams in the next launch beside the
+        // routing (one workgroup), which the routed experts wait for
+        MOE_STEP(launch_router_rotate(x, T, router_w, logits, xt, xt_scale, s));
     else
-        // up to kRouteSmallMaxTokens tokens this launch also rotates x, and the
-        // routing is one workgroup
-        MOE_STEP(launch_router_and_shared_gateup(x, T, router_w, nullptr, logits, shared_w, hs,
-                                                 small_route ? xt : nullptr, xt_scale, s));
+        MOE_STEP(launch_router_and_shared_gateup(x, T, router_w, nullptr, logits, shared_w, hs, nullptr, xt_scale,
+                                                 s));
     MOE_MARK();
     if (small_route) {
-        MOE_STEP(launch_route_small(logits, T, bias, policy, topk_idx, topk_w, offsets, perm, pos, n_active, active,
-                                    chunks, n_chunks, error_clear, s));
+        MOE_STEP(launch_shared_gateup_route(x, T, shared_w, hs, logits, bias, policy, topk_idx, topk_w, offsets, perm,
+                                            pos, n_active, active, chunks, n_chunks, error_clear, s));
     } else {
         MOE_STEP(launch_topk_rotate(logits, x, T, bias, policy, topk_idx, topk_w, xt, xt_scale, s));
-        MOE_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, error_clear, s));
+        if (grouped)   // many workgroups
+            MOE_STEP(launch_sort_wide(topk_idx, T, ws_at<int>(ws, L.hist), offsets, perm, pos, n_active, active,
+                                      chunks, n_chunks, error_clear, s));
+        else
+            MOE_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, error_clear,
+                                 s));
     }
     MOE_MARK();
     if (grouped) {
@@ -327,7 +338,11 @@ int run_forward_nvfp4(const void *x_, const void *router_w_, const void *codes_,
     } else {
         // (the rotated x it also writes is not used by NVFP4 experts)
         NV_STEP(launch_topk_rotate(logits, x, T, bias, 0, topk_idx, topk_w, xt, xt_scale, s));
-        NV_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, error, s));
+        if (dense)
+            NV_STEP(launch_sort_wide(topk_idx, T, ws_at<int>(ws, L.hist), offsets, perm, pos, n_active, active,
+                                     chunks, n_chunks, error, s));
+        else
+            NV_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, error, s));
     }
     NV_MARK();
     NV_STEP(launch_gateup_nvfp4(codes, scales, tscales, x, perm, active, T, act, s));

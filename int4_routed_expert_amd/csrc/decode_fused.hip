@@ -3,48 +3,52 @@
 // At these sizes every step of the layer moves little data, so the layer is
 // bound by the latency of its dependent steps rather than by bandwidth: a
 // launch per step (router, top-6, sort, gate/up, rotation of a, down, combine)
-// costs a few microseconds each.  Here the first launch computes everything
-// that needs only x: the router logits (one wave per router row) and the
-// shared expert's h = bf16(silu(x Wsg^T) * (x Wsu^T)) (ungated bf16 SwiGLU of
-// width 1024, Flint model card, Aijuus/flint-w4exp, introduction; four
-// columns of h per workgroup).  In a layer of a stack it also computes x
-// itself from the residual stream (rmsnorm), and the second launch adds y to
-// the residual stream, so a stack layer is two launches as well.  The second
-// launch runs all the rest, with two roles of workgroups:
+// costs a few microseconds each.  The first launch computes the router logits
+// (one wave per router row; fp32 sums of exact bf16 products, NInfer README of
+// Flint, "What is inside").  In a layer of a stack it also computes x itself
+// from the residual stream (rmsnorm), and the second launch adds y to the
+// residual stream, so a stack layer is two launches as well.  The second
+// launch runs all the rest, with three roles of workgroups:
 //
-//   every workgroup: the routing of all tokens from the logits (wave t: top-6
-//       of token t, model card, introduction: 256 experts, top-6; weights
-//       sigmoid / max(sum, 2^-14), bloomery issue #632, design thread), then a
-//       stable sort of the <= 48 assignments in LDS;
-//   gate/up workgroups (the first 256): x is rotated in LDS (fwht128 per
-//       128-block, model card, table row "weights"; one task per 512-wide
-//       quarter of a token, dealt from the last wave down so that it runs
-//       beside the top-6 of the first waves; one power-of-two prescale per
-//       block), then wave batches
-//       of 2 (gate, up) row pairs of an active expert for all of its tokens,
-//       a = silu(g) * u in fp32 (sorted-position order), the next batch's codes
-//       in flight while one is multiplied;
-//   down workgroups (the other 256): each owns 8 output features.  Before
-//       waiting it computes the shared down projection z of its features and
-//       requests the down codes of its features for every active expert; once
-//       a is complete it rotates a of every assignment in LDS, finishes the
-//       routed down products and writes y = bf16(z + sum_j w_j o_j) in slot
-//       order.
+//   gate/up workgroups (the first 256): the routing of all tokens from the
+//       logits (wave t: top-6 of token t, model card, introduction: 256
+//       experts, top-6; weights sigmoid / max(sum, 2^-14), bloomery issue
+//       #632, design thread), then a stable sort of the <= 48 assignments in
+//       LDS; x is rotated in LDS (fwht128 per 128-block, model card, table row
+//       "weights"; one task per 512-wide quarter of a token, dealt from the
+//       last wave down so that it runs beside the top-6 of the first waves; one
+//       power-of-two prescale per block), then wave batches of 2 (gate, up) row
+//       pairs of an active expert for all of its tokens, a = silu(g) * u in
+//       fp32 (sorted-position order), the next batch's codes in flight while
+//       one is multiplied;
+//   shared workgroups (the next 256): the shared expert's h =
+//       bf16(silu(x Wsg^T) * (x Wsu^T)) (ungated bf16 SwiGLU of width 1024,
+//       Flint model card, introduction; four columns of h per workgroup, waves
+//       0-3 the gate rows, 4-7 the up rows), streamed beside the routed
+//       experts' codes;
+//   down workgroups (the last 256): each owns 8 output features.  It requests
+//       the shared down weights of its features, routes as the gate/up
+//       workgroups do and requests its down codes for every active expert;
+//       once h is complete it computes the shared down projection z of its
+//       features, and once a is complete it rotates a of every assignment in
+//       LDS, finishes the routed down products and writes y = bf16(z + sum_j
+//       w_j o_j) in slot order.
 //
-// a crosses between workgroups through device-scope stores and loads (cache
-// policy sc0 sc1: written through to, and read from, the level shared by all
-// XCDs), so neither side needs a whole-L2 writeback or invalidate, and through
-// a completion counter that the first launch sets to zero.  The counter is
-// kept in 16 replicas on separate lines (every gate/up workgroup adds 1 to
-// each, one atomic per lane) and each down workgroup polls one replica: 256
-// pollers of a single line crowd its memory channel, and code loads that land
-// on the same channel wait behind them.  Only the down workgroups wait, and
-// only for gate/up workgroups, which have lower indices and never wait, so
-// they were dispatched first and finish whatever else is resident; the wait
-// is also bounded in time (5 ms by default), and a down workgroup that gives
-// up writes NaN to its outputs (y, and in a stack layer the residual stream,
-// so that every later layer's output is NaN too) and sets the workspace's
-// error word, so a failure cannot hang the device and cannot go unnoticed.
+// h and a cross between workgroups through device-scope stores and loads
+// (cache policy sc0 sc1: written through to, and read from, the level shared
+// by all XCDs), so neither side needs a whole-L2 writeback or invalidate, and
+// through two completion counters (h done, a done) that the first launch sets
+// to zero.  Each counter is kept in 16 replicas on separate lines (every
+// producing workgroup adds 1 to each, one atomic per lane) and each down
+// workgroup polls one replica: 256 pollers of a single line crowd its memory
+// channel, and code loads that land on the same channel wait behind them.
+// Only the down workgroups wait, and only for gate/up and shared workgroups,
+// which have lower indices and never wait, so they were dispatched first and
+// finish whatever else is resident; the waits are also bounded in time (5 ms
+// by default), and a down workgroup that gives up writes NaN to its outputs
+// (y, and in a stack layer the residual stream, so that every later layer's
+// output is NaN too) and sets the workspace's error word, so a failure cannot
+// hang the device and cannot go unnoticed.
 #include "common.h"
 #include "gemv_ops.h"
 #include "launch.h"
@@ -57,7 +61,9 @@ namespace {
 constexpr int kFuThreads = 512;
 constexpr int kFuWaves = kFuThreads / kWave;        // 8
 constexpr int kFuGuWgs = 256;                       // gate/up workgroups
+constexpr int kFuShWgs = kIS / 4;                   // shared gate/up workgroups (4 columns of h each)
 constexpr int kFuDnWgs = 256;                       // down workgroups
+constexpr int kFuDn0 = kFuGuWgs + kFuShWgs;         // first down workgroup
 constexpr int kFuCols = kH / kFuDnWgs;              // 8 output features per down workgroup
 constexpr int kFuPairs = 2;                         // (gate, up) row pairs per wave batch
 constexpr int kFuBatchesPerExpert = kI / kFuPairs;  // 256
@@ -97,13 +103,20 @@ struct FuDown {
     float atsc[N][kI / kG];
     float o[N][kFuCols];            // routed outputs of this workgroup's features
     float z[T][kFuCols];            // shared expert outputs
-    int fail;
+    int fail_h, fail_a;             // a wait gave up
+};
+
+template <int T>
+struct FuShared {
+    uint4 xl[T][kH / 8];            // x, bf16
+    float part[8][8];               // [wave][token] row sums
 };
 
 template <int T>
 union FuWork {
     FuGateUp<T> gu;
     FuDown<T> dn;
+    FuShared<T> sh;
 };
 
 // Empty asm that "rewrites" a register quad: the mask conversion of codes that
@@ -175,42 +188,23 @@ __device__ __forceinline__ float row_dot_tokens(const uint4 (&w)[4], const uint4
 }
 
 // ---------------------------------------------------------------------------
-// Launch 1: what needs only x.  Workgroups of 8 waves, one weight row per
-// wave: the first 32 compute router logits (fp32 sums of exact bf16
-// products, NInfer README of Flint, "What is inside": router rows widened
-// exactly from bf16), the other 256 four columns c of h each (waves 0-3 the
-// gate rows, 4-7 the up rows).  x is staged in LDS once per workgroup; in a
-// stack layer (RESID) it is computed there from the fp32 residual stream as
-// bf16(resid / sqrt(mean(resid^2) + 1e-6)) (wave t: token t; every
-// workgroup sums in the same order, so all agree bit for bit) and workgroup 0
-// writes it out.  Workgroup 0 also clears the counters of the second launch
-// and, if `error` is not null, the error word.
+// Launch 1: the router logits.  32 workgroups of 8 waves, one router row per
+// wave (fp32 sums of exact bf16 products, NInfer README of Flint, "What is
+// inside": router rows widened exactly from bf16).  x is staged in LDS once
+// per workgroup; in a stack layer (RESID) it is computed there from the fp32
+// residual stream as bf16(resid / sqrt(mean(resid^2) + 1e-6)) (wave t: token
+// t; every workgroup sums in the same order, so all agree bit for bit) and
+// workgroup 0 writes it out.  Workgroup 0 also clears the counters of the
+// second launch and, if `error` is not null, the error word.
 // ---------------------------------------------------------------------------
 constexpr int kRouterWgs = kE / 8;
-constexpr int kSharedWgs = kIS / 4;
 
+// Stage x [T][2048] bf16 in LDS, from x itself or (RESID) as the bf16 RMS
+// norm of the residual stream; workgroup 0 of the launch writes that x out.
 template <int T, bool RESID>
-__global__ __launch_bounds__(512) void k_router_shared_small(const uint16_t *__restrict__ x,
-                                                             const float *__restrict__ resid,
-                                                             uint16_t *__restrict__ x_out,
-                                                             const uint16_t *__restrict__ router_w,
-                                                             const float *__restrict__ bias,
-                                                             const uint16_t *__restrict__ shared_gu,
-                                                             float *__restrict__ logits, uint16_t *__restrict__ hs,
-                                                             int *__restrict__ counters, int *__restrict__ error) {
-    __shared__ uint4 xl[T][kH / 8];
-    __shared__ float part[8][8];   // shared role: [wave][token]
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
-    if (blockIdx.x == 0 && tid < kFusedCounters) counters[tid * kFusedCounterStride] = 0;
-    if (blockIdx.x == 0 && tid == kFusedCounters && error) *error = 0;
-    // this wave's weight row (router row e, or gate (waves 0-3) / up (4-7) row
-    // c0 + (wave & 3) of the shared expert), requested before x is staged
-    const bool router = (int)blockIdx.x < kRouterWgs;
-    const int e = 8 * (int)blockIdx.x + wave;
-    const int c0 = ((int)blockIdx.x - kRouterWgs) * 4;
-    uint4 w[4];
-    row_load(router ? router_w + (size_t)e * kH : shared_gu + (size_t)((wave < 4 ? 0 : kIS) + c0 + (wave & 3)) * kH,
-             lane, w);
+__device__ __forceinline__ void stage_x(const uint16_t *__restrict__ x, const float *__restrict__ resid,
+                                        uint16_t *__restrict__ x_out, uint4 (*xl)[kH / 8], int tid, int lane,
+                                        int wave) {
     if (!RESID) {
 #pragma unroll
         for (int i = 0; i < (T * (kH / 8) + 511) / 512; ++i) {
@@ -246,19 +240,28 @@ __global__ __launch_bounds__(512) void k_router_shared_small(const uint16_t *__r
             if (blockIdx.x == 0) reinterpret_cast<uint4 *>(x_out + (size_t)t * kH + 512 * i + 8 * lane)[0] = q;
         }
     }
+}
+
+template <int T, bool RESID>
+__global__ __launch_bounds__(512) void k_router_small(const uint16_t *__restrict__ x, const float *__restrict__ resid,
+                                                      uint16_t *__restrict__ x_out,
+                                                      const uint16_t *__restrict__ router_w,
+                                                      const float *__restrict__ bias, float *__restrict__ logits,
+                                                      int *__restrict__ counters, int *__restrict__ error) {
+    __shared__ uint4 xl[T][kH / 8];
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid >> 6;
+    // both counters of the second launch (a done, h done) and the error word
+    if (blockIdx.x == 0 && tid < 2 * kFusedCounters) counters[tid * kFusedCounterStride] = 0;
+    if (blockIdx.x == 0 && tid == 2 * kFusedCounters && error) *error = 0;
+    // this wave's router row, requested before x is staged
+    const int e = 8 * (int)blockIdx.x + wave;
+    uint4 w[4];
+    row_load(router_w + (size_t)e * kH, lane, w);
+    stage_x<T, RESID>(x, resid, x_out, xl, tid, lane, wave);
     __syncthreads();
     const int t = lane >> 3;
     const float sum = row_dot_tokens<T>(w, xl, lane);
-    if (router) {
-        if ((lane & 7) == 0 && t < T) logits[(size_t)t * kE + e] = sum + (bias ? bias[e] : 0.0f);
-        return;
-    }
-    if ((lane & 7) == 0) part[wave][t] = sum;
-    __syncthreads();
-    if (tid < 4 * T) {
-        const int tt = tid >> 2, c = tid & 3;
-        hs[(size_t)tt * kIS + c0 + c] = f32_to_bf16(silu_f(part[c][tt]) * part[4 + c][tt]);
-    }
+    if ((lane & 7) == 0 && t < T) logits[(size_t)t * kE + e] = sum + (bias ? bias[e] : 0.0f);
 }
 
 // ---------------------------------------------------------------------------
@@ -275,14 +278,39 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = wave_id();
     const bool gu_role = blockIdx.x < kFuGuWgs;
 
+    if ((int)blockIdx.x >= kFuGuWgs && (int)blockIdx.x < kFuDn0) {
+        // ---- shared role: 4 columns c0 .. c0+3 of h for every token; this
+        // wave's gate (waves 0-3) or up (4-7) row requested before x is staged
+        const int c0 = ((int)blockIdx.x - kFuGuWgs) * 4;
+        uint4 w[4];
+        row_load(A.shared_gu + (size_t)((wave < 4 ? 0 : kIS) + c0 + (wave & 3)) * kH, lane, w);
+        stage_x<T, false>(A.x, nullptr, nullptr, U.sh.xl, tid, lane, wave);
+        __syncthreads();
+        const float sum = row_dot_tokens<T>(w, U.sh.xl, lane);
+        if ((lane & 7) == 0) U.sh.part[wave][lane >> 3] = sum;
+        __syncthreads();
+        if (tid < 4 * T) {
+            const int tt = tid >> 2, c = tid & 3;
+            const uint16_t hv = f32_to_bf16(silu_f(U.sh.part[c][tt]) * U.sh.part[4 + c][tt]);
+            __builtin_amdgcn_raw_buffer_store_b16(hv, make_buf(A.hs, (uint32_t)(T * kIS * 2)),
+                                                  2 * (tt * kIS + c0 + c), 0, kHandOff);
+        }
+        // count this workgroup done once its stores of h are complete
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (wave == 0) count_done(A.counters_h, lane);
+        return;
+    }
+
     // ---- work that depends on nothing: the loads of the logits and of x
-    // (gate/up role), or the shared down projection of this workgroup's
-    // features, z[t][c0 + wave] = h_t . Wsd[c0 + wave], load i of lane l taking
-    // K [512i + 8l, 512i + 8l + 8) (down role) ----
+    // (gate/up role), or of the shared down weights of this workgroup's
+    // features (down role: load i of lane l takes K [512i + 8l, 512i + 8l + 8)
+    // of row c0 + wave) ----
     float4 lv = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     if (wave < T) lv = reinterpret_cast<const float4 *>(A.logits + (size_t)wave * kE)[lane];
     constexpr int kRotTasks = (4 * T + kFuWaves - 1) / kFuWaves;   // x quarters per wave
     uint4 xq[kRotTasks];
+    uint4 wsd0 = make_uint4(0, 0, 0, 0), wsd1 = wsd0;
     if (gu_role) {
         // task k = (token k / 4, 512-wide quarter k % 4), dealt from the last wave down
 #pragma unroll
@@ -291,30 +319,10 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
             xq[i] = reinterpret_cast<const uint4 *>(A.x + (size_t)(k >> 2) * kH + (k & 3) * 512)[lane];
         }
     } else {
-        const int c0 = ((int)blockIdx.x - kFuGuWgs) * kFuCols;
+        const int c0 = ((int)blockIdx.x - kFuDn0) * kFuCols;
         const __amdgpu_buffer_rsrc_t wb = make_buf(A.shared_down + (size_t)(c0 + wave) * kIS, kIS * 2);
-        const __amdgpu_buffer_rsrc_t hb = make_buf(A.hs, (uint32_t)(T * kIS * 2));
-        const uint4 w0 = bload16_nt(wb, lane * 16, 0), w1 = bload16_nt(wb, lane * 16 + 1024, 0);
-        uint4 hq[T][2];
-#pragma unroll
-        for (int t = 0; t < T; ++t) {
-            hq[t][0] = bload16(hb, lane * 16, t * kIS * 2);
-            hq[t][1] = bload16(hb, lane * 16 + 1024, t * kIS * 2);
-        }
-        float v[8];
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
-            float acc = 0.0f;
-            if (t < T) {
-                acc = dot2b(hq[t][0].x, w0.x, acc); acc = dot2b(hq[t][0].y, w0.y, acc);
-                acc = dot2b(hq[t][0].z, w0.z, acc); acc = dot2b(hq[t][0].w, w0.w, acc);
-                acc = dot2b(hq[t][1].x, w1.x, acc); acc = dot2b(hq[t][1].y, w1.y, acc);
-                acc = dot2b(hq[t][1].z, w1.z, acc); acc = dot2b(hq[t][1].w, w1.w, acc);
-            }
-            v[t] = acc;
-        }
-        const float sum = transpose_reduce<8, kWave>(v);   // token lane / 8
-        if ((lane & 7) == 0 && (lane >> 3) < T) U.dn.z[lane >> 3][wave] = sum;
+        wsd0 = bload16_nt(wb, lane * 16, 0);
+        wsd1 = bload16_nt(wb, lane * 16 + 1024, 0);
     }
 
     // ---- routing: wave t selects token t's six experts ----
@@ -489,7 +497,7 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
     }
 
     // ---- down role ----
-    const int c0 = ((int)blockIdx.x - kFuGuWgs) * kFuCols;
+    const int c0 = ((int)blockIdx.x - kFuDn0) * kFuCols;
     const int replica = ((int)blockIdx.x % kFusedCounters) * kFusedCounterStride;
     // down codes of this workgroup's 8 features for every active expert this
     // wave handles (experts wave, wave + 8, ...): lane l takes row l / 8 and,
@@ -515,18 +523,64 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
         }
     }
 
-    // wait until every gate/up workgroup is done (bounded)
-    if (tid == 0) U.dn.fail = !wait_count(A.counters + replica, kFuGuWgs + A.wait_target_extra, A.wait_ticks);
-    __syncthreads();
-    if (U.dn.fail) {
-        // NaN outputs for this workgroup's features (and in the residual
-        // stream of a stack layer), and the error word
+    // NaN outputs for this workgroup's features (and in the residual stream of
+    // a stack layer), and the error word: a wait gave up
+    auto give_up = [&]() {
         if (tid < T * kFuCols) {
             const size_t i = (size_t)(tid / kFuCols) * kH + c0 + tid % kFuCols;
             A.y[i] = 0x7fc0;
             if (A.resid) A.resid[i] = __builtin_nanf("");
         }
         if (tid == 0) __hip_atomic_store(A.error, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+
+    // the shared down projection once every shared workgroup is done (bounded):
+    // z[t][c0 + wave] = h_t . Wsd[c0 + wave]
+    if (tid == 0) U.dn.fail_h = !wait_count(A.counters_h + replica, kFuShWgs, A.wait_ticks);
+    __syncthreads();
+    if (U.dn.fail_h) {
+        give_up();
+        return;
+    }
+    {
+        const rsrc_t hb = make_buf(A.hs, (uint32_t)(T * kIS * 2));
+        float v[8];
+        // four tokens at a time (the down codes in flight hold many registers)
+#pragma unroll
+        for (int t0 = 0; t0 < 8; t0 += 4) {
+            uint4 hq[4][2];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (t0 + i < T) {
+                    const int ho = (t0 + i) * kIS * 2;
+                    hq[i][0] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(hb, lane * 16, ho,
+                                                                                               kHandOff));
+                    hq[i][1] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(hb, lane * 16 + 1024,
+                                                                                               ho, kHandOff));
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float acc = 0.0f;
+                if (t0 + i < T) {
+                    acc = dot2b(hq[i][0].x, wsd0.x, acc); acc = dot2b(hq[i][0].y, wsd0.y, acc);
+                    acc = dot2b(hq[i][0].z, wsd0.z, acc); acc = dot2b(hq[i][0].w, wsd0.w, acc);
+                    acc = dot2b(hq[i][1].x, wsd1.x, acc); acc = dot2b(hq[i][1].y, wsd1.y, acc);
+                    acc = dot2b(hq[i][1].z, wsd1.z, acc); acc = dot2b(hq[i][1].w, wsd1.w, acc);
+                }
+                v[t0 + i] = acc;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        const float sum = transpose_reduce<8, kWave>(v);   // token lane / 8
+        if ((lane & 7) == 0 && (lane >> 3) < T) U.dn.z[lane >> 3][wave] = sum;
+    }
+
+    // wait until every gate/up workgroup is done (bounded)
+    if (tid == 0) U.dn.fail_a = !wait_count(A.counters + replica, kFuGuWgs + A.wait_target_extra, A.wait_ticks);
+    __syncthreads();
+    if (U.dn.fail_a) {
+        give_up();
         return;
     }
 
@@ -619,15 +673,14 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
     default: break;                                                              \
     }
 
-void launch_router_shared_small(const uint16_t *x, const float *resid, uint16_t *x_out, int T,
-                                const uint16_t *router_w, const float *bias, const uint16_t *shared_w, float *logits,
-                                uint16_t *hs, int *counters, int *error, hipStream_t s) {
+void launch_router_small(const uint16_t *x, const float *resid, uint16_t *x_out, int T, const uint16_t *router_w,
+                         const float *bias, float *logits, int *counters, int *error, hipStream_t s) {
     if (resid) {
-        MOE_FUSED_DISPATCH2(k_router_shared_small, true, dim3(kRouterWgs + kSharedWgs), dim3(512), 0, s, x, resid, x_out,
-                            router_w, bias, shared_w, logits, hs, counters, error)
+        MOE_FUSED_DISPATCH2(k_router_small, true, dim3(kRouterWgs), dim3(512), 0, s, x, resid, x_out, router_w, bias,
+                            logits, counters, error)
     } else {
-        MOE_FUSED_DISPATCH2(k_router_shared_small, false, dim3(kRouterWgs + kSharedWgs), dim3(512), 0, s, x, resid, x_out,
-                            router_w, bias, shared_w, logits, hs, counters, error)
+        MOE_FUSED_DISPATCH2(k_router_small, false, dim3(kRouterWgs), dim3(512), 0, s, x, resid, x_out, router_w, bias,
+                            logits, counters, error)
     }
 }
 
@@ -635,7 +688,7 @@ void launch_router_shared_small(const uint16_t *x, const float *resid, uint16_t 
 
 void launch_decode_fused(const FusedDecodeArgs &args, hipStream_t s) {
     const int T = args.T;
-    MOE_FUSED_DISPATCH(k_decode_fused, dim3(kFuGuWgs + kFuDnWgs), dim3(kFuThreads), 0, s, args)
+    MOE_FUSED_DISPATCH(k_decode_fused, dim3(kFuDn0 + kFuDnWgs), dim3(kFuThreads), 0, s, args)
 }
 
 #undef MOE_FUSED_DISPATCH

@@ -14,14 +14,25 @@ void launch_router_and_shared_gateup(const uint16_t *x, int T, const uint16_t *r
                                      float *logits, const uint16_t *shared_w, uint16_t *hs, uint32_t *xt,
                                      float *xt_scale, hipStream_t s);
 
-// Decode sizes (1..kFusedMaxTokens tokens): one launch for what needs only x
-// (router logits and the shared expert's h; it also clears the counters of the
-// launch after it), then the whole rest of the layer in one launch (top-6,
-// sort, rotation of x, routed gate/up, rotation of a, routed and shared down,
-// combine).
+// 9..kRouteSmallMaxTokens tokens: the router logits (without the bias) and the
+// rotated fp16 x in one launch, then the shared expert's gate/up (h) and, in
+// its workgroup 0, the top-6 and the sort (as launch_route_small) in the next.
+void launch_router_rotate(const uint16_t *x, int T, const uint16_t *router_w, float *logits, uint32_t *xt,
+                          float *xt_scale, hipStream_t s);
+void launch_shared_gateup_route(const uint16_t *x, int T, const uint16_t *shared_w, uint16_t *hs,
+                                const float *logits, const float *bias, int policy, int *topk_idx, float *topk_w,
+                                int *offsets, int *perm, int *pos, int *n_active, int *slots, int *chunks,
+                                int *n_chunks, int *error, hipStream_t s);
+
+// Decode sizes (1..kFusedMaxTokens tokens): one launch for the router logits
+// (it also clears the counters of the launch after it), then the whole rest
+// of the layer in one launch (top-6, sort, rotation of x, routed gate/up, the
+// shared expert's gate/up, rotation of a, routed and shared down, combine).
 constexpr int kFusedMaxTokens = 8;
-constexpr int kFusedCounters = 16;        // replicas of the completion counter,
+constexpr int kFusedCounters = 16;        // replicas of each completion counter,
 constexpr int kFusedCounterStride = 64;   // one per 256 bytes of `counters`
+// bytes of the counters: a done, then h done (16 replicas each)
+constexpr int kFusedSyncBytes = 2 * kFusedCounters * kFusedCounterStride * 4;
 struct FusedDecodeArgs {
     const uint16_t *x;
     const float *logits;           // without the router bias
@@ -29,8 +40,9 @@ struct FusedDecodeArgs {
     int router_policy;             // MOE_W4_ROUTER_* flags
     const uint8_t *codes;
     const uint16_t *scales;
+    const uint16_t *shared_gu;     // [2048][2048] bf16: gate rows, then up rows
     const uint16_t *shared_down;   // [2048][1024] bf16
-    const uint16_t *hs;            // [T][1024] bf16, from the first launch
+    uint16_t *hs;                  // [T][1024] bf16 scratch: the shared expert's h
     int T;
     int *topk_idx;
     float *topk_w;
@@ -44,7 +56,8 @@ struct FusedDecodeArgs {
     float *act;                    // [6T][512] fp32 scratch, sorted-position order
     uint16_t *y;
     float *resid;                  // stack layer: resid += y (else null)
-    int *counters;                 // 4096 bytes; zero at launch (the first launch clears them)
+    int *counters;                 // a done: 4096 bytes, zero at launch (the first launch clears them)
+    int *counters_h;               // h done: the next 4096 bytes, likewise
     int *error;                    // set to 1 by a down workgroup whose wait gave up
     int wait_target_extra;         // added to the count the wait needs (0; > 0 only to test the failure path)
     uint32_t wait_ticks;           // bound of the wait, in ticks of the 100 MHz real-time clock
@@ -53,24 +66,32 @@ struct FusedDecodeArgs {
 // moe_w4_set_fused_wait in the ABI).
 void fused_wait_params(uint32_t &ticks, int &extra);
 // With resid (a stack layer), x is computed as bf16(rmsnorm(resid)) and also
-// written to x_out, and the second launch adds y to resid.
-// error: the workspace's error word, cleared by this launch when non-null.
-void launch_router_shared_small(const uint16_t *x, const float *resid, uint16_t *x_out, int T,
-                                const uint16_t *router_w, const float *bias, const uint16_t *shared_w, float *logits,
-                                uint16_t *hs, int *counters, int *error, hipStream_t s);
+// written to x_out, and the second launch adds y to resid.  counters:
+// kFusedSyncBytes, cleared by this launch; error: the workspace's error word,
+// cleared by this launch when non-null.
+void launch_router_small(const uint16_t *x, const float *resid, uint16_t *x_out, int T, const uint16_t *router_w,
+                         const float *bias, float *logits, int *counters, int *error, hipStream_t s);
 void launch_decode_fused(const FusedDecodeArgs &args, hipStream_t s);
 
 // Per token: top-6 of the logits (+ bias, if any), the sigmoid weights
 // normalised as the router policy says (bias, policy: MOE_W4_ROUTER_* flags),
 // and the Hadamard-rotated fp16 copy of x (with its power-of-two scale).  The
 // router launches write the logits without the bias.
+// rotate = false: xt gets x itself as natural-order fp16 with the same
+// per-token prescale (the operands of the NVFP4 experts' MFMA form).
 void launch_topk_rotate(const float *logits, const uint16_t *x, int T, const float *bias, int policy,
-                        int *topk_idx, float *topk_w, uint32_t *xt, float *xt_scale, hipStream_t s);
+                        int *topk_idx, float *topk_w, uint32_t *xt, float *xt_scale, hipStream_t s,
+                        bool rotate = true);
 // Stable counting sort of the 6T assignments by expert (one workgroup).
 // slots: int[256][8] records {expert, first sorted position, count, first
 // token, second token, 0, 0, 0}, one per expert with tokens, then expert -1.
 // chunks: int[max_chunks(T)][4] records {expert, first sorted position, rows
 // (<= 96), 0} covering every expert's assignments; *n_chunks of them.
+// The same result from many workgroups (two launches), for prefill sizes:
+// hist is int[sort_hist_blocks(T)][256] scratch.
+int sort_hist_blocks(int T);
+void launch_sort_wide(const int *topk_idx, int T, int *hist, int *offsets, int *perm, int *pos, int *n_active,
+                      int *slots, int *chunks, int *n_chunks, int *error, hipStream_t s);
 // error (or null): the workspace's error word, cleared (this sequence cannot fail).
 void launch_sort(const int *topk_idx, int T, int *offsets, int *perm, int *pos, int *n_active,
                  int *slots, int *chunks, int *n_chunks, int *error, hipStream_t s);

@@ -9,10 +9,14 @@
 // a fwht128-rotated basis, so x is rotated per 128-block before the experts.
 #include "common.h"
 #include "launch.h"
+#include "route_small.h"
 #include "token_ops.h"
 
 namespace moe_w4 {
 
+// ROTATE: xt gets the fwht128-rotated x in the int4 experts' operand order;
+// otherwise x itself as natural-order fp16 (the NVFP4 experts' operands).
+template <bool ROTATE>
 __global__ __launch_bounds__(256) void k_topk_rotate(const float *__restrict__ logits,
                                                      const uint16_t *__restrict__ x, int T,
                                                      int *__restrict__ topk_idx,
@@ -40,14 +44,19 @@ __global__ __launch_bounds__(256) void k_topk_rotate(const float *__restrict__ l
             topk_w[(size_t)t * kTopK + j] = sel.w[j];
         }
     }
-    const int sh = rotate_x_wave(xq, lane, xt + (size_t)t * (kH / 2) + lane * 16);
+    const int sh = ROTATE ? rotate_x_wave(xq, lane, xt + (size_t)t * (kH / 2) + lane * 16)
+                          : natural_x_wave(xq, lane, xt + (size_t)t * (kH / 2) + lane * 16);
     if (lane == 0) xt_scale[t] = ldexpf(1.0f, sh);
 }
 
 void launch_topk_rotate(const float *logits, const uint16_t *x, int T, const float *bias, int policy,
-                        int *topk_idx, float *topk_w, uint32_t *xt, float *xt_scale, hipStream_t s) {
-    hipLaunchKernelGGL(k_topk_rotate, dim3((T + 3) / 4), dim3(256), 0, s, logits, x, T, topk_idx,
-                       topk_w, xt, xt_scale, RouterPolicy{bias, policy});
+                        int *topk_idx, float *topk_w, uint32_t *xt, float *xt_scale, hipStream_t s, bool rotate) {
+    if (rotate)
+        hipLaunchKernelGGL(k_topk_rotate<true>, dim3((T + 3) / 4), dim3(256), 0, s, logits, x, T, topk_idx, topk_w,
+                           xt, xt_scale, RouterPolicy{bias, policy});
+    else
+        hipLaunchKernelGGL(k_topk_rotate<false>, dim3((T + 3) / 4), dim3(256), 0, s, logits, x, T, topk_idx,
+                           topk_w, xt, xt_scale, RouterPolicy{bias, policy});
 }
 
 // ---------------------------------------------------------------------------
@@ -231,158 +240,184 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
 }
 
 // ---------------------------------------------------------------------------
-// Top-6 and sort of a few tokens (up to kRouteSmallMaxTokens) in one
-// workgroup of 16 waves: wave w selects tokens w, w + 16, ... (all their logit
-// loads issued first); then a stable counting sort of the <= 288 assignments
-// in LDS (the algorithm of k_sort, with the chosen experts never leaving the
-// workgroup).
+// The same stable counting sort spread over many workgroups (prefill sizes):
+// workgroup b owns assignments [1024 b, 1024 b + 1024), wave w of it the 64
+// from 1024 b + 64 w.
+//   1. k_sort_hist: each workgroup's histogram over the experts -> hist[b][e].
+//   2. k_sort_place: every workgroup reads all histograms: per expert the
+//      total (-> offsets) and the counts of the workgroups before it (its base
+//      inside the expert); inside the workgroup, per-wave counts and ballots
+//      rank its assignments exactly as k_sort does.  Workgroup 0 writes the
+//      offsets, the chunk list and the slot records; the workgroup that places
+//      an expert's first (second) sorted assignment writes its first (second)
+//      token into the expert's record.
+// The result is that of k_sort bit for bit: stable in the assignment index.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_route_small(const float *__restrict__ logits, int T,
-                                                      int *__restrict__ topk_idx, float *__restrict__ topk_w,
-                                                      int *__restrict__ offsets, int *__restrict__ perm,
-                                                      int *__restrict__ pos, int *__restrict__ n_active,
-                                                      int *__restrict__ slots, int4 *__restrict__ chunks,
-                                                      int *__restrict__ n_chunks, int *__restrict__ error,
-                                                      RouterPolicy rp) {
-    constexpr int kPerWave = (kRouteSmallMaxTokens + kSortWaves - 1) / kSortWaves;
-    constexpr int kMaxChunks = (kTopK * kRouteSmallMaxTokens + 63) / 64;
-    __shared__ int sel[kTopK * kRouteSmallMaxTokens];     // expert of assignment a
-    __shared__ int sperm[kTopK * kRouteSmallMaxTokens];   // assignment at sorted position p
-    __shared__ int cnt[kMaxChunks][kE];                   // per chunk: count, then base of each expert
+constexpr int kSortWgAssign = kSortWaves * 64;   // assignments per workgroup
+
+int sort_hist_blocks(int T) { return (kTopK * T + kSortWgAssign - 1) / kSortWgAssign; }
+
+__global__ __launch_bounds__(1024) void k_sort_hist(const int *__restrict__ topk_idx, int N, int *__restrict__ hist) {
+    __shared__ int cnt[kE];
+    const int tid = threadIdx.x;
+    if (tid < kE) cnt[tid] = 0;
+    const int a = (int)blockIdx.x * kSortWgAssign + tid;
+    const int e = a < N ? topk_idx[a] : -1;
+    __syncthreads();
+    if (e >= 0) atomicAdd(&cnt[e], 1);
+    __syncthreads();
+    if (tid < kE) hist[(size_t)blockIdx.x * kE + tid] = cnt[tid];
+}
+
+__global__ __launch_bounds__(1024) void k_sort_place(const int *__restrict__ topk_idx, int N, int nb,
+                                                     const int *__restrict__ hist, int *__restrict__ offsets,
+                                                     int *__restrict__ perm, int *__restrict__ pos,
+                                                     int *__restrict__ n_active, int *__restrict__ slots,
+                                                     int4 *__restrict__ chunks, int *__restrict__ n_chunks,
+                                                     int *__restrict__ error) {
+    __shared__ int cnt[kSortWaves][kE];   // per wave: count, then base of each expert
+    __shared__ int base[kE];              // this workgroup's first sorted position of each expert
     __shared__ int tot[kE];
     __shared__ int offs[kE + 1];
-    __shared__ int act_rank[kE];                          // active experts below e (-1: e not active)
-    __shared__ int act_list[kE];                          // active expert of each slot
-    __shared__ int n_act_s;
+    __shared__ int act_rank[kE];          // active experts below e (-1: e not active)
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int N = kTopK * T;
-    for (int i = tid; i < kMaxChunks * kE; i += blockDim.x) (&cnt[0][0])[i] = 0;
-    if (tid == 0 && error) *error = 0;   // this launch sequence cannot fail on the device
-
-    float4 lv[kPerWave];
-#pragma unroll
-    for (int i = 0; i < kPerWave; ++i) {
-        const int t = min(wave + kSortWaves * i, T - 1);   // past the end: token T-1 again (unused)
-        lv[i] = reinterpret_cast<const float4 *>(logits + (size_t)t * kE)[lane];
-    }
-#pragma unroll
-    for (int i = 0; i < kPerWave; ++i) {
-        const int t = wave + kSortWaves * i;
-        if (t < T) {
-            const Top6 r = top6_wave(lv[i], lane, rp);
-#pragma unroll
-            for (int j = 0; j < kTopK; ++j) {
-                if (lane == j) {
-                    topk_idx[(size_t)t * kTopK + j] = r.e[j];
-                    topk_w[(size_t)t * kTopK + j] = r.w[j];
-                    sel[kTopK * t + j] = r.e[j];
-                }
-            }
-        }
-    }
-    __syncthreads();
-
-    // stable counting sort: chunk c = assignments [64c, 64c + 64) belongs to
-    // wave c; equal experts inside a chunk are ranked with ballots, and the
-    // counts of earlier chunks and of smaller experts give the base
-    const int n_chunks_a = (N + 63) >> 6;
-    int e_mine = -1, within = 0;
-    if (wave < n_chunks_a) {
-        const int a = 64 * wave + lane;
-        const bool valid = a < N;
-        e_mine = valid ? sel[a] : 0;
-        uint64_t same = __ballot(valid);
-#pragma unroll
-        for (int bit = 0; bit < 8; ++bit) {
-            const uint64_t bal = __ballot((e_mine >> bit) & 1);
-            same &= ((e_mine >> bit) & 1) ? bal : ~bal;
-        }
-        const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-        within = __popcll(same & below);
-        // the lowest lane of each group of equal experts records the group size
-        if (valid && (same & below) == 0) cnt[wave][e_mine] = __popcll(same);
-        if (!valid) e_mine = -1;
-    }
-    __syncthreads();
-    // per expert: base of each chunk, total (thread e < 256)
+    const int b = blockIdx.x;
+    for (int i = tid; i < kSortWaves * kE; i += blockDim.x) (&cnt[0][0])[i] = 0;
+    if (b == 0 && tid == 0 && error) *error = 0;   // this launch sequence cannot fail on the device
+    // this thread's assignment and the histograms of every workgroup (thread e < 256)
+    const int a = b * kSortWgAssign + tid;
+    const bool valid = a < N;
+    const int e_mine = valid ? topk_idx[a] : 0;
     if (tid < kE) {
-        int run = 0;
-        for (int c = 0; c < n_chunks_a; ++c) {
-            const int v = cnt[c][tid];
-            cnt[c][tid] = run;
-            run += v;
+        int before = 0, total = 0;
+        for (int k = 0; k < nb; ++k) {
+            const int c = hist[(size_t)k * kE + tid];
+            before += k < b ? c : 0;
+            total += c;
         }
-        tot[tid] = run;
+        base[tid] = before;
+        tot[tid] = total;
     }
     __syncthreads();
-    // exclusive scan of the totals (wave 0, 4 per lane) -> offsets; flags of
-    // the non-empty experts -> slot of each active expert
+    if (valid) atomicAdd(&cnt[wave][e_mine], 1);
+    // exclusive scans of the totals (offsets), of the non-empty flags (slot
+    // of each active expert) and of the chunk counts (wave 0, 4 per lane)
     if (wave == 0) {
-        int c4[4], f[4], sc = 0, sf = 0;
+        int c[4], f[4], k[4], sc = 0, sf = 0, sk = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            c4[i] = tot[4 * lane + i];
-            f[i] = c4[i] > 0;
-            sc += c4[i];
+            c[i] = tot[4 * lane + i];
+            f[i] = c[i] > 0;
+            k[i] = (c[i] + kSortChunkRows - 1) / kSortChunkRows;
+            sc += c[i];
             sf += f[i];
+            sk += k[i];
         }
-        int ic = sc, jf = sf;
+        int ic = sc, jf = sf, jk = sk;
 #pragma unroll
         for (int d = 1; d < 64; d <<= 1) {
-            const int pc = __shfl_up(ic, d, kWave), pf = __shfl_up(jf, d, kWave);
-            if (lane >= d) { ic += pc; jf += pf; }
+            const int pc = __shfl_up(ic, d, kWave), pf = __shfl_up(jf, d, kWave), pk = __shfl_up(jk, d, kWave);
+            if (lane >= d) { ic += pc; jf += pf; jk += pk; }
         }
-        int ec = ic - sc, ef = jf - sf;
+        int ec = ic - sc, ef = jf - sf, ek = jk - sk;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int e = 4 * lane + i;
             offs[e] = ec;
-            offsets[e] = ec;
             act_rank[e] = f[i] ? ef : -1;
-            ec += c4[i];
+            if (b == 0) {
+                offsets[e] = ec;
+                if (f[i]) {
+                    // the expert's record (its tokens are written where they are placed)
+                    int *rec = slots + 8 * ef;
+                    rec[0] = e;
+                    rec[1] = ec;
+                    rec[2] = c[i];
+                    rec[5] = 0;
+                    rec[6] = 0;
+                    rec[7] = 0;
+                }
+                for (int r = 0, q = ek; r < c[i]; r += kSortChunkRows, ++q)
+                    chunks[q] = make_int4(e, ec + r, min(kSortChunkRows, c[i] - r), 0);
+            }
+            ec += c[i];
             ef += f[i];
+            ek += k[i];
         }
         if (lane == 63) {
             offs[kE] = ec;
-            offsets[kE] = ec;
-            *n_active = ef;
-            *n_chunks = ef;
-            n_act_s = ef;
+            if (b == 0) {
+                offsets[kE] = ec;
+                *n_active = ef;
+                *n_chunks = ek;
+            }
+        }
+        // records past the active experts
+        if (b == 0) {
+            const int n_act = __shfl(jf, 63, kWave);
+            for (int r = n_act + lane; r < kE; r += kWave) {
+                int4 *rec = reinterpret_cast<int4 *>(slots + 8 * r);
+                rec[0] = make_int4(-1, 0, 0, 0);
+                rec[1] = make_int4(0, 0, 0, 0);
+            }
         }
     }
     __syncthreads();
-    if (e_mine >= 0) {
-        const int a = 64 * wave + lane;
-        const int dest = offs[e_mine] + cnt[wave][e_mine] + within;
-        pos[a] = dest;
-        perm[dest] = a;
-        sperm[dest] = a;
-    }
-    if (tid < kE && act_rank[tid] >= 0) act_list[act_rank[tid]] = tid;
-    __syncthreads();
-    // slot records {expert, first sorted position, count, first token, second
-    // token}, records past n_active hold expert -1; chunks {expert, first
-    // position, rows, 0} (rows <= 48 < 96: one chunk per active expert)
+    // per-wave bases: offset of the expert + this workgroup's base + the counts
+    // of the earlier waves of the workgroup (thread e < 256)
     if (tid < kE) {
-        int4 *rec = reinterpret_cast<int4 *>(slots + 8 * tid);
-        if (tid < n_act_s) {
-            const int e = act_list[tid], b = offs[e], n = offs[e + 1] - offs[e];
-            const int t0 = sperm[b] / kTopK, t1 = n > 1 ? sperm[b + 1] / kTopK : t0;
-            rec[0] = make_int4(e, b, n, t0);
-            rec[1] = make_int4(t1, 0, 0, 0);
-            chunks[tid] = make_int4(e, b, n, 0);
-        } else {
-            rec[0] = make_int4(-1, 0, 0, 0);
-            rec[1] = make_int4(0, 0, 0, 0);
+        int run = offs[tid] + base[tid];
+        for (int w = 0; w < kSortWaves; ++w) {
+            const int c = cnt[w][tid];
+            cnt[w][tid] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    // stable rank inside the wave's 64 assignments: equal experts ranked by
+    // lane through the ballots of the expert's bits
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+        const uint64_t bal = __ballot((e_mine >> bit) & 1);
+        same &= ((e_mine >> bit) & 1) ? bal : ~bal;
+    }
+    if (valid) {
+        const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+        const int dest = cnt[wave][e_mine] + __popcll(same & below);
+        perm[dest] = a;
+        pos[a] = dest;
+        // the expert's first and second tokens into its record
+        const int r = dest - offs[e_mine];
+        const int n_e = offs[e_mine + 1] - offs[e_mine];
+        int *rec = slots + 8 * act_rank[e_mine];
+        if (r == 0) {
+            rec[3] = a / kTopK;
+            if (n_e == 1) rec[4] = a / kTopK;
+        } else if (r == 1) {
+            rec[4] = a / kTopK;
         }
     }
 }
 
+// Top-6 and sort of a few tokens (up to kRouteSmallMaxTokens) in one
+// workgroup of 16 waves (route_small.h).
+__global__ __launch_bounds__(1024) void k_route_small(RouteSmallArgs A) { route_small_block<kSortWaves>(A); }
+
 void launch_route_small(const float *logits, int T, const float *bias, int policy, int *topk_idx, float *topk_w,
                         int *offsets, int *perm, int *pos, int *n_active, int *slots, int *chunks, int *n_chunks,
                         int *error, hipStream_t s) {
-    hipLaunchKernelGGL(k_route_small, dim3(1), dim3(1024), 0, s, logits, T, topk_idx, topk_w, offsets, perm, pos,
-                       n_active, slots, reinterpret_cast<int4 *>(chunks), n_chunks, error, RouterPolicy{bias, policy});
+    const RouteSmallArgs A{logits, T, RouterPolicy{bias, policy}, topk_idx, topk_w, offsets, perm, pos, n_active,
+                           slots, reinterpret_cast<int4 *>(chunks), n_chunks, error};
+    hipLaunchKernelGGL(k_route_small, dim3(1), dim3(1024), 0, s, A);
+}
+
+void launch_sort_wide(const int *topk_idx, int T, int *hist, int *offsets, int *perm, int *pos, int *n_active,
+                      int *slots, int *chunks, int *n_chunks, int *error, hipStream_t s) {
+    const int nb = sort_hist_blocks(T), N = kTopK * T;
+    hipLaunchKernelGGL(k_sort_hist, dim3(nb), dim3(1024), 0, s, topk_idx, N, hist);
+    hipLaunchKernelGGL(k_sort_place, dim3(nb), dim3(1024), 0, s, topk_idx, N, nb, hist, offsets, perm, pos, n_active,
+                       slots, reinterpret_cast<int4 *>(chunks), n_chunks, error);
 }
 
 void launch_sort(const int *topk_idx, int T, int *offsets, int *perm, int *pos, int *n_active,

@@ -27,6 +27,7 @@
 // order inside an MFMA is the same for both operands.
 #include "common.h"
 #include "launch.h"
+#include "route_small.h"
 #include "token_ops.h"
 
 namespace moe_w4 {
@@ -62,6 +63,9 @@ struct SkinnyJobs {
     int rot_tokens;
     uint32_t *xt;
     float *xt_scale;
+    // optional fourth role (the ROUTE instances), workgroup 0: the top-6 and
+    // the sort of up to kRouteSmallMaxTokens tokens (route_small.h)
+    RouteSmallArgs route;
 };
 
 __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
@@ -75,17 +79,22 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 // lanes r and r + 8 read the same weight row, which doubles the workgroups of
 // a small matrix (the 1024-row shared down projection would otherwise leave
 // half the CUs idle); the MFMA units have ample room for the duplicate columns.
-template <int MT, int KS, int KB, int CW>
+template <int MT, int KS, int KB, int CW, bool ROUTE>
 __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__ A, int M, SkinnyJobs jobs) {
     constexpr int K = 128 * KS * KB;
     __shared__ f32x4_t red[KS][MT][64];
+    if (ROUTE && blockIdx.x == 0) {
+        route_small_block<KS>(jobs.route);
+        return;
+    }
+    const int bx = (int)blockIdx.x - (ROUTE ? 1 : 0);
     // both jobs' fields are read (in parallel, at fixed kernel-argument
     // offsets) and then selected: indexing the argument by the job number
     // would make every field a dependent scalar load
     const SkinnyJob j0 = jobs.job[0], j1 = jobs.job[1];
-    if ((int)blockIdx.x >= j0.n_blocks + j1.n_blocks) {
+    if (bx >= j0.n_blocks + j1.n_blocks) {
         const int lane = threadIdx.x & 63;
-        const int t = ((int)blockIdx.x - j0.n_blocks - j1.n_blocks) * KS + wave_id();
+        const int t = (bx - j0.n_blocks - j1.n_blocks) * KS + wave_id();
         if (t >= jobs.rot_tokens) return;
         uint4 xq[4];
         const uint4 *xp = reinterpret_cast<const uint4 *>(jobs.rot_x + (size_t)t * kH + lane * 32);
@@ -95,7 +104,7 @@ __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__
         if (lane == 0) jobs.xt_scale[t] = ldexpf(1.0f, sh);
         return;
     }
-    const bool second = (int)blockIdx.x >= j0.n_blocks;
+    const bool second = bx >= j0.n_blocks;
     SkinnyJob J;
     J.B = second ? j1.B : j0.B;
     J.b_rows = second ? j1.b_rows : j0.b_rows;
@@ -108,7 +117,7 @@ __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__
     J.topk_w = second ? j1.topk_w : j0.topk_w;
     J.pos = second ? j1.pos : j0.pos;
     J.o = second ? j1.o : j0.o;
-    const int blk = second ? (int)blockIdx.x - j0.n_blocks : (int)blockIdx.x;
+    const int blk = second ? bx - j0.n_blocks : bx;
     const int epi = J.epi;
     const int lane = threadIdx.x & 63, wave = wave_id();
     const int r = lane & 15, g = lane >> 4;
@@ -228,19 +237,53 @@ __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__
     }
 }
 
-template <int KB, int CW>
+template <int KB, int CW, bool ROUTE = false>
 static void launch_skinny_k(const uint16_t *A, int M, const SkinnyJobs &jobs, hipStream_t s) {
     constexpr int KS = 8;
-    dim3 grid(jobs.job[0].n_blocks + jobs.job[1].n_blocks + (jobs.rot_tokens + KS - 1) / KS), block(64 * KS);
+    dim3 grid((ROUTE ? 1 : 0) + jobs.job[0].n_blocks + jobs.job[1].n_blocks + (jobs.rot_tokens + KS - 1) / KS),
+        block(64 * KS);
     if (M <= 16)
-        hipLaunchKernelGGL((k_skinny<1, KS, KB, CW>), grid, block, 0, s, A, M, jobs);
+        hipLaunchKernelGGL((k_skinny<1, KS, KB, CW, ROUTE>), grid, block, 0, s, A, M, jobs);
     else if (M <= 32)
-        hipLaunchKernelGGL((k_skinny<2, KS, KB, CW>), grid, block, 0, s, A, M, jobs);
+        hipLaunchKernelGGL((k_skinny<2, KS, KB, CW, ROUTE>), grid, block, 0, s, A, M, jobs);
     else
-        hipLaunchKernelGGL((k_skinny<4, KS, KB, CW>), grid, block, 0, s, A, M, jobs);
+        hipLaunchKernelGGL((k_skinny<4, KS, KB, CW, ROUTE>), grid, block, 0, s, A, M, jobs);
 }
 
 static SkinnyJob no_job() { return SkinnyJob{nullptr, 0, 0, 0, kEpiStoreF32, nullptr, nullptr, 0, nullptr, nullptr, nullptr}; }
+
+static SkinnyJobs no_jobs() {
+    SkinnyJobs jobs;
+    jobs.job[0] = jobs.job[1] = no_job();
+    jobs.rot_x = nullptr;
+    jobs.rot_tokens = 0;
+    jobs.xt = nullptr;
+    jobs.xt_scale = nullptr;
+    jobs.route = RouteSmallArgs{};
+    return jobs;
+}
+
+void launch_router_rotate(const uint16_t *x, int T, const uint16_t *router_w, float *logits, uint32_t *xt,
+                          float *xt_scale, hipStream_t s) {
+    SkinnyJobs jobs = no_jobs();
+    jobs.rot_x = x;
+    jobs.rot_tokens = T;
+    jobs.xt = xt;
+    jobs.xt_scale = xt_scale;
+    jobs.job[0] = SkinnyJob{router_w, kE, 0, kE / 16, kEpiStoreF32, nullptr, logits, kE, nullptr, nullptr, nullptr};
+    launch_skinny_k<kH / (128 * 8), 16>(x, T, jobs, s);
+}
+
+void launch_shared_gateup_route(const uint16_t *x, int T, const uint16_t *shared_w, uint16_t *hs,
+                                const float *logits, const float *bias, int policy, int *topk_idx, float *topk_w,
+                                int *offsets, int *perm, int *pos, int *n_active, int *slots, int *chunks,
+                                int *n_chunks, int *error, hipStream_t s) {
+    SkinnyJobs jobs = no_jobs();
+    jobs.job[0] = SkinnyJob{shared_w, 2 * kIS, kIS, 2 * kIS / 16, kEpiSwiglu, nullptr, hs, kIS, nullptr, nullptr, nullptr};
+    jobs.route = RouteSmallArgs{logits, T, RouterPolicy{bias, policy}, topk_idx, topk_w, offsets, perm, pos,
+                                n_active, slots, reinterpret_cast<int4 *>(chunks), n_chunks, error};
+    launch_skinny_k<kH / (128 * 8), 16, true>(x, T, jobs, s);
+}
 
 void launch_router_and_shared_gateup(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
                                      float *logits, const uint16_t *shared_w, uint16_t *hs, uint32_t *xt,

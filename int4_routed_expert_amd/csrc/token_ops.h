@@ -202,4 +202,35 @@ __device__ __forceinline__ int rotate_x_wave(const uint4 (&xq)[4], int lane, uin
     return sh;
 }
 
+// x of one token by one wave as natural-order fp16 operands (the NVFP4
+// experts' basis: no Hadamard): lane l holds K [32l, 32l+32) of the bf16 row
+// and writes words (x[2i], x[2i+1]) * 2^-sh to dst[0..15]; returns the
+// token's prescale shift sh (largest magnitude in [2^13, 2^14), bf16 values
+// times a power of two: exact in fp16 unless they fall below its normal range).
+__device__ __forceinline__ int natural_x_wave(const uint4 (&xq)[4], int lane, uint32_t *dst) {
+    float v[32];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint4 q = xq[i];
+        v[8 * i + 0] = bf16lo(q.x); v[8 * i + 1] = bf16hi(q.x);
+        v[8 * i + 2] = bf16lo(q.y); v[8 * i + 3] = bf16hi(q.y);
+        v[8 * i + 4] = bf16lo(q.z); v[8 * i + 5] = bf16hi(q.z);
+        v[8 * i + 6] = bf16lo(q.w); v[8 * i + 7] = bf16hi(q.w);
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    amax = wave_max(amax);
+    const int sh = prescale_shift(amax);
+    uint4 *d = reinterpret_cast<uint4 *>(dst);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float *q = v + 8 * i;
+        d[i] = make_uint4(pack_half2(ldexpf(q[0], -sh), ldexpf(q[1], -sh)), pack_half2(ldexpf(q[2], -sh), ldexpf(q[3], -sh)),
+                          pack_half2(ldexpf(q[4], -sh), ldexpf(q[5], -sh)), pack_half2(ldexpf(q[6], -sh), ldexpf(q[7], -sh)));
+    }
+    (void)lane;
+    return sh;
+}
+
 }  // namespace moe_w4

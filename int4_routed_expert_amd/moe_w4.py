@@ -51,7 +51,7 @@ class MoeW4Error(RuntimeError):
 class WsLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_size_t) for n in (
         "logits", "topk_idx", "topk_w", "offsets", "perm", "pos", "n_active", "active",
-        "xt", "xt_scale", "act", "at", "at_scale", "hs", "o", "z", "chunks", "n_chunks", "sync", "error", "total")]
+        "xt", "xt_scale", "act", "at", "at_scale", "hs", "o", "z", "chunks", "n_chunks", "sync", "error", "hist", "total")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}
