@@ -43,6 +43,29 @@ ROUTER_BYTES = 256 * 2048 * 2
 SHARED_BYTES = 3 * 1024 * 2048 * 2
 
 
+def roofline_entry(kernel, nbytes, flops, kernel_us, traffic):
+    """The roofline of one kernel: its binding roof is the one whose peak takes
+    longer for the kernel's algorithmic work (HBM bytes at 8 TB/s against
+    MFMA flops at 2.5 PFLOP/s, i.e. arithmetic intensity below or above the
+    ridge of 312 flop/B); both fractions are reported."""
+    sec = kernel_us * 1e-6
+    gbs = nbytes / sec / 1e9
+    tf = flops / sec / 1e12 if flops else 0.0
+    mfma_bound = flops and flops / (MFMA_BF16_PEAK_TFLOPS * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9)
+    r = {"bound": "mfma" if mfma_bound else "hbm", "kernel": kernel,
+         "achieved": tf if mfma_bound else gbs, "peak": MFMA_BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBS,
+         "unit": "TFLOP/s" if mfma_bound else "GB/s"}
+    r["frac"] = r["achieved"] / r["peak"]
+    r["traffic"] = traffic
+    r["algorithmic_bytes"] = nbytes
+    if flops:
+        r["algorithmic_flops"] = flops
+        r["hbm_frac"] = gbs / HBM_PEAK_GBS
+        r["mfma_frac"] = tf / MFMA_BF16_PEAK_TFLOPS
+    r["kernel_us"] = kernel_us
+    return r
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -107,13 +130,18 @@ STAGE_KERNELS_NVFP4 = {
     "routed_gateup": ("k_gateup_nv", ["nvfp4.hip", "gemv_ops.h", "token_ops.h"]),
     "routed_down": ("k_down_nv", ["nvfp4.hip", "gemv_ops.h", "token_ops.h"]),
 }
+# from 128 tokens on the NVFP4 experts run on the grouped MFMA kernels
+STAGE_KERNELS_NVFP4_MFMA = {
+    "routed_gateup": ("k_gateup_mfma<true>", ["grouped_mfma.hip"]),
+    "routed_down": ("k_down_mfma<true>", ["grouped_mfma.hip"]),
+}
 
 
 def stage_kernels(T, workload=""):
     if T is None:   # the packer workload
         return STAGE_KERNELS_PACK
     if workload.startswith("nvfp4"):
-        return STAGE_KERNELS_NVFP4
+        return STAGE_KERNELS_NVFP4_MFMA if T >= GROUPED_MIN_TOKENS else STAGE_KERNELS_NVFP4
     if T <= FUSED_MAX_TOKENS:
         return STAGE_KERNELS_FUSED
     if T >= GROUPED_MIN_TOKENS:
@@ -341,7 +369,10 @@ def bench_nvfp4(a, T):
         "shared_down_combine": 1024 * 2048 * 2 + T * 1024 * 2 + T * 6 * 2048 * 4 + act,
     }
     dom_bytes = stage_bytes.get(dom, 0.0)
-    achieved = dom_bytes / (stage[dom] * 1e-3) / 1e9
+    dom_flops = 0.0
+    if T >= GROUPED_MIN_TOKENS:
+        dom_flops = {"routed_gateup": T * 6 * 2 * 512 * 2048 * 2, "routed_down": T * 6 * 2048 * 512 * 2}.get(dom, 0.0)
+    roof = roofline_entry(dom, dom_bytes, dom_flops, stage[dom] * 1e3, recorded_traffic(a.config, dom, T))
     result = {
         "metric": "routed-MoE layer tokens/s, NVFP4 experts (W4A16)", "value": T / (ms / 1e3), "unit": "tokens/s",
         "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True,
@@ -350,9 +381,7 @@ def bench_nvfp4(a, T):
         "config": {"workload": f"{a.config}: one MoE layer with NVFP4 experts, T={T}, x seed {cfg['x_seed']}, "
                                f"weights seed {cfg['w_seed']}", "T": T, "layers_rotated": n_layers,
                    "touched_experts": n_touched},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(a.config, dom, T),
-                     "algorithmic_bytes": dom_bytes, "kernel_us": stage[dom] * 1e3},
+        "roofline": roof,
         "layer": {"algorithmic_bytes": layer_bytes, "hbm_gbs": layer_bytes / (ms * 1e-3) / 1e9,
                   "hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                   "stage_us": {k: v * 1e3 for k, v in stage.items()}},
@@ -456,16 +485,8 @@ def bench_mlp(a, T):
     ev.close()
     nbytes = m.DENSE_WEIGHTS * 2 + 2 * T * 2048 * 2
     flops = 2 * T * 3 * m.DENSE_INTER * 2048
-    if T >= 128:
-        tf = flops / (call_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "kernel": "dense MLP call (gate/up + down launches)", "achieved": tf,
-                "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS, "traffic": None,
-                "algorithmic_flops": flops, "algorithmic_bytes": nbytes, "kernel_us": call_ms * 1e3}
-    else:
-        gbs = nbytes / (call_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "kernel": "dense MLP call (gate/up + down launches)", "achieved": gbs,
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS, "traffic": None,
-                "algorithmic_bytes": nbytes, "kernel_us": call_ms * 1e3}
+    roof = roofline_entry("dense MLP call (gate/up + down launches)", nbytes, flops if T >= 128 else 0.0,
+                          call_ms * 1e3, None)
     result = {"metric": "dense SwiGLU MLP block (width 6144) tokens/s", "value": T / (ms * 1e-3), "unit": "tokens/s",
               "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True,
               "scaling": "weak", "vs_baseline": None, "dtype": "bf16 x bf16 -> fp32", "data": "synthetic",
@@ -618,9 +639,8 @@ def bench_layer(a, name, steps, warmup, with_cpu):
         stage_bytes["routed_gateup"] = (n_touched * EXPERT_BYTES + SHARED_BYTES + T * 256 * 4 + act
                                         + 2 * T * 1024 * 2 + act)
     dom_bytes = stage_bytes.get(dom, 0.0)
-    achieved = dom_bytes / (stage[dom] * 1e-3) / 1e9
     # from 128 tokens on the routed experts and the shared expert run as MFMA
-    # contractions: their roofline is the fp16/bf16 MFMA peak
+    # contractions: their flops enter the roofline beside their bytes
     stage_flops = {
         "router_shared_gateup": T * (256 + 2 * 1024) * 2048 * 2,
         "routed_gateup": T * 6 * 2 * 512 * 2048 * 2,
@@ -636,17 +656,8 @@ def bench_layer(a, name, steps, warmup, with_cpu):
                    "T": T, "layers_rotated": n_layers, "touched_experts": n_touched},
         "step_us": dist,
     }
-    if T >= GROUPED_MIN_TOKENS:
-        dom_flops = stage_flops.get(dom, 0.0)
-        tf = dom_flops / (stage[dom] * 1e-3) / 1e12
-        result["roofline"] = {"bound": "mfma", "kernel": dom, "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS,
-                              "unit": "TFLOP/s", "frac": tf / MFMA_BF16_PEAK_TFLOPS,
-                              "traffic": recorded_traffic(name, dom, T), "algorithmic_flops": dom_flops,
-                              "algorithmic_bytes": dom_bytes, "kernel_us": stage[dom] * 1e3}
-    else:
-        result["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                              "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(name, dom, T),
-                              "algorithmic_bytes": dom_bytes, "kernel_us": stage[dom] * 1e3}
+    result["roofline"] = roofline_entry(dom, dom_bytes, stage_flops.get(dom, 0.0) if T >= GROUPED_MIN_TOKENS else 0.0,
+                                        stage[dom] * 1e3, recorded_traffic(name, dom, T))
     result["layer"] = {"algorithmic_bytes": layer_bytes, "hbm_gbs": layer_bytes / (ms * 1e-3) / 1e9,
                        "hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                        "tflops": flops / (ms * 1e-3) / 1e12,

@@ -336,8 +336,9 @@ int run_forward_nvfp4(const void *x_, const void *router_w_, const void *codes_,
         NV_STEP(launch_route_small(logits, T, bias, 0, topk_idx, topk_w, offsets, perm, pos, n_active, active, chunks,
                                    n_chunks, error, s));
     } else {
-        // (the rotated x it also writes is not used by NVFP4 experts)
-        NV_STEP(launch_topk_rotate(logits, x, T, bias, 0, topk_idx, topk_w, xt, xt_scale, s));
+        // from 128 tokens on x as natural-order fp16 for the MFMA experts (the
+        // GEMVs below that read x itself)
+        NV_STEP(launch_topk_rotate(logits, x, T, bias, 0, topk_idx, topk_w, xt, xt_scale, s, false));
         if (dense)
             NV_STEP(launch_sort_wide(topk_idx, T, ws_at<int>(ws, L.hist), offsets, perm, pos, n_active, active,
                                      chunks, n_chunks, error, s));
@@ -345,11 +346,22 @@ int run_forward_nvfp4(const void *x_, const void *router_w_, const void *codes_,
             NV_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, error, s));
     }
     NV_MARK();
-    NV_STEP(launch_gateup_nvfp4(codes, scales, tscales, x, perm, active, T, act, s));
-    NV_MARK();
-    NV_MARK();
-    NV_STEP(launch_down_nvfp4(codes, scales, tscales, act, active, T, o, s));
-    NV_MARK();
+    if (dense) {
+        // MFMA tiles over chunks of up to 96 assignments of one expert
+        NV_STEP(launch_gateup_mfma_nvfp4(codes, scales, tscales, xt, xt_scale, perm, chunks, n_chunks, T,
+                                         ws_at<uint32_t>(ws, L.at), ws_at<float>(ws, L.at_scale), s));
+        NV_MARK();
+        NV_MARK();
+        NV_STEP(launch_down_mfma_nvfp4(codes, scales, tscales, ws_at<uint32_t>(ws, L.at), ws_at<float>(ws, L.at_scale),
+                                       chunks, n_chunks, T, o, s));
+        NV_MARK();
+    } else {
+        NV_STEP(launch_gateup_nvfp4(codes, scales, tscales, x, perm, active, T, act, s));
+        NV_MARK();
+        NV_MARK();
+        NV_STEP(launch_down_nvfp4(codes, scales, tscales, act, active, T, o, s));
+        NV_MARK();
+    }
     if (dense) {
         NV_STEP(launch_shared_down_dense(shared_w, hs, T, z, s));
         NV_STEP(launch_combine(z, topk_w, pos, o, T, y, s));

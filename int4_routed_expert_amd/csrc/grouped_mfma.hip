@@ -30,6 +30,17 @@
 // Work mapping: workgroups are dealt to the 8 XCDs round robin, so the tiles
 // of one chunk are given consecutive per-XCD slots and share that XCD's L2
 // for the chunk's activations.
+//
+// The same two kernels serve the NVFP4 experts (template argument NV; Flint
+// NVFP4 repack, kekzle/Flint-NVFP4, rows "Layout per Linear" and
+// "Declaration": E2M1 codes two per byte in the int4 layout's rows, one E4M3
+// scale per 16 of K, one fp32 tensor scale per Linear, W4A16, original
+// basis).  Eight codes become four exact fp16 pairs by the gfx950 FP4 convert
+// instruction (natural order), times their block's E4M3 scale in fp16 (exact:
+// at most 6 significant bits, never below the fp16 normal range); the
+// activations are natural-order fp16 (no Hadamard); the tensor scale is
+// applied to the fp32 sums; gate/up writes a without a rotation and down
+// writes fp32 expert rows.
 #include "common.h"
 #include "launch.h"
 
@@ -184,10 +195,33 @@ constexpr int kGuBuf = kChunkRows * 256;   // one A block: 96 rows x 128 fp16
 constexpr int kGuRing = 3;
 constexpr int kGuCodeRing = 4;
 
+// NVFP4 block scales of an expert: gate [512][128], up [512][128], down [2048][32] bytes
+constexpr uint32_t kNvScGate = (uint32_t)kI * kH / 16;
+constexpr uint32_t kNvScGu = 2 * kNvScGate;
+constexpr uint32_t kNvScPerExpert = kNvScGu + (uint32_t)kH * kI / 16;
+
+// Eight E2M1 codes (element 2b in the low nibble of byte b) times one fp16
+// scale (both halves): the B operand (c0 s, c1 s, ..., c7 s), exact.
+__device__ __forceinline__ uint4 nv_codes_to_f16(uint32_t w, half2_t s) {
+    uint4 r;
+    r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s);
+    r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s);
+    r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s);
+    r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s);
+    return r;
+}
+// Byte i of four E4M3 scales -> fp16 pair (exact).
+__device__ __forceinline__ half2_t e4m3_half2(uint32_t w, int i) {
+    const _Float16 h = (_Float16)e4m3_to_f32((w >> (8 * i)) & 0xffu);
+    return half2_t{h, h};
+}
+
+template <bool NV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gateup_mfma(
-    const uint8_t *__restrict__ codes, const uint16_t *__restrict__ scales, const uint32_t *__restrict__ xt,
-    const float *__restrict__ xt_scale, const int *__restrict__ perm, const int4 *__restrict__ chunks,
-    const int *__restrict__ n_chunks, uint32_t *__restrict__ at, float *__restrict__ at_scale) {
+    const uint8_t *__restrict__ codes, const void *__restrict__ scales_, const float *__restrict__ tscales,
+    const uint32_t *__restrict__ xt, const float *__restrict__ xt_scale, const int *__restrict__ perm,
+    const int4 *__restrict__ chunks, const int *__restrict__ n_chunks, uint32_t *__restrict__ at,
+    float *__restrict__ at_scale) {
     // three separate arrays rather than one: the compiler then knows that a
     // block's reads do not alias the direct loads in flight into the other two
     // slots and does not wait for those loads before every LDS read
@@ -207,16 +241,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     // this lane's gate and up rows
     const int gr = kG * nt + 32 * wave + n;
     const __amdgpu_buffer_rsrc_t cres = make_buf(codes + (size_t)e * kCodeBytesPerExpert, (uint32_t)kCodeBytesGu);
-    const __amdgpu_buffer_rsrc_t sres = make_buf(scales + (size_t)e * kScalesPerExpert, (uint32_t)kScalesGu * 2);
+    const uint16_t *scales = static_cast<const uint16_t *>(scales_);
+    const uint8_t *nv_scales = static_cast<const uint8_t *>(scales_);
+    const __amdgpu_buffer_rsrc_t sres =
+        NV ? make_buf(nv_scales + (size_t)e * kNvScPerExpert, kNvScGu)
+           : make_buf(scales + (size_t)e * kScalesPerExpert, (uint32_t)kScalesGu * 2);
     const uint32_t goff = (uint32_t)gr * (kH / 2) + 32 * g, uoff = goff + (uint32_t)kPlaneGateBytes;
     const uint32_t gsoff = (uint32_t)gr * 32, usoff = gsoff + (uint32_t)kScalesGate * 2;
+    // NVFP4: the lane's four E4M3 scales of a block (16-blocks 8 blk + 4 g ..)
+    const uint32_t nsg = (uint32_t)gr * (kH / 16) + 4 * g, nsu = nsg + kNvScGate;
     uint4 cb[kGuCodeRing][4];
+    uint32_t csg[kGuCodeRing], csu[kGuCodeRing];
+    constexpr int kFetchLoads = NV ? 6 : 4;   // loads of one fetch
     auto fetch = [&](int slot, int blk) {
         const uint32_t o = (uint32_t)blk * 64;
         cb[slot][0] = bload16(cres, goff + o, 0);
         cb[slot][1] = bload16(cres, goff + o + 16, 0);
         cb[slot][2] = bload16(cres, uoff + o, 0);
         cb[slot][3] = bload16(cres, uoff + o + 16, 0);
+        if constexpr (NV) {
+            csg[slot] = bload4(sres, nsg + 8 * blk, 0);
+            csu[slot] = bload4(sres, nsu + 8 * blk, 0);
+        }
     };
     // the codes and scales depend only on the expert: requested before the
     // chunk's tokens are looked up.  Issue order: codes(0..2), scales, then
@@ -229,10 +275,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     fetch(2, 2);
     // the 16 block scales of the gate row and of the up row (bf16)
     uint4 sg[2], su[2];
-    sg[0] = bload16(sres, gsoff, 0);
-    sg[1] = bload16(sres, gsoff + 16, 0);
-    su[0] = bload16(sres, usoff, 0);
-    su[1] = bload16(sres, usoff + 16, 0);
+    if constexpr (!NV) {
+        sg[0] = bload16(sres, gsoff, 0);
+        sg[1] = bload16(sres, gsoff + 16, 0);
+        su[0] = bload16(sres, usoff, 0);
+        su[1] = bload16(sres, usoff + 16, 0);
+    }
     __builtin_amdgcn_sched_barrier(0);
     if (tid < kChunkRows) row_p[tid] = xt_scale[perm[row0 + min(tid, rows - 1)] / kTopK];
 
@@ -263,7 +311,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     issue_a(0, 0);
     issue_a(1, 1);
     __builtin_amdgcn_sched_barrier(0);
-    const int kg = scale_shift(sg[0], sg[1]), ku = scale_shift(su[0], su[1]);
+    const int kg = NV ? 0 : scale_shift(sg[0], sg[1]), ku = NV ? 0 : scale_shift(su[0], su[1]);
     wait_vmcnt_lds<NI>();   // A(0) and the row_p stores done (A(1) may be in flight)
     block_barrier();
 
@@ -281,14 +329,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         if (b + 3 < kBlocks) fetch((b + 3) % kGuCodeRing, b + 3);
         if (b + 2 < kBlocks) issue_a((b + 2) % kGuRing, b + 2);
         __builtin_amdgcn_sched_barrier(0);
-        const half2_t s_g = scaled_half2(word(sg[b >> 3], (b >> 1) & 3), b & 1, kg);
-        const half2_t s_u = scaled_half2(word(su[b >> 3], (b >> 1) & 3), b & 1, ku);
+        half2_t s_g, s_u, ng[4], nu[4];
+        if constexpr (NV) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                ng[i] = e4m3_half2(csg[cs], i);
+                nu[i] = e4m3_half2(csu[cs], i);
+            }
+        } else {
+            s_g = scaled_half2(word(sg[b >> 3], (b >> 1) & 3), b & 1, kg);
+            s_u = scaled_half2(word(su[b >> 3], (b >> 1) & 3), b & 1, ku);
+        }
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint4 bg = codes_to_f16_scaled(word(cb[cs][q], j), s_g);
-                const uint4 bu = codes_to_f16_scaled(word(cb[cs][2 + q], j), s_u);
+                // 8-group 8g + 4q + j of the block: NVFP4 16-block 4g + 2q + j/2
+                const uint4 bg = NV ? nv_codes_to_f16(word(cb[cs][q], j), ng[2 * q + (j >> 1)])
+                                    : codes_to_f16_scaled(word(cb[cs][q], j), s_g);
+                const uint4 bu = NV ? nv_codes_to_f16(word(cb[cs][2 + q], j), nu[2 * q + (j >> 1)])
+                                    : codes_to_f16_scaled(word(cb[cs][2 + q], j), s_u);
                 const int grp = 8 * g + 4 * q + j;
 #pragma unroll
                 for (int h = 0; h < MT; ++h) {
@@ -303,7 +363,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         // next block; after A(b+1) only codes(b+3) and A(b+2) were issued
         __builtin_amdgcn_sched_barrier(0);
         if (b + 3 < kBlocks)
-            wait_vmcnt<4 + NI>();
+            wait_vmcnt<kFetchLoads + NI>();
         else if (b + 2 < kBlocks)
             wait_vmcnt<NI>();
         else if (b + 1 < kBlocks)
@@ -312,7 +372,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
     mfma_drain();
     __syncthreads();
-    const float gscale = ldexpf(1.0f, -kg), uscale = ldexpf(1.0f, -ku);
+    const float gscale = NV ? tscales[3 * e] : ldexpf(1.0f, -kg);
+    const float uscale = NV ? tscales[3 * e + 1] : ldexpf(1.0f, -ku);
 #pragma unroll
     for (int h = 0; h < MT; ++h)
 #pragma unroll
@@ -326,7 +387,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     });
     __syncthreads();
 
-    // fwht128 of each row: 16 lanes per row, 8 values per lane, 4 rows per pass
+    // fwht128 of each row (int4 experts; NVFP4 ones keep a in the original
+    // basis): 16 lanes per row, 8 values per lane, 4 rows per pass
     const int rl = lane & 15;
     for (int r0 = 4 * wave; r0 < 32 * n_mt; r0 += 16) {
         const int m = r0 + (lane >> 4);
@@ -334,7 +396,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         const float4 a0 = sp[0], a1 = sp[1];
         float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
-        for (int hs = 1; hs < 8; hs <<= 1)
+        for (int hs = 1; hs < (NV ? 1 : 8); hs <<= 1)
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 if ((i & hs) == 0) {
@@ -343,7 +405,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                     v[i + hs] = x0 - x1;
                 }
 #pragma unroll
-        for (int msk = 1; msk <= 8; msk <<= 1) {   // strides 8..64 across the row's 16 lanes
+        for (int msk = 1; msk <= (NV ? 0 : 8); msk <<= 1) {   // strides 8..64 across the row's 16 lanes
             const bool upper = (lane & msk) != 0;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -354,7 +416,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         float amax = 0.0f;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            v[i] *= 0.08838834764831845f;   // 1/sqrt(128)
+            if (!NV) v[i] *= 0.08838834764831845f;   // 1/sqrt(128)
             amax = fmaxf(amax, fabsf(v[i]));
         }
 #pragma unroll
@@ -367,10 +429,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         }
         if (m < rows) {
             uint4 w;
-            w.x = pack_half2(ldexpf(v[0], -sh), ldexpf(v[4], -sh));
-            w.y = pack_half2(ldexpf(v[1], -sh - 4), ldexpf(v[5], -sh - 4));
-            w.z = pack_half2(ldexpf(v[2], -sh), ldexpf(v[6], -sh));
-            w.w = pack_half2(ldexpf(v[3], -sh - 4), ldexpf(v[7], -sh - 4));
+            if (NV) {   // natural order, the order of the E2M1 conversion
+                w.x = pack_half2(ldexpf(v[0], -sh), ldexpf(v[1], -sh));
+                w.y = pack_half2(ldexpf(v[2], -sh), ldexpf(v[3], -sh));
+                w.z = pack_half2(ldexpf(v[4], -sh), ldexpf(v[5], -sh));
+                w.w = pack_half2(ldexpf(v[6], -sh), ldexpf(v[7], -sh));
+            } else {    // the operand order of int4x8_to_q
+                w.x = pack_half2(ldexpf(v[0], -sh), ldexpf(v[4], -sh));
+                w.y = pack_half2(ldexpf(v[1], -sh - 4), ldexpf(v[5], -sh - 4));
+                w.z = pack_half2(ldexpf(v[2], -sh), ldexpf(v[6], -sh));
+                w.w = pack_half2(ldexpf(v[3], -sh - 4), ldexpf(v[7], -sh - 4));
+            }
             const size_t p = (size_t)(row0 + m);
             reinterpret_cast<uint4 *>(at + p * (kI / 2) + nt * (kG / 2))[rl] = w;
             if (rl == 0) at_scale[p * (kI / kG) + nt] = ldexpf(1.0f, sh);
@@ -406,13 +475,15 @@ constexpr int kDnHalves = 2;     // wave groups of the workgroup, each over half
 constexpr int kDnTiles = kH / 128 / kDnHalves;
 constexpr int kDnCodeRing = 2;
 
-__global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu(2))) void k_down_mfma(const uint8_t *__restrict__ codes,
-                                                   const uint16_t *__restrict__ scales,
-                                                   const uint32_t *__restrict__ at,
-                                                   const float *__restrict__ at_scale,
-                                                   const int4 *__restrict__ chunks,
-                                                   const int *__restrict__ n_chunks, uint16_t *__restrict__ o,
-                                                   float *__restrict__ o_scale) {
+// NVFP4 (NV): no scale normalisation; each lane's four E4M3 scales of a
+// block come with its codes, and o is written as fp32 rows (o_scale unused).
+template <bool NV>
+__global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu(2))) void k_down_mfma(
+    const uint8_t *__restrict__ codes, const void *__restrict__ scales_, const float *__restrict__ tscales,
+    const uint32_t *__restrict__ at, const float *__restrict__ at_scale, const int4 *__restrict__ chunks,
+    const int *__restrict__ n_chunks, void *__restrict__ o_, float *__restrict__ o_scale) {
+    const uint16_t *scales = static_cast<const uint16_t *>(scales_);
+    uint16_t *o = static_cast<uint16_t *>(o_);
     __shared__ __attribute__((aligned(16))) uint8_t lds[kChunkRows * kDnPitch];
     __shared__ float fk_wave[4];                                              // largest 2^-k per wave
     __shared__ float row_p[kChunkRows];                                       // per token
@@ -432,13 +503,21 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
     // the feature whose codes this lane loads, in tile 0 of its half
     const int fh = half * (kH / kDnHalves);
     const int f0 = fh + 32 * wave + n;
+    const __amdgpu_buffer_rsrc_t nsres =
+        make_buf(static_cast<const uint8_t *>(scales_) + (size_t)e * kNvScPerExpert + kNvScGu, kH * kI / 16);
     uint4 cb[kDnCodeRing][8];
+    uint32_t cs4[kDnCodeRing][4];   // NVFP4: the lane's four E4M3 scales of each block
     auto fetch = [&](int slot, int tile) {
         const uint32_t off = (uint32_t)(f0 + 128 * tile) * (kI / 2) + 32 * g;
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             cb[slot][2 * b] = bload16(cres, off + 64 * b, 0);
             cb[slot][2 * b + 1] = bload16(cres, off + 64 * b + 16, 0);
+        }
+        if constexpr (NV) {
+            const uint32_t so = (uint32_t)(f0 + 128 * tile) * (kI / 16) + 4 * g;
+#pragma unroll
+            for (int b = 0; b < 4; ++b) cs4[slot][b] = bload4(nsres, so + 8 * b, 0);
         }
     };
     // the chunk's activations are needed first: thread -> (row, part), load
@@ -458,7 +537,7 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
     }
     // the expert's down scales: thread t < 256 takes features 8t..8t+7
     uint4 s4[4];
-    if (tid < 256) {
+    if (!NV && tid < 256) {
         const uint4 *src = reinterpret_cast<const uint4 *>(scales + (size_t)e * kScalesPerExpert + kScalesGu) + 4 * tid;
 #pragma unroll
         for (int i = 0; i < 4; ++i) s4[i] = src[i];
@@ -470,7 +549,7 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
 
     // the down scales transposed to [block][feature], and each feature's
     // normalisation
-    if (tid < 256) {
+    if (!NV && tid < 256) {
         const uint32_t w[16] = {s4[0].x, s4[0].y, s4[0].z, s4[0].w, s4[1].x, s4[1].y, s4[1].z, s4[1].w,
                                 s4[2].x, s4[2].y, s4[2].z, s4[2].w, s4[3].x, s4[3].y, s4[3].z, s4[3].w};
         // feature f = 8t + k holds blocks 0,1 in w[2k] and 2,3 in w[2k+1]
@@ -522,11 +601,14 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
     // o rows of the chunk (fp16) through a buffer descriptor: stores of rows
     // past the chunk's end fall outside it and are dropped by the hardware
     // bounds check
-    const __amdgpu_buffer_rsrc_t ores = make_buf(o + (size_t)row0 * kH, (uint32_t)rows * kH * 2);
-    float fkmax = fmaxf(fmaxf(fk_wave[0], fk_wave[1]), fmaxf(fk_wave[2], fk_wave[3]));
+    const __amdgpu_buffer_rsrc_t ores =
+        NV ? make_buf(static_cast<float *>(o_) + (size_t)row0 * kH, (uint32_t)rows * kH * 4)
+           : make_buf(o + (size_t)row0 * kH, (uint32_t)rows * kH * 2);
+    float fkmax = NV ? 1.0f : fmaxf(fmaxf(fk_wave[0], fk_wave[1]), fmaxf(fk_wave[2], fk_wave[3]));
     if (fkmax == 0.0f) fkmax = 1.0f;   // every scale of the expert is zero: o is 0
     const float to_half = 0x1p-20f / fkmax;   // a power of two
-    if (tid < rows) o_scale[row0 + tid] = row_p[tid] * fkmax * 0x1p20f;
+    if (!NV && tid < rows) o_scale[row0 + tid] = row_p[tid] * fkmax * 0x1p20f;
+    const float tsd = NV ? tscales[3 * e + 2] : 1.0f;
 
     // unrolled by the ring size, so ring slots are compile-time; the fetch
     // index is clamped (the last tiles re-read the last tile, in bounds) so
@@ -542,13 +624,21 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
         const uint32_t zero = opaque(0);
         const uint8_t *abase = lds + zero;
         // this lane's codes feature and its normalised scales, as fp16 pairs
+        // (NVFP4: the four E4M3 scales of each block, exact in fp16)
         const int fl = f0 + 128 * t;
-        const int kf = -ilogbf(fk[fl + zero]);
-        half2_t s2[4];
+        half2_t s2[4], ns[4][4];
+        if constexpr (NV) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const _Float16 h = (_Float16)ldexpf(bf16_to_f32(sc[b][fl + zero]), kf);
-            s2[b] = half2_t{h, h};
+            for (int b = 0; b < 4; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ns[b][i] = e4m3_half2(cs4[cs][b], i);
+        } else {
+            const int kf = -ilogbf(fk[fl + zero]);
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                const _Float16 h = (_Float16)ldexpf(bf16_to_f32(sc[b][fl + zero]), kf);
+                s2[b] = half2_t{h, h};
+            }
         }
         f32x16_t acc[MT];
 #pragma unroll
@@ -567,7 +657,9 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
         };
         auto slice_b = [&](int ks) -> uint4 {
             const int b = ks >> 3, q = (ks >> 2) & 1, j = ks & 3;
-            return codes_to_f16_scaled(word(cb[cs][2 * b + q], j), s2[b]);
+            // NVFP4: 8-group 16b + 8g + 4q + j, 16-block 8b + 4g + 2q + j/2
+            return NV ? nv_codes_to_f16(word(cb[cs][2 * b + q], j), ns[b][2 * q + (j >> 1)])
+                      : codes_to_f16_scaled(word(cb[cs][2 * b + q], j), s2[b]);
         };
         uint4 a_cur[MT], a_nxt[MT];
         slice_a(0, a_cur);
@@ -589,6 +681,22 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
         mfma_drain();
         // lane: token 32h + n, features 128t + 32w + 8q + 4g + 0..3 in acc[h][4q..4q+3]
         const int fb = fh + 128 * t + 32 * wave + 4 * g;
+        if constexpr (NV) {
+            // fp32 rows: acc times the tensor scale and the row's prescale
+#pragma unroll
+            for (int h = 0; h < MT; ++h) {
+                const float mlt = tsd * row_p[min(32 * h + n, kChunkRows - 1)];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const u32x4_t v = {__float_as_uint(acc[h][4 * q] * mlt), __float_as_uint(acc[h][4 * q + 1] * mlt),
+                                       __float_as_uint(acc[h][4 * q + 2] * mlt),
+                                       __float_as_uint(acc[h][4 * q + 3] * mlt)};
+                    __builtin_amdgcn_raw_buffer_store_b128(v, ores, (uint32_t)((32 * h + n) * kH + fb + 8 * q) * 4, 0,
+                                                           0);
+                }
+            }
+            continue;
+        }
         float4 kq[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) kq[q] = *reinterpret_cast<const float4 *>(&fk[fb + 8 * q + zero]);
@@ -620,14 +728,32 @@ static int grid_for(int T, int tiles) {
 void launch_gateup_mfma(const uint8_t *codes, const uint16_t *scales, const uint32_t *xt, const float *xt_scale,
                         const int *perm, const int *chunks, const int *n_chunks, int T, uint32_t *at,
                         float *at_scale, hipStream_t s) {
-    hipLaunchKernelGGL(k_gateup_mfma, dim3(grid_for(T, kI / kG)), dim3(256), 0, s, codes, scales, xt, xt_scale,
-                       perm, reinterpret_cast<const int4 *>(chunks), n_chunks, at, at_scale);
+    hipLaunchKernelGGL(k_gateup_mfma<false>, dim3(grid_for(T, kI / kG)), dim3(256), 0, s, codes,
+                       static_cast<const void *>(scales), nullptr, xt, xt_scale, perm,
+                       reinterpret_cast<const int4 *>(chunks), n_chunks, at, at_scale);
 }
 
 void launch_down_mfma(const uint8_t *codes, const uint16_t *scales, const uint32_t *at, const float *at_scale,
                       const int *chunks, const int *n_chunks, int T, uint16_t *o, float *o_scale, hipStream_t s) {
-    hipLaunchKernelGGL(k_down_mfma, dim3(grid_for(T, 1)), dim3(256 * kDnHalves), 0, s, codes, scales, at, at_scale,
-                       reinterpret_cast<const int4 *>(chunks), n_chunks, o, o_scale);
+    hipLaunchKernelGGL(k_down_mfma<false>, dim3(grid_for(T, 1)), dim3(256 * kDnHalves), 0, s, codes,
+                       static_cast<const void *>(scales), nullptr, at, at_scale,
+                       reinterpret_cast<const int4 *>(chunks), n_chunks, static_cast<void *>(o), o_scale);
+}
+
+void launch_gateup_mfma_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscales, const uint32_t *xn,
+                              const float *xn_scale, const int *perm, const int *chunks, const int *n_chunks, int T,
+                              uint32_t *an, float *an_scale, hipStream_t s) {
+    hipLaunchKernelGGL(k_gateup_mfma<true>, dim3(grid_for(T, kI / kG)), dim3(256), 0, s, codes,
+                       static_cast<const void *>(scales), tscales, xn, xn_scale, perm,
+                       reinterpret_cast<const int4 *>(chunks), n_chunks, an, an_scale);
+}
+
+void launch_down_mfma_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscales, const uint32_t *an,
+                            const float *an_scale, const int *chunks, const int *n_chunks, int T, float *o,
+                            hipStream_t s) {
+    hipLaunchKernelGGL(k_down_mfma<true>, dim3(grid_for(T, 1)), dim3(256 * kDnHalves), 0, s, codes,
+                       static_cast<const void *>(scales), tscales, an, an_scale,
+                       reinterpret_cast<const int4 *>(chunks), n_chunks, static_cast<void *>(o), nullptr);
 }
 
 }  // namespace moe_w4

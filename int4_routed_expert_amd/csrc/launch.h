@@ -123,6 +123,18 @@ void launch_gateup_mfma(const uint8_t *codes, const uint16_t *scales, const uint
 void launch_down_mfma(const uint8_t *codes, const uint16_t *scales, const uint32_t *at, const float *at_scale,
                       const int *chunks, const int *n_chunks, int T, uint16_t *o, float *o_scale, hipStream_t s);
 
+// The same two kernels for NVFP4 experts (E2M1 codes, E4M3 scales per 16 of
+// K, fp32 tensor scales [256][3]; original basis): xn, xn_scale are x as
+// natural-order fp16 with a per-token prescale (launch_topk_rotate with rotate
+// = false); gate/up writes a (an, an_scale) in natural order without a
+// rotation; down writes fp32 rows o [6T][2048].
+void launch_gateup_mfma_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscales, const uint32_t *xn,
+                              const float *xn_scale, const int *perm, const int *chunks, const int *n_chunks, int T,
+                              uint32_t *an, float *an_scale, hipStream_t s);
+void launch_down_mfma_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscales, const uint32_t *an,
+                            const float *an_scale, const int *chunks, const int *n_chunks, int T, float *o,
+                            hipStream_t s);
+
 // Shared expert down projection fused with the combine:
 // y = bf16(h Wsd^T + sum_j w_j o[pos[6t+j]]), slots in order.
 void launch_shared_down_combine(const uint16_t *shared_w, const uint16_t *hs, int T, const float *topk_w,

@@ -40,15 +40,6 @@ __device__ __forceinline__ void e2m1x8_to_half(uint32_t w, uint32_t (&h)[4]) {
     h[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3));
 }
 
-// E4M3 byte -> fp32 (exact): sign, 4 exponent bits (bias 7), 3 mantissa bits,
-// exponent 0 subnormal (m * 2^-9), S.1111.111 NaN.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-    float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-    if (e == 15u && m == 7u) mag = __uint_as_float(0x7fc00000u);
-    return (b & 0x80u) ? -mag : mag;
-}
-
 // One lane's 32 codes (word i: elements 8i .. 8i + 7) as fp16 pairs
 // h[4i + b] = (value 8i + 2b, value 8i + 2b + 1).
 __device__ __forceinline__ void conv32_nv(const uint4 c, uint32_t (&h)[16]) {

@@ -151,3 +151,55 @@ def test_nvfp4_deterministic(m, layer0, nv):
     a = P.run_gpu(m, x_bits, layer0, nvfp4=nv)["y_bits"]
     b = P.run_gpu(m, x_bits, layer0, nvfp4=nv, poison=True)["y_bits"]
     np.testing.assert_array_equal(a, b)
+
+
+# ------------------------------------------------- MFMA form (from 128 tokens)
+def test_nvfp4_mfma_large_scales_and_determinism(m, layer0, nv):
+    """The MFMA form with every block scale 2^8 times larger (expert outputs
+    ~10^4 times the shared expert's), all rows; then twice more on a poisoned
+    workspace, bit for bit."""
+    T = 160
+    print("[nvfp4] case MFMA large scales", flush=True)
+    big = (host_scales() + np.uint8(0x40)).astype(np.uint8)
+    x_bits = synth.gen_x(17, T)
+    dev = dict(nv, scales=torch.from_numpy(big.ravel().copy()).cuda())
+    gpu = P.run_gpu(m, x_bits, layer0, nvfp4=dev)
+    report("MFMA large scales", P.compare(gpu, oracle(x_bits, scales=big), label="nvfp4 MFMA large scales"))
+    again = P.run_gpu(m, x_bits, layer0, nvfp4=dev, poison=True)
+    np.testing.assert_array_equal(gpu["y_bits"], again["y_bits"])
+
+
+def test_nvfp4_mfma_zero_codes_and_nan_scale(m, layer0, nv):
+    T = 140
+    print("[nvfp4] case MFMA zero codes / NaN scale", flush=True)
+    x_bits = synth.gen_x(18, T)
+    zero = dict(nv, codes=torch.zeros_like(nv["codes"]))
+    gpu = P.run_gpu(m, x_bits, layer0, nvfp4=zero)
+    ref = oracle(x_bits, zero_codes=True)
+    P.compare(gpu, ref, label="nvfp4 MFMA zero codes")
+    # a NaN in one block scale of one down row of the first token's first expert
+    e_bad = int(ref["topk_idx"][0, 0])
+    sc = host_scales().copy()
+    d0 = 2 * O.I_R * O.H // O.NV_BLOCK
+    sc[e_bad, d0 + 77 * (O.I_R // O.NV_BLOCK) + 5] = 0x7F
+    dev = dict(nv, scales=torch.from_numpy(sc.ravel().copy()).cuda())
+    g = P.run_gpu(m, x_bits, layer0, nvfp4=dev)
+    y = O.bf16_to_f64(g["y_bits"])
+    hit = np.any(g["topk_idx"] == e_bad, axis=1)
+    assert hit[0]
+    assert np.all(np.isnan(y[hit, 77]))            # only the poisoned feature of its tokens
+    assert np.all(np.isfinite(y[hit][:, np.arange(2048) != 77]))
+    assert np.all(np.isfinite(y[~hit]))
+
+
+def test_nvfp4_mfma_hot_expert_chunks(m, layer0, nv):
+    """One expert takes all 200 tokens: chunks of 96, 96 and 8 rows."""
+    T = 200
+    print("[nvfp4] case MFMA hot expert", flush=True)
+    x_bits = synth.gen_x(19, T)
+    bias = np.zeros(256, dtype=np.float32)
+    bias[40] = 100.0
+    g = P.run_gpu(m, x_bits, layer0, bias=bias, nvfp4=nv)
+    assert np.all(g["topk_idx"][:, 0] == 40)
+    ref = O.moe_layer_nvfp4(x_bits, P.host_router(SEED), blobs(), P.host_shared(SEED), bias=bias, pool=P.pool())
+    report("MFMA hot expert", P.compare(g, ref, label="nvfp4 MFMA hot expert"))
