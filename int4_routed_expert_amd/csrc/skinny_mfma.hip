@@ -34,6 +34,7 @@ namespace moe_w4 {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 enum { kEpiStoreF32 = 0, kEpiSwiglu = 1, kEpiCombine = 2, kEpiStoreBf16 = 3 };
 
@@ -82,7 +83,23 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 template <int MT, int KS, int KB, int CW, bool ROUTE>
 __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__ A, int M, SkinnyJobs jobs) {
     constexpr int K = 128 * KS * KB;
-    __shared__ f32x4_t red[KS][MT][64];
+    // Activations through LDS (KB <= 2): each wave stages its own K slice of
+    // the token tiles with whole-line direct loads (one wave instruction reads
+    // 1 KiB: 4 / KB rows x KB * 256 contiguous bytes) and reads the MFMA
+    // operands back from LDS.  Loading them straight into the operand layout
+    // (16 rows x 64 bytes per instruction) runs ~3.5x slower per CU, and every
+    // workgroup reads all of x.  Slot P of row R holds 16-byte chunk
+    // P ^ (R & 15) of the row's slice, so the 16 rows of an operand read hit
+    // 16 different 4-bank groups.  The reduction buffer reuses the wave's own
+    // staging area.  KB = 6 (the dense block's down projection) would not fit:
+    // it loads the operands directly.
+    constexpr bool kLds = KB <= 2;
+    constexpr int kRowBytes = KB * 256;              // one token's K slice of one wave
+    constexpr int kTileBytes = 16 * kRowBytes;
+    constexpr int kWaveBytes = kLds ? MT * kTileBytes : MT * 64 * 16;
+    static_assert(!kLds || kWaveBytes >= MT * 64 * 16, "the reduction fits the staging area");
+    __shared__ __attribute__((aligned(16))) uint8_t xs[KS][kWaveBytes];
+    auto red_at = [&](int w, int t) -> f32x4_t * { return reinterpret_cast<f32x4_t *>(xs[w]) + t * 64; };
     if (ROUTE && blockIdx.x == 0) {
         route_small_block<KS>(jobs.route);
         return;
@@ -156,19 +173,53 @@ __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__
         f32x4_t acc[MT];
 #pragma unroll
         for (int t = 0; t < MT; ++t) acc[t] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (kLds) {
+            // instruction i of tile t: rows 4i/KB + l / (16 KB) of the tile, slot l % (16 KB)
+            constexpr int kCpr = KB * 16, kRpi = 4 / KB, kInstr = 16 / kRpi;
+            const int rr = lane / kCpr, slot = lane % kCpr;
 #pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            const int m = min(m0 + 16 * t + r, M - 1);
-            const uint4 *ap = reinterpret_cast<const uint4 *>(A + (size_t)m * K + k_begin + 8 * g);
-            uint4 a[KB][4];
+            for (int t = 0; t < MT; ++t)
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+                for (int i = 0; i < kInstr; ++i) {
+                    const int R = kRpi * i + rr;
+                    const int m = min(m0 + 16 * t + R, M - 1);
+                    const uint16_t *src = A + (size_t)m * K + k_begin + 8 * (slot ^ (R & 15));
+                    __builtin_amdgcn_global_load_lds(src, (lds_void_t *)(xs[wave] + t * kTileBytes + i * 1024), 16,
+                                                     0, 0);
+                }
+            __builtin_amdgcn_s_waitcnt(0);   // the staged rows (and the weights) have arrived
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int s = 0; s < 4; ++s) a[kb][s] = ap[16 * kb + 4 * s];
+            for (int t = 0; t < MT; ++t) {
+                uint4 a[KB][4];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+                for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-                for (int s = 0; s < 4; ++s) acc[t] = mfma16(a[kb][s], b[kb][s], acc[t]);
+                    for (int s = 0; s < 4; ++s) {
+                        const int c = 16 * kb + 4 * s + g;
+                        a[kb][s] = *reinterpret_cast<const uint4 *>(xs[wave] + t * kTileBytes + r * kRowBytes +
+                                                                    16 * (c ^ r));
+                    }
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) acc[t] = mfma16(a[kb][s], b[kb][s], acc[t]);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                const int m = min(m0 + 16 * t + r, M - 1);
+                const uint4 *ap = reinterpret_cast<const uint4 *>(A + (size_t)m * K + k_begin + 8 * g);
+                uint4 a[KB][4];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) a[kb][s] = ap[16 * kb + 4 * s];
+#pragma unroll
+                for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) acc[t] = mfma16(a[kb][s], b[kb][s], acc[t]);
+            }
         }
         // The accumulators are read right after the last MFMA; give the MFMA
         // pipeline its wait states explicitly (the hazard is not always
@@ -176,13 +227,13 @@ __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__
         __builtin_amdgcn_sched_barrier(0);
         asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3" ::: "memory");
 #pragma unroll
-        for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
+        for (int t = 0; t < MT; ++t) red_at(wave, t)[lane] = acc[t];
         __syncthreads();
         // wave t (< MT) finishes token tile t; lanes with r < CW own the columns
         for (int t = wave; t < MT; t += KS) {
-            f32x4_t sum = red[0][t][lane];
+            f32x4_t sum = red_at(0, t)[lane];
 #pragma unroll
-            for (int w = 1; w < KS; ++w) sum += red[w][t][lane];
+            for (int w = 1; w < KS; ++w) sum += red_at(w, t)[lane];
             // lane holds rows m0 + 16t + 4g + i of column c0 + c
             if (epi == kEpiStoreBf16) {
                 uint16_t *o = static_cast<uint16_t *>(J.out);
@@ -244,10 +295,8 @@ static void launch_skinny_k(const uint16_t *A, int M, const SkinnyJobs &jobs, hi
         block(64 * KS);
     if (M <= 16)
         hipLaunchKernelGGL((k_skinny<1, KS, KB, CW, ROUTE>), grid, block, 0, s, A, M, jobs);
-    else if (M <= 32)
-        hipLaunchKernelGGL((k_skinny<2, KS, KB, CW, ROUTE>), grid, block, 0, s, A, M, jobs);
     else
-        hipLaunchKernelGGL((k_skinny<4, KS, KB, CW, ROUTE>), grid, block, 0, s, A, M, jobs);
+        hipLaunchKernelGGL((k_skinny<2, KS, KB, CW, ROUTE>), grid, block, 0, s, A, M, jobs);
 }
 
 static SkinnyJob no_job() { return SkinnyJob{nullptr, 0, 0, 0, kEpiStoreF32, nullptr, nullptr, 0, nullptr, nullptr, nullptr}; }
