@@ -99,7 +99,8 @@ def parse():
 
 # stage -> (kernel name prefix, sources that define it) for the HBM-traffic
 # record, per launch sequence (1-8 tokens: two launches; 9-127: GEMVs, the
-# routing in one workgroup up to 48 tokens; from 128: MFMA tiles)
+# routing in one launch of one workgroup per 8 tokens up to 48 tokens; from
+# 128: MFMA tiles)
 FUSED_MAX_TOKENS = 8
 ROUTE_SMALL_MAX_TOKENS = 48
 GROUPED_MIN_TOKENS = 128
@@ -147,8 +148,9 @@ def stage_kernels(T, workload=""):
     if T >= GROUPED_MIN_TOKENS:
         return STAGE_KERNELS_GROUPED
     if T <= ROUTE_SMALL_MAX_TOKENS:
-        # the router (+ rotation of x), then the shared gate/up beside the routing
-        return dict(STAGE_KERNELS_GEMV, topk_sort=("k_skinny", ["skinny_mfma.hip", "route_small.h", "token_ops.h"]))
+        # the router, shared gate/up and rotation of x, then the routing launch
+        return dict(STAGE_KERNELS_GEMV, topk_sort=("k_route_par", ["router.hip", "route_small.h", "handoff.h",
+                                                                  "token_ops.h"]))
     return STAGE_KERNELS_GEMV
 
 
@@ -628,9 +630,10 @@ def bench_layer(a, name, steps, warmup, with_cpu):
         "shared_down_combine": 1024 * 2048 * 2 + T * 1024 * 2 + T * 6 * 2048 * 4 + act,
     }
     if FUSED_MAX_TOKENS < T <= ROUTE_SMALL_MAX_TOKENS:
-        # the router and the rotated x, then the shared gate/up beside the routing
-        stage_bytes["router_shared_gateup"] = ROUTER_BYTES + act + T * 256 * 4 + act
-        stage_bytes["topk_sort"] = 2 * 1024 * 2048 * 2 + act + T * 1024 * 2 + T * 256 * 4 + T * 6 * 4 * 4
+        # the router, the shared gate/up and the rotated x in one launch, then
+        # the routing (logits in, selections and sort records out)
+        stage_bytes["router_shared_gateup"] += act
+        stage_bytes["topk_sort"] = T * 256 * 4 + T * 6 * 4 * 4 + 257 * 4 + 256 * 32
     if T <= FUSED_MAX_TOKENS:
         # the first launch is the router alone; the second runs the rest of the
         # layer, the shared expert included (its time is recorded under

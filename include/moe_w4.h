@@ -79,7 +79,9 @@ extern "C" {
  * the rest of the layer in one launch whose workgroups hand the routed gate/up
  * results and the shared expert's activations to the down projection through
  * device-scope counters in the workspace's `sync` region, cleared by the first
- * launch); from MOE_W4_FUSED_MAX_TOKENS + 1 tokens on, one launch per step. */
+ * launch); from MOE_W4_FUSED_MAX_TOKENS + 1 tokens on, one launch per step
+ * (up to 48 tokens the routing launch hands its workgroups' top-6 selections
+ * to its workgroup 0 through the same counters, cleared by the launch before). */
 #define MOE_W4_FUSED_MAX_TOKENS 8
 /* Most layers in one moe_w4_stack_forward call. */
 #define MOE_W4_STACK_MAX_LAYERS 1024
@@ -121,13 +123,15 @@ extern "C" {
  *                         positions in order, ascending by expert; n_chunks i32 [1]
  *                         holds n.  (Written at every T; read only on that path.)
  *   logits    f32 [T][256] router logits R x, without the bias
- *   sync      8192 bytes of counters for the fused decode launch; their
- *             contents on entry do not matter (the call clears them itself).
- *   error     i32 [1]: 0 after a call that completed normally; 1 if a down
- *             workgroup of the two-launch form (1-8 tokens) gave up its
- *             bounded wait for the gate/up results (its outputs are then NaN;
- *             see moe_w4_set_fused_wait).  A stack call keeps a failure of any
- *             of its layers.
+ *   sync      8192 bytes of counters for the hand-offs inside a launch (1-48
+ *             tokens); their contents on entry do not matter (the call clears
+ *             them itself).
+ *   error     i32 [1]: 0 after a call that completed normally; 1 if a bounded
+ *             wait of a hand-off gave up: a down workgroup of the two-launch
+ *             form (1-8 tokens) waiting for the gate/up results, or the
+ *             routing launch (9-48 tokens) waiting for the top-6 selections
+ *             (the outputs are then NaN; see moe_w4_set_fused_wait).  A stack
+ *             call keeps a failure of any of its layers.
  *   hist      scratch of the sort at prefill sizes (per-workgroup histograms). */
 typedef struct moe_w4_ws_layout {
     size_t logits, topk_idx, topk_w, offsets, perm, pos, n_active, active;
@@ -287,14 +291,17 @@ size_t moe_w4_stack_workspace_bytes(int64_t T);
 int moe_w4_stack_forward(float *resid, const moe_w4_layer *layers, int n_layers, int64_t T, void *trace,
                          void *workspace, size_t workspace_bytes, void *stream);
 
-/* Diagnostic of the two-launch form (1-8 tokens), for tests of its failure
- * path.  Its down workgroups wait, bounded in time, for the gate/up results:
- * max_ticks sets the bound in ticks of the GPU's 100 MHz real-time clock (0
- * restores the default, 500,000 = 5 ms) and extra_count a count the wait
- * needs beyond the gate/up workgroups (default 0).  With extra_count > 0 the
- * wait can never complete, so every down workgroup gives up after max_ticks:
- * it writes NaN to its outputs (and to the residual stream in a stack layer)
- * and sets the workspace's error word, and every kernel still exits normally.
+/* Diagnostic of the bounded hand-off waits (1-48 tokens), for tests of their
+ * failure path.  The down workgroups of the two-launch form (1-8 tokens) wait
+ * for the gate/up results, and workgroup 0 of the routing launch (9-48
+ * tokens) for the other workgroups' top-6 selections: max_ticks sets the bound
+ * in ticks of the GPU's 100 MHz real-time clock (0 restores the default,
+ * 500,000 = 5 ms) and extra_count a count the waits need beyond the producing
+ * workgroups (default 0).  With extra_count > 0 a wait can never complete, so
+ * it gives up after max_ticks: the down workgroups write NaN to their outputs
+ * (and to the residual stream in a stack layer), the routing workgroup leaves
+ * no expert active and NaN expert rows (so y is NaN), and the workspace's
+ * error word is set; every kernel still exits normally.
  * Process-wide; read when a call enqueues its launches (a captured graph keeps
  * the values of its capture), so set it only while no other thread calls the
  * library.  EINVAL for max_ticks outside [0, 2^32) or extra_count < 0. */

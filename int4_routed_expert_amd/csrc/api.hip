@@ -221,17 +221,20 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
     if (grouped)
         MOE_STEP(launch_router_and_shared_gateup_dense(x, T, router_w, nullptr, logits, shared_w, hs, s));
     else if (small_route)
-        // up to kRouteSmallMaxTokens tokens: the router and the rotation of x
-        // first; the shared gate/up streams in the next launch beside the
-        // routing (one workgroup), which the routed experts wait for
-        MOE_STEP(launch_router_rotate(x, T, router_w, logits, xt, xt_scale, s));
+        // up to kRouteSmallMaxTokens tokens: the router, the shared gate/up
+        // and the rotation of x in one launch, which also clears the counter
+        // of the routing launch after it
+        MOE_STEP(launch_router_and_shared_gateup(x, T, router_w, nullptr, logits, shared_w, hs, xt, xt_scale,
+                                                 counters, s));
     else
         MOE_STEP(launch_router_and_shared_gateup(x, T, router_w, nullptr, logits, shared_w, hs, nullptr, xt_scale,
-                                                 s));
+                                                 nullptr, s));
     MOE_MARK();
     if (small_route) {
-        MOE_STEP(launch_shared_gateup_route(x, T, shared_w, hs, logits, bias, policy, topk_idx, topk_w, offsets, perm,
-                                            pos, n_active, active, chunks, n_chunks, error_clear, s));
+        MOE_STEP(launch_route_par(logits, T, bias, policy, topk_idx, topk_w, offsets, perm, pos, n_active, active,
+                                  chunks, n_chunks, o, counters, error_clear, error,
+                                  g_wait_extra.load(std::memory_order_relaxed),
+                                  g_wait_ticks.load(std::memory_order_relaxed), s));
     } else {
         MOE_STEP(launch_topk_rotate(logits, x, T, bias, policy, topk_idx, topk_w, xt, xt_scale, s));
         if (grouped)   // many workgroups
@@ -303,6 +306,7 @@ int run_forward_nvfp4(const void *x_, const void *router_w_, const void *codes_,
     int *chunks = ws_at<int>(ws, L.chunks);
     int *n_chunks = ws_at<int>(ws, L.n_chunks);
     int *error = ws_at<int>(ws, L.error);
+    int *counters = ws_at<int>(ws, L.sync);
     const bool dense = T >= kPrefillMinTokens;
     const bool small_route = T <= kRouteSmallMaxTokens;
 
@@ -330,11 +334,13 @@ int run_forward_nvfp4(const void *x_, const void *router_w_, const void *codes_,
     if (dense)
         NV_STEP(launch_router_and_shared_gateup_dense(x, T, router_w, nullptr, logits, shared_w, hs, s));
     else
-        NV_STEP(launch_router_and_shared_gateup(x, T, router_w, nullptr, logits, shared_w, hs, nullptr, xt_scale, s));
+        NV_STEP(launch_router_and_shared_gateup(x, T, router_w, nullptr, logits, shared_w, hs, nullptr, xt_scale,
+                                                small_route ? counters : nullptr, s));
     NV_MARK();
     if (small_route) {
-        NV_STEP(launch_route_small(logits, T, bias, 0, topk_idx, topk_w, offsets, perm, pos, n_active, active, chunks,
-                                   n_chunks, error, s));
+        NV_STEP(launch_route_par(logits, T, bias, 0, topk_idx, topk_w, offsets, perm, pos, n_active, active, chunks,
+                                 n_chunks, o, counters, error, error, g_wait_extra.load(std::memory_order_relaxed),
+                                 g_wait_ticks.load(std::memory_order_relaxed), s));
     } else {
         // from 128 tokens on x as natural-order fp16 for the MFMA experts (the
         // GEMVs below that read x itself)

@@ -51,6 +51,7 @@
 // hang the device and cannot go unnoticed.
 #include "common.h"
 #include "gemv_ops.h"
+#include "handoff.h"
 #include "launch.h"
 #include "token_ops.h"
 
@@ -71,10 +72,6 @@ constexpr int kFuBatchesPerExpert = kI / kFuPairs;  // 256
 static_assert(kFuWaves == kFuCols, "a down wave owns one feature of the shared projection");
 static_assert(kFuWaves >= kFusedMaxTokens, "one wave per token for the routing");
 
-// Cache policy of the a hand-off: device scope (sc1) plus the volatile
-// bit, which keeps the accesses in program order around the counter and
-// barriers (the compiler adds sc0: system scope, also coherent across XCDs).
-constexpr int kHandOff = 16 | (int)(1u << 31);
 
 template <int T>
 struct FuRouting {
@@ -131,23 +128,6 @@ __device__ __forceinline__ float4 bf16x4_lo(uint4 q) {
 }
 __device__ __forceinline__ float4 bf16x4_hi(uint4 q) {
     return make_float4(bf16lo(q.z), bf16hi(q.z), bf16lo(q.w), bf16hi(q.w));
-}
-
-// Poll one replica of a completion counter until it reaches `target` or
-// `ticks` of the 100 MHz real-time clock pass; returns whether it was reached.
-__device__ __forceinline__ bool wait_count(const int *counter, int target, uint32_t ticks) {
-    const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
-    for (;;) {
-        if (__hip_atomic_load(counter, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target) return true;
-        if (__builtin_amdgcn_s_memrealtime() - t_start > ticks) return false;
-        __builtin_amdgcn_s_sleep(8);
-    }
-}
-
-// Add 1 to every replica of a counter (lanes 0..15 of the calling wave).
-__device__ __forceinline__ void count_done(int *counters, int lane) {
-    if (lane < kFusedCounters)
-        __hip_atomic_fetch_add(counters + lane * kFusedCounterStride, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // One wave batch of gate/up codes: 2 row pairs, lane l owning K [32l, 32l+32).

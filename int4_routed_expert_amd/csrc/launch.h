@@ -9,20 +9,12 @@ namespace moe_w4 {
 
 // One launch: router logits[T][256] = x R^T (+ bias), and the shared expert's
 // h[T][1024] = bf16(silu(x Wsg^T) * (x Wsu^T)); if xt is not null, also the
-// rotated fp16 copy of x (xt, xt_scale, as launch_topk_rotate writes them).
+// rotated fp16 copy of x (xt, xt_scale, as launch_topk_rotate writes them);
+// if clear_counters is not null, workgroup 0 clears those counter replicas
+// (kFusedCounters of them) for launch_route_par.
 void launch_router_and_shared_gateup(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
                                      float *logits, const uint16_t *shared_w, uint16_t *hs, uint32_t *xt,
-                                     float *xt_scale, hipStream_t s);
-
-// 9..kRouteSmallMaxTokens tokens: the router logits (without the bias) and the
-// rotated fp16 x in one launch, then the shared expert's gate/up (h) and, in
-// its workgroup 0, the top-6 and the sort (as launch_route_small) in the next.
-void launch_router_rotate(const uint16_t *x, int T, const uint16_t *router_w, float *logits, uint32_t *xt,
-                          float *xt_scale, hipStream_t s);
-void launch_shared_gateup_route(const uint16_t *x, int T, const uint16_t *shared_w, uint16_t *hs,
-                                const float *logits, const float *bias, int policy, int *topk_idx, float *topk_w,
-                                int *offsets, int *perm, int *pos, int *n_active, int *slots, int *chunks,
-                                int *n_chunks, int *error, hipStream_t s);
+                                     float *xt_scale, int *clear_counters, hipStream_t s);
 
 // Decode sizes (1..kFusedMaxTokens tokens): one launch for the router logits
 // (it also clears the counters of the launch after it), then the whole rest
@@ -95,13 +87,18 @@ void launch_sort_wide(const int *topk_idx, int T, int *hist, int *offsets, int *
 // error (or null): the workspace's error word, cleared (this sequence cannot fail).
 void launch_sort(const int *topk_idx, int T, int *offsets, int *perm, int *pos, int *n_active,
                  int *slots, int *chunks, int *n_chunks, int *error, hipStream_t s);
-// Top-6 and the stable sort in one workgroup (16 waves, one token per wave at
-// a time; the sort ranks the <= 288 assignments in LDS), for up to
-// kRouteSmallMaxTokens tokens whose rotated x is written elsewhere.
+// Top-6 of up to kRouteSmallMaxTokens tokens, one wave per token over
+// ceil(T/8) workgroups, handed to workgroup 0, which sorts the assignments
+// in LDS (offsets, perm, pos, slot records, chunk list).  counters: replicas
+// that the launch before cleared (launch_router_and_shared_gateup);
+// error_clear (or null) is cleared; if the hand-off wait gives up after
+// wait_ticks of the 100 MHz clock (target raised by wait_target_extra, for
+// tests), error is set to 1, no expert is active and o[6T][2048] is NaN.
 constexpr int kRouteSmallMaxTokens = 48;
-void launch_route_small(const float *logits, int T, const float *bias, int policy, int *topk_idx, float *topk_w,
-                        int *offsets, int *perm, int *pos, int *n_active, int *slots, int *chunks, int *n_chunks,
-                        int *error, hipStream_t s);
+void launch_route_par(const float *logits, int T, const float *bias, int policy, int *topk_idx, float *topk_w,
+                      int *offsets, int *perm, int *pos, int *n_active, int *slots, int *chunks, int *n_chunks,
+                      float *o, int *counters, int *error_clear, int *error, int wait_target_extra,
+                      uint32_t wait_ticks, hipStream_t s);
 
 // Routed experts, GEMV form (few tokens per expert), driven by the slot records.
 void launch_gateup_gemv(const uint8_t *codes, const uint16_t *scales, const uint32_t *xt,

@@ -1,14 +1,18 @@
-// Top-6 and the stable token->expert sort of a few tokens (up to
-// kRouteSmallMaxTokens) in one workgroup of NW waves: wave w selects tokens
-// w, w + NW, ... (all their logit loads issued first; model card, introduction:
-// 256 experts, top-6; weights sigmoid / max(sum, 2^-14), bloomery issue #632,
-// design thread); then a stable counting sort of the <= 288 assignments in LDS
-// (the algorithm of k_sort, with the chosen experts never leaving the
-// workgroup).  Used by the routing launch and by the launch that routes beside
-// the shared expert's gate/up.
+// Routing of a few tokens (up to kRouteSmallMaxTokens) in one launch of
+// ceil(T / 8) workgroups of 8 waves: wave w of workgroup b selects the top-6
+// of token 8b + w (model card, introduction: 256 experts, top-6; weights
+// sigmoid / max(sum, 2^-14), bloomery issue #632, design thread), all tokens
+// side by side; the selections are handed to workgroup 0 through the
+// workspace (coherent stores and a completion counter that the launch before
+// clears), and workgroup 0 sorts the <= 288 assignments by expert in LDS
+// (a stable counting sort, the algorithm of k_sort) and writes offsets,
+// perm, pos, the slot records and the chunk list.  One token per wave: the
+// selection is a chain of ~450 dependent instructions (~1.2 us), which one
+// workgroup walking four tokens per wave paid four times.
 #pragma once
 
 #include "common.h"
+#include "handoff.h"
 #include "launch.h"
 #include "token_ops.h"
 
@@ -27,14 +31,45 @@ struct RouteSmallArgs {
     int *slots;
     int4 *chunks;
     int *n_chunks;
-    int *error;            // cleared (this launch sequence cannot fail), or null
+    int *error_clear;      // cleared at the start, or null (keep an earlier failure visible)
+    int *error;            // set to 1 if the hand-off wait gives up
+    float *o;              // expert rows [6T][2048] fp32 (filled with NaN if the wait gives up)
+    int *counters;         // completion counter replicas (zero on entry)
+    int wait_target_extra; // added to the wait target (tests of the failure path)
+    uint32_t wait_ticks;
 };
 
-template <int NW>
-__device__ __forceinline__ void route_small_block(const RouteSmallArgs &A) {
-    constexpr int kPerWave = (kRouteSmallMaxTokens + NW - 1) / NW;
-    constexpr int kMaxChunks = (kTopK * kRouteSmallMaxTokens + 63) / 64;
-    static_assert(NW >= kMaxChunks, "one wave per 64 assignments in the ranking");
+constexpr int kRouteWaves = 8;
+constexpr int kRouteMaxChunks = (kTopK * kRouteSmallMaxTokens + 63) / 64;
+static_assert(kRouteWaves >= kRouteMaxChunks, "one wave per 64 assignments in the ranking");
+
+// The hand-off wait gave up: routing that no kernel after it can misuse (no
+// active expert, pos and perm the identity), NaN expert rows so that every y
+// the combine writes is NaN, and the error word set.
+__device__ __forceinline__ void route_give_up(const RouteSmallArgs &A, int tid) {
+    const int N = kTopK * A.T;
+    for (int i = tid; i <= kE; i += 64 * kRouteWaves) A.offsets[i] = 0;
+    for (int i = tid; i < kE; i += 64 * kRouteWaves) {
+        int4 *rec = reinterpret_cast<int4 *>(A.slots + 8 * i);
+        rec[0] = make_int4(-1, 0, 0, 0);
+        rec[1] = make_int4(0, 0, 0, 0);
+    }
+    for (int a = tid; a < N; a += 64 * kRouteWaves) {
+        A.pos[a] = a;
+        A.perm[a] = a;
+    }
+    for (size_t i = tid; i < (size_t)N * kH; i += 64 * kRouteWaves) A.o[i] = __builtin_nanf("");
+    if (tid == 0) {
+        *A.n_active = 0;
+        *A.n_chunks = 0;
+        *A.error = 1;
+    }
+}
+
+// (router.hip is the one translation unit that includes this file)
+__global__ __launch_bounds__(64 * kRouteWaves) void k_route_par(RouteSmallArgs A) {
+    constexpr int NW = kRouteWaves;
+    constexpr int kMaxChunks = kRouteMaxChunks;
     __shared__ int sel[kTopK * kRouteSmallMaxTokens];     // expert of assignment a
     __shared__ int sperm[kTopK * kRouteSmallMaxTokens];   // assignment at sorted position p
     __shared__ int cnt[kMaxChunks][kE];                   // per chunk: count, then base of each expert
@@ -43,32 +78,48 @@ __device__ __forceinline__ void route_small_block(const RouteSmallArgs &A) {
     __shared__ int act_rank[kE];                          // active experts below e (-1: e not active)
     __shared__ int act_list[kE];                          // active expert of each slot
     __shared__ int n_act_s;
+    __shared__ int fail;
     const int T = A.T;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int N = kTopK * T;
-    for (int i = tid; i < kMaxChunks * kE; i += 64 * NW) (&cnt[0][0])[i] = 0;
-    if (tid == 0 && A.error) *A.error = 0;
+    const int G = (int)gridDim.x;
 
-    float4 lv[kPerWave];
+    // ---- top-6 of token t: one wave each ----
+    const int t = NW * (int)blockIdx.x + wave;
+    if (t < T) {
+        const float4 lv = reinterpret_cast<const float4 *>(A.logits + (size_t)t * kE)[lane];
+        const Top6 r = top6_wave(lv, lane, A.rp);
+        const __amdgpu_buffer_rsrc_t ib = make_buf(A.topk_idx, (uint32_t)(4 * N));
 #pragma unroll
-    for (int i = 0; i < kPerWave; ++i) {
-        const int t = min(wave + NW * i, T - 1);   // past the end: token T-1 again (unused)
-        lv[i] = reinterpret_cast<const float4 *>(A.logits + (size_t)t * kE)[lane];
-    }
-#pragma unroll
-    for (int i = 0; i < kPerWave; ++i) {
-        const int t = wave + NW * i;
-        if (t < T) {
-            const Top6 r = top6_wave(lv[i], lane, A.rp);
-#pragma unroll
-            for (int j = 0; j < kTopK; ++j) {
-                if (lane == j) {
-                    A.topk_idx[(size_t)t * kTopK + j] = r.e[j];
-                    A.topk_w[(size_t)t * kTopK + j] = r.w[j];
-                    sel[kTopK * t + j] = r.e[j];
-                }
+        for (int j = 0; j < kTopK; ++j) {
+            if (lane == j) {
+                __builtin_amdgcn_raw_buffer_store_b32(r.e[j], ib, 4 * (kTopK * t + j), 0, kHandOff);
+                A.topk_w[(size_t)t * kTopK + j] = r.w[j];
+                sel[kTopK * t + j] = r.e[j];
             }
         }
+    }
+    if (blockIdx.x != 0) {
+        // count this workgroup done once every wave's selections are stored
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (wave == 0) count_done(A.counters, lane);
+        return;
+    }
+
+    // ---- workgroup 0: wait for the other selections, then sort ----
+    for (int i = tid; i < kMaxChunks * kE; i += 64 * NW) (&cnt[0][0])[i] = 0;
+    if (tid == 0 && A.error_clear) *A.error_clear = 0;
+    if (tid == 0) fail = G > 1 && !wait_count(A.counters, G - 1 + A.wait_target_extra, A.wait_ticks);
+    __syncthreads();
+    if (fail) {
+        route_give_up(A, tid);
+        return;
+    }
+    {
+        const __amdgpu_buffer_rsrc_t ib = make_buf(A.topk_idx, (uint32_t)(4 * N));
+        for (int a = kTopK * NW + tid; a < N; a += 64 * NW)
+            sel[a] = (int)__builtin_amdgcn_raw_buffer_load_b32(ib, 4 * a, 0, kHandOff);
     }
     __syncthreads();
 

@@ -400,16 +400,16 @@ __global__ __launch_bounds__(1024) void k_sort_place(const int *__restrict__ top
     }
 }
 
-// Top-6 and sort of a few tokens (up to kRouteSmallMaxTokens) in one
-// workgroup of 16 waves (route_small.h).
-__global__ __launch_bounds__(1024) void k_route_small(RouteSmallArgs A) { route_small_block<kSortWaves>(A); }
-
-void launch_route_small(const float *logits, int T, const float *bias, int policy, int *topk_idx, float *topk_w,
-                        int *offsets, int *perm, int *pos, int *n_active, int *slots, int *chunks, int *n_chunks,
-                        int *error, hipStream_t s) {
+// Top-6 and sort of a few tokens (up to kRouteSmallMaxTokens): one wave per
+// token, then workgroup 0 sorts (route_small.h).
+void launch_route_par(const float *logits, int T, const float *bias, int policy, int *topk_idx, float *topk_w,
+                      int *offsets, int *perm, int *pos, int *n_active, int *slots, int *chunks, int *n_chunks,
+                      float *o, int *counters, int *error_clear, int *error, int wait_target_extra,
+                      uint32_t wait_ticks, hipStream_t s) {
     const RouteSmallArgs A{logits, T, RouterPolicy{bias, policy}, topk_idx, topk_w, offsets, perm, pos, n_active,
-                           slots, reinterpret_cast<int4 *>(chunks), n_chunks, error};
-    hipLaunchKernelGGL(k_route_small, dim3(1), dim3(1024), 0, s, A);
+                           slots, reinterpret_cast<int4 *>(chunks), n_chunks, error_clear, error, o, counters,
+                           wait_target_extra, wait_ticks};
+    hipLaunchKernelGGL(k_route_par, dim3((T + kRouteWaves - 1) / kRouteWaves), dim3(64 * kRouteWaves), 0, s, A);
 }
 
 void launch_sort_wide(const int *topk_idx, int T, int *hist, int *offsets, int *perm, int *pos, int *n_active,

@@ -27,7 +27,6 @@
 // order inside an MFMA is the same for both operands.
 #include "common.h"
 #include "launch.h"
-#include "route_small.h"
 #include "token_ops.h"
 
 namespace moe_w4 {
@@ -64,9 +63,9 @@ struct SkinnyJobs {
     int rot_tokens;
     uint32_t *xt;
     float *xt_scale;
-    // optional fourth role (the ROUTE instances), workgroup 0: the top-6 and
-    // the sort of up to kRouteSmallMaxTokens tokens (route_small.h)
-    RouteSmallArgs route;
+    // completion counter replicas cleared by workgroup 0 for the next launch
+    // (kFusedCounters of them, kFusedCounterStride apart), or null
+    int *clear_counters;
 };
 
 __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
@@ -80,7 +79,7 @@ __device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
 // lanes r and r + 8 read the same weight row, which doubles the workgroups of
 // a small matrix (the 1024-row shared down projection would otherwise leave
 // half the CUs idle); the MFMA units have ample room for the duplicate columns.
-template <int MT, int KS, int KB, int CW, bool ROUTE>
+template <int MT, int KS, int KB, int CW>
 __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__ A, int M, SkinnyJobs jobs) {
     constexpr int K = 128 * KS * KB;
     // Activations through LDS (KB <= 2): each wave stages its own K slice of
@@ -100,11 +99,9 @@ __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__
     static_assert(!kLds || kWaveBytes >= MT * 64 * 16, "the reduction fits the staging area");
     __shared__ __attribute__((aligned(16))) uint8_t xs[KS][kWaveBytes];
     auto red_at = [&](int w, int t) -> f32x4_t * { return reinterpret_cast<f32x4_t *>(xs[w]) + t * 64; };
-    if (ROUTE && blockIdx.x == 0) {
-        route_small_block<KS>(jobs.route);
-        return;
-    }
-    const int bx = (int)blockIdx.x - (ROUTE ? 1 : 0);
+    if (jobs.clear_counters && blockIdx.x == 0 && threadIdx.x < kFusedCounters)
+        jobs.clear_counters[threadIdx.x * kFusedCounterStride] = 0;
+    const int bx = (int)blockIdx.x;
     // both jobs' fields are read (in parallel, at fixed kernel-argument
     // offsets) and then selected: indexing the argument by the job number
     // would make every field a dependent scalar load
@@ -288,15 +285,14 @@ __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__
     }
 }
 
-template <int KB, int CW, bool ROUTE = false>
+template <int KB, int CW>
 static void launch_skinny_k(const uint16_t *A, int M, const SkinnyJobs &jobs, hipStream_t s) {
     constexpr int KS = 8;
-    dim3 grid((ROUTE ? 1 : 0) + jobs.job[0].n_blocks + jobs.job[1].n_blocks + (jobs.rot_tokens + KS - 1) / KS),
-        block(64 * KS);
+    dim3 grid(jobs.job[0].n_blocks + jobs.job[1].n_blocks + (jobs.rot_tokens + KS - 1) / KS), block(64 * KS);
     if (M <= 16)
-        hipLaunchKernelGGL((k_skinny<1, KS, KB, CW, ROUTE>), grid, block, 0, s, A, M, jobs);
+        hipLaunchKernelGGL((k_skinny<1, KS, KB, CW>), grid, block, 0, s, A, M, jobs);
     else
-        hipLaunchKernelGGL((k_skinny<2, KS, KB, CW, ROUTE>), grid, block, 0, s, A, M, jobs);
+        hipLaunchKernelGGL((k_skinny<2, KS, KB, CW>), grid, block, 0, s, A, M, jobs);
 }
 
 static SkinnyJob no_job() { return SkinnyJob{nullptr, 0, 0, 0, kEpiStoreF32, nullptr, nullptr, 0, nullptr, nullptr, nullptr}; }
@@ -308,40 +304,19 @@ static SkinnyJobs no_jobs() {
     jobs.rot_tokens = 0;
     jobs.xt = nullptr;
     jobs.xt_scale = nullptr;
-    jobs.route = RouteSmallArgs{};
+    jobs.clear_counters = nullptr;
     return jobs;
-}
-
-void launch_router_rotate(const uint16_t *x, int T, const uint16_t *router_w, float *logits, uint32_t *xt,
-                          float *xt_scale, hipStream_t s) {
-    SkinnyJobs jobs = no_jobs();
-    jobs.rot_x = x;
-    jobs.rot_tokens = T;
-    jobs.xt = xt;
-    jobs.xt_scale = xt_scale;
-    jobs.job[0] = SkinnyJob{router_w, kE, 0, kE / 16, kEpiStoreF32, nullptr, logits, kE, nullptr, nullptr, nullptr};
-    launch_skinny_k<kH / (128 * 8), 16>(x, T, jobs, s);
-}
-
-void launch_shared_gateup_route(const uint16_t *x, int T, const uint16_t *shared_w, uint16_t *hs,
-                                const float *logits, const float *bias, int policy, int *topk_idx, float *topk_w,
-                                int *offsets, int *perm, int *pos, int *n_active, int *slots, int *chunks,
-                                int *n_chunks, int *error, hipStream_t s) {
-    SkinnyJobs jobs = no_jobs();
-    jobs.job[0] = SkinnyJob{shared_w, 2 * kIS, kIS, 2 * kIS / 16, kEpiSwiglu, nullptr, hs, kIS, nullptr, nullptr, nullptr};
-    jobs.route = RouteSmallArgs{logits, T, RouterPolicy{bias, policy}, topk_idx, topk_w, offsets, perm, pos,
-                                n_active, slots, reinterpret_cast<int4 *>(chunks), n_chunks, error};
-    launch_skinny_k<kH / (128 * 8), 16, true>(x, T, jobs, s);
 }
 
 void launch_router_and_shared_gateup(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
                                      float *logits, const uint16_t *shared_w, uint16_t *hs, uint32_t *xt,
-                                     float *xt_scale, hipStream_t s) {
-    SkinnyJobs jobs;
+                                     float *xt_scale, int *clear_counters, hipStream_t s) {
+    SkinnyJobs jobs = no_jobs();
     jobs.rot_x = x;
     jobs.rot_tokens = xt ? T : 0;
     jobs.xt = xt;
     jobs.xt_scale = xt_scale;
+    jobs.clear_counters = clear_counters;
     jobs.job[0] = SkinnyJob{router_w, kE, 0, kE / 16, kEpiStoreF32, bias, logits, kE, nullptr, nullptr, nullptr};
     // columns: 16-wide tiles of (8 gate rows, the same 8 up rows); up rows start at row 1024
     jobs.job[1] = SkinnyJob{shared_w, 2 * kIS, kIS, 2 * kIS / 16, kEpiSwiglu, nullptr, hs, kIS, nullptr, nullptr, nullptr};
@@ -350,11 +325,7 @@ void launch_router_and_shared_gateup(const uint16_t *x, int T, const uint16_t *r
 
 void launch_shared_down_combine(const uint16_t *shared_w, const uint16_t *hs, int T, const float *topk_w,
                                 const int *pos, const float *o, uint16_t *y, hipStream_t s) {
-    SkinnyJobs jobs;
-    jobs.rot_x = nullptr;
-    jobs.rot_tokens = 0;
-    jobs.xt = nullptr;
-    jobs.xt_scale = nullptr;
+    SkinnyJobs jobs = no_jobs();
     jobs.job[0] = SkinnyJob{shared_w + 2 * kSharedGateElems, kH, 0, kH / 8, kEpiCombine, nullptr, y, kH, topk_w, pos, o};
     jobs.job[1] = no_job();
     launch_skinny_k<kIS / (128 * 8), 8>(hs, T, jobs, s);
@@ -366,11 +337,7 @@ void launch_shared_down_combine(const uint16_t *shared_w, const uint16_t *hs, in
 // gate/up job as for the shared expert, 16-column tiles of (8 gate rows, the
 // same 8 up rows); the down projection over K = 6144, 8 waves splitting K.
 void launch_dense_mlp_gateup_skinny(const uint16_t *x, int T, const uint16_t *w, uint16_t *h, hipStream_t s) {
-    SkinnyJobs jobs;
-    jobs.rot_x = nullptr;
-    jobs.rot_tokens = 0;
-    jobs.xt = nullptr;
-    jobs.xt_scale = nullptr;
+    SkinnyJobs jobs = no_jobs();
     jobs.job[0] = SkinnyJob{w, 2 * kDenseInter, kDenseInter, 2 * kDenseInter / 16, kEpiSwiglu, nullptr, h, kDenseInter,
                             nullptr, nullptr, nullptr};
     jobs.job[1] = no_job();
@@ -378,11 +345,7 @@ void launch_dense_mlp_gateup_skinny(const uint16_t *x, int T, const uint16_t *w,
 }
 
 void launch_dense_mlp_down_skinny(const uint16_t *w, const uint16_t *h, int T, uint16_t *y, hipStream_t s) {
-    SkinnyJobs jobs;
-    jobs.rot_x = nullptr;
-    jobs.rot_tokens = 0;
-    jobs.xt = nullptr;
-    jobs.xt_scale = nullptr;
+    SkinnyJobs jobs = no_jobs();
     jobs.job[0] = SkinnyJob{w + 2 * (size_t)kDenseInter * kH, kH, 0, kH / 8, kEpiStoreBf16, nullptr, y, kH, nullptr,
                             nullptr, nullptr};
     jobs.job[1] = no_job();

@@ -406,12 +406,15 @@ def test_expert_relabel_invariance(m, layer0, T):
 
 
 # ------------------------------------------------------------ failure path
-def test_fused_wait_failure_path(m, layer0):
-    """The two-launch form's bounded wait, made to give up from the host (a
-    count the gate/up workgroups never reach, a 200 us bound): every kernel
-    exits normally, y and the residual stream come out NaN and the error word
-    is set; with the defaults back, the same calls are correct again."""
-    T = 3
+@pytest.mark.parametrize("T", [3, 32])
+def test_fused_wait_failure_path(m, layer0, T):
+    """The bounded hand-off waits, made to give up from the host (a count the
+    producing workgroups never reach, a 200 us bound): at T = 3 the down
+    workgroups of the two-launch form, at T = 32 workgroup 0 of the routing
+    launch.  Every kernel exits normally, y and the residual stream come out
+    NaN and the error word is set; with the defaults back, the same calls are
+    correct again."""
+    print(f"[failure path] T={T}", flush=True)
     x = synth.gen_x(210, T)
     ws = m.workspace(T)
     w = layer0
