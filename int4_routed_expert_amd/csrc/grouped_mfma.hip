@@ -448,10 +448,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 }
 
 // =========================================================================
-// down: a workgroup owns a chunk and loops over all 2048 output features in
-// tiles of 128 (32 per wave), so the chunk's A (96 rows x 512 fp16) is staged
-// in LDS once; the codes of the next three tiles are in flight during each
-// tile.  The MFMA runs transposed (codes as the row operand, tokens as the
+// down: four workgroups own a chunk, each a quarter of the 2048 output
+// features in tiles of 128 (32 per wave, two wave groups), with the chunk's A
+// (96 rows x 512 fp16) staged in LDS; the codes of the next tile are in
+// flight during each tile.  The MFMA runs transposed (codes as the row operand, tokens as the
 // column operand), so a lane ends with 4 consecutive features of one token
 // per group.  o is stored in fp16 with one power-of-two multiplier per row
 // (o_scale), which halves the traffic of the fp32 rows at a relative rounding
@@ -471,8 +471,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // normalisations are undone once per output.
 // =========================================================================
 constexpr int kDnPitch = 1040;   // bytes per LDS row (1024 + 16)
-constexpr int kDnHalves = 2;     // wave groups of the workgroup, each over half of the features
-constexpr int kDnTiles = kH / 128 / kDnHalves;
+constexpr int kDnParts = 4;      // workgroups per chunk, each over a quarter of the features
+constexpr int kDnHalves = 2;     // wave groups of the workgroup, each over half of its features
+constexpr int kDnTiles = kH / 128 / kDnParts / kDnHalves;
 constexpr int kDnCodeRing = 2;
 
 // NVFP4 (NV): no scale normalisation; each lane's four E4M3 scales of a
@@ -489,8 +490,11 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
     __shared__ float row_p[kChunkRows];                                       // per token
     __shared__ __attribute__((aligned(16))) uint16_t sc[kI / kG][kH];         // [block][feature] bf16
     __shared__ __attribute__((aligned(16))) float fk[kH];                     // 2^-k per feature
-    int chunk, tile0;
-    chunk_tile(1, chunk, tile0);
+    // four workgroups per chunk (one per quarter of the features, on one XCD
+    // so that they share the chunk's activations in L2): one workgroup per
+    // chunk left the grid at ~1.1 rounds of the 256 CUs at T = 2048
+    int chunk, quarter;
+    chunk_tile(kDnParts, chunk, quarter);
     if (chunk >= *n_chunks) return;
     const int4 ch = chunks[chunk];
     const int e = uniform(ch.x), row0 = uniform(ch.y), rows = uniform(ch.z);
@@ -501,7 +505,7 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
     const __amdgpu_buffer_rsrc_t cres =
         make_buf(codes + (size_t)e * kCodeBytesPerExpert + kCodeBytesGu, (uint32_t)(kH * kI / 2));
     // the feature whose codes this lane loads, in tile 0 of its half
-    const int fh = half * (kH / kDnHalves);
+    const int fh = quarter * (kH / kDnParts) + half * (kH / kDnParts / kDnHalves);
     const int f0 = fh + 32 * wave + n;
     const __amdgpu_buffer_rsrc_t nsres =
         make_buf(static_cast<const uint8_t *>(scales_) + (size_t)e * kNvScPerExpert + kNvScGu, kH * kI / 16);
@@ -607,19 +611,18 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
     float fkmax = NV ? 1.0f : fmaxf(fmaxf(fk_wave[0], fk_wave[1]), fmaxf(fk_wave[2], fk_wave[3]));
     if (fkmax == 0.0f) fkmax = 1.0f;   // every scale of the expert is zero: o is 0
     const float to_half = 0x1p-20f / fkmax;   // a power of two
-    if (!NV && tid < rows) o_scale[row0 + tid] = row_p[tid] * fkmax * 0x1p20f;
+    if (!NV && quarter == 0 && tid < rows) o_scale[row0 + tid] = row_p[tid] * fkmax * 0x1p20f;
     const float tsd = NV ? tscales[3 * e + 2] : 1.0f;
 
-    // unrolled by the ring size, so ring slots are compile-time; the fetch
-    // index is clamped (the last tiles re-read the last tile, in bounds) so
-    // that every iteration issues the same loads and the waits stay exact
+    // fully unrolled, so ring slots are compile-time; the next tile's codes
+    // are requested before this tile's products
     with_tiles(n_mt, [&](auto tiles) {
     constexpr int MT = decltype(tiles)::value;
 #pragma unroll
     for (int t = 0; t < kDnTiles; ++t) {
         const int cs = t % kDnCodeRing;
         __builtin_amdgcn_sched_barrier(0);
-        fetch((t + kDnCodeRing - 1) % kDnCodeRing, min(t + kDnCodeRing - 1, kDnTiles - 1));
+        if (t + kDnCodeRing - 1 < kDnTiles) fetch((t + kDnCodeRing - 1) % kDnCodeRing, t + kDnCodeRing - 1);
         __builtin_amdgcn_sched_barrier(0);
         const uint32_t zero = opaque(0);
         const uint8_t *abase = lds + zero;
@@ -735,7 +738,7 @@ void launch_gateup_mfma(const uint8_t *codes, const uint16_t *scales, const uint
 
 void launch_down_mfma(const uint8_t *codes, const uint16_t *scales, const uint32_t *at, const float *at_scale,
                       const int *chunks, const int *n_chunks, int T, uint16_t *o, float *o_scale, hipStream_t s) {
-    hipLaunchKernelGGL(k_down_mfma<false>, dim3(grid_for(T, 1)), dim3(256 * kDnHalves), 0, s, codes,
+    hipLaunchKernelGGL(k_down_mfma<false>, dim3(grid_for(T, kDnParts)), dim3(256 * kDnHalves), 0, s, codes,
                        static_cast<const void *>(scales), nullptr, at, at_scale,
                        reinterpret_cast<const int4 *>(chunks), n_chunks, static_cast<void *>(o), o_scale);
 }
@@ -751,7 +754,7 @@ void launch_gateup_mfma_nvfp4(const uint8_t *codes, const uint8_t *scales, const
 void launch_down_mfma_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscales, const uint32_t *an,
                             const float *an_scale, const int *chunks, const int *n_chunks, int T, float *o,
                             hipStream_t s) {
-    hipLaunchKernelGGL(k_down_mfma<true>, dim3(grid_for(T, 1)), dim3(256 * kDnHalves), 0, s, codes,
+    hipLaunchKernelGGL(k_down_mfma<true>, dim3(grid_for(T, kDnParts)), dim3(256 * kDnHalves), 0, s, codes,
                        static_cast<const void *>(scales), tscales, an, an_scale,
                        reinterpret_cast<const int4 *>(chunks), n_chunks, static_cast<void *>(o), nullptr);
 }
