@@ -106,7 +106,7 @@ ROUTE_SMALL_MAX_TOKENS = 48
 GROUPED_MIN_TOKENS = 128
 STAGE_KERNELS_FUSED = {
     "router_shared_gateup": ("k_router_small", ["decode_fused.hip", "gemv_ops.h", "token_ops.h"]),
-    "routed_gateup": ("k_decode_fused", ["decode_fused.hip", "gemv_ops.h", "token_ops.h"]),
+    "routed_gateup": ("k_decode_fused", ["decode_fused.hip", "gemv_ops.h", "token_ops.h", "nvfp4_ops.h"]),
 }
 STAGE_KERNELS_GEMV = {
     "router_shared_gateup": ("k_skinny", ["skinny_mfma.hip"]),
@@ -128,8 +128,8 @@ STAGE_KERNELS_PACK = {"pack": ("k_pack_groups", ["pack.hip"])}
 
 
 STAGE_KERNELS_NVFP4 = {
-    "routed_gateup": ("k_gateup_nv", ["nvfp4.hip", "gemv_ops.h", "token_ops.h"]),
-    "routed_down": ("k_down_nv", ["nvfp4.hip", "gemv_ops.h", "token_ops.h"]),
+    "routed_gateup": ("k_gateup_nv", ["nvfp4.hip", "nvfp4_ops.h", "gemv_ops.h", "token_ops.h"]),
+    "routed_down": ("k_down_nv", ["nvfp4.hip", "nvfp4_ops.h", "gemv_ops.h", "token_ops.h"]),
 }
 # from 128 tokens on the NVFP4 experts run on the grouped MFMA kernels
 STAGE_KERNELS_NVFP4_MFMA = {
@@ -141,7 +141,7 @@ STAGE_KERNELS_NVFP4_MFMA = {
 def stage_kernels(T, workload=""):
     if T is None:   # the packer workload
         return STAGE_KERNELS_PACK
-    if workload.startswith("nvfp4"):
+    if workload.startswith("nvfp4") and T > FUSED_MAX_TOKENS:
         return STAGE_KERNELS_NVFP4_MFMA if T >= GROUPED_MIN_TOKENS else STAGE_KERNELS_NVFP4
     if T <= FUSED_MAX_TOKENS:
         return STAGE_KERNELS_FUSED

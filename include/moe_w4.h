@@ -203,7 +203,11 @@ int moe_w4_forward_profiled(const void *x, const void *router_w, const void *cod
  * sign, 4 exponent bits bias 7, 3 mantissa bits, S.1111.111 NaN), weights in
  * the original basis (x and a are not rotated), activations not quantised.
  * Router, shared expert, routing and combine are those of moe_w4_forward
- * (Flint's router policy); expert outputs are fp32 sums of exact products.
+ * (Flint's router policy); x and the SwiGLU activations a enter the expert
+ * products as fp16 with one power-of-two prescale per token or assignment,
+ * and expert outputs are fp32 sums of exact products.  1-8 tokens run as the
+ * two launches of moe_w4_forward's decode form (same hand-off waits, error
+ * word and moe_w4_set_fused_wait).
  * codes: u8, expert e at e * MOE_W4_NVFP4_CODE_BYTES: gate [512][1024], up
  *        [512][1024], down [2048][256]; code of even k in the low nibble.
  * scales: u8 E4M3, expert e at e * MOE_W4_NVFP4_SCALE_BYTES: gate [512][128],

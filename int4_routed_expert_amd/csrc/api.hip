@@ -193,6 +193,8 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
         fa.router_policy = policy;
         fa.codes = codes;
         fa.scales = scales;
+        fa.nv_scales = nullptr;
+        fa.tscales = nullptr;
         fa.shared_gu = shared_w;
         fa.shared_down = shared_w + 2 * kSharedGateElems;
         fa.hs = hs;
@@ -331,6 +333,46 @@ int run_forward_nvfp4(const void *x_, const void *router_w_, const void *codes_,
     } while (0)
     (void)hipGetLastError();
     NV_MARK();
+    if (T <= kFusedMaxTokens) {
+        // the two launches of the int4 layer's fused form, with the NVFP4
+        // experts' codes and scales
+        NV_STEP(launch_router_small(x, nullptr, nullptr, T, router_w, nullptr, logits, counters, error, s));
+        NV_MARK();
+        NV_MARK();
+        FusedDecodeArgs fa;
+        fa.x = x;
+        fa.logits = logits;
+        fa.router_bias = bias;
+        fa.router_policy = 0;
+        fa.codes = codes;
+        fa.scales = nullptr;
+        fa.nv_scales = scales;
+        fa.tscales = tscales;
+        fa.shared_gu = shared_w;
+        fa.shared_down = shared_w + 2 * kSharedGateElems;
+        fa.hs = hs;
+        fa.T = T;
+        fa.topk_idx = topk_idx;
+        fa.topk_w = topk_w;
+        fa.offsets = offsets;
+        fa.perm = perm;
+        fa.pos = pos;
+        fa.n_active = n_active;
+        fa.slots = active;
+        fa.chunks = reinterpret_cast<int4 *>(chunks);
+        fa.n_chunks = n_chunks;
+        fa.act = act;
+        fa.y = y;
+        fa.resid = nullptr;
+        fa.counters = counters;
+        fa.counters_h = counters + kFusedCounters * kFusedCounterStride;
+        fa.error = error;
+        fa.wait_target_extra = g_wait_extra.load(std::memory_order_relaxed);
+        fa.wait_ticks = g_wait_ticks.load(std::memory_order_relaxed);
+        NV_STEP(launch_decode_fused(fa, s));
+        for (int i = 0; i < 4; ++i) NV_MARK();
+        return MOE_W4_OK;
+    }
     if (dense)
         NV_STEP(launch_router_and_shared_gateup_dense(x, T, router_w, nullptr, logits, shared_w, hs, s));
     else

@@ -53,6 +53,7 @@
 #include "gemv_ops.h"
 #include "handoff.h"
 #include "launch.h"
+#include "nvfp4_ops.h"
 #include "token_ops.h"
 
 namespace moe_w4 {
@@ -249,7 +250,11 @@ __global__ __launch_bounds__(512) void k_router_small(const uint16_t *__restrict
 // over tokens, assignments and down slots has a compile-time trip count and
 // the loads of a phase are all issued before the first of them is waited for).
 // ---------------------------------------------------------------------------
-template <int T>
+// NV: NVFP4 experts (nvfp4_ops.h) instead of the int4 ones: x and a as
+// natural-order fp16 operands with one power-of-two prescale per token or
+// assignment (no Hadamard), E2M1 codes times their E4M3 block scales, and the
+// tensor scales applied to the row sums.
+template <int T, bool NV>
 __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_decode_fused(FusedDecodeArgs A) {
     constexpr int N = kTopK * T;                              // assignments
     constexpr int kSlots = (N + kFuWaves - 1) / kFuWaves;     // down experts (or positions) per wave at most
@@ -290,8 +295,15 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
     if (wave < T) lv = reinterpret_cast<const float4 *>(A.logits + (size_t)wave * kE)[lane];
     constexpr int kRotTasks = (4 * T + kFuWaves - 1) / kFuWaves;   // x quarters per wave
     uint4 xq[kRotTasks];
+    uint4 xn[4];   // NV: wave t < T holds x[t][32 lane .. 32 lane + 32)
     uint4 wsd0 = make_uint4(0, 0, 0, 0), wsd1 = wsd0;
-    if (gu_role) {
+    if (NV && gu_role) {
+        if (wave < T) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                xn[i] = reinterpret_cast<const uint4 *>(A.x + (size_t)wave * kH + 32 * lane + 8 * i)[0];
+        }
+    } else if (gu_role) {
         // task k = (token k / 4, 512-wide quarter k % 4), dealt from the last wave down
 #pragma unroll
         for (int i = 0; i < kRotTasks; ++i) {
@@ -317,7 +329,13 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
             }
         }
     }
-    if (gu_role) {
+    if (NV && gu_role) {
+        // x as natural-order fp16 operands, one prescale per token
+        if (wave < T) {
+            const int sh = natural_x_wave(xn, lane, &U.gu.xt[wave][16 * lane]);
+            if (lane == 0) U.gu.xsc[wave][0] = ldexpf(1.0f, sh);
+        }
+    } else if (gu_role) {
         // rotated x, 4 blocks per task, beside the top-6 (waves from the first up)
 #pragma unroll
         for (int i = 0; i < kRotTasks; ++i) {
@@ -408,20 +426,32 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
             const int ai = bb / kFuBatchesPerExpert, r0 = (bb % kFuBatchesPerExpert) * kFuPairs;
             const int e = uniform(R.act_e[ai]);
             const rsrc_t cg = make_buf(A.codes + (size_t)e * kCodeBytesPerExpert, kCodeBytesGu);
-            const rsrc_t sp = make_buf(A.scales + (size_t)e * kScalesPerExpert, 2 * kScalesGu);
+            const rsrc_t sp = NV ? make_buf(A.nv_scales + (size_t)e * kNvScalePerExpert, kNvScaleGu)
+                                 : make_buf(A.scales + (size_t)e * kScalesPerExpert, 2 * kScalesGu);
 #pragma unroll
             for (int i = 0; i < kFuPairs; ++i) {
                 const int r = r0 + i;
                 G.g[i] = bload16_nt(cg, cv, r * (kH / 2));
                 G.u[i] = bload16_nt(cg, cv, kPlaneGateBytes + r * (kH / 2));
-                G.sg[i] = bload2_nt(sp, sv, 2 * r * (kH / kG));
-                G.su[i] = bload2_nt(sp, sv, 2 * (kScalesGate + r * (kH / kG)));
+                if constexpr (NV) {   // the E4M3 scales of blocks 2 lane, 2 lane + 1
+                    G.sg[i] = bload2_nt(sp, 2 * lane, r * (kH / kNvBlock));
+                    G.su[i] = bload2_nt(sp, 2 * lane, kNvScaleGate + r * (kH / kNvBlock));
+                } else {
+                    G.sg[i] = bload2_nt(sp, sv, 2 * r * (kH / kG));
+                    G.su[i] = bload2_nt(sp, sv, 2 * (kScalesGate + r * (kH / kG)));
+                }
             }
         };
         // a batch's products for every token of its expert (codes in G)
         auto compute = [&](GuBatch &G, int bb) {
             const int ai = bb / kFuBatchesPerExpert, r0 = (bb % kFuBatchesPerExpert) * kFuPairs;
             const int p0 = uniform(R.act_begin[ai]), n = uniform(R.act_n[ai]);
+            float tg = 1.0f, tu = 1.0f;   // NV: the gate and up tensor scales
+            if constexpr (NV) {
+                const int e = uniform(R.act_e[ai]);
+                tg = A.tscales[3 * e];
+                tu = A.tscales[3 * e + 1];
+            }
             for (int k = 0; k < n; ++k) {
                 const int p = p0 + k;
                 const int t = R.perm[p] / kTopK;
@@ -431,23 +461,42 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
                     refresh(G.u[i]);
                 }
                 uint32_t xs[16];
-                const float off = load_operand32(&U.gu.xt[t][lane * 16], xs);
-                const float xsc = U.gu.xsc[t][lane >> 2];
                 float v[2 * kFuPairs];
+                if constexpr (NV) {
+                    const uint4 *src = reinterpret_cast<const uint4 *>(&U.gu.xt[t][lane * 16]);
 #pragma unroll
-                for (int i = 0; i < kFuPairs; ++i) {
+                    for (int i = 0; i < 4; ++i) {
+                        const uint4 w = src[i];
+                        xs[4 * i] = w.x; xs[4 * i + 1] = w.y; xs[4 * i + 2] = w.z; xs[4 * i + 3] = w.w;
+                    }
+                    const float xm = U.gu.xsc[t][0];
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        Q4 q[4];
-                        convert16(h ? G.u[i] : G.g[i], q);
-                        v[2 * i + h] = dot_slice(q, xs, -off) * (bf16_to_f32(h ? G.su[i] : G.sg[i]) * xsc);
+                    for (int i = 0; i < kFuPairs; ++i) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            const uint16_t sc = h ? G.su[i] : G.sg[i];
+                            v[2 * i + h] = dot32_nv(h ? G.u[i] : G.g[i], xs, e4m3_to_f32(sc & 0xffu),
+                                                    e4m3_to_f32(sc >> 8)) * xm;
+                        }
+                    }
+                } else {
+                    const float off = load_operand32(&U.gu.xt[t][lane * 16], xs);
+                    const float xsc = U.gu.xsc[t][lane >> 2];
+#pragma unroll
+                    for (int i = 0; i < kFuPairs; ++i) {
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) {
+                            Q4 q[4];
+                            convert16(h ? G.u[i] : G.g[i], q);
+                            v[2 * i + h] = dot_slice(q, xs, -off) * (bf16_to_f32(h ? G.su[i] : G.sg[i]) * xsc);
+                        }
                     }
                 }
                 // value 2i (gate row r0+i) ends on lanes 32i..32i+15, its up row on the next 16
                 const float red = transpose_reduce<2 * kFuPairs, kWave>(v);
                 const float other = shfl_xor_f(red, 16);
                 if ((lane & 31) == 0)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(silu_f(red) * other), act_buf,
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(silu_f(red * tg) * (other * tu)), act_buf,
                                                           4 * (p * kI + r0 + (lane >> 5)), 0, kHandOff);
             }
         };
@@ -494,12 +543,17 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
         const int e = uniform(R.act_e[ai]);
         const rsrc_t cd = make_buf(A.codes + (size_t)e * kCodeBytesPerExpert + kCodeBytesGu + (size_t)c0 * (kI / 2),
                                    kFuCols * (kI / 2));
-        const rsrc_t sd = make_buf(A.scales + (size_t)e * kScalesPerExpert + kScalesGu + (size_t)c0 * (kI / kG),
-                                   kFuCols * (kI / kG) * 2);
+        const rsrc_t sd =
+            NV ? make_buf(A.nv_scales + (size_t)e * kNvScalePerExpert + kNvScaleGu + (size_t)c0 * (kI / kNvBlock),
+                          kFuCols * (kI / kNvBlock))
+               : make_buf(A.scales + (size_t)e * kScalesPerExpert + kScalesGu + (size_t)c0 * (kI / kG),
+                          kFuCols * (kI / kG) * 2);
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
             dw[s][hf] = bload16_nt(cd, rr * (kI / 2) + 128 * hf + kq * 16, 0);
-            ds[s][hf] = bload2_nt(sd, 2 * (rr * (kI / kG) + 2 * hf + (kq >> 2)), 0);
+            // NV: the E4M3 scales of blocks 16 hf + 2 kq, +1; else the bf16 scale of block 2 hf + kq / 4
+            ds[s][hf] = NV ? bload2_nt(sd, rr * (kI / kNvBlock) + 16 * hf + 2 * kq, 0)
+                           : bload2_nt(sd, 2 * (rr * (kI / kG) + 2 * hf + (kq >> 2)), 0);
         }
     }
 
@@ -577,9 +631,27 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
         for (int i = 0; i < kSlots; ++i) {
             const int p = wave + kFuWaves * i;
-            if (p < N)
-                rotate_act_wave(__builtin_bit_cast(float4, a[i][0]), __builtin_bit_cast(float4, a[i][1]), lane,
-                                &U.dn.at[p][0], &U.dn.atsc[p][0]);
+            if (p < N) {
+                if constexpr (NV) {
+                    // natural-order fp16 operands, one prescale per assignment
+                    const float4 a0 = __builtin_bit_cast(float4, a[i][0]), a1 = __builtin_bit_cast(float4, a[i][1]);
+                    const float v[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                    float amax = 0.0f;
+#pragma unroll
+                    for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(v[k]));
+                    const int sh = prescale_shift(wave_max(amax));
+                    uint4 w;
+                    w.x = pack_half2(ldexpf(v[0], -sh), ldexpf(v[1], -sh));
+                    w.y = pack_half2(ldexpf(v[2], -sh), ldexpf(v[3], -sh));
+                    w.z = pack_half2(ldexpf(v[4], -sh), ldexpf(v[5], -sh));
+                    w.w = pack_half2(ldexpf(v[6], -sh), ldexpf(v[7], -sh));
+                    reinterpret_cast<uint4 *>(&U.dn.at[p][0])[lane] = w;
+                    if (lane == 0) U.dn.atsc[p][0] = ldexpf(1.0f, sh);
+                } else {
+                    rotate_act_wave(__builtin_bit_cast(float4, a[i][0]), __builtin_bit_cast(float4, a[i][1]), lane,
+                                    &U.dn.at[p][0], &U.dn.atsc[p][0]);
+                }
+            }
         }
     }
     __syncthreads();
@@ -590,6 +662,7 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
         const int ai = wave + kFuWaves * s;
         if (ai < n_act) {
             const int p0 = uniform(R.act_begin[ai]), n = uniform(R.act_n[ai]);
+            const float tsd = NV ? A.tscales[3 * uniform(R.act_e[ai]) + 2] : 1.0f;   // NV: down tensor scale
             for (int k = 0; k < n; ++k) {
                 const int p = p0 + k;
                 // operands of K [256h + 32 kq, +32): words 128h + 16 kq .. +15
@@ -597,13 +670,24 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf) {
                     refresh(dw[s][hf]);
-                    Q4 q[4];
-                    convert16(dw[s][hf], q);
                     uint32_t xs[16];
-                    const float off = load_operand32(&U.dn.at[p][128 * hf + 16 * kq], xs);
-                    acc += dot_slice(q, xs, -off) *
-                           (bf16_to_f32(ds[s][hf]) * U.dn.atsc[p][2 * hf + (kq >> 2)]);
+                    if constexpr (NV) {
+                        const uint4 *src = reinterpret_cast<const uint4 *>(&U.dn.at[p][128 * hf + 16 * kq]);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const uint4 w = src[i];
+                            xs[4 * i] = w.x; xs[4 * i + 1] = w.y; xs[4 * i + 2] = w.z; xs[4 * i + 3] = w.w;
+                        }
+                        acc += dot32_nv(dw[s][hf], xs, e4m3_to_f32(ds[s][hf] & 0xffu), e4m3_to_f32(ds[s][hf] >> 8));
+                    } else {
+                        Q4 q[4];
+                        convert16(dw[s][hf], q);
+                        const float off = load_operand32(&U.dn.at[p][128 * hf + 16 * kq], xs);
+                        acc += dot_slice(q, xs, -off) *
+                               (bf16_to_f32(ds[s][hf]) * U.dn.atsc[p][2 * hf + (kq >> 2)]);
+                    }
                 }
+                if constexpr (NV) acc *= U.dn.atsc[p][0] * tsd;
                 acc += shfl_xor_f(acc, 1);
                 acc += shfl_xor_f(acc, 2);
                 acc += shfl_xor_f(acc, 4);
@@ -626,19 +710,6 @@ __global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(4)))
 }
 
 }  // namespace
-
-#define MOE_FUSED_DISPATCH(KERNEL, ...)                                          \
-    switch (T) {                                                                 \
-    case 1: hipLaunchKernelGGL(KERNEL<1>, __VA_ARGS__); break;                   \
-    case 2: hipLaunchKernelGGL(KERNEL<2>, __VA_ARGS__); break;                   \
-    case 3: hipLaunchKernelGGL(KERNEL<3>, __VA_ARGS__); break;                   \
-    case 4: hipLaunchKernelGGL(KERNEL<4>, __VA_ARGS__); break;                   \
-    case 5: hipLaunchKernelGGL(KERNEL<5>, __VA_ARGS__); break;                   \
-    case 6: hipLaunchKernelGGL(KERNEL<6>, __VA_ARGS__); break;                   \
-    case 7: hipLaunchKernelGGL(KERNEL<7>, __VA_ARGS__); break;                   \
-    case 8: hipLaunchKernelGGL(KERNEL<8>, __VA_ARGS__); break;                   \
-    default: break;                                                              \
-    }
 
 #define MOE_FUSED_DISPATCH2(KERNEL, B, ...)                                      \
     switch (T) {                                                                 \
@@ -664,13 +735,16 @@ void launch_router_small(const uint16_t *x, const float *resid, uint16_t *x_out,
     }
 }
 
-#undef MOE_FUSED_DISPATCH2
-
 void launch_decode_fused(const FusedDecodeArgs &args, hipStream_t s) {
     const int T = args.T;
-    MOE_FUSED_DISPATCH(k_decode_fused, dim3(kFuDn0 + kFuDnWgs), dim3(kFuThreads), 0, s, args)
+    if (args.nv_scales) {
+        MOE_FUSED_DISPATCH2(k_decode_fused, true, dim3(kFuDn0 + kFuDnWgs), dim3(kFuThreads), 0, s, args)
+    } else {
+        MOE_FUSED_DISPATCH2(k_decode_fused, false, dim3(kFuDn0 + kFuDnWgs), dim3(kFuThreads), 0, s, args)
+    }
 }
 
-#undef MOE_FUSED_DISPATCH
+#undef MOE_FUSED_DISPATCH2
+
 
 }  // namespace moe_w4

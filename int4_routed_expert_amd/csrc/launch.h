@@ -31,7 +31,9 @@ struct FusedDecodeArgs {
     const float *router_bias;      // fp32 [256] or null
     int router_policy;             // MOE_W4_ROUTER_* flags
     const uint8_t *codes;
-    const uint16_t *scales;
+    const uint16_t *scales;        // int4 experts: bf16 group scales (null for NVFP4)
+    const uint8_t *nv_scales;      // NVFP4 experts: E4M3 block scales (null for int4)
+    const float *tscales;          // NVFP4 experts: fp32 tensor scales [256][3]
     const uint16_t *shared_gu;     // [2048][2048] bf16: gate rows, then up rows
     const uint16_t *shared_down;   // [2048][1024] bf16
     uint16_t *hs;                  // [T][1024] bf16 scratch: the shared expert's h

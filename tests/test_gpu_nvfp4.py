@@ -2,12 +2,13 @@
 
 Inputs: the seeded layer of seed 0 (router, shared expert and the code bytes,
 read as E2M1 codes), seeded E4M3 block scales and fp32 tensor scales.  Sizes
-cover the launch sequences the entry point uses (1-48 tokens: the one-workgroup
-routing; 49-127: top-6 and sort; from 128: the dense router/shared GEMMs), with
-ragged tails of the expert tiles; every output row compared, T = 2048
-included.  Edge cases:
+cover the launch sequences the entry point uses (1-8 tokens: the two-launch
+fused form; 9-48: the parallel routing launch; 49-127: top-6 and sort; from
+128: the dense router/shared GEMMs and MFMA experts), with ragged tails of the
+expert tiles; every output row compared, T = 2048 included.  Edge cases:
 T = 0, zero codes (the routed part vanishes), scales 256 times larger, a NaN
-block scale, and the same result twice.  Bar: that of tests/parity.py.
+block scale, the same result twice, and hand-off waits that give up.  Bar:
+that of tests/parity.py.
 """
 import functools
 
@@ -203,3 +204,26 @@ def test_nvfp4_mfma_hot_expert_chunks(m, layer0, nv):
     assert np.all(g["topk_idx"][:, 0] == 40)
     ref = O.moe_layer_nvfp4(x_bits, P.host_router(SEED), blobs(), P.host_shared(SEED), bias=bias, pool=P.pool())
     report("MFMA hot expert", P.compare(g, ref, label="nvfp4 MFMA hot expert"))
+
+
+@pytest.mark.parametrize("T", [3, 32])
+def test_nvfp4_wait_failure_path(m, layer0, nv, T):
+    """The bounded hand-off waits of the NVFP4 layer, made to give up from the
+    host (a count the producing workgroups never reach, a 200 us bound): at
+    T = 3 the down workgroups of the two-launch form, at T = 32 workgroup 0 of
+    the routing launch.  Every kernel exits normally, y comes out NaN and the
+    error word is set; with the defaults back the same call is correct."""
+    print(f"[nvfp4] failure path T={T}", flush=True)
+    x_bits = synth.gen_x(211, T)
+    ws = m.workspace(T)
+    err = lambda: int(m.ws_view(ws, T, "error", torch.int32, 1).item())
+    try:
+        m.moe_w4_set_fused_wait(20000, 1)
+        g = P.run_gpu(m, x_bits, layer0, ws=ws, nvfp4=nv)
+        assert err() == 1
+        assert np.all(np.isnan(O.bf16_to_f64(g["y_bits"])))
+    finally:
+        m.moe_w4_set_fused_wait(0, 0)
+    g = P.run_gpu(m, x_bits, layer0, ws=ws, nvfp4=nv)
+    assert err() == 0
+    report("after the failure path", P.compare(g, oracle(x_bits), label="nvfp4 after the failure path"))
