@@ -119,7 +119,7 @@ extern "C" {
  *                         second token (= first if one), 0, 0, 0}; records past
  *                         n_active hold expert -1
  *   chunks    i32 [n][4]  from T >= 128 on (MFMA grouped path): {expert, first sorted
- *                         position, rows <= 96, 0} covering each expert's sorted
+ *                         position, rows <= 64, 0} covering each expert's sorted
  *                         positions in order, ascending by expert; n_chunks i32 [1]
  *                         holds n.  (Written at every T; read only on that path.)
  *   logits    f32 [T][256] router logits R x, without the bias

@@ -106,7 +106,7 @@ const char *kStageNames[] = {"router_shared_gateup", "topk_sort", "routed_gateup
 constexpr int kStages = sizeof(kStageNames) / sizeof(kStageNames[0]);
 
 // From this many tokens on, the routed experts run as MFMA grouped products
-// (chunks of up to 96 tokens per expert) and the router and shared expert as
+// (chunks of up to 64 tokens per expert) and the router and shared expert as
 // LDS-tiled GEMMs; below it, as streaming GEMVs and few-row MFMA products.
 constexpr int kPrefillMinTokens = 128;
 
@@ -395,7 +395,7 @@ int run_forward_nvfp4(const void *x_, const void *router_w_, const void *codes_,
     }
     NV_MARK();
     if (dense) {
-        // MFMA tiles over chunks of up to 96 assignments of one expert
+        // MFMA tiles over chunks of up to 64 assignments of one expert
         NV_STEP(launch_gateup_mfma_nvfp4(codes, scales, tscales, xt, xt_scale, perm, chunks, n_chunks, T,
                                          ws_at<uint32_t>(ws, L.at), ws_at<float>(ws, L.at_scale), s));
         NV_MARK();

@@ -6,7 +6,7 @@
 // layout (NInfer README of Flint, "What is inside"): per expert, gate rows then
 // up rows (2 x 512, K = 2048) and 2,048 down rows (K = 512).
 //
-// Work unit: a chunk of at most 96 sorted assignments of one expert (the chunk
+// Work unit: a chunk of at most 64 sorted assignments of one expert (the chunk
 // list comes from the sort) times a tile of weight rows.  Every code byte of
 // the tile is read from HBM once per chunk and turned into exact fp16 values
 // in registers: the mask trick of int4x8_to_q gives 1024+u and 1024+16u, and
@@ -52,7 +52,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kChunkRows = 96;   // assignments per chunk: up to three 32-row MFMA tiles
 constexpr int kXcds = 8;
 
 __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
@@ -113,6 +112,19 @@ __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// wait_vmcnt with a count that is a constant once the loop around the call
+// is unrolled (one case survives); a count above the table waits for all
+__device__ __forceinline__ void wait_vmcnt_n(int n) {
+    switch (n) {
+#define MOE_VM(k) \
+    case k: wait_vmcnt<k>(); break;
+        MOE_VM(1) MOE_VM(2) MOE_VM(3) MOE_VM(4) MOE_VM(5) MOE_VM(6) MOE_VM(7) MOE_VM(8) MOE_VM(9) MOE_VM(10)
+        MOE_VM(11) MOE_VM(12) MOE_VM(13) MOE_VM(14) MOE_VM(15) MOE_VM(16) MOE_VM(17) MOE_VM(18) MOE_VM(19)
+        MOE_VM(20) MOE_VM(21) MOE_VM(22) MOE_VM(23) MOE_VM(24)
+#undef MOE_VM
+    default: wait_vmcnt<0>(); break;
+    }
+}
 // the same, and every LDS access of this wave completed (lgkmcnt 0)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_lds() {
@@ -137,11 +149,16 @@ template <int N>
 struct Tiles {
     static constexpr int value = N;
 };
-template <class F>
+template <int MaxTiles, class F>
 __device__ __forceinline__ void with_tiles(int n_mt, F &&f) {
-    if (n_mt >= 3)
-        f(Tiles<3>{});
-    else if (n_mt == 2)
+    static_assert(MaxTiles == 2 || MaxTiles == 3, "two or three 32-row tiles at most");
+    if constexpr (MaxTiles == 3) {
+        if (n_mt >= 3) {
+            f(Tiles<3>{});
+            return;
+        }
+    }
+    if (n_mt >= 2)
         f(Tiles<2>{});
     else
         f(Tiles<1>{});
@@ -182,7 +199,7 @@ __device__ __forceinline__ half2_t scaled_half2(uint32_t word2, int hi, int k) {
 // =========================================================================
 // gate/up + SwiGLU + rotation of a
 //
-// The chunk's A block (up to 96 rows) lives in LDS as [row][16 groups of 16 B]
+// The chunk's A block (up to 64 rows) lives in LDS as [row][16 groups of 16 B]
 // with group position grp ^ (row & 15): unpadded rows (one wave's direct
 // global->LDS load fills 4 whole rows) whose MFMA reads still hit 16
 // different 4-bank slots for 16 consecutive rows.  A three-slot ring keeps
@@ -191,9 +208,66 @@ __device__ __forceinline__ half2_t scaled_half2(uint32_t word2, int hi, int k) {
 // scales normalised by one power of two), so the MFMA accumulates over the
 // whole of K and the normalisation is undone once at the end.
 // =========================================================================
-constexpr int kGuBuf = kChunkRows * 256;   // one A block: 96 rows x 128 fp16
-constexpr int kGuRing = 3;
-constexpr int kGuCodeRing = 4;
+constexpr int kGuBuf = kChunkRows * 256;   // one A block: 64 rows x 128 fp16
+// (a fourth A slot, three blocks in flight, measured no faster)
+constexpr int kGuRing = 3;                     // A blocks in LDS (kGuRing - 1 in flight)
+constexpr int kGuCodeDist = 3;                 // codes requested this many blocks ahead
+constexpr int kGuCodeRing = kGuCodeDist + 1;
+constexpr int kGuADist = kGuRing - 1;          // A requested this many blocks ahead
+constexpr int kGuBlocks = kH / kG;
+constexpr bool kGuCodesFirst = kGuCodeDist <= kGuADist;   // order of the two requests of a block
+
+// Issue order of the main loop's loads: codes(0 .. Dc-1) and A(0 .. Da-1) in
+// the prologue, then per block b codes(b + Dc) and A(b + Da) (those below the
+// block count; codes first if kGuCodesFirst).  The waits count on it: the
+// number of loads requested after A(b + 1) up to the end of block b (F loads
+// per codes block, NI per A block) may stay in flight when block b + 1 starts.
+__host__ __device__ constexpr int gu_loads_after_a(int b, int ni, int f) {
+    int n = 0;
+    bool seen = false;
+    for (int k = 0; k < kGuADist; ++k) {
+        if (seen) n += ni;
+        if (k == b + 1) seen = true;
+    }
+    for (int k = 0; k <= b; ++k) {
+        const bool c = k + kGuCodeDist < kGuBlocks, a = k + kGuADist < kGuBlocks;
+        if (kGuCodesFirst && c && seen) n += f;
+        if (a) {
+            if (seen) n += ni;
+            if (k + kGuADist == b + 1) seen = true;
+        }
+        if (!kGuCodesFirst && c && seen) n += f;
+    }
+    return n;
+}
+// ... which covers codes(b + 1) only if it was requested before A(b + 1)
+__host__ __device__ constexpr bool gu_codes_before_a() {
+    for (int b = 0; b + 1 < kGuBlocks; ++b) {
+        int pos = 0, pc = -1, pa = -1;
+        for (int k = 0; k < kGuCodeDist; ++k, ++pos)
+            if (k == b + 1) pc = pos;
+        for (int k = 0; k < kGuADist; ++k, ++pos)
+            if (k == b + 1) pa = pos;
+        for (int k = 0; k < kGuBlocks; ++k) {
+            const int ci = k + kGuCodeDist, ai = k + kGuADist;
+            if (kGuCodesFirst) {
+                if (ci == b + 1) pc = pos;
+                ++pos;
+                if (ai == b + 1) pa = pos;
+                ++pos;
+            } else {
+                if (ai == b + 1) pa = pos;
+                ++pos;
+                if (ci == b + 1) pc = pos;
+                ++pos;
+            }
+        }
+        if (pc > pa) return false;
+    }
+    return true;
+}
+static_assert(gu_codes_before_a(), "codes(b+1) must be requested before A(b+1)");
+static_assert(kGuRing == 3 || kGuRing == 4, "three or four LDS slots");
 
 // NVFP4 block scales of an expert: gate [512][128], up [512][128], down [2048][32] bytes
 constexpr uint32_t kNvScGate = (uint32_t)kI * kH / 16;
@@ -220,23 +294,29 @@ template <bool NV>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gateup_mfma(
     const uint8_t *__restrict__ codes, const void *__restrict__ scales_, const float *__restrict__ tscales,
     const uint32_t *__restrict__ xt, const float *__restrict__ xt_scale, const int *__restrict__ perm,
-    const int4 *__restrict__ chunks, const int *__restrict__ n_chunks, uint32_t *__restrict__ at,
+    const int4 *__restrict__ chunks, const int *__restrict__ n_chunks, int chunk_cap, uint32_t *__restrict__ at,
     float *__restrict__ at_scale) {
-    // three separate arrays rather than one: the compiler then knows that a
-    // block's reads do not alias the direct loads in flight into the other two
-    // slots and does not wait for those loads before every LDS read
-    __shared__ __attribute__((aligned(16))) uint8_t ring0[kGuBuf], ring1[kGuBuf], ring2[kGuBuf];
+    // separate arrays rather than one: the compiler then knows that a block's
+    // reads do not alias the direct loads in flight into the other slots and
+    // does not wait for those loads before every LDS read
+    __shared__ __attribute__((aligned(16))) uint8_t ring0[kGuBuf], ring1[kGuBuf], ring2[kGuBuf],
+        ring3[kGuRing > 3 ? kGuBuf : 16];
     __shared__ float row_p[kChunkRows];
-    auto slot_ptr = [&](int slot) -> uint8_t * { return slot == 0 ? ring0 : slot == 1 ? ring1 : ring2; };
+    auto slot_ptr = [&](int slot) -> uint8_t * {
+        return slot == 0 ? ring0 : slot == 1 ? ring1 : slot == 2 ? ring2 : ring3;
+    };
     int chunk, nt;
     chunk_tile(kI / kG, chunk, nt);
-    if (chunk >= *n_chunks) return;
-    const int4 ch = chunks[chunk];
+    // the chunk record is read beside the chunk count (one dependent load
+    // less before the codes can be requested); chunk_cap records exist
+    const int nch = *n_chunks;
+    const int4 ch = chunks[min(chunk, chunk_cap - 1)];
+    if (chunk >= nch) return;
     const int e = uniform(ch.x), row0 = uniform(ch.y), rows = uniform(ch.z);
     const int n_mt = uniform((rows + 31) >> 5);   // 32-row MFMA tiles in use
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int n = lane & 31, g = lane >> 5;
-    constexpr int kBlocks = kH / kG;
+    constexpr int kBlocks = kGuBlocks;
 
     // this lane's gate and up rows
     const int gr = kG * nt + 32 * wave + n;
@@ -265,14 +345,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         }
     };
     // the codes and scales depend only on the expert: requested before the
-    // chunk's tokens are looked up.  Issue order: codes(0..2), scales, then
-    // (below) A(0), A(1); per block b: codes(b+3) (4 loads), A(b+2) (NI
-    // loads).  The vmcnt waits count on this order: waiting for A(b+1) also
-    // covers every codes block up to b+2.
+    // chunk's tokens are looked up, then (below) A(0 .. Da-1); the main loop
+    // keeps the order of gu_loads_after_a, whose count of loads after A(b+1)
+    // is what the wait at the end of block b lets stay in flight.
     __builtin_amdgcn_sched_barrier(0);
-    fetch(0, 0);
-    fetch(1, 1);
-    fetch(2, 2);
+#pragma unroll
+    for (int d = 0; d < kGuCodeDist; ++d) fetch(d, d);
     // the 16 block scales of the gate row and of the up row (bf16)
     uint4 sg[2], su[2];
     if constexpr (!NV) {
@@ -285,11 +363,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     if (tid < kChunkRows) row_p[tid] = xt_scale[perm[row0 + min(tid, rows - 1)] / kTopK];
 
     // a = silu(g) * u for this workgroup's 128 columns goes into LDS (fp32)
-    // after the main loop: rows 0..47 in ring0, rows 48..95 in ring1
+    // after the main loop: rows 0..31 in ring0, rows 32..63 in ring1
+    constexpr int kActRowsPerSlot = kGuBuf / (kG * 4);
+    static_assert(2 * kActRowsPerSlot >= kChunkRows, "the fp32 rows of a fit two ring slots");
     auto act_row = [&](int m) -> float * {
-        return reinterpret_cast<float *>(m < 48 ? ring0 : ring1) + (m < 48 ? m : m - 48) * kG;
+        return reinterpret_cast<float *>(m < kActRowsPerSlot ? ring0 : ring1) +
+               (m < kActRowsPerSlot ? m : m - kActRowsPerSlot) * kG;
     };
-    with_tiles(n_mt, [&](auto tiles) {
+    with_tiles<kChunkRows / 32>(n_mt, [&](auto tiles) {
     constexpr int MT = decltype(tiles)::value;
     // A loads of the 32*MT rows in use: NI instructions per wave, 4 rows (1 KB)
     // each; lane l writes position l & 15 of row 4*(NI*w + i) + (l >> 4)
@@ -308,11 +389,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
                                              (lds_void_t *)(slot_ptr(slot) + 4 * (NI * wave + i) * 256), 16, 0, 0);
     };
     __builtin_amdgcn_sched_barrier(0);
-    issue_a(0, 0);
-    issue_a(1, 1);
+#pragma unroll
+    for (int d = 0; d < kGuADist; ++d) issue_a(d, d);
     __builtin_amdgcn_sched_barrier(0);
     const int kg = NV ? 0 : scale_shift(sg[0], sg[1]), ku = NV ? 0 : scale_shift(su[0], su[1]);
-    wait_vmcnt_lds<NI>();   // A(0) and the row_p stores done (A(1) may be in flight)
+    wait_vmcnt_lds<(kGuADist - 1) * NI>();   // A(0) and the row_p stores done (later A blocks may be in flight)
     block_barrier();
 
     f32x16_t accg[MT], accu[MT];
@@ -326,8 +407,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         const uint8_t *buf = slot_ptr(b % kGuRing);
         const int cs = b % kGuCodeRing;
         __builtin_amdgcn_sched_barrier(0);
-        if (b + 3 < kBlocks) fetch((b + 3) % kGuCodeRing, b + 3);
-        if (b + 2 < kBlocks) issue_a((b + 2) % kGuRing, b + 2);
+        if (kGuCodesFirst && b + kGuCodeDist < kBlocks) fetch((b + kGuCodeDist) % kGuCodeRing, b + kGuCodeDist);
+        if (b + kGuADist < kBlocks) issue_a((b + kGuADist) % kGuRing, b + kGuADist);
+        if (!kGuCodesFirst && b + kGuCodeDist < kBlocks) fetch((b + kGuCodeDist) % kGuCodeRing, b + kGuCodeDist);
         __builtin_amdgcn_sched_barrier(0);
         half2_t s_g, s_u, ng[4], nu[4];
         if constexpr (NV) {
@@ -360,14 +442,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             }
         }
         // codes(b+1) and A(b+1) must have landed for every wave before the
-        // next block; after A(b+1) only codes(b+3) and A(b+2) were issued
+        // next block; what was requested after A(b+1) may stay in flight
         __builtin_amdgcn_sched_barrier(0);
-        if (b + 3 < kBlocks)
-            wait_vmcnt<kFetchLoads + NI>();
-        else if (b + 2 < kBlocks)
-            wait_vmcnt<NI>();
-        else if (b + 1 < kBlocks)
-            wait_vmcnt<0>();
+        if (b + 1 < kBlocks) wait_vmcnt_n(gu_loads_after_a(b, NI, kFetchLoads));
         block_barrier();
     }
     mfma_drain();
@@ -449,9 +526,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
 // =========================================================================
 // down: four workgroups own a chunk, each a quarter of the 2048 output
-// features in tiles of 128 (32 per wave, two wave groups), with the chunk's A
-// (96 rows x 512 fp16) staged in LDS; the codes of the next tile are in
-// flight during each tile.  The MFMA runs transposed (codes as the row operand, tokens as the
+// features in four tiles of 128 (32 per wave), with the chunk's A (64 rows x
+// 512 fp16) staged in LDS.  At ~73 KB of LDS two workgroups share a CU, so
+// one stages its rows while the other multiplies (with chunks of 96 rows,
+// one workgroup per CU left every staging exposed).  The codes of the next
+// tile are in flight during each tile.  The MFMA runs transposed (codes as the row operand, tokens as the
 // column operand), so a lane ends with 4 consecutive features of one token
 // per group.  o is stored in fp16 with one power-of-two multiplier per row
 // (o_scale), which halves the traffic of the fp32 rows at a relative rounding
@@ -471,41 +550,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 // normalisations are undone once per output.
 // =========================================================================
 constexpr int kDnPitch = 1040;   // bytes per LDS row (1024 + 16)
-constexpr int kDnParts = 4;      // workgroups per chunk, each over a quarter of the features
-constexpr int kDnHalves = 2;     // wave groups of the workgroup, each over half of its features
-constexpr int kDnTiles = kH / 128 / kDnParts / kDnHalves;
+constexpr int kDnParts = 4;              // workgroups per chunk, each over a quarter of the features
+constexpr int kDnFeat = kH / kDnParts;   // features of one workgroup
+constexpr int kDnTiles = kDnFeat / 128;  // 128-feature tiles of a workgroup (32 features per wave)
 constexpr int kDnCodeRing = 2;
 
 // NVFP4 (NV): no scale normalisation; each lane's four E4M3 scales of a
 // block come with its codes, and o is written as fp32 rows (o_scale unused).
 template <bool NV>
-__global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu(2))) void k_down_mfma(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_down_mfma(
     const uint8_t *__restrict__ codes, const void *__restrict__ scales_, const float *__restrict__ tscales,
     const uint32_t *__restrict__ at, const float *__restrict__ at_scale, const int4 *__restrict__ chunks,
-    const int *__restrict__ n_chunks, void *__restrict__ o_, float *__restrict__ o_scale) {
+    const int *__restrict__ n_chunks, int chunk_cap, void *__restrict__ o_, float *__restrict__ o_scale) {
     const uint16_t *scales = static_cast<const uint16_t *>(scales_);
     uint16_t *o = static_cast<uint16_t *>(o_);
     __shared__ __attribute__((aligned(16))) uint8_t lds[kChunkRows * kDnPitch];
     __shared__ float fk_wave[4];                                              // largest 2^-k per wave
     __shared__ float row_p[kChunkRows];                                       // per token
-    __shared__ __attribute__((aligned(16))) uint16_t sc[kI / kG][kH];         // [block][feature] bf16
-    __shared__ __attribute__((aligned(16))) float fk[kH];                     // 2^-k per feature
+    __shared__ __attribute__((aligned(16))) uint16_t sc[kI / kG][kDnFeat];    // [block][feature] bf16
+    __shared__ __attribute__((aligned(16))) float fk[kDnFeat];                // 2^-k per feature
     // four workgroups per chunk (one per quarter of the features, on one XCD
-    // so that they share the chunk's activations in L2): one workgroup per
-    // chunk left the grid at ~1.1 rounds of the 256 CUs at T = 2048
+    // so that they share the chunk's activations and codes in L2): one
+    // workgroup per chunk left the grid at ~1.1 rounds of the CUs at T = 2048
     int chunk, quarter;
     chunk_tile(kDnParts, chunk, quarter);
-    if (chunk >= *n_chunks) return;
-    const int4 ch = chunks[chunk];
+    const int nch = *n_chunks;
+    const int4 ch = chunks[min(chunk, chunk_cap - 1)];   // beside the count, as in gate/up
+    if (chunk >= nch) return;
     const int e = uniform(ch.x), row0 = uniform(ch.y), rows = uniform(ch.z);
     const int n_mt = uniform((rows + 31) >> 5);
-    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id() & 3, half = wave_id() >> 2;
+    const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int n = lane & 31, g = lane >> 5;
 
     const __amdgpu_buffer_rsrc_t cres =
         make_buf(codes + (size_t)e * kCodeBytesPerExpert + kCodeBytesGu, (uint32_t)(kH * kI / 2));
-    // the feature whose codes this lane loads, in tile 0 of its half
-    const int fh = quarter * (kH / kDnParts) + half * (kH / kDnParts / kDnHalves);
+    // the feature whose codes this lane loads, in tile 0
+    const int fh = quarter * kDnFeat;
     const int f0 = fh + 32 * wave + n;
     const __amdgpu_buffer_rsrc_t nsres =
         make_buf(static_cast<const uint8_t *>(scales_) + (size_t)e * kNvScPerExpert + kNvScGu, kH * kI / 16);
@@ -526,63 +606,21 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
     };
     // the chunk's activations are needed first: thread -> (row, part), load
     // i takes the row's 16-byte group 4i + part (block i / 4); the codes of
-    // the first tiles are requested right behind them
-    const bool stager = tid < 4 * kChunkRows;
+    // the first tile are requested right behind them
+    static_assert(4 * kChunkRows == 256, "one thread per quarter row");
     const int srow = tid >> 2, part = tid & 3;
     uint4 v[16];
     float4 ps;
     __builtin_amdgcn_sched_barrier(0);
-    if (stager) {
+    {
         const int p = row0 + min(srow, rows - 1);
         const uint4 *src = reinterpret_cast<const uint4 *>(at + (size_t)p * (kI / 2)) + part;
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = src[4 * i];
         ps = *reinterpret_cast<const float4 *>(at_scale + (size_t)p * (kI / kG));
     }
-    // the expert's down scales: thread t < 256 takes features 8t..8t+7
-    uint4 s4[4];
-    if (!NV && tid < 256) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(scales + (size_t)e * kScalesPerExpert + kScalesGu) + 4 * tid;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) s4[i] = src[i];
-    }
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int d = 0; d < kDnCodeRing - 1; ++d) fetch(d, d);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // the down scales transposed to [block][feature], and each feature's
-    // normalisation
-    if (!NV && tid < 256) {
-        const uint32_t w[16] = {s4[0].x, s4[0].y, s4[0].z, s4[0].w, s4[1].x, s4[1].y, s4[1].z, s4[1].w,
-                                s4[2].x, s4[2].y, s4[2].z, s4[2].w, s4[3].x, s4[3].y, s4[3].z, s4[3].w};
-        // feature f = 8t + k holds blocks 0,1 in w[2k] and 2,3 in w[2k+1]
-#pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
-            uint32_t t4[4];
-#pragma unroll
-            for (int k2 = 0; k2 < 4; ++k2) {
-                const uint32_t lo = w[2 * (2 * k2) + (bb >> 1)], hi = w[2 * (2 * k2 + 1) + (bb >> 1)];
-                const uint32_t a0 = (bb & 1) ? (lo >> 16) : (lo & 0xffffu);
-                const uint32_t a1 = (bb & 1) ? (hi >> 16) : (hi & 0xffffu);
-                t4[k2] = a0 | (a1 << 16);
-            }
-            *reinterpret_cast<uint4 *>(&sc[bb][8 * tid]) = make_uint4(t4[0], t4[1], t4[2], t4[3]);
-        }
-        // the expert's largest normalisation, over the features with a
-        // nonzero scale (an all-zero feature's outputs are 0 whatever it is)
-        float fmax = 0.0f;
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float f = ldexpf(1.0f, -scale_shift4(w[2 * k], w[2 * k + 1]));
-            fk[8 * tid + k] = f;
-            if ((w[2 * k] | w[2 * k + 1]) & 0x7f807f80u) fmax = fmaxf(fmax, f);
-        }
-        fmax = wave_max(fmax);
-        if (lane == 0) fk_wave[wave] = fmax;
-    }
-    // stage the activations, each block brought to the row's largest prescale
-    if (stager) {
+    // each block brought to the row's largest prescale, into LDS
+    auto stage_store = [&]() {
         const float pm = fmaxf(fmaxf(ps.x, ps.y), fmaxf(ps.z, ps.w));
         const float pb[4] = {ps.x / pm, ps.y / pm, ps.z / pm, ps.w / pm};   // exact powers of two <= 1
 #pragma unroll
@@ -600,23 +638,70 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
         for (int i = 0; i < 16; ++i) *reinterpret_cast<uint4 *>(lds + srow * kDnPitch + part * 16 + 64 * i) = v[i];
         if (part == 0) row_p[srow] = pm;
+    };
+    // the expert's down scales: thread t < 256 takes features 8t..8t+7
+    uint4 s4[4];
+    if (!NV) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(scales + (size_t)e * kScalesPerExpert + kScalesGu) + 4 * tid;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s4[i] = src[i];
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int d = 0; d < kDnCodeRing - 1; ++d) fetch(d, d);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // the down scales transposed to [block][feature], and each feature's
+    // normalisation
+    if (!NV) {
+        const uint32_t w[16] = {s4[0].x, s4[0].y, s4[0].z, s4[0].w, s4[1].x, s4[1].y, s4[1].z, s4[1].w,
+                                s4[2].x, s4[2].y, s4[2].z, s4[2].w, s4[3].x, s4[3].y, s4[3].z, s4[3].w};
+        // feature f = 8t + k holds blocks 0,1 in w[2k] and 2,3 in w[2k+1];
+        // the workgroup keeps its own features' scales (all of them give the
+        // expert's largest normalisation)
+        const int f_lo = quarter * kDnFeat;
+        const bool own = 8 * tid >= f_lo && 8 * tid < f_lo + kDnFeat;
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+            uint32_t t4[4];
+#pragma unroll
+            for (int k2 = 0; k2 < 4; ++k2) {
+                const uint32_t lo = w[2 * (2 * k2) + (bb >> 1)], hi = w[2 * (2 * k2 + 1) + (bb >> 1)];
+                const uint32_t a0 = (bb & 1) ? (lo >> 16) : (lo & 0xffffu);
+                const uint32_t a1 = (bb & 1) ? (hi >> 16) : (hi & 0xffffu);
+                t4[k2] = a0 | (a1 << 16);
+            }
+            if (own) *reinterpret_cast<uint4 *>(&sc[bb][8 * tid - f_lo]) = make_uint4(t4[0], t4[1], t4[2], t4[3]);
+        }
+        // the expert's largest normalisation, over the features with a
+        // nonzero scale (an all-zero feature's outputs are 0 whatever it is)
+        float fmax = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float f = ldexpf(1.0f, -scale_shift4(w[2 * k], w[2 * k + 1]));
+            if (own) fk[8 * tid - f_lo + k] = f;
+            if ((w[2 * k] | w[2 * k + 1]) & 0x7f807f80u) fmax = fmaxf(fmax, f);
+        }
+        fmax = wave_max(fmax);
+        if (lane == 0) fk_wave[wave] = fmax;
+    }
+    stage_store();
     __syncthreads();
-    // o rows of the chunk (fp16) through a buffer descriptor: stores of rows
-    // past the chunk's end fall outside it and are dropped by the hardware
-    // bounds check
-    const __amdgpu_buffer_rsrc_t ores =
-        NV ? make_buf(static_cast<float *>(o_) + (size_t)row0 * kH, (uint32_t)rows * kH * 4)
-           : make_buf(o + (size_t)row0 * kH, (uint32_t)rows * kH * 2);
     float fkmax = NV ? 1.0f : fmaxf(fmaxf(fk_wave[0], fk_wave[1]), fmaxf(fk_wave[2], fk_wave[3]));
     if (fkmax == 0.0f) fkmax = 1.0f;   // every scale of the expert is zero: o is 0
     const float to_half = 0x1p-20f / fkmax;   // a power of two
-    if (!NV && quarter == 0 && tid < rows) o_scale[row0 + tid] = row_p[tid] * fkmax * 0x1p20f;
     const float tsd = NV ? tscales[3 * e + 2] : 1.0f;
+
+    // o rows of the chunk through a buffer descriptor: stores of rows past
+    // its end fall outside it and are dropped by the hardware bounds check
+    const __amdgpu_buffer_rsrc_t ores =
+        NV ? make_buf(static_cast<float *>(o_) + (size_t)row0 * kH, (uint32_t)rows * kH * 4)
+           : make_buf(o + (size_t)row0 * kH, (uint32_t)rows * kH * 2);
+    if (!NV && quarter == 0 && tid < rows) o_scale[row0 + tid] = row_p[tid] * fkmax * 0x1p20f;
 
     // fully unrolled, so ring slots are compile-time; the next tile's codes
     // are requested before this tile's products
-    with_tiles(n_mt, [&](auto tiles) {
+    with_tiles<kChunkRows / 32>(n_mt, [&](auto tiles) {
     constexpr int MT = decltype(tiles)::value;
 #pragma unroll
     for (int t = 0; t < kDnTiles; ++t) {
@@ -636,10 +721,10 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
 #pragma unroll
                 for (int i = 0; i < 4; ++i) ns[b][i] = e4m3_half2(cs4[cs][b], i);
         } else {
-            const int kf = -ilogbf(fk[fl + zero]);
+            const int kf = -ilogbf(fk[fl - quarter * kDnFeat + zero]);
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
-                const _Float16 h = (_Float16)ldexpf(bf16_to_f32(sc[b][fl + zero]), kf);
+                const _Float16 h = (_Float16)ldexpf(bf16_to_f32(sc[b][fl - quarter * kDnFeat + zero]), kf);
                 s2[b] = half2_t{h, h};
             }
         }
@@ -702,7 +787,7 @@ __global__ __launch_bounds__(256 * kDnHalves) __attribute__((amdgpu_waves_per_eu
         }
         float4 kq[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) kq[q] = *reinterpret_cast<const float4 *>(&fk[fb + 8 * q + zero]);
+        for (int q = 0; q < 4; ++q) kq[q] = *reinterpret_cast<const float4 *>(&fk[fb - quarter * kDnFeat + 8 * q + zero]);
         const uint32_t ob = (uint32_t)(n * kH + fb) * 2;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -733,14 +818,14 @@ void launch_gateup_mfma(const uint8_t *codes, const uint16_t *scales, const uint
                         float *at_scale, hipStream_t s) {
     hipLaunchKernelGGL(k_gateup_mfma<false>, dim3(grid_for(T, kI / kG)), dim3(256), 0, s, codes,
                        static_cast<const void *>(scales), nullptr, xt, xt_scale, perm,
-                       reinterpret_cast<const int4 *>(chunks), n_chunks, at, at_scale);
+                       reinterpret_cast<const int4 *>(chunks), n_chunks, max_chunks(T), at, at_scale);
 }
 
 void launch_down_mfma(const uint8_t *codes, const uint16_t *scales, const uint32_t *at, const float *at_scale,
                       const int *chunks, const int *n_chunks, int T, uint16_t *o, float *o_scale, hipStream_t s) {
-    hipLaunchKernelGGL(k_down_mfma<false>, dim3(grid_for(T, kDnParts)), dim3(256 * kDnHalves), 0, s, codes,
+    hipLaunchKernelGGL(k_down_mfma<false>, dim3(grid_for(T, kDnParts)), dim3(256), 0, s, codes,
                        static_cast<const void *>(scales), nullptr, at, at_scale,
-                       reinterpret_cast<const int4 *>(chunks), n_chunks, static_cast<void *>(o), o_scale);
+                       reinterpret_cast<const int4 *>(chunks), n_chunks, max_chunks(T), static_cast<void *>(o), o_scale);
 }
 
 void launch_gateup_mfma_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscales, const uint32_t *xn,
@@ -748,15 +833,15 @@ void launch_gateup_mfma_nvfp4(const uint8_t *codes, const uint8_t *scales, const
                               uint32_t *an, float *an_scale, hipStream_t s) {
     hipLaunchKernelGGL(k_gateup_mfma<true>, dim3(grid_for(T, kI / kG)), dim3(256), 0, s, codes,
                        static_cast<const void *>(scales), tscales, xn, xn_scale, perm,
-                       reinterpret_cast<const int4 *>(chunks), n_chunks, an, an_scale);
+                       reinterpret_cast<const int4 *>(chunks), n_chunks, max_chunks(T), an, an_scale);
 }
 
 void launch_down_mfma_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscales, const uint32_t *an,
                             const float *an_scale, const int *chunks, const int *n_chunks, int T, float *o,
                             hipStream_t s) {
-    hipLaunchKernelGGL(k_down_mfma<true>, dim3(grid_for(T, kDnParts)), dim3(256 * kDnHalves), 0, s, codes,
+    hipLaunchKernelGGL(k_down_mfma<true>, dim3(grid_for(T, kDnParts)), dim3(256), 0, s, codes,
                        static_cast<const void *>(scales), tscales, an, an_scale,
-                       reinterpret_cast<const int4 *>(chunks), n_chunks, static_cast<void *>(o), nullptr);
+                       reinterpret_cast<const int4 *>(chunks), n_chunks, max_chunks(T), static_cast<void *>(o), nullptr);
 }
 
 }  // namespace moe_w4

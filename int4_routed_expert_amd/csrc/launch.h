@@ -76,11 +76,15 @@ void launch_decode_fused(const FusedDecodeArgs &args, hipStream_t s);
 void launch_topk_rotate(const float *logits, const uint16_t *x, int T, const float *bias, int policy,
                         int *topk_idx, float *topk_w, uint32_t *xt, float *xt_scale, hipStream_t s,
                         bool rotate = true);
+// Assignments per chunk of the MFMA grouped kernels: two 32-row MFMA tiles
+// (a chunk's rows of the down projection's A, 64 x 1 KB, then fit in LDS
+// twice per CU).
+constexpr int kChunkRows = 64;
 // Stable counting sort of the 6T assignments by expert (one workgroup).
 // slots: int[256][8] records {expert, first sorted position, count, first
 // token, second token, 0, 0, 0}, one per expert with tokens, then expert -1.
 // chunks: int[max_chunks(T)][4] records {expert, first sorted position, rows
-// (<= 96), 0} covering every expert's assignments; *n_chunks of them.
+// (<= kChunkRows), 0} covering every expert's assignments; *n_chunks of them.
 // The same result from many workgroups (two launches), for prefill sizes:
 // hist is int[sort_hist_blocks(T)][256] scratch.
 int sort_hist_blocks(int T);
@@ -111,9 +115,9 @@ void launch_gateup_gemv(const uint8_t *codes, const uint16_t *scales, const uint
 void launch_down_gemv(const uint8_t *codes, const uint16_t *scales, const float *act, const int *slots, int T,
                       float *o, hipStream_t s);
 
-// Routed experts, MFMA form (prefill): chunks of <= 96 assignments of one
-// expert against tiles of weight rows.  gate/up writes the rotated fp16
-// operands of the down projection directly (at, at_scale).
+// Routed experts, MFMA form (prefill): chunks of <= kChunkRows assignments
+// of one expert against tiles of weight rows.  gate/up writes the rotated
+// fp16 operands of the down projection directly (at, at_scale).
 int max_chunks(int T);
 void launch_gateup_mfma(const uint8_t *codes, const uint16_t *scales, const uint32_t *xt, const float *xt_scale,
                         const int *perm, const int *chunks, const int *n_chunks, int T, uint32_t *at,

@@ -70,7 +70,6 @@ void launch_topk_rotate(const float *logits, const uint16_t *x, int T, const flo
 constexpr int kSortWaves = 16;
 constexpr int kSortBatch = 8;        // chunks of 64 assignments whose loads are issued together
 constexpr int kSortKeep = 16;        // chunks per wave kept in registers between the two passes
-constexpr int kSortChunkRows = 96;   // rows of one chunk of the MFMA grouped kernels
 
 __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx, int T,
                                                int *__restrict__ offsets, int *__restrict__ perm,
@@ -139,7 +138,7 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
         for (int i = 0; i < 4; ++i) {
             c[i] = tot[4 * lane + i];
             f[i] = c[i] > 0;
-            k[i] = (c[i] + kSortChunkRows - 1) / kSortChunkRows;
+            k[i] = (c[i] + kChunkRows - 1) / kChunkRows;
             sc += c[i];
             sf += f[i];
             sk += k[i];
@@ -177,8 +176,8 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
     // chunk list of the MFMA grouped path: {expert, first sorted position, rows, 0}
     if (tid < kE) {
         const int n = tot[tid];
-        for (int r = 0, q = chunk0[tid]; r < n; r += kSortChunkRows, ++q)
-            chunks[q] = make_int4(tid, offs[tid] + r, min(kSortChunkRows, n - r), 0);
+        for (int r = 0, q = chunk0[tid]; r < n; r += kChunkRows, ++q)
+            chunks[q] = make_int4(tid, offs[tid] + r, min(kChunkRows, n - r), 0);
     }
     __syncthreads();
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -308,7 +307,7 @@ __global__ __launch_bounds__(1024) void k_sort_place(const int *__restrict__ top
         for (int i = 0; i < 4; ++i) {
             c[i] = tot[4 * lane + i];
             f[i] = c[i] > 0;
-            k[i] = (c[i] + kSortChunkRows - 1) / kSortChunkRows;
+            k[i] = (c[i] + kChunkRows - 1) / kChunkRows;
             sc += c[i];
             sf += f[i];
             sk += k[i];
@@ -337,8 +336,8 @@ __global__ __launch_bounds__(1024) void k_sort_place(const int *__restrict__ top
                     rec[6] = 0;
                     rec[7] = 0;
                 }
-                for (int r = 0, q = ek; r < c[i]; r += kSortChunkRows, ++q)
-                    chunks[q] = make_int4(e, ec + r, min(kSortChunkRows, c[i] - r), 0);
+                for (int r = 0, q = ek; r < c[i]; r += kChunkRows, ++q)
+                    chunks[q] = make_int4(e, ec + r, min(kChunkRows, c[i] - r), 0);
             }
             ec += c[i];
             ef += f[i];

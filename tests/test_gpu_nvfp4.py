@@ -194,7 +194,7 @@ def test_nvfp4_mfma_zero_codes_and_nan_scale(m, layer0, nv):
 
 
 def test_nvfp4_mfma_hot_expert_chunks(m, layer0, nv):
-    """One expert takes all 200 tokens: chunks of 96, 96 and 8 rows."""
+    """One expert takes all 200 tokens: chunks of 64, 64, 64 and 8 rows."""
     T = 200
     print("[nvfp4] case MFMA hot expert", flush=True)
     x_bits = synth.gen_x(19, T)

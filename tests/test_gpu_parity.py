@@ -85,7 +85,7 @@ def test_layer_small_T(m, layer0, T):
 
 
 # ------------------------------------------------- MFMA grouped path (T >= 128)
-CHUNK_ROWS = 96   # rows of one chunk of the grouped kernels (include/moe_w4.h)
+CHUNK_ROWS = 64   # rows of one chunk of the grouped kernels (include/moe_w4.h)
 
 
 def expected_chunks(offsets):
@@ -118,7 +118,7 @@ def test_grouped_path_all_rows(m, layer0, T):
 
 
 def test_grouped_chunks_of_a_hot_expert(m, layer0):
-    """One expert takes all 200 tokens: chunks of 96, 96 and a ragged 8."""
+    """One expert takes all 200 tokens: chunks of 64, 64, 64 and a ragged 8."""
     T = 200
     x = synth.gen_x(402, T)
     bias = np.zeros(256, dtype=np.float32)
@@ -128,8 +128,8 @@ def test_grouped_chunks_of_a_hot_expert(m, layer0):
     assert np.all(g["topk_idx"][:, 0] == 17)
     ch = read_chunks(m, ws, T)
     np.testing.assert_array_equal(ch, expected_chunks(g["offsets"]))
-    assert (ch[:, 0] == 17).sum() == 3 and ch[ch[:, 0] == 17][-1, 2] == 8
-    tokens = np.array([0, 1, 31, 32, 63, 64, 95, 96, 191, 192, 199])
+    assert (ch[:, 0] == 17).sum() == 4 and ch[ch[:, 0] == 17][-1, 2] == 8
+    tokens = np.array([0, 1, 31, 32, 63, 64, 95, 96, 127, 128, 191, 192, 199])
     report("grouped hot expert", P.compare(g, oracle_layer(x, bias=bias, tokens=tokens), tokens=tokens,
                                            label="grouped hot expert"))
 
