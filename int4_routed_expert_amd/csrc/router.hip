@@ -17,33 +17,34 @@ namespace moe_w4 {
 // ROTATE: xt gets the fwht128-rotated x in the int4 experts' operand order;
 // otherwise x itself as natural-order fp16 (the NVFP4 experts' operands).
 template <bool ROTATE>
-__global__ __launch_bounds__(256) void k_topk_rotate(const float *__restrict__ logits,
+__global__ __launch_bounds__(512) void k_topk_rotate(const float *__restrict__ logits,
                                                      const uint16_t *__restrict__ x, int T,
                                                      int *__restrict__ topk_idx,
                                                      float *__restrict__ topk_w,
                                                      uint32_t *__restrict__ xt,
                                                      float *__restrict__ xt_scale, RouterPolicy rp) {
+    // two waves per token, side by side: waves 0-3 select the top-6 of tokens
+    // 4b .. 4b+3, waves 4-7 turn the same tokens' x into operands (the two
+    // are independent; one wave doing both ran the chains back to back)
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t = blockIdx.x * 4 + wave;
+    const int t = blockIdx.x * 4 + (wave & 3);
     if (t >= T) return;
-
-    // x is independent of the logits: its loads go out first, so the two
-    // memory round trips overlap
-    uint4 xq[4];
-    {
-        const uint4 *xp = reinterpret_cast<const uint4 *>(x + (size_t)t * kH + lane * 32);
+    if (wave < 4) {
+        const float4 lv = reinterpret_cast<const float4 *>(logits + (size_t)t * kE)[lane];
+        const Top6 sel = top6_wave(lv, lane, rp);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) xq[i] = xp[i];
-    }
-    const float4 lv = reinterpret_cast<const float4 *>(logits + (size_t)t * kE)[lane];
-    const Top6 sel = top6_wave(lv, lane, rp);
-#pragma unroll
-    for (int j = 0; j < kTopK; ++j) {
-        if (lane == j) {
-            topk_idx[(size_t)t * kTopK + j] = sel.e[j];
-            topk_w[(size_t)t * kTopK + j] = sel.w[j];
+        for (int j = 0; j < kTopK; ++j) {
+            if (lane == j) {
+                topk_idx[(size_t)t * kTopK + j] = sel.e[j];
+                topk_w[(size_t)t * kTopK + j] = sel.w[j];
+            }
         }
+        return;
     }
+    uint4 xq[4];
+    const uint4 *xp = reinterpret_cast<const uint4 *>(x + (size_t)t * kH + lane * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xq[i] = xp[i];
     const int sh = ROTATE ? rotate_x_wave(xq, lane, xt + (size_t)t * (kH / 2) + lane * 16)
                           : natural_x_wave(xq, lane, xt + (size_t)t * (kH / 2) + lane * 16);
     if (lane == 0) xt_scale[t] = ldexpf(1.0f, sh);
@@ -52,10 +53,10 @@ __global__ __launch_bounds__(256) void k_topk_rotate(const float *__restrict__ l
 void launch_topk_rotate(const float *logits, const uint16_t *x, int T, const float *bias, int policy,
                         int *topk_idx, float *topk_w, uint32_t *xt, float *xt_scale, hipStream_t s, bool rotate) {
     if (rotate)
-        hipLaunchKernelGGL(k_topk_rotate<true>, dim3((T + 3) / 4), dim3(256), 0, s, logits, x, T, topk_idx, topk_w,
+        hipLaunchKernelGGL(k_topk_rotate<true>, dim3((T + 3) / 4), dim3(512), 0, s, logits, x, T, topk_idx, topk_w,
                            xt, xt_scale, RouterPolicy{bias, policy});
     else
-        hipLaunchKernelGGL(k_topk_rotate<false>, dim3((T + 3) / 4), dim3(256), 0, s, logits, x, T, topk_idx,
+        hipLaunchKernelGGL(k_topk_rotate<false>, dim3((T + 3) / 4), dim3(512), 0, s, logits, x, T, topk_idx,
                            topk_w, xt, xt_scale, RouterPolicy{bias, policy});
 }
 
