@@ -221,7 +221,9 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
         return MOE_W4_OK;
     }
     if (grouped)
-        MOE_STEP(launch_router_and_shared_gateup_dense(x, T, router_w, nullptr, logits, shared_w, hs, s));
+        // (it also zeroes the sort's histograms, which the top-6 launch fills)
+        MOE_STEP(launch_router_and_shared_gateup_dense(x, T, router_w, nullptr, logits, shared_w, hs, s,
+                                                       ws_at<int>(ws, L.hist), kE * sort_hist_blocks(T)));
     else if (small_route)
         // up to kRouteSmallMaxTokens tokens: the router, the shared gate/up
         // and the rotation of x in one launch, which also clears the counter
@@ -238,10 +240,11 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
                                   g_wait_extra.load(std::memory_order_relaxed),
                                   g_wait_ticks.load(std::memory_order_relaxed), s));
     } else {
-        MOE_STEP(launch_topk_rotate(logits, x, T, bias, policy, topk_idx, topk_w, xt, xt_scale, s));
+        MOE_STEP(launch_topk_rotate(logits, x, T, bias, policy, topk_idx, topk_w, xt, xt_scale, s, true,
+                                    grouped ? ws_at<int>(ws, L.hist) : nullptr));
         if (grouped)   // many workgroups
             MOE_STEP(launch_sort_wide(topk_idx, T, ws_at<int>(ws, L.hist), offsets, perm, pos, n_active, active,
-                                      chunks, n_chunks, error_clear, s));
+                                      chunks, n_chunks, error_clear, s, true));
         else
             MOE_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, error_clear,
                                  s));
@@ -374,7 +377,8 @@ int run_forward_nvfp4(const void *x_, const void *router_w_, const void *codes_,
         return MOE_W4_OK;
     }
     if (dense)
-        NV_STEP(launch_router_and_shared_gateup_dense(x, T, router_w, nullptr, logits, shared_w, hs, s));
+        NV_STEP(launch_router_and_shared_gateup_dense(x, T, router_w, nullptr, logits, shared_w, hs, s,
+                                                      ws_at<int>(ws, L.hist), kE * sort_hist_blocks(T)));
     else
         NV_STEP(launch_router_and_shared_gateup(x, T, router_w, nullptr, logits, shared_w, hs, nullptr, xt_scale,
                                                 small_route ? counters : nullptr, s));
@@ -386,10 +390,11 @@ int run_forward_nvfp4(const void *x_, const void *router_w_, const void *codes_,
     } else {
         // from 128 tokens on x as natural-order fp16 for the MFMA experts (the
         // GEMVs below that read x itself)
-        NV_STEP(launch_topk_rotate(logits, x, T, bias, 0, topk_idx, topk_w, xt, xt_scale, s, false));
+        NV_STEP(launch_topk_rotate(logits, x, T, bias, 0, topk_idx, topk_w, xt, xt_scale, s, false,
+                                   dense ? ws_at<int>(ws, L.hist) : nullptr));
         if (dense)
             NV_STEP(launch_sort_wide(topk_idx, T, ws_at<int>(ws, L.hist), offsets, perm, pos, n_active, active,
-                                     chunks, n_chunks, error, s));
+                                     chunks, n_chunks, error, s, true));
         else
             NV_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, error, s));
     }

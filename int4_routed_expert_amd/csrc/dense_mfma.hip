@@ -50,6 +50,8 @@ struct DenseJob {
 };
 struct DenseJobs {
     DenseJob job[2];
+    int *clear;    // n_clear ints zeroed by the first workgroups (256 each), or null
+    int n_clear;
 };
 
 __device__ __forceinline__ f32x16_t mfma_bf16(uint4 a, uint4 b, f32x16_t c) {
@@ -71,6 +73,10 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
     constexpr int kSteps = K / kStepK;
     static_assert(kSteps >= 3, "pipeline prologue");
     __shared__ __attribute__((aligned(16))) uint8_t sa[2][kSlotBytes], sb[2][kSlotBytes];
+    if (jobs.clear) {
+        const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
+        if (i < jobs.n_clear) jobs.clear[i] = 0;
+    }
 
     // work item: XCD-aware when there are enough m tiles (each XCD keeps a
     // few m tiles' A rows in its L2 and walks all n tiles), else linear
@@ -251,15 +257,18 @@ static void launch_dense(const uint16_t *A, int M, const DenseJobs &jobs, hipStr
 }
 
 void launch_router_and_shared_gateup_dense(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
-                                           float *logits, const uint16_t *shared_w, uint16_t *hs, hipStream_t s) {
+                                           float *logits, const uint16_t *shared_w, uint16_t *hs, hipStream_t s,
+                                           int *clear, int n_clear) {
     DenseJobs jobs;
+    jobs.clear = clear;
+    jobs.n_clear = n_clear;
     jobs.job[0] = DenseJob{router_w, kE / kTile, kEpiStore, 0, bias, logits, kE};
     jobs.job[1] = DenseJob{shared_w, kIS / 64, kEpiSwiglu, kIS, nullptr, hs, kIS};
     launch_dense<kH>(x, T, jobs, s);
 }
 
 void launch_shared_down_dense(const uint16_t *shared_w, const uint16_t *hs, int T, float *z, hipStream_t s) {
-    DenseJobs jobs;
+    DenseJobs jobs = {};
     jobs.job[0] = DenseJob{shared_w + 2 * kSharedGateElems, kH / kTile, kEpiStore, 0, nullptr, z, kH};
     jobs.job[1] = no_dense_job();
     launch_dense<kIS>(hs, T, jobs, s);
@@ -269,14 +278,14 @@ void launch_shared_down_dense(const uint16_t *shared_w, const uint16_t *hs, int 
 // and 1 are dense SwiGLU MLPs of width 6144; the model card keeps every
 // linear bf16): h = bf16(silu(x Wg^T) * (x Wu^T)), then y = bf16(h Wd^T).
 void launch_dense_mlp_gateup_dense(const uint16_t *x, int T, const uint16_t *w, uint16_t *h, hipStream_t s) {
-    DenseJobs jobs;
+    DenseJobs jobs = {};
     jobs.job[0] = DenseJob{w, kDenseInter / 64, kEpiSwiglu, kDenseInter, nullptr, h, kDenseInter};
     jobs.job[1] = no_dense_job();
     launch_dense<kH>(x, T, jobs, s);
 }
 
 void launch_dense_mlp_down_dense(const uint16_t *w, const uint16_t *h, int T, uint16_t *y, hipStream_t s) {
-    DenseJobs jobs;
+    DenseJobs jobs = {};
     jobs.job[0] = DenseJob{w + 2 * (size_t)kDenseInter * kH, kH / kTile, kEpiStoreBf16, 0, nullptr, y, kH};
     jobs.job[1] = no_dense_job();
     launch_dense<kDenseInter>(h, T, jobs, s);

@@ -73,9 +73,12 @@ void launch_decode_fused(const FusedDecodeArgs &args, hipStream_t s);
 // router launches write the logits without the bias.
 // rotate = false: xt gets x itself as natural-order fp16 with the same
 // per-token prescale (the operands of the NVFP4 experts' MFMA form).
+// hist (or null): the wide sort's int[sort_hist_blocks(T)][256] histograms,
+// zero on entry, which the selections are counted into (the sort then skips
+// its own histogram launch).
 void launch_topk_rotate(const float *logits, const uint16_t *x, int T, const float *bias, int policy,
                         int *topk_idx, float *topk_w, uint32_t *xt, float *xt_scale, hipStream_t s,
-                        bool rotate = true);
+                        bool rotate = true, int *hist = nullptr);
 // Assignments per chunk of the MFMA grouped kernels: two 32-row MFMA tiles
 // (a chunk's rows of the down projection's A, 64 x 1 KB, then fit in LDS
 // twice per CU).
@@ -85,11 +88,12 @@ constexpr int kChunkRows = 64;
 // token, second token, 0, 0, 0}, one per expert with tokens, then expert -1.
 // chunks: int[max_chunks(T)][4] records {expert, first sorted position, rows
 // (<= kChunkRows), 0} covering every expert's assignments; *n_chunks of them.
-// The same result from many workgroups (two launches), for prefill sizes:
-// hist is int[sort_hist_blocks(T)][256] scratch.
+// The same result from many workgroups (two launches, or one when the
+// top-6 launch already counted hist_ready), for prefill sizes: hist is
+// int[sort_hist_blocks(T)][256], the experts' counts per workgroup.
 int sort_hist_blocks(int T);
 void launch_sort_wide(const int *topk_idx, int T, int *hist, int *offsets, int *perm, int *pos, int *n_active,
-                      int *slots, int *chunks, int *n_chunks, int *error, hipStream_t s);
+                      int *slots, int *chunks, int *n_chunks, int *error, hipStream_t s, bool hist_ready = false);
 // error (or null): the workspace's error word, cleared (this sequence cannot fail).
 void launch_sort(const int *topk_idx, int T, int *offsets, int *perm, int *pos, int *n_active,
                  int *slots, int *chunks, int *n_chunks, int *error, hipStream_t s);
@@ -144,8 +148,11 @@ void launch_shared_down_combine(const uint16_t *shared_w, const uint16_t *hs, in
                                 const int *pos, const float *o, uint16_t *y, hipStream_t s);
 
 // The same two launches for many tokens (prefill sizes): LDS-tiled MFMA GEMMs.
+// clear (or null): n_clear ints zeroed by the launch (the wide sort's
+// histograms, which the top-6 launch after it counts into).
 void launch_router_and_shared_gateup_dense(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
-                                           float *logits, const uint16_t *shared_w, uint16_t *hs, hipStream_t s);
+                                           float *logits, const uint16_t *shared_w, uint16_t *hs, hipStream_t s,
+                                           int *clear = nullptr, int n_clear = 0);
 // shared down projection z = h Wsd^T (fp32), then the combine as its own pass
 void launch_shared_down_dense(const uint16_t *shared_w, const uint16_t *hs, int T, float *z, hipStream_t s);
 void launch_combine(const float *z, const float *topk_w, const int *pos, const float *o, int T, uint16_t *y,

@@ -14,6 +14,9 @@
 
 namespace moe_w4 {
 
+constexpr int kSortWaves = 16;
+constexpr int kSortWgAssign = kSortWaves * 64;   // assignments per workgroup of the wide sort
+
 // ROTATE: xt gets the fwht128-rotated x in the int4 experts' operand order;
 // otherwise x itself as natural-order fp16 (the NVFP4 experts' operands).
 template <bool ROTATE>
@@ -22,7 +25,8 @@ __global__ __launch_bounds__(512) void k_topk_rotate(const float *__restrict__ l
                                                      int *__restrict__ topk_idx,
                                                      float *__restrict__ topk_w,
                                                      uint32_t *__restrict__ xt,
-                                                     float *__restrict__ xt_scale, RouterPolicy rp) {
+                                                     float *__restrict__ xt_scale, RouterPolicy rp,
+                                                     int *__restrict__ hist) {
     // two waves per token, side by side: waves 0-3 select the top-6 of tokens
     // 4b .. 4b+3, waves 4-7 turn the same tokens' x into operands (the two
     // are independent; one wave doing both ran the chains back to back)
@@ -37,6 +41,9 @@ __global__ __launch_bounds__(512) void k_topk_rotate(const float *__restrict__ l
             if (lane == j) {
                 topk_idx[(size_t)t * kTopK + j] = sel.e[j];
                 topk_w[(size_t)t * kTopK + j] = sel.w[j];
+                // the wide sort's count of expert e in the workgroup of
+                // assignment 6t + j (a sum: the order of the adds is free)
+                if (hist) atomicAdd(&hist[(size_t)((kTopK * t + j) / kSortWgAssign) * kE + sel.e[j]], 1);
             }
         }
         return;
@@ -51,13 +58,14 @@ __global__ __launch_bounds__(512) void k_topk_rotate(const float *__restrict__ l
 }
 
 void launch_topk_rotate(const float *logits, const uint16_t *x, int T, const float *bias, int policy,
-                        int *topk_idx, float *topk_w, uint32_t *xt, float *xt_scale, hipStream_t s, bool rotate) {
+                        int *topk_idx, float *topk_w, uint32_t *xt, float *xt_scale, hipStream_t s, bool rotate,
+                        int *hist) {
     if (rotate)
         hipLaunchKernelGGL(k_topk_rotate<true>, dim3((T + 3) / 4), dim3(512), 0, s, logits, x, T, topk_idx, topk_w,
-                           xt, xt_scale, RouterPolicy{bias, policy});
+                           xt, xt_scale, RouterPolicy{bias, policy}, hist);
     else
         hipLaunchKernelGGL(k_topk_rotate<false>, dim3((T + 3) / 4), dim3(512), 0, s, logits, x, T, topk_idx,
-                           topk_w, xt, xt_scale, RouterPolicy{bias, policy});
+                           topk_w, xt, xt_scale, RouterPolicy{bias, policy}, hist);
 }
 
 // ---------------------------------------------------------------------------
@@ -68,7 +76,6 @@ void launch_topk_rotate(const float *logits, const uint16_t *x, int T, const flo
 //   time, ranking equal experts inside the chunk with ballots.
 // The result depends only on topk_idx: offsets, perm and pos are exact.
 // ---------------------------------------------------------------------------
-constexpr int kSortWaves = 16;
 constexpr int kSortBatch = 8;        // chunks of 64 assignments whose loads are issued together
 constexpr int kSortKeep = 16;        // chunks per wave kept in registers between the two passes
 
@@ -253,7 +260,6 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
 //      token into the expert's record.
 // The result is that of k_sort bit for bit: stable in the assignment index.
 // ---------------------------------------------------------------------------
-constexpr int kSortWgAssign = kSortWaves * 64;   // assignments per workgroup
 
 int sort_hist_blocks(int T) { return (kTopK * T + kSortWgAssign - 1) / kSortWgAssign; }
 
@@ -413,9 +419,9 @@ void launch_route_par(const float *logits, int T, const float *bias, int policy,
 }
 
 void launch_sort_wide(const int *topk_idx, int T, int *hist, int *offsets, int *perm, int *pos, int *n_active,
-                      int *slots, int *chunks, int *n_chunks, int *error, hipStream_t s) {
+                      int *slots, int *chunks, int *n_chunks, int *error, hipStream_t s, bool hist_ready) {
     const int nb = sort_hist_blocks(T), N = kTopK * T;
-    hipLaunchKernelGGL(k_sort_hist, dim3(nb), dim3(1024), 0, s, topk_idx, N, hist);
+    if (!hist_ready) hipLaunchKernelGGL(k_sort_hist, dim3(nb), dim3(1024), 0, s, topk_idx, N, hist);
     hipLaunchKernelGGL(k_sort_place, dim3(nb), dim3(1024), 0, s, topk_idx, N, nb, hist, offsets, perm, pos, n_active,
                        slots, reinterpret_cast<int4 *>(chunks), n_chunks, error);
 }
