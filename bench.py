@@ -370,6 +370,12 @@ def bench_nvfp4(a, T):
         "routed_down": n_touched * NV_D_BYTES + T * 6 * 512 * 4 + T * 6 * 2048 * 4,
         "shared_down_combine": 1024 * 2048 * 2 + T * 1024 * 2 + T * 6 * 2048 * 4 + act,
     }
+    if T <= FUSED_MAX_TOKENS:
+        # the two launches of the decode form: the router, then the rest of the
+        # layer with the shared expert (recorded under routed_gateup)
+        stage_bytes["router_shared_gateup"] = ROUTER_BYTES + act + T * 256 * 4
+        stage_bytes["routed_gateup"] = (n_touched * (NV_GU_BYTES + NV_D_BYTES) + SHARED_BYTES + T * 256 * 4 + act
+                                        + 2 * T * 1024 * 2 + act)
     dom_bytes = stage_bytes.get(dom, 0.0)
     dom_flops = 0.0
     if T >= GROUPED_MIN_TOKENS:
