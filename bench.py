@@ -312,7 +312,9 @@ def bench_nvfp4(a, T):
     from oracle import moe_oracle as O
     cfg = synth.CONFIGS[{1: "decode_t1", 32: "decode_t32", 2048: "prefill_t2048"}[T]]
     assert cfg["T"] == T
-    n_layers = a.layers or 4
+    # at T = 1 a layer touches ~24 MB: 24 layers keep the weights a run
+    # touches above the 256 MB Infinity Cache, as for the int4 layer
+    n_layers = a.layers or DEFAULT_LAYERS.get(T, 4)
     log(f"config {a.config}: T={T}, {n_layers} layers with NVFP4 experts on the device")
     layers = []
     for l in range(n_layers):
@@ -343,6 +345,7 @@ def bench_nvfp4(a, T):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / a.steps
     log(f"timed {a.steps} steps: {ms * 1e3:.1f} us/step")
+    dist = step_distribution(m, step, max(a.steps, 200))
     events = m.HipEvents(a.steps * n_pts)
     for i in range(a.steps):
         step(i, events.handles[i * n_pts:(i + 1) * n_pts])
@@ -389,6 +392,7 @@ def bench_nvfp4(a, T):
         "config": {"workload": f"{a.config}: one MoE layer with NVFP4 experts, T={T}, x seed {cfg['x_seed']}, "
                                f"weights seed {cfg['w_seed']}", "T": T, "layers_rotated": n_layers,
                    "touched_experts": n_touched},
+        "step_us": dist,
         "roofline": roof,
         "layer": {"algorithmic_bytes": layer_bytes, "hbm_gbs": layer_bytes / (ms * 1e-3) / 1e9,
                   "hbm_frac": layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
