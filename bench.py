@@ -116,11 +116,11 @@ STAGE_KERNELS_GEMV = {
     "shared_down_combine": ("k_skinny", ["skinny_mfma.hip"]),
 }
 STAGE_KERNELS_GROUPED = {
-    "router_shared_gateup": ("k_dense_mfma<2048>", ["dense_mfma.hip"]),
+    "router_shared_gateup": ("k_dense_mfma<2048", ["dense_mfma.hip"]),
     "topk_sort": ("k_topk_rotate", ["router.hip", "token_ops.h"]),
     "routed_gateup": ("k_gateup_mfma", ["grouped_mfma.hip"]),
     "routed_down": ("k_down_mfma", ["grouped_mfma.hip"]),
-    "shared_down_combine": ("k_dense_mfma<1024>", ["dense_mfma.hip"]),
+    "shared_down_combine": ("k_dense_mfma<1024", ["dense_mfma.hip"]),
 }
 
 

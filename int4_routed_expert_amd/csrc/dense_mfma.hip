@@ -52,7 +52,13 @@ struct DenseJobs {
     DenseJob job[2];
     int *clear;    // n_clear ints zeroed by the first workgroups (256 each), or null
     int n_clear;
+    // RT (router folded into the shared gate/up tiles): tile nt of job 0 also
+    // computes router columns [kRtCols nt, kRtCols nt + kRtCols) of its rows
+    const uint16_t *router_w;
+    const float *router_bias;   // per column, or null
+    float *logits;              // [M][256] fp32
 };
+constexpr int kRtCols = 16;   // router columns per shared tile (16 tiles x 16 = 256)
 
 __device__ __forceinline__ f32x16_t mfma_bf16(uint4 a, uint4 b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
@@ -67,12 +73,19 @@ __device__ __forceinline__ void mfma_drain() {
 }  // namespace
 
 // A: [M][K] bf16 rows.  Work item: (m tile, job n tile).
-template <int K>
+// RT: the router's 256 columns ride along the 16 shared gate/up tiles, 16 per
+// tile (B gets 16 more rows in LDS; wave (wm, wn) multiplies the 32 A rows
+// 64 wm + 32 wn .. of its own operands by them, the 16 columns padded to the
+// MFMA's 32 by repeating them).  A launch of 256 tiles then fills the 256 CUs
+// once; the router as tiles of its own made 288, and the 32 CUs that ran two
+// set the launch's time (42 -> 31 us at T = 2048 without the router tiles).
+template <int K, bool RT>
 __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__ A, int M, int m_tiles,
                                                     DenseJobs jobs) {
     constexpr int kSteps = K / kStepK;
     static_assert(kSteps >= 3, "pipeline prologue");
-    __shared__ __attribute__((aligned(16))) uint8_t sa[2][kSlotBytes], sb[2][kSlotBytes];
+    constexpr int kSlotBytesB = kSlotBytes + (RT ? kRtCols * kRowBytes : 0);
+    __shared__ __attribute__((aligned(16))) uint8_t sa[2][kSlotBytes], sb[2][kSlotBytesB];
     if (jobs.clear) {
         const int i = (int)blockIdx.x * 256 + (int)threadIdx.x;
         if (i < jobs.n_clear) jobs.clear[i] = 0;
@@ -130,6 +143,17 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
     const __amdgpu_buffer_rsrc_t bres = make_buf(J.B, 0xffffffffu);
     uint32_t aoff[kStageLoads], boff[kStageLoads];
     int ldst[kStageLoads];
+    // RT: threads 0..127 also move the 16 router rows' chunk tid (row kTile + tid / 8)
+    const bool rt_stager = RT && tid < kRtCols * kChunksPerRow;
+    const __amdgpu_buffer_rsrc_t rres = make_buf(RT ? jobs.router_w : J.B, 0xffffffffu);
+    uint32_t rt_off = 0;
+    int rt_ldst = 0;
+    if (rt_stager) {
+        const int r = kTile + tid / kChunksPerRow, pos = tid % kChunksPerRow;
+        const int grp = pos ^ ((r >> 1) & 7);
+        rt_off = (uint32_t)(nt * kRtCols + tid / kChunksPerRow) * (K * 2) + grp * 16;
+        rt_ldst = r * kRowBytes + pos * 16;
+    }
 #pragma unroll
     for (int i = 0; i < kStageLoads; ++i) {
         const int c = tid + 256 * i, r = c / kChunksPerRow, pos = c % kChunksPerRow;
@@ -138,12 +162,15 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
         boff[i] = (uint32_t)b_row(r) * (K * 2) + grp * 16;
         ldst[i] = r * kRowBytes + pos * 16;
     }
-    uint4 stg[kPrefetch][2 * kStageLoads];
+    uint4 stg[kPrefetch][2 * kStageLoads + (RT ? 1 : 0)];
     auto load = [&](int set, int step) {
 #pragma unroll
         for (int i = 0; i < kStageLoads; ++i) {
             stg[set][i] = bload16(ares, aoff[i] + step * kRowBytes, 0);
             stg[set][kStageLoads + i] = bload16(bres, boff[i] + step * kRowBytes, 0);
+        }
+        if constexpr (RT) {
+            if (rt_stager) stg[set][2 * kStageLoads] = bload16(rres, rt_off + step * kRowBytes, 0);
         }
     };
     auto store = [&](int set, int slot) {
@@ -152,15 +179,20 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
             *reinterpret_cast<uint4 *>(sa[slot] + ldst[i]) = stg[set][i];
             *reinterpret_cast<uint4 *>(sb[slot] + ldst[i]) = stg[set][kStageLoads + i];
         }
+        if constexpr (RT) {
+            if (rt_stager) *reinterpret_cast<uint4 *>(sb[slot] + rt_ldst) = stg[set][2 * kStageLoads];
+        }
     };
 
-    f32x16_t acc[2][2];
+    f32x16_t acc[2][2], acc_r;
 #pragma unroll
     for (int x = 0; x < 2; ++x)
 #pragma unroll
         for (int y = 0; y < 2; ++y)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[x][y][i] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc_r[i] = 0.0f;
 
     // step k's operands live in register set k % 2 until stored to LDS slot
     // k % 2: step 0 is stored before the loop, step s + 1 during step s
@@ -178,10 +210,14 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
         const int slot = s & 1;
         // every operand of the step is requested from LDS first, so the MFMAs
         // below wait for the LDS latency once per step, not once per k-slice
-        uint4 a[kChunksPerRow / 2][2], b[kChunksPerRow / 2][2];
+        uint4 a[kChunksPerRow / 2][2], b[kChunksPerRow / 2][2], br[kChunksPerRow / 2];
 #pragma unroll
         for (int j = 0; j < kChunksPerRow / 2; ++j) {
             const int grp = (kChunksPerRow / 2) * g + j;
+            if constexpr (RT) {   // router row n % 16 (lanes n and n + 16 alike)
+                const int r = kTile + (n & (kRtCols - 1));
+                br[j] = *reinterpret_cast<const uint4 *>(sb[slot] + r * kRowBytes + ((grp ^ ((r >> 1) & 7)) * 16));
+            }
 #pragma unroll
             for (int x = 0; x < 2; ++x) {
                 const int r = 64 * wm + 32 * x + n;
@@ -200,16 +236,36 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
         if (s + 3 < kSteps) load((s + 1) % kPrefetch, s + 3);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int j = 0; j < kChunksPerRow / 2; ++j)
+        for (int j = 0; j < kChunksPerRow / 2; ++j) {
 #pragma unroll
             for (int x = 0; x < 2; ++x)
 #pragma unroll
                 for (int y = 0; y < 2; ++y) acc[x][y] = mfma_bf16(a[j][x], b[j][y], acc[x][y]);
+            if constexpr (RT) {
+                // the wave's rows 32 wn .. of its 64: a component-wise select
+                // (an index by wn would move the operands to scratch)
+                const uint4 lo = a[j][0], hi = a[j][1];
+                const uint4 ar = make_uint4(wn ? hi.x : lo.x, wn ? hi.y : lo.y, wn ? hi.z : lo.z, wn ? hi.w : lo.w);
+                acc_r = mfma_bf16(ar, br[j], acc_r);
+            }
+        }
         __syncthreads();
     }
     mfma_drain();
 
     // epilogue: lane holds rows 64wm + 32x + 8(i/4) + 4g + (i%4), column 64wn + 32y + n
+    if constexpr (RT) {
+        // router columns: rows 64wm + 32wn + 8(i/4) + 4g + (i%4), column n < 16
+        if (n < kRtCols) {
+            const int c = nt * kRtCols + n;
+            const float bc = jobs.router_bias ? jobs.router_bias[c] : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int m = m0 + 64 * wm + 32 * wn + 8 * (i >> 2) + 4 * g + (i & 3);
+                if (m < M) jobs.logits[(size_t)m * kE + c] = acc_r[i] + bc;
+            }
+        }
+    }
     float bcol[2] = {0.0f, 0.0f};
     if (J.epi == kEpiStore && J.bias) {
         bcol[0] = J.bias[nt * kTile + 64 * wn + n];
@@ -246,25 +302,54 @@ __global__ __launch_bounds__(256) void k_dense_mfma(const uint16_t *__restrict__
     }
 }
 
+// Compute units of the current device (queried once per process).
+static int cu_count() {
+    static const int n = [] {
+        int dev = 0, v = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+            v = 256;
+        return v;
+    }();
+    return n;
+}
+
 static DenseJob no_dense_job() { return DenseJob{nullptr, 0, kEpiStore, 0, nullptr, nullptr, 0}; }
 
-template <int K>
+template <int K, bool RT = false>
 static void launch_dense(const uint16_t *A, int M, const DenseJobs &jobs, hipStream_t s) {
     const int m_tiles = (M + kTile - 1) / kTile;
     const int n_total = jobs.job[0].n_tiles + jobs.job[1].n_tiles;
     const int grid = (m_tiles >= kXcds) ? kXcds * ((m_tiles + kXcds - 1) / kXcds) * n_total : m_tiles * n_total;
-    hipLaunchKernelGGL(k_dense_mfma<K>, dim3(grid), dim3(256), 0, s, A, M, m_tiles, jobs);
+    hipLaunchKernelGGL((k_dense_mfma<K, RT>), dim3(grid), dim3(256), 0, s, A, M, m_tiles, jobs);
 }
 
 void launch_router_and_shared_gateup_dense(const uint16_t *x, int T, const uint16_t *router_w, const float *bias,
                                            float *logits, const uint16_t *shared_w, uint16_t *hs, hipStream_t s,
                                            int *clear, int n_clear) {
-    DenseJobs jobs;
+    DenseJobs jobs = {};
     jobs.clear = clear;
     jobs.n_clear = n_clear;
-    jobs.job[0] = DenseJob{router_w, kE / kTile, kEpiStore, 0, bias, logits, kE};
-    jobs.job[1] = DenseJob{shared_w, kIS / 64, kEpiSwiglu, kIS, nullptr, hs, kIS};
-    launch_dense<kH>(x, T, jobs, s);
+    // the shared gate/up in 16 tiles of 64 gate + 64 up rows per 128 tokens;
+    // the router either as 2 tiles of its own per 128 tokens, or folded into
+    // the shared tiles (16 columns each) when its own tiles would take the
+    // launch past one round of the CUs and the folded ones fit in it (15-16
+    // token tiles, 1793-2048 tokens on 256 CUs); elsewhere the fold only
+    // lengthens every tile
+    static_assert((kIS / 64) * kRtCols == kE, "the router's columns spread over the shared tiles");
+    const int m_tiles = (T + kTile - 1) / kTile, cus = cu_count();
+    const bool fold = m_tiles * (kIS / 64) <= cus && m_tiles * (kIS / 64 + kE / kTile) > cus;
+    jobs.job[0] = DenseJob{shared_w, kIS / 64, kEpiSwiglu, kIS, nullptr, hs, kIS};
+    if (fold) {
+        jobs.job[1] = no_dense_job();
+        jobs.router_w = router_w;
+        jobs.router_bias = bias;
+        jobs.logits = logits;
+        launch_dense<kH, true>(x, T, jobs, s);
+    } else {
+        jobs.job[1] = DenseJob{router_w, kE / kTile, kEpiStore, 0, bias, logits, kE};
+        launch_dense<kH>(x, T, jobs, s);
+    }
 }
 
 void launch_shared_down_dense(const uint16_t *shared_w, const uint16_t *hs, int T, float *z, hipStream_t s) {

@@ -193,9 +193,9 @@ __global__ __launch_bounds__(64 * KS) void k_skinny(const uint16_t *__restrict__
                 for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
                     for (int s = 0; s < 4; ++s) {
-                        const int c = 16 * kb + 4 * s + g;
+                        const int cq = 16 * kb + 4 * s + g;   // 16-byte group of the row
                         a[kb][s] = *reinterpret_cast<const uint4 *>(xs[wave] + t * kTileBytes + r * kRowBytes +
-                                                                    16 * (c ^ r));
+                                                                    16 * (cq ^ r));
                     }
 #pragma unroll
                 for (int kb = 0; kb < KB; ++kb)
