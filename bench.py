@@ -133,8 +133,8 @@ STAGE_KERNELS_NVFP4 = {
 }
 # from 128 tokens on the NVFP4 experts run on the grouped MFMA kernels
 STAGE_KERNELS_NVFP4_MFMA = {
-    "routed_gateup": ("k_gateup_mfma<true>", ["grouped_mfma.hip"]),
-    "routed_down": ("k_down_mfma<true>", ["grouped_mfma.hip"]),
+    "routed_gateup": ("k_gateup_mfma<true", ["grouped_mfma.hip"]),
+    "routed_down": ("k_down_mfma<true", ["grouped_mfma.hip"]),
 }
 
 

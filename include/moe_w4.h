@@ -119,8 +119,10 @@ extern "C" {
  *                         second token (= first if one), 0, 0, 0}; records past
  *                         n_active hold expert -1
  *   chunks    i32 [n][4]  from T >= 128 on (MFMA grouped path): {expert, first sorted
- *                         position, rows <= 64, 0} covering each expert's sorted
- *                         positions in order, ascending by expert; n_chunks i32 [1]
+ *                         position, rows, 0} covering each expert's sorted
+ *                         positions in order, ascending by expert (chunks of
+ *                         64 and a ragged last one; from T = 1536 on, one chunk
+ *                         for an expert with <= 96 rows); n_chunks i32 [1]
  *                         holds n.  (Written at every T; read only on that path.)
  *   logits    f32 [T][256] router logits R x, without the bias
  *   sync      8192 bytes of counters for the hand-offs inside a launch (1-48

@@ -112,19 +112,6 @@ __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
-// wait_vmcnt with a count that is a constant once the loop around the call
-// is unrolled (one case survives); a count above the table waits for all
-__device__ __forceinline__ void wait_vmcnt_n(int n) {
-    switch (n) {
-#define MOE_VM(k) \
-    case k: wait_vmcnt<k>(); break;
-        MOE_VM(1) MOE_VM(2) MOE_VM(3) MOE_VM(4) MOE_VM(5) MOE_VM(6) MOE_VM(7) MOE_VM(8) MOE_VM(9) MOE_VM(10)
-        MOE_VM(11) MOE_VM(12) MOE_VM(13) MOE_VM(14) MOE_VM(15) MOE_VM(16) MOE_VM(17) MOE_VM(18) MOE_VM(19)
-        MOE_VM(20) MOE_VM(21) MOE_VM(22) MOE_VM(23) MOE_VM(24)
-#undef MOE_VM
-    default: wait_vmcnt<0>(); break;
-    }
-}
 // the same, and every LDS access of this wave completed (lgkmcnt 0)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt_lds() {
@@ -208,7 +195,6 @@ __device__ __forceinline__ half2_t scaled_half2(uint32_t word2, int hi, int k) {
 // scales normalised by one power of two), so the MFMA accumulates over the
 // whole of K and the normalisation is undone once at the end.
 // =========================================================================
-constexpr int kGuBuf = kChunkRows * 256;   // one A block: 64 rows x 128 fp16
 // (a fourth A slot, three blocks in flight, measured no faster)
 constexpr int kGuRing = 3;                     // A blocks in LDS (kGuRing - 1 in flight)
 constexpr int kGuCodeDist = 3;                 // codes requested this many blocks ahead
@@ -267,7 +253,20 @@ __host__ __device__ constexpr bool gu_codes_before_a() {
     return true;
 }
 static_assert(gu_codes_before_a(), "codes(b+1) must be requested before A(b+1)");
-static_assert(kGuRing == 3 || kGuRing == 4, "three or four LDS slots");
+// The main loop's waits are written out as constant counts (a count chosen
+// at run time through a switch cost the kernel 80 bytes of spills per lane);
+// they must agree with gu_loads_after_a for every block
+__host__ __device__ constexpr int gu_wait_written(int b, int ni, int f) {
+    return b + 3 < kGuBlocks ? (b >= 1 ? 2 * f + ni : f + ni) : b + 2 < kGuBlocks ? f + ni : 0;
+}
+__host__ __device__ constexpr bool gu_waits_agree() {
+    for (int ni = 2; ni <= 6; ni += 2)
+        for (int f = 4; f <= 6; f += 2)
+            for (int b = 0; b + 1 < kGuBlocks; ++b)
+                if (gu_wait_written(b, ni, f) != gu_loads_after_a(b, ni, f)) return false;
+    return true;
+}
+static_assert(kGuRing == 3 && kGuCodeDist == 3 && gu_waits_agree(), "the written-out waits follow the issue order");
 
 // NVFP4 block scales of an expert: gate [512][128], up [512][128], down [2048][32] bytes
 constexpr uint32_t kNvScGate = (uint32_t)kI * kH / 16;
@@ -290,7 +289,8 @@ __device__ __forceinline__ half2_t e4m3_half2(uint32_t w, int i) {
     return half2_t{h, h};
 }
 
-template <bool NV>
+// MaxMT: 32-row tiles of the longest chunk (2: chunks of <= 64 rows; 3: up to 96)
+template <bool NV, int MaxMT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_gateup_mfma(
     const uint8_t *__restrict__ codes, const void *__restrict__ scales_, const float *__restrict__ tscales,
     const uint32_t *__restrict__ xt, const float *__restrict__ xt_scale, const int *__restrict__ perm,
@@ -299,9 +299,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     // separate arrays rather than one: the compiler then knows that a block's
     // reads do not alias the direct loads in flight into the other slots and
     // does not wait for those loads before every LDS read
+    constexpr int kRows = 32 * MaxMT;          // rows of the longest chunk
+    constexpr int kGuBuf = kRows * 256;        // one A block: kRows rows x 128 fp16
     __shared__ __attribute__((aligned(16))) uint8_t ring0[kGuBuf], ring1[kGuBuf], ring2[kGuBuf],
         ring3[kGuRing > 3 ? kGuBuf : 16];
-    __shared__ float row_p[kChunkRows];
+    __shared__ float row_p[kRows];
     auto slot_ptr = [&](int slot) -> uint8_t * {
         return slot == 0 ? ring0 : slot == 1 ? ring1 : slot == 2 ? ring2 : ring3;
     };
@@ -360,17 +362,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         su[1] = bload16(sres, usoff + 16, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
-    if (tid < kChunkRows) row_p[tid] = xt_scale[perm[row0 + min(tid, rows - 1)] / kTopK];
+    if (tid < kRows) row_p[tid] = xt_scale[perm[row0 + min(tid, rows - 1)] / kTopK];
 
     // a = silu(g) * u for this workgroup's 128 columns goes into LDS (fp32)
     // after the main loop: rows 0..31 in ring0, rows 32..63 in ring1
     constexpr int kActRowsPerSlot = kGuBuf / (kG * 4);
-    static_assert(2 * kActRowsPerSlot >= kChunkRows, "the fp32 rows of a fit two ring slots");
+    static_assert(2 * kActRowsPerSlot >= kRows, "the fp32 rows of a fit two ring slots");
     auto act_row = [&](int m) -> float * {
         return reinterpret_cast<float *>(m < kActRowsPerSlot ? ring0 : ring1) +
                (m < kActRowsPerSlot ? m : m - kActRowsPerSlot) * kG;
     };
-    with_tiles<kChunkRows / 32>(n_mt, [&](auto tiles) {
+    with_tiles<MaxMT>(n_mt, [&](auto tiles) {
     constexpr int MT = decltype(tiles)::value;
     // A loads of the 32*MT rows in use: NI instructions per wave, 4 rows (1 KB)
     // each; lane l writes position l & 15 of row 4*(NI*w + i) + (l >> 4)
@@ -444,7 +446,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         // codes(b+1) and A(b+1) must have landed for every wave before the
         // next block; what was requested after A(b+1) may stay in flight
         __builtin_amdgcn_sched_barrier(0);
-        if (b + 1 < kBlocks) wait_vmcnt_n(gu_loads_after_a(b, NI, kFetchLoads));
+        if (b + 3 < kBlocks) {
+            if (b >= 1)
+                wait_vmcnt<2 * kFetchLoads + NI>();
+            else
+                wait_vmcnt<kFetchLoads + NI>();
+        } else if (b + 2 < kBlocks) {
+            wait_vmcnt<kFetchLoads + NI>();
+        } else if (b + 1 < kBlocks) {
+            wait_vmcnt<0>();
+        }
         block_barrier();
     }
     mfma_drain();
@@ -526,11 +537,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
 // =========================================================================
 // down: four workgroups own a chunk, each a quarter of the 2048 output
-// features in four tiles of 128 (32 per wave), with the chunk's A (64 rows x
-// 512 fp16) staged in LDS.  At ~73 KB of LDS two workgroups share a CU, so
-// one stages its rows while the other multiplies (with chunks of 96 rows,
-// one workgroup per CU left every staging exposed).  The codes of the next
-// tile are in flight during each tile.  The MFMA runs transposed (codes as the row operand, tokens as the
+// features in four tiles of 128 (32 per wave), with up to 64 rows of the
+// chunk's A (x 512 fp16) staged in LDS at a time: a chunk of 65-96 rows (an
+// expert with that many) takes two passes, the second re-reading the
+// workgroup's codes from L2.  At ~73 KB of LDS two workgroups share a CU, so
+// one stages its rows while the other multiplies (96 staged rows, one
+// workgroup per CU, left every staging exposed).  The codes of the next tile
+// are in flight during each tile.  The MFMA runs transposed (codes as the row operand, tokens as the
 // column operand), so a lane ends with 4 consecutive features of one token
 // per group.  o is stored in fp16 with one power-of-two multiplier per row
 // (o_scale), which halves the traffic of the fp32 rows at a relative rounding
@@ -553,20 +566,24 @@ constexpr int kDnPitch = 1040;   // bytes per LDS row (1024 + 16)
 constexpr int kDnParts = 4;              // workgroups per chunk, each over a quarter of the features
 constexpr int kDnFeat = kH / kDnParts;   // features of one workgroup
 constexpr int kDnTiles = kDnFeat / 128;  // 128-feature tiles of a workgroup (32 features per wave)
+constexpr int kDnRows = kChunkRows;    // rows of A staged at once (one pass)
 constexpr int kDnCodeRing = 2;
+static_assert(kDnTiles % kDnCodeRing == 0, "every pass starts on ring slot 0");
+static_assert(2 * kDnRows >= kChunkMaxRows, "two passes cover a chunk");
 
 // NVFP4 (NV): no scale normalisation; each lane's four E4M3 scales of a
 // block come with its codes, and o is written as fp32 rows (o_scale unused).
-template <bool NV>
+// PASSES: chunks may have more than kDnRows rows (then up to two passes)
+template <bool NV, bool PASSES>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_down_mfma(
     const uint8_t *__restrict__ codes, const void *__restrict__ scales_, const float *__restrict__ tscales,
     const uint32_t *__restrict__ at, const float *__restrict__ at_scale, const int4 *__restrict__ chunks,
     const int *__restrict__ n_chunks, int chunk_cap, void *__restrict__ o_, float *__restrict__ o_scale) {
     const uint16_t *scales = static_cast<const uint16_t *>(scales_);
     uint16_t *o = static_cast<uint16_t *>(o_);
-    __shared__ __attribute__((aligned(16))) uint8_t lds[kChunkRows * kDnPitch];
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kDnRows * kDnPitch];
     __shared__ float fk_wave[4];                                              // largest 2^-k per wave
-    __shared__ float row_p[kChunkRows];                                       // per token
+    __shared__ float row_p[kDnRows];                                          // per token
     __shared__ __attribute__((aligned(16))) uint16_t sc[kI / kG][kDnFeat];    // [block][feature] bf16
     __shared__ __attribute__((aligned(16))) float fk[kDnFeat];                // 2^-k per feature
     // four workgroups per chunk (one per quarter of the features, on one XCD
@@ -578,7 +595,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const int4 ch = chunks[min(chunk, chunk_cap - 1)];   // beside the count, as in gate/up
     if (chunk >= nch) return;
     const int e = uniform(ch.x), row0 = uniform(ch.y), rows = uniform(ch.z);
-    const int n_mt = uniform((rows + 31) >> 5);
+    const int n_pass = PASSES ? uniform((rows + kDnRows - 1) / kDnRows) : 1;
     const int tid = threadIdx.x, lane = tid & 63, wave = wave_id();
     const int n = lane & 31, g = lane >> 5;
 
@@ -604,21 +621,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             for (int b = 0; b < 4; ++b) cs4[slot][b] = bload4(nsres, so + 8 * b, 0);
         }
     };
-    // the chunk's activations are needed first: thread -> (row, part), load
+    // the activations of a pass are needed first: thread -> (row, part), load
     // i takes the row's 16-byte group 4i + part (block i / 4); the codes of
-    // the first tile are requested right behind them
-    static_assert(4 * kChunkRows == 256, "one thread per quarter row");
+    // the first tile are requested right behind those of pass 0
+    static_assert(4 * kDnRows == 256, "one thread per quarter row");
     const int srow = tid >> 2, part = tid & 3;
     uint4 v[16];
     float4 ps;
-    __builtin_amdgcn_sched_barrier(0);
-    {
-        const int p = row0 + min(srow, rows - 1);
+    auto stage_load = [&](int pass) {
+        const int p = row0 + min(kDnRows * pass + srow, rows - 1);
         const uint4 *src = reinterpret_cast<const uint4 *>(at + (size_t)p * (kI / 2)) + part;
 #pragma unroll
         for (int i = 0; i < 16; ++i) v[i] = src[4 * i];
         ps = *reinterpret_cast<const float4 *>(at_scale + (size_t)p * (kI / kG));
-    }
+    };
+    __builtin_amdgcn_sched_barrier(0);
+    stage_load(0);
     // each block brought to the row's largest prescale, into LDS
     auto stage_store = [&]() {
         const float pm = fmaxf(fmaxf(ps.x, ps.y), fmaxf(ps.z, ps.w));
@@ -692,22 +710,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     const float to_half = 0x1p-20f / fkmax;   // a power of two
     const float tsd = NV ? tscales[3 * e + 2] : 1.0f;
 
-    // o rows of the chunk through a buffer descriptor: stores of rows past
-    // its end fall outside it and are dropped by the hardware bounds check
+    for (int pass = 0; pass < n_pass; ++pass) {
+    if (PASSES && pass > 0) {
+        // every wave is done with the previous rows before they are replaced
+        __syncthreads();
+        stage_load(pass);
+        stage_store();
+        __syncthreads();
+    }
+    const int prow0 = row0 + kDnRows * pass, prows = min(kDnRows, rows - kDnRows * pass);
+    // o rows of the pass through a buffer descriptor: stores of rows past its
+    // end fall outside it and are dropped by the hardware bounds check
     const __amdgpu_buffer_rsrc_t ores =
-        NV ? make_buf(static_cast<float *>(o_) + (size_t)row0 * kH, (uint32_t)rows * kH * 4)
-           : make_buf(o + (size_t)row0 * kH, (uint32_t)rows * kH * 2);
-    if (!NV && quarter == 0 && tid < rows) o_scale[row0 + tid] = row_p[tid] * fkmax * 0x1p20f;
+        NV ? make_buf(static_cast<float *>(o_) + (size_t)prow0 * kH, (uint32_t)prows * kH * 4)
+           : make_buf(o + (size_t)prow0 * kH, (uint32_t)prows * kH * 2);
+    if (!NV && quarter == 0 && tid < prows) o_scale[prow0 + tid] = row_p[tid] * fkmax * 0x1p20f;
 
     // fully unrolled, so ring slots are compile-time; the next tile's codes
-    // are requested before this tile's products
-    with_tiles<kChunkRows / 32>(n_mt, [&](auto tiles) {
+    // (or the next pass's first tile's) are requested before this tile's
+    // products
+    with_tiles<kDnRows / 32>((prows + 31) >> 5, [&](auto tiles) {
     constexpr int MT = decltype(tiles)::value;
 #pragma unroll
     for (int t = 0; t < kDnTiles; ++t) {
         const int cs = t % kDnCodeRing;
         __builtin_amdgcn_sched_barrier(0);
-        if (t + kDnCodeRing - 1 < kDnTiles) fetch((t + kDnCodeRing - 1) % kDnCodeRing, t + kDnCodeRing - 1);
+        if (t + kDnCodeRing - 1 < kDnTiles)
+            fetch((t + kDnCodeRing - 1) % kDnCodeRing, t + kDnCodeRing - 1);
+        else if (PASSES && pass + 1 < n_pass)
+            fetch((t + kDnCodeRing - 1) % kDnCodeRing, t + kDnCodeRing - 1 - kDnTiles);
         __builtin_amdgcn_sched_barrier(0);
         const uint32_t zero = opaque(0);
         const uint8_t *abase = lds + zero;
@@ -773,7 +804,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
             // fp32 rows: acc times the tensor scale and the row's prescale
 #pragma unroll
             for (int h = 0; h < MT; ++h) {
-                const float mlt = tsd * row_p[min(32 * h + n, kChunkRows - 1)];
+                const float mlt = tsd * row_p[min(32 * h + n, kDnRows - 1)];
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const u32x4_t v = {__float_as_uint(acc[h][4 * q] * mlt), __float_as_uint(acc[h][4 * q + 1] * mlt),
@@ -804,6 +835,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         }
     }
     });
+    }   // passes
 }
 
 int max_chunks(int T) { return min(kE, kTopK * T) + (kTopK * T + kChunkRows - 1) / kChunkRows; }
@@ -816,14 +848,16 @@ static int grid_for(int T, int tiles) {
 void launch_gateup_mfma(const uint8_t *codes, const uint16_t *scales, const uint32_t *xt, const float *xt_scale,
                         const int *perm, const int *chunks, const int *n_chunks, int T, uint32_t *at,
                         float *at_scale, hipStream_t s) {
-    hipLaunchKernelGGL(k_gateup_mfma<false>, dim3(grid_for(T, kI / kG)), dim3(256), 0, s, codes,
+    auto k = chunk_long(T) ? k_gateup_mfma<false, 3> : k_gateup_mfma<false, 2>;
+    hipLaunchKernelGGL(k, dim3(grid_for(T, kI / kG)), dim3(256), 0, s, codes,
                        static_cast<const void *>(scales), nullptr, xt, xt_scale, perm,
                        reinterpret_cast<const int4 *>(chunks), n_chunks, max_chunks(T), at, at_scale);
 }
 
 void launch_down_mfma(const uint8_t *codes, const uint16_t *scales, const uint32_t *at, const float *at_scale,
                       const int *chunks, const int *n_chunks, int T, uint16_t *o, float *o_scale, hipStream_t s) {
-    hipLaunchKernelGGL(k_down_mfma<false>, dim3(grid_for(T, kDnParts)), dim3(256), 0, s, codes,
+    auto k = chunk_long(T) ? k_down_mfma<false, true> : k_down_mfma<false, false>;
+    hipLaunchKernelGGL(k, dim3(grid_for(T, kDnParts)), dim3(256), 0, s, codes,
                        static_cast<const void *>(scales), nullptr, at, at_scale,
                        reinterpret_cast<const int4 *>(chunks), n_chunks, max_chunks(T), static_cast<void *>(o), o_scale);
 }
@@ -831,7 +865,8 @@ void launch_down_mfma(const uint8_t *codes, const uint16_t *scales, const uint32
 void launch_gateup_mfma_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscales, const uint32_t *xn,
                               const float *xn_scale, const int *perm, const int *chunks, const int *n_chunks, int T,
                               uint32_t *an, float *an_scale, hipStream_t s) {
-    hipLaunchKernelGGL(k_gateup_mfma<true>, dim3(grid_for(T, kI / kG)), dim3(256), 0, s, codes,
+    auto k = chunk_long(T) ? k_gateup_mfma<true, 3> : k_gateup_mfma<true, 2>;
+    hipLaunchKernelGGL(k, dim3(grid_for(T, kI / kG)), dim3(256), 0, s, codes,
                        static_cast<const void *>(scales), tscales, xn, xn_scale, perm,
                        reinterpret_cast<const int4 *>(chunks), n_chunks, max_chunks(T), an, an_scale);
 }
@@ -839,7 +874,8 @@ void launch_gateup_mfma_nvfp4(const uint8_t *codes, const uint8_t *scales, const
 void launch_down_mfma_nvfp4(const uint8_t *codes, const uint8_t *scales, const float *tscales, const uint32_t *an,
                             const float *an_scale, const int *chunks, const int *n_chunks, int T, float *o,
                             hipStream_t s) {
-    hipLaunchKernelGGL(k_down_mfma<true>, dim3(grid_for(T, kDnParts)), dim3(256), 0, s, codes,
+    auto k = chunk_long(T) ? k_down_mfma<true, true> : k_down_mfma<true, false>;
+    hipLaunchKernelGGL(k, dim3(grid_for(T, kDnParts)), dim3(256), 0, s, codes,
                        static_cast<const void *>(scales), tscales, an, an_scale,
                        reinterpret_cast<const int4 *>(chunks), n_chunks, max_chunks(T), static_cast<void *>(o), nullptr);
 }

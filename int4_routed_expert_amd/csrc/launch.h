@@ -79,15 +79,30 @@ void launch_decode_fused(const FusedDecodeArgs &args, hipStream_t s);
 void launch_topk_rotate(const float *logits, const uint16_t *x, int T, const float *bias, int policy,
                         int *topk_idx, float *topk_w, uint32_t *xt, float *xt_scale, hipStream_t s,
                         bool rotate = true, int *hist = nullptr);
-// Assignments per chunk of the MFMA grouped kernels: two 32-row MFMA tiles
-// (a chunk's rows of the down projection's A, 64 x 1 KB, then fit in LDS
-// twice per CU).
+// Chunks of the MFMA grouped kernels: an expert's sorted assignments are cut
+// into chunks of kChunkRows (two 32-row MFMA tiles; the down kernel stages
+// 64 rows of A, 64 x 1 KB fitting in LDS twice per CU).  From
+// kChunkMaxRowsMinT tokens on, an expert with at most kChunkMaxRows is one
+// chunk instead (three tiles; the down kernel takes 65-96 rows in two
+// passes): one chunk per expert keeps the number of workgroups at the number
+// of touched experts (T = 2048 with uniform routing: 256 chunks, 1024 gate/up
+// workgroups, two full rounds of the 512 slots, where 64-row chunks made 261
+// and a tail).  Below that size no expert usually passes 64 rows and the
+// lighter two-tile kernels are faster.
 constexpr int kChunkRows = 64;
+constexpr int kChunkMaxRows = 96;
+constexpr int kChunkMaxRowsMinT = 1536;
+__host__ __device__ constexpr bool chunk_long(int T) { return T >= kChunkMaxRowsMinT; }
+// rows between the chunks of an expert with n sorted assignments (T tokens)
+__host__ __device__ constexpr int chunk_step(int n, int T) {
+    return chunk_long(T) && n <= kChunkMaxRows ? kChunkMaxRows : kChunkRows;
+}
+__host__ __device__ constexpr int chunk_count(int n, int T) { return (n + chunk_step(n, T) - 1) / chunk_step(n, T); }
 // Stable counting sort of the 6T assignments by expert (one workgroup).
 // slots: int[256][8] records {expert, first sorted position, count, first
 // token, second token, 0, 0, 0}, one per expert with tokens, then expert -1.
 // chunks: int[max_chunks(T)][4] records {expert, first sorted position, rows
-// (<= kChunkRows), 0} covering every expert's assignments; *n_chunks of them.
+// (see chunk_step), 0} covering every expert's assignments; *n_chunks of them.
 // The same result from many workgroups (two launches, or one when the
 // top-6 launch already counted hist_ready), for prefill sizes: hist is
 // int[sort_hist_blocks(T)][256], the experts' counts per workgroup.
@@ -119,7 +134,7 @@ void launch_gateup_gemv(const uint8_t *codes, const uint16_t *scales, const uint
 void launch_down_gemv(const uint8_t *codes, const uint16_t *scales, const float *act, const int *slots, int T,
                       float *o, hipStream_t s);
 
-// Routed experts, MFMA form (prefill): chunks of <= kChunkRows assignments
+// Routed experts, MFMA form (prefill): chunks of <= kChunkMaxRows assignments
 // of one expert against tiles of weight rows.  gate/up writes the rotated
 // fp16 operands of the down projection directly (at, at_scale).
 int max_chunks(int T);

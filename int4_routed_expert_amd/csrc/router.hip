@@ -140,13 +140,13 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
     __syncthreads();
     if (wave == 0) {
         // exclusive scans of the 256 totals (4 per lane), of the non-empty
-        // flags and of the chunk counts (kChunkRows assignments per chunk)
+        // flags and of the chunk counts (chunk_count)
         int c[4], f[4], k[4], sc = 0, sf = 0, sk = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             c[i] = tot[4 * lane + i];
             f[i] = c[i] > 0;
-            k[i] = (c[i] + kChunkRows - 1) / kChunkRows;
+            k[i] = chunk_count(c[i], T);
             sc += c[i];
             sf += f[i];
             sk += k[i];
@@ -184,8 +184,8 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
     // chunk list of the MFMA grouped path: {expert, first sorted position, rows, 0}
     if (tid < kE) {
         const int n = tot[tid];
-        for (int r = 0, q = chunk0[tid]; r < n; r += kChunkRows, ++q)
-            chunks[q] = make_int4(tid, offs[tid] + r, min(kChunkRows, n - r), 0);
+        for (int r = 0, q = chunk0[tid], st = chunk_step(n, T); r < n; r += st, ++q)
+            chunks[q] = make_int4(tid, offs[tid] + r, min(st, n - r), 0);
     }
     __syncthreads();
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
@@ -314,7 +314,7 @@ __global__ __launch_bounds__(1024) void k_sort_place(const int *__restrict__ top
         for (int i = 0; i < 4; ++i) {
             c[i] = tot[4 * lane + i];
             f[i] = c[i] > 0;
-            k[i] = (c[i] + kChunkRows - 1) / kChunkRows;
+            k[i] = chunk_count(c[i], N / kTopK);
             sc += c[i];
             sf += f[i];
             sk += k[i];
@@ -343,8 +343,8 @@ __global__ __launch_bounds__(1024) void k_sort_place(const int *__restrict__ top
                     rec[6] = 0;
                     rec[7] = 0;
                 }
-                for (int r = 0, q = ek; r < c[i]; r += kChunkRows, ++q)
-                    chunks[q] = make_int4(e, ec + r, min(kChunkRows, c[i] - r), 0);
+                for (int r = 0, q = ek, st = chunk_step(c[i], N / kTopK); r < c[i]; r += st, ++q)
+                    chunks[q] = make_int4(e, ec + r, min(st, c[i] - r), 0);
             }
             ec += c[i];
             ef += f[i];

@@ -85,13 +85,21 @@ def test_layer_small_T(m, layer0, T):
 
 
 # ------------------------------------------------- MFMA grouped path (T >= 128)
-CHUNK_ROWS = 64   # rows of one chunk of the grouped kernels (include/moe_w4.h)
+# chunks of the grouped kernels (include/moe_w4.h): chunks of CHUNK_ROWS; from
+# CHUNK_MAX_ROWS_MIN_T tokens on an expert with at most CHUNK_MAX_ROWS sorted
+# rows is one chunk
+CHUNK_ROWS = 64
+CHUNK_MAX_ROWS = 96
+CHUNK_MAX_ROWS_MIN_T = 1536
 
 
-def expected_chunks(offsets):
+def expected_chunks(offsets, T):
     counts = np.diff(offsets)
-    return np.array([(e, offsets[e] + r, min(CHUNK_ROWS, counts[e] - r), 0)
-                     for e in np.nonzero(counts)[0] for r in range(0, counts[e], CHUNK_ROWS)]).reshape(-1, 4)
+    long_ok = T >= CHUNK_MAX_ROWS_MIN_T
+    step = lambda n: CHUNK_MAX_ROWS if long_ok and n <= CHUNK_MAX_ROWS else CHUNK_ROWS
+    return np.array([(e, offsets[e] + r, min(step(counts[e]), counts[e] - r), 0)
+                     for e in np.nonzero(counts)[0]
+                     for r in range(0, counts[e], step(counts[e]))]).reshape(-1, 4)
 
 
 def read_chunks(m, ws, T):
@@ -105,7 +113,7 @@ def test_grouped_path_all_tokens(m, layer0):
     x = synth.gen_x(400, T)
     ws = m.workspace(T)
     g = P.run_gpu(m, x, layer0, ws=ws)
-    np.testing.assert_array_equal(read_chunks(m, ws, T), expected_chunks(g["offsets"]))
+    np.testing.assert_array_equal(read_chunks(m, ws, T), expected_chunks(g["offsets"], T))
     report("grouped T=128", P.compare(g, oracle_layer(x), label="grouped T=128"))
 
 
@@ -127,7 +135,7 @@ def test_grouped_chunks_of_a_hot_expert(m, layer0):
     g = P.run_gpu(m, x, layer0, bias=bias, ws=ws)
     assert np.all(g["topk_idx"][:, 0] == 17)
     ch = read_chunks(m, ws, T)
-    np.testing.assert_array_equal(ch, expected_chunks(g["offsets"]))
+    np.testing.assert_array_equal(ch, expected_chunks(g["offsets"], T))
     assert (ch[:, 0] == 17).sum() == 4 and ch[ch[:, 0] == 17][-1, 2] == 8
     tokens = np.array([0, 1, 31, 32, 63, 64, 95, 96, 127, 128, 191, 192, 199])
     report("grouped hot expert", P.compare(g, oracle_layer(x, bias=bias, tokens=tokens), tokens=tokens,
@@ -354,7 +362,7 @@ def test_sort_past_its_register_resident_size(m, layer0):
     x = synth.gen_x(410, T)
     ws = m.workspace(T)
     g = P.run_gpu(m, x, layer0, ws=ws)
-    np.testing.assert_array_equal(read_chunks(m, ws, T), expected_chunks(g["offsets"]))
+    np.testing.assert_array_equal(read_chunks(m, ws, T), expected_chunks(g["offsets"], T))
     report(f"T={T}", P.compare(g, oracle_layer(x), label=f"T={T}"))
 
 
@@ -378,7 +386,7 @@ def test_largest_token_count(m, layer0):
     x = gen_x_chunked(411, T)
     ws = m.workspace(T)
     g = P.run_gpu(m, x, layer0, ws=ws)
-    np.testing.assert_array_equal(read_chunks(m, ws, T), expected_chunks(g["offsets"]))
+    np.testing.assert_array_equal(read_chunks(m, ws, T), expected_chunks(g["offsets"], T))
     counts = np.diff(g["offsets"])
     busiest = int(np.argmax(counts))
     rows = g["perm"][[g["offsets"][busiest], g["offsets"][busiest + 1] - 1]] // 6
