@@ -244,7 +244,7 @@ int run_forward(const void *x_, const void *router_w_, const void *codes_, const
                                     grouped ? ws_at<int>(ws, L.hist) : nullptr));
         if (grouped)   // many workgroups
             MOE_STEP(launch_sort_wide(topk_idx, T, ws_at<int>(ws, L.hist), offsets, perm, pos, n_active, active,
-                                      chunks, n_chunks, error_clear, s, true));
+                                      chunks, n_chunks, error_clear, s));
         else
             MOE_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, error_clear,
                                  s));
@@ -394,7 +394,7 @@ int run_forward_nvfp4(const void *x_, const void *router_w_, const void *codes_,
                                    dense ? ws_at<int>(ws, L.hist) : nullptr));
         if (dense)
             NV_STEP(launch_sort_wide(topk_idx, T, ws_at<int>(ws, L.hist), offsets, perm, pos, n_active, active,
-                                     chunks, n_chunks, error, s, true));
+                                     chunks, n_chunks, error, s));
         else
             NV_STEP(launch_sort(topk_idx, T, offsets, perm, pos, n_active, active, chunks, n_chunks, error, s));
     }

@@ -74,8 +74,7 @@ void launch_decode_fused(const FusedDecodeArgs &args, hipStream_t s);
 // rotate = false: xt gets x itself as natural-order fp16 with the same
 // per-token prescale (the operands of the NVFP4 experts' MFMA form).
 // hist (or null): the wide sort's int[sort_hist_blocks(T)][256] histograms,
-// zero on entry, which the selections are counted into (the sort then skips
-// its own histogram launch).
+// zero on entry, which the selections are counted into.
 void launch_topk_rotate(const float *logits, const uint16_t *x, int T, const float *bias, int policy,
                         int *topk_idx, float *topk_w, uint32_t *xt, float *xt_scale, hipStream_t s,
                         bool rotate = true, int *hist = nullptr);
@@ -103,12 +102,12 @@ __host__ __device__ constexpr int chunk_count(int n, int T) { return (n + chunk_
 // token, second token, 0, 0, 0}, one per expert with tokens, then expert -1.
 // chunks: int[max_chunks(T)][4] records {expert, first sorted position, rows
 // (see chunk_step), 0} covering every expert's assignments; *n_chunks of them.
-// The same result from many workgroups (two launches, or one when the
-// top-6 launch already counted hist_ready), for prefill sizes: hist is
-// int[sort_hist_blocks(T)][256], the experts' counts per workgroup.
+// The same result from many workgroups, for prefill sizes: hist is
+// int[sort_hist_blocks(T)][256], the experts' counts per workgroup of 1024
+// assignments, which the top-6 launch before it filled (launch_topk_rotate).
 int sort_hist_blocks(int T);
-void launch_sort_wide(const int *topk_idx, int T, int *hist, int *offsets, int *perm, int *pos, int *n_active,
-                      int *slots, int *chunks, int *n_chunks, int *error, hipStream_t s, bool hist_ready = false);
+void launch_sort_wide(const int *topk_idx, int T, const int *hist, int *offsets, int *perm, int *pos,
+                      int *n_active, int *slots, int *chunks, int *n_chunks, int *error, hipStream_t s);
 // error (or null): the workspace's error word, cleared (this sequence cannot fail).
 void launch_sort(const int *topk_idx, int T, int *offsets, int *perm, int *pos, int *n_active,
                  int *slots, int *chunks, int *n_chunks, int *error, hipStream_t s);

@@ -250,7 +250,9 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
 // The same stable counting sort spread over many workgroups (prefill sizes):
 // workgroup b owns assignments [1024 b, 1024 b + 1024), wave w of it the 64
 // from 1024 b + 64 w.
-//   1. k_sort_hist: each workgroup's histogram over the experts -> hist[b][e].
+//   1. the top-6 launch before it adds each selection into the histogram of
+//      its workgroup over the experts, hist[b][e] (zeroed by the launch before
+//      that; a sum, so the order of the adds is free).
 //   2. k_sort_place: every workgroup reads all histograms: per expert the
 //      total (-> offsets) and the counts of the workgroups before it (its base
 //      inside the expert); inside the workgroup, per-wave counts and ballots
@@ -262,18 +264,6 @@ __global__ __launch_bounds__(1024) void k_sort(const int *__restrict__ topk_idx,
 // ---------------------------------------------------------------------------
 
 int sort_hist_blocks(int T) { return (kTopK * T + kSortWgAssign - 1) / kSortWgAssign; }
-
-__global__ __launch_bounds__(1024) void k_sort_hist(const int *__restrict__ topk_idx, int N, int *__restrict__ hist) {
-    __shared__ int cnt[kE];
-    const int tid = threadIdx.x;
-    if (tid < kE) cnt[tid] = 0;
-    const int a = (int)blockIdx.x * kSortWgAssign + tid;
-    const int e = a < N ? topk_idx[a] : -1;
-    __syncthreads();
-    if (e >= 0) atomicAdd(&cnt[e], 1);
-    __syncthreads();
-    if (tid < kE) hist[(size_t)blockIdx.x * kE + tid] = cnt[tid];
-}
 
 __global__ __launch_bounds__(1024) void k_sort_place(const int *__restrict__ topk_idx, int N, int nb,
                                                      const int *__restrict__ hist, int *__restrict__ offsets,
@@ -418,10 +408,9 @@ void launch_route_par(const float *logits, int T, const float *bias, int policy,
     hipLaunchKernelGGL(k_route_par, dim3((T + kRouteWaves - 1) / kRouteWaves), dim3(64 * kRouteWaves), 0, s, A);
 }
 
-void launch_sort_wide(const int *topk_idx, int T, int *hist, int *offsets, int *perm, int *pos, int *n_active,
-                      int *slots, int *chunks, int *n_chunks, int *error, hipStream_t s, bool hist_ready) {
+void launch_sort_wide(const int *topk_idx, int T, const int *hist, int *offsets, int *perm, int *pos,
+                      int *n_active, int *slots, int *chunks, int *n_chunks, int *error, hipStream_t s) {
     const int nb = sort_hist_blocks(T), N = kTopK * T;
-    if (!hist_ready) hipLaunchKernelGGL(k_sort_hist, dim3(nb), dim3(1024), 0, s, topk_idx, N, hist);
     hipLaunchKernelGGL(k_sort_place, dim3(nb), dim3(1024), 0, s, topk_idx, N, nb, hist, offsets, perm, pos, n_active,
                        slots, reinterpret_cast<int4 *>(chunks), n_chunks, error);
 }
