@@ -49,6 +49,13 @@
 // (y, and in a stack layer the residual stream, so that every later layer's
 // output is NaN too) and sets the workspace's error word, so a failure cannot
 // hang the device and cannot go unnoticed.
+//
+// The same launch serves the experts in the NVFP4 container (template
+// argument NV; Flint NVFP4 repack, kekzle/Flint-NVFP4, rows "Layout per
+// Linear" and "Declaration"): x and a enter as natural-order fp16 with one
+// power-of-two prescale per token or assignment (no Hadamard), the E2M1 codes
+// times their E4M3 block scales are exact products against them
+// (nvfp4_ops.h), and the fp32 tensor scales multiply the row sums.
 #include "common.h"
 #include "gemv_ops.h"
 #include "handoff.h"
