@@ -142,6 +142,32 @@ def test_grouped_chunks_of_a_hot_expert(m, layer0):
                                            label="grouped hot expert"))
 
 
+def test_grouped_chunk_of_96_rows(m, layer0):
+    """From 1536 tokens on an expert with at most 96 rows is one chunk: 96
+    tokens steered to expert 23 (x along its router row; a -100 bias keeps
+    every other token off it) make a 96-row chunk, three MFMA row tiles in
+    gate/up and two passes of 64 and 32 rows in down; every row compared."""
+    T, e = 1600, 23
+    print(f"[parity] case T={T} expert {e} with 96 rows", flush=True)
+    x = synth.gen_x(404, T).copy()
+    r = O.bf16_to_f64(synth.gen_router(0, 0)[e])
+    x[:96] = synth.f32_to_bf16_bits((500.0 * r).astype(np.float32))[None, :]
+    bias = np.zeros(256, dtype=np.float32)
+    bias[e] = -100.0
+    ws = m.workspace(T)
+    g = P.run_gpu(m, x, layer0, bias=bias, ws=ws)
+    assert np.diff(g["offsets"])[e] == 96
+    ch = read_chunks(m, ws, T)
+    np.testing.assert_array_equal(ch, expected_chunks(g["offsets"], T))
+    assert ch[ch[:, 0] == e].tolist() == [[e, int(g["offsets"][e]), 96, 0]]
+    # the steered rows are ~50 times larger than the others (x of norm ~460):
+    # each population is compared against its own rms
+    for label, tokens in (("steered", np.arange(96)), ("other", np.arange(96, T))):
+        s = P.compare(g, oracle_layer(x, bias=bias, tokens=tokens), tokens=tokens,
+                      label=f"grouped 96-row chunk, {label} rows")
+        report(f"grouped 96-row chunk, {label} rows", s)
+
+
 def test_grouped_batch_invariance(m, layer0):
     """Rows do not interact on the grouped path: the first 128 tokens of a
     256-token batch give the bits of the 128-token batch."""
