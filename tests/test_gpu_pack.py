@@ -108,3 +108,37 @@ def test_pack_full_layer(m):
     print(f"[pack] 256 experts: relative Frobenius error of the gate/up planes {rel.min():.4f}..{rel.max():.4f}",
           flush=True)
     assert np.all(np.abs(rel - c["int4_rel_frobenius"]) < 0.01)
+
+
+def test_pack_against_the_fp64_quantiser(m):
+    """The packer's output against the oracle's fp64 quantiser, which shares
+    no stage order with the packer's fp32 one: a scale moves by at most one
+    bf16 step (rarely), and inside groups of equal scale a code moves by at
+    most one step, only on rounding boundaries (the card's format; the
+    quantiser is the plain reading absmax / 7 and round-half-even)."""
+    bits = host_weights(61, 3)
+    codes, scales = run_pack(m, bits)
+    H, I, n = O.H, O.I_R, bits.shape[0]
+    nb_gu, ns_gu = 2 * I * H // 2, 2 * I * H // O.G
+    n_scales = n_codes = n_scale_moves = n_code_moves = 0
+    for e in range(n):
+        w = O.bf16_to_f64(bits[e])
+        planes = ((w[:2 * I * H].reshape(2 * I, H), codes[e, :nb_gu].reshape(2 * I, H // 2), scales[e, :ns_gu]),
+                  (w[2 * I * H:].reshape(H, I), codes[e, nb_gu:].reshape(H, I // 2), scales[e, ns_gu:]))
+        for wp, cp, sp in planes:
+            k = wp.shape[1]
+            c64, s64 = O.quantize_rotated(wp)
+            s_gpu = sp.reshape(s64.shape)
+            ds = np.abs(s_gpu.astype(np.int32) - s64.astype(np.int32))
+            assert ds.max() <= 1
+            same = np.repeat(ds == 0, O.G, axis=1)
+            dc = np.abs(O.unpack_int4(cp, k).astype(np.int32) - c64)
+            assert dc[same].max() <= 1
+            n_scales += s64.size
+            n_scale_moves += int((ds != 0).sum())
+            n_codes += int(same.sum())
+            n_code_moves += int((dc[same] != 0).sum())
+    print(f"[pack] against the fp64 quantiser: {n_scale_moves} of {n_scales} scales one step apart, "
+          f"{n_code_moves} of {n_codes} codes one step apart", flush=True)
+    assert n_scale_moves <= 1e-3 * n_scales
+    assert n_code_moves <= 1e-4 * n_codes
