@@ -27,7 +27,7 @@ Everything here is plain NumPy in float64 and follows the pages step by step:
   scales per 16 columns and an F32 tensor scale, W4A16 (the section at the
   end of this module, with its readings).
 
-Readings where the pages are silent (each is listed in the design doc too):
+Readings where the pages are silent:
 
 * Hadamard: Sylvester order, H[i][j] = (-1)**popcount(i & j) / sqrt(128),
   no random signs; symmetric and its own inverse.
@@ -497,7 +497,7 @@ def unrotated_effective(codes: np.ndarray, s_bits: np.ndarray) -> np.ndarray:
 # kekzle/Flint-NVFP4, table rows "Repack", "Layout per Linear" and
 # "Declaration"): per Linear, E2M1 codes two per byte, one E4M3 block scale
 # per 16 columns and one F32 tensor scale, declared W4A16 (weights 4-bit,
-# activations 16-bit).  Readings (listed in the design doc):
+# activations 16-bit).  Readings:
 #
 # * E2M1 and E4M3 are the OCP microscaling element and FP8 "FN" formats the
 #   names denote: E2M1 = sign, 2 exponent bits (bias 1), 1 mantissa bit,
