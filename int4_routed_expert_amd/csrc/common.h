@@ -68,11 +68,6 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
 // ---------------------------------------------------------------------------
 // int4 -> fp16 operands without a per-nibble conversion.
 //
-// This is the classic magic-number conversion of an integer to floating point
-// (write the integer into the low mantissa bits of 2^n, whose ulp is 1, and
-// subtract 2^n; the same move as the well-known 2^52 + i trick for doubles),
-// applied to fp16 with n = 10 and to nibbles.
-//
 // Eight signed int4 codes c0..c7 sit in one dword (c_i in bits 4i..4i+3).
 // XOR with 0x88888888 turns each into u_i = c_i + 8 in [0, 15].  OR-ing a
 // nibble into the mantissa of the fp16 1024.0 (0x6400) gives 1024 + u exactly;
